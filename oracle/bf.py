@@ -1,0 +1,227 @@
+"""Oracle, brute-force form: the STILL layer's definitions written out in fp64.
+
+TEST INFRASTRUCTURE ONLY. Nothing on the product path imports this module;
+only tests/, the smoke check and the bench's CPU-baseline leg may use it.
+It shares no code with the HIP path.
+
+Pages cited (short tag -> page title):
+  [P2] "NeurIPS 2026|层内混合注意力：告别位置「伪混合」，STILL首个内容感知的层内混合注意力架构"
+       (Chinese press article), sections 亮点一 (固定预算路由, 延迟选择与分块并行) and 亮点二
+  [P3] "STILL: Content-Aware Intra-Layer Hybrid Attention for Efficient LLM
+       Linearization", sections "Content-Aware Routing with Fixed Budget",
+       "Delayed Chunk-Level Selection for Unified Training-Inference
+       Parallelism", "Self-Saliency Score", "Theoretical Guarantee:
+       Local-Global Consistency", "NP-Map: Norm-Preserving Feature Map"
+
+Every query is handled on its own: the key set of each branch is built as an
+explicit index set and summed over directly (O(L^2 d) per unit). The state
+is summed over its explicit token set. Readings where the pages are silent
+(score form, merge rule, NP-Map form, GQA grouping, T_max) are the ones
+listed under "Readings" in the design notes; each function names its own.
+"""
+from __future__ import annotations
+
+import math
+from typing import Dict, List, Optional
+
+import numpy as np
+
+
+def budget_lambda(window: int, chunk: int, budget: int, t_max: int) -> int:
+    """Tokens kept per completed chunk.
+
+    [P2 固定预算路由], [P3 "Content-Aware Routing with Fixed Budget"]: of the
+    per-head budget m, W slots hold the recent window and the other m - W
+    are spread over completed chunks, floor((m - W) / T_max) per chunk.
+    Reading: the count is capped at C (a chunk has only C tokens).
+    """
+    if budget < window or t_max < 1 or chunk < 1 or window < 1:
+        raise ValueError("need budget >= window >= 1, chunk >= 1, t_max >= 1")
+    return min(chunk, (budget - window) // t_max)
+
+
+def full_chunks_out_of_window(c: int, window: int, chunk: int) -> int:
+    """Number of leading chunks lying wholly before the window of every
+    query of chunk c: chunk c' qualifies iff its last position
+    (c'+1)C - 1 <= cC - W. These are the chunks folded into the exported
+    linear-attention state (reading: the state absorbs whole chunks)."""
+    x = c * chunk - window + 1
+    return max(0, x // chunk) if x >= 0 else 0
+
+
+def saliency_kl(logits: np.ndarray, self_idx: int, eps: float) -> float:
+    """Self-Saliency Score of one token for one head.
+
+    [P3 "Self-Saliency Score"], [P2 亮点二]: two window attention
+    distributions are formed, a_diag with the token's own (diagonal) term
+    and a_nodiag without it, and the score is a KL-type sensitivity between
+    them. Reading (the formula is not printed): KL(a_diag || (1-eps) a_nodiag
+    + eps delta_self), eps > 0 small, so that the self entry has mass.
+    Computed here literally, entry by entry, from the two softmaxes.
+    """
+    s = np.asarray(logits, dtype=np.float64)
+    n = s.shape[0]
+    a_diag = np.exp(s - s.max())
+    a_diag /= a_diag.sum()
+    a_nodiag = np.zeros(n)
+    if n > 1:
+        others = np.delete(np.arange(n), self_idx)
+        e = np.exp(s[others] - s[others].max())
+        a_nodiag[others] = e / e.sum()
+    mix = (1.0 - eps) * a_nodiag
+    mix[self_idx] += eps
+    kl = 0.0
+    for j in range(n):
+        if a_diag[j] > 0.0:
+            kl += a_diag[j] * math.log(a_diag[j] / mix[j])
+    return kl
+
+
+def np_map(x: np.ndarray, F: np.ndarray) -> np.ndarray:
+    """NP-Map feature of a row vector x with map weights F [d, d].
+
+    [P3 "NP-Map: Norm-Preserving Feature Map"]: a learned map sets only the
+    direction of the feature, the input's own norm ||x|| is put back, and
+    the feature is non-negative. Reading: direction = softmax(x F) (a
+    Hedgehog-style softmax feature) normalised to unit L2 norm, then scaled
+    by ||x||_2. phi(0) = 0.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    a = x @ F
+    u = np.exp(a - a.max())
+    return np.linalg.norm(x) * u / np.linalg.norm(u)
+
+
+def prefill(q, k, v, fmap_w, gate, *, window: int, chunk: int, budget: int,
+            t_max: int, eps: float = 1e-6, sm_scale: Optional[float] = None,
+            partials: bool = False) -> Dict[str, np.ndarray]:
+    """One STILL layer over a whole sequence, every query by brute force.
+
+    q [B,Hq,L,d], k/v [B,Hkv,L,d], fmap_w [Hkv,d,d], gate [Hq] (any array
+    type convertible to float64). Query head h belongs to kv group h // G.
+
+    Returns y [B,Hq,L,d], score [B,Hkv,L], sel [B,Hkv,n_dec,lam] (ascending
+    positions, -1 where a chunk kept fewer), n_pool [B,Hkv], the exported
+    state S [B,Hkv,d,d], z [B,Hkv,d], and pending [B,Hkv,C] (scores of the
+    undecided chunk's tokens, NaN beyond the sequence end). With
+    partials=True also y_sa, lse_sa, y_la, lse_la (NaN where a branch is
+    empty or the gate is 0).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    Fw = np.asarray(fmap_w, dtype=np.float64)
+    g_all = np.asarray(gate, dtype=np.float64)
+    B, Hq, L, d = q.shape
+    Hkv = k.shape[1]
+    G = Hq // Hkv
+    W, C, m = window, chunk, budget
+    scale = 1.0 / math.sqrt(d) if sm_scale is None else sm_scale
+    lam = budget_lambda(W, C, m, t_max)
+    n_dec = (L - 1) // C if L > 0 else 0
+
+    y = np.zeros((B, Hq, L, d))
+    score = np.zeros((B, Hkv, L))
+    sel = -np.ones((B, Hkv, n_dec, lam), dtype=np.int64)
+    n_pool = np.zeros((B, Hkv), dtype=np.int64)
+    S = np.zeros((B, Hkv, d, d))
+    z = np.zeros((B, Hkv, d))
+    pending = np.full((B, Hkv, C), np.nan)
+    if partials:
+        y_sa = np.full((B, Hq, L, d), np.nan)
+        lse_sa = np.full((B, Hq, L), np.nan)
+        y_la = np.full((B, Hq, L, d), np.nan)
+        lse_la = np.full((B, Hq, L), np.nan)
+
+    pos = np.arange(L)
+    chunk_of = pos // C
+    for b in range(B):
+        for kv in range(Hkv):
+            K, V, F = k[b, kv], v[b, kv], Fw[kv]
+            heads = range(kv * G, kv * G + G)
+            # Score of every token, summed over the query heads of the group
+            # (reading: routing is per kv head).
+            sc = np.zeros(L)
+            for t in range(L):
+                lo = max(0, t - W + 1)
+                for h in heads:
+                    logits = scale * (K[lo:t + 1] @ q[b, h, t])
+                    sc[t] += saliency_kl(logits, t - lo, eps)
+            score[b, kv] = sc
+
+            # Delayed chunk-level Top-lambda: chunk c is decided when chunk
+            # c+1 begins [P3 "Delayed Chunk-Level Selection"], keeping the
+            # lambda best by (score desc, position asc); selections are
+            # permanent and the pool never exceeds m - W [P2 固定预算路由].
+            selected = np.zeros(L, dtype=bool)
+            pool = 0
+            for c in range(n_dec):
+                lam_c = lam if pool + lam <= m - W else 0
+                cand = sorted(range(c * C, (c + 1) * C), key=lambda j: (-sc[j], j))
+                chosen = sorted(cand[:lam_c])
+                selected[chosen] = True
+                sel[b, kv, c, :len(chosen)] = chosen
+                pool += lam_c
+            n_pool[b, kv] = pool
+
+            phik = np.stack([np_map(K[j], F) for j in range(L)]) if L else np.zeros((0, d))
+            for t in range(L):
+                c = t // C
+                in_pool = selected & (chunk_of < c)
+                in_a = (pos <= t) & ((pos >= t - W + 1) | (chunk_of == c) | in_pool)
+                in_b = (pos <= t) & ~in_a
+                ia, ib = np.nonzero(in_a)[0], np.nonzero(in_b)[0]
+                for h in heads:
+                    s = scale * (K[ia] @ q[b, h, t])
+                    w = g_all[h] * (phik[ib] @ np_map(q[b, h, t], F))
+                    with np.errstate(divide="ignore"):
+                        logw = np.concatenate([s, np.log(w)])
+                    mx = logw.max()
+                    e = np.exp(logw - mx)
+                    vals = np.concatenate([V[ia], V[ib]])
+                    y[b, h, t] = (e @ vals) / e.sum()
+                    if partials:
+                        ea = np.exp(s - s.max())
+                        y_sa[b, h, t] = (ea @ V[ia]) / ea.sum()
+                        lse_sa[b, h, t] = s.max() + math.log(ea.sum())
+                        if len(ib) and w.sum() > 0:
+                            y_la[b, h, t] = (w @ V[ib]) / w.sum()
+                            lse_la[b, h, t] = math.log(w.sum())
+
+            if L:
+                c_last = (L - 1) // C
+                cf = full_chunks_out_of_window(c_last, W, C)
+                folded = (~selected) & (chunk_of < cf)
+                S[b, kv] = phik[folded].T @ V[folded]
+                z[b, kv] = phik[folded].sum(axis=0)
+                pend = pos[chunk_of == c_last]
+                pending[b, kv, :len(pend)] = sc[pend]
+
+    out = {"y": y, "score": score, "sel": sel, "n_pool": n_pool, "S": S, "z": z,
+           "pending": pending, "lam": lam, "n_dec": n_dec}
+    if partials:
+        out.update(y_sa=y_sa, lse_sa=lse_sa, y_la=y_la, lse_la=lse_la)
+    return out
+
+
+def key_sets(L: int, window: int, chunk: int, sel_rows: List[List[int]]):
+    """The softmax (A) and linear (B) key sets of every query, for tests.
+
+    sel_rows[c] lists the positions kept from chunk c. Returns boolean
+    matrices A, B of shape [L, L] (row = query, column = key).
+    """
+    pos = np.arange(L)
+    chunk_of = pos // chunk
+    selected_chunk = np.full(L, -1)
+    for c, row in enumerate(sel_rows):
+        for j in row:
+            if j >= 0:
+                selected_chunk[j] = c
+    A = np.zeros((L, L), dtype=bool)
+    Bm = np.zeros((L, L), dtype=bool)
+    for t in range(L):
+        c = t // chunk
+        in_pool = (selected_chunk >= 0) & (chunk_of < c)
+        A[t] = (pos <= t) & ((pos >= t - window + 1) | (chunk_of == c) | in_pool)
+        Bm[t] = (pos <= t) & ~A[t]
+    return A, Bm

@@ -1,0 +1,114 @@
+"""Python wrapper of the recurrent oracle (oracle/still_oracle.c).
+
+TEST INFRASTRUCTURE ONLY: used by tests/, the smoke check and the bench's
+CPU-baseline leg. It never touches a GPU and imports nothing from the HIP
+path.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import subprocess
+from typing import Dict, Optional, Sequence, Tuple
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "still_oracle.c")
+_OUT_DIR = os.path.join(_HERE, "_build")
+_LIB_PATH = os.path.join(_OUT_DIR, "liboracle.so")
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (fp64, strict evaluation order)."""
+    if not force and os.path.exists(_LIB_PATH):
+        return _LIB_PATH
+    os.makedirs(_OUT_DIR, exist_ok=True)
+    tmp = _LIB_PATH + ".tmp%d" % os.getpid()
+    subprocess.run(["gcc", "-O3", "-march=native", "-ffp-contract=off", "-fPIC",
+                    "-shared", "-pthread", "-o", tmp, _SRC, "-lm"], check=True)
+    os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH) or (
+                os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC)):
+            build()
+        lib = ctypes.CDLL(_LIB_PATH)
+        f = lib.still_oracle_run
+        P = ctypes.c_void_p
+        f.argtypes = [ctypes.c_int] * 8 + [ctypes.c_double] * 2 + [P] * 5 + \
+            [ctypes.c_int] + [P] * 7
+        f.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def _f32(a) -> np.ndarray:
+    if hasattr(a, "detach"):  # torch tensor: widen to float32 (exact for bf16)
+        a = a.detach().to("cpu").float().numpy()
+    return np.ascontiguousarray(np.asarray(a, dtype=np.float32))
+
+
+def units_of(B: int, Hkv: int) -> Sequence[Tuple[int, int]]:
+    return [(b, kv) for b in range(B) for kv in range(Hkv)]
+
+
+def prefill(q, k, v, fmap_w, gate, *, window: int, chunk: int, budget: int,
+            t_max: int, eps: float = 1e-6, sm_scale: Optional[float] = None,
+            units: Optional[Sequence[Tuple[int, int]]] = None,
+            n_threads: int = 1) -> Dict[str, np.ndarray]:
+    """Run the recurrent oracle on the listed (batch, kv head) units.
+
+    q [B,Hq,L,d], k/v [B,Hkv,L,d], fmap_w [Hkv,d,d], gate [Hq]. Outputs
+    are per unit, in the order of `units` (default: every unit, batch-major):
+    y [U,G,L,d], score [U,L], sel [U,n_dec,lam], S [U,d,d], z [U,d],
+    pending [U,C], n_pool [U].
+    """
+    B, Hq, L, d = q.shape
+    Hkv = k.shape[1]
+    G = Hq // Hkv
+    units = list(units_of(B, Hkv) if units is None else units)
+    U = len(units)
+    qs = np.stack([_f32(q[b, kv * G:(kv + 1) * G]) for b, kv in units]) if U else \
+        np.zeros((0, G, L, d), np.float32)
+    ks = np.stack([_f32(k[b, kv]) for b, kv in units]) if U else np.zeros((0, L, d), np.float32)
+    vs = np.stack([_f32(v[b, kv]) for b, kv in units]) if U else np.zeros((0, L, d), np.float32)
+    Fs = np.stack([_f32(fmap_w[kv]) for _, kv in units]) if U else np.zeros((0, d, d), np.float32)
+    gs = np.stack([_f32(gate[kv * G:(kv + 1) * G]) for _, kv in units]) if U else \
+        np.zeros((0, G), np.float32)
+    return run_units(qs, ks, vs, Fs, gs, window=window, chunk=chunk, budget=budget,
+                     t_max=t_max, eps=eps, sm_scale=sm_scale, n_threads=n_threads)
+
+
+def run_units(qs, ks, vs, Fs, gs, *, window: int, chunk: int, budget: int, t_max: int,
+              eps: float = 1e-6, sm_scale: Optional[float] = None,
+              n_threads: int = 1) -> Dict[str, np.ndarray]:
+    """Run on pre-gathered per-unit arrays (see still_oracle_run)."""
+    qs, ks, vs, Fs, gs = (_f32(a) for a in (qs, ks, vs, Fs, gs))
+    U, G, L, d = qs.shape
+    lam = min(chunk, (budget - window) // t_max) if budget >= window else 0
+    n_dec = (L - 1) // chunk if L > 0 else 0
+    scale = 1.0 / math.sqrt(d) if sm_scale is None else float(sm_scale)
+    y = np.zeros((U, G, L, d))
+    score = np.zeros((U, L))
+    sel = np.full((U, n_dec, max(lam, 0)), -1, dtype=np.int32)
+    S = np.zeros((U, d, d))
+    z = np.zeros((U, d))
+    pending = np.zeros((U, chunk))
+    n_pool = np.zeros((U,), dtype=np.int32)
+    lib = _load()
+    ptr = lambda a: a.ctypes.data_as(ctypes.c_void_p)
+    rc = lib.still_oracle_run(U, L, d, G, window, chunk, budget, t_max, float(eps), scale,
+                              ptr(qs), ptr(ks), ptr(vs), ptr(Fs), ptr(gs), int(n_threads),
+                              ptr(y), ptr(score), ptr(sel), ptr(S), ptr(z), ptr(pending),
+                              ptr(n_pool))
+    if rc != 0:
+        raise ValueError("still_oracle_run rejected its arguments (rc=%d)" % rc)
+    return {"y": y, "score": score, "sel": sel, "S": S, "z": z, "pending": pending,
+            "n_pool": n_pool, "lam": lam, "n_dec": n_dec}

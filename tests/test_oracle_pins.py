@@ -1,0 +1,369 @@
+"""Pins of the oracle against facts fixed outside it (CPU only).
+
+Each test checks the oracle against something other than itself: a
+hand-worked example, a closed form, a library routine a special case reduces
+to (scipy's relative entropy, torch's scaled-dot-product attention and
+softmax), invariants the pages state, or the other oracle form on random
+tiny shapes. Citations name the article "STILL: Content-Aware Intra-Layer
+Hybrid Attention for Efficient LLM Linearization" by section.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+from scipy.special import rel_entr, softmax as sp_softmax
+
+from oracle import bf, rec
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+EPS = 1e-6
+
+
+def rand_inputs(rng, B, Hq, Hkv, L, d, sigma=0.5, outliers=0):
+    def tok(H):
+        z = rng.standard_normal((B, H, L, d))
+        r = np.exp(sigma * rng.standard_normal((B, H, L, 1)))
+        if outliers:
+            for b in range(B):
+                r[b, :, rng.choice(L, outliers, replace=False)] *= 8.0
+        return (z * r).astype(np.float32).astype(np.float64)
+    q, k, v = tok(Hq), tok(Hkv), tok(Hkv)
+    F = (rng.standard_normal((Hkv, d, d)) / math.sqrt(d)).astype(np.float32).astype(np.float64)
+    g = rng.uniform(0, 1, Hq).astype(np.float32).astype(np.float64)
+    return q, k, v, F, g
+
+
+def phi_torch(x, F):
+    """NP-Map via torch's softmax: ||x|| * softmax(xF) / ||softmax(xF)||."""
+    x = torch.as_tensor(x, dtype=torch.float64)
+    u = torch.softmax(x @ torch.as_tensor(F, dtype=torch.float64), dim=-1)
+    return (x.norm(dim=-1, keepdim=True) * u / u.norm(dim=-1, keepdim=True)).numpy()
+
+
+def sdpa(q, k, v, mask, scale):
+    """torch's scaled-dot-product attention in fp64 on the CPU."""
+    return torch.nn.functional.scaled_dot_product_attention(
+        torch.as_tensor(q), torch.as_tensor(k), torch.as_tensor(v),
+        attn_mask=torch.as_tensor(mask), scale=scale).numpy()
+
+
+# ---------------------------------------------------------------- score ----
+
+def test_score_hand_example():
+    """W = 2, logits (0, ln 3) with the token last: p = 3/4, so the score is
+    the two-point KL 3/4 ln(3/4 / eps) + 1/4 ln(1/4 / (1 - eps))."""
+    s = np.array([0.0, math.log(3.0)])
+    want = 0.75 * math.log(0.75 / EPS) + 0.25 * math.log(0.25 / (1 - EPS))
+    assert bf.saliency_kl(s, 1, EPS) == pytest.approx(want, rel=1e-14)
+
+
+@pytest.mark.parametrize("n", [2, 3, 16, 64])
+def test_score_is_bernoulli_relative_entropy(n):
+    """The literal KL over the window equals KL(Bern(p) || Bern(eps)) with
+    p the self entry of the window softmax (scipy's rel_entr)."""
+    rng = np.random.default_rng(n)
+    for _ in range(20):
+        s = rng.standard_normal(n) * rng.uniform(0.1, 10)
+        idx = int(rng.integers(n))
+        p = sp_softmax(s)[idx]
+        want = rel_entr(p, EPS) + rel_entr(1 - p, 1 - EPS)
+        assert bf.saliency_kl(s, idx, EPS) == pytest.approx(want, rel=1e-10, abs=1e-12)
+
+
+def test_score_single_key_window():
+    assert bf.saliency_kl(np.array([3.7]), 0, EPS) == pytest.approx(math.log(1 / EPS), rel=1e-15)
+
+
+def test_score_monotone_in_self_probability():
+    """Proposition 1 (section "Theoretical Guarantee"): the score increases
+    with the local self-attention probability p for p > eps."""
+    p_vals = np.linspace(2 * EPS, 1.0, 400)
+    scores = []
+    for p in p_vals:
+        # window of 4: self logit chosen so the self probability is p
+        others = np.zeros(3)
+        s_self = math.log(p / (1 - p) * 3.0) if p < 1 else 50.0
+        scores.append(bf.saliency_kl(np.concatenate([others, [s_self]]), 3, EPS))
+    assert np.all(np.diff(scores) > 0)
+
+
+# --------------------------------------------------------------- NP-Map ----
+
+def test_np_map_properties():
+    """Section "NP-Map": direction from the learned map, norm re-injected,
+    non-negative features."""
+    rng = np.random.default_rng(1)
+    d = 32
+    F = rng.standard_normal((d, d)) / math.sqrt(d)
+    for scale in [1e-3, 1.0, 30.0]:
+        x = rng.standard_normal(d) * scale
+        f = bf.np_map(x, F)
+        assert np.linalg.norm(f) == pytest.approx(np.linalg.norm(x), rel=1e-12)
+        assert np.all(f > 0)
+        np.testing.assert_allclose(f, phi_torch(x, F), rtol=1e-12)
+    assert np.all(bf.np_map(np.zeros(d), F) == 0)
+
+
+# --------------------------------------------------- hand-worked example ----
+
+def _hand():
+    with open(os.path.join(HERE, "golden", "hand_example.json")) as fh:
+        fx = json.load(fh)
+    env = {"sqrt2*ln2": math.sqrt(2) * math.log(2), "sqrt2*ln3": math.sqrt(2) * math.log(3)}
+    conv = lambda a: np.array(json.loads(json.dumps(a)), dtype=object)
+
+    def num(a):
+        return np.vectorize(lambda e: env[e] if isinstance(e, str) else float(e))(conv(a)).astype(np.float64)
+    ins = {k: num(v) for k, v in fx["inputs"].items()}
+    return fx, ins
+
+
+def _hand_expected():
+    r2, l3 = math.sqrt(2), math.log(3)
+    v = np.array([[1, 0], [0, 1], [2, 2], [-1, 3]], dtype=np.float64)
+    y = np.zeros((4, 2))
+    y[0] = v[0]
+    y[1] = (v[0] + 4 * v[1]) / 5
+    y[2] = (v[2] + (r2 / 2) * v[0] + r2 * v[1]) / (1 + 3 * r2 / 2)
+    y[3] = (3 * v[2] + v[3] / 3 + (r2 / 2) * l3 * v[0] + r2 * l3 * v[1]) / (3 + 1 / 3 + 1.5 * r2 * l3)
+    S = np.array([[1 / r2, r2], [1 / r2, r2]])
+    z = np.array([3 / r2, 3 / r2])
+    return y, S, z
+
+
+@pytest.mark.parametrize("form", ["bf", "rec"])
+def test_hand_worked_example(form):
+    fx, ins = _hand()
+    p = fx["params"]
+    kw = dict(window=p["window"], chunk=p["chunk"], budget=p["budget"], t_max=p["t_max"], eps=p["eps"])
+    run = bf.prefill if form == "bf" else rec.prefill
+    o = run(ins["q"], ins["k"], ins["v"], ins["fmap_w"], ins["gate"], **kw)
+    y, S, z = _hand_expected()
+    # rec's inputs pass through float32: sqrt2*ln2 etc. are rounded there
+    tol = 1e-12 if form == "bf" else 1e-6
+    np.testing.assert_allclose(o["y"].reshape(4, 2), y, atol=tol)
+    np.testing.assert_allclose(o["S"].reshape(2, 2), S, atol=tol)
+    np.testing.assert_allclose(o["z"].reshape(2), z, atol=tol)
+    np.testing.assert_allclose(o["score"].reshape(4), math.log(1 / EPS), rtol=1e-14)
+    np.testing.assert_allclose(o["pending"].reshape(2), math.log(1 / EPS), rtol=1e-14)
+    assert o["lam"] == 0
+
+
+# ---------------------------------------------- textbook reductions --------
+
+@pytest.mark.parametrize("form", ["bf", "rec"])
+@pytest.mark.parametrize("W,C,L", [(4, 8, 40), (8, 8, 33), (12, 4, 29)])
+def test_everything_kept_is_causal_softmax(form, W, C, L):
+    """lambda = C (m - W >= T_max C): every decided chunk is kept whole, the
+    linear branch is empty and the layer is causal softmax attention."""
+    rng = np.random.default_rng(W * 100 + C)
+    q, k, v, F, g = rand_inputs(rng, 1, 2, 1, L, 16)
+    t_max = -(-L // C)
+    run = bf.prefill if form == "bf" else rec.prefill
+    o = run(q, k, v, F, g, window=W, chunk=C, budget=W + t_max * C, t_max=t_max)
+    assert o["lam"] == C
+    y = o["y"] if form == "bf" else o["y"][None, :, :, :].reshape(1, 2, L, 16)
+    causal = np.tril(np.ones((L, L), dtype=bool))
+    want = sdpa(q, np.repeat(k, 2, 1), np.repeat(v, 2, 1), causal, 1 / 4.0)
+    np.testing.assert_allclose(y, want, atol=1e-12)
+
+
+def test_gate_zero_is_softmax_over_kept_and_window():
+    """g = 0: the output is softmax attention restricted to A(t) (window,
+    own chunk, kept tokens); checked with torch's masked SDPA."""
+    rng = np.random.default_rng(5)
+    L, C, W = 48, 8, 5
+    q, k, v, F, g = rand_inputs(rng, 1, 1, 1, L, 16)
+    o = bf.prefill(q, k, v, F, np.zeros(1), window=W, chunk=C, budget=W + 12, t_max=6)
+    A, _ = bf.key_sets(L, W, C, o["sel"][0, 0].tolist())
+    want = sdpa(q, k, v, A, 1 / 4.0)
+    np.testing.assert_allclose(o["y"], want, atol=1e-12)
+
+
+@pytest.mark.parametrize("W,C", [(3, 8), (8, 8), (10, 4)])
+def test_nothing_kept_gate_zero_is_sliding_window(W, C):
+    """lambda = 0 and g = 0 reduce to sliding-window (plus own chunk)
+    softmax attention, the positional routing the pages contrast with."""
+    rng = np.random.default_rng(W + C)
+    L = 37
+    q, k, v, F, _ = rand_inputs(rng, 1, 1, 1, L, 8)
+    o = bf.prefill(q, k, v, F, np.zeros(1), window=W, chunk=C, budget=W, t_max=5)
+    i, j = np.indices((L, L))
+    mask = (j <= i) & ((j >= i - W + 1) | (j // C == i // C))
+    np.testing.assert_allclose(o["y"], sdpa(q, k, v, mask, 1 / math.sqrt(8)), atol=1e-12)
+
+
+def test_linear_branch_is_masked_linear_attention():
+    """With nothing kept, the linear branch is the textbook quadratic form
+    of (NP-Map) linear attention over keys outside the window and chunk:
+    (M * phi(Q) phi(K)^T) V / row sums."""
+    rng = np.random.default_rng(7)
+    L, C, W, d = 40, 8, 6, 16
+    q, k, v, F, g = rand_inputs(rng, 1, 1, 1, L, d)
+    o = bf.prefill(q, k, v, F, g, window=W, chunk=C, budget=W, t_max=5, partials=True)
+    pq, pk = phi_torch(q[0, 0], F[0]), phi_torch(k[0, 0], F[0])
+    i, j = np.indices((L, L))
+    M = (j <= i - W) & (j // C < i // C)
+    Wm = M * (pq @ pk.T)
+    rows = M.any(1)
+    want = (Wm @ v[0, 0])[rows] / Wm.sum(1, keepdims=True)[rows]
+    np.testing.assert_allclose(o["y_la"][0, 0][rows], want, rtol=1e-11, atol=1e-12)
+    assert np.all(np.isnan(o["y_la"][0, 0][~rows]))
+    # the merge: one normaliser over exp(logits) and g * <phi, phi>
+    za, zl = np.exp(o["lse_sa"][0, 0][rows]), g[0] * Wm.sum(1)[rows]
+    mix = (za[:, None] * o["y_sa"][0, 0][rows] + zl[:, None] * want) / (za + zl)[:, None]
+    np.testing.assert_allclose(o["y"][0, 0][rows], mix, rtol=1e-10, atol=1e-12)
+
+
+# ------------------------------------------------------------ invariants ----
+
+def _check_selection(o, L, W, C, m):
+    lam, n_dec = o["lam"], o["n_dec"]
+    for b in range(o["sel"].shape[0]):
+        for kv in range(o["sel"].shape[1]):
+            pool = 0
+            sc = o["score"][b, kv]
+            for c in range(n_dec):
+                row = [int(j) for j in o["sel"][b, kv, c] if j >= 0]
+                lam_c = lam if pool + lam <= m - W else 0
+                assert len(row) == lam_c
+                assert row == sorted(row) and len(set(row)) == len(row)
+                assert all(c * C <= j < (c + 1) * C for j in row)
+                rest = [j for j in range(c * C, (c + 1) * C) if j not in row]
+                if row and rest:
+                    worst_kept = min(row, key=lambda j: (sc[j], -j))
+                    best_left = max(rest, key=lambda j: (sc[j], -j))
+                    assert (sc[worst_kept], -worst_kept) > (sc[best_left], -best_left)
+                pool += lam_c
+            assert pool == o["n_pool"][b, kv] <= m - W
+
+
+def test_selection_invariants_and_state_excludes_kept():
+    """Exactly lambda kept per decided chunk while the budget lasts, the
+    kept ones outrank the rest, none enters the linear state."""
+    rng = np.random.default_rng(11)
+    L, C, W, m, tm, d = 70, 8, 5, 5 + 12, 4, 8   # lam = 3; pool fills at 4 chunks
+    q, k, v, F, g = rand_inputs(rng, 2, 4, 2, L, d)
+    o = bf.prefill(q, k, v, F, g, window=W, chunk=C, budget=m, t_max=tm)
+    assert o["lam"] == 3 and o["n_dec"] == 8
+    _check_selection(o, L, W, C, m)
+    for b in range(2):
+        for kv in range(2):
+            kept = {int(j) for j in o["sel"][b, kv].ravel() if j >= 0}
+            c_last = (L - 1) // C
+            cf = bf.full_chunks_out_of_window(c_last, W, C)
+            folded = [j for j in range(cf * C) if j not in kept]
+            pk = phi_torch(k[b, kv], F[kv])
+            want_S = pk[folded].T @ v[b, kv][folded]
+            np.testing.assert_allclose(o["S"][b, kv], want_S, rtol=1e-11, atol=1e-11)
+            np.testing.assert_allclose(o["z"][b, kv], pk[folded].sum(0), rtol=1e-12)
+            with_kept = pk[:cf * C].T @ v[b, kv][:cf * C]
+            assert np.abs(with_kept - o["S"][b, kv]).max() > 1e-3
+
+
+def test_tie_rule_lower_index_first():
+    """W = 1: every window holds only the token, p = 1 and all scores tie;
+    ties go to the lower position, so each chunk keeps its first lambda."""
+    rng = np.random.default_rng(3)
+    L, C = 40, 8
+    q, k, v, F, g = rand_inputs(rng, 1, 2, 1, L, 8)
+    for run in (bf.prefill, rec.prefill):
+        o = run(q, k, v, F, g, window=1, chunk=C, budget=1 + 2 * 5, t_max=5)
+        sel = np.asarray(o["sel"]).reshape(-1, 2)
+        want = np.array([[c * C, c * C + 1] for c in range(4)])
+        np.testing.assert_array_equal(sel, want)
+        np.testing.assert_allclose(np.asarray(o["score"]).ravel(), 2 * math.log(1 / EPS), rtol=1e-14)
+
+
+def test_output_is_convex_combination():
+    rng = np.random.default_rng(13)
+    L = 50
+    q, k, v, F, g = rand_inputs(rng, 1, 2, 1, L, 8, outliers=3)
+    o = bf.prefill(q, k, v, F, g, window=4, chunk=8, budget=4 + 6, t_max=6)
+    vv = v[0, 0]
+    for t in range(L):
+        lo, hi = vv[:t + 1].min(0), vv[:t + 1].max(0)
+        for h in range(2):
+            assert np.all(o["y"][0, h, t] >= lo - 1e-12) and np.all(o["y"][0, h, t] <= hi + 1e-12)
+
+
+def test_causality_and_prefix_consistency():
+    """Changing tokens after position t0 changes no output, score or
+    decision made by t0 (decode of later tokens continues the prefill)."""
+    rng = np.random.default_rng(17)
+    L, t0, C, W = 56, 30, 8, 6
+    q, k, v, F, g = rand_inputs(rng, 1, 2, 1, L, 8)
+    kw = dict(window=W, chunk=C, budget=W + 9, t_max=3)
+    a = rec.prefill(q, k, v, F, g, **kw)
+    q2, k2, v2 = q.copy(), k.copy(), v.copy()
+    for x in (q2, k2, v2):
+        x[:, :, t0 + 1:] = rng.standard_normal(x[:, :, t0 + 1:].shape)
+    b = rec.prefill(q2, k2, v2, F, g, **kw)
+    np.testing.assert_array_equal(a["y"][..., :t0 + 1, :], b["y"][..., :t0 + 1, :])
+    np.testing.assert_array_equal(a["score"][..., :t0 + 1], b["score"][..., :t0 + 1])
+    n_decided = t0 // C
+    np.testing.assert_array_equal(a["sel"][:, :n_decided], b["sel"][:, :n_decided])
+    c = rec.prefill(q[:, :, :t0 + 1], k[:, :, :t0 + 1], v[:, :, :t0 + 1], F, g, **kw)
+    np.testing.assert_array_equal(c["y"], a["y"][..., :t0 + 1, :])
+
+
+def test_gqa_group_and_permutations():
+    """G = 1 is multi-head attention; permuting batch rows or kv groups
+    (with their heads, map weights and gates) permutes the outputs."""
+    rng = np.random.default_rng(19)
+    L = 24
+    q, k, v, F, g = rand_inputs(rng, 2, 4, 2, L, 8)
+    kw = dict(window=3, chunk=4, budget=3 + 6, t_max=6)
+    o = bf.prefill(q, k, v, F, g, **kw)
+    # each kv group alone, as G = 2 MHA-like runs
+    for kv in range(2):
+        oo = bf.prefill(q[:, 2 * kv:2 * kv + 2], k[:, kv:kv + 1], v[:, kv:kv + 1], F[kv:kv + 1],
+                        g[2 * kv:2 * kv + 2], **kw)
+        np.testing.assert_allclose(oo["y"], o["y"][:, 2 * kv:2 * kv + 2], atol=1e-14)
+    perm_q = [2, 3, 0, 1]
+    op = bf.prefill(q[::-1][:, perm_q], k[::-1][:, ::-1], v[::-1][:, ::-1], F[::-1], g[perm_q], **kw)
+    np.testing.assert_allclose(op["y"], o["y"][::-1][:, perm_q], atol=1e-14)
+    np.testing.assert_array_equal(op["sel"], o["sel"][::-1][:, ::-1])
+    # G = 1: one query head per kv head
+    o1 = bf.prefill(q[:, :1], k[:, :1], v[:, :1], F[:1], g[:1], **kw)
+    o1b = bf.prefill(q[:, :1], k[:, :1], v[:, :1], F[:1], g[:1], **kw)
+    np.testing.assert_array_equal(o1["y"], o1b["y"])
+
+
+CASES = [
+    # (B, Hq, Hkv, L, d, W, C, m, t_max, outliers)
+    (1, 1, 1, 64, 8, 4, 8, 4 + 8, 8, 0),          # W < C, lam = 1
+    (1, 2, 1, 61, 8, 8, 8, 8 + 14, 7, 2),         # W = C, ragged L
+    (2, 4, 2, 45, 8, 11, 4, 11 + 24, 6, 1),       # W > C, lam = 4 = C
+    (1, 2, 2, 50, 16, 5, 8, 5 + 3, 7, 0),         # lam = 0
+    (1, 3, 1, 77, 8, 6, 8, 6 + 8, 2, 2),          # lam = 4, budget fills
+    (1, 2, 1, 1, 8, 4, 8, 12, 1, 0),              # one token
+    (1, 2, 1, 8, 8, 4, 8, 12, 1, 0),              # one chunk, nothing decided
+    (1, 2, 1, 9, 8, 2, 8, 12, 1, 0),              # one decided chunk
+]
+
+
+@pytest.mark.parametrize("case", CASES)
+def test_recurrent_matches_brute_force(case):
+    """The two oracle forms (explicit sets vs. token-by-token recurrence)
+    agree to fp64 rounding on tiny shapes covering the edge cases."""
+    B, Hq, Hkv, L, d, W, C, m, tm, nout = case
+    rng = np.random.default_rng(sum(case))
+    q, k, v, F, g = rand_inputs(rng, B, Hq, Hkv, L, d, outliers=nout)
+    kw = dict(window=W, chunk=C, budget=m, t_max=tm)
+    a = bf.prefill(q, k, v, F, g, **kw)
+    r = rec.prefill(q, k, v, F, g, **kw)
+    G = Hq // Hkv
+    U = B * Hkv
+    np.testing.assert_allclose(r["y"], a["y"].reshape(B, Hkv, G, L, d).reshape(U, G, L, d),
+                               rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(r["score"], a["score"].reshape(U, L), rtol=1e-12, atol=1e-12)
+    np.testing.assert_array_equal(r["sel"], a["sel"].reshape(U, a["n_dec"], a["lam"]))
+    np.testing.assert_allclose(r["S"], a["S"].reshape(U, d, d), rtol=1e-11, atol=1e-11)
+    np.testing.assert_allclose(r["z"], a["z"].reshape(U, d), rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(r["pending"], a["pending"].reshape(U, C), rtol=1e-12, atol=1e-12)
+    np.testing.assert_array_equal(r["n_pool"], a["n_pool"].reshape(U))
+    _check_selection(a, L, W, C, m)
