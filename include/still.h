@@ -1,0 +1,159 @@
+/*
+ * still.h -- C ABI of libstill.so: the forward pass of one STILL attention
+ * layer (intra-layer hybrid of softmax and linear attention) on gfx950.
+ *
+ * Pages cited (short tag -> page title):
+ *   [P2] "NeurIPS 2026|层内混合注意力：告别位置「伪混合」，STILL首个内容感知的层内混合注意力架构",
+ *        sections 亮点一 (固定预算路由, 延迟选择与分块并行), 亮点二
+ *   [P3] "STILL: Content-Aware Intra-Layer Hybrid Attention for Efficient
+ *        LLM Linearization", sections "Content-Aware Routing with Fixed
+ *        Budget", "Delayed Chunk-Level Selection for Unified
+ *        Training-Inference Parallelism", "Self-Saliency Score",
+ *        "NP-Map: Norm-Preserving Feature Map"
+ *
+ * What one layer computes, per batch row b and kv head k (query heads
+ * h = k*G .. k*G+G-1 share k's keys, values, routing and state):
+ *   score(t)  Self-Saliency Score [P3 "Self-Saliency Score"], reading:
+ *             sum over the group's heads of KL(a_diag || (1-eps) a_nodiag +
+ *             eps delta_t) over the window [t-W+1, t], logits scaled by
+ *             sm_scale.
+ *   routing   [P3 "Content-Aware Routing ..."], [P2 固定预算路由]: budget m =
+ *             W window slots + m-W kept slots; when chunk c+1 begins, chunk c
+ *             keeps its lambda = min(C, floor((m-W)/T_max)) best tokens by
+ *             (score desc, position asc) [P3 "Delayed Chunk-Level
+ *             Selection ..."], while the kept pool has room; kept tokens stay.
+ *   output    softmax over A(t) = window, own chunk's prefix and kept tokens;
+ *             NP-Map linear attention over B(t) = every other past token
+ *             (decided, not kept, left the window) [P3 "NP-Map ..."]; one
+ *             normaliser over exp(logit) and gate[h] * <phi(q), phi(k)>.
+ *   state     S = sum phi(k_j) v_j^T, z = sum phi(k_j) over the unkept tokens
+ *             of the chunks lying wholly before the window of every query of
+ *             the current chunk; the kept pool; the recent tokens (ring); the
+ *             fp64 scores of the undecided chunk; the position.
+ *
+ * Conventions (all entry points):
+ *   - Tensor pointers are DEVICE pointers to contiguous arrays, 16-byte
+ *     aligned; params are host memory. The caller owns every buffer; the
+ *     library never allocates, frees or synchronises in these calls.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = default stream)
+ *     and is asynchronous. Arguments are validated on the host before any
+ *     launch: on failure a negative status is returned and nothing is
+ *     written or launched. A launch failure returns STILL_EHIP.
+ *   - Layouts are row-major: q/out [B, Hq, L, d], k/v [B, Hkv, L, d].
+ *     Element type of q, k, v, fmap_w, out is params.dtype (out is float32
+ *     when STILL_FLAG_FP32_OUT is set). gate is float32 [Hq], each in [0,1].
+ *   - Supported: head_dim 64 or 128; chunk 16, 32, 64 or 128; window >= 1;
+ *     budget >= window; t_max >= 1; n_q_heads a multiple of n_kv_heads
+ *     with G = n_q_heads / n_kv_heads <= 8. All sequences of a batch share
+ *     one length / position.
+ */
+#ifndef STILL_H
+#define STILL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define STILL_ABI_VERSION 1
+
+enum { STILL_DTYPE_F32 = 0, STILL_DTYPE_BF16 = 1 };
+
+/* flags */
+#define STILL_FLAG_FP32_OUT 1u /* write `out` as float32 whatever the dtype */
+
+/* status codes */
+#define STILL_OK 0
+#define STILL_EINVAL (-1)       /* null pointer, bad size or value */
+#define STILL_EUNSUPPORTED (-2) /* valid but not built (head_dim, chunk, G) */
+#define STILL_EWORKSPACE (-3)   /* workspace smaller than still_workspace_bytes */
+#define STILL_EHIP (-4)         /* a HIP launch failed */
+#define STILL_ESTATE (-5)       /* decode position does not follow the state */
+
+typedef struct still_params {
+  int32_t abi_version; /* STILL_ABI_VERSION */
+  int32_t dtype;       /* STILL_DTYPE_F32 or STILL_DTYPE_BF16 */
+  int32_t batch, n_q_heads, n_kv_heads, head_dim;
+  int32_t window; /* W: recent tokens always kept for softmax */
+  int32_t chunk;  /* C: routing decision granularity */
+  int32_t budget; /* m: softmax KV slots per kv head (window + kept) */
+  int32_t t_max;  /* T_max: chunks the m - W kept slots are spread over */
+  float eps;      /* score smoothing, > 0 (1e-6 if <= 0) */
+  float sm_scale; /* logit scale; <= 0 means 1/sqrt(head_dim) */
+  uint32_t flags; /* STILL_FLAG_* */
+} still_params;
+
+/* Byte offsets of one unit's (batch row, kv head) state inside the state
+ * blob; unit u = b * n_kv_heads + k starts at u * unit_bytes. */
+typedef struct still_state_layout {
+  int64_t unit_bytes;
+  int64_t S;        /* float32 [d][d], S[i][j] = sum phi(k)_i v_j     */
+  int64_t z;        /* float32 [d]                                     */
+  int64_t pool_k;   /* dtype [m-W][d], kept keys, ascending position   */
+  int64_t pool_v;   /* dtype [m-W][d]                                  */
+  int64_t pool_pos; /* int32 [m-W]                                     */
+  int64_t ring_k;   /* dtype [R][d], token at position p in slot p % R */
+  int64_t ring_v;   /* dtype [R][d]                                    */
+  int64_t ring_phi; /* dtype [R][d], NP-Map feature of ring_k          */
+  int64_t ring_flag;/* int32 [R], 1 = kept                             */
+  int64_t pending;  /* float64 [C], scores of the undecided chunk      */
+  int64_t meta;     /* int64 [4]: position, pool count, error, spare   */
+  int32_t ring_slots; /* R = W + 2C */
+  int32_t pool_slots; /* m - W */
+} still_state_layout;
+
+/* Kept tokens per decided chunk: min(C, floor((m - W) / T_max)).
+ * Returns >= 0, or STILL_EINVAL. No device work. */
+int still_lambda(const still_params* p);
+
+/* Fills *out with the state layout. No device work. */
+int still_state_layout_get(const still_params* p, still_state_layout* out);
+
+/* Bytes of the state blob (batch * n_kv_heads units), or < 0 on error. */
+int64_t still_state_bytes(const still_params* p);
+
+/* Bytes of scratch needed by still_prefill for seq_len tokens (or by
+ * still_decode_step when seq_len <= 0), or < 0 on error. */
+int64_t still_workspace_bytes(const still_params* p, int64_t seq_len);
+
+/* Prefill: runs the layer over seq_len >= 1 tokens (chunk-parallel form,
+ * [P3 "Delayed Chunk-Level Selection ..."]) and writes
+ *   out     [B, Hq, L, d]   outputs,
+ *   sel_idx int32 [B, Hkv, n_dec, lambda], n_dec = (L-1)/C: positions kept
+ *           from each decided chunk, ascending, -1 where the budget was full,
+ *   score   float32 [B, Hkv, L] or NULL: scores (float32 evaluation),
+ *   state   still_state_bytes(p) bytes: the decode state after token L-1.
+ * q, k, v, fmap_w ([Hkv, d, d], phi uses x @ fmap_w[k]) and gate are read
+ * only. workspace: ws_bytes >= still_workspace_bytes(p, seq_len), device
+ * memory, contents need not be initialised. */
+int still_prefill(const still_params* p, int64_t seq_len, const void* q, const void* k,
+                  const void* v, const void* fmap_w, const float* gate, void* out,
+                  int32_t* sel_idx, float* score, void* state, void* workspace,
+                  size_t ws_bytes, void* stream);
+
+/* Decode one token per sequence at position pos (the state must hold
+ * position pos, i.e. pos tokens already processed), [P3 "Delayed
+ * Chunk-Level Selection ..."]: the same routing and memory update as the
+ * prefill. q [B, Hq, d], k/v [B, Hkv, d]; out [B, Hq, d]; sel_new int32
+ * [B, Hkv, lambda] receives the positions kept from chunk pos/C - 1 when
+ * pos % C == 0 (and -1 otherwise or where the budget was full; may be NULL).
+ * The state is updated in place. A position mismatch found on the device
+ * sets the state's error word (meta[2] = STILL_ESTATE) and skips the step;
+ * a mismatch between pos and C-boundaries is not possible to detect earlier
+ * because the state lives on the device. workspace may be NULL when
+ * still_workspace_bytes(p, 0) is 0. */
+int still_decode_step(const still_params* p, int64_t pos, const void* q, const void* k,
+                      const void* v, const void* fmap_w, const float* gate, void* state,
+                      void* out, int32_t* sel_new, void* workspace, size_t ws_bytes,
+                      void* stream);
+
+/* Human-readable text of a status code (static storage). */
+const char* still_status_str(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* STILL_H */

@@ -1,0 +1,374 @@
+// Host side of libstill.so: argument validation, state / workspace layout and
+// the launch sequences of still_prefill and still_decode_step. Validation
+// makes no HIP call, so it runs (and is tested) without a GPU.
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include "still.h"
+#include "still_decode.hip"
+#include "still_prefill.hip"
+
+namespace {
+
+using still::bf16;
+
+constexpr int64_t kAlign = 256;
+inline int64_t align_up(int64_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+struct Derived {
+  int B, Hq, Hkv, G, D, W, C, m, t_max, lam, cap_chunks, R, P, esz;
+  float eps, scale;
+};
+
+int derive(const still_params* p, Derived* d) {
+  if (!p) return STILL_EINVAL;
+  if (p->abi_version != STILL_ABI_VERSION) return STILL_EINVAL;
+  if (p->dtype != STILL_DTYPE_F32 && p->dtype != STILL_DTYPE_BF16) return STILL_EINVAL;
+  if (p->batch < 1 || p->n_q_heads < 1 || p->n_kv_heads < 1) return STILL_EINVAL;
+  if (p->n_q_heads % p->n_kv_heads != 0) return STILL_EINVAL;
+  if (p->window < 1 || p->chunk < 1 || p->budget < p->window || p->t_max < 1) return STILL_EINVAL;
+  if (p->head_dim < 1) return STILL_EINVAL;
+  const int G = p->n_q_heads / p->n_kv_heads;
+  if (G != 1 && G != 2 && G != 4 && G != 8) return STILL_EUNSUPPORTED;
+  if (p->head_dim != 64 && p->head_dim != 128) return STILL_EUNSUPPORTED;
+  if (p->dtype == STILL_DTYPE_F32 && p->head_dim != 64) return STILL_EUNSUPPORTED;
+  if (p->chunk != 16 && p->chunk != 32 && p->chunk != 64 && p->chunk != 128)
+    return STILL_EUNSUPPORTED;
+  if (p->window > 256) return STILL_EUNSUPPORTED;
+  if ((int64_t)p->budget - p->window > (1 << 20)) return STILL_EUNSUPPORTED;
+  d->B = p->batch;
+  d->Hq = p->n_q_heads;
+  d->Hkv = p->n_kv_heads;
+  d->G = G;
+  d->D = p->head_dim;
+  d->W = p->window;
+  d->C = p->chunk;
+  d->m = p->budget;
+  d->t_max = p->t_max;
+  int lam = (p->budget - p->window) / p->t_max;
+  if (lam > p->chunk) lam = p->chunk;
+  d->lam = lam;
+  d->cap_chunks = lam > 0 ? (p->budget - p->window) / lam : 0;
+  d->R = p->window + 2 * p->chunk;
+  d->P = p->budget - p->window;
+  d->esz = p->dtype == STILL_DTYPE_F32 ? 4 : 2;
+  d->eps = p->eps > 0.f ? p->eps : 1e-6f;
+  d->scale = p->sm_scale > 0.f ? p->sm_scale : 1.0f / sqrtf((float)p->head_dim);
+  return STILL_OK;
+}
+
+void layout(const Derived& d, still_state_layout* s) {
+  int64_t o = 0;
+  auto take = [&](int64_t bytes) {
+    const int64_t at = o;
+    o = align_up(o + bytes);
+    return at;
+  };
+  s->S = take((int64_t)d.D * d.D * 4);
+  s->z = take((int64_t)d.D * 4);
+  s->pool_k = take((int64_t)d.P * d.D * d.esz);
+  s->pool_v = take((int64_t)d.P * d.D * d.esz);
+  s->pool_pos = take((int64_t)d.P * 4);
+  s->ring_k = take((int64_t)d.R * d.D * d.esz);
+  s->ring_v = take((int64_t)d.R * d.D * d.esz);
+  s->ring_phi = take((int64_t)d.R * d.D * d.esz);
+  s->ring_flag = take((int64_t)d.R * 4);
+  s->pending = take((int64_t)d.C * 8);
+  s->meta = take(4 * 8);
+  s->unit_bytes = o;
+  s->ring_slots = d.R;
+  s->pool_slots = d.P;
+}
+
+// Prefill launch geometry.
+struct Plan {
+  int L, T, n_dec, n_pend, K, NS, Gs, nHG, TPW;
+  int64_t ws_ft, ws_score, ws_delta, ws_flag, ws_dS, ws_total;
+};
+
+Plan plan(const Derived& d, int64_t L) {
+  Plan pl;
+  pl.L = (int)L;
+  pl.T = (int)((L + d.C - 1) / d.C);
+  pl.n_dec = (int)((L - 1) / d.C);
+  pl.n_pend = (int)(L - (int64_t)pl.n_dec * d.C);
+  int gs = 256 / d.C;
+  if (gs > d.G) gs = d.G;
+  pl.Gs = gs;
+  pl.nHG = d.G / gs;
+  const int rows16 = gs * d.C / 16;
+  pl.TPW = rows16 > 8 ? 2 : 1;
+  // chunks walked per workgroup: enough workgroups to fill the chip
+  const int64_t units = (int64_t)d.B * d.Hkv * pl.nHG;
+  int K = (int)((int64_t)pl.T * units / 1024);
+  if (K < 1) K = 1;
+  if (K > 8) K = 8;
+  if (const char* e = getenv("STILL_CHUNKS_PER_WG")) {
+    const int k = atoi(e);
+    if (k >= 1 && k <= 64) K = k;
+  }
+  if (K > pl.T) K = pl.T;
+  pl.K = K;
+  pl.NS = (pl.T + K - 1) / K;
+  int64_t o = 0;
+  auto take = [&](int64_t bytes) {
+    const int64_t at = o;
+    o = align_up(o + bytes);
+    return at;
+  };
+  const int64_t nu = (int64_t)d.B * d.Hkv;
+  pl.ws_ft = take((int64_t)d.Hkv * d.D * d.D * d.esz);
+  pl.ws_score = take(nu * L * 4);
+  pl.ws_delta = take(nu * L * 4);
+  pl.ws_flag = take(nu * L);
+  pl.ws_dS = take(nu * pl.NS * ((int64_t)d.D * d.D + d.D) * 4);
+  pl.ws_total = o;
+  return pl;
+}
+
+bool misaligned(const void* p) { return ((uintptr_t)p & 15u) != 0; }
+
+template <typename T, int D, int TPW>
+void set_lds_attr() {
+  static bool done = false;
+  if (done) return;
+  (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&still::attend_kernel<T, D, TPW>),
+                      hipFuncAttributeMaxDynamicSharedMemorySize,
+                      (int)still::Blk<T, D>::bytes);
+  (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&still::state_delta_kernel<T, D>),
+                      hipFuncAttributeMaxDynamicSharedMemorySize,
+                      (int)still::Blk<T, D>::bytes);
+  done = true;
+}
+
+template <typename T, int D>
+int launch_prefill(const Derived& d, const Plan& pl, still::PrefillArgs a, hipStream_t s) {
+  using namespace still;
+  const int nkt = d.C / 16 + (d.W + 14) / 16 + 1;
+  const size_t lds_score =
+      (size_t)nkt * 16 * (D + Pad<T>::v) * sizeof(T) + (size_t)(2 * d.G * d.C + 4) * 4;
+  const size_t lds_sel = (size_t)(d.G * d.W + 8 + d.C) * 8 + (size_t)(3 * d.C + 4) * 4;
+  fmap_transpose_kernel<T, D><<<dim3(d.Hkv), dim3(256), 0, s>>>(a);
+  score_kernel<T, D><<<dim3(pl.T, d.Hkv, d.B), dim3(256), lds_score, s>>>(a);
+  select_kernel<T, D><<<dim3(pl.n_dec + pl.n_pend, d.Hkv, d.B), dim3(256), lds_sel, s>>>(a);
+  if (pl.TPW == 2) set_lds_attr<T, D, 2>();
+  else set_lds_attr<T, D, 1>();
+  if (pl.NS > 1)
+    state_delta_kernel<T, D><<<dim3(pl.NS - 1, d.Hkv, d.B), dim3(512), Blk<T, D>::bytes, s>>>(a);
+  state_scan_kernel<<<dim3((D * D + D + 255) / 256, d.Hkv, d.B), dim3(256), 0, s>>>(
+      a.dS, pl.NS, D * D + D);
+  if (pl.TPW == 2)
+    attend_kernel<T, D, 2><<<dim3(pl.NS, d.Hkv * pl.nHG, d.B), dim3(512), Blk<T, D>::bytes, s>>>(a);
+  else
+    attend_kernel<T, D, 1><<<dim3(pl.NS, d.Hkv * pl.nHG, d.B), dim3(512), Blk<T, D>::bytes, s>>>(a);
+  const int ring_lo = pl.L - d.R > 0 ? pl.L - d.R : 0;
+  const int n_ring_grp = (pl.L - ring_lo + 15) / 16;
+  const int n_pool = pool_count_at(pl.n_dec, d.lam, d.cap_chunks);
+  export_kernel<T, D><<<dim3(n_ring_grp + (n_pool + 15) / 16, d.Hkv, d.B), dim3(256), 0, s>>>(a);
+  return hipGetLastError() == hipSuccess ? STILL_OK : STILL_EHIP;
+}
+
+template <typename T, int D>
+int launch_decode(const Derived& d, still::DecodeArgs a, hipStream_t s) {
+  using namespace still;
+  const size_t floats = (size_t)d.G * D * 2 + 16 * D * 4 + 32 + 8 + 32 + (size_t)d.G * D +
+                        2 * (size_t)d.G * D;
+  const size_t lds = floats * 4 + (size_t)(d.C + 8) * 4 + (size_t)(d.G * d.W + d.C + 8) * 8 +
+                     (size_t)d.G * a.n_keys_max * 4;
+  static bool attr = false;
+  if (!attr) {
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_kernel<T, D>),
+                        hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    attr = true;
+  }
+  decode_kernel<T, D><<<dim3(d.Hkv, d.B), dim3(256), lds, s>>>(a);
+  return hipGetLastError() == hipSuccess ? STILL_OK : STILL_EHIP;
+}
+
+void fill_state_offsets(const still_state_layout& L, long* unit, long* S, long* z, long* pk,
+                        long* pv, long* pp, long* rk, long* rv, long* rp, long* rf, long* pend,
+                        long* meta) {
+  *unit = L.unit_bytes;
+  *S = L.S;
+  *z = L.z;
+  *pk = L.pool_k;
+  *pv = L.pool_v;
+  *pp = L.pool_pos;
+  *rk = L.ring_k;
+  *rv = L.ring_v;
+  *rp = L.ring_phi;
+  *rf = L.ring_flag;
+  *pend = L.pending;
+  *meta = L.meta;
+}
+
+}  // namespace
+
+extern "C" {
+
+int still_lambda(const still_params* p) {
+  Derived d;
+  const int rc = derive(p, &d);
+  return rc == STILL_OK ? d.lam : rc;
+}
+
+int still_state_layout_get(const still_params* p, still_state_layout* out) {
+  Derived d;
+  const int rc = derive(p, &d);
+  if (rc != STILL_OK) return rc;
+  if (!out) return STILL_EINVAL;
+  layout(d, out);
+  return STILL_OK;
+}
+
+int64_t still_state_bytes(const still_params* p) {
+  Derived d;
+  const int rc = derive(p, &d);
+  if (rc != STILL_OK) return rc;
+  still_state_layout L;
+  layout(d, &L);
+  return L.unit_bytes * d.B * d.Hkv;
+}
+
+int64_t still_workspace_bytes(const still_params* p, int64_t seq_len) {
+  Derived d;
+  const int rc = derive(p, &d);
+  if (rc != STILL_OK) return rc;
+  if (seq_len <= 0) return 0;
+  if (seq_len > (int64_t)1 << 30) return STILL_EINVAL;
+  return plan(d, seq_len).ws_total;
+}
+
+int still_prefill(const still_params* p, int64_t seq_len, const void* q, const void* k,
+                  const void* v, const void* fmap_w, const float* gate, void* out,
+                  int32_t* sel_idx, float* score, void* state, void* workspace,
+                  size_t ws_bytes, void* stream) {
+  Derived d;
+  int rc = derive(p, &d);
+  if (rc != STILL_OK) return rc;
+  if (seq_len < 1 || seq_len > ((int64_t)1 << 30)) return STILL_EINVAL;
+  if ((int64_t)d.B * d.Hq * seq_len * d.D > ((int64_t)1 << 40)) return STILL_EINVAL;
+  if (!q || !k || !v || !fmap_w || !gate || !out || !state || !workspace) return STILL_EINVAL;
+  const int n_dec = (int)((seq_len - 1) / d.C);
+  if (!sel_idx && n_dec > 0 && d.lam > 0) return STILL_EINVAL;
+  if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(fmap_w) || misaligned(out) ||
+      misaligned(state) || misaligned(workspace) || misaligned(gate))
+    return STILL_EINVAL;
+  const Plan pl = plan(d, seq_len);
+  if ((int64_t)ws_bytes < pl.ws_total) return STILL_EWORKSPACE;
+  still_state_layout SL;
+  layout(d, &SL);
+
+  still::PrefillArgs a;
+  memset(&a, 0, sizeof(a));
+  char* ws = reinterpret_cast<char*>(workspace);
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.fmap_w = fmap_w;
+  a.gate = gate;
+  a.out = out;
+  a.sel = sel_idx;
+  a.score = score ? score : reinterpret_cast<float*>(ws + pl.ws_score);
+  a.delta = reinterpret_cast<float*>(ws + pl.ws_delta);
+  a.selflag = reinterpret_cast<uint8_t*>(ws + pl.ws_flag);
+  a.ft = ws + pl.ws_ft;
+  a.dS = reinterpret_cast<float*>(ws + pl.ws_dS);
+  a.state = reinterpret_cast<char*>(state);
+  a.B = d.B;
+  a.Hq = d.Hq;
+  a.Hkv = d.Hkv;
+  a.G = d.G;
+  a.L = pl.L;
+  a.W = d.W;
+  a.C = d.C;
+  a.m = d.m;
+  a.T = pl.T;
+  a.n_dec = pl.n_dec;
+  a.lam = d.lam;
+  a.cap_chunks = d.cap_chunks;
+  a.K = pl.K;
+  a.NS = pl.NS;
+  a.nHG = pl.nHG;
+  a.Gs = pl.Gs;
+  a.fp32_out = (p->flags & STILL_FLAG_FP32_OUT) ? 1 : 0;
+  a.scale = d.scale;
+  a.eps = d.eps;
+  a.R = d.R;
+  fill_state_offsets(SL, &a.st_unit, &a.st_S, &a.st_z, &a.st_pool_k, &a.st_pool_v,
+                     &a.st_pool_pos, &a.st_ring_k, &a.st_ring_v, &a.st_ring_phi,
+                     &a.st_ring_flag, &a.st_pending, &a.st_meta);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (p->dtype == STILL_DTYPE_BF16) {
+    if (d.D == 128) return launch_prefill<bf16, 128>(d, pl, a, s);
+    return launch_prefill<bf16, 64>(d, pl, a, s);
+  }
+  return launch_prefill<float, 64>(d, pl, a, s);
+}
+
+int still_decode_step(const still_params* p, int64_t pos, const void* q, const void* k,
+                      const void* v, const void* fmap_w, const float* gate, void* state,
+                      void* out, int32_t* sel_new, void* workspace, size_t ws_bytes,
+                      void* stream) {
+  (void)workspace;
+  (void)ws_bytes;
+  Derived d;
+  int rc = derive(p, &d);
+  if (rc != STILL_OK) return rc;
+  if (pos < 1 || pos > ((int64_t)1 << 30)) return STILL_EINVAL;
+  if (!q || !k || !v || !fmap_w || !gate || !state || !out) return STILL_EINVAL;
+  if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(fmap_w) || misaligned(out) ||
+      misaligned(state) || misaligned(gate))
+    return STILL_EINVAL;
+  still_state_layout SL;
+  layout(d, &SL);
+  still::DecodeArgs a;
+  memset(&a, 0, sizeof(a));
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.fmap_w = fmap_w;
+  a.gate = gate;
+  a.state = reinterpret_cast<char*>(state);
+  a.out = out;
+  a.sel_new = sel_new;
+  a.B = d.B;
+  a.Hq = d.Hq;
+  a.Hkv = d.Hkv;
+  a.G = d.G;
+  a.W = d.W;
+  a.C = d.C;
+  a.m = d.m;
+  a.lam = d.lam;
+  a.R = d.R;
+  a.t = (int)pos;
+  a.boundary = (pos % d.C) == 0 ? 1 : 0;
+  a.fp32_out = (p->flags & STILL_FLAG_FP32_OUT) ? 1 : 0;
+  a.n_keys_max = d.P + (d.W > d.C ? d.W : d.C) + d.W + d.C + 1;
+  a.scale = d.scale;
+  a.eps = d.eps;
+  fill_state_offsets(SL, &a.st_unit, &a.st_S, &a.st_z, &a.st_pool_k, &a.st_pool_v,
+                     &a.st_pool_pos, &a.st_ring_k, &a.st_ring_v, &a.st_ring_phi,
+                     &a.st_ring_flag, &a.st_pending, &a.st_meta);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (p->dtype == STILL_DTYPE_BF16) {
+    if (d.D == 128) return launch_decode<bf16, 128>(d, a, s);
+    return launch_decode<bf16, 64>(d, a, s);
+  }
+  return launch_decode<float, 64>(d, a, s);
+}
+
+const char* still_status_str(int status) {
+  switch (status) {
+    case STILL_OK: return "ok";
+    case STILL_EINVAL: return "invalid argument";
+    case STILL_EUNSUPPORTED: return "unsupported configuration";
+    case STILL_EWORKSPACE: return "workspace too small";
+    case STILL_EHIP: return "HIP launch failed";
+    case STILL_ESTATE: return "decode position does not match the state";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,208 @@
+// Shared device helpers for the STILL kernels (gfx950, wave64).
+//
+// Matrix products use 16x16 output tiles on the MFMA units:
+//   bf16: v_mfma_f32_16x16x32_bf16 (one instruction per 32-deep step)
+//   f32 : v_mfma_f32_16x16x4f32    (eight instructions per 32-deep step)
+// A "fragment" is what one lane contributes to one 16x16x32 step: 8 values.
+// With lane = 16*g + r (r = lane & 15, g = lane >> 4):
+//   A fragment (16 rows x 32 deep): row r, depth slots 8g .. 8g+7
+//   B fragment (32 deep x 16 cols): col r, depth slots 8g .. 8g+7
+//   accumulator (16 x 16, 4 floats): acc[i] = C[4g + i][r]
+// Depth slots only need to mean the same index in A and B. When a B (or A)
+// fragment is assembled from two accumulator tiles X0 (depth 0..15) and X1
+// (depth 16..31), lane (r, g) holds depths {4g+i} and {16+4g+i}: slot s maps
+// to depth perm(g, s) = s < 4 ? 4g + s : 16 + 4g + (s - 4). Operands paired
+// with such fragments are laid out in LDS with the same permutation.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace still {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+#define STILL_NEG_INF (-__builtin_huge_valf())
+
+template <typename T>
+struct Frag;
+template <>
+struct Frag<bf16> {
+  bf16x8 v;
+};
+template <>
+struct Frag<float> {
+  f32x4 lo, hi;
+};
+
+__device__ __forceinline__ void mma(f32x4& c, const Frag<bf16>& a, const Frag<bf16>& b) {
+  c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v, b.v, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ void mma(f32x4& c, const Frag<float>& a, const Frag<float>& b) {
+  c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.lo[0], b.lo[0], c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.lo[1], b.lo[1], c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.lo[2], b.lo[2], c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.lo[3], b.lo[3], c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.hi[0], b.hi[0], c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.hi[1], b.hi[1], c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.hi[2], b.hi[2], c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.hi[3], b.hi[3], c, 0, 0, 0);
+}
+
+// 8 consecutive elements (16-byte aligned for bf16, 32-byte for f32).
+__device__ __forceinline__ Frag<bf16> ld_frag(const bf16* p) {
+  Frag<bf16> f;
+  f.v = *reinterpret_cast<const bf16x8*>(p);
+  return f;
+}
+__device__ __forceinline__ Frag<float> ld_frag(const float* p) {
+  Frag<float> f;
+  f.lo = *reinterpret_cast<const f32x4*>(p);
+  f.hi = *reinterpret_cast<const f32x4*>(p + 4);
+  return f;
+}
+__device__ __forceinline__ void st_frag(bf16* p, const Frag<bf16>& f) {
+  *reinterpret_cast<bf16x8*>(p) = f.v;
+}
+__device__ __forceinline__ void st_frag(float* p, const Frag<float>& f) {
+  *reinterpret_cast<f32x4*>(p) = f.lo;
+  *reinterpret_cast<f32x4*>(p + 4) = f.hi;
+}
+
+template <typename T>
+__device__ __forceinline__ Frag<T> zero_frag();
+template <>
+__device__ __forceinline__ Frag<bf16> zero_frag<bf16>() {
+  Frag<bf16> f;
+  for (int i = 0; i < 8; ++i) f.v[i] = (bf16)0.0f;
+  return f;
+}
+template <>
+__device__ __forceinline__ Frag<float> zero_frag<float>() {
+  Frag<float> f;
+  f.lo = f32x4{0.f, 0.f, 0.f, 0.f};
+  f.hi = f.lo;
+  return f;
+}
+
+// Fragment from two accumulator tiles (slots 0..3 from x0, 4..7 from x1).
+template <typename T>
+__device__ __forceinline__ Frag<T> frag_from(const f32x4& x0, const f32x4& x1);
+template <>
+__device__ __forceinline__ Frag<bf16> frag_from<bf16>(const f32x4& x0, const f32x4& x1) {
+  Frag<bf16> f;
+  f.v[0] = (bf16)x0[0]; f.v[1] = (bf16)x0[1]; f.v[2] = (bf16)x0[2]; f.v[3] = (bf16)x0[3];
+  f.v[4] = (bf16)x1[0]; f.v[5] = (bf16)x1[1]; f.v[6] = (bf16)x1[2]; f.v[7] = (bf16)x1[3];
+  return f;
+}
+template <>
+__device__ __forceinline__ Frag<float> frag_from<float>(const f32x4& x0, const f32x4& x1) {
+  Frag<float> f;
+  f.lo = x0;
+  f.hi = x1;
+  return f;
+}
+
+// Split fp32 values into three bf16 parts (hi + mid + lo carries ~24
+// significant bits, the float32 value up to ~2^-27 relative); for f32 the
+// "high" part is the value and the others are zero.
+template <typename T>
+__device__ __forceinline__ void split3_frag(const f32x4& x0, const f32x4& x1, Frag<T>& hi,
+                                            Frag<T>& mid, Frag<T>& lo);
+template <>
+__device__ __forceinline__ void split3_frag<bf16>(const f32x4& x0, const f32x4& x1,
+                                                  Frag<bf16>& hi, Frag<bf16>& mid,
+                                                  Frag<bf16>& lo) {
+  for (int i = 0; i < 8; ++i) {
+    const float x = i < 4 ? x0[i] : x1[i - 4];
+    const bf16 a = (bf16)x;
+    const float r1 = x - (float)a;
+    const bf16 b = (bf16)r1;
+    hi.v[i] = a;
+    mid.v[i] = b;
+    lo.v[i] = (bf16)(r1 - (float)b);
+  }
+}
+template <>
+__device__ __forceinline__ void split3_frag<float>(const f32x4& x0, const f32x4& x1,
+                                                   Frag<float>& hi, Frag<float>& mid,
+                                                   Frag<float>& lo) {
+  hi.lo = x0;
+  hi.hi = x1;
+  mid = zero_frag<float>();
+  lo = mid;
+}
+
+template <typename T>
+__device__ __forceinline__ float frag_sumsq(const Frag<T>& f);
+template <>
+__device__ __forceinline__ float frag_sumsq<bf16>(const Frag<bf16>& f) {
+  float s = 0.f;
+  for (int i = 0; i < 8; ++i) {
+    const float x = (float)f.v[i];
+    s += x * x;
+  }
+  return s;
+}
+template <>
+__device__ __forceinline__ float frag_sumsq<float>(const Frag<float>& f) {
+  float s = 0.f;
+  for (int i = 0; i < 4; ++i) s += f.lo[i] * f.lo[i] + f.hi[i] * f.hi[i];
+  return s;
+}
+
+__device__ __forceinline__ float frag_sum(const Frag<bf16>& f) {
+  float s = 0.f;
+  for (int i = 0; i < 8; ++i) s += (float)f.v[i];
+  return s;
+}
+__device__ __forceinline__ float frag_sum(const Frag<float>& f) {
+  return (f.lo[0] + f.lo[1]) + (f.lo[2] + f.lo[3]) + (f.hi[0] + f.hi[1]) + (f.hi[2] + f.hi[3]);
+}
+
+__device__ __forceinline__ float to_f32(bf16 x) { return (float)x; }
+__device__ __forceinline__ float to_f32(float x) { return x; }
+template <typename T>
+__device__ __forceinline__ T from_f32(float x);
+template <>
+__device__ __forceinline__ bf16 from_f32<bf16>(float x) { return (bf16)x; }
+template <>
+__device__ __forceinline__ float from_f32<float>(float x) { return x; }
+
+// Sum / max over the four lanes sharing r (lanes r, r+16, r+32, r+48).
+__device__ __forceinline__ float sum_over_g(float x) {
+  x += __shfl_xor(x, 16);
+  x += __shfl_xor(x, 32);
+  return x;
+}
+__device__ __forceinline__ float max_over_g(float x) {
+  x = fmaxf(x, __shfl_xor(x, 16));
+  x = fmaxf(x, __shfl_xor(x, 32));
+  return x;
+}
+
+// Position of key kk (0..63) of a 64-key block in a permuted LDS row, so that
+// a 16-byte read at column 32*(kk/32) + 8g yields depth slots perm(g, 0..7).
+__device__ __forceinline__ int perm_col(int kk) {
+  const int k32 = kk & 31;
+  return (kk & 32) + 8 * ((k32 & 15) >> 2) + ((k32 >> 4) << 2) + (k32 & 3);
+}
+
+// Chunks lying wholly at or before position cC - W, i.e. before the window
+// of every query of chunk c.
+__device__ __host__ __forceinline__ int full_chunks_before(int c, int W, int C) {
+  const long x = (long)c * C - W + 1;
+  return x >= 0 ? (int)(x / C) : 0;
+}
+
+// Kept-pool size when chunk c starts: lambda per decided chunk until the
+// budget of m - W slots is full.
+__device__ __host__ __forceinline__ int pool_count_at(int c, int lam, int cap_chunks) {
+  if (lam <= 0) return 0;
+  return (c < cap_chunks ? c : cap_chunks) * lam;
+}
+
+}  // namespace still

@@ -1,0 +1,935 @@
+// Prefill kernels of one STILL layer (chunk-parallel form) for gfx950.
+//
+// Pages cited (short tag -> page title):
+//   [P2] "NeurIPS 2026|层内混合注意力：告别位置「伪混合」，STILL首个内容感知的层内混合注意力架构",
+//        sections 亮点一 (固定预算路由, 延迟选择与分块并行), 亮点二
+//   [P3] "STILL: Content-Aware Intra-Layer Hybrid Attention for Efficient
+//        LLM Linearization", sections "Content-Aware Routing with Fixed
+//        Budget", "Delayed Chunk-Level Selection for Unified
+//        Training-Inference Parallelism", "Self-Saliency Score",
+//        "NP-Map: Norm-Preserving Feature Map"
+//
+// Launch sequence on one stream (host side in still_api.hip):
+//   1. fmap_transpose   F^T copy so MFMA fragments of F^T are 16-byte reads
+//   2. score            windowed Self-Saliency Score, float32, + error bound
+//   3. select           per decided chunk: Top-lambda, float64 refinement of
+//                       candidates the float32 bound cannot separate; float64
+//                       scores of the undecided chunk (decode state)
+//   4. state_delta      per super-chunk: sum of phi(k) v^T over the chunks it
+//                       folds into the linear state
+//   5. state_scan       exclusive prefix over super-chunks (in place)
+//   6. attend           per super-chunk, chunk by chunk: softmax over window
+//                       + own chunk + kept pool, NP-Map linear attention over
+//                       the state and the not-yet-folded band, one softmax-
+//                       style normaliser over both, then fold the next chunk
+//   7. export           decode state: kept pool, recent-token ring, position
+#include "still_common.h"
+
+namespace still {
+
+struct PrefillArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* fmap_w;
+  const float* gate;
+  void* out;
+  int32_t* sel;      // [B][Hkv][n_dec][lam]
+  float* score;      // [B][Hkv][L]
+  float* delta;      // [B][Hkv][L]  float32 score error bound
+  uint8_t* selflag;  // [B][Hkv][L]
+  void* ft;          // [Hkv][D][D] F^T in T
+  float* dS;         // [B][Hkv][NS][D*D + D]
+  char* state;
+  int B, Hq, Hkv, G, L, W, C, m, T, n_dec, lam, cap_chunks, K, NS, nHG, Gs, fp32_out;
+  float scale, eps;
+  long st_unit, st_S, st_z, st_pool_k, st_pool_v, st_pool_pos, st_ring_k, st_ring_v,
+      st_ring_phi, st_ring_flag, st_pending, st_meta;
+  int R;
+};
+
+template <typename T>
+struct Pad {
+  static constexpr int v = 16 / sizeof(T);  // one 16-byte vector of padding
+};
+
+// ------------------------------------------------------------ 1. F^T ----
+template <typename T, int D>
+__global__ __launch_bounds__(256) void fmap_transpose_kernel(PrefillArgs a) {
+  const T* F = reinterpret_cast<const T*>(a.fmap_w) + (size_t)blockIdx.x * D * D;
+  T* Ft = reinterpret_cast<T*>(a.ft) + (size_t)blockIdx.x * D * D;
+  for (int e = threadIdx.x; e < D * D; e += 256) {
+    const int i = e / D, j = e % D;
+    Ft[(size_t)j * D + i] = F[e];
+  }
+}
+
+// ----------------------------------------------------------- 2. score ----
+// One workgroup per (chunk, kv head, batch row), 4 waves. Keys of the
+// chunk's windows [cC-W+1, cC+C-1] are staged in LDS; each wave takes
+// 16-query tiles of one head, computes window logits with MFMA, keeps an
+// online max / total / non-self total and the self logit, and turns them
+// into the two-point KL form of the score [P3 "Self-Saliency Score"]
+// (reading: KL(a_diag || (1-eps) a_nodiag + eps delta_t)). The group's heads
+// are summed through LDS and the float32 score is written with a bound on
+// its float32 evaluation error.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void score_kernel(PrefillArgs a) {
+  extern __shared__ __align__(16) char smem[];
+  const int c = blockIdx.x, kv = blockIdx.y, b = blockIdx.z;
+  const int L = a.L, C = a.C, W = a.W, G = a.G;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int r16 = lane & 15, g4 = lane >> 4;
+  constexpr int KS = D + Pad<T>::v;
+  const int cC = c * C;
+  const int kbase = cC - W + 1;
+  const int nkt = C / 16 + (W + 14) / 16 + 1;
+  T* Ks = reinterpret_cast<T*>(smem);
+  float* part = reinterpret_cast<float*>(smem + (size_t)nkt * 16 * KS * sizeof(T));
+  float* pdel = part + G * C;
+  float* kmax = pdel + G * C;
+
+  const T* kg = reinterpret_cast<const T*>(a.k) + (size_t)(b * a.Hkv + kv) * L * D;
+  constexpr int VEC = 16 / sizeof(T);
+  const int nvec = nkt * 16 * (D / VEC);
+  if (tid == 0) kmax[0] = 0.f;
+  for (int idx = tid; idx < nvec; idx += 256) {
+    const int row = idx / (D / VEC), col = (idx % (D / VEC)) * VEC;
+    const int j = kbase + row;
+    uint4 val = {0, 0, 0, 0};
+    if (j >= 0 && j < L && j < cC + C) val = *reinterpret_cast<const uint4*>(kg + (size_t)j * D + col);
+    *reinterpret_cast<uint4*>(Ks + row * KS + col) = val;
+  }
+  __syncthreads();
+  for (int row = tid; row < nkt * 16; row += 256) {
+    float s = 0.f;
+    for (int i = 0; i < D; ++i) {
+      const float x = to_f32(Ks[row * KS + i]);
+      s += x * x;
+    }
+    atomicMax(reinterpret_cast<int*>(kmax), __float_as_int(s));  // s >= 0
+  }
+  __syncthreads();
+  const float kn_max = sqrtf(kmax[0]);
+
+  const int n_qt = C / 16;
+  const int n_rt = G * n_qt;
+  for (int rt = wave; rt < n_rt; rt += 4) {
+    const int hl = rt / n_qt, qt = rt % n_qt;
+    const int h = kv * G + hl;
+    const int t = cC + 16 * qt + r16;
+    const T* qg = reinterpret_cast<const T*>(a.q) + ((size_t)(b * a.Hq + h) * L) * D;
+    Frag<T> qf[D / 32];
+    float qn2 = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < D / 32; ++kb) {
+      qf[kb] = (t < L) ? ld_frag(qg + (size_t)t * D + 32 * kb + 8 * g4) : zero_frag<T>();
+      qn2 += frag_sumsq(qf[kb]);
+    }
+    qn2 = sum_over_g(qn2);
+    float mrun = STILL_NEG_INF, zall = 0.f, zoth = 0.f, sself = STILL_NEG_INF;
+    const int kt_lo = qt, kt_hi = qt + (W + 14) / 16;
+    for (int kt = kt_lo; kt <= kt_hi; ++kt) {
+      f32x4 s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb = 0; kb < D / 32; ++kb)
+        mma(s, ld_frag(Ks + (16 * kt + r16) * KS + 32 * kb + 8 * g4), qf[kb]);
+      float lv[4];
+      float mx = STILL_NEG_INF;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int j = kbase + 16 * kt + 4 * g4 + i;
+        const bool ok = j >= 0 && j <= t && j >= t - W + 1;
+        lv[i] = ok ? s[i] * a.scale : STILL_NEG_INF;
+        if (ok && j == t) sself = lv[i];
+        mx = fmaxf(mx, lv[i]);
+      }
+      const float mn = fmaxf(mrun, mx);
+      if (mn != STILL_NEG_INF) {
+        const float al = (mrun == STILL_NEG_INF) ? 0.f : __expf(mrun - mn);
+        zall *= al;
+        zoth *= al;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if (lv[i] == STILL_NEG_INF) continue;
+          const float e = __expf(lv[i] - mn);
+          zall += e;
+          const int j = kbase + 16 * kt + 4 * g4 + i;
+          if (j != t) zoth += e;
+        }
+        mrun = mn;
+      }
+    }
+#pragma unroll
+    for (int off = 16; off <= 32; off <<= 1) {
+      const float m2 = __shfl_xor(mrun, off), za2 = __shfl_xor(zall, off),
+                  zo2 = __shfl_xor(zoth, off), ss2 = __shfl_xor(sself, off);
+      const float mn = fmaxf(mrun, m2);
+      if (mn != STILL_NEG_INF) {
+        const float f1 = (mrun == STILL_NEG_INF) ? 0.f : __expf(mrun - mn);
+        const float f2 = (m2 == STILL_NEG_INF) ? 0.f : __expf(m2 - mn);
+        zall = zall * f1 + za2 * f2;
+        zoth = zoth * f1 + zo2 * f2;
+      }
+      mrun = mn;
+      sself = fmaxf(sself, ss2);
+    }
+    float sc = 0.f, dl = 0.f;
+    if (t < L) {
+      const float p = __expf(sself - mrun) / zall;
+      const float pn = zoth / zall;
+      const float lp = p > 0.f ? logf(p / a.eps) : 0.f;
+      const float lpn = pn > 0.f ? logf(pn / (1.f - a.eps)) : 0.f;
+      sc = (p > 0.f ? p * lp : 0.f) + (pn > 0.f ? pn * lpn : 0.f);
+      // Bound on the float32 evaluation error of this head's score: logit
+      // error <= 4e-6 * scale * |q| * max|k| (a wide margin over the MFMA
+      // accumulation error), propagated through d score / d p, plus
+      // rounding of exp/log at a few float32 ulps.
+      const float ds = 4e-6f * a.scale * sqrtf(qn2) * kn_max + 1e-6f * fabsf(mrun);
+      const float dp = 2.f * p * pn * ds + 2e-6f * p;
+      dl = 4.f * (fabsf(lp - lpn) * dp + 2e-6f * (fabsf(sc) + 1.f));
+    }
+    if (g4 == 0) {
+      part[hl * C + 16 * qt + r16] = sc;
+      pdel[hl * C + 16 * qt + r16] = dl;
+    }
+  }
+  __syncthreads();
+  for (int qi = tid; qi < C; qi += 256) {
+    const int t = cC + qi;
+    if (t >= L) continue;
+    float s = 0.f, d = 0.f;
+    for (int hl = 0; hl < G; ++hl) {
+      s += part[hl * C + qi];
+      d += pdel[hl * C + qi];
+    }
+    const size_t o = (size_t)(b * a.Hkv + kv) * L + t;
+    a.score[o] = s;
+    a.delta[o] = d;
+  }
+}
+
+// ---------------------------------------------------------- 3. select ----
+// Score of token t in float64 [P3 "Self-Saliency Score"], cooperatively by
+// the 256 threads of a workgroup: logits over the window of each of the
+// group's heads (bf16 / f32 products are exact in float64), then per head the
+// two-point KL form with 1-p summed from the other entries.
+template <typename T, int D>
+__device__ __forceinline__ double score_f64(const PrefillArgs& a, int b, int kv, int t, double* lg,
+                            double* red) {
+  const int tid = threadIdx.x;
+  const int W = a.W, G = a.G, L = a.L;
+  const int lo = t - W + 1 > 0 ? t - W + 1 : 0;
+  const int n = t - lo + 1;
+  const T* kg = reinterpret_cast<const T*>(a.k) + (size_t)(b * a.Hkv + kv) * L * D;
+  for (int p = tid; p < G * n; p += 256) {
+    const int hl = p / n, jj = p % n;
+    const T* qr = reinterpret_cast<const T*>(a.q) +
+                  ((size_t)(b * a.Hq + kv * G + hl) * L + t) * D;
+    const T* kr = kg + (size_t)(lo + jj) * D;
+    double s = 0.0;
+    for (int i = 0; i < D; ++i) s += (double)to_f32(qr[i]) * (double)to_f32(kr[i]);
+    lg[hl * W + jj] = (double)a.scale * s;
+  }
+  __syncthreads();
+  if (tid < G) {
+    const double* x = lg + tid * W;
+    double mx = x[0];
+    for (int j = 1; j < n; ++j) mx = x[j] > mx ? x[j] : mx;
+    double za = 0.0, zo = 0.0;
+    for (int j = 0; j < n; ++j) {
+      const double e = exp(x[j] - mx);
+      za += e;
+      if (j != n - 1) zo += e;
+    }
+    const double p = exp(x[n - 1] - mx) / za, pn = zo / za;
+    double sc = 0.0;
+    if (p > 0.0) sc += p * log(p / (double)a.eps);
+    if (pn > 0.0) sc += pn * log(pn / (1.0 - (double)a.eps));
+    red[tid] = sc;
+  }
+  __syncthreads();
+  double tot = 0.0;
+  for (int h = 0; h < G; ++h) tot += red[h];
+  __syncthreads();
+  return tot;
+}
+
+// Workgroup x < n_dec decides chunk x [P3 "Delayed Chunk-Level Selection"]:
+// keep lambda_c = lambda tokens while the pool of m - W slots has room
+// [P2 固定预算路由], ranked by (score desc, position asc). The float32 scores
+// with their error bounds give, for every token, an interval; tokens whose
+// upper end is below the lambda-th largest lower end cannot be kept. If more
+// than lambda tokens remain, their scores are recomputed in float64 and the
+// ranking is made on those. Workgroups x >= n_dec compute the float64 score
+// of one token of the undecided last chunk into the decode state.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void select_kernel(PrefillArgs a) {
+  extern __shared__ __align__(16) char smem[];
+  double* lg = reinterpret_cast<double*>(smem);     // [G * W]
+  double* red = lg + (size_t)a.G * a.W;             // [8]
+  double* s64 = red + 8;                            // [C]
+  float* lb = reinterpret_cast<float*>(s64 + a.C);  // [C]
+  float* ub = lb + a.C;                             // [C]
+  int* flag = reinterpret_cast<int*>(ub + a.C);     // [C] candidate / kept
+  int* misc = flag + a.C;                           // [4]
+  const int x = blockIdx.x, kv = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, C = a.C, L = a.L, lam = a.lam;
+  const size_t ub_off = (size_t)(b * a.Hkv + kv) * L;
+
+  if (x >= a.n_dec) {
+    const int c_last = (L - 1) / C;
+    const int j = x - a.n_dec, t = c_last * C + j;
+    double* pend = reinterpret_cast<double*>(a.state + (size_t)(b * a.Hkv + kv) * a.st_unit +
+                                             a.st_pending);
+    const double s = score_f64<T, D>(a, b, kv, t, lg, red);
+    if (tid == 0) {
+      pend[j] = s;
+      a.selflag[ub_off + t] = 0;
+      if (j == 0)
+        for (int i = L - c_last * C; i < C; ++i) pend[i] = __builtin_nan("");
+    }
+    return;
+  }
+
+  const int c = x, base = c * C;
+  const int lam_c = ((c + 1) * lam <= a.m - a.W) ? lam : 0;
+  int32_t* selrow = a.sel + ((size_t)(b * a.Hkv + kv) * a.n_dec + c) * lam;
+  if (lam_c == 0 || lam_c == C) {
+    for (int j = tid; j < C; j += 256) a.selflag[ub_off + base + j] = lam_c == C ? 1 : 0;
+    for (int i = tid; i < lam; i += 256) selrow[i] = lam_c == C ? base + i : -1;
+    return;
+  }
+  for (int j = tid; j < C; j += 256) {
+    const float s = a.score[ub_off + base + j], d = a.delta[ub_off + base + j];
+    lb[j] = s - d;
+    ub[j] = s + d;
+  }
+  if (tid == 0) misc[1] = 0;
+  __syncthreads();
+  // lambda-th largest lower bound (rank by (lb desc, index asc))
+  for (int j = tid; j < C; j += 256) {
+    int r = 0;
+    for (int i = 0; i < C; ++i) r += (lb[i] > lb[j] || (lb[i] == lb[j] && i < j)) ? 1 : 0;
+    if (r == lam_c - 1) misc[0] = __float_as_int(lb[j]);
+  }
+  __syncthreads();
+  const float LB = __int_as_float(misc[0]);
+  for (int j = tid; j < C; j += 256) {
+    flag[j] = ub[j] >= LB ? 1 : 0;
+    if (flag[j]) atomicAdd(&misc[1], 1);
+  }
+  __syncthreads();
+  const int n_cand = misc[1];
+  if (n_cand > lam_c) {
+    for (int j = 0; j < C; ++j) {
+      if (!flag[j]) continue;  // uniform: flag is in LDS
+      const double s = score_f64<T, D>(a, b, kv, base + j, lg, red);
+      if (tid == 0) s64[j] = s;
+      __syncthreads();
+    }
+    for (int j = tid; j < C; j += 256) {
+      int r = 0;
+      if (flag[j])
+        for (int i = 0; i < C; ++i)
+          r += (flag[i] && (s64[i] > s64[j] || (s64[i] == s64[j] && i < j))) ? 1 : 0;
+      lb[j] = (flag[j] && r < lam_c) ? 1.f : 0.f;
+    }
+  } else {
+    for (int j = tid; j < C; j += 256) lb[j] = flag[j] ? 1.f : 0.f;
+  }
+  __syncthreads();
+  for (int j = tid; j < C; j += 256) {
+    const bool kept = lb[j] != 0.f;
+    a.selflag[ub_off + base + j] = kept ? 1 : 0;
+    if (kept) {
+      int k = 0;
+      for (int i = 0; i < j; ++i) k += lb[i] != 0.f ? 1 : 0;
+      selrow[k] = base + j;
+    }
+  }
+}
+
+// ----------------------------------------- shared block machinery (4-6) ----
+// A workgroup of 8 waves streams 64-key blocks through LDS:
+//   Ks   [64][D+pad]      keys, row-major (A fragments of K, B of K^T)
+//   VTs  [D][64+pad]      values transposed, keys permuted (perm_col)
+//   phiK [64][D+4] f32    NP-Map features of the block's keys
+// The linear state S (d_k x d_v, float32) lives in the accumulators of the
+// waves: pair p = (d_v tile vt, d_k 32-block bb) holds tiles (2bb, vt) and
+// (2bb+1, vt).
+template <typename T, int D>
+struct Blk {
+  static constexpr int KS = D + Pad<T>::v;
+  static constexpr int VS = 64 + Pad<T>::v;
+  static constexpr int PS = D + 4;
+  static constexpr int NPAIR = (D / 16) * (D / 32);
+  static constexpr int PPW = NPAIR / 8;
+  static constexpr size_t ks_bytes = 64 * KS * sizeof(T);
+  static constexpr size_t vs_bytes = D * VS * sizeof(T);
+  static constexpr size_t ps_bytes = 64 * PS * sizeof(float);
+  static constexpr size_t stf_bytes = (size_t)(D / 16) * (D / 32) * 64 * 8 * sizeof(T);
+  static constexpr size_t meta_bytes = 64 * 3 * 4 + D * 4;
+  static constexpr size_t bytes = ks_bytes + vs_bytes + ps_bytes + stf_bytes + meta_bytes;
+};
+
+template <typename T, int D>
+struct BlkPtr {
+  T* Ks;
+  T* VTs;
+  float* phiK;
+  T* STF;
+  int* kpos;
+  int* ksel;
+  float* fmask;
+  float* zs;
+  __device__ BlkPtr(char* smem) {
+    using B_ = Blk<T, D>;
+    Ks = reinterpret_cast<T*>(smem);
+    VTs = reinterpret_cast<T*>(smem + B_::ks_bytes);
+    phiK = reinterpret_cast<float*>(smem + B_::ks_bytes + B_::vs_bytes);
+    STF = reinterpret_cast<T*>(smem + B_::ks_bytes + B_::vs_bytes + B_::ps_bytes);
+    char* m = smem + B_::ks_bytes + B_::vs_bytes + B_::ps_bytes + B_::stf_bytes;
+    kpos = reinterpret_cast<int*>(m);
+    ksel = kpos + 64;
+    fmask = reinterpret_cast<float*>(ksel + 64);
+    zs = fmask + 64;
+  }
+};
+
+// Loads 64 keys/values at the given positions (pos < 0: zero row) into Ks and
+// VTs, with their positions and kept flags. All 512 threads take part.
+template <typename T, int D>
+__device__ __forceinline__ void load_block(const PrefillArgs& a, const BlkPtr<T, D>& P, const T* kg,
+                           const T* vg, const uint8_t* sf, const int32_t* gather, int n_gather,
+                           int range_lo, int range_hi, int fold_lo, int fold_hi) {
+  using B_ = Blk<T, D>;
+  const int tid = threadIdx.x;
+  constexpr int VEC = 16 / sizeof(T);
+  if (tid < 64) {
+    int j;
+    if (gather) j = tid < n_gather ? gather[tid] : -1;
+    else j = range_lo + tid < range_hi ? range_lo + tid : -1;
+    const int s = j >= 0 ? (gather ? 1 : (int)sf[j]) : 0;
+    P.kpos[tid] = j;
+    P.ksel[tid] = s;
+    P.fmask[tid] = (j >= fold_lo && j < fold_hi && !s) ? 1.f : 0.f;
+  }
+  for (int idx = tid; idx < 64 * (D / VEC); idx += 512) {
+    const int kk = idx / (D / VEC), col = (idx % (D / VEC)) * VEC;
+    int j;
+    if (gather) j = kk < n_gather ? gather[kk] : -1;
+    else j = range_lo + kk < range_hi ? range_lo + kk : -1;
+    uint4 kvv = {0, 0, 0, 0}, vvv = {0, 0, 0, 0};
+    if (j >= 0) {
+      kvv = *reinterpret_cast<const uint4*>(kg + (size_t)j * D + col);
+      vvv = *reinterpret_cast<const uint4*>(vg + (size_t)j * D + col);
+    }
+    *reinterpret_cast<uint4*>(P.Ks + kk * B_::KS + col) = kvv;
+    const T* ve = reinterpret_cast<const T*>(&vvv);
+    const int pc = perm_col(kk);
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) P.VTs[(col + e) * B_::VS + pc] = ve[e];
+  }
+}
+
+// NP-Map [P3 "NP-Map: Norm-Preserving Feature Map"], reading: direction =
+// softmax(x F) scaled to unit L2 norm, magnitude = ||x||. Computes, for one
+// 16-row tile whose B fragments of X^T are xf[], the feature values in the
+// accumulator layout of (X F)^T: out[ft][i] = phi(x_r)[16 ft + 4g + i].
+template <typename T, int D>
+__device__ __forceinline__ void np_map_tile(const T* ftg, const Frag<T>* xf, f32x4* out) {
+  const int lane = threadIdx.x & 63, r16 = lane & 15, g4 = lane >> 4;
+  float xn2 = 0.f;
+#pragma unroll
+  for (int kb = 0; kb < D / 32; ++kb) xn2 += frag_sumsq(xf[kb]);
+  xn2 = sum_over_g(xn2);
+  float mx = STILL_NEG_INF;
+#pragma unroll
+  for (int ft = 0; ft < D / 16; ++ft) {
+    out[ft] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < D / 32; ++kb)
+      mma(out[ft], ld_frag(ftg + (size_t)(16 * ft + r16) * D + 32 * kb + 8 * g4), xf[kb]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) mx = fmaxf(mx, out[ft][i]);
+  }
+  mx = max_over_g(mx);
+  float ss = 0.f;
+#pragma unroll
+  for (int ft = 0; ft < D / 16; ++ft)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float e = __expf(out[ft][i] - mx);
+      out[ft][i] = e;
+      ss += e * e;
+    }
+  ss = sum_over_g(ss);
+  const float f = sqrtf(xn2) / sqrtf(ss);
+#pragma unroll
+  for (int ft = 0; ft < D / 16; ++ft) out[ft] *= f;
+}
+
+// phi(K) of the block's 64 keys into phiK; waves 0..3 take one 16-key tile.
+template <typename T, int D>
+__device__ __forceinline__ void block_phi(const BlkPtr<T, D>& P, const T* ftg) {
+  using B_ = Blk<T, D>;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, r16 = lane & 15, g4 = lane >> 4;
+  if (wave >= 4) return;
+  Frag<T> kf[D / 32];
+#pragma unroll
+  for (int kb = 0; kb < D / 32; ++kb) kf[kb] = ld_frag(P.Ks + (16 * wave + r16) * B_::KS + 32 * kb + 8 * g4);
+  f32x4 ph[D / 16];
+  np_map_tile<T, D>(ftg, kf, ph);
+#pragma unroll
+  for (int ft = 0; ft < D / 16; ++ft)
+    *reinterpret_cast<f32x4*>(P.phiK + (16 * wave + r16) * B_::PS + 16 * ft + 4 * g4) = ph[ft];
+}
+
+// S += phi(K)^T diag(fmask) V over the block (fold into the linear state),
+// with phi split into three bf16 parts so the products keep float32
+// accuracy (values are exact in bf16); z += sum of the same features.
+template <typename T, int D>
+__device__ __forceinline__ void block_fold(const BlkPtr<T, D>& P, f32x4 (*Sacc)[2]) {
+  using B_ = Blk<T, D>;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, r16 = lane & 15, g4 = lane >> 4;
+#pragma unroll
+  for (int pp = 0; pp < B_::PPW; ++pp) {
+    const int p = wave * B_::PPW + pp;
+    const int vt = p / (D / 32), bb = p % (D / 32);
+#pragma unroll
+    for (int kb2 = 0; kb2 < 2; ++kb2) {
+      const Frag<T> bv = ld_frag(P.VTs + (16 * vt + r16) * B_::VS + 32 * kb2 + 8 * g4);
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int f = 16 * (2 * bb + e) + r16;
+        f32x4 x0, x1;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const int k0 = 32 * kb2 + 4 * g4 + s, k1 = k0 + 16;
+          x0[s] = P.fmask[k0] * P.phiK[k0 * B_::PS + f];
+          x1[s] = P.fmask[k1] * P.phiK[k1 * B_::PS + f];
+        }
+        Frag<T> hi, mid, lo;
+        split3_frag<T>(x0, x1, hi, mid, lo);
+        mma(Sacc[pp][e], hi, bv);
+        if constexpr (sizeof(T) == 2) {
+          mma(Sacc[pp][e], mid, bv);
+          mma(Sacc[pp][e], lo, bv);
+        }
+      }
+    }
+  }
+  const int tid = threadIdx.x;
+  if (tid < D) {
+    float zsum = 0.f;
+    for (int kk = 0; kk < 64; ++kk) zsum += P.fmask[kk] * P.phiK[kk * B_::PS + tid];
+    P.zs[tid] += zsum;
+  }
+}
+
+// S^T fragments (A operand of the readout S^T phi(Q)^T) from the state
+// accumulators into LDS: STF[vt][bb][lane].
+template <typename T, int D>
+__device__ __forceinline__ void write_stf(const BlkPtr<T, D>& P, f32x4 (*Sacc)[2]) {
+  using B_ = Blk<T, D>;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+#pragma unroll
+  for (int pp = 0; pp < B_::PPW; ++pp) {
+    const int p = wave * B_::PPW + pp;
+    const int vt = p / (D / 32), bb = p % (D / 32);
+    st_frag(P.STF + ((size_t)(vt * (D / 32) + bb) * 64 + lane) * 8, frag_from<T>(Sacc[pp][0], Sacc[pp][1]));
+  }
+}
+
+template <typename T, int D>
+__device__ __forceinline__ void load_state_acc(const float* S, f32x4 (*Sacc)[2]) {
+  using B_ = Blk<T, D>;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, r16 = lane & 15, g4 = lane >> 4;
+#pragma unroll
+  for (int pp = 0; pp < B_::PPW; ++pp) {
+    const int p = wave * B_::PPW + pp;
+    const int vt = p / (D / 32), bb = p % (D / 32);
+#pragma unroll
+    for (int e = 0; e < 2; ++e)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        Sacc[pp][e][i] = S[(size_t)(16 * (2 * bb + e) + 4 * g4 + i) * D + 16 * vt + r16];
+  }
+}
+
+template <typename T, int D>
+__device__ __forceinline__ void store_state_acc(float* S, f32x4 (*Sacc)[2]) {
+  using B_ = Blk<T, D>;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, r16 = lane & 15, g4 = lane >> 4;
+#pragma unroll
+  for (int pp = 0; pp < B_::PPW; ++pp) {
+    const int p = wave * B_::PPW + pp;
+    const int vt = p / (D / 32), bb = p % (D / 32);
+#pragma unroll
+    for (int e = 0; e < 2; ++e)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        S[(size_t)(16 * (2 * bb + e) + 4 * g4 + i) * D + 16 * vt + r16] = Sacc[pp][e][i];
+  }
+}
+
+// ---------------------------------------------------- 4. state_delta ----
+// Super-chunk s folds the chunks [cf(sK), cf(sK+K)) into the state, cf(c) =
+// chunks wholly before the window of chunk c. This kernel sums their
+// unkept tokens' phi(k) v^T (and phi(k)) so the scan can give every
+// super-chunk its starting state.
+template <typename T, int D>
+__global__ __launch_bounds__(512) void state_delta_kernel(PrefillArgs a) {
+  extern __shared__ __align__(16) char smem[];
+  const BlkPtr<T, D> P(smem);
+  const int s = blockIdx.x, kv = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x;
+  const int unit = b * a.Hkv + kv;
+  const T* kg = reinterpret_cast<const T*>(a.k) + (size_t)unit * a.L * D;
+  const T* vg = reinterpret_cast<const T*>(a.v) + (size_t)unit * a.L * D;
+  const uint8_t* sf = a.selflag + (size_t)unit * a.L;
+  const T* ftg = reinterpret_cast<const T*>(a.ft) + (size_t)kv * D * D;
+  f32x4 Sacc[Blk<T, D>::PPW][2];
+#pragma unroll
+  for (int pp = 0; pp < Blk<T, D>::PPW; ++pp) Sacc[pp][0] = Sacc[pp][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+  if (tid < D) P.zs[tid] = 0.f;
+  const int lo = full_chunks_before(s * a.K, a.W, a.C) * a.C;
+  const int hi = full_chunks_before(s * a.K + a.K, a.W, a.C) * a.C;
+  for (int blo = lo; blo < hi; blo += 64) {
+    __syncthreads();
+    load_block<T, D>(a, P, kg, vg, sf, nullptr, 0, blo, hi, lo, hi);
+    __syncthreads();
+    block_phi<T, D>(P, ftg);
+    __syncthreads();
+    block_fold<T, D>(P, Sacc);
+  }
+  __syncthreads();
+  float* dst = a.dS + ((size_t)unit * a.NS + s) * (D * D + D);
+  store_state_acc<T, D>(dst, Sacc);
+  if (tid < D) dst[D * D + tid] = P.zs[tid];
+}
+
+// ----------------------------------------------------- 5. state_scan ----
+__global__ __launch_bounds__(256) void state_scan_kernel(float* dS, int NS, int n_elem) {
+  const int e = blockIdx.x * 256 + threadIdx.x;
+  if (e >= n_elem) return;
+  float* base = dS + (size_t)(blockIdx.y + gridDim.y * blockIdx.z) * NS * n_elem;
+  double run = 0.0;  // float64 running sum: one float32 rounding per start
+  for (int s = 0; s < NS; ++s) {
+    const float x = base[(size_t)s * n_elem + e];
+    base[(size_t)s * n_elem + e] = (float)run;
+    if (s + 1 < NS) run += (double)x;
+  }
+}
+
+// ---------------------------------------------------------- 6. attend ----
+// One workgroup per (super-chunk, kv head x head group, batch row); 8 waves,
+// each owning up to TPW 16-query row tiles (one head, 16 positions). For
+// each chunk of the super-chunk, in order:
+//  * phi(Q) and the state readout S^T phi(Q)^T, z . phi(q): the linear
+//    state enters as one virtual key of weight g*z.phi(q) and value
+//    S^T phi(q) / z.phi(q) [P3 "NP-Map ..."];
+//  * kept-pool keys below the band (all visible) [P2 固定预算路由];
+//  * band keys from the first chunk not yet folded to the chunk's end: a key
+//    is softmax-visible if it is in the window, in the query's own chunk or
+//    kept; otherwise (decided, unkept, out of the window) it is a linear key
+//    with weight g <phi(q), phi(k)>;
+//  * every weight enters one running max / sum in the log domain (reading:
+//    a single normaliser over softmax and gated linear weights);
+//  * the next chunk's newly folded tokens are added to the state.
+template <typename T, int D, int TPW>
+__global__ __launch_bounds__(512) void attend_kernel(PrefillArgs a) {
+  using B_ = Blk<T, D>;
+  extern __shared__ __align__(16) char smem[];
+  const BlkPtr<T, D> P(smem);
+  const int s = blockIdx.x, kv = blockIdx.y / a.nHG, hg = blockIdx.y % a.nHG, b = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, r16 = lane & 15, g4 = lane >> 4;
+  const int L = a.L, C = a.C, W = a.W;
+  const int unit = b * a.Hkv + kv;
+  const T* kg = reinterpret_cast<const T*>(a.k) + (size_t)unit * L * D;
+  const T* vg = reinterpret_cast<const T*>(a.v) + (size_t)unit * L * D;
+  const uint8_t* sf = a.selflag + (size_t)unit * L;
+  const int32_t* selu = a.sel + (size_t)unit * a.n_dec * a.lam;
+  const T* ftg = reinterpret_cast<const T*>(a.ft) + (size_t)kv * D * D;
+  const int n_qt = C / 16;
+  const int n_rt = a.Gs * n_qt;
+
+  f32x4 Sacc[B_::PPW][2];
+  const float* Sst = a.dS + ((size_t)unit * a.NS + s) * (D * D + D);
+  load_state_acc<T, D>(Sst, Sacc);
+  if (tid < D) P.zs[tid] = Sst[D * D + tid];
+  write_stf<T, D>(P, Sacc);
+
+  const int c_begin = s * a.K;
+  const int c_end = min(c_begin + a.K, a.T);
+  for (int c = c_begin; c < c_end; ++c) {
+    __syncthreads();
+    const int cC = c * C;
+    const bool fold = c + 1 < c_end;
+    const int cf = full_chunks_before(c, W, C);
+    const int fold_lo = cf * C;
+    const int fold_hi = fold ? full_chunks_before(c + 1, W, C) * C : fold_lo;
+    const int band_lo = cf * C;
+    const int band_hi = min(cC + C, L);
+    const int n_oob = pool_count_at(cf, a.lam, a.cap_chunks);
+
+    // per row tile: query fragments, phi(q), state readout
+    Frag<T> qf[TPW][D / 32];
+    Frag<T> phq[TPW][D / 32];
+    f32x4 O[TPW][D / 16];
+    float mrun[TPW], lrun[TPW], lgate[TPW];
+    int tq[TPW], hq[TPW];
+#pragma unroll
+    for (int rr = 0; rr < TPW; ++rr) {
+      const int rt = wave + 8 * rr;
+      const bool act = rt < n_rt;
+      const int hl = act ? rt / n_qt : 0, qt = act ? rt % n_qt : 0;
+      const int h = kv * a.G + hg * a.Gs + hl;
+      const int t = cC + 16 * qt + r16;
+      tq[rr] = act ? t : -1;
+      hq[rr] = h;
+      const T* qg = reinterpret_cast<const T*>(a.q) + ((size_t)(b * a.Hq + h) * L) * D;
+#pragma unroll
+      for (int kb = 0; kb < D / 32; ++kb)
+        qf[rr][kb] = (act && t < L) ? ld_frag(qg + (size_t)t * D + 32 * kb + 8 * g4) : zero_frag<T>();
+      f32x4 ph[D / 16];
+      np_map_tile<T, D>(ftg, qf[rr], ph);
+      float dz = 0.f;
+#pragma unroll
+      for (int ft = 0; ft < D / 16; ++ft)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dz += ph[ft][i] * P.zs[16 * ft + 4 * g4 + i];
+      dz = sum_over_g(dz);
+#pragma unroll
+      for (int bb = 0; bb < D / 32; ++bb) phq[rr][bb] = frag_from<T>(ph[2 * bb], ph[2 * bb + 1]);
+      const float g = a.gate[h];
+      lgate[rr] = g > 0.f ? __logf(g) : STILL_NEG_INF;
+#pragma unroll
+      for (int dt = 0; dt < D / 16; ++dt) {
+        O[rr][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int bb = 0; bb < D / 32; ++bb)
+          mma(O[rr][dt], ld_frag(P.STF + ((size_t)(dt * (D / 32) + bb) * 64 + lane) * 8), phq[rr][bb]);
+      }
+      if (g > 0.f && dz > 0.f) {
+        mrun[rr] = __logf(g * dz);
+        lrun[rr] = g4 == 0 ? 1.f : 0.f;
+        const float inv = 1.f / dz;
+#pragma unroll
+        for (int dt = 0; dt < D / 16; ++dt) O[rr][dt] *= inv;
+      } else {
+        mrun[rr] = STILL_NEG_INF;
+        lrun[rr] = 0.f;
+#pragma unroll
+        for (int dt = 0; dt < D / 16; ++dt) O[rr][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+    }
+
+    // key blocks: kept pool below the band, then the band
+    const int n_pool_blk = (n_oob + 63) / 64;
+    const int n_band_blk = (band_hi - band_lo + 63) / 64;
+    for (int blk = 0; blk < n_pool_blk + n_band_blk; ++blk) {
+      const bool is_pool = blk < n_pool_blk;
+      const int blo = is_pool ? 64 * blk : band_lo + 64 * (blk - n_pool_blk);
+      const bool la_blk = !is_pool && blo < cC;
+      const bool need_phi = !is_pool && blo < max(cC, fold_hi);
+      __syncthreads();
+      if (is_pool)
+        load_block<T, D>(a, P, kg, vg, sf, selu + blo, min(64, n_oob - blo), 0, 0, 0, 0);
+      else
+        load_block<T, D>(a, P, kg, vg, sf, nullptr, 0, blo, band_hi, fold_lo, fold_hi);
+      __syncthreads();
+      if (need_phi) {
+        block_phi<T, D>(P, ftg);
+        __syncthreads();
+      }
+#pragma unroll
+      for (int rr = 0; rr < TPW; ++rr) {
+        if (wave + 8 * rr >= n_rt) continue;  // wave-uniform
+        const int t = tq[rr];
+        f32x4 st[4], wt[4];
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt) {
+          st[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int kb = 0; kb < D / 32; ++kb)
+            mma(st[kt], ld_frag(P.Ks + (16 * kt + r16) * B_::KS + 32 * kb + 8 * g4), qf[rr][kb]);
+        }
+        if (la_blk) {
+#pragma unroll
+          for (int kt = 0; kt < 4; ++kt) {
+            wt[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int bb = 0; bb < D / 32; ++bb) {
+              const float* pr = P.phiK + (16 * kt + r16) * B_::PS + 32 * bb + 4 * g4;
+              mma(wt[kt], frag_from<T>(*reinterpret_cast<const f32x4*>(pr),
+                                       *reinterpret_cast<const f32x4*>(pr + 16)),
+                  phq[rr][bb]);
+            }
+          }
+        }
+        float mx = STILL_NEG_INF;
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int kk = 16 * kt + 4 * g4 + i;
+            const int j = P.kpos[kk];
+            float lw = STILL_NEG_INF;
+            if (j >= 0 && j <= t) {
+              if (is_pool || j >= t - W + 1 || j >= cC || P.ksel[kk]) {
+                lw = st[kt][i] * a.scale;
+              } else if (la_blk) {
+                const float w = wt[kt][i];
+                lw = w > 0.f ? lgate[rr] + __logf(w) : STILL_NEG_INF;
+              }
+            }
+            st[kt][i] = lw;
+            mx = fmaxf(mx, lw);
+          }
+        mx = max_over_g(mx);
+        const float mn = fmaxf(mrun[rr], mx);
+        // rows with nothing visible so far keep m = -inf, O = 0, l = 0
+        const float al = mrun[rr] == STILL_NEG_INF ? 0.f : __expf(mrun[rr] - mn);
+        mrun[rr] = mn;
+        float lsum = 0.f;
+        f32x4 pv[4];
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float lw = st[kt][i];
+            pv[kt][i] = lw == STILL_NEG_INF ? 0.f : __expf(lw - mn);
+          }
+        const Frag<T> pf0 = frag_from<T>(pv[0], pv[1]);
+        const Frag<T> pf1 = frag_from<T>(pv[2], pv[3]);
+        // the running sum uses the rounded weights the product uses
+        lsum = frag_sum(pf0) + frag_sum(pf1);
+        lrun[rr] = lrun[rr] * al + lsum;
+#pragma unroll
+        for (int dt = 0; dt < D / 16; ++dt) {
+          O[rr][dt] *= al;
+          mma(O[rr][dt], ld_frag(P.VTs + (16 * dt + r16) * B_::VS + 8 * g4), pf0);
+          mma(O[rr][dt], ld_frag(P.VTs + (16 * dt + r16) * B_::VS + 32 + 8 * g4), pf1);
+        }
+      }
+      if (fold && !is_pool && blo < fold_hi) block_fold<T, D>(P, Sacc);
+    }
+
+    // outputs
+#pragma unroll
+    for (int rr = 0; rr < TPW; ++rr) {
+      const int t = tq[rr];
+      const float l = sum_over_g(lrun[rr]);
+      if (t < 0 || t >= L) continue;
+      const float inv = 1.f / l;
+      const size_t ob = ((size_t)(b * a.Hq + hq[rr]) * L + t) * D;
+#pragma unroll
+      for (int dt = 0; dt < D / 16; ++dt) {
+        const f32x4 y = O[rr][dt] * inv;
+        if (a.fp32_out) {
+          *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.out) + ob + 16 * dt + 4 * g4) = y;
+        } else {
+          T* o = reinterpret_cast<T*>(a.out) + ob + 16 * dt + 4 * g4;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) o[i] = from_f32<T>(y[i]);
+        }
+      }
+    }
+    if (c == a.T - 1 && hg == 0) {
+      __syncthreads();
+      char* st = a.state + (size_t)unit * a.st_unit;
+      store_state_acc<T, D>(reinterpret_cast<float*>(st + a.st_S), Sacc);
+      if (tid < D) reinterpret_cast<float*>(st + a.st_z)[tid] = P.zs[tid];
+    }
+    if (fold) {
+      __syncthreads();
+      write_stf<T, D>(P, Sacc);
+    }
+  }
+}
+
+// ---------------------------------------------------------- 7. export ----
+// Decode state after the prefill: ring slots of the last R positions (keys,
+// values, NP-Map features, kept flags), the kept pool, and the position.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void export_kernel(PrefillArgs a) {
+  const int x = blockIdx.x, kv = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, L = a.L, R = a.R;
+  const int unit = b * a.Hkv + kv;
+  char* st = a.state + (size_t)unit * a.st_unit;
+  const T* kg = reinterpret_cast<const T*>(a.k) + (size_t)unit * L * D;
+  const T* vg = reinterpret_cast<const T*>(a.v) + (size_t)unit * L * D;
+  const int ring_lo = L - R > 0 ? L - R : 0;
+  const int n_ring_grp = (L - ring_lo + 15) / 16;
+  if (x < n_ring_grp) {
+    __shared__ float xs[16][D];
+    __shared__ float us[16][D];
+    __shared__ float red[16][3];
+    const T* F = reinterpret_cast<const T*>(a.fmap_w) + (size_t)kv * D * D;
+    for (int e = tid; e < 16 * D; e += 256) {
+      const int r = e / D, i = e % D, p = ring_lo + 16 * x + r;
+      xs[r][i] = p < L ? to_f32(kg[(size_t)p * D + i]) : 0.f;
+    }
+    __syncthreads();
+    for (int e = tid; e < 16 * D; e += 256) {
+      const int r = e / D, j = e % D;
+      float u = 0.f;
+      for (int i = 0; i < D; ++i) u += xs[r][i] * to_f32(F[(size_t)i * D + j]);
+      us[r][j] = u;
+    }
+    __syncthreads();
+    if (tid < 16) {
+      float mx = STILL_NEG_INF, xn = 0.f;
+      for (int j = 0; j < D; ++j) mx = fmaxf(mx, us[tid][j]);
+      for (int i = 0; i < D; ++i) xn += xs[tid][i] * xs[tid][i];
+      float ss = 0.f;
+      for (int j = 0; j < D; ++j) {
+        const float e = __expf(us[tid][j] - mx);
+        ss += e * e;
+      }
+      red[tid][0] = mx;
+      red[tid][1] = sqrtf(xn) / sqrtf(ss);
+    }
+    __syncthreads();
+    T* rk = reinterpret_cast<T*>(st + a.st_ring_k);
+    T* rv = reinterpret_cast<T*>(st + a.st_ring_v);
+    T* rp = reinterpret_cast<T*>(st + a.st_ring_phi);
+    int32_t* rf = reinterpret_cast<int32_t*>(st + a.st_ring_flag);
+    for (int e = tid; e < 16 * D; e += 256) {
+      const int r = e / D, j = e % D, p = ring_lo + 16 * x + r;
+      if (p >= L) continue;
+      const int slot = p % R;
+      rk[(size_t)slot * D + j] = kg[(size_t)p * D + j];
+      rv[(size_t)slot * D + j] = vg[(size_t)p * D + j];
+      rp[(size_t)slot * D + j] = from_f32<T>(__expf(us[r][j] - red[r][0]) * red[r][1]);
+      if (j == 0) rf[slot] = a.selflag[(size_t)unit * L + p];
+    }
+    return;
+  }
+  // kept pool rows, 16 per workgroup
+  const int n_pool = pool_count_at(a.n_dec, a.lam, a.cap_chunks);
+  const int i0 = (x - n_ring_grp) * 16;
+  const int32_t* selu = a.sel + (size_t)unit * a.n_dec * a.lam;
+  T* pk = reinterpret_cast<T*>(st + a.st_pool_k);
+  T* pvv = reinterpret_cast<T*>(st + a.st_pool_v);
+  int32_t* pp = reinterpret_cast<int32_t*>(st + a.st_pool_pos);
+  for (int e = tid; e < 16 * D; e += 256) {
+    const int r = e / D, j = e % D, i = i0 + r;
+    if (i >= n_pool) continue;
+    const int p = selu[i];
+    pk[(size_t)i * D + j] = kg[(size_t)p * D + j];
+    pvv[(size_t)i * D + j] = vg[(size_t)p * D + j];
+    if (j == 0) pp[i] = p;
+  }
+  if (x == n_ring_grp && tid == 0) {
+    int64_t* meta = reinterpret_cast<int64_t*>(st + a.st_meta);
+    meta[0] = L;
+    meta[1] = n_pool;
+    meta[2] = 0;
+    meta[3] = 0;
+  }
+}
+
+}  // namespace still

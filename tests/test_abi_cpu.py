@@ -1,0 +1,126 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+the header declares, and validates arguments on the host before any launch.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from linear_attention_still_amd import still
+from linear_attention_still_amd.inputs import WORKLOADS
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_functions():
+    with open(os.path.join(ROOT, "include", "still.h")) as fh:
+        text = fh.read()
+    return sorted(set(re.findall(r"^\s*(?:int|int64_t|const char\*)\s+(still_\w+)\s*\(",
+                                 text, re.M)))
+
+
+def test_library_exports_every_declared_function():
+    names = header_functions()
+    assert {"still_prefill", "still_decode_step", "still_lambda", "still_state_bytes",
+            "still_workspace_bytes", "still_state_layout_get", "still_status_str"} <= set(names)
+    L = still.lib()
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_struct_sizes_match_header():
+    assert ctypes.sizeof(still.still_params) == 13 * 4
+    assert ctypes.sizeof(still.still_state_layout) == 12 * 8 + 8
+
+
+def base_params(**kw):
+    wl = WORKLOADS["llama8b_bf16_L16K"]
+    p = still.params_for(wl)
+    for k, v in kw.items():
+        setattr(p, k, v)
+    return p
+
+
+def test_lambda_values():
+    assert still.still_lambda(still.params_for(WORKLOADS["small_f32_L256"])) == 6
+    assert still.still_lambda(still.params_for(WORKLOADS["gqa_bf16_L4K"])) == 3
+    assert still.still_lambda(still.params_for(WORKLOADS["llama8b_bf16_L16K"])) == 1
+    assert still.still_lambda(still.params_for(WORKLOADS["llama8b_bf16_L64K"])) == 1
+    assert still.still_lambda(base_params(budget=64 + 64 * 1000, t_max=2)) == 64  # capped at C
+    assert still.still_lambda(base_params(budget=64)) == 0
+
+
+@pytest.mark.parametrize("field,value,rc", [
+    ("abi_version", 2, still.STILL_EINVAL),
+    ("dtype", 7, still.STILL_EINVAL),
+    ("batch", 0, still.STILL_EINVAL),
+    ("n_q_heads", 30, still.STILL_EINVAL),
+    ("window", 0, still.STILL_EINVAL),
+    ("budget", 10, still.STILL_EINVAL),
+    ("t_max", 0, still.STILL_EINVAL),
+    ("head_dim", 96, still.STILL_EUNSUPPORTED),
+    ("chunk", 48, still.STILL_EUNSUPPORTED),
+    ("window", 300, still.STILL_EUNSUPPORTED),
+])
+def test_invalid_params_rejected(field, value, rc):
+    p = base_params(**{field: value})
+    L = still.lib()
+    assert L.still_lambda(ctypes.byref(p)) == rc
+    assert L.still_state_bytes(ctypes.byref(p)) == rc
+    assert L.still_workspace_bytes(ctypes.byref(p), 1024) == rc
+
+
+def test_f32_head_dim_128_unsupported():
+    p = still.make_params(dtype="f32", batch=1, n_q_heads=1, n_kv_heads=1, head_dim=128,
+                          window=16, chunk=32, budget=64, t_max=8)
+    assert still.lib().still_lambda(ctypes.byref(p)) == still.STILL_EUNSUPPORTED
+
+
+def test_state_layout_and_sizes():
+    p = still.params_for(WORKLOADS["decode_bf16_B64_ctx16K"])
+    lay = still.still_state_layout_get(p)
+    assert lay.ring_slots == 64 + 2 * 64 and lay.pool_slots == 512 - 64
+    offs = [lay.S, lay.z, lay.pool_k, lay.pool_v, lay.pool_pos, lay.ring_k, lay.ring_v,
+            lay.ring_phi, lay.ring_flag, lay.pending, lay.meta]
+    assert offs == sorted(offs) and all(o % 256 == 0 for o in offs)
+    assert lay.pool_v - lay.pool_k >= 448 * 128 * 2
+    assert lay.unit_bytes >= lay.meta + 32
+    assert still.still_state_bytes(p) == lay.unit_bytes * 64 * 8
+    assert still.still_workspace_bytes(p, 0) == 0
+    assert still.still_workspace_bytes(p, 16384) > 64 * 8 * 16384 * 9
+
+
+def test_prefill_validates_before_any_launch():
+    """Null pointers, bad lengths and a short workspace are rejected on the
+    host (these calls make no HIP call, so they work without a GPU)."""
+    p = still.params_for(WORKLOADS["small_f32_L256"])
+    L = still.lib()
+    fake = ctypes.c_void_p(1 << 20)
+    args = [fake] * 10
+    ws = still.still_workspace_bytes(p, 256)
+    rc = L.still_prefill(ctypes.byref(p), 256, *([None] + args[1:]), ws, None)
+    assert rc == still.STILL_EINVAL
+    rc = L.still_prefill(ctypes.byref(p), 0, *args, ws, None)
+    assert rc == still.STILL_EINVAL
+    rc = L.still_prefill(ctypes.byref(p), 256, *args, ws - 1, None)
+    assert rc == still.STILL_EWORKSPACE
+    odd = ctypes.c_void_p((1 << 20) + 4)
+    rc = L.still_prefill(ctypes.byref(p), 256, *([odd] + args[1:]), ws, None)
+    assert rc == still.STILL_EINVAL
+
+
+def test_decode_validates_before_any_launch():
+    p = still.params_for(WORKLOADS["decode_bf16_B64_ctx16K"])
+    L = still.lib()
+    fake = ctypes.c_void_p(1 << 20)
+    rc = L.still_decode_step(ctypes.byref(p), 0, *([fake] * 9), 0, None)
+    assert rc == still.STILL_EINVAL
+    rc = L.still_decode_step(ctypes.byref(p), 16384, *([None] + [fake] * 8), 0, None)
+    assert rc == still.STILL_EINVAL
+
+
+def test_status_strings():
+    for rc in (0, -1, -2, -3, -4, -5):
+        assert still.still_status_str(rc) != "unknown status"
+    assert still.still_status_str(42) == "unknown status"

@@ -1,0 +1,196 @@
+"""Parity of the HIP path (through the C ABI) with the oracle, on the GPU.
+
+Every input is seeded and synthetic (linear_attention_still_amd.inputs).
+Small shapes are compared element by element over every unit; the full
+workloads are compared over every unit where the oracle finishes in seconds
+and over sampled (batch row, kv head) units otherwise, in the launch
+configuration the bench uses.
+"""
+import numpy as np
+import pytest
+import torch
+
+from linear_attention_still_amd import still
+from linear_attention_still_amd.inputs import WORKLOADS, Workload, make_decode_tokens, make_inputs
+from oracle import rec
+from tests import _parity as P
+
+pytestmark = pytest.mark.gpu
+
+
+def small(name, dtype, B, Hq, Hkv, d, L, W, C, m, t_max, sigma=0.5, out=0.01, seed=11):
+    return Workload(name, dtype, B, Hq, Hkv, d, L, W, C, m, t_max, sigma=sigma,
+                    outlier_frac=out, seed=seed)
+
+
+SHAPES = [
+    small("f32_d64_W16_C32", "f32", 1, 2, 1, 64, 200, 16, 32, 64, 7, out=0.0),
+    small("f32_gqa_ragged", "f32", 2, 4, 2, 64, 333, 40, 64, 40 + 6 * 3, 6),
+    small("bf16_d64_W64_C64", "bf16", 1, 4, 1, 64, 600, 64, 64, 64 + 3 * 10, 10),
+    small("bf16_d128_ragged", "bf16", 1, 8, 2, 128, 1000, 64, 64, 64 + 16 * 3, 16),
+    small("bf16_W_lt_C", "bf16", 1, 4, 2, 128, 700, 16, 64, 16 + 11 * 2, 11),
+    small("bf16_W_gt_C", "bf16", 1, 2, 1, 64, 500, 96, 32, 96 + 16 * 2, 16),
+    small("bf16_lambda0", "bf16", 1, 4, 1, 128, 400, 32, 32, 32, 13),
+    small("bf16_full_softmax", "bf16", 1, 4, 1, 64, 256, 32, 32, 32 + 8 * 32, 8),
+    small("bf16_C128_split_heads", "bf16", 1, 4, 1, 128, 700, 128, 128, 128 + 6 * 4, 6),
+    small("bf16_C16_W8", "bf16", 1, 2, 1, 64, 300, 8, 16, 8 + 19 * 2, 19),
+    small("bf16_G8", "bf16", 1, 8, 1, 64, 300, 32, 32, 32 + 10 * 2, 10),
+    small("bf16_G1", "bf16", 2, 3, 3, 64, 260, 32, 32, 32 + 9 * 2, 9),
+    small("bf16_budget_fills", "bf16", 1, 4, 1, 64, 640, 16, 32, 16 + 6 * 2, 3),
+    small("bf16_W1_ties", "bf16", 1, 2, 1, 64, 160, 1, 32, 1 + 5 * 4, 5),
+    small("bf16_one_token", "bf16", 1, 4, 1, 64, 1, 16, 32, 64, 4),
+    small("bf16_one_chunk", "bf16", 1, 4, 1, 64, 64, 16, 64, 64, 1),
+    small("bf16_one_decided", "bf16", 1, 4, 1, 64, 65, 16, 64, 80, 1),
+]
+
+
+@pytest.mark.parametrize("wl", SHAPES, ids=[w.name for w in SHAPES])
+def test_prefill_parity_shapes(wl):
+    x = make_inputs(wl)
+    o = P.oracle(wl, x)
+    g = P.gpu_prefill(wl, x, fp32_out=(wl.dtype == "bf16"))
+    P.compare_prefill(wl, g, o, out_fp32=(wl.dtype == "bf16"))
+    if wl.dtype == "bf16":
+        g2 = P.gpu_prefill(wl, x, fp32_out=False)
+        P.compare_prefill(wl, g2, o, out_fp32=False, check_state_too=False)
+
+
+def test_small_f32_workload():
+    wl = WORKLOADS["small_f32_L256"]
+    x = make_inputs(wl)
+    P.compare_prefill(wl, P.gpu_prefill(wl, x), P.oracle(wl, x))
+
+
+@pytest.mark.timeout(600)
+def test_gqa_L4K_workload():
+    wl = WORKLOADS["gqa_bf16_L4K"]
+    x = make_inputs(wl)
+    o = P.oracle(wl, x)
+    P.compare_prefill(wl, P.gpu_prefill(wl, x, fp32_out=True), o, out_fp32=True)
+    P.compare_prefill(wl, P.gpu_prefill(wl, x), o, check_state_too=False)
+
+
+@pytest.mark.timeout(600)
+def test_llama8b_L16K_workload():
+    wl = WORKLOADS["llama8b_bf16_L16K"]
+    x = make_inputs(wl)
+    o = P.oracle(wl, x)
+    P.compare_prefill(wl, P.gpu_prefill(wl, x, fp32_out=True), o, out_fp32=True)
+    P.compare_prefill(wl, P.gpu_prefill(wl, x), o, check_state_too=False)
+
+
+@pytest.mark.timeout(900)
+def test_llama8b_L64K_workload_sampled_units():
+    """All 8 kv heads run on the GPU; the oracle checks kv heads 0 and 5."""
+    wl = WORKLOADS["llama8b_bf16_L64K"]
+    x = make_inputs(wl)
+    units = [(0, 0), (0, 5)]
+    o = P.oracle(wl, x, units=units)
+    P.compare_prefill(wl, P.gpu_prefill(wl, x, fp32_out=True), o, units=units, out_fp32=True)
+
+
+def test_prefill_deterministic():
+    wl = WORKLOADS["gqa_bf16_L4K"]
+    x = make_inputs(wl)
+    a = P.gpu_prefill(wl, x)
+    b = P.gpu_prefill(wl, x)
+    for k in ("y", "sel", "score", "S", "z", "pending", "ring_k", "pool_k"):
+        assert torch.equal(a[k], b[k]), k
+
+
+DECODE_SHAPES = [
+    # (workload, prefill length, decode steps)
+    (small("dec_f32", "f32", 1, 2, 1, 64, 90, 16, 32, 16 + 4 * 6, 6, out=0.0), 90, 70),
+    (small("dec_bf16_d128", "bf16", 2, 8, 2, 128, 256, 64, 64, 64 + 8 * 2, 8), 256, 130),
+    (small("dec_bf16_W_lt_C", "bf16", 1, 4, 1, 64, 100, 16, 32, 16 + 3 * 10, 10), 100, 75),
+    (small("dec_bf16_W_gt_C", "bf16", 1, 2, 1, 64, 70, 48, 16, 48 + 2 * 12, 12), 70, 60),
+    (small("dec_bf16_fill", "bf16", 1, 4, 1, 64, 96, 8, 16, 8 + 2 * 4, 4), 96, 80),
+]
+
+
+@pytest.mark.parametrize("case", DECODE_SHAPES, ids=[c[0].name for c in DECODE_SHAPES])
+def test_decode_matches_prefill_of_extended_sequence(case):
+    """Prefill L0 tokens, decode n more one by one; the oracle runs the layer
+    over all L0 + n tokens (prefill and decode share one rule)."""
+    wl, L0, n = case
+    x = make_inputs(wl, seq_len=L0)
+    toks = make_decode_tokens(wl, n)
+    g = P.gpu_prefill(wl, x, keep_device=True)
+    p = still.params_for(wl, fp32_out=(wl.dtype == "bf16"))
+    xd = {k: v.cuda() for k, v in x.items()}
+    td = {k: v.cuda() for k, v in toks.items()}
+    outs, sels = P.run_decode(wl, g["_state"], p, xd, td, L0, fp32_out=(wl.dtype == "bf16"))
+    units = [(b, kv) for b in range(wl.batch) for kv in range(wl.n_kv_heads)]
+    qs, ks, vs, Fs, gs = P.concat_units(x, toks, wl, units)
+    o = rec.run_units(qs, ks, vs, Fs, gs, window=wl.window, chunk=wl.chunk, budget=wl.budget,
+                      t_max=wl.t_max, n_threads=P.n_threads())
+    G = wl.group
+    yg = np.stack([outs[:, b, kv * G:(kv + 1) * G].numpy().transpose(1, 0, 2) for b, kv in units])
+    P.check_outputs(yg, o["y"][:, :, L0:], wl.dtype, True, "decode y")
+    lam = o["lam"]
+    for s in range(n):
+        t = L0 + s
+        if t % wl.chunk == 0 and lam > 0:
+            want = o["sel"][:, t // wl.chunk - 1]
+            got = np.stack([sels[s, b, kv].numpy() for b, kv in units])
+            assert np.array_equal(got, want), (s, got, want)
+    sv = still.state_views(p, g["_state"])
+    P.check_state(sv["S"].cpu().numpy(), o["S"], wl.dtype, "decode S")
+    P.check_state(sv["z"].cpu().numpy(), o["z"], wl.dtype, "decode z")
+    meta = sv["meta"].cpu().numpy()
+    assert np.all(meta[:, 0] == L0 + n) and np.all(meta[:, 2] == 0)
+    assert np.array_equal(meta[:, 1], o["n_pool"])
+    pend = sv["pending"].cpu().numpy()
+    assert np.array_equal(np.isnan(pend), np.isnan(o["pending"]))
+    ok = ~np.isnan(pend)
+    assert np.allclose(pend[ok], o["pending"][ok], rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.timeout(900)
+def test_decode_workload_sampled_units():
+    """Batch 64 at 16K context: prefill on the GPU, 64 decode steps (one
+    chunk-boundary decision); the oracle checks two sampled units."""
+    wl = WORKLOADS["decode_bf16_B64_ctx16K"]
+    L0, n = wl.seq_len, wl.decode_steps
+    x = make_inputs(wl, device="cuda")
+    toks = make_decode_tokens(wl, n, device="cuda")
+    p = still.params_for(wl, fp32_out=True)
+    print("  gpu prefill B=64 L=16384", flush=True)
+    bufs = still.PrefillBuffers(p, L0)
+    still.run_prefill(p, x, bufs)
+    outs, sels = P.run_decode(wl, bufs.state, p, x, toks, L0, fp32_out=True)
+    units = [(0, 0), (37, 5)]
+    qs, ks, vs, Fs, gs = P.concat_units(x, toks, wl, units)
+    print("  oracle 2 units, %d tokens" % (L0 + n), flush=True)
+    o = rec.run_units(qs, ks, vs, Fs, gs, window=wl.window, chunk=wl.chunk, budget=wl.budget,
+                      t_max=wl.t_max, n_threads=P.n_threads())
+    G = wl.group
+    yg = np.stack([outs[:, b, kv * G:(kv + 1) * G].numpy().transpose(1, 0, 2) for b, kv in units])
+    P.check_outputs(yg, o["y"][:, :, L0:], "bf16", True, "decode y")
+    got = np.stack([sels[0, b, kv].numpy() for b, kv in units])
+    assert np.array_equal(got, o["sel"][:, L0 // wl.chunk - 1])
+    sv = still.state_views(p, bufs.state)
+    idx = [b * wl.n_kv_heads + kv for b, kv in units]
+    P.check_state(sv["S"][idx].cpu().numpy(), o["S"], "bf16", "S")
+    P.check_state(sv["z"][idx].cpu().numpy(), o["z"], "bf16", "z")
+
+
+def test_prefill_then_decode_equals_longer_prefill():
+    """GPU only: prefill(L1) + decode to L gives the outputs, kept positions
+    and state of prefill(L)."""
+    wl = small("pd", "bf16", 1, 4, 2, 128, 320, 64, 64, 64 + 5 * 2, 5)
+    L1 = 190
+    x = make_inputs(wl)
+    xs = {k: (v[:, :, :L1].contiguous() if k in ("q", "k", "v") else v) for k, v in x.items()}
+    toks = {k: x[k][:, :, L1:].permute(2, 0, 1, 3).contiguous() for k in ("q", "k", "v")}
+    full = P.gpu_prefill(wl, x, fp32_out=True)
+    g = P.gpu_prefill(wl, xs, keep_device=True)
+    p = still.params_for(wl, fp32_out=True)
+    xd = {k: v.cuda() for k, v in x.items()}
+    td = {k: v.cuda() for k, v in toks.items()}
+    outs, sels = P.run_decode(wl, g["_state"], p, xd, td, L1, fp32_out=True)
+    err = (outs.permute(1, 2, 0, 3) - full["y"][:, :, L1:]).abs().max().item()
+    assert err <= 2e-2, err
+    sv = still.state_views(p, g["_state"])
+    assert torch.equal(sv["pool_pos"].cpu(), full["pool_pos"])
+    assert (sv["S"].cpu() - full["S"]).abs().max().item() <= 2e-2
