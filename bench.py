@@ -1,0 +1,207 @@
+#!/usr/bin/env python3
+"""Throughput of one STILL hybrid-attention layer on one MI355X.
+
+A step is one prefill of the layer (score -> chunk Top-lambda -> window +
+kept softmax -> NP-Map linear attention + merge, plus the decode-state
+export) over one batch of seeded synthetic inputs shaped like a
+Llama-3-8B layer at 16K context (32 query / 8 kv heads, head dim 128,
+W = C = 64, budget m = 512). Inputs are resident in HBM before the timed
+region. The decode leg (batch 64 at 16K context, 64 steps including one
+chunk-boundary decision) and the oracle's CPU baseline are reported in the
+same JSON line.
+
+  python bench.py [--steps K] [--warmup W] [--no-cpu-baseline] [--no-decode]
+
+One GPU only: --gpus above 1 exits with a message.
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+METRIC = "hybrid-attn prefill tokens/s/layer at 16K (MFMA %peak); decode tok/s (HBM GB/s)"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+
+def algorithmic_work(wl, sel):
+    """Algorithmic flops of the layer and of the attention kernel, counted
+    from the actual selection (no padding, masked tile halves or
+    recomputation): softmax 4d|A(t)| per (head, query); NP-Map 2d^2 per
+    query row and per key; linear readout (2d^2 + 2d) per (head, query);
+    state update (2d^2 + 2d) per folded token per kv head."""
+    import numpy as np
+    B, Hkv, G, d = wl.batch, wl.n_kv_heads, wl.group, wl.head_dim
+    L, W, C = wl.seq_len, wl.window, wl.chunk
+    t = np.arange(L)
+    c = t // C
+    lo = np.maximum(0, np.minimum(t - W + 1, c * C))
+    sum_A = 0
+    n_la = 0
+    for b in range(B):
+        for kv in range(Hkv):
+            pool = np.sort(sel[b, kv].reshape(-1))
+            pool = pool[pool >= 0]
+            a_t = (t - lo + 1) + np.searchsorted(pool, lo)
+            sum_A += int(a_t.sum())
+            c_last = (L - 1) // C
+            last_ok = min(L - 1 - W, c_last * C - 1)
+            n_la += max(0, last_ok + 1) - int(np.count_nonzero(pool <= last_ok))
+    Hq = B * Hkv * G
+    sa = 4 * d * G * sum_A
+    phi = 2 * d * d * L * (B * Hkv * G + B * Hkv)
+    phi_q = 2 * d * d * L * Hq
+    readout = (2 * d * d + 2 * d) * L * Hq
+    update = (2 * d * d + 2 * d) * n_la
+    total = sa + phi + readout + update
+    attend = sa + phi_q + readout
+    return {"total": total, "attend": attend, "sa": sa, "phi": phi, "readout": readout,
+            "update": update, "sum_A": sum_A}
+
+
+def run_prefill_bench(args, torch, still, inputs):
+    wl = inputs.WORKLOADS["llama8b_bf16_L16K"]
+    p = still.params_for(wl)
+    x = inputs.make_inputs(wl, device="cuda")
+    bufs = still.PrefillBuffers(p, wl.seq_len)
+    nk = len(still.PREFILL_KERNELS)
+    for _ in range(args.warmup):
+        still.run_prefill(p, x, bufs)
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2 * nk)] for _ in range(args.steps)]
+    for evs in ev:  # create the handles
+        for e in evs:
+            e.record()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        still.still_prefill_timed(p, wl.seq_len, x["q"], x["k"], x["v"], x["fmap_w"], x["gate"],
+                                  bufs.out, bufs.sel, bufs.score, bufs.state, bufs.workspace,
+                                  ev[s])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms = {k: sum(ev[s][2 * i].elapsed_time(ev[s][2 * i + 1]) for s in range(args.steps)) / args.steps
+          for i, k in enumerate(still.PREFILL_KERNELS)}
+    work = algorithmic_work(wl, bufs.sel.cpu().numpy())
+    return wl, x, bufs, elapsed, ms, work
+
+
+def run_decode_bench(torch, still, inputs, n_steps):
+    wl = inputs.WORKLOADS["decode_bf16_B64_ctx16K"]
+    p = still.params_for(wl)
+    x = inputs.make_inputs(wl, device="cuda")
+    bufs = still.PrefillBuffers(p, wl.seq_len)
+    still.run_prefill(p, x, bufs)
+    del x["q"]
+    toks = inputs.make_decode_tokens(wl, n_steps + 8, device="cuda")
+    out = torch.empty((wl.batch, wl.n_q_heads, wl.head_dim), dtype=torch.bfloat16, device="cuda")
+    sel = torch.empty((wl.batch, wl.n_kv_heads, still.still_lambda(p)), dtype=torch.int32,
+                      device="cuda")
+    # warm-up on a copy of the state
+    st2 = bufs.state.clone()
+    for s in range(8):
+        still.still_decode_step(p, wl.seq_len + s, toks["q"][s], toks["k"][s], toks["v"][s],
+                                x["fmap_w"], x["gate"], st2, out, sel)
+    torch.cuda.synchronize()
+    del st2
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record()
+    for s in range(n_steps):
+        still.still_decode_step(p, wl.seq_len + s, toks["q"][8 + s], toks["k"][8 + s],
+                                toks["v"][8 + s], x["fmap_w"], x["gate"], bufs.state, out, sel)
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    step_ms = e0.elapsed_time(e1) / n_steps
+    d, units = wl.head_dim, wl.batch * wl.n_kv_heads
+    n_pool = 256  # 255 kept after the prefill, +1 at the boundary of step 0
+    per_unit = (wl.window + n_pool) * 2 * d * 2 + d * d * 4 + d * 4
+    io = (wl.batch * wl.n_q_heads * d * 2) * 2 + wl.batch * wl.n_kv_heads * d * 2 * 2
+    step_bytes = units * per_unit + io
+    return {"workload": wl.name, "batch": wl.batch, "context": wl.seq_len, "steps": n_steps,
+            "ms_per_step": step_ms, "tokens_per_s": wl.batch / (step_ms * 1e-3),
+            "wall_s": wall, "algorithmic_bytes_per_step": step_bytes,
+            "hbm_gbs": step_bytes / (step_ms * 1e-3) / 1e9,
+            "hbm_frac": step_bytes / (step_ms * 1e-3) / 1e9 / PEAK_HBM_GBS}
+
+
+def run_cpu_baseline(wl, x):
+    from oracle import rec
+    cores = len(os.sched_getaffinity(0))
+    units = [(b, kv) for b in range(wl.batch) for kv in range(wl.n_kv_heads)]
+    threads = max(1, min(cores, len(units)))
+    xc = {k: v.cpu() for k, v in x.items()}
+    t0 = time.perf_counter()
+    rec.prefill(xc["q"], xc["k"], xc["v"], xc["fmap_w"], xc["gate"], window=wl.window,
+                chunk=wl.chunk, budget=wl.budget, t_max=wl.t_max, units=units, n_threads=threads)
+    wall = time.perf_counter() - t0
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"value": wl.batch * wl.seq_len / wall, "unit": "tokens/s/layer", "cores": threads,
+            "kind": "oracle",
+            "sample": "whole 16K layer (%d kv-head units, one per thread), float64 recurrent "
+                      "oracle, %.1f s wall on %s" % (len(units), wall, model or "host CPU")}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--decode-steps", type=int, default=64)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one MI355X: the layer runs on a single GPU and --gpus %d is "
+              "not supported" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from linear_attention_still_amd import inputs, still
+
+    wl, x, bufs, elapsed, ms, work = run_prefill_bench(args, torch, still, inputs)
+    tokens = wl.batch * wl.seq_len
+    value = tokens * args.steps / elapsed
+    att_s = ms["attend"] * 1e-3
+    achieved = work["attend"] / att_s / 1e12
+    res = {
+        "metric": METRIC, "value": value, "unit": "tokens/s/layer", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": elapsed * 1e3 / args.steps, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": wl.name, "batch": wl.batch, "seq_len": wl.seq_len,
+                   "q_heads": wl.n_q_heads, "kv_heads": wl.n_kv_heads,
+                   "head_dim": wl.head_dim, "window": wl.window, "chunk": wl.chunk,
+                   "budget": wl.budget, "t_max": wl.t_max},
+        "roofline": {"bound": "mfma", "kernel": "attend", "achieved": achieved,
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None,
+                     "flops_per_launch": work["attend"]},
+        "layer": {"algorithmic_tflop": work["total"] / 1e12,
+                  "tflops": work["total"] / (elapsed / args.steps) / 1e12,
+                  "mfma_frac": work["total"] / (elapsed / args.steps) / 1e12 / PEAK_BF16_TFLOPS},
+        "kernels_ms": ms,
+    }
+    if not args.no_decode:
+        del x, bufs
+        torch.cuda.empty_cache()
+        res["decode"] = run_decode_bench(torch, still, inputs, args.decode_steps)
+    if not args.no_cpu_baseline:
+        xc = inputs.make_inputs(wl, device="cuda")
+        res["cpu_baseline"] = run_cpu_baseline(wl, xc)
+    print(json.dumps(res))
+
+
+if __name__ == "__main__":
+    main()

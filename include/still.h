@@ -133,6 +133,18 @@ int still_prefill(const still_params* p, int64_t seq_len, const void* q, const v
                   int32_t* sel_idx, float* score, void* state, void* workspace,
                   size_t ws_bytes, void* stream);
 
+/* still_prefill with per-kernel timing, for benchmarks: for i < n_pairs it
+ * records events[2i] before and events[2i+1] after the i-th kernel of the
+ * prefill on `stream` (events are caller-created hipEvent_t handles). Kernel
+ * order: 0 F^T copy, 1 score, 2 select, 3 state deltas, 4 state scan,
+ * 5 attention walk, 6 state export; a kernel not launched for a given
+ * length gets its two events recorded back to back. n_pairs <= 7. Same
+ * results and errors as still_prefill. */
+int still_prefill_timed(const still_params* p, int64_t seq_len, const void* q, const void* k,
+                        const void* v, const void* fmap_w, const float* gate, void* out,
+                        int32_t* sel_idx, float* score, void* state, void* workspace,
+                        size_t ws_bytes, void* stream, void* const* events, int n_pairs);
+
 /* Decode one token per sequence at position pos (the state must hold
  * position pos, i.e. pos tokens already processed), [P3 "Delayed
  * Chunk-Level Selection ..."]: the same routing and memory update as the

@@ -19,6 +19,7 @@ inline int64_t align_up(int64_t x) { return (x + kAlign - 1) / kAlign * kAlign; 
 struct Derived {
   int B, Hq, Hkv, G, D, W, C, m, t_max, lam, cap_chunks, R, P, esz;
   float eps, scale;
+  double eps64, scale64;
 };
 
 int derive(const still_params* p, Derived* d) {
@@ -55,6 +56,10 @@ int derive(const still_params* p, Derived* d) {
   d->esz = p->dtype == STILL_DTYPE_F32 ? 4 : 2;
   d->eps = p->eps > 0.f ? p->eps : 1e-6f;
   d->scale = p->sm_scale > 0.f ? p->sm_scale : 1.0f / sqrtf((float)p->head_dim);
+  // float64 paths (score refinement, decode score): the default values are
+  // taken in float64, a caller-given value as the float it was given as
+  d->eps64 = p->eps > 0.f ? (double)p->eps : 1e-6;
+  d->scale64 = p->sm_scale > 0.f ? (double)p->sm_scale : 1.0 / sqrt((double)p->head_dim);
   return STILL_OK;
 }
 
@@ -142,30 +147,56 @@ void set_lds_attr() {
   done = true;
 }
 
+// Optional per-kernel events (still_prefill_timed).
+struct Marks {
+  void* const* ev;
+  int n;
+  hipStream_t s;
+  void at(int i, int which) const {
+    if (ev && i < n) (void)hipEventRecord(reinterpret_cast<hipEvent_t>(ev[2 * i + which]), s);
+  }
+};
+
 template <typename T, int D>
-int launch_prefill(const Derived& d, const Plan& pl, still::PrefillArgs a, hipStream_t s) {
+int launch_prefill(const Derived& d, const Plan& pl, still::PrefillArgs a, hipStream_t s,
+                   const Marks& mk) {
   using namespace still;
   const int nkt = d.C / 16 + (d.W + 14) / 16 + 1;
   const size_t lds_score =
       (size_t)nkt * 16 * (D + Pad<T>::v) * sizeof(T) + (size_t)(2 * d.G * d.C + 4) * 4;
   const size_t lds_sel = (size_t)(d.G * d.W + 8 + d.C) * 8 + (size_t)(3 * d.C + 4) * 4;
-  fmap_transpose_kernel<T, D><<<dim3(d.Hkv), dim3(256), 0, s>>>(a);
-  score_kernel<T, D><<<dim3(pl.T, d.Hkv, d.B), dim3(256), lds_score, s>>>(a);
-  select_kernel<T, D><<<dim3(pl.n_dec + pl.n_pend, d.Hkv, d.B), dim3(256), lds_sel, s>>>(a);
   if (pl.TPW == 2) set_lds_attr<T, D, 2>();
   else set_lds_attr<T, D, 1>();
+  mk.at(0, 0);
+  fmap_transpose_kernel<T, D><<<dim3(d.Hkv), dim3(256), 0, s>>>(a);
+  mk.at(0, 1);
+  mk.at(1, 0);
+  score_kernel<T, D><<<dim3(pl.T, d.Hkv, d.B), dim3(256), lds_score, s>>>(a);
+  mk.at(1, 1);
+  mk.at(2, 0);
+  select_kernel<T, D><<<dim3(pl.n_dec + pl.n_pend, d.Hkv, d.B), dim3(256), lds_sel, s>>>(a);
+  mk.at(2, 1);
+  mk.at(3, 0);
   if (pl.NS > 1)
     state_delta_kernel<T, D><<<dim3(pl.NS - 1, d.Hkv, d.B), dim3(512), Blk<T, D>::bytes, s>>>(a);
+  mk.at(3, 1);
+  mk.at(4, 0);
   state_scan_kernel<<<dim3((D * D + D + 255) / 256, d.Hkv, d.B), dim3(256), 0, s>>>(
       a.dS, pl.NS, D * D + D);
+  mk.at(4, 1);
+  mk.at(5, 0);
   if (pl.TPW == 2)
     attend_kernel<T, D, 2><<<dim3(pl.NS, d.Hkv * pl.nHG, d.B), dim3(512), Blk<T, D>::bytes, s>>>(a);
   else
     attend_kernel<T, D, 1><<<dim3(pl.NS, d.Hkv * pl.nHG, d.B), dim3(512), Blk<T, D>::bytes, s>>>(a);
+  mk.at(5, 1);
   const int ring_lo = pl.L - d.R > 0 ? pl.L - d.R : 0;
   const int n_ring_grp = (pl.L - ring_lo + 15) / 16;
   const int n_pool = pool_count_at(pl.n_dec, d.lam, d.cap_chunks);
-  export_kernel<T, D><<<dim3(n_ring_grp + (n_pool + 15) / 16, d.Hkv, d.B), dim3(256), 0, s>>>(a);
+  const int n_pool_grp = n_pool > 0 ? (n_pool + 15) / 16 : 1;  // >= 1: it writes the position
+  mk.at(6, 0);
+  export_kernel<T, D><<<dim3(n_ring_grp + n_pool_grp, d.Hkv, d.B), dim3(256), 0, s>>>(a);
+  mk.at(6, 1);
   return hipGetLastError() == hipSuccess ? STILL_OK : STILL_EHIP;
 }
 
@@ -173,7 +204,7 @@ template <typename T, int D>
 int launch_decode(const Derived& d, still::DecodeArgs a, hipStream_t s) {
   using namespace still;
   const size_t floats = (size_t)d.G * D * 2 + 16 * D * 4 + 32 + 8 + 32 + (size_t)d.G * D +
-                        2 * (size_t)d.G * D;
+                        256 * (size_t)d.G;
   const size_t lds = floats * 4 + (size_t)(d.C + 8) * 4 + (size_t)(d.G * d.W + d.C + 8) * 8 +
                      (size_t)d.G * a.n_keys_max * 4;
   static bool attr = false;
@@ -240,10 +271,10 @@ int64_t still_workspace_bytes(const still_params* p, int64_t seq_len) {
   return plan(d, seq_len).ws_total;
 }
 
-int still_prefill(const still_params* p, int64_t seq_len, const void* q, const void* k,
-                  const void* v, const void* fmap_w, const float* gate, void* out,
-                  int32_t* sel_idx, float* score, void* state, void* workspace,
-                  size_t ws_bytes, void* stream) {
+static int prefill_impl(const still_params* p, int64_t seq_len, const void* q, const void* k,
+                        const void* v, const void* fmap_w, const float* gate, void* out,
+                        int32_t* sel_idx, float* score, void* state, void* workspace,
+                        size_t ws_bytes, void* stream, void* const* events, int n_pairs) {
   Derived d;
   int rc = derive(p, &d);
   if (rc != STILL_OK) return rc;
@@ -295,16 +326,36 @@ int still_prefill(const still_params* p, int64_t seq_len, const void* q, const v
   a.fp32_out = (p->flags & STILL_FLAG_FP32_OUT) ? 1 : 0;
   a.scale = d.scale;
   a.eps = d.eps;
+  a.scale64 = d.scale64;
+  a.eps64 = d.eps64;
   a.R = d.R;
   fill_state_offsets(SL, &a.st_unit, &a.st_S, &a.st_z, &a.st_pool_k, &a.st_pool_v,
                      &a.st_pool_pos, &a.st_ring_k, &a.st_ring_v, &a.st_ring_phi,
                      &a.st_ring_flag, &a.st_pending, &a.st_meta);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const Marks mk{events, n_pairs, s};
   if (p->dtype == STILL_DTYPE_BF16) {
-    if (d.D == 128) return launch_prefill<bf16, 128>(d, pl, a, s);
-    return launch_prefill<bf16, 64>(d, pl, a, s);
+    if (d.D == 128) return launch_prefill<bf16, 128>(d, pl, a, s, mk);
+    return launch_prefill<bf16, 64>(d, pl, a, s, mk);
   }
-  return launch_prefill<float, 64>(d, pl, a, s);
+  return launch_prefill<float, 64>(d, pl, a, s, mk);
+}
+
+int still_prefill(const still_params* p, int64_t seq_len, const void* q, const void* k,
+                  const void* v, const void* fmap_w, const float* gate, void* out,
+                  int32_t* sel_idx, float* score, void* state, void* workspace,
+                  size_t ws_bytes, void* stream) {
+  return prefill_impl(p, seq_len, q, k, v, fmap_w, gate, out, sel_idx, score, state, workspace,
+                      ws_bytes, stream, nullptr, 0);
+}
+
+int still_prefill_timed(const still_params* p, int64_t seq_len, const void* q, const void* k,
+                        const void* v, const void* fmap_w, const float* gate, void* out,
+                        int32_t* sel_idx, float* score, void* state, void* workspace,
+                        size_t ws_bytes, void* stream, void* const* events, int n_pairs) {
+  if (n_pairs < 0 || n_pairs > 7 || (n_pairs > 0 && !events)) return STILL_EINVAL;
+  return prefill_impl(p, seq_len, q, k, v, fmap_w, gate, out, sel_idx, score, state, workspace,
+                      ws_bytes, stream, events, n_pairs);
 }
 
 int still_decode_step(const still_params* p, int64_t pos, const void* q, const void* k,
@@ -348,6 +399,8 @@ int still_decode_step(const still_params* p, int64_t pos, const void* q, const v
   a.n_keys_max = d.P + (d.W > d.C ? d.W : d.C) + d.W + d.C + 1;
   a.scale = d.scale;
   a.eps = d.eps;
+  a.scale64 = d.scale64;
+  a.eps64 = d.eps64;
   fill_state_offsets(SL, &a.st_unit, &a.st_S, &a.st_z, &a.st_pool_k, &a.st_pool_v,
                      &a.st_pool_pos, &a.st_ring_k, &a.st_ring_v, &a.st_ring_phi,
                      &a.st_ring_flag, &a.st_pending, &a.st_meta);

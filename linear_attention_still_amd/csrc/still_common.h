@@ -136,6 +136,42 @@ __device__ __forceinline__ void split3_frag<float>(const f32x4& x0, const f32x4&
   lo = mid;
 }
 
+// Split fp32 values into a high and a low bf16 part (hi + lo keeps ~16
+// significant bits); for f32 the high part is the value and lo is zero.
+template <typename T>
+__device__ __forceinline__ void split2_frag(const f32x4& x0, const f32x4& x1, Frag<T>& hi,
+                                            Frag<T>& lo);
+template <>
+__device__ __forceinline__ void split2_frag<bf16>(const f32x4& x0, const f32x4& x1,
+                                                  Frag<bf16>& hi, Frag<bf16>& lo) {
+  for (int i = 0; i < 8; ++i) {
+    const float x = i < 4 ? x0[i] : x1[i - 4];
+    const bf16 a = (bf16)x;
+    hi.v[i] = a;
+    lo.v[i] = (bf16)(x - (float)a);
+  }
+}
+template <>
+__device__ __forceinline__ void split2_frag<float>(const f32x4& x0, const f32x4& x1,
+                                                   Frag<float>& hi, Frag<float>& lo) {
+  hi.lo = x0;
+  hi.hi = x1;
+  lo = zero_frag<float>();
+}
+
+// exp / log on float32 data use the accurate library routines; on bf16 data
+// (rounded to 2^-9 anyway) the hardware approximations.
+template <typename T>
+__device__ __forceinline__ float exp_acc(float x) {
+  if constexpr (sizeof(T) == 4) return expf(x);
+  else return __expf(x);
+}
+template <typename T>
+__device__ __forceinline__ float log_acc(float x) {
+  if constexpr (sizeof(T) == 4) return logf(x);
+  else return __logf(x);
+}
+
 template <typename T>
 __device__ __forceinline__ float frag_sumsq(const Frag<T>& f);
 template <>

@@ -37,6 +37,7 @@ struct DecodeArgs {
   int32_t* sel_new;  // [B][Hkv][lam] or null
   int B, Hq, Hkv, G, W, C, m, lam, R, t, boundary, fp32_out, n_keys_max;
   float scale, eps;
+  double scale64, eps64;  // the same parameters for the float64 score
   long st_unit, st_S, st_z, st_pool_k, st_pool_v, st_pool_pos, st_ring_k, st_ring_v,
       st_ring_phi, st_ring_flag, st_pending, st_meta;
 };
@@ -77,7 +78,7 @@ __device__ __forceinline__ void np_map_rows(const T* F, const float* xs, int n, 
     for (int i = 0; i < D; ++i) xn += xs[r * D + i] * xs[r * D + i];
     float ss = 0.f;
     for (int j = 0; j < D; ++j) {
-      const float e = __expf(us[r * D + j] - mx);
+      const float e = expf(us[r * D + j] - mx);
       ss += e * e;
     }
     rowinfo[2 * r] = mx;
@@ -86,7 +87,7 @@ __device__ __forceinline__ void np_map_rows(const T* F, const float* xs, int n, 
   __syncthreads();
   for (int e = tid; e < n * D; e += 256) {
     const int r = e / D;
-    ph[e] = __expf(us[e] - rowinfo[2 * r]) * rowinfo[2 * r + 1];
+    ph[e] = expf(us[e] - rowinfo[2 * r]) * rowinfo[2 * r + 1];
   }
   __syncthreads();
 }
@@ -122,8 +123,8 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   float* red = rowinfo + 32;                    // [8]
   float* headv = red + 8;                       // [8][4]  per-head scalars
   float* nst = headv + 32;                      // [G][D]  state readout
-  float* acc2 = nst + G * D;                    // [2][G][D] partial sums
-  int* ibuf = reinterpret_cast<int*>(acc2 + 2 * G * D);  // [C + 8]
+  float* acc2 = nst + G * D;                    // [256/D][G][D] partial sums
+  int* ibuf = reinterpret_cast<int*>(acc2 + 256 * G);    // [C + 8]
   double* d64 = reinterpret_cast<double*>(ibuf + C + 8);  // [G*W + C + 8]
   float* lw = reinterpret_cast<float*>(d64 + G * W + C + 8);  // [G][n_keys_max]
   const int NK = a.n_keys_max;
@@ -237,7 +238,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
         const double kx = pos == t ? (double)xs[i] : (double)to_f32(kr[i]);
         s += (double)qs[hl * D + i] * kx;
       }
-      lg[hl * W + jj] = (double)a.scale * s;
+      lg[hl * W + jj] = a.scale64 * s;
     }
     __syncthreads();
     double* hs = d64 + G * W;
@@ -253,8 +254,8 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
       }
       const double p = exp(x[n - 1] - mx) / za, pn = zo / za;
       double sc = 0.0;
-      if (p > 0.0) sc += p * log(p / (double)a.eps);
-      if (pn > 0.0) sc += pn * log(pn / (1.0 - (double)a.eps));
+      if (p > 0.0) sc += p * log(p / a.eps64);
+      if (pn > 0.0) sc += pn * log(pn / (1.0 - a.eps64));
       hs[tid] = sc;
     }
     __syncthreads();

@@ -43,6 +43,7 @@ struct PrefillArgs {
   char* state;
   int B, Hq, Hkv, G, L, W, C, m, T, n_dec, lam, cap_chunks, K, NS, nHG, Gs, fp32_out;
   float scale, eps;
+  double scale64, eps64;  // the same parameters for the float64 paths
   long st_unit, st_S, st_z, st_pool_k, st_pool_v, st_pool_pos, st_ring_k, st_ring_v,
       st_ring_phi, st_ring_flag, st_pending, st_meta;
   int R;
@@ -229,7 +230,7 @@ __device__ __forceinline__ double score_f64(const PrefillArgs& a, int b, int kv,
     const T* kr = kg + (size_t)(lo + jj) * D;
     double s = 0.0;
     for (int i = 0; i < D; ++i) s += (double)to_f32(qr[i]) * (double)to_f32(kr[i]);
-    lg[hl * W + jj] = (double)a.scale * s;
+    lg[hl * W + jj] = a.scale64 * s;
   }
   __syncthreads();
   if (tid < G) {
@@ -244,8 +245,8 @@ __device__ __forceinline__ double score_f64(const PrefillArgs& a, int b, int kv,
     }
     const double p = exp(x[n - 1] - mx) / za, pn = zo / za;
     double sc = 0.0;
-    if (p > 0.0) sc += p * log(p / (double)a.eps);
-    if (pn > 0.0) sc += pn * log(pn / (1.0 - (double)a.eps));
+    if (p > 0.0) sc += p * log(p / a.eps64);
+    if (pn > 0.0) sc += pn * log(pn / (1.0 - a.eps64));
     red[tid] = sc;
   }
   __syncthreads();
@@ -355,9 +356,12 @@ __global__ __launch_bounds__(256) void select_kernel(PrefillArgs a) {
 //   Ks   [64][D+pad]      keys, row-major (A fragments of K, B of K^T)
 //   VTs  [D][64+pad]      values transposed, keys permuted (perm_col)
 //   phiK [64][D+4] f32    NP-Map features of the block's keys
-// The linear state S (d_k x d_v, float32) lives in the accumulators of the
-// waves: pair p = (d_v tile vt, d_k 32-block bb) holds tiles (2bb, vt) and
-// (2bb+1, vt).
+//   SP   float32 linear state S (d_k x d_v), stored fragment-linear: pair
+//        p = (d_v tile vt, d_k 32-block bb) holds, per lane, the 8 values
+//        {S[32bb + 4g + i][16vt + r], S[32bb + 16 + 4g + i][16vt + r]},
+//        i.e. the accumulators of tiles (2bb, vt), (2bb+1, vt) and, read as
+//        one fragment, the A operand of S^T for the readout. Wave w owns the
+//        pairs w*PPW .. w*PPW+PPW-1 when folding.
 template <typename T, int D>
 struct Blk {
   static constexpr int KS = D + Pad<T>::v;
@@ -368,9 +372,9 @@ struct Blk {
   static constexpr size_t ks_bytes = 64 * KS * sizeof(T);
   static constexpr size_t vs_bytes = D * VS * sizeof(T);
   static constexpr size_t ps_bytes = 64 * PS * sizeof(float);
-  static constexpr size_t stf_bytes = (size_t)(D / 16) * (D / 32) * 64 * 8 * sizeof(T);
-  static constexpr size_t meta_bytes = 64 * 3 * 4 + D * 4;
-  static constexpr size_t bytes = ks_bytes + vs_bytes + ps_bytes + stf_bytes + meta_bytes;
+  static constexpr size_t sp_bytes = (size_t)NPAIR * 64 * 8 * sizeof(float);
+  static constexpr size_t meta_bytes = 64 * 3 * 4 + D * 8;
+  static constexpr size_t bytes = ks_bytes + vs_bytes + ps_bytes + sp_bytes + meta_bytes;
 };
 
 template <typename T, int D>
@@ -378,23 +382,24 @@ struct BlkPtr {
   T* Ks;
   T* VTs;
   float* phiK;
-  T* STF;
+  float* SP;
   int* kpos;
   int* ksel;
   float* fmask;
-  float* zs;
+  double* zs;  // running z of the walk, float64
   __device__ BlkPtr(char* smem) {
     using B_ = Blk<T, D>;
     Ks = reinterpret_cast<T*>(smem);
     VTs = reinterpret_cast<T*>(smem + B_::ks_bytes);
     phiK = reinterpret_cast<float*>(smem + B_::ks_bytes + B_::vs_bytes);
-    STF = reinterpret_cast<T*>(smem + B_::ks_bytes + B_::vs_bytes + B_::ps_bytes);
-    char* m = smem + B_::ks_bytes + B_::vs_bytes + B_::ps_bytes + B_::stf_bytes;
+    SP = reinterpret_cast<float*>(smem + B_::ks_bytes + B_::vs_bytes + B_::ps_bytes);
+    char* m = smem + B_::ks_bytes + B_::vs_bytes + B_::ps_bytes + B_::sp_bytes;
     kpos = reinterpret_cast<int*>(m);
     ksel = kpos + 64;
     fmask = reinterpret_cast<float*>(ksel + 64);
-    zs = fmask + 64;
+    zs = reinterpret_cast<double*>(fmask + 64);
   }
+  __device__ float* pair(int p) const { return SP + ((size_t)p * 64 + (threadIdx.x & 63)) * 8; }
 };
 
 // Loads 64 keys/values at the given positions (pos < 0: zero row) into Ks and
@@ -460,7 +465,7 @@ __device__ __forceinline__ void np_map_tile(const T* ftg, const Frag<T>* xf, f32
   for (int ft = 0; ft < D / 16; ++ft)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const float e = __expf(out[ft][i] - mx);
+      const float e = exp_acc<T>(out[ft][i] - mx);
       out[ft][i] = e;
       ss += e * e;
     }
@@ -486,91 +491,99 @@ __device__ __forceinline__ void block_phi(const BlkPtr<T, D>& P, const T* ftg) {
     *reinterpret_cast<f32x4*>(P.phiK + (16 * wave + r16) * B_::PS + 16 * ft + 4 * g4) = ph[ft];
 }
 
-// S += phi(K)^T diag(fmask) V over the block (fold into the linear state),
-// with phi split into three bf16 parts so the products keep float32
-// accuracy (values are exact in bf16); z += sum of the same features.
+// The block's contribution phi(K)^T diag(fmask) V to the linear state, for
+// the wave's pairs, in fresh accumulators (so its rounding is relative to the
+// block's own sum, not to the running state); phi is split into three bf16
+// parts so the products keep float32 accuracy (values are exact in bf16).
 template <typename T, int D>
-__device__ __forceinline__ void block_fold(const BlkPtr<T, D>& P, f32x4 (*Sacc)[2]) {
+__device__ __forceinline__ void block_fold_half(const BlkPtr<T, D>& P, int kb2,
+                                                f32x4 (&acc)[Blk<T, D>::PPW][2]) {
   using B_ = Blk<T, D>;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, r16 = lane & 15, g4 = lane >> 4;
 #pragma unroll
   for (int pp = 0; pp < B_::PPW; ++pp) {
     const int p = wave * B_::PPW + pp;
     const int vt = p / (D / 32), bb = p % (D / 32);
+    const Frag<T> bv = ld_frag(P.VTs + (16 * vt + r16) * B_::VS + 32 * kb2 + 8 * g4);
 #pragma unroll
-    for (int kb2 = 0; kb2 < 2; ++kb2) {
-      const Frag<T> bv = ld_frag(P.VTs + (16 * vt + r16) * B_::VS + 32 * kb2 + 8 * g4);
+    for (int e = 0; e < 2; ++e) {
+      const int f = 16 * (2 * bb + e) + r16;
+      f32x4 x0, x1;
 #pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const int f = 16 * (2 * bb + e) + r16;
-        f32x4 x0, x1;
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          const int k0 = 32 * kb2 + 4 * g4 + s, k1 = k0 + 16;
-          x0[s] = P.fmask[k0] * P.phiK[k0 * B_::PS + f];
-          x1[s] = P.fmask[k1] * P.phiK[k1 * B_::PS + f];
-        }
-        Frag<T> hi, mid, lo;
-        split3_frag<T>(x0, x1, hi, mid, lo);
-        mma(Sacc[pp][e], hi, bv);
-        if constexpr (sizeof(T) == 2) {
-          mma(Sacc[pp][e], mid, bv);
-          mma(Sacc[pp][e], lo, bv);
-        }
+      for (int q = 0; q < 4; ++q) {
+        const int k0 = 32 * kb2 + 4 * g4 + q, k1 = k0 + 16;
+        x0[q] = P.fmask[k0] * P.phiK[k0 * B_::PS + f];
+        x1[q] = P.fmask[k1] * P.phiK[k1 * B_::PS + f];
+      }
+      Frag<T> hi, mid, lo;
+      split3_frag<T>(x0, x1, hi, mid, lo);
+      mma(acc[pp][e], hi, bv);
+      if constexpr (sizeof(T) == 2) {
+        mma(acc[pp][e], mid, bv);
+        mma(acc[pp][e], lo, bv);
       }
     }
   }
-  const int tid = threadIdx.x;
-  if (tid < D) {
-    float zsum = 0.f;
-    for (int kk = 0; kk < 64; ++kk) zsum += P.fmask[kk] * P.phiK[kk * B_::PS + tid];
-    P.zs[tid] += zsum;
-  }
 }
 
-// S^T fragments (A operand of the readout S^T phi(Q)^T) from the state
-// accumulators into LDS: STF[vt][bb][lane].
+// Both 32-key halves of the block into fresh accumulators.
 template <typename T, int D>
-__device__ __forceinline__ void write_stf(const BlkPtr<T, D>& P, f32x4 (*Sacc)[2]) {
+__device__ __forceinline__ void block_fold_acc(const BlkPtr<T, D>& P,
+                                               f32x4 (&acc)[Blk<T, D>::PPW][2]) {
+#pragma unroll
+  for (int pp = 0; pp < Blk<T, D>::PPW; ++pp) acc[pp][0] = acc[pp][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+  block_fold_half<T, D>(P, 0, acc);
+  block_fold_half<T, D>(P, 1, acc);
+}
+
+// The block's contribution to z for feature threadIdx.x (< D).
+template <typename T, int D>
+__device__ __forceinline__ float block_zsum(const BlkPtr<T, D>& P) {
   using B_ = Blk<T, D>;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  float zsum = 0.f;
+  for (int kk = 0; kk < 64; ++kk) zsum += P.fmask[kk] * P.phiK[kk * B_::PS + threadIdx.x];
+  return zsum;
+}
+
+// Fold the block into the walk's state in LDS: SP += contribution, z += ...
+template <typename T, int D>
+__device__ __forceinline__ void block_fold(const BlkPtr<T, D>& P) {
+  using B_ = Blk<T, D>;
+  f32x4 acc[B_::PPW][2];
+  block_fold_acc<T, D>(P, acc);
+  const int wave = threadIdx.x >> 6;
 #pragma unroll
   for (int pp = 0; pp < B_::PPW; ++pp) {
-    const int p = wave * B_::PPW + pp;
-    const int vt = p / (D / 32), bb = p % (D / 32);
-    st_frag(P.STF + ((size_t)(vt * (D / 32) + bb) * 64 + lane) * 8, frag_from<T>(Sacc[pp][0], Sacc[pp][1]));
+    float* sp = P.pair(wave * B_::PPW + pp);
+    *reinterpret_cast<f32x4*>(sp) += acc[pp][0];
+    *reinterpret_cast<f32x4*>(sp + 4) += acc[pp][1];
   }
+  if (threadIdx.x < D) P.zs[threadIdx.x] += (double)block_zsum<T, D>(P);
+}
+
+// Super-chunk states in the workspace use the fragment-linear layout of SP
+// (element (p*64 + lane)*8 + slot), so moving them is a straight copy; the
+// exported state is row-major S[d_k][d_v].
+template <typename T, int D>
+__device__ __forceinline__ void load_state(const BlkPtr<T, D>& P, const float* Sfl) {
+  for (int e = threadIdx.x * 4; e < D * D; e += 512 * 4)
+    *reinterpret_cast<f32x4*>(P.SP + e) = *reinterpret_cast<const f32x4*>(Sfl + e);
 }
 
 template <typename T, int D>
-__device__ __forceinline__ void load_state_acc(const float* S, f32x4 (*Sacc)[2]) {
+__device__ __forceinline__ void store_state_rowmajor(const BlkPtr<T, D>& P, float* S) {
   using B_ = Blk<T, D>;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, r16 = lane & 15, g4 = lane >> 4;
 #pragma unroll
   for (int pp = 0; pp < B_::PPW; ++pp) {
     const int p = wave * B_::PPW + pp;
     const int vt = p / (D / 32), bb = p % (D / 32);
+    const float* sp = P.pair(p);
 #pragma unroll
     for (int e = 0; e < 2; ++e)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        Sacc[pp][e][i] = S[(size_t)(16 * (2 * bb + e) + 4 * g4 + i) * D + 16 * vt + r16];
-  }
-}
-
-template <typename T, int D>
-__device__ __forceinline__ void store_state_acc(float* S, f32x4 (*Sacc)[2]) {
-  using B_ = Blk<T, D>;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, r16 = lane & 15, g4 = lane >> 4;
-#pragma unroll
-  for (int pp = 0; pp < B_::PPW; ++pp) {
-    const int p = wave * B_::PPW + pp;
-    const int vt = p / (D / 32), bb = p % (D / 32);
-#pragma unroll
-    for (int e = 0; e < 2; ++e)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        S[(size_t)(16 * (2 * bb + e) + 4 * g4 + i) * D + 16 * vt + r16] = Sacc[pp][e][i];
+        S[(size_t)(32 * bb + 16 * e + 4 * g4 + i) * D + 16 * vt + r16] = sp[4 * e + i];
   }
 }
 
@@ -590,10 +603,13 @@ __global__ __launch_bounds__(512) void state_delta_kernel(PrefillArgs a) {
   const T* vg = reinterpret_cast<const T*>(a.v) + (size_t)unit * a.L * D;
   const uint8_t* sf = a.selflag + (size_t)unit * a.L;
   const T* ftg = reinterpret_cast<const T*>(a.ft) + (size_t)kv * D * D;
-  f32x4 Sacc[Blk<T, D>::PPW][2];
+  using B_ = Blk<T, D>;
+  double sum[B_::PPW][8];  // float64 running sums of the block contributions
 #pragma unroll
-  for (int pp = 0; pp < Blk<T, D>::PPW; ++pp) Sacc[pp][0] = Sacc[pp][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-  if (tid < D) P.zs[tid] = 0.f;
+  for (int pp = 0; pp < B_::PPW; ++pp)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) sum[pp][i] = 0.0;
+  double zsum = 0.0;
   const int lo = full_chunks_before(s * a.K, a.W, a.C) * a.C;
   const int hi = full_chunks_before(s * a.K + a.K, a.W, a.C) * a.C;
   for (int blo = lo; blo < hi; blo += 64) {
@@ -602,12 +618,34 @@ __global__ __launch_bounds__(512) void state_delta_kernel(PrefillArgs a) {
     __syncthreads();
     block_phi<T, D>(P, ftg);
     __syncthreads();
-    block_fold<T, D>(P, Sacc);
+    // each 32-key group lands in the float64 sums on its own: a single
+    // outlier token can make a group's sum ~1e4, where one float32 rounding
+    // is already ~5e-4
+#pragma unroll
+    for (int kb2 = 0; kb2 < 2; ++kb2) {
+      f32x4 acc[B_::PPW][2];
+#pragma unroll
+      for (int pp = 0; pp < B_::PPW; ++pp) acc[pp][0] = acc[pp][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+      block_fold_half<T, D>(P, kb2, acc);
+#pragma unroll
+      for (int pp = 0; pp < B_::PPW; ++pp)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          sum[pp][i] += (double)acc[pp][0][i];
+          sum[pp][4 + i] += (double)acc[pp][1][i];
+        }
+    }
+    if (tid < D) zsum += (double)block_zsum<T, D>(P);
   }
-  __syncthreads();
   float* dst = a.dS + ((size_t)unit * a.NS + s) * (D * D + D);
-  store_state_acc<T, D>(dst, Sacc);
-  if (tid < D) dst[D * D + tid] = P.zs[tid];
+  const int wave = tid >> 6, lane = tid & 63;
+#pragma unroll
+  for (int pp = 0; pp < B_::PPW; ++pp) {
+    float* o = dst + ((size_t)(wave * B_::PPW + pp) * 64 + lane) * 8;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) o[i] = (float)sum[pp][i];
+  }
+  if (tid < D) dst[D * D + tid] = (float)zsum;
 }
 
 // ----------------------------------------------------- 5. state_scan ----
@@ -655,11 +693,9 @@ __global__ __launch_bounds__(512) void attend_kernel(PrefillArgs a) {
   const int n_qt = C / 16;
   const int n_rt = a.Gs * n_qt;
 
-  f32x4 Sacc[B_::PPW][2];
   const float* Sst = a.dS + ((size_t)unit * a.NS + s) * (D * D + D);
-  load_state_acc<T, D>(Sst, Sacc);
-  if (tid < D) P.zs[tid] = Sst[D * D + tid];
-  write_stf<T, D>(P, Sacc);
+  load_state<T, D>(P, Sst);
+  if (tid < D) P.zs[tid] = (double)Sst[D * D + tid];
 
   const int c_begin = s * a.K;
   const int c_end = min(c_begin + a.K, a.T);
@@ -676,7 +712,7 @@ __global__ __launch_bounds__(512) void attend_kernel(PrefillArgs a) {
 
     // per row tile: query fragments, phi(q), state readout
     Frag<T> qf[TPW][D / 32];
-    Frag<T> phq[TPW][D / 32];
+    Frag<T> phq[TPW][D / 32], phl[TPW][D / 32];  // phi(q) as hi + lo parts
     f32x4 O[TPW][D / 16];
     float mrun[TPW], lrun[TPW], lgate[TPW];
     int tq[TPW], hq[TPW];
@@ -699,21 +735,31 @@ __global__ __launch_bounds__(512) void attend_kernel(PrefillArgs a) {
 #pragma unroll
       for (int ft = 0; ft < D / 16; ++ft)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) dz += ph[ft][i] * P.zs[16 * ft + 4 * g4 + i];
+        for (int i = 0; i < 4; ++i) dz += ph[ft][i] * (float)P.zs[16 * ft + 4 * g4 + i];
       dz = sum_over_g(dz);
 #pragma unroll
-      for (int bb = 0; bb < D / 32; ++bb) phq[rr][bb] = frag_from<T>(ph[2 * bb], ph[2 * bb + 1]);
+      for (int bb = 0; bb < D / 32; ++bb) split2_frag<T>(ph[2 * bb], ph[2 * bb + 1], phq[rr][bb], phl[rr][bb]);
       const float g = a.gate[h];
-      lgate[rr] = g > 0.f ? __logf(g) : STILL_NEG_INF;
+      lgate[rr] = g > 0.f ? log_acc<T>(g) : STILL_NEG_INF;
 #pragma unroll
       for (int dt = 0; dt < D / 16; ++dt) {
         O[rr][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int bb = 0; bb < D / 32; ++bb)
-          mma(O[rr][dt], ld_frag(P.STF + ((size_t)(dt * (D / 32) + bb) * 64 + lane) * 8), phq[rr][bb]);
+        for (int bb = 0; bb < D / 32; ++bb) {
+          // S^T phi(q) to ~2^-16 relative: hi*hi + lo*hi + hi*lo
+          const float* sp = P.pair(dt * (D / 32) + bb);
+          Frag<T> sh, sl;
+          split2_frag<T>(*reinterpret_cast<const f32x4*>(sp),
+                         *reinterpret_cast<const f32x4*>(sp + 4), sh, sl);
+          mma(O[rr][dt], sh, phq[rr][bb]);
+          if constexpr (sizeof(T) == 2) {
+            mma(O[rr][dt], sl, phq[rr][bb]);
+            mma(O[rr][dt], sh, phl[rr][bb]);
+          }
+        }
       }
       if (g > 0.f && dz > 0.f) {
-        mrun[rr] = __logf(g * dz);
+        mrun[rr] = log_acc<T>(g * dz);
         lrun[rr] = g4 == 0 ? 1.f : 0.f;
         const float inv = 1.f / dz;
 #pragma unroll
@@ -762,10 +808,16 @@ __global__ __launch_bounds__(512) void attend_kernel(PrefillArgs a) {
             wt[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int bb = 0; bb < D / 32; ++bb) {
+              // <phi(k), phi(q)> to ~2^-16 relative: hi*hi + lo*hi + hi*lo
               const float* pr = P.phiK + (16 * kt + r16) * B_::PS + 32 * bb + 4 * g4;
-              mma(wt[kt], frag_from<T>(*reinterpret_cast<const f32x4*>(pr),
-                                       *reinterpret_cast<const f32x4*>(pr + 16)),
-                  phq[rr][bb]);
+              Frag<T> kh, kl;
+              split2_frag<T>(*reinterpret_cast<const f32x4*>(pr),
+                             *reinterpret_cast<const f32x4*>(pr + 16), kh, kl);
+              mma(wt[kt], kh, phq[rr][bb]);
+              if constexpr (sizeof(T) == 2) {
+                mma(wt[kt], kl, phq[rr][bb]);
+                mma(wt[kt], kh, phl[rr][bb]);
+              }
             }
           }
         }
@@ -782,7 +834,7 @@ __global__ __launch_bounds__(512) void attend_kernel(PrefillArgs a) {
                 lw = st[kt][i] * a.scale;
               } else if (la_blk) {
                 const float w = wt[kt][i];
-                lw = w > 0.f ? lgate[rr] + __logf(w) : STILL_NEG_INF;
+                lw = w > 0.f ? lgate[rr] + log_acc<T>(w) : STILL_NEG_INF;
               }
             }
             st[kt][i] = lw;
@@ -791,7 +843,7 @@ __global__ __launch_bounds__(512) void attend_kernel(PrefillArgs a) {
         mx = max_over_g(mx);
         const float mn = fmaxf(mrun[rr], mx);
         // rows with nothing visible so far keep m = -inf, O = 0, l = 0
-        const float al = mrun[rr] == STILL_NEG_INF ? 0.f : __expf(mrun[rr] - mn);
+        const float al = mrun[rr] == STILL_NEG_INF ? 0.f : exp_acc<T>(mrun[rr] - mn);
         mrun[rr] = mn;
         float lsum = 0.f;
         f32x4 pv[4];
@@ -800,21 +852,30 @@ __global__ __launch_bounds__(512) void attend_kernel(PrefillArgs a) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const float lw = st[kt][i];
-            pv[kt][i] = lw == STILL_NEG_INF ? 0.f : __expf(lw - mn);
+            pv[kt][i] = lw == STILL_NEG_INF ? 0.f : exp_acc<T>(lw - mn);
           }
-        const Frag<T> pf0 = frag_from<T>(pv[0], pv[1]);
-        const Frag<T> pf1 = frag_from<T>(pv[2], pv[3]);
-        // the running sum uses the rounded weights the product uses
-        lsum = frag_sum(pf0) + frag_sum(pf1);
+        // weights as hi + lo bf16 parts (float32 as is): the products and the
+        // running sum see the same weights, to ~2^-16 relative
+        Frag<T> ph0, pl0, ph1, pl1;
+        split2_frag<T>(pv[0], pv[1], ph0, pl0);
+        split2_frag<T>(pv[2], pv[3], ph1, pl1);
+        lsum = frag_sum(ph0) + frag_sum(ph1);
+        if constexpr (sizeof(T) == 2) lsum += frag_sum(pl0) + frag_sum(pl1);
         lrun[rr] = lrun[rr] * al + lsum;
 #pragma unroll
         for (int dt = 0; dt < D / 16; ++dt) {
           O[rr][dt] *= al;
-          mma(O[rr][dt], ld_frag(P.VTs + (16 * dt + r16) * B_::VS + 8 * g4), pf0);
-          mma(O[rr][dt], ld_frag(P.VTs + (16 * dt + r16) * B_::VS + 32 + 8 * g4), pf1);
+          const Frag<T> v0 = ld_frag(P.VTs + (16 * dt + r16) * B_::VS + 8 * g4);
+          const Frag<T> v1 = ld_frag(P.VTs + (16 * dt + r16) * B_::VS + 32 + 8 * g4);
+          mma(O[rr][dt], v0, ph0);
+          mma(O[rr][dt], v1, ph1);
+          if constexpr (sizeof(T) == 2) {
+            mma(O[rr][dt], v0, pl0);
+            mma(O[rr][dt], v1, pl1);
+          }
         }
       }
-      if (fold && !is_pool && blo < fold_hi) block_fold<T, D>(P, Sacc);
+      if (fold && !is_pool && blo < fold_hi) block_fold<T, D>(P);
     }
 
     // outputs
@@ -840,12 +901,8 @@ __global__ __launch_bounds__(512) void attend_kernel(PrefillArgs a) {
     if (c == a.T - 1 && hg == 0) {
       __syncthreads();
       char* st = a.state + (size_t)unit * a.st_unit;
-      store_state_acc<T, D>(reinterpret_cast<float*>(st + a.st_S), Sacc);
-      if (tid < D) reinterpret_cast<float*>(st + a.st_z)[tid] = P.zs[tid];
-    }
-    if (fold) {
-      __syncthreads();
-      write_stf<T, D>(P, Sacc);
+      store_state_rowmajor<T, D>(P, reinterpret_cast<float*>(st + a.st_S));
+      if (tid < D) reinterpret_cast<float*>(st + a.st_z)[tid] = (float)P.zs[tid];
     }
   }
 }
@@ -886,7 +943,7 @@ __global__ __launch_bounds__(256) void export_kernel(PrefillArgs a) {
       for (int i = 0; i < D; ++i) xn += xs[tid][i] * xs[tid][i];
       float ss = 0.f;
       for (int j = 0; j < D; ++j) {
-        const float e = __expf(us[tid][j] - mx);
+        const float e = exp_acc<T>(us[tid][j] - mx);
         ss += e * e;
       }
       red[tid][0] = mx;
@@ -903,7 +960,7 @@ __global__ __launch_bounds__(256) void export_kernel(PrefillArgs a) {
       const int slot = p % R;
       rk[(size_t)slot * D + j] = kg[(size_t)p * D + j];
       rv[(size_t)slot * D + j] = vg[(size_t)p * D + j];
-      rp[(size_t)slot * D + j] = from_f32<T>(__expf(us[r][j] - red[r][0]) * red[r][1]);
+      rp[(size_t)slot * D + j] = from_f32<T>(exp_acc<T>(us[r][j] - red[r][0]) * red[r][1]);
       if (j == 0) rf[slot] = a.selflag[(size_t)unit * L + p];
     }
     return;

@@ -70,6 +70,8 @@ def lib() -> ctypes.CDLL:
         L.still_workspace_bytes.restype = I64
         L.still_prefill.argtypes = [pp, I64] + [P] * 10 + [ctypes.c_size_t, P]
         L.still_prefill.restype = I32
+        L.still_prefill_timed.argtypes = [pp, I64] + [P] * 10 + [ctypes.c_size_t, P, P, I32]
+        L.still_prefill_timed.restype = I32
         L.still_decode_step.argtypes = [pp, I64] + [P] * 9 + [ctypes.c_size_t, P]
         L.still_decode_step.restype = I32
         L.still_status_str.argtypes = [I32]
@@ -79,8 +81,10 @@ def lib() -> ctypes.CDLL:
 
 
 def make_params(*, dtype: str, batch: int, n_q_heads: int, n_kv_heads: int, head_dim: int,
-                window: int, chunk: int, budget: int, t_max: int, eps: float = 1e-6,
+                window: int, chunk: int, budget: int, t_max: int, eps: float = 0.0,
                 sm_scale: float = 0.0, fp32_out: bool = False) -> still_params:
+    """eps <= 0 and sm_scale <= 0 select the library defaults (1e-6 and
+    1/sqrt(head_dim))."""
     return still_params(STILL_ABI_VERSION,
                         STILL_DTYPE_F32 if dtype in ("f32", torch.float32) else STILL_DTYPE_BF16,
                         batch, n_q_heads, n_kv_heads, head_dim, window, chunk, budget, t_max,
@@ -150,6 +154,26 @@ def still_prefill(p: still_params, seq_len: int, q, k, v, fmap_w, gate, out, sel
                              _stream(stream))
     if rc != STILL_OK:
         raise StillError("still_prefill", rc)
+
+
+PREFILL_KERNELS = ("fmap_transpose", "score", "select", "state_delta", "state_scan", "attend",
+                   "export")
+
+
+def still_prefill_timed(p: still_params, seq_len: int, q, k, v, fmap_w, gate, out, sel_idx,
+                        score, state, workspace, events, stream=None) -> None:
+    """events: flat list of 2*n torch.cuda.Event (enable_timing=True), already
+    recorded once so their handles exist; kernel i is bracketed by
+    events[2i], events[2i+1]."""
+    n = len(events) // 2
+    arr = (ctypes.c_void_p * (2 * n))(*[ctypes.c_void_p(e.cuda_event) for e in events])
+    rc = lib().still_prefill_timed(ctypes.byref(p), int(seq_len), _ptr(q), _ptr(k), _ptr(v),
+                                   _ptr(fmap_w), _ptr(gate), _ptr(out), _ptr(sel_idx),
+                                   _ptr(score), _ptr(state), _ptr(workspace),
+                                   workspace.numel() * workspace.element_size(),
+                                   _stream(stream), arr, n)
+    if rc != STILL_OK:
+        raise StillError("still_prefill_timed", rc)
 
 
 def still_decode_step(p: still_params, pos: int, q, k, v, fmap_w, gate, state, out,

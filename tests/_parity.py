@@ -72,11 +72,25 @@ def check_outputs(y_gpu: np.ndarray, y_ref: np.ndarray, dtype: str, out_fp32: bo
         assert rel <= 1e-2, (what, rel)
 
 
+# The state is float32 and its entries reach 1e4 or more (sums over
+# thousands of tokens, 8x-norm tokens contribute products of ~1e4). float32
+# storage alone has an ulp of ~4e-3 at 3.9e4, and the float32 feature logits
+# x F of an 8x-norm key carry ~2e-6 absolute error, i.e. ~2e-6 relative error
+# in phi(k) and ~2e-2 on one product of 1e4. The state bar is therefore the
+# max-abs bar at unit scale plus 16 float32 ulps of the reference value.
+STATE_RTOL = 16 * 2.0 ** -23
+
+
 def check_state(got: np.ndarray, ref: np.ndarray, dtype: str, what=""):
-    err = float(np.abs(got.astype(np.float64) - ref).max()) if ref.size else 0.0
-    print("    %s max_abs=%.3e (|ref| max %.3g)" % (what, err, float(np.abs(ref).max()) if ref.size else 0),
-          flush=True)
-    assert err <= (1e-4 if dtype == "f32" else 2e-2), (what, err)
+    atol = 1e-4 if dtype == "f32" else 2e-2
+    diff = np.abs(got.astype(np.float64) - ref)
+    err = float(diff.max()) if ref.size else 0.0
+    excess = float((diff - STATE_RTOL * np.abs(ref)).max()) if ref.size else 0.0
+    rel = float(np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-30)) if ref.size else 0.0
+    print("    %s max_abs=%.3e (|ref| max %.3g) beyond-rtol %.3e rel_l2=%.2e"
+          % (what, err, float(np.abs(ref).max()) if ref.size else 0, excess, rel), flush=True)
+    assert excess <= atol, (what, err, excess)
+    assert rel <= (1e-6 if dtype == "f32" else 1e-2), (what, rel)
 
 
 def unit_rows(wl: Workload, units: Sequence[Tuple[int, int]]):
