@@ -61,6 +61,33 @@ def algorithmic_work(wl, sel):
             "update": update, "sum_A": sum_A}
 
 
+HERE = os.path.dirname(os.path.abspath(__file__))
+TRAFFIC_SOURCES = ("linear_attention_still_amd/csrc/still_prefill.hip",
+                   "linear_attention_still_amd/csrc/still_common.h",
+                   "linear_attention_still_amd/csrc/still_api.hip")
+
+
+def measured_traffic(kernel="attend_kernel"):
+    """HBM bytes per launch from the committed rocprofv3 counter summary,
+    or None when the kernel sources changed since the counters were taken."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in TRAFFIC_SOURCES:
+        with open(os.path.join(HERE, f), "rb") as fh:
+            h.update(fh.read())
+    sha = h.hexdigest()[:16]
+    try:
+        with open(os.path.join(HERE, "profiles", "prefill_llama8b_L16K.md")) as fh:
+            for line in fh:
+                if line.startswith("traffic %s " % kernel):
+                    kv = dict(x.split("=") for x in line.split()[2:])
+                    if kv.get("source_sha256") == sha:
+                        return int(kv["bytes_per_launch"])
+    except OSError:
+        pass
+    return None
+
+
 def run_prefill_bench(args, torch, still, inputs):
     wl = inputs.WORKLOADS["llama8b_bf16_L16K"]
     p = still.params_for(wl)
@@ -162,12 +189,23 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=64)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--copy-bytes", type=int, default=0,
+                    help="only run a plain device copy of this many bytes (HBM counter "
+                         "calibration for rocprofv3 --pmc)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one MI355X: the layer runs on a single GPU and --gpus %d is "
               "not supported" % args.gpus, file=sys.stderr)
         sys.exit(2)
     import torch
+    if args.copy_bytes > 0:
+        src = torch.ones(args.copy_bytes, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": args.copy_bytes, "launches": 3}))
+        return
     from linear_attention_still_amd import inputs, still
 
     wl, x, bufs, elapsed, ms, work = run_prefill_bench(args, torch, still, inputs)
@@ -186,7 +224,7 @@ def main():
                    "budget": wl.budget, "t_max": wl.t_max},
         "roofline": {"bound": "mfma", "kernel": "attend", "achieved": achieved,
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None,
+                     "frac": achieved / PEAK_BF16_TFLOPS, "traffic": measured_traffic(),
                      "flops_per_launch": work["attend"]},
         "layer": {"algorithmic_tflop": work["total"] / 1e12,
                   "tflops": work["total"] / (elapsed / args.steps) / 1e12,
