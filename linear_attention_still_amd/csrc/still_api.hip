@@ -98,12 +98,12 @@ Plan plan(const Derived& d, int64_t L) {
   pl.T = (int)((L + d.C - 1) / d.C);
   pl.n_dec = (int)((L - 1) / d.C);
   pl.n_pend = (int)(L - (int64_t)pl.n_dec * d.C);
-  int gs = 256 / d.C;
+  int gs = 128 / d.C;  // at most 8 row tiles of 16 queries per workgroup
+  if (gs < 1) gs = 1;
   if (gs > d.G) gs = d.G;
   pl.Gs = gs;
   pl.nHG = d.G / gs;
-  const int rows16 = gs * d.C / 16;
-  pl.TPW = rows16 > 8 ? 2 : 1;
+  pl.TPW = 1;
   // chunks walked per workgroup: enough workgroups to fill the chip
   const int64_t units = (int64_t)d.B * d.Hkv * pl.nHG;
   int K = (int)((int64_t)pl.T * units / 1024);
@@ -134,11 +134,11 @@ Plan plan(const Derived& d, int64_t L) {
 
 bool misaligned(const void* p) { return ((uintptr_t)p & 15u) != 0; }
 
-template <typename T, int D, int TPW>
+template <typename T, int D>
 void set_lds_attr() {
   static bool done = false;
   if (done) return;
-  (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&still::attend_kernel<T, D, TPW>),
+  (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&still::attend_kernel<T, D>),
                       hipFuncAttributeMaxDynamicSharedMemorySize,
                       (int)still::Blk<T, D>::bytes);
   (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&still::state_delta_kernel<T, D>),
@@ -165,8 +165,7 @@ int launch_prefill(const Derived& d, const Plan& pl, still::PrefillArgs a, hipSt
   const size_t lds_score =
       (size_t)nkt * 16 * (D + Pad<T>::v) * sizeof(T) + (size_t)(2 * d.G * d.C + 4) * 4;
   const size_t lds_sel = (size_t)(d.G * d.W + 8 + d.C) * 8 + (size_t)(3 * d.C + 4) * 4;
-  if (pl.TPW == 2) set_lds_attr<T, D, 2>();
-  else set_lds_attr<T, D, 1>();
+  set_lds_attr<T, D>();
   mk.at(0, 0);
   fmap_transpose_kernel<T, D><<<dim3(d.Hkv), dim3(256), 0, s>>>(a);
   mk.at(0, 1);
@@ -185,10 +184,7 @@ int launch_prefill(const Derived& d, const Plan& pl, still::PrefillArgs a, hipSt
       a.dS, pl.NS, D * D + D);
   mk.at(4, 1);
   mk.at(5, 0);
-  if (pl.TPW == 2)
-    attend_kernel<T, D, 2><<<dim3(pl.NS, d.Hkv * pl.nHG, d.B), dim3(512), Blk<T, D>::bytes, s>>>(a);
-  else
-    attend_kernel<T, D, 1><<<dim3(pl.NS, d.Hkv * pl.nHG, d.B), dim3(512), Blk<T, D>::bytes, s>>>(a);
+  attend_kernel<T, D><<<dim3(pl.NS * d.Hkv * pl.nHG * d.B), dim3(512), Blk<T, D>::bytes, s>>>(a);
   mk.at(5, 1);
   const int ring_lo = pl.L - d.R > 0 ? pl.L - d.R : 0;
   const int n_ring_grp = (pl.L - ring_lo + 15) / 16;
@@ -280,6 +276,8 @@ static int prefill_impl(const still_params* p, int64_t seq_len, const void* q, c
   if (rc != STILL_OK) return rc;
   if (seq_len < 1 || seq_len > ((int64_t)1 << 30)) return STILL_EINVAL;
   if ((int64_t)d.B * d.Hq * seq_len * d.D > ((int64_t)1 << 40)) return STILL_EINVAL;
+  // one (batch row, head) sequence is addressed with 32-bit byte offsets
+  if (seq_len * d.D * (int64_t)d.esz >= ((int64_t)1 << 31)) return STILL_EUNSUPPORTED;
   if (!q || !k || !v || !fmap_w || !gate || !out || !state || !workspace) return STILL_EINVAL;
   const int n_dec = (int)((seq_len - 1) / d.C);
   if (!sel_idx && n_dec > 0 && d.lam > 0) return STILL_EINVAL;

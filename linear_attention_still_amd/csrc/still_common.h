@@ -26,11 +26,18 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 #define STILL_NEG_INF (-__builtin_huge_valf())
 
+typedef _Float16 f16;
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+
 template <typename T>
 struct Frag;
 template <>
 struct Frag<bf16> {
   bf16x8 v;
+};
+template <>
+struct Frag<f16> {
+  f16x8 v;
 };
 template <>
 struct Frag<float> {
@@ -39,6 +46,10 @@ struct Frag<float> {
 
 __device__ __forceinline__ void mma(f32x4& c, const Frag<bf16>& a, const Frag<bf16>& b) {
   c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v, b.v, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ void mma(f32x4& c, const Frag<f16>& a, const Frag<f16>& b) {
+  c = __builtin_amdgcn_mfma_f32_16x16x32_f16(a.v, b.v, c, 0, 0, 0);
 }
 
 __device__ __forceinline__ void mma(f32x4& c, const Frag<float>& a, const Frag<float>& b) {
@@ -58,14 +69,50 @@ __device__ __forceinline__ Frag<bf16> ld_frag(const bf16* p) {
   f.v = *reinterpret_cast<const bf16x8*>(p);
   return f;
 }
+__device__ __forceinline__ Frag<f16> ld_frag(const f16* p) {
+  Frag<f16> f;
+  f.v = *reinterpret_cast<const f16x8*>(p);
+  return f;
+}
 __device__ __forceinline__ Frag<float> ld_frag(const float* p) {
   Frag<float> f;
   f.lo = *reinterpret_cast<const f32x4*>(p);
   f.hi = *reinterpret_cast<const f32x4*>(p + 4);
   return f;
 }
+// Buffer-resource loads: the lane-dependent part of an address is a 32-bit
+// VGPR offset and the uniform part an SGPR offset, so unrolled loops over
+// uniform offsets need no per-iteration 64-bit address registers. Reads at
+// or past `bytes` return zero (raw buffer range check).
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
+}
+template <typename T>
+__device__ __forceinline__ Frag<T> ld_frag_buf(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff);
+template <>
+__device__ __forceinline__ Frag<bf16> ld_frag_buf<bf16>(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  Frag<bf16> f;
+  f.v = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+  return f;
+}
+template <>
+__device__ __forceinline__ Frag<float> ld_frag_buf<float>(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  Frag<float> f;
+  f.lo = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+  f.hi = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff + 16, 0));
+  return f;
+}
+__device__ __forceinline__ uint4 ld_u4_buf(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+  return uint4{x[0], x[1], x[2], x[3]};
+}
+
 __device__ __forceinline__ void st_frag(bf16* p, const Frag<bf16>& f) {
   *reinterpret_cast<bf16x8*>(p) = f.v;
+}
+__device__ __forceinline__ void st_frag(f16* p, const Frag<f16>& f) {
+  *reinterpret_cast<f16x8*>(p) = f.v;
 }
 __device__ __forceinline__ void st_frag(float* p, const Frag<float>& f) {
   *reinterpret_cast<f32x4*>(p) = f.lo;
@@ -78,6 +125,12 @@ template <>
 __device__ __forceinline__ Frag<bf16> zero_frag<bf16>() {
   Frag<bf16> f;
   for (int i = 0; i < 8; ++i) f.v[i] = (bf16)0.0f;
+  return f;
+}
+template <>
+__device__ __forceinline__ Frag<f16> zero_frag<f16>() {
+  Frag<f16> f;
+  for (int i = 0; i < 8; ++i) f.v[i] = (f16)0.0f;
   return f;
 }
 template <>
@@ -96,6 +149,13 @@ __device__ __forceinline__ Frag<bf16> frag_from<bf16>(const f32x4& x0, const f32
   Frag<bf16> f;
   f.v[0] = (bf16)x0[0]; f.v[1] = (bf16)x0[1]; f.v[2] = (bf16)x0[2]; f.v[3] = (bf16)x0[3];
   f.v[4] = (bf16)x1[0]; f.v[5] = (bf16)x1[1]; f.v[6] = (bf16)x1[2]; f.v[7] = (bf16)x1[3];
+  return f;
+}
+template <>
+__device__ __forceinline__ Frag<f16> frag_from<f16>(const f32x4& x0, const f32x4& x1) {
+  Frag<f16> f;
+  f.v[0] = (f16)x0[0]; f.v[1] = (f16)x0[1]; f.v[2] = (f16)x0[2]; f.v[3] = (f16)x0[3];
+  f.v[4] = (f16)x1[0]; f.v[5] = (f16)x1[1]; f.v[6] = (f16)x1[2]; f.v[7] = (f16)x1[3];
   return f;
 }
 template <>
@@ -152,6 +212,16 @@ __device__ __forceinline__ void split2_frag<bf16>(const f32x4& x0, const f32x4& 
   }
 }
 template <>
+__device__ __forceinline__ void split2_frag<f16>(const f32x4& x0, const f32x4& x1,
+                                                 Frag<f16>& hi, Frag<f16>& lo) {
+  for (int i = 0; i < 8; ++i) {
+    const float x = i < 4 ? x0[i] : x1[i - 4];
+    const f16 a = (f16)x;
+    hi.v[i] = a;
+    lo.v[i] = (f16)(x - (float)a);
+  }
+}
+template <>
 __device__ __forceinline__ void split2_frag<float>(const f32x4& x0, const f32x4& x1,
                                                    Frag<float>& hi, Frag<float>& lo) {
   hi.lo = x0;
@@ -195,10 +265,29 @@ __device__ __forceinline__ float frag_sum(const Frag<bf16>& f) {
   for (int i = 0; i < 8; ++i) s += (float)f.v[i];
   return s;
 }
+__device__ __forceinline__ float frag_sum(const Frag<f16>& f) {
+  float s = 0.f;
+  for (int i = 0; i < 8; ++i) s += (float)f.v[i];
+  return s;
+}
 __device__ __forceinline__ float frag_sum(const Frag<float>& f) {
   return (f.lo[0] + f.lo[1]) + (f.lo[2] + f.lo[3]) + (f.hi[0] + f.hi[1]) + (f.hi[2] + f.hi[3]);
 }
 
+// Type of the operands whose range fits binary16 (softmax weights, values,
+// NP-Map feature parts): fp16 next to bf16 data (3 more significand bits;
+// bf16 -> fp16 is exact for values in fp16's normal range), float next to
+// float data.
+template <typename T>
+struct HalfOf {
+  typedef f16 type;
+};
+template <>
+struct HalfOf<float> {
+  typedef float type;
+};
+
+__device__ __forceinline__ float to_f32(f16 x) { return (float)x; }
 __device__ __forceinline__ float to_f32(bf16 x) { return (float)x; }
 __device__ __forceinline__ float to_f32(float x) { return x; }
 template <typename T>
@@ -207,6 +296,8 @@ template <>
 __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return (bf16)x; }
 template <>
 __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+template <>
+__device__ __forceinline__ f16 from_f32<f16>(float x) { return (f16)x; }
 
 // Sum / max over the four lanes sharing r (lanes r, r+16, r+32, r+48).
 __device__ __forceinline__ float sum_over_g(float x) {

@@ -353,88 +353,135 @@ __global__ __launch_bounds__(256) void select_kernel(PrefillArgs a) {
 
 // ----------------------------------------- shared block machinery (4-6) ----
 // A workgroup of 8 waves streams 64-key blocks through LDS:
-//   Ks   [64][D+pad]      keys, row-major (A fragments of K, B of K^T)
-//   VTs  [D][64+pad]      values transposed, keys permuted (perm_col)
-//   phiK [64][D+4] f32    NP-Map features of the block's keys
-//   SP   float32 linear state S (d_k x d_v), stored fragment-linear: pair
-//        p = (d_v tile vt, d_k 32-block bb) holds, per lane, the 8 values
-//        {S[32bb + 4g + i][16vt + r], S[32bb + 16 + 4g + i][16vt + r]},
-//        i.e. the accumulators of tiles (2bb, vt), (2bb+1, vt) and, read as
-//        one fragment, the A operand of S^T for the readout. Wave w owns the
-//        pairs w*PPW .. w*PPW+PPW-1 when folding.
+//   Ks    [64][D+pad] T         keys, row-major (A fragments of K)
+//   VTs   [D][64+pad] H         values transposed, keys permuted (perm_col);
+//                               H = fp16 next to bf16 data, float otherwise
+//   WF    [4 kt][D/32][hi,lo]   NP-Map features of the block's keys as H
+//                               A fragments (rows = keys) of <phi(k),phi(q)>
+//   SP    float32 linear state S (d_k x d_v), fragment-linear: pair
+//         p = (d_v tile vt, d_k 32-block bb) holds, per lane, the 8 values
+//         {S[32bb + 4g + i][16vt + r], S[32bb + 16 + 4g + i][16vt + r]},
+//         i.e. the accumulators of tiles (2bb, vt), (2bb+1, vt) and, read as
+//         one fragment, the A operand of S^T for the readout.
+//   stat  per-key softmax statistics of the feature map
+// At the start of a chunk the first region (Ks..WF) holds the state split
+// into hi/lo bf16 fragments for the readout (RS).
 template <typename T, int D>
 struct Blk {
+  typedef typename HalfOf<T>::type H;
   static constexpr int KS = D + Pad<T>::v;
-  static constexpr int VS = 64 + Pad<T>::v;
-  static constexpr int PS = D + 4;
+  static constexpr int VS = 64 + Pad<H>::v;
+  static constexpr int NFT = D / 16;  // feature (and d_v) tiles
   static constexpr int NPAIR = (D / 16) * (D / 32);
-  static constexpr int PPW = NPAIR / 8;
   static constexpr size_t ks_bytes = 64 * KS * sizeof(T);
-  static constexpr size_t vs_bytes = D * VS * sizeof(T);
-  static constexpr size_t ps_bytes = 64 * PS * sizeof(float);
+  static constexpr size_t vs_bytes = (size_t)D * VS * sizeof(H);
+  static constexpr size_t wf_bytes = (size_t)4 * (D / 32) * 2 * 64 * 8 * sizeof(H);
+  static constexpr size_t rs_bytes = (size_t)NPAIR * 2 * 64 * 8 * sizeof(T);
+  static constexpr size_t lo_bytes =
+      (ks_bytes + vs_bytes + wf_bytes > rs_bytes ? ks_bytes + vs_bytes + wf_bytes : rs_bytes);
   static constexpr size_t sp_bytes = (size_t)NPAIR * 64 * 8 * sizeof(float);
-  static constexpr size_t meta_bytes = 64 * 3 * 4 + D * 8;
-  static constexpr size_t bytes = ks_bytes + vs_bytes + ps_bytes + sp_bytes + meta_bytes;
+  static constexpr size_t stat_bytes = (8 * 64 * 2 + 64 * 3) * 4;
+  static constexpr size_t meta_bytes = 64 * 4 + 16 + D * 8;
+  static constexpr size_t bytes = lo_bytes + sp_bytes + stat_bytes + meta_bytes;
 };
 
 template <typename T, int D>
 struct BlkPtr {
+  typedef typename HalfOf<T>::type H;
   T* Ks;
-  T* VTs;
-  float* phiK;
+  H* VTs;
+  H* WF;
+  T* RS;
   float* SP;
-  int* kpos;
-  int* ksel;
-  float* fmask;
+  float* kmax;   // [8][64] per-wave partial max
+  float* ksum;   // [8][64] per-wave partial sum of squares
+  float* kstat;  // [3][64]: max, scale, |k|^2
+  float* fmask;  // [64]
+  uint32_t* selw;
   double* zs;  // running z of the walk, float64
   __device__ BlkPtr(char* smem) {
     using B_ = Blk<T, D>;
     Ks = reinterpret_cast<T*>(smem);
-    VTs = reinterpret_cast<T*>(smem + B_::ks_bytes);
-    phiK = reinterpret_cast<float*>(smem + B_::ks_bytes + B_::vs_bytes);
-    SP = reinterpret_cast<float*>(smem + B_::ks_bytes + B_::vs_bytes + B_::ps_bytes);
-    char* m = smem + B_::ks_bytes + B_::vs_bytes + B_::ps_bytes + B_::sp_bytes;
-    kpos = reinterpret_cast<int*>(m);
-    ksel = kpos + 64;
-    fmask = reinterpret_cast<float*>(ksel + 64);
-    zs = reinterpret_cast<double*>(fmask + 64);
+    VTs = reinterpret_cast<H*>(smem + B_::ks_bytes);
+    WF = reinterpret_cast<H*>(smem + B_::ks_bytes + B_::vs_bytes);
+    RS = reinterpret_cast<T*>(smem);
+    SP = reinterpret_cast<float*>(smem + B_::lo_bytes);
+    kmax = reinterpret_cast<float*>(smem + B_::lo_bytes + B_::sp_bytes);
+    ksum = kmax + 8 * 64;
+    kstat = ksum + 8 * 64;
+    fmask = kstat + 3 * 64;
+    selw = reinterpret_cast<uint32_t*>(fmask + 64);
+    zs = reinterpret_cast<double*>(selw + 4);
   }
   __device__ float* pair(int p) const { return SP + ((size_t)p * 64 + (threadIdx.x & 63)) * 8; }
+  __device__ H* wf(int kt, int bb, int part) const {
+    return WF + ((size_t)((kt * (D / 32) + bb) * 2 + part) * 64) * 8;
+  }
 };
 
 // Loads 64 keys/values at the given positions (pos < 0: zero row) into Ks and
-// VTs, with their positions and kept flags. All 512 threads take part.
-template <typename T, int D>
-__device__ __forceinline__ void load_block(const PrefillArgs& a, const BlkPtr<T, D>& P, const T* kg,
-                           const T* vg, const uint8_t* sf, const int32_t* gather, int n_gather,
-                           int range_lo, int range_hi, int fold_lo, int fold_hi) {
+// VTs (values converted to H), with the kept flags as a 64-bit mask, the
+// fold mask and the keys' squared norms. Values go to VTs four keys at a time: keys 4a..4a+3 land in four
+// adjacent permuted columns. All NT threads take part.
+template <typename T, int D, int NT>
+__device__ __forceinline__ void load_block(const BlkPtr<T, D>& P, __amdgpu_buffer_rsrc_t kr,
+                                           __amdgpu_buffer_rsrc_t vr, uint32_t kv_bytes,
+                                           const uint8_t* sf, const int32_t* gather,
+                                           int n_gather, int range_lo, int range_hi,
+                                           int fold_lo, int fold_hi) {
   using B_ = Blk<T, D>;
+  typedef typename HalfOf<T>::type H;
   const int tid = threadIdx.x;
   constexpr int VEC = 16 / sizeof(T);
+  auto pos_of = [&](int kk) {
+    if (gather) return kk < n_gather ? gather[kk] : -1;
+    return range_lo + kk < range_hi ? range_lo + kk : -1;
+  };
+  // byte offset of a row; absent rows read past the range and load zeros
+  auto row_off = [&](int j) { return j >= 0 ? (uint32_t)j * (uint32_t)(D * sizeof(T)) : kv_bytes; };
   if (tid < 64) {
-    int j;
-    if (gather) j = tid < n_gather ? gather[tid] : -1;
-    else j = range_lo + tid < range_hi ? range_lo + tid : -1;
-    const int s = j >= 0 ? (gather ? 1 : (int)sf[j]) : 0;
-    P.kpos[tid] = j;
-    P.ksel[tid] = s;
-    P.fmask[tid] = (j >= fold_lo && j < fold_hi && !s) ? 1.f : 0.f;
-  }
-  for (int idx = tid; idx < 64 * (D / VEC); idx += 512) {
-    const int kk = idx / (D / VEC), col = (idx % (D / VEC)) * VEC;
-    int j;
-    if (gather) j = kk < n_gather ? gather[kk] : -1;
-    else j = range_lo + kk < range_hi ? range_lo + kk : -1;
-    uint4 kvv = {0, 0, 0, 0}, vvv = {0, 0, 0, 0};
-    if (j >= 0) {
-      kvv = *reinterpret_cast<const uint4*>(kg + (size_t)j * D + col);
-      vvv = *reinterpret_cast<const uint4*>(vg + (size_t)j * D + col);
+    const int j = pos_of(tid);
+    const int sel = j >= 0 ? (gather ? 1 : (int)sf[j]) : 0;
+    P.fmask[tid] = (j >= fold_lo && j < fold_hi && !sel) ? 1.f : 0.f;
+    const uint64_t bits = __ballot(sel != 0);
+    if (tid == 0) {
+      P.selw[0] = (uint32_t)bits;
+      P.selw[1] = (uint32_t)(bits >> 32);
     }
-    *reinterpret_cast<uint4*>(P.Ks + kk * B_::KS + col) = kvv;
-    const T* ve = reinterpret_cast<const T*>(&vvv);
-    const int pc = perm_col(kk);
+  }
 #pragma unroll
-    for (int e = 0; e < VEC; ++e) P.VTs[(col + e) * B_::VS + pc] = ve[e];
+  for (int idx = tid; idx < 64 * (D / VEC); idx += NT) {
+    const int kk = idx / (D / VEC), col = (idx % (D / VEC)) * VEC;
+    const uint4 kvv = ld_u4_buf(kr, row_off(pos_of(kk)) + col * sizeof(T), 0);
+    *reinterpret_cast<uint4*>(P.Ks + kk * B_::KS + col) = kvv;
+    // |k|^2 for the feature map: D/VEC consecutive lanes hold one row
+    const T* ke = reinterpret_cast<const T*>(&kvv);
+    float q2 = 0.f;
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) q2 += to_f32(ke[e]) * to_f32(ke[e]);
+#pragma unroll
+    for (int o = 1; o < D / VEC; o <<= 1) q2 += __shfl_xor(q2, o);
+    if (col == 0) P.kstat[128 + kk] = q2;
+  }
+#pragma unroll
+  for (int idx = tid; idx < 16 * (D / VEC); idx += NT) {
+    const int a4 = idx / (D / VEC), col = (idx % (D / VEC)) * VEC;
+    T v4[4][VEC];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint4 vv = ld_u4_buf(vr, row_off(pos_of(4 * a4 + i)) + col * sizeof(T), 0);
+      *reinterpret_cast<uint4*>(v4[i]) = vv;
+    }
+    const int pc = perm_col(4 * a4);
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) {
+      H w4[4] = {from_f32<H>(to_f32(v4[0][e])), from_f32<H>(to_f32(v4[1][e])),
+                 from_f32<H>(to_f32(v4[2][e])), from_f32<H>(to_f32(v4[3][e]))};
+      if constexpr (sizeof(H) == 2)
+        *reinterpret_cast<uint2*>(P.VTs + (col + e) * B_::VS + pc) = *reinterpret_cast<uint2*>(w4);
+      else
+        *reinterpret_cast<uint4*>(P.VTs + (col + e) * B_::VS + pc) = *reinterpret_cast<uint4*>(w4);
+    }
   }
 }
 
@@ -443,7 +490,7 @@ __device__ __forceinline__ void load_block(const PrefillArgs& a, const BlkPtr<T,
 // 16-row tile whose B fragments of X^T are xf[], the feature values in the
 // accumulator layout of (X F)^T: out[ft][i] = phi(x_r)[16 ft + 4g + i].
 template <typename T, int D>
-__device__ __forceinline__ void np_map_tile(const T* ftg, const Frag<T>* xf, f32x4* out) {
+__device__ __forceinline__ void np_map_tile(__amdgpu_buffer_rsrc_t ftr, const Frag<T>* xf, f32x4* out) {
   const int lane = threadIdx.x & 63, r16 = lane & 15, g4 = lane >> 4;
   float xn2 = 0.f;
 #pragma unroll
@@ -455,7 +502,8 @@ __device__ __forceinline__ void np_map_tile(const T* ftg, const Frag<T>* xf, f32
     out[ft] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kb = 0; kb < D / 32; ++kb)
-      mma(out[ft], ld_frag(ftg + (size_t)(16 * ft + r16) * D + 32 * kb + 8 * g4), xf[kb]);
+      mma(out[ft], ld_frag_buf<T>(ftr, (r16 * D + 8 * g4) * sizeof(T), (16 * ft * D + 32 * kb) * sizeof(T)),
+          xf[kb]);
 #pragma unroll
     for (int i = 0; i < 4; ++i) mx = fmaxf(mx, out[ft][i]);
   }
@@ -475,90 +523,160 @@ __device__ __forceinline__ void np_map_tile(const T* ftg, const Frag<T>* xf, f32
   for (int ft = 0; ft < D / 16; ++ft) out[ft] *= f;
 }
 
-// phi(K) of the block's 64 keys into phiK; waves 0..3 take one 16-key tile.
-template <typename T, int D>
-__device__ __forceinline__ void block_phi(const BlkPtr<T, D>& P, const T* ftg) {
-  using B_ = Blk<T, D>;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, r16 = lane & 15, g4 = lane >> 4;
-  if (wave >= 4) return;
-  Frag<T> kf[D / 32];
-#pragma unroll
-  for (int kb = 0; kb < D / 32; ++kb) kf[kb] = ld_frag(P.Ks + (16 * wave + r16) * B_::KS + 32 * kb + 8 * g4);
-  f32x4 ph[D / 16];
-  np_map_tile<T, D>(ftg, kf, ph);
-#pragma unroll
-  for (int ft = 0; ft < D / 16; ++ft)
-    *reinterpret_cast<f32x4*>(P.phiK + (16 * wave + r16) * B_::PS + 16 * ft + 4 * g4) = ph[ft];
+// Max / sum over the 16 lanes sharing g (the 16 columns of a C tile).
+__device__ __forceinline__ float max_over_r(float x) {
+  x = fmaxf(x, __shfl_xor(x, 1));
+  x = fmaxf(x, __shfl_xor(x, 2));
+  x = fmaxf(x, __shfl_xor(x, 4));
+  x = fmaxf(x, __shfl_xor(x, 8));
+  return x;
+}
+__device__ __forceinline__ float sum_over_r(float x) {
+  x += __shfl_xor(x, 1);
+  x += __shfl_xor(x, 2);
+  x += __shfl_xor(x, 4);
+  x += __shfl_xor(x, 8);
+  return x;
 }
 
-// The block's contribution phi(K)^T diag(fmask) V to the linear state, for
-// the wave's pairs, in fresh accumulators (so its rounding is relative to the
-// block's own sum, not to the running state); phi is split into three bf16
-// parts so the products keep float32 accuracy (values are exact in bf16).
+// NP-Map features of the block's 64 keys, computed once by the waves
+// w < D/16, wave w holding feature tile w of every key in the accumulator
+// layout of K F: ph[kt][i] = phi(k_{16kt+4g+i})[16w + r]. Per-key softmax
+// statistics are combined across waves through LDS. With want_w the
+// features are also written as H hi/lo A fragments (rows = keys) to WF.
+// Four workgroup barriers (five with want_w); every thread must call it with
+// the same want_w.
 template <typename T, int D>
-__device__ __forceinline__ void block_fold_half(const BlkPtr<T, D>& P, int kb2,
-                                                f32x4 (&acc)[Blk<T, D>::PPW][2]) {
+__device__ __forceinline__ void block_phi(const BlkPtr<T, D>& P, __amdgpu_buffer_rsrc_t ftr, f32x4 (&ph)[4],
+                                          bool want_w) {
   using B_ = Blk<T, D>;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, r16 = lane & 15, g4 = lane >> 4;
+  typedef typename HalfOf<T>::type H;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, r16 = lane & 15, g4 = lane >> 4;
+  const bool mine = wave < B_::NFT;  // wave-uniform
+  if (mine) {
+    Frag<T> fb[D / 32];
 #pragma unroll
-  for (int pp = 0; pp < B_::PPW; ++pp) {
-    const int p = wave * B_::PPW + pp;
-    const int vt = p / (D / 32), bb = p % (D / 32);
-    const Frag<T> bv = ld_frag(P.VTs + (16 * vt + r16) * B_::VS + 32 * kb2 + 8 * g4);
+    for (int kb = 0; kb < D / 32; ++kb)
+      fb[kb] = ld_frag_buf<T>(ftr, ((16 * wave + r16) * D + 8 * g4) * sizeof(T), 32 * kb * sizeof(T));
 #pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      const int f = 16 * (2 * bb + e) + r16;
-      f32x4 x0, x1;
+    for (int kt = 0; kt < 4; ++kt) {
+      ph[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int k0 = 32 * kb2 + 4 * g4 + q, k1 = k0 + 16;
-        x0[q] = P.fmask[k0] * P.phiK[k0 * B_::PS + f];
-        x1[q] = P.fmask[k1] * P.phiK[k1 * B_::PS + f];
+      for (int kb = 0; kb < D / 32; ++kb)
+        mma(ph[kt], ld_frag(P.Ks + (16 * kt + r16) * B_::KS + 32 * kb + 8 * g4), fb[kb]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float m = max_over_r(ph[kt][i]);
+        if (r16 == 0) P.kmax[wave * 64 + 16 * kt + 4 * g4 + i] = m;
       }
-      Frag<T> hi, mid, lo;
-      split3_frag<T>(x0, x1, hi, mid, lo);
-      mma(acc[pp][e], hi, bv);
-      if constexpr (sizeof(T) == 2) {
-        mma(acc[pp][e], mid, bv);
-        mma(acc[pp][e], lo, bv);
+    }
+  }
+  __syncthreads();
+  if (tid < 64) {
+    float m = STILL_NEG_INF;
+    for (int w = 0; w < B_::NFT; ++w) m = fmaxf(m, P.kmax[w * 64 + tid]);
+    P.kstat[tid] = m;
+  }
+  __syncthreads();
+  if (mine) {
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float e = exp_acc<T>(ph[kt][i] - P.kstat[16 * kt + 4 * g4 + i]);
+        ph[kt][i] = e;
+        const float s2 = sum_over_r(e * e);
+        if (r16 == 0) P.ksum[wave * 64 + 16 * kt + 4 * g4 + i] = s2;
       }
+  }
+  __syncthreads();
+  if (tid < 64) {
+    float s2 = 0.f;
+    for (int w = 0; w < B_::NFT; ++w) s2 += P.ksum[w * 64 + tid];
+    P.kstat[64 + tid] = sqrtf(P.kstat[128 + tid]) / sqrtf(s2);
+  }
+  __syncthreads();
+  if (mine) {
+    const int f = 16 * wave + r16, bb = f >> 5, o = f & 31;
+    const int gp = (o & 15) >> 2, sl = (o & 3) + ((o >> 4) << 2);
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int key = 16 * kt + 4 * g4 + i;
+        const float v = ph[kt][i] * P.kstat[64 + key];
+        ph[kt][i] = v;
+        if (want_w) {
+          const H hi = from_f32<H>(v);
+          const int ln = 16 * gp + (key & 15);
+          P.wf(kt, bb, 0)[ln * 8 + sl] = hi;
+          if constexpr (sizeof(H) == 2) P.wf(kt, bb, 1)[ln * 8 + sl] = from_f32<H>(v - to_f32(hi));
+        }
+      }
+  }
+  if (want_w) __syncthreads();  // WF is read by every wave
+}
+
+// The block's contribution phi(K)^T diag(fmask) V to the d_k tile of wave w
+// (< D/16): acc[vt] for every d_v tile, key halves kb2 in [kb_lo, kb_hi).
+// phi is split into two H parts (fp16 hi + lo keep ~22 significant bits;
+// values are exact in H), so the products keep float32 accuracy.
+template <typename T, int D>
+__device__ __forceinline__ void fold_tile(const BlkPtr<T, D>& P, const f32x4 (&ph)[4], int kb_lo,
+                                          int kb_hi, f32x4 (&acc)[D / 16]) {
+  using B_ = Blk<T, D>;
+  typedef typename HalfOf<T>::type H;
+  const int lane = threadIdx.x & 63, r16 = lane & 15, g4 = lane >> 4;
+#pragma unroll
+  for (int kb2 = 0; kb2 < 2; ++kb2) {
+    if (kb2 < kb_lo || kb2 >= kb_hi) continue;
+    f32x4 x0 = ph[2 * kb2], x1 = ph[2 * kb2 + 1];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x0[i] *= P.fmask[32 * kb2 + 4 * g4 + i];
+      x1[i] *= P.fmask[32 * kb2 + 16 + 4 * g4 + i];
+    }
+    Frag<H> hi, lo;
+    split2_frag<H>(x0, x1, hi, lo);
+#pragma unroll
+    for (int vt = 0; vt < D / 16; ++vt) {
+      const Frag<H> bv = ld_frag(P.VTs + (16 * vt + r16) * B_::VS + 32 * kb2 + 8 * g4);
+      mma(acc[vt], hi, bv);
+      if constexpr (sizeof(H) == 2) mma(acc[vt], lo, bv);
     }
   }
 }
 
-// Both 32-key halves of the block into fresh accumulators.
+// The block's contribution to z for feature 16w + r (lanes with g == 0).
 template <typename T, int D>
-__device__ __forceinline__ void block_fold_acc(const BlkPtr<T, D>& P,
-                                               f32x4 (&acc)[Blk<T, D>::PPW][2]) {
+__device__ __forceinline__ float fold_zsum(const BlkPtr<T, D>& P, const f32x4 (&ph)[4]) {
+  const int lane = threadIdx.x & 63, g4 = lane >> 4;
+  float z = 0.f;
 #pragma unroll
-  for (int pp = 0; pp < Blk<T, D>::PPW; ++pp) acc[pp][0] = acc[pp][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-  block_fold_half<T, D>(P, 0, acc);
-  block_fold_half<T, D>(P, 1, acc);
+  for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) z += P.fmask[16 * kt + 4 * g4 + i] * ph[kt][i];
+  return sum_over_g(z);
 }
 
-// The block's contribution to z for feature threadIdx.x (< D).
+// Fold the block into the walk's state in LDS (SP += contribution, z += ...);
+// wave w updates the d_k tile w, i.e. half e = w % 2 of the pairs (vt, w/2).
 template <typename T, int D>
-__device__ __forceinline__ float block_zsum(const BlkPtr<T, D>& P) {
+__device__ __forceinline__ void block_fold(const BlkPtr<T, D>& P, const f32x4 (&ph)[4]) {
   using B_ = Blk<T, D>;
-  float zsum = 0.f;
-  for (int kk = 0; kk < 64; ++kk) zsum += P.fmask[kk] * P.phiK[kk * B_::PS + threadIdx.x];
-  return zsum;
-}
-
-// Fold the block into the walk's state in LDS: SP += contribution, z += ...
-template <typename T, int D>
-__device__ __forceinline__ void block_fold(const BlkPtr<T, D>& P) {
-  using B_ = Blk<T, D>;
-  f32x4 acc[B_::PPW][2];
-  block_fold_acc<T, D>(P, acc);
-  const int wave = threadIdx.x >> 6;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, r16 = lane & 15, g4 = lane >> 4;
+  if (wave >= B_::NFT) return;
+  f32x4 acc[D / 16];
 #pragma unroll
-  for (int pp = 0; pp < B_::PPW; ++pp) {
-    float* sp = P.pair(wave * B_::PPW + pp);
-    *reinterpret_cast<f32x4*>(sp) += acc[pp][0];
-    *reinterpret_cast<f32x4*>(sp + 4) += acc[pp][1];
+  for (int vt = 0; vt < D / 16; ++vt) acc[vt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  fold_tile<T, D>(P, ph, 0, 2, acc);
+#pragma unroll
+  for (int vt = 0; vt < D / 16; ++vt) {
+    float* sp = P.pair(vt * (D / 32) + (wave >> 1)) + 4 * (wave & 1);
+    *reinterpret_cast<f32x4*>(sp) += acc[vt];
   }
-  if (threadIdx.x < D) P.zs[threadIdx.x] += (double)block_zsum<T, D>(P);
+  const float z = fold_zsum<T, D>(P, ph);
+  if (g4 == 0) P.zs[16 * wave + r16] += (double)z;
 }
 
 // Super-chunk states in the workspace use the fragment-linear layout of SP
@@ -573,79 +691,80 @@ __device__ __forceinline__ void load_state(const BlkPtr<T, D>& P, const float* S
 template <typename T, int D>
 __device__ __forceinline__ void store_state_rowmajor(const BlkPtr<T, D>& P, float* S) {
   using B_ = Blk<T, D>;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, r16 = lane & 15, g4 = lane >> 4;
-#pragma unroll
-  for (int pp = 0; pp < B_::PPW; ++pp) {
-    const int p = wave * B_::PPW + pp;
+  const int r16 = threadIdx.x & 15;
+  for (int e = threadIdx.x; e < B_::NPAIR * 64; e += 512) {
+    const int p = e >> 6, ln = e & 63, g4 = ln >> 4;
     const int vt = p / (D / 32), bb = p % (D / 32);
-    const float* sp = P.pair(p);
+    const float* sp = P.SP + (size_t)e * 8;
 #pragma unroll
-    for (int e = 0; e < 2; ++e)
+    for (int q = 0; q < 2; ++q)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        S[(size_t)(32 * bb + 16 * e + 4 * g4 + i) * D + 16 * vt + r16] = sp[4 * e + i];
+        S[(size_t)(32 * bb + 16 * q + 4 * g4 + i) * D + 16 * vt + (ln & 15)] = sp[4 * q + i];
   }
+  (void)r16;
 }
 
 // ---------------------------------------------------- 4. state_delta ----
 // Super-chunk s folds the chunks [cf(sK), cf(sK+K)) into the state, cf(c) =
 // chunks wholly before the window of chunk c. This kernel sums their
 // unkept tokens' phi(k) v^T (and phi(k)) so the scan can give every
-// super-chunk its starting state.
+// super-chunk its starting state. Every 32-key group lands in float64 sums on
+// its own: a single 8x-norm token can make a group's sum ~1e4, where one
+// float32 rounding is already ~5e-4.
 template <typename T, int D>
 __global__ __launch_bounds__(512) void state_delta_kernel(PrefillArgs a) {
+  using B_ = Blk<T, D>;
   extern __shared__ __align__(16) char smem[];
   const BlkPtr<T, D> P(smem);
   const int s = blockIdx.x, kv = blockIdx.y, b = blockIdx.z;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, r16 = lane & 15, g4 = lane >> 4;
   const int unit = b * a.Hkv + kv;
-  const T* kg = reinterpret_cast<const T*>(a.k) + (size_t)unit * a.L * D;
-  const T* vg = reinterpret_cast<const T*>(a.v) + (size_t)unit * a.L * D;
+  const uint32_t kv_bytes = (uint32_t)((size_t)a.L * D * sizeof(T));
+  const __amdgpu_buffer_rsrc_t kr = make_rsrc(reinterpret_cast<const T*>(a.k) + (size_t)unit * a.L * D, kv_bytes);
+  const __amdgpu_buffer_rsrc_t vr = make_rsrc(reinterpret_cast<const T*>(a.v) + (size_t)unit * a.L * D, kv_bytes);
   const uint8_t* sf = a.selflag + (size_t)unit * a.L;
-  const T* ftg = reinterpret_cast<const T*>(a.ft) + (size_t)kv * D * D;
-  using B_ = Blk<T, D>;
-  double sum[B_::PPW][8];  // float64 running sums of the block contributions
+  const __amdgpu_buffer_rsrc_t ftr =
+      make_rsrc(reinterpret_cast<const T*>(a.ft) + (size_t)kv * D * D, D * D * sizeof(T));
+  double sum[D / 16][4];
 #pragma unroll
-  for (int pp = 0; pp < B_::PPW; ++pp)
+  for (int vt = 0; vt < D / 16; ++vt)
 #pragma unroll
-    for (int i = 0; i < 8; ++i) sum[pp][i] = 0.0;
+    for (int i = 0; i < 4; ++i) sum[vt][i] = 0.0;
   double zsum = 0.0;
   const int lo = full_chunks_before(s * a.K, a.W, a.C) * a.C;
   const int hi = full_chunks_before(s * a.K + a.K, a.W, a.C) * a.C;
   for (int blo = lo; blo < hi; blo += 64) {
     __syncthreads();
-    load_block<T, D>(a, P, kg, vg, sf, nullptr, 0, blo, hi, lo, hi);
+    load_block<T, D, 512>(P, kr, vr, kv_bytes, sf, nullptr, 0, blo, hi, lo, hi);
     __syncthreads();
-    block_phi<T, D>(P, ftg);
-    __syncthreads();
-    // each 32-key group lands in the float64 sums on its own: a single
-    // outlier token can make a group's sum ~1e4, where one float32 rounding
-    // is already ~5e-4
+    f32x4 ph[4];
+    block_phi<T, D>(P, ftr, ph, false);
+    if (wave < B_::NFT) {
 #pragma unroll
-    for (int kb2 = 0; kb2 < 2; ++kb2) {
-      f32x4 acc[B_::PPW][2];
+      for (int kb2 = 0; kb2 < 2; ++kb2) {
+        f32x4 acc[D / 16];
 #pragma unroll
-      for (int pp = 0; pp < B_::PPW; ++pp) acc[pp][0] = acc[pp][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-      block_fold_half<T, D>(P, kb2, acc);
+        for (int vt = 0; vt < D / 16; ++vt) acc[vt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        fold_tile<T, D>(P, ph, kb2, kb2 + 1, acc);
 #pragma unroll
-      for (int pp = 0; pp < B_::PPW; ++pp)
+        for (int vt = 0; vt < D / 16; ++vt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          sum[pp][i] += (double)acc[pp][0][i];
-          sum[pp][4 + i] += (double)acc[pp][1][i];
-        }
+          for (int i = 0; i < 4; ++i) sum[vt][i] += (double)acc[vt][i];
+      }
+      zsum += (double)fold_zsum<T, D>(P, ph);
     }
-    if (tid < D) zsum += (double)block_zsum<T, D>(P);
   }
   float* dst = a.dS + ((size_t)unit * a.NS + s) * (D * D + D);
-  const int wave = tid >> 6, lane = tid & 63;
+  if (wave < B_::NFT) {
 #pragma unroll
-  for (int pp = 0; pp < B_::PPW; ++pp) {
-    float* o = dst + ((size_t)(wave * B_::PPW + pp) * 64 + lane) * 8;
+    for (int vt = 0; vt < D / 16; ++vt) {
+      float* o = dst + ((size_t)(vt * (D / 32) + (wave >> 1)) * 64 + lane) * 8 + 4 * (wave & 1);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) o[i] = (float)sum[pp][i];
+      for (int i = 0; i < 4; ++i) o[i] = (float)sum[vt][i];
+    }
+    if (g4 == 0) dst[D * D + 16 * wave + r16] = (float)zsum;
   }
-  if (tid < D) dst[D * D + tid] = (float)zsum;
 }
 
 // ----------------------------------------------------- 5. state_scan ----
@@ -663,8 +782,12 @@ __global__ __launch_bounds__(256) void state_scan_kernel(float* dS, int NS, int 
 
 // ---------------------------------------------------------- 6. attend ----
 // One workgroup per (super-chunk, kv head x head group, batch row); 8 waves,
-// each owning up to TPW 16-query row tiles (one head, 16 positions). For
-// each chunk of the super-chunk, in order:
+// each owning one 16-query row tile (one head, 16 positions), so a
+// workgroup holds at most 8 row tiles (head groups split the heads of a kv
+// head across workgroups). Workgroups are ordered so that consecutive ids of
+// one (batch, kv head, head group) unit share an XCD (ids are dealt to the 8
+// XCDs round robin), keeping that unit's kept pool, F^T and state in one L2.
+// For each chunk of the super-chunk, in order:
 //  * phi(Q) and the state readout S^T phi(Q)^T, z . phi(q): the linear
 //    state enters as one virtual key of weight g*z.phi(q) and value
 //    S^T phi(q) / z.phi(q) [P3 "NP-Map ..."];
@@ -676,22 +799,41 @@ __global__ __launch_bounds__(256) void state_scan_kernel(float* dS, int NS, int 
 //  * every weight enters one running max / sum in the log domain (reading:
 //    a single normaliser over softmax and gated linear weights);
 //  * the next chunk's newly folded tokens are added to the state.
-template <typename T, int D, int TPW>
+// Precision: logits from exact bf16 products; the readout with hi/lo bf16
+// splits of S and phi(q); <phi(k),phi(q)> with phi(k) as fp16 hi + lo;
+// softmax weights and values in fp16 (11-bit significands, values exact).
+template <typename T, int D>
 __global__ __launch_bounds__(512) void attend_kernel(PrefillArgs a) {
   using B_ = Blk<T, D>;
+  typedef typename HalfOf<T>::type H;
   extern __shared__ __align__(16) char smem[];
   const BlkPtr<T, D> P(smem);
-  const int s = blockIdx.x, kv = blockIdx.y / a.nHG, hg = blockIdx.y % a.nHG, b = blockIdx.z;
+  // XCD-grouped order: logical id = xcd * (n / 8) + (id / 8)
+  const int n_units = a.Hkv * a.nHG * a.B;
+  const int n_wg = a.NS * n_units;
+  int id = blockIdx.x;
+  if ((n_wg & 7) == 0) id = (id & 7) * (n_wg >> 3) + (id >> 3);
+  const int s = id % a.NS;
+  const int u3 = id / a.NS;  // (b, kv, hg)
+  const int hg = u3 % a.nHG, kv = (u3 / a.nHG) % a.Hkv, b = u3 / (a.nHG * a.Hkv);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, r16 = lane & 15, g4 = lane >> 4;
   const int L = a.L, C = a.C, W = a.W;
   const int unit = b * a.Hkv + kv;
-  const T* kg = reinterpret_cast<const T*>(a.k) + (size_t)unit * L * D;
-  const T* vg = reinterpret_cast<const T*>(a.v) + (size_t)unit * L * D;
+  const uint32_t kv_bytes = (uint32_t)((size_t)L * D * sizeof(T));
+  const __amdgpu_buffer_rsrc_t kr = make_rsrc(reinterpret_cast<const T*>(a.k) + (size_t)unit * L * D, kv_bytes);
+  const __amdgpu_buffer_rsrc_t vr = make_rsrc(reinterpret_cast<const T*>(a.v) + (size_t)unit * L * D, kv_bytes);
   const uint8_t* sf = a.selflag + (size_t)unit * L;
   const int32_t* selu = a.sel + (size_t)unit * a.n_dec * a.lam;
-  const T* ftg = reinterpret_cast<const T*>(a.ft) + (size_t)kv * D * D;
+  const __amdgpu_buffer_rsrc_t ftr =
+      make_rsrc(reinterpret_cast<const T*>(a.ft) + (size_t)kv * D * D, D * D * sizeof(T));
   const int n_qt = C / 16;
-  const int n_rt = a.Gs * n_qt;
+  const bool act = wave < a.Gs * n_qt;  // wave-uniform
+  const int hl = act ? wave / n_qt : 0, qt = act ? wave % n_qt : 0;
+  const int h = kv * a.G + hg * a.Gs + hl;
+  const float g = a.gate[h];
+  const float lgate = g > 0.f ? log_acc<T>(g) : STILL_NEG_INF;
+  const __amdgpu_buffer_rsrc_t qr =
+      make_rsrc(reinterpret_cast<const T*>(a.q) + ((size_t)(b * a.Hq + h) * L) * D, kv_bytes);
 
   const float* Sst = a.dS + ((size_t)unit * a.NS + s) * (D * D + D);
   load_state<T, D>(P, Sst);
@@ -709,66 +851,70 @@ __global__ __launch_bounds__(512) void attend_kernel(PrefillArgs a) {
     const int band_lo = cf * C;
     const int band_hi = min(cC + C, L);
     const int n_oob = pool_count_at(cf, a.lam, a.cap_chunks);
+    const int t = cC + 16 * qt + r16;
 
-    // per row tile: query fragments, phi(q), state readout
-    Frag<T> qf[TPW][D / 32];
-    Frag<T> phq[TPW][D / 32], phl[TPW][D / 32];  // phi(q) as hi + lo parts
-    f32x4 O[TPW][D / 16];
-    float mrun[TPW], lrun[TPW], lgate[TPW];
-    int tq[TPW], hq[TPW];
+    // the state as hi/lo bf16 fragments (split once, shared by every wave)
+    for (int e = tid; e < B_::NPAIR * 64; e += 512) {
+      const float* sp = P.SP + (size_t)e * 8;
+      Frag<T> sh, sl;
+      split2_frag<T>(*reinterpret_cast<const f32x4*>(sp), *reinterpret_cast<const f32x4*>(sp + 4), sh, sl);
+      const int p = e >> 6, ln = e & 63;
+      st_frag(P.RS + ((size_t)(2 * p) * 64 + ln) * 8, sh);
+      st_frag(P.RS + ((size_t)(2 * p + 1) * 64 + ln) * 8, sl);
+    }
+    __syncthreads();
+
+    // query fragments, phi(q), state readout
+    Frag<T> qf[D / 32];
+    Frag<H> pq[D / 32];  // phi(q) as H for <phi(k), phi(q)>
 #pragma unroll
-    for (int rr = 0; rr < TPW; ++rr) {
-      const int rt = wave + 8 * rr;
-      const bool act = rt < n_rt;
-      const int hl = act ? rt / n_qt : 0, qt = act ? rt % n_qt : 0;
-      const int h = kv * a.G + hg * a.Gs + hl;
-      const int t = cC + 16 * qt + r16;
-      tq[rr] = act ? t : -1;
-      hq[rr] = h;
-      const T* qg = reinterpret_cast<const T*>(a.q) + ((size_t)(b * a.Hq + h) * L) * D;
-#pragma unroll
-      for (int kb = 0; kb < D / 32; ++kb)
-        qf[rr][kb] = (act && t < L) ? ld_frag(qg + (size_t)t * D + 32 * kb + 8 * g4) : zero_frag<T>();
+    for (int kb = 0; kb < D / 32; ++kb)
+      qf[kb] = ld_frag_buf<T>(qr, act ? (uint32_t)(t * D + 8 * g4) * sizeof(T) : kv_bytes,
+                              32 * kb * sizeof(T));
+    f32x4 O[D / 16];
+    float mrun, lrun;
+    {
       f32x4 ph[D / 16];
-      np_map_tile<T, D>(ftg, qf[rr], ph);
+      np_map_tile<T, D>(ftr, qf, ph);
       float dz = 0.f;
 #pragma unroll
       for (int ft = 0; ft < D / 16; ++ft)
 #pragma unroll
         for (int i = 0; i < 4; ++i) dz += ph[ft][i] * (float)P.zs[16 * ft + 4 * g4 + i];
       dz = sum_over_g(dz);
+      Frag<T> phq[D / 32], phl[D / 32];
 #pragma unroll
-      for (int bb = 0; bb < D / 32; ++bb) split2_frag<T>(ph[2 * bb], ph[2 * bb + 1], phq[rr][bb], phl[rr][bb]);
-      const float g = a.gate[h];
-      lgate[rr] = g > 0.f ? log_acc<T>(g) : STILL_NEG_INF;
+      for (int bb = 0; bb < D / 32; ++bb) {
+        split2_frag<T>(ph[2 * bb], ph[2 * bb + 1], phq[bb], phl[bb]);
+        pq[bb] = frag_from<H>(ph[2 * bb], ph[2 * bb + 1]);
+      }
 #pragma unroll
       for (int dt = 0; dt < D / 16; ++dt) {
-        O[rr][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        O[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int bb = 0; bb < D / 32; ++bb) {
           // S^T phi(q) to ~2^-16 relative: hi*hi + lo*hi + hi*lo
-          const float* sp = P.pair(dt * (D / 32) + bb);
-          Frag<T> sh, sl;
-          split2_frag<T>(*reinterpret_cast<const f32x4*>(sp),
-                         *reinterpret_cast<const f32x4*>(sp + 4), sh, sl);
-          mma(O[rr][dt], sh, phq[rr][bb]);
+          const int p = dt * (D / 32) + bb;
+          const Frag<T> sh = ld_frag(P.RS + ((size_t)(2 * p) * 64 + lane) * 8);
+          mma(O[dt], sh, phq[bb]);
           if constexpr (sizeof(T) == 2) {
-            mma(O[rr][dt], sl, phq[rr][bb]);
-            mma(O[rr][dt], sh, phl[rr][bb]);
+            const Frag<T> sl = ld_frag(P.RS + ((size_t)(2 * p + 1) * 64 + lane) * 8);
+            mma(O[dt], sl, phq[bb]);
+            mma(O[dt], sh, phl[bb]);
           }
         }
       }
       if (g > 0.f && dz > 0.f) {
-        mrun[rr] = log_acc<T>(g * dz);
-        lrun[rr] = g4 == 0 ? 1.f : 0.f;
+        mrun = log_acc<T>(g * dz);
+        lrun = g4 == 0 ? 1.f : 0.f;
         const float inv = 1.f / dz;
 #pragma unroll
-        for (int dt = 0; dt < D / 16; ++dt) O[rr][dt] *= inv;
+        for (int dt = 0; dt < D / 16; ++dt) O[dt] *= inv;
       } else {
-        mrun[rr] = STILL_NEG_INF;
-        lrun[rr] = 0.f;
+        mrun = STILL_NEG_INF;
+        lrun = 0.f;
 #pragma unroll
-        for (int dt = 0; dt < D / 16; ++dt) O[rr][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int dt = 0; dt < D / 16; ++dt) O[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
       }
     }
 
@@ -778,74 +924,81 @@ __global__ __launch_bounds__(512) void attend_kernel(PrefillArgs a) {
     for (int blk = 0; blk < n_pool_blk + n_band_blk; ++blk) {
       const bool is_pool = blk < n_pool_blk;
       const int blo = is_pool ? 64 * blk : band_lo + 64 * (blk - n_pool_blk);
+      const int nvalid = is_pool ? min(64, n_oob - blo) : min(64, band_hi - blo);
       const bool la_blk = !is_pool && blo < cC;
-      const bool need_phi = !is_pool && blo < max(cC, fold_hi);
+      const bool do_fold = fold && !is_pool && blo < fold_hi;
       __syncthreads();
       if (is_pool)
-        load_block<T, D>(a, P, kg, vg, sf, selu + blo, min(64, n_oob - blo), 0, 0, 0, 0);
+        load_block<T, D, 512>(P, kr, vr, kv_bytes, sf, selu + blo, nvalid, 0, 0, 0, 0);
       else
-        load_block<T, D>(a, P, kg, vg, sf, nullptr, 0, blo, band_hi, fold_lo, fold_hi);
+        load_block<T, D, 512>(P, kr, vr, kv_bytes, sf, nullptr, 0, blo, band_hi, fold_lo, fold_hi);
       __syncthreads();
-      if (need_phi) {
-        block_phi<T, D>(P, ftg);
-        __syncthreads();
+      if (la_blk || do_fold) {
+        f32x4 phk[4];
+        block_phi<T, D>(P, ftr, phk, la_blk);  // ends with a barrier
+        // the fold writes only SP / zs, which this chunk no longer reads
+        if (do_fold) block_fold<T, D>(P, phk);
       }
-#pragma unroll
-      for (int rr = 0; rr < TPW; ++rr) {
-        if (wave + 8 * rr >= n_rt) continue;  // wave-uniform
-        const int t = tq[rr];
-        f32x4 st[4], wt[4];
+      if (act) {  // wave-uniform
+        const uint64_t selbits = ((uint64_t)P.selw[1] << 32) | P.selw[0];
+        f32x4 st[4];
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt) {
           st[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int kb = 0; kb < D / 32; ++kb)
-            mma(st[kt], ld_frag(P.Ks + (16 * kt + r16) * B_::KS + 32 * kb + 8 * g4), qf[rr][kb]);
-        }
-        if (la_blk) {
-#pragma unroll
-          for (int kt = 0; kt < 4; ++kt) {
-            wt[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int bb = 0; bb < D / 32; ++bb) {
-              // <phi(k), phi(q)> to ~2^-16 relative: hi*hi + lo*hi + hi*lo
-              const float* pr = P.phiK + (16 * kt + r16) * B_::PS + 32 * bb + 4 * g4;
-              Frag<T> kh, kl;
-              split2_frag<T>(*reinterpret_cast<const f32x4*>(pr),
-                             *reinterpret_cast<const f32x4*>(pr + 16), kh, kl);
-              mma(wt[kt], kh, phq[rr][bb]);
-              if constexpr (sizeof(T) == 2) {
-                mma(wt[kt], kl, phq[rr][bb]);
-                mma(wt[kt], kh, phl[rr][bb]);
-              }
-            }
-          }
+            mma(st[kt], ld_frag(P.Ks + (16 * kt + r16) * B_::KS + 32 * kb + 8 * g4), qf[kb]);
         }
         float mx = STILL_NEG_INF;
+        if (is_pool) {
 #pragma unroll
-        for (int kt = 0; kt < 4; ++kt)
+          for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int kk = 16 * kt + 4 * g4 + i;
-            const int j = P.kpos[kk];
-            float lw = STILL_NEG_INF;
-            if (j >= 0 && j <= t) {
-              if (is_pool || j >= t - W + 1 || j >= cC || P.ksel[kk]) {
-                lw = st[kt][i] * a.scale;
-              } else if (la_blk) {
-                const float w = wt[kt][i];
-                lw = w > 0.f ? lgate[rr] + log_acc<T>(w) : STILL_NEG_INF;
+            for (int i = 0; i < 4; ++i) {
+              const int kk = 16 * kt + 4 * g4 + i;
+              const float lw = kk < nvalid ? st[kt][i] * a.scale : STILL_NEG_INF;
+              st[kt][i] = lw;
+              mx = fmaxf(mx, lw);
+            }
+        } else {
+          f32x4 wt[4];
+          if (la_blk) {
+#pragma unroll
+            for (int kt = 0; kt < 4; ++kt) {
+              wt[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+              for (int bb = 0; bb < D / 32; ++bb) {
+                // <phi(k), phi(q)> with phi(k) as hi + lo parts
+                mma(wt[kt], ld_frag(P.wf(kt, bb, 0) + lane * 8), pq[bb]);
+                if constexpr (sizeof(H) == 2) mma(wt[kt], ld_frag(P.wf(kt, bb, 1) + lane * 8), pq[bb]);
               }
             }
-            st[kt][i] = lw;
-            mx = fmaxf(mx, lw);
           }
+          const int vis_lo = min(t - W + 1, cC);  // softmax-visible from here
+#pragma unroll
+          for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int kk = 16 * kt + 4 * g4 + i;
+              const int j = blo + kk;
+              const bool sel = (selbits >> kk) & 1ull;
+              const bool valid = kk < nvalid && j <= t;
+              const bool sa = valid && (j >= vis_lo || sel);
+              float lw = sa ? st[kt][i] * a.scale : STILL_NEG_INF;
+              if (la_blk) {
+                const float w = wt[kt][i];
+                const bool la = valid && !sa && w > 0.f;
+                lw = la ? lgate + log_acc<T>(fmaxf(w, 1e-37f)) : lw;
+              }
+              st[kt][i] = lw;
+              mx = fmaxf(mx, lw);
+            }
+        }
         mx = max_over_g(mx);
-        const float mn = fmaxf(mrun[rr], mx);
+        const float mn = fmaxf(mrun, mx);
         // rows with nothing visible so far keep m = -inf, O = 0, l = 0
-        const float al = mrun[rr] == STILL_NEG_INF ? 0.f : exp_acc<T>(mrun[rr] - mn);
-        mrun[rr] = mn;
-        float lsum = 0.f;
+        const float al = mrun == STILL_NEG_INF ? 0.f : exp_acc<T>(mrun - mn);
+        mrun = mn;
         f32x4 pv[4];
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt)
@@ -854,49 +1007,60 @@ __global__ __launch_bounds__(512) void attend_kernel(PrefillArgs a) {
             const float lw = st[kt][i];
             pv[kt][i] = lw == STILL_NEG_INF ? 0.f : exp_acc<T>(lw - mn);
           }
-        // weights as hi + lo bf16 parts (float32 as is): the products and the
-        // running sum see the same weights, to ~2^-16 relative
-        Frag<T> ph0, pl0, ph1, pl1;
-        split2_frag<T>(pv[0], pv[1], ph0, pl0);
-        split2_frag<T>(pv[2], pv[3], ph1, pl1);
-        lsum = frag_sum(ph0) + frag_sum(ph1);
-        if constexpr (sizeof(T) == 2) lsum += frag_sum(pl0) + frag_sum(pl1);
-        lrun[rr] = lrun[rr] * al + lsum;
+        // weights as H; the running sum uses the same rounded weights
+        const Frag<H> pf0 = frag_from<H>(pv[0], pv[1]);
+        const Frag<H> pf1 = frag_from<H>(pv[2], pv[3]);
+        lrun = lrun * al + frag_sum(pf0) + frag_sum(pf1);
 #pragma unroll
         for (int dt = 0; dt < D / 16; ++dt) {
-          O[rr][dt] *= al;
-          const Frag<T> v0 = ld_frag(P.VTs + (16 * dt + r16) * B_::VS + 8 * g4);
-          const Frag<T> v1 = ld_frag(P.VTs + (16 * dt + r16) * B_::VS + 32 + 8 * g4);
-          mma(O[rr][dt], v0, ph0);
-          mma(O[rr][dt], v1, ph1);
-          if constexpr (sizeof(T) == 2) {
-            mma(O[rr][dt], v0, pl0);
-            mma(O[rr][dt], v1, pl1);
-          }
+          O[dt] *= al;
+          mma(O[dt], ld_frag(P.VTs + (16 * dt + r16) * B_::VS + 8 * g4), pf0);
+          mma(O[dt], ld_frag(P.VTs + (16 * dt + r16) * B_::VS + 32 + 8 * g4), pf1);
         }
       }
-      if (fold && !is_pool && blo < fold_hi) block_fold<T, D>(P);
     }
 
-    // outputs
+    // outputs: normalise; bf16 rows go through LDS for full-line stores
+    const float l = sum_over_g(lrun);
+    const float inv = 1.f / l;
+    const size_t ob = ((size_t)(b * a.Hq + h) * L) * D;
+    if constexpr (sizeof(T) == 2) {
+      if (!a.fp32_out) {
+        __syncthreads();  // Ks / VTs are free again
+        constexpr int OS = D + 8;  // padded row, elements
+        bf16* tile = reinterpret_cast<bf16*>(smem) + (size_t)wave * 16 * OS;
+        if (act) {
 #pragma unroll
-    for (int rr = 0; rr < TPW; ++rr) {
-      const int t = tq[rr];
-      const float l = sum_over_g(lrun[rr]);
-      if (t < 0 || t >= L) continue;
-      const float inv = 1.f / l;
-      const size_t ob = ((size_t)(b * a.Hq + hq[rr]) * L + t) * D;
+          for (int dt = 0; dt < D / 16; ++dt) {
+            const f32x4 y = O[dt] * inv;
+            bf16 y4[4] = {(bf16)y[0], (bf16)y[1], (bf16)y[2], (bf16)y[3]};
+            *reinterpret_cast<uint2*>(tile + r16 * OS + 16 * dt + 4 * g4) = *reinterpret_cast<uint2*>(y4);
+          }
+          // wave-local: the tile is written and read by this wave only
+          __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+          __builtin_amdgcn_wave_barrier();
+          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+          constexpr int CPR = D / 8;  // 16-byte chunks per row
 #pragma unroll
-      for (int dt = 0; dt < D / 16; ++dt) {
-        const f32x4 y = O[rr][dt] * inv;
-        if (a.fp32_out) {
-          *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.out) + ob + 16 * dt + 4 * g4) = y;
-        } else {
-          T* o = reinterpret_cast<T*>(a.out) + ob + 16 * dt + 4 * g4;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) o[i] = from_f32<T>(y[i]);
+          for (int it = 0; it < 16 * CPR / 64; ++it) {
+            const int e = it * 64 + lane, row = e / CPR, ch = e % CPR;
+            const int tr = cC + 16 * qt + row;
+            if (tr < L)
+              *reinterpret_cast<uint4*>(reinterpret_cast<bf16*>(a.out) + ob + (size_t)tr * D + 8 * ch) =
+                  *reinterpret_cast<const uint4*>(tile + row * OS + 8 * ch);
+          }
         }
+      } else if (act && t < L) {
+#pragma unroll
+        for (int dt = 0; dt < D / 16; ++dt)
+          *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.out) + ob + (size_t)t * D + 16 * dt + 4 * g4) =
+              O[dt] * inv;
       }
+    } else if (act && t < L) {
+#pragma unroll
+      for (int dt = 0; dt < D / 16; ++dt)
+        *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.out) + ob + (size_t)t * D + 16 * dt + 4 * g4) =
+            O[dt] * inv;
     }
     if (c == a.T - 1 && hg == 0) {
       __syncthreads();
