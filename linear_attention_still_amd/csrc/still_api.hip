@@ -196,21 +196,35 @@ int launch_prefill(const Derived& d, const Plan& pl, still::PrefillArgs a, hipSt
   return hipGetLastError() == hipSuccess ? STILL_OK : STILL_EHIP;
 }
 
+template <typename T, int D, int G>
+int launch_decode_g(const Derived& d, still::DecodeArgs a, hipStream_t s) {
+  using namespace still;
+  const size_t lds = DecLds<T, D, G>::bytes(d.W, a.n_keys_max);
+  if (lds > 160 * 1024) return STILL_EUNSUPPORTED;
+  static bool attr = false;
+  if (!attr) {
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_kernel<T, D, G>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    attr = true;
+  }
+  decode_kernel<T, D, G><<<dim3(d.Hkv, d.B), dim3(DEC_THREADS), lds, s>>>(a);
+  return hipGetLastError() == hipSuccess ? STILL_OK : STILL_EHIP;
+}
+
 template <typename T, int D>
 int launch_decode(const Derived& d, still::DecodeArgs a, hipStream_t s) {
   using namespace still;
-  const size_t floats = (size_t)d.G * D * 2 + 16 * D * 4 + 32 + 8 + 32 + (size_t)d.G * D +
-                        256 * (size_t)d.G;
-  const size_t lds = floats * 4 + (size_t)(d.C + 8) * 4 + (size_t)(d.G * d.W + d.C + 8) * 8 +
-                     (size_t)d.G * a.n_keys_max * 4;
-  static bool attr = false;
-  if (!attr) {
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_kernel<T, D>),
-                        hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-    attr = true;
+  if (a.boundary) {
+    const size_t lds = DecLds<T, D, 1>::uni + DecLds<T, D, 1>::map_bytes;
+    decode_boundary_kernel<T, D><<<dim3(d.Hkv, d.B), dim3(DEC_THREADS), lds, s>>>(a);
+    if (hipGetLastError() != hipSuccess) return STILL_EHIP;
   }
-  decode_kernel<T, D><<<dim3(d.Hkv, d.B), dim3(256), lds, s>>>(a);
-  return hipGetLastError() == hipSuccess ? STILL_OK : STILL_EHIP;
+  switch (d.G) {
+    case 1: return launch_decode_g<T, D, 1>(d, a, s);
+    case 2: return launch_decode_g<T, D, 2>(d, a, s);
+    case 4: return launch_decode_g<T, D, 4>(d, a, s);
+    default: return launch_decode_g<T, D, 8>(d, a, s);
+  }
 }
 
 void fill_state_offsets(const still_state_layout& L, long* unit, long* S, long* z, long* pk,
