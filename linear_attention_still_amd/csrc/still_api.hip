@@ -199,7 +199,7 @@ int launch_prefill(const Derived& d, const Plan& pl, still::PrefillArgs a, hipSt
 template <typename T, int D, int G>
 int launch_decode_g(const Derived& d, still::DecodeArgs a, hipStream_t s) {
   using namespace still;
-  const size_t lds = DecLds<T, D, G>::bytes(d.W, a.n_keys_max);
+  const size_t lds = DecLds<T, D, G>::bytes(d.W);
   if (lds > 160 * 1024) return STILL_EUNSUPPORTED;
   static bool attr = false;
   if (!attr) {
@@ -215,7 +215,7 @@ template <typename T, int D>
 int launch_decode(const Derived& d, still::DecodeArgs a, hipStream_t s) {
   using namespace still;
   if (a.boundary) {
-    const size_t lds = DecLds<T, D, 1>::uni + DecLds<T, D, 1>::map_bytes;
+    const size_t lds = DecLds<T, D, 1>::uni + DecLds<T, D, 1>::fold_bytes;
     decode_boundary_kernel<T, D><<<dim3(d.Hkv, d.B), dim3(DEC_THREADS), lds, s>>>(a);
     if (hipGetLastError() != hipSuccess) return STILL_EHIP;
   }
@@ -408,7 +408,6 @@ int still_decode_step(const still_params* p, int64_t pos, const void* q, const v
   a.t = (int)pos;
   a.boundary = (pos % d.C) == 0 ? 1 : 0;
   a.fp32_out = (p->flags & STILL_FLAG_FP32_OUT) ? 1 : 0;
-  a.n_keys_max = d.P + (d.W > d.C ? d.W : d.C) + d.W + d.C + 1;
   a.scale = d.scale;
   a.eps = d.eps;
   a.scale64 = d.scale64;

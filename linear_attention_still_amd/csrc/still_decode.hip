@@ -25,8 +25,10 @@
 //      (its window logits come from the same pass over the ring keys).
 //
 // The step is bound by HBM reads (pool and ring K/V, S): rows are read as
-// 16-byte vectors, D / (16 / sizeof(T)) consecutive lanes per row, several
-// rows in flight per lane, and partial sums are combined through LDS once.
+// 8-byte vectors, D * sizeof(T) / 8 consecutive lanes per row, several rows
+// in flight per lane, and partial sums are combined through LDS once. Two
+// workgroups fit on a CU (at most 128 VGPRs, small LDS), so every unit of a
+// 512-unit step is resident at once.
 #include "still_common.h"
 
 namespace still {
@@ -40,7 +42,7 @@ struct DecodeArgs {
   char* state;
   void* out;         // [B][Hq][D]
   int32_t* sel_new;  // [B][Hkv][lam] or null
-  int B, Hq, Hkv, G, W, C, m, lam, R, t, boundary, fp32_out, n_keys_max;
+  int B, Hq, Hkv, G, W, C, m, lam, R, t, boundary, fp32_out;
   float scale, eps;
   double scale64, eps64;  // the same parameters for the float64 score
   long st_unit, st_S, st_z, st_pool_k, st_pool_v, st_pool_pos, st_ring_k, st_ring_v,
@@ -49,49 +51,53 @@ struct DecodeArgs {
 
 constexpr int DEC_THREADS = 512;
 constexpr int DEC_WAVES = DEC_THREADS / 64;
-constexpr int DEC_MAP_ROWS = 16;  // rows per NP-Map batch
 
 // LDS carve-up of the decode kernel, in bytes from the base.
 template <typename T, int D, int G>
 struct DecLds {
   static constexpr size_t qs = 0;                                  // f32 [G][D]
   static constexpr size_t phq = qs + (size_t)G * D * 4;            // f32 [G][D]
-  static constexpr size_t hv = phq + (size_t)G * D * 4;            // f32 [G][4]
-  static constexpr size_t ibuf = hv + (size_t)G * 4 * 4;           // int [2 + 130]
+  static constexpr size_t hv = phq + (size_t)G * D * 4;            // f32 [G][12]
+  static constexpr size_t ml = hv + (size_t)G * 12 * 4;            // f32 [waves][G][2]
+  static constexpr size_t ibuf = ml + (size_t)DEC_WAVES * G * 2 * 4;  // int [2 + 130]
   static constexpr size_t d64 = ibuf + (2 + 130) * 4;              // f64 [128 + 8]
   static constexpr size_t rowst = d64 + (128 + 8) * 8;             // f32 [16][2]
-  static constexpr size_t uni = rowst + DEC_MAP_ROWS * 2 * 4;      // union below
-  // union member 1 (NP-Map and fold): xs, us, ph, vs f32 [16][D] each
-  static constexpr size_t map_bytes = (size_t)4 * DEC_MAP_ROWS * D * 4;
+  static constexpr size_t uni = rowst + 16 * 2 * 4;                // union below
+  // union member 1 (NP-Map and fold): xs, us, ph, vs [8][D] and red8
+  // [waves][8][D] f32 in the boundary kernel; xs, us, ph [G+1][D] and red8
+  // [waves][G+1][D] per token
+  static constexpr size_t fold_bytes = (size_t)(4 + DEC_WAVES) * 8 * D * 4;
+  static constexpr size_t mapg_bytes = (size_t)(3 + DEC_WAVES) * (G + 1) * D * 4;
   // union member 2 (value and state partial sums): f32 [2][waves][G][D]
   static constexpr size_t red_bytes = (size_t)2 * DEC_WAVES * G * D * 4;
-  static constexpr size_t uni_bytes = map_bytes > red_bytes ? map_bytes : red_bytes;
+  static constexpr size_t uni_bytes = mapg_bytes > red_bytes ? mapg_bytes : red_bytes;
   static constexpr size_t lg = uni + uni_bytes;                    // f64 [G][W] (runtime W)
-  __host__ __device__ static size_t lw(int W) { return lg + (size_t)G * W * 8; }  // f32 [G][NK]
-  __host__ __device__ static size_t bytes(int W, int NK) { return lw(W) + (size_t)G * NK * 4; }
+  __host__ __device__ static size_t bytes(int W) { return lg + (size_t)G * W * 8; }
 };
 
-// 16 bytes of a row as floats.
+// 8 bytes of a row as floats: rows are read as 8-byte vectors, so a row of
+// D elements spans D * sizeof(T) / 8 lanes.
 template <typename T>
 struct RowVec;
 template <>
 struct RowVec<bf16> {
-  static constexpr int N = 8;
-  __device__ __forceinline__ static void get(const uint4& u, float (&x)[8]) {
+  static constexpr int N = 4;
+  __device__ __forceinline__ static void get(const uint2& u, float (&x)[4]) {
     const bf16* e = reinterpret_cast<const bf16*>(&u);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) x[i] = (float)e[i];
+    for (int i = 0; i < 4; ++i) x[i] = (float)e[i];
   }
 };
 template <>
 struct RowVec<float> {
-  static constexpr int N = 4;
-  __device__ __forceinline__ static void get(const uint4& u, float (&x)[4]) {
+  static constexpr int N = 2;
+  __device__ __forceinline__ static void get(const uint2& u, float (&x)[2]) {
     const float* e = reinterpret_cast<const float*>(&u);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) x[i] = e[i];
+    x[0] = e[0];
+    x[1] = e[1];
   }
 };
+__device__ __forceinline__ uint2 ld8(const void* p) { return *reinterpret_cast<const uint2*>(p); }
 
 // Sum over the n consecutive lanes (n a power of two) that hold one row.
 template <int N>
@@ -117,27 +123,62 @@ __device__ __forceinline__ float wave_sum(float x) {
   return x;
 }
 
-// NP-Map [P3 "NP-Map: Norm-Preserving Feature Map"] of n <= 16 rows of xs
-// (float32, row stride D) into ph; reading: ||x|| * softmax(x F) /
-// ||softmax(x F)||, exact expf. us is scratch; rowst holds (max, scale).
-// All threads; ends with a barrier.
-template <typename T, int D>
-__device__ __forceinline__ void np_map_rows(const T* F, const float* xs, int n, float* us,
-                                            float* ph, float* rowst) {
+// NP-Map [P3 "NP-Map: Norm-Preserving Feature Map"] of NR <= 9 rows, reading:
+// ||x|| * softmax(x F) / ||softmax(x F)|| with exact expf. u = x F with the rows
+// of F read once as 16-byte vectors (all loads of a lane in flight at once),
+// partial sums over the F rows reduced across lanes and then across waves
+// through red8 [waves][NR][D]. xs, us, ph are [NR][D] float32 in LDS. All
+// threads; ends with a barrier.
+template <typename T, int D, int NR>
+__device__ __forceinline__ void np_map_vec(const T* F, const float* xs, float* red8, float* us,
+                                           float* ph, float* rowst) {
+  constexpr int VEC = RowVec<T>::N, LPK = D / VEC, KPW = 64 / LPK;
+  constexpr int ITS = D / (DEC_WAVES * KPW);  // F rows per lane
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  for (int e = tid; e < n * D; e += DEC_THREADS) {
-    const int r = e / D, j = e % D;
-    const float* x = xs + r * D;
-    float u0 = 0.f, u1 = 0.f;
-#pragma unroll 8
-    for (int i = 0; i < D; i += 2) {
-      u0 += x[i] * to_f32(F[(size_t)i * D + j]);
-      u1 += x[i + 1] * to_f32(F[(size_t)(i + 1) * D + j]);
+  const int part = lane % LPK, grp = lane / LPK;
+  float acc[NR][VEC];
+#pragma unroll
+  for (int r = 0; r < NR; ++r)
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) acc[r][e] = 0.f;
+  uint2 raw[ITS];
+#pragma unroll
+  for (int it = 0; it < ITS; ++it) {
+    const int i = (it * DEC_WAVES + wave) * KPW + grp;
+    raw[it] = ld8(F + (size_t)i * D + part * VEC);
+  }
+#pragma unroll
+  for (int it = 0; it < ITS; ++it) {
+    const int i = (it * DEC_WAVES + wave) * KPW + grp;
+    float f[VEC];
+    RowVec<T>::get(raw[it], f);
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+      const float x = xs[r * D + i];
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) acc[r][e] += x * f[e];
     }
-    us[e] = u0 + u1;
+  }
+#pragma unroll
+  for (int r = 0; r < NR; ++r)
+#pragma unroll
+    for (int e = 0; e < VEC; ++e)
+#pragma unroll
+      for (int o = LPK; o < 64; o <<= 1) acc[r][e] += __shfl_xor(acc[r][e], o);
+  if (grp == 0)
+#pragma unroll
+    for (int r = 0; r < NR; ++r)
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) red8[(wave * NR + r) * D + part * VEC + e] = acc[r][e];
+  __syncthreads();
+  for (int e = tid; e < NR * D; e += DEC_THREADS) {
+    float u = 0.f;
+#pragma unroll
+    for (int w = 0; w < DEC_WAVES; ++w) u += red8[w * NR * D + e];
+    us[e] = u;
   }
   __syncthreads();
-  for (int r = wave; r < n; r += DEC_WAVES) {
+  for (int r = wave; r < NR; r += DEC_WAVES) {
     float mx = STILL_NEG_INF, xn = 0.f;
     for (int j = lane; j < D; j += 64) {
       mx = fmaxf(mx, us[r * D + j]);
@@ -157,13 +198,12 @@ __device__ __forceinline__ void np_map_rows(const T* F, const float* xs, int n, 
     }
   }
   __syncthreads();
-  for (int e = tid; e < n * D; e += DEC_THREADS) {
+  for (int e = tid; e < NR * D; e += DEC_THREADS) {
     const int r = e / D;
     ph[e] = expf(us[e] - rowst[2 * r]) * rowst[2 * r + 1];
   }
   __syncthreads();
 }
-
 
 // Chunk boundary (position t = cC): decide chunk c-1 by Top-lambda over its
 // float64 scores, append the kept tokens to the pool [P2 固定预算路由], and
@@ -194,10 +234,12 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_boundary_kernel(DecodeArgs
   int* ibuf = reinterpret_cast<int*>(smem + LD::ibuf);
   double* d64 = reinterpret_cast<double*>(smem + LD::d64);
   float* rowst = reinterpret_cast<float*>(smem + LD::rowst);
-  float* xs = reinterpret_cast<float*>(smem + LD::uni);
-  float* us = xs + DEC_MAP_ROWS * D;
-  float* ph = us + DEC_MAP_ROWS * D;
-  float* vs = ph + DEC_MAP_ROWS * D;
+  constexpr int FR = 8;  // rows per fold group
+  float* xs = reinterpret_cast<float*>(smem + LD::uni);  // [FR][D]
+  float* us = xs + FR * D;
+  float* ph = us + FR * D;
+  float* vs = ph + FR * D;
+  float* red8 = vs + FR * D;  // [waves][FR][D]
   if (meta[0] != t || meta[2] != 0) return;
   int n_pool = (int)meta[1];
   const int c = t / C, cC = c * C;
@@ -223,8 +265,8 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_boundary_kernel(DecodeArgs
     if (kept[j] < 0) continue;
     const int pos = base + j, slot = pos % R, row = n_pool + kept[j];
     const size_t src = (size_t)slot * D + part * VEC, dst = (size_t)row * D + part * VEC;
-    *reinterpret_cast<uint4*>(pool_k + dst) = *reinterpret_cast<const uint4*>(ring_k + src);
-    *reinterpret_cast<uint4*>(pool_v + dst) = *reinterpret_cast<const uint4*>(ring_v + src);
+    *reinterpret_cast<uint2*>(pool_k + dst) = ld8(ring_k + src);
+    *reinterpret_cast<uint2*>(pool_v + dst) = ld8(ring_v + src);
     if (part == 0) {
       pool_pos[row] = pos;
       ring_flag[slot] = 1;
@@ -246,9 +288,9 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_boundary_kernel(DecodeArgs
 #pragma unroll
   for (int q2 = 0; q2 < PER; ++q2) dacc[q2] = 0.f;
   float dz = 0.f;
-  for (int g0 = f_lo; g0 < f_hi; g0 += DEC_MAP_ROWS) {
-    const int n = min(DEC_MAP_ROWS, f_hi - g0);
-    for (int e = tid; e < DEC_MAP_ROWS * D; e += DEC_THREADS) {
+  for (int g0 = f_lo; g0 < f_hi; g0 += FR) {
+    const int n = min(FR, f_hi - g0);
+    for (int e = tid; e < FR * D; e += DEC_THREADS) {
       const int r = e / D, i = e % D, pos = g0 + r;
       const int slot = pos % R;
       const bool use = r < n && ring_flag[slot] == 0;
@@ -256,17 +298,17 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_boundary_kernel(DecodeArgs
       vs[e] = use ? to_f32(ring_v[(size_t)slot * D + i]) : 0.f;
     }
     __syncthreads();
-    np_map_rows<T, D>(F, xs, DEC_MAP_ROWS, us, ph, rowst);
+    np_map_vec<T, D, FR>(F, xs, red8, us, ph, rowst);
     // thread tid owns S[i][jv] for jv = tid % D and i = tid / D + q2 * (512 / D)
 #pragma unroll 1
-    for (int r = 0; r < DEC_MAP_ROWS; ++r) {
+    for (int r = 0; r < FR; ++r) {
       const float vr = vs[r * D + tid % D];
       const float* pr = ph + r * D + tid / D;
 #pragma unroll
       for (int q2 = 0; q2 < PER; ++q2) dacc[q2] += pr[q2 * (DEC_THREADS / D)] * vr;
     }
     if (tid < D)
-      for (int r = 0; r < DEC_MAP_ROWS; ++r) dz += ph[r * D + tid];
+      for (int r = 0; r < FR; ++r) dz += ph[r * D + tid];
     __syncthreads();
   }
   if (f_hi > f_lo) {
@@ -278,14 +320,15 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_boundary_kernel(DecodeArgs
 }
 
 template <typename T, int D, int G>
-__global__ __launch_bounds__(DEC_THREADS) void decode_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(DEC_THREADS) __attribute__((amdgpu_waves_per_eu(G >= 8 ? 2 : 4)))
+void decode_kernel(DecodeArgs a) {
   using LD = DecLds<T, D, G>;
-  constexpr int VEC = RowVec<T>::N;  // elements per 16-byte vector
+  constexpr int VEC = RowVec<T>::N;  // elements per 8-byte vector
   constexpr int LPK = D / VEC;       // lanes per K/V row
   constexpr int KPW = 64 / LPK;      // rows per wave and vector load
   constexpr int SL = D / 4;          // lanes per S row (float4)
   constexpr int RPW = 64 / SL;       // S rows per wave and vector load
-  constexpr int U = G >= 8 ? 2 : 4;  // rows in flight per lane
+  constexpr int U = 4;               // rows in flight per lane
   extern __shared__ __align__(16) char smem[];
   const int kv = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
@@ -311,14 +354,12 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_kernel(DecodeArgs a) {
   int* ibuf = reinterpret_cast<int*>(smem + LD::ibuf);
   double* d64 = reinterpret_cast<double*>(smem + LD::d64);
   float* rowst = reinterpret_cast<float*>(smem + LD::rowst);
-  float* xs = reinterpret_cast<float*>(smem + LD::uni);
-  float* us = xs + DEC_MAP_ROWS * D;
-  float* ph = us + DEC_MAP_ROWS * D;
-  float* vs = ph + DEC_MAP_ROWS * D;
+  float* xs = reinterpret_cast<float*>(smem + LD::uni);  // [G+1][D] q rows, then k
+  float* us = xs + (G + 1) * D;
+  float* ph = us + (G + 1) * D;
+  float* red8 = ph + (G + 1) * D;  // [waves][G+1][D]
   float* red = reinterpret_cast<float*>(smem + LD::uni);  // [2][waves][G][D]
   double* lg = reinterpret_cast<double*>(smem + LD::lg);
-  float* lw = reinterpret_cast<float*>(smem + LD::lw(W));
-  const int NK = a.n_keys_max;
 
   if (meta[0] != t || meta[2] != 0) {
     __syncthreads();
@@ -347,7 +388,7 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_kernel(DecodeArgs a) {
     xs[e] = x;
   }
   __syncthreads();
-  np_map_rows<T, D>(F, xs, G + 1, us, ph, rowst);
+  np_map_vec<T, D, G + 1>(F, xs, red8, us, ph, rowst);
   for (int e = tid; e < G * D; e += DEC_THREADS) phq[e] = ph[e];
   for (int i = tid; i < D; i += DEC_THREADS) ring_phi[(size_t)slot_t * D + i] = from_f32<T>(ph[G * D + i]);
 
@@ -371,20 +412,90 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_kernel(DecodeArgs a) {
   const int la_lo = full_chunks_before(c, W, C) * C;
   const int la_hi = min(t - W, cC - 1);  // inclusive
   const int n_la = la_hi >= la_lo ? la_hi - la_lo + 1 : 0;
-  const int n_keys = n_sa + n_la;
   const int sc_lo = t - W + 1 > 0 ? t - W + 1 : 0;  // score window
 
+  float* redA = red;                                          // [waves][G][D]
+  float* redS = red + DEC_WAVES * G * D;                      // [waves][G][D]
+  float* mlw = reinterpret_cast<float*>(smem + LD::ml);       // [waves][G][2]
   const int part = lane % LPK, grp = lane / LPK;
-  auto key_row = [&](int kk) -> const T* {
-    return kk < n_oob ? pool_k + (size_t)kk * D : ring_k + (size_t)((lo + kk - n_oob) % R) * D;
-  };
-  auto val_row = [&](int kk) -> const T* {
-    if (kk < n_oob) return pool_v + (size_t)kk * D;
-    if (kk < n_sa) return ring_v + (size_t)((lo + kk - n_oob) % R) * D;
-    return ring_v + (size_t)((la_lo + kk - n_sa) % R) * D;
-  };
 
-  // ---- 3a. softmax logits (float32) and window logits (float64) -----------
+  // ---- 3a. state readout partials: sum_i phi_h[i] S[i][f] ----------------
+  {
+    float accS[G][4];
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) accS[h][e] = 0.f;
+    const int sp = lane % SL, sg = lane / SL;
+    constexpr int ROUNDS = D / (DEC_WAVES * RPW);
+    f32x4 sv[ROUNDS];
+#pragma unroll
+    for (int rr = 0; rr < ROUNDS; ++rr) {
+      const int i = (rr * DEC_WAVES + wave) * RPW + sg;
+      sv[rr] = *reinterpret_cast<const f32x4*>(S + (size_t)i * D + sp * 4);
+    }
+#pragma unroll
+    for (int rr = 0; rr < ROUNDS; ++rr) {
+      const int i = (rr * DEC_WAVES + wave) * RPW + sg;
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const float p = phq[h * D + i];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) accS[h][e] += p * sv[rr][e];
+      }
+    }
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+#pragma unroll
+        for (int o = SL; o < 64; o <<= 1) accS[h][e] += __shfl_xor(accS[h][e], o);
+    if (sg == 0)
+#pragma unroll
+      for (int h = 0; h < G; ++h)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) redS[(wave * G + h) * D + sp * 4 + e] = accS[h][e];
+  }
+
+  // ---- 3b. one streaming pass over the keys: running max m, sum l and
+  //         weighted values per (row group, head); softmax keys take
+  //         logits, linear keys log(g) + log <phi(q), phi(k)> -------------
+  float m[G], l[G], acc[G][VEC];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    m[h] = STILL_NEG_INF;
+    l[h] = 0.f;
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) acc[h][e] = 0.f;
+  }
+  // folds U keys of log-weights s[u][h] and values rv[u] into (m, l, acc)
+  auto absorb = [&](const float (&s)[U][G], const uint2 (&rv)[U]) {
+    float al[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      float mb = m[h];
+#pragma unroll
+      for (int u = 0; u < U; ++u) mb = fmaxf(mb, s[u][h]);
+      // rows with nothing visible yet keep m = -inf and zero sums
+      al[h] = (m[h] == STILL_NEG_INF || mb == STILL_NEG_INF) ? 0.f : __expf(m[h] - mb);
+      m[h] = mb;
+      l[h] *= al[h];
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) acc[h][e] *= al[h];
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      float x[VEC];
+      RowVec<T>::get(rv[u], x);
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const float p = s[u][h] == STILL_NEG_INF ? 0.f : __expf(s[u][h] - m[h]);
+        l[h] += p;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) acc[h][e] += p * x[e];
+      }
+    }
+  };
   {
     float qv[G][VEC];
 #pragma unroll
@@ -392,65 +503,102 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_kernel(DecodeArgs a) {
 #pragma unroll
       for (int e = 0; e < VEC; ++e) qv[h][e] = qs[h * D + part * VEC + e];
     for (int k0 = wave * KPW * U; k0 < n_sa; k0 += DEC_WAVES * KPW * U) {
-      uint4 raw[U];
+      uint2 rk[U], rv[U];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int kk = k0 + u * KPW + grp;
-        raw[u] = kk < n_sa ? *reinterpret_cast<const uint4*>(key_row(kk) + part * VEC)
-                           : uint4{0, 0, 0, 0};
+        const bool ok = kk < n_sa;
+        const size_t row = kk < n_oob ? (size_t)kk : (size_t)((lo + kk - n_oob) % R);
+        rk[u] = ok ? ld8((kk < n_oob ? pool_k : ring_k) + row * D + part * VEC) : uint2{0, 0};
+        rv[u] = ok ? ld8((kk < n_oob ? pool_v : ring_v) + row * D + part * VEC) : uint2{0, 0};
       }
+      float s[U][G];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int kk = k0 + u * KPW + grp;
         float x[VEC];
-        RowVec<T>::get(raw[u], x);
+        RowVec<T>::get(rk[u], x);
         const int pos = kk < n_oob ? -1 : lo + kk - n_oob;
         const bool in_sc = kk < n_sa && pos >= sc_lo;  // uniform over the row's lanes
 #pragma unroll
         for (int h = 0; h < G; ++h) {
-          float s = 0.f;
+          float d = 0.f;
 #pragma unroll
-          for (int e = 0; e < VEC; ++e) s += qv[h][e] * x[e];
-          s = sum_lanes<LPK>(s);
-          if (part == 0 && kk < n_sa) lw[h * NK + kk] = s * a.scale;
+          for (int e = 0; e < VEC; ++e) d += qv[h][e] * x[e];
+          d = sum_lanes<LPK>(d);
+          s[u][h] = kk < n_sa ? d * a.scale : STILL_NEG_INF;
           if (in_sc) {  // products of bf16/f32 values are exact in float64
-            double s64 = 0.0;
+            double d64s = 0.0;
 #pragma unroll
-            for (int e = 0; e < VEC; ++e) s64 += (double)qv[h][e] * (double)x[e];
-            s64 = sum_lanes_f64<LPK>(s64);
-            if (part == 0) lg[h * W + (pos - sc_lo)] = a.scale64 * s64;
+            for (int e = 0; e < VEC; ++e) d64s += (double)qv[h][e] * (double)x[e];
+            d64s = sum_lanes_f64<LPK>(d64s);
+            if (part == 0) lg[h * W + (pos - sc_lo)] = a.scale64 * d64s;
           }
         }
       }
+      absorb(s, rv);
     }
   }
-  // ---- 3b. gated linear weights of the unfolded ring tokens ----------------
-  {
-    float pv[G][VEC];
+  if (n_la > 0) {
+    float pv[G][VEC], lgate[G];
 #pragma unroll
-    for (int h = 0; h < G; ++h)
+    for (int h = 0; h < G; ++h) {
+      const float g = a.gate[kv * G + h];
+      lgate[h] = g > 0.f ? __logf(g) : STILL_NEG_INF;
 #pragma unroll
       for (int e = 0; e < VEC; ++e) pv[h][e] = phq[h * D + part * VEC + e];
-    for (int k0 = wave * KPW; k0 < n_la; k0 += DEC_WAVES * KPW) {
-      const int kk = k0 + grp;
-      const int slot = (la_lo + kk) % R;
-      uint4 raw = uint4{0, 0, 0, 0};
-      bool la = false;
-      if (kk < n_la) {
-        raw = *reinterpret_cast<const uint4*>(ring_phi + (size_t)slot * D + part * VEC);
-        la = ring_flag[slot] == 0;
+    }
+    for (int k0 = wave * KPW * U; k0 < n_la; k0 += DEC_WAVES * KPW * U) {
+      uint2 rk[U], rv[U];
+      bool la[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int kk = k0 + u * KPW + grp;
+        const size_t slot = (size_t)((la_lo + kk) % R);
+        la[u] = kk < n_la && ring_flag[slot] == 0;
+        rk[u] = la[u] ? ld8(ring_phi + slot * D + part * VEC) : uint2{0, 0};
+        rv[u] = la[u] ? ld8(ring_v + slot * D + part * VEC) : uint2{0, 0};
       }
-      float x[VEC];
-      RowVec<T>::get(raw, x);
+      float s[U][G];
 #pragma unroll
-      for (int h = 0; h < G; ++h) {
-        float w = 0.f;
+      for (int u = 0; u < U; ++u) {
+        float x[VEC];
+        RowVec<T>::get(rk[u], x);
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) w += pv[h][e] * x[e];
-        w = sum_lanes<LPK>(w);
-        const float g = a.gate[kv * G + h];
-        if (part == 0 && kk < n_la)
-          lw[h * NK + n_sa + kk] = (la && w > 0.f && g > 0.f) ? __logf(g) + __logf(w) : STILL_NEG_INF;
+        for (int h = 0; h < G; ++h) {
+          float w = 0.f;
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) w += pv[h][e] * x[e];
+          w = sum_lanes<LPK>(w);
+          s[u][h] = (la[u] && w > 0.f) ? lgate[h] + __logf(w) : STILL_NEG_INF;
+        }
+      }
+      absorb(s, rv);
+    }
+  }
+  // merge the row groups of each wave, then publish per wave
+#pragma unroll
+  for (int o = LPK; o < 64; o <<= 1) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float m2 = __shfl_xor(m[h], o), l2 = __shfl_xor(l[h], o);
+      const float mm = fmaxf(m[h], m2);
+      const float a1 = m[h] == STILL_NEG_INF ? 0.f : __expf(m[h] - mm);
+      const float a2 = m2 == STILL_NEG_INF ? 0.f : __expf(m2 - mm);
+      l[h] = l[h] * a1 + l2 * a2;
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) acc[h][e] = acc[h][e] * a1 + __shfl_xor(acc[h][e], o) * a2;
+      m[h] = mm;
+    }
+  }
+  if (grp == 0) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) redA[(wave * G + h) * D + part * VEC + e] = acc[h][e];
+      if (part == 0) {
+        mlw[(wave * G + h) * 2] = m[h];
+        mlw[(wave * G + h) * 2 + 1] = l[h];
       }
     }
   }
@@ -460,8 +608,7 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_kernel(DecodeArgs a) {
   //         normaliser of each head (wave h) --------------------------------
   if (wave < G) {
     const int h = wave;
-    // score: KL(a_diag || (1-eps) a_nodiag + eps delta_t) in float64
-    {
+    {  // score: KL(a_diag || (1-eps) a_nodiag + eps delta_t) in float64
       const int n = t - sc_lo + 1;
       const double* x = lg + h * W;
       double mx = -__builtin_huge_val();
@@ -490,28 +637,31 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_kernel(DecodeArgs a) {
         d64[128 + h] = sc;
       }
     }
-    // state as a virtual key: log-weight log(g * phi(q).z)
+    // the state as a virtual key: log-weight log(g * phi(q).z), value
+    // S^T phi(q) / phi(q).z; one normaliser over the waves' partials
     float dz = 0.f;
     for (int i = lane; i < D; i += 64) dz += phq[h * D + i] * z[i];
     dz = wave_sum(dz);
     const float g = a.gate[kv * G + h];
     const float lws = (g > 0.f && dz > 0.f) ? __logf(g * dz) : STILL_NEG_INF;
     float mx = lws;
-    for (int kk = lane; kk < n_keys; kk += 64) mx = fmaxf(mx, lw[h * NK + kk]);
-    mx = wave_max(mx);
-    float sum = 0.f;
-    for (int kk = lane; kk < n_keys; kk += 64) {
-      const float x = lw[h * NK + kk];
-      const float e = x == STILL_NEG_INF ? 0.f : __expf(x - mx);
-      lw[h * NK + kk] = e;
-      sum += e;
+#pragma unroll
+    for (int w = 0; w < DEC_WAVES; ++w) mx = fmaxf(mx, mlw[(w * G + h) * 2]);
+    if (lane < DEC_WAVES) {
+      const float mw = mlw[(lane * G + h) * 2];
+      hv[h * 12 + 4 + lane] = mw == STILL_NEG_INF ? 0.f : __expf(mw - mx);
     }
-    sum = wave_sum(sum);
     if (lane == 0) {
+      float tot = 0.f;
+#pragma unroll
+      for (int w = 0; w < DEC_WAVES; ++w) {
+        const float mw = mlw[(w * G + h) * 2];
+        tot += mw == STILL_NEG_INF ? 0.f : mlw[(w * G + h) * 2 + 1] * __expf(mw - mx);
+      }
       const float es = lws == STILL_NEG_INF ? 0.f : __expf(lws - mx);
-      hv[h * 4 + 0] = dz;
-      hv[h * 4 + 1] = es;
-      hv[h * 4 + 2] = sum + es;
+      hv[h * 12 + 0] = dz;
+      hv[h * 12 + 1] = es;
+      hv[h * 12 + 2] = tot + es;
     }
   }
   __syncthreads();
@@ -520,97 +670,15 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_kernel(DecodeArgs a) {
     for (int h = 0; h < G; ++h) tot += d64[128 + h];
     pend[t - cC] = tot;
   }
-
-  // ---- 5. weighted values and the state readout ---------------------------
-  {
-    float acc[G][VEC];
-#pragma unroll
-    for (int h = 0; h < G; ++h)
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) acc[h][e] = 0.f;
-    for (int k0 = wave * KPW * U; k0 < n_keys; k0 += DEC_WAVES * KPW * U) {
-      uint4 raw[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int kk = k0 + u * KPW + grp;
-        raw[u] = kk < n_keys ? *reinterpret_cast<const uint4*>(val_row(kk) + part * VEC)
-                             : uint4{0, 0, 0, 0};
-      }
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int kk = k0 + u * KPW + grp;
-        if (kk >= n_keys) continue;
-        float x[VEC];
-        RowVec<T>::get(raw[u], x);
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-          const float w = lw[h * NK + kk];
-#pragma unroll
-          for (int e = 0; e < VEC; ++e) acc[h][e] += w * x[e];
-        }
-      }
-    }
-    // the row groups of a wave, then the waves (through LDS)
-#pragma unroll
-    for (int h = 0; h < G; ++h)
-#pragma unroll
-      for (int e = 0; e < VEC; ++e)
-#pragma unroll
-        for (int o = LPK; o < 64; o <<= 1) acc[h][e] += __shfl_xor(acc[h][e], o);
-    if (grp == 0)
-#pragma unroll
-      for (int h = 0; h < G; ++h)
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) red[(wave * G + h) * D + part * VEC + e] = acc[h][e];
-  }
-  {
-    // nst[h][f] = sum_i phi_h[i] S[i][f]: rows of S as float4 vectors
-    float acc[G][4];
-#pragma unroll
-    for (int h = 0; h < G; ++h)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) acc[h][e] = 0.f;
-    const int sp = lane % SL, sg = lane / SL;
-    constexpr int ROUNDS = D / (DEC_WAVES * RPW);
-    f32x4 sv[ROUNDS];
-#pragma unroll
-    for (int rr = 0; rr < ROUNDS; ++rr) {
-      const int i = (rr * DEC_WAVES + wave) * RPW + sg;
-      sv[rr] = *reinterpret_cast<const f32x4*>(S + (size_t)i * D + sp * 4);
-    }
-#pragma unroll
-    for (int rr = 0; rr < ROUNDS; ++rr) {
-      const int i = (rr * DEC_WAVES + wave) * RPW + sg;
-#pragma unroll
-      for (int h = 0; h < G; ++h) {
-        const float p = phq[h * D + i];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) acc[h][e] += p * sv[rr][e];
-      }
-    }
-#pragma unroll
-    for (int h = 0; h < G; ++h)
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-#pragma unroll
-        for (int o = SL; o < 64; o <<= 1) acc[h][e] += __shfl_xor(acc[h][e], o);
-    float* red2 = red + DEC_WAVES * G * D;
-    if (sg == 0)
-#pragma unroll
-      for (int h = 0; h < G; ++h)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) red2[(wave * G + h) * D + sp * 4 + e] = acc[h][e];
-  }
-  __syncthreads();
   for (int e = tid; e < G * D; e += DEC_THREADS) {
     const int h = e / D, f = e % D;
     float sv = 0.f, ns = 0.f;
 #pragma unroll
     for (int w = 0; w < DEC_WAVES; ++w) {
-      sv += red[(w * G + h) * D + f];
-      ns += red[((DEC_WAVES + w) * G + h) * D + f];
+      sv += redA[(w * G + h) * D + f] * hv[h * 12 + 4 + w];
+      ns += redS[(w * G + h) * D + f];
     }
-    const float dz = hv[h * 4 + 0], es = hv[h * 4 + 1], tot = hv[h * 4 + 2];
+    const float dz = hv[h * 12 + 0], es = hv[h * 12 + 1], tot = hv[h * 12 + 2];
     if (es > 0.f) sv += es * ns / dz;
     const float y = sv / tot;
     const size_t o = ((size_t)b * a.Hq + kv * G + h) * D + f;
