@@ -167,7 +167,7 @@ int launch_prefill(const Derived& d, const Plan& pl, still::PrefillArgs a, hipSt
   const size_t lds_sel = (size_t)(d.G * d.W + 8 + d.C) * 8 + (size_t)(3 * d.C + 4) * 4;
   set_lds_attr<T, D>();
   mk.at(0, 0);
-  fmap_transpose_kernel<T, D><<<dim3(d.Hkv), dim3(256), 0, s>>>(a);
+  fmap_transpose_kernel<T, D><<<dim3(D * D / 2048, d.Hkv), dim3(256), 0, s>>>(a);
   mk.at(0, 1);
   mk.at(1, 0);
   score_kernel<T, D><<<dim3(pl.T, d.Hkv, d.B), dim3(256), lds_score, s>>>(a);

@@ -57,11 +57,18 @@ struct Pad {
 // ------------------------------------------------------------ 1. F^T ----
 template <typename T, int D>
 __global__ __launch_bounds__(256) void fmap_transpose_kernel(PrefillArgs a) {
-  const T* F = reinterpret_cast<const T*>(a.fmap_w) + (size_t)blockIdx.x * D * D;
-  T* Ft = reinterpret_cast<T*>(a.ft) + (size_t)blockIdx.x * D * D;
-  for (int e = threadIdx.x; e < D * D; e += 256) {
-    const int i = e / D, j = e % D;
-    Ft[(size_t)j * D + i] = F[e];
+  // F^T in fragment order: element ((ft * D/32 + kb) * 64 + lane) * 8 + s
+  // holds F[32 kb + 8 g + s][16 ft + r], lane = 16 g + r, i.e. the B operand
+  // fragments of X F for feature tile ft and d block kb, 8 per lane.
+  const T* F = reinterpret_cast<const T*>(a.fmap_w) + (size_t)blockIdx.y * D * D;
+  T* Ft = reinterpret_cast<T*>(a.ft) + (size_t)blockIdx.y * D * D;
+  const int base = blockIdx.x * 256 * 8;
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    const int e = base + q * 256 + threadIdx.x;
+    const int sl = e & 7, lane = (e >> 3) & 63, pr = e >> 9;
+    const int ftile = pr / (D / 32), kb = pr % (D / 32);
+    Ft[e] = F[(size_t)(32 * kb + 8 * (lane >> 4) + sl) * D + 16 * ftile + (lane & 15)];
   }
 }
 
@@ -373,16 +380,19 @@ struct Blk {
   static constexpr int VS = 64 + Pad<H>::v;
   static constexpr int NFT = D / 16;  // feature (and d_v) tiles
   static constexpr int NPAIR = (D / 16) * (D / 32);
+  static constexpr int PCAP = 1024;   // pool positions staged in LDS per chunk
   static constexpr size_t ks_bytes = 64 * KS * sizeof(T);
   static constexpr size_t vs_bytes = (size_t)D * VS * sizeof(H);
-  static constexpr size_t wf_bytes = (size_t)4 * (D / 32) * 2 * 64 * 8 * sizeof(H);
-  static constexpr size_t rs_bytes = (size_t)NPAIR * 2 * 64 * 8 * sizeof(T);
+  static constexpr size_t wf_bytes = (size_t)4 * (D / 32) * 64 * 8 * sizeof(H);
+  // readout fragments of half the d_v tiles: [NPAIR / 2][hi, lo][64][8]
+  static constexpr size_t rs_bytes = (size_t)(NPAIR / 2) * 2 * 64 * 8 * sizeof(T);
   static constexpr size_t lo_bytes =
       (ks_bytes + vs_bytes + wf_bytes > rs_bytes ? ks_bytes + vs_bytes + wf_bytes : rs_bytes);
   static constexpr size_t sp_bytes = (size_t)NPAIR * 64 * 8 * sizeof(float);
+  static constexpr size_t ft_bytes = (size_t)D * D * sizeof(T);
   static constexpr size_t stat_bytes = (8 * 64 * 2 + 64 * 3) * 4;
-  static constexpr size_t meta_bytes = 64 * 4 + 16 + D * 8;
-  static constexpr size_t bytes = lo_bytes + sp_bytes + stat_bytes + meta_bytes;
+  static constexpr size_t meta_bytes = 64 * 4 + 16 + D * 8 + PCAP * 4;
+  static constexpr size_t bytes = lo_bytes + sp_bytes + ft_bytes + stat_bytes + meta_bytes;
 };
 
 template <typename T, int D>
@@ -393,12 +403,14 @@ struct BlkPtr {
   H* WF;
   T* RS;
   float* SP;
+  T* FT;         // F^T of the kv head in fragment order
   float* kmax;   // [8][64] per-wave partial max
   float* ksum;   // [8][64] per-wave partial sum of squares
   float* kstat;  // [3][64]: max, scale, |k|^2
   float* fmask;  // [64]
   uint32_t* selw;
-  double* zs;  // running z of the walk, float64
+  double* zs;     // running z of the walk, float64
+  int32_t* pidx;  // [PCAP] kept-pool positions of the chunk
   __device__ BlkPtr(char* smem) {
     using B_ = Blk<T, D>;
     Ks = reinterpret_cast<T*>(smem);
@@ -406,18 +418,30 @@ struct BlkPtr {
     WF = reinterpret_cast<H*>(smem + B_::ks_bytes + B_::vs_bytes);
     RS = reinterpret_cast<T*>(smem);
     SP = reinterpret_cast<float*>(smem + B_::lo_bytes);
-    kmax = reinterpret_cast<float*>(smem + B_::lo_bytes + B_::sp_bytes);
+    FT = reinterpret_cast<T*>(smem + B_::lo_bytes + B_::sp_bytes);
+    kmax = reinterpret_cast<float*>(smem + B_::lo_bytes + B_::sp_bytes + B_::ft_bytes);
     ksum = kmax + 8 * 64;
     kstat = ksum + 8 * 64;
     fmask = kstat + 3 * 64;
     selw = reinterpret_cast<uint32_t*>(fmask + 64);
     zs = reinterpret_cast<double*>(selw + 4);
+    pidx = reinterpret_cast<int32_t*>(zs + D);
   }
   __device__ float* pair(int p) const { return SP + ((size_t)p * 64 + (threadIdx.x & 63)) * 8; }
-  __device__ H* wf(int kt, int bb, int part) const {
-    return WF + ((size_t)((kt * (D / 32) + bb) * 2 + part) * 64) * 8;
+  __device__ H* wf(int kt, int bb) const { return WF + ((size_t)(kt * (D / 32) + bb) * 64) * 8; }
+  // fragment (feature tile ft, d block kb) of F^T: B operand of X F
+  __device__ const T* ft(int ftile, int kb) const {
+    return FT + ((size_t)(ftile * (D / 32) + kb) * 64 + (threadIdx.x & 63)) * 8;
   }
 };
+
+// Copies F^T of one kv head (fragment order, D*D elements) into LDS.
+template <typename T, int D, int NT>
+__device__ __forceinline__ void load_ft(const BlkPtr<T, D>& P, const T* ftg) {
+  constexpr int N16 = D * D * (int)sizeof(T) / 16;
+  for (int e = threadIdx.x; e < N16; e += NT)
+    reinterpret_cast<uint4*>(P.FT)[e] = reinterpret_cast<const uint4*>(ftg)[e];
+}
 
 // Loads 64 keys/values at the given positions (pos < 0: zero row) into Ks and
 // VTs (values converted to H), with the kept flags as a 64-bit mask, the
@@ -490,7 +514,7 @@ __device__ __forceinline__ void load_block(const BlkPtr<T, D>& P, __amdgpu_buffe
 // 16-row tile whose B fragments of X^T are xf[], the feature values in the
 // accumulator layout of (X F)^T: out[ft][i] = phi(x_r)[16 ft + 4g + i].
 template <typename T, int D>
-__device__ __forceinline__ void np_map_tile(__amdgpu_buffer_rsrc_t ftr, const Frag<T>* xf, f32x4* out) {
+__device__ __forceinline__ void np_map_tile(const BlkPtr<T, D>& P, const Frag<T>* xf, f32x4* out) {
   const int lane = threadIdx.x & 63, r16 = lane & 15, g4 = lane >> 4;
   float xn2 = 0.f;
 #pragma unroll
@@ -502,8 +526,7 @@ __device__ __forceinline__ void np_map_tile(__amdgpu_buffer_rsrc_t ftr, const Fr
     out[ft] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kb = 0; kb < D / 32; ++kb)
-      mma(out[ft], ld_frag_buf<T>(ftr, (r16 * D + 8 * g4) * sizeof(T), (16 * ft * D + 32 * kb) * sizeof(T)),
-          xf[kb]);
+      mma(out[ft], ld_frag(P.ft(ft, kb)), xf[kb]);
 #pragma unroll
     for (int i = 0; i < 4; ++i) mx = fmaxf(mx, out[ft][i]);
   }
@@ -547,7 +570,7 @@ __device__ __forceinline__ float sum_over_r(float x) {
 // Four workgroup barriers (five with want_w); every thread must call it with
 // the same want_w.
 template <typename T, int D>
-__device__ __forceinline__ void block_phi(const BlkPtr<T, D>& P, __amdgpu_buffer_rsrc_t ftr, f32x4 (&ph)[4],
+__device__ __forceinline__ void block_phi(const BlkPtr<T, D>& P, f32x4 (&ph)[4],
                                           bool want_w) {
   using B_ = Blk<T, D>;
   typedef typename HalfOf<T>::type H;
@@ -556,8 +579,7 @@ __device__ __forceinline__ void block_phi(const BlkPtr<T, D>& P, __amdgpu_buffer
   if (mine) {
     Frag<T> fb[D / 32];
 #pragma unroll
-    for (int kb = 0; kb < D / 32; ++kb)
-      fb[kb] = ld_frag_buf<T>(ftr, ((16 * wave + r16) * D + 8 * g4) * sizeof(T), 32 * kb * sizeof(T));
+    for (int kb = 0; kb < D / 32; ++kb) fb[kb] = ld_frag(P.ft(wave, kb));
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) {
       ph[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -606,12 +628,7 @@ __device__ __forceinline__ void block_phi(const BlkPtr<T, D>& P, __amdgpu_buffer
         const int key = 16 * kt + 4 * g4 + i;
         const float v = ph[kt][i] * P.kstat[64 + key];
         ph[kt][i] = v;
-        if (want_w) {
-          const H hi = from_f32<H>(v);
-          const int ln = 16 * gp + (key & 15);
-          P.wf(kt, bb, 0)[ln * 8 + sl] = hi;
-          if constexpr (sizeof(H) == 2) P.wf(kt, bb, 1)[ln * 8 + sl] = from_f32<H>(v - to_f32(hi));
-        }
+        if (want_w) P.wf(kt, bb)[(16 * gp + (key & 15)) * 8 + sl] = from_f32<H>(v);
       }
   }
   if (want_w) __syncthreads();  // WF is read by every wave
@@ -724,8 +741,7 @@ __global__ __launch_bounds__(512) void state_delta_kernel(PrefillArgs a) {
   const __amdgpu_buffer_rsrc_t kr = make_rsrc(reinterpret_cast<const T*>(a.k) + (size_t)unit * a.L * D, kv_bytes);
   const __amdgpu_buffer_rsrc_t vr = make_rsrc(reinterpret_cast<const T*>(a.v) + (size_t)unit * a.L * D, kv_bytes);
   const uint8_t* sf = a.selflag + (size_t)unit * a.L;
-  const __amdgpu_buffer_rsrc_t ftr =
-      make_rsrc(reinterpret_cast<const T*>(a.ft) + (size_t)kv * D * D, D * D * sizeof(T));
+  load_ft<T, D, 512>(P, reinterpret_cast<const T*>(a.ft) + (size_t)kv * D * D);
   double sum[D / 16][4];
 #pragma unroll
   for (int vt = 0; vt < D / 16; ++vt)
@@ -739,7 +755,7 @@ __global__ __launch_bounds__(512) void state_delta_kernel(PrefillArgs a) {
     load_block<T, D, 512>(P, kr, vr, kv_bytes, sf, nullptr, 0, blo, hi, lo, hi);
     __syncthreads();
     f32x4 ph[4];
-    block_phi<T, D>(P, ftr, ph, false);
+    block_phi<T, D>(P, ph, false);
     if (wave < B_::NFT) {
 #pragma unroll
       for (int kb2 = 0; kb2 < 2; ++kb2) {
@@ -800,8 +816,9 @@ __global__ __launch_bounds__(256) void state_scan_kernel(float* dS, int NS, int 
 //    a single normaliser over softmax and gated linear weights);
 //  * the next chunk's newly folded tokens are added to the state.
 // Precision: logits from exact bf16 products; the readout with hi/lo bf16
-// splits of S and phi(q); <phi(k),phi(q)> with phi(k) as fp16 hi + lo;
-// softmax weights and values in fp16 (11-bit significands, values exact).
+// splits of S and phi(q); <phi(k),phi(q)> with both features in fp16 (all
+// terms are positive, so the relative error stays within 2^-11); softmax
+// weights and values in fp16 (11-bit significands, bf16 values exact).
 template <typename T, int D>
 __global__ __launch_bounds__(512) void attend_kernel(PrefillArgs a) {
   using B_ = Blk<T, D>;
@@ -824,8 +841,7 @@ __global__ __launch_bounds__(512) void attend_kernel(PrefillArgs a) {
   const __amdgpu_buffer_rsrc_t vr = make_rsrc(reinterpret_cast<const T*>(a.v) + (size_t)unit * L * D, kv_bytes);
   const uint8_t* sf = a.selflag + (size_t)unit * L;
   const int32_t* selu = a.sel + (size_t)unit * a.n_dec * a.lam;
-  const __amdgpu_buffer_rsrc_t ftr =
-      make_rsrc(reinterpret_cast<const T*>(a.ft) + (size_t)kv * D * D, D * D * sizeof(T));
+  load_ft<T, D, 512>(P, reinterpret_cast<const T*>(a.ft) + (size_t)kv * D * D);
   const int n_qt = C / 16;
   const bool act = wave < a.Gs * n_qt;  // wave-uniform
   const int hl = act ? wave / n_qt : 0, qt = act ? wave % n_qt : 0;
@@ -853,18 +869,10 @@ __global__ __launch_bounds__(512) void attend_kernel(PrefillArgs a) {
     const int n_oob = pool_count_at(cf, a.lam, a.cap_chunks);
     const int t = cC + 16 * qt + r16;
 
-    // the state as hi/lo bf16 fragments (split once, shared by every wave)
-    for (int e = tid; e < B_::NPAIR * 64; e += 512) {
-      const float* sp = P.SP + (size_t)e * 8;
-      Frag<T> sh, sl;
-      split2_frag<T>(*reinterpret_cast<const f32x4*>(sp), *reinterpret_cast<const f32x4*>(sp + 4), sh, sl);
-      const int p = e >> 6, ln = e & 63;
-      st_frag(P.RS + ((size_t)(2 * p) * 64 + ln) * 8, sh);
-      st_frag(P.RS + ((size_t)(2 * p + 1) * 64 + ln) * 8, sl);
-    }
-    __syncthreads();
+    // kept-pool positions of the chunk: gather indices of the pool blocks
+    for (int i = tid; i < min(n_oob, B_::PCAP); i += 512) P.pidx[i] = selu[i];
 
-    // query fragments, phi(q), state readout
+    // query fragments, phi(q) (F^T from LDS), state readout
     Frag<T> qf[D / 32];
     Frag<H> pq[D / 32];  // phi(q) as H for <phi(k), phi(q)>
 #pragma unroll
@@ -875,7 +883,7 @@ __global__ __launch_bounds__(512) void attend_kernel(PrefillArgs a) {
     float mrun, lrun;
     {
       f32x4 ph[D / 16];
-      np_map_tile<T, D>(ftr, qf, ph);
+      np_map_tile<T, D>(P, qf, ph);
       float dz = 0.f;
 #pragma unroll
       for (int ft = 0; ft < D / 16; ++ft)
@@ -888,21 +896,38 @@ __global__ __launch_bounds__(512) void attend_kernel(PrefillArgs a) {
         split2_frag<T>(ph[2 * bb], ph[2 * bb + 1], phq[bb], phl[bb]);
         pq[bb] = frag_from<H>(ph[2 * bb], ph[2 * bb + 1]);
       }
+      // S as hi/lo bf16 fragments, split once and shared by every wave, in
+      // two halves of the d_v tiles (the split region holds one half)
+      constexpr int HP = B_::NPAIR / 2;
 #pragma unroll
-      for (int dt = 0; dt < D / 16; ++dt) {
-        O[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int half = 0; half < 2; ++half) {
+        for (int e = tid; e < HP * 64; e += 512) {
+          const float* sp = P.SP + ((size_t)half * HP * 64 + e) * 8;
+          Frag<T> sh, sl;
+          split2_frag<T>(*reinterpret_cast<const f32x4*>(sp), *reinterpret_cast<const f32x4*>(sp + 4), sh, sl);
+          const int pl = e >> 6, ln = e & 63;
+          st_frag(P.RS + ((size_t)(2 * pl) * 64 + ln) * 8, sh);
+          st_frag(P.RS + ((size_t)(2 * pl + 1) * 64 + ln) * 8, sl);
+        }
+        __syncthreads();
 #pragma unroll
-        for (int bb = 0; bb < D / 32; ++bb) {
-          // S^T phi(q) to ~2^-16 relative: hi*hi + lo*hi + hi*lo
-          const int p = dt * (D / 32) + bb;
-          const Frag<T> sh = ld_frag(P.RS + ((size_t)(2 * p) * 64 + lane) * 8);
-          mma(O[dt], sh, phq[bb]);
-          if constexpr (sizeof(T) == 2) {
-            const Frag<T> sl = ld_frag(P.RS + ((size_t)(2 * p + 1) * 64 + lane) * 8);
-            mma(O[dt], sl, phq[bb]);
-            mma(O[dt], sh, phl[bb]);
+        for (int dh = 0; dh < D / 32; ++dh) {
+          const int dt = half * (D / 32) + dh;
+          O[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int bb = 0; bb < D / 32; ++bb) {
+            // S^T phi(q) to ~2^-16 relative: hi*hi + lo*hi + hi*lo
+            const int pl = dh * (D / 32) + bb;
+            const Frag<T> sh = ld_frag(P.RS + ((size_t)(2 * pl) * 64 + lane) * 8);
+            mma(O[dt], sh, phq[bb]);
+            if constexpr (sizeof(T) == 2) {
+              const Frag<T> sl = ld_frag(P.RS + ((size_t)(2 * pl + 1) * 64 + lane) * 8);
+              mma(O[dt], sl, phq[bb]);
+              mma(O[dt], sh, phl[bb]);
+            }
           }
         }
+        if (half == 0) __syncthreads();  // the region is split into again
       }
       if (g > 0.f && dz > 0.f) {
         mrun = log_acc<T>(g * dz);
@@ -928,14 +953,15 @@ __global__ __launch_bounds__(512) void attend_kernel(PrefillArgs a) {
       const bool la_blk = !is_pool && blo < cC;
       const bool do_fold = fold && !is_pool && blo < fold_hi;
       __syncthreads();
-      if (is_pool)
-        load_block<T, D, 512>(P, kr, vr, kv_bytes, sf, selu + blo, nvalid, 0, 0, 0, 0);
+      if (is_pool)  // positions from LDS where staged
+        load_block<T, D, 512>(P, kr, vr, kv_bytes, sf, blo + 64 <= B_::PCAP ? P.pidx + blo : selu + blo,
+                              nvalid, 0, 0, 0, 0);
       else
         load_block<T, D, 512>(P, kr, vr, kv_bytes, sf, nullptr, 0, blo, band_hi, fold_lo, fold_hi);
       __syncthreads();
       if (la_blk || do_fold) {
         f32x4 phk[4];
-        block_phi<T, D>(P, ftr, phk, la_blk);  // ends with a barrier
+        block_phi<T, D>(P, phk, la_blk);  // ends with a barrier
         // the fold writes only SP / zs, which this chunk no longer reads
         if (do_fold) block_fold<T, D>(P, phk);
       }
@@ -967,11 +993,7 @@ __global__ __launch_bounds__(512) void attend_kernel(PrefillArgs a) {
             for (int kt = 0; kt < 4; ++kt) {
               wt[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-              for (int bb = 0; bb < D / 32; ++bb) {
-                // <phi(k), phi(q)> with phi(k) as hi + lo parts
-                mma(wt[kt], ld_frag(P.wf(kt, bb, 0) + lane * 8), pq[bb]);
-                if constexpr (sizeof(H) == 2) mma(wt[kt], ld_frag(P.wf(kt, bb, 1) + lane * 8), pq[bb]);
-              }
+              for (int bb = 0; bb < D / 32; ++bb) mma(wt[kt], ld_frag(P.wf(kt, bb) + lane * 8), pq[bb]);
             }
           }
           const int vis_lo = min(t - W + 1, cC);  // softmax-visible from here
