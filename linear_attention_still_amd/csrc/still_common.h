@@ -80,6 +80,19 @@ __device__ __forceinline__ Frag<float> ld_frag(const float* p) {
   f.hi = *reinterpret_cast<const f32x4*>(p + 4);
   return f;
 }
+// An LDS address the optimizer cannot see through (held in an SGPR).
+// Accesses at constant offsets from it use the 16-bit offset field of the
+// LDS instruction; without this, offsets from a known base above 64 KiB each
+// take an address register of their own, which the compiler hoists out of
+// loops.
+typedef __attribute__((address_space(3))) char lds_char;
+template <typename X>
+__device__ __forceinline__ X* lds_opaque(X* p) {
+  unsigned a = (unsigned)(__UINTPTR_TYPE__)(lds_char*)(char*)p;
+  asm volatile("" : "+s"(a));
+  return (X*)(char*)(lds_char*)(__UINTPTR_TYPE__)a;
+}
+
 // Buffer-resource loads: the lane-dependent part of an address is a 32-bit
 // VGPR offset and the uniform part an SGPR offset, so unrolled loops over
 // uniform offsets need no per-iteration 64-bit address registers. Reads at

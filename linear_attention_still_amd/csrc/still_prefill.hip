@@ -411,21 +411,23 @@ struct BlkPtr {
   uint32_t* selw;
   double* zs;     // running z of the walk, float64
   int32_t* pidx;  // [PCAP] kept-pool positions of the chunk
+  // every region base is opaque (see lds_opaque)
   __device__ BlkPtr(char* smem) {
     using B_ = Blk<T, D>;
-    Ks = reinterpret_cast<T*>(smem);
-    VTs = reinterpret_cast<H*>(smem + B_::ks_bytes);
-    WF = reinterpret_cast<H*>(smem + B_::ks_bytes + B_::vs_bytes);
-    RS = reinterpret_cast<T*>(smem);
-    SP = reinterpret_cast<float*>(smem + B_::lo_bytes);
-    FT = reinterpret_cast<T*>(smem + B_::lo_bytes + B_::sp_bytes);
-    kmax = reinterpret_cast<float*>(smem + B_::lo_bytes + B_::sp_bytes + B_::ft_bytes);
-    ksum = kmax + 8 * 64;
-    kstat = ksum + 8 * 64;
-    fmask = kstat + 3 * 64;
-    selw = reinterpret_cast<uint32_t*>(fmask + 64);
-    zs = reinterpret_cast<double*>(selw + 4);
-    pidx = reinterpret_cast<int32_t*>(zs + D);
+    Ks = lds_opaque(reinterpret_cast<T*>(smem));
+    VTs = lds_opaque(reinterpret_cast<H*>(smem + B_::ks_bytes));
+    WF = lds_opaque(reinterpret_cast<H*>(smem + B_::ks_bytes + B_::vs_bytes));
+    RS = lds_opaque(reinterpret_cast<T*>(smem));
+    SP = lds_opaque(reinterpret_cast<float*>(smem + B_::lo_bytes));
+    FT = lds_opaque(reinterpret_cast<T*>(smem + B_::lo_bytes + B_::sp_bytes));
+    char* st = smem + B_::lo_bytes + B_::sp_bytes + B_::ft_bytes;
+    kmax = lds_opaque(reinterpret_cast<float*>(st));
+    ksum = lds_opaque(reinterpret_cast<float*>(st + 8 * 64 * 4));
+    kstat = lds_opaque(reinterpret_cast<float*>(st + 16 * 64 * 4));
+    fmask = lds_opaque(reinterpret_cast<float*>(st + 19 * 64 * 4));
+    selw = lds_opaque(reinterpret_cast<uint32_t*>(st + 20 * 64 * 4));
+    zs = lds_opaque(reinterpret_cast<double*>(st + 20 * 64 * 4 + 16));
+    pidx = lds_opaque(reinterpret_cast<int32_t*>(st + 20 * 64 * 4 + 16 + D * 8));
   }
   __device__ float* pair(int p) const { return SP + ((size_t)p * 64 + (threadIdx.x & 63)) * 8; }
   __device__ H* wf(int kt, int bb) const { return WF + ((size_t)(kt * (D / 32) + bb) * 64) * 8; }
