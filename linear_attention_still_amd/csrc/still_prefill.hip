@@ -445,68 +445,116 @@ __device__ __forceinline__ void load_ft(const BlkPtr<T, D>& P, const T* ftg) {
     reinterpret_cast<uint4*>(P.FT)[e] = reinterpret_cast<const uint4*>(ftg)[e];
 }
 
-// Loads 64 keys/values at the given positions (pos < 0: zero row) into Ks and
-// VTs (values converted to H), with the kept flags as a 64-bit mask, the
-// fold mask and the keys' squared norms. Values go to VTs four keys at a time: keys 4a..4a+3 land in four
-// adjacent permuted columns. All NT threads take part.
+// A block of 64 keys/values in flight: the global loads of a block are
+// issued into registers (issue_block) while the previous block is still
+// being used, and written to LDS after it (commit_block). Positions come
+// from a gather list (kept pool) or a range; absent rows read past the
+// buffer range and load zeros.
 template <typename T, int D, int NT>
-__device__ __forceinline__ void load_block(const BlkPtr<T, D>& P, __amdgpu_buffer_rsrc_t kr,
-                                           __amdgpu_buffer_rsrc_t vr, uint32_t kv_bytes,
-                                           const uint8_t* sf, const int32_t* gather,
-                                           int n_gather, int range_lo, int range_hi,
-                                           int fold_lo, int fold_hi) {
-  using B_ = Blk<T, D>;
-  typedef typename HalfOf<T>::type H;
-  const int tid = threadIdx.x;
-  constexpr int VEC = 16 / sizeof(T);
+struct BlkRegs {
+  static constexpr int VEC = 16 / sizeof(T), CPR = D / VEC;  // 16-byte chunks per row
+  static constexpr int KIT = (64 * CPR + NT - 1) / NT;       // key chunks per thread
+  static constexpr int VIT = (32 * CPR + NT - 1) / NT;       // value chunk pairs per thread
+  uint4 k[KIT];
+  uint4 v[VIT][2];
+  int pos;  // threads < 64: position of key tid (-1: none)
+  int sel;  // threads < 64: kept flag of key tid
+};
+
+template <typename T, int D, int NT>
+__device__ __forceinline__ void issue_block(BlkRegs<T, D, NT>& R, __amdgpu_buffer_rsrc_t kr,
+                                            __amdgpu_buffer_rsrc_t vr, uint32_t kv_bytes,
+                                            const uint8_t* sf, const int32_t* gather,
+                                            int n_gather, int range_lo, int range_hi) {
+  using BR = BlkRegs<T, D, NT>;
+  constexpr int VEC = BR::VEC, CPR = BR::CPR;
+  // lane-dependent addresses are recomputed here rather than kept live
+  // across the caller's loop (they would be hoisted out of it and spilled)
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));
   auto pos_of = [&](int kk) {
     if (gather) return kk < n_gather ? gather[kk] : -1;
     return range_lo + kk < range_hi ? range_lo + kk : -1;
   };
-  // byte offset of a row; absent rows read past the range and load zeros
   auto row_off = [&](int j) { return j >= 0 ? (uint32_t)j * (uint32_t)(D * sizeof(T)) : kv_bytes; };
+  // all row positions first (gather lists are read before any row load is
+  // issued, so waiting for them does not wait for the row loads)
+  uint32_t koff[BR::KIT], voff[BR::VIT][2];
+#pragma unroll
+  for (int it = 0; it < BR::KIT; ++it) {
+    const int idx = tid + it * NT;
+    koff[it] = idx < 64 * CPR ? row_off(pos_of(idx / CPR)) + (idx % CPR) * VEC * sizeof(T) : kv_bytes;
+  }
+#pragma unroll
+  for (int it = 0; it < BR::VIT; ++it) {
+    const int idx = tid + it * NT;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      voff[it][i] = idx < 32 * CPR ? row_off(pos_of(2 * (idx / CPR) + i)) + (idx % CPR) * VEC * sizeof(T)
+                                   : kv_bytes;
+  }
   if (tid < 64) {
-    const int j = pos_of(tid);
-    const int sel = j >= 0 ? (gather ? 1 : (int)sf[j]) : 0;
-    P.fmask[tid] = (j >= fold_lo && j < fold_hi && !sel) ? 1.f : 0.f;
-    const uint64_t bits = __ballot(sel != 0);
+    R.pos = pos_of(tid);
+    R.sel = R.pos >= 0 ? (gather ? 1 : (int)sf[R.pos]) : 0;
+  }
+#pragma unroll
+  for (int it = 0; it < BR::KIT; ++it) R.k[it] = ld_u4_buf(kr, koff[it], 0);
+#pragma unroll
+  for (int it = 0; it < BR::VIT; ++it)
+#pragma unroll
+    for (int i = 0; i < 2; ++i) R.v[it][i] = ld_u4_buf(vr, voff[it][i], 0);
+}
+
+// Writes an issued block to LDS: keys row-major into Ks, values transposed
+// (as H) into VTs with keys 2a, 2a+1 in adjacent permuted columns, the kept
+// flags as a 64-bit mask, the fold mask and the keys' squared norms.
+template <typename T, int D, int NT>
+__device__ __forceinline__ void commit_block(const BlkPtr<T, D>& P, const BlkRegs<T, D, NT>& R,
+                                             int fold_lo, int fold_hi) {
+  using B_ = Blk<T, D>;
+  using BR = BlkRegs<T, D, NT>;
+  typedef typename HalfOf<T>::type H;
+  constexpr int VEC = BR::VEC, CPR = BR::CPR;
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));  // as in issue_block
+  if (tid < 64) {
+    P.fmask[tid] = (R.pos >= fold_lo && R.pos < fold_hi && !R.sel) ? 1.f : 0.f;
+    const uint64_t bits = __ballot(R.sel != 0);
     if (tid == 0) {
       P.selw[0] = (uint32_t)bits;
       P.selw[1] = (uint32_t)(bits >> 32);
     }
   }
 #pragma unroll
-  for (int idx = tid; idx < 64 * (D / VEC); idx += NT) {
-    const int kk = idx / (D / VEC), col = (idx % (D / VEC)) * VEC;
-    const uint4 kvv = ld_u4_buf(kr, row_off(pos_of(kk)) + col * sizeof(T), 0);
-    *reinterpret_cast<uint4*>(P.Ks + kk * B_::KS + col) = kvv;
-    // |k|^2 for the feature map: D/VEC consecutive lanes hold one row
-    const T* ke = reinterpret_cast<const T*>(&kvv);
+  for (int it = 0; it < BR::KIT; ++it) {
+    const int idx = tid + it * NT;
+    if (BR::KIT * NT > 64 * CPR && idx >= 64 * CPR) break;  // uniform per wave
+    const int kk = idx / CPR, col = (idx % CPR) * VEC;
+    *reinterpret_cast<uint4*>(P.Ks + kk * B_::KS + col) = R.k[it];
+    // |k|^2 for the feature map: CPR consecutive lanes hold one row
+    const T* ke = reinterpret_cast<const T*>(&R.k[it]);
     float q2 = 0.f;
 #pragma unroll
     for (int e = 0; e < VEC; ++e) q2 += to_f32(ke[e]) * to_f32(ke[e]);
 #pragma unroll
-    for (int o = 1; o < D / VEC; o <<= 1) q2 += __shfl_xor(q2, o);
+    for (int o = 1; o < CPR; o <<= 1) q2 += __shfl_xor(q2, o);
     if (col == 0) P.kstat[128 + kk] = q2;
   }
 #pragma unroll
-  for (int idx = tid; idx < 16 * (D / VEC); idx += NT) {
-    const int a4 = idx / (D / VEC), col = (idx % (D / VEC)) * VEC;
-    T v4[4][VEC];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint4 vv = ld_u4_buf(vr, row_off(pos_of(4 * a4 + i)) + col * sizeof(T), 0);
-      *reinterpret_cast<uint4*>(v4[i]) = vv;
-    }
-    const int pc = perm_col(4 * a4);
+  for (int it = 0; it < BR::VIT; ++it) {
+    const int idx = tid + it * NT;
+    if (BR::VIT * NT > 32 * CPR && idx >= 32 * CPR) break;
+    const int a2 = idx / CPR, col = (idx % CPR) * VEC;
+    const T* v0 = reinterpret_cast<const T*>(&R.v[it][0]);
+    const T* v1 = reinterpret_cast<const T*>(&R.v[it][1]);
+    const int pc = perm_col(2 * a2);
 #pragma unroll
     for (int e = 0; e < VEC; ++e) {
-      H w4[4] = {from_f32<H>(to_f32(v4[0][e])), from_f32<H>(to_f32(v4[1][e])),
-                 from_f32<H>(to_f32(v4[2][e])), from_f32<H>(to_f32(v4[3][e]))};
+      H w2[2] = {from_f32<H>(to_f32(v0[e])), from_f32<H>(to_f32(v1[e]))};
       if constexpr (sizeof(H) == 2)
-        *reinterpret_cast<uint2*>(P.VTs + (col + e) * B_::VS + pc) = *reinterpret_cast<uint2*>(w4);
+        *reinterpret_cast<uint32_t*>(P.VTs + (col + e) * B_::VS + pc) = *reinterpret_cast<uint32_t*>(w2);
       else
-        *reinterpret_cast<uint4*>(P.VTs + (col + e) * B_::VS + pc) = *reinterpret_cast<uint4*>(w4);
+        *reinterpret_cast<uint2*>(P.VTs + (col + e) * B_::VS + pc) = *reinterpret_cast<uint2*>(w2);
     }
   }
 }
@@ -753,8 +801,10 @@ __global__ __launch_bounds__(512) void state_delta_kernel(PrefillArgs a) {
   const int lo = full_chunks_before(s * a.K, a.W, a.C) * a.C;
   const int hi = full_chunks_before(s * a.K + a.K, a.W, a.C) * a.C;
   for (int blo = lo; blo < hi; blo += 64) {
+    BlkRegs<T, D, 512> R;
+    issue_block<T, D, 512>(R, kr, vr, kv_bytes, sf, nullptr, 0, blo, hi);
     __syncthreads();
-    load_block<T, D, 512>(P, kr, vr, kv_bytes, sf, nullptr, 0, blo, hi, lo, hi);
+    commit_block<T, D, 512>(P, R, lo, hi);
     __syncthreads();
     f32x4 ph[4];
     block_phi<T, D>(P, ph, false);
@@ -945,21 +995,102 @@ __global__ __launch_bounds__(512) void attend_kernel(PrefillArgs a) {
       }
     }
 
-    // key blocks: kept pool below the band, then the band
+    // key blocks: the band first (linear-attention weights, fold), then the
+    // kept pool below the band, whose global loads for block i+1 are in
+    // flight while block i is used
     const int n_pool_blk = (n_oob + 63) / 64;
     const int n_band_blk = (band_hi - band_lo + 63) / 64;
-    for (int blk = 0; blk < n_pool_blk + n_band_blk; ++blk) {
-      const bool is_pool = blk < n_pool_blk;
-      const int blo = is_pool ? 64 * blk : band_lo + 64 * (blk - n_pool_blk);
-      const int nvalid = is_pool ? min(64, n_oob - blo) : min(64, band_hi - blo);
-      const bool la_blk = !is_pool && blo < cC;
-      const bool do_fold = fold && !is_pool && blo < fold_hi;
-      __syncthreads();
-      if (is_pool)  // positions from LDS where staged
-        load_block<T, D, 512>(P, kr, vr, kv_bytes, sf, blo + 64 <= B_::PCAP ? P.pidx + blo : selu + blo,
-                              nvalid, 0, 0, 0, 0);
+    // softmax / linear weights of one block in LDS folded into (m, l, O)
+    auto attend_block = [&](const bool is_pool, const int blo, const int nvalid, const bool la_blk) {
+      const uint64_t selbits = ((uint64_t)P.selw[1] << 32) | P.selw[0];
+      f32x4 st[4];
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) {
+        st[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < D / 32; ++kb)
+          mma(st[kt], ld_frag(P.Ks + (16 * kt + r16) * B_::KS + 32 * kb + 8 * g4), qf[kb]);
+      }
+      float mx = STILL_NEG_INF;
+      if (is_pool) {
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int kk = 16 * kt + 4 * g4 + i;
+            const float lw = kk < nvalid ? st[kt][i] * a.scale : STILL_NEG_INF;
+            st[kt][i] = lw;
+            mx = fmaxf(mx, lw);
+          }
+      } else {
+        f32x4 wt[4];
+        if (la_blk) {
+#pragma unroll
+          for (int kt = 0; kt < 4; ++kt) {
+            wt[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int bb = 0; bb < D / 32; ++bb) mma(wt[kt], ld_frag(P.wf(kt, bb) + lane * 8), pq[bb]);
+          }
+        }
+        const int vis_lo = min(t - W + 1, cC);  // softmax-visible from here
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int kk = 16 * kt + 4 * g4 + i;
+            const int j = blo + kk;
+            const bool sel = (selbits >> kk) & 1ull;
+            const bool valid = kk < nvalid && j <= t;
+            const bool sa = valid && (j >= vis_lo || sel);
+            float lw = sa ? st[kt][i] * a.scale : STILL_NEG_INF;
+            if (la_blk) {
+              const float w = wt[kt][i];
+              const bool la = valid && !sa && w > 0.f;
+              lw = la ? lgate + log_acc<T>(fmaxf(w, 1e-37f)) : lw;
+            }
+            st[kt][i] = lw;
+            mx = fmaxf(mx, lw);
+          }
+      }
+      mx = max_over_g(mx);
+      const float mn = fmaxf(mrun, mx);
+      // rows with nothing visible so far keep m = -inf, O = 0, l = 0
+      const float al = mrun == STILL_NEG_INF ? 0.f : exp_acc<T>(mrun - mn);
+      mrun = mn;
+      f32x4 pv[4];
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float lw = st[kt][i];
+          pv[kt][i] = lw == STILL_NEG_INF ? 0.f : exp_acc<T>(lw - mn);
+        }
+      // weights as H; the running sum uses the same rounded weights
+      const Frag<H> pf0 = frag_from<H>(pv[0], pv[1]);
+      const Frag<H> pf1 = frag_from<H>(pv[2], pv[3]);
+      lrun = lrun * al + frag_sum(pf0) + frag_sum(pf1);
+#pragma unroll
+      for (int dt = 0; dt < D / 16; ++dt) {
+        O[dt] *= al;
+        mma(O[dt], ld_frag(P.VTs + (16 * dt + r16) * B_::VS + 8 * g4), pf0);
+        mma(O[dt], ld_frag(P.VTs + (16 * dt + r16) * B_::VS + 32 + 8 * g4), pf1);
+      }
+    };
+    BlkRegs<T, D, 512> R;
+    auto issue_pool = [&](int pb) {
+      const int blo = 64 * pb;
+      if (blo + 64 <= B_::PCAP)  // positions staged in LDS
+        issue_block<T, D, 512>(R, kr, vr, kv_bytes, sf, P.pidx + blo, min(64, n_oob - blo), 0, 0);
       else
-        load_block<T, D, 512>(P, kr, vr, kv_bytes, sf, nullptr, 0, blo, band_hi, fold_lo, fold_hi);
+        issue_block<T, D, 512>(R, kr, vr, kv_bytes, sf, selu + blo, min(64, n_oob - blo), 0, 0);
+    };
+    for (int bb = 0; bb < n_band_blk; ++bb) {
+      const int blo = band_lo + 64 * bb;
+      const bool la_blk = blo < cC;
+      const bool do_fold = fold && blo < fold_hi;
+      issue_block<T, D, 512>(R, kr, vr, kv_bytes, sf, nullptr, 0, blo, band_hi);
+      __syncthreads();  // the previous block (or the readout) is done with LDS
+      commit_block<T, D, 512>(P, R, fold_lo, fold_hi);
       __syncthreads();
       if (la_blk || do_fold) {
         f32x4 phk[4];
@@ -967,80 +1098,20 @@ __global__ __launch_bounds__(512) void attend_kernel(PrefillArgs a) {
         // the fold writes only SP / zs, which this chunk no longer reads
         if (do_fold) block_fold<T, D>(P, phk);
       }
-      if (act) {  // wave-uniform
-        const uint64_t selbits = ((uint64_t)P.selw[1] << 32) | P.selw[0];
-        f32x4 st[4];
-#pragma unroll
-        for (int kt = 0; kt < 4; ++kt) {
-          st[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int kb = 0; kb < D / 32; ++kb)
-            mma(st[kt], ld_frag(P.Ks + (16 * kt + r16) * B_::KS + 32 * kb + 8 * g4), qf[kb]);
-        }
-        float mx = STILL_NEG_INF;
-        if (is_pool) {
-#pragma unroll
-          for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int kk = 16 * kt + 4 * g4 + i;
-              const float lw = kk < nvalid ? st[kt][i] * a.scale : STILL_NEG_INF;
-              st[kt][i] = lw;
-              mx = fmaxf(mx, lw);
-            }
-        } else {
-          f32x4 wt[4];
-          if (la_blk) {
-#pragma unroll
-            for (int kt = 0; kt < 4; ++kt) {
-              wt[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-              for (int bb = 0; bb < D / 32; ++bb) mma(wt[kt], ld_frag(P.wf(kt, bb) + lane * 8), pq[bb]);
-            }
-          }
-          const int vis_lo = min(t - W + 1, cC);  // softmax-visible from here
-#pragma unroll
-          for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int kk = 16 * kt + 4 * g4 + i;
-              const int j = blo + kk;
-              const bool sel = (selbits >> kk) & 1ull;
-              const bool valid = kk < nvalid && j <= t;
-              const bool sa = valid && (j >= vis_lo || sel);
-              float lw = sa ? st[kt][i] * a.scale : STILL_NEG_INF;
-              if (la_blk) {
-                const float w = wt[kt][i];
-                const bool la = valid && !sa && w > 0.f;
-                lw = la ? lgate + log_acc<T>(fmaxf(w, 1e-37f)) : lw;
-              }
-              st[kt][i] = lw;
-              mx = fmaxf(mx, lw);
-            }
-        }
-        mx = max_over_g(mx);
-        const float mn = fmaxf(mrun, mx);
-        // rows with nothing visible so far keep m = -inf, O = 0, l = 0
-        const float al = mrun == STILL_NEG_INF ? 0.f : exp_acc<T>(mrun - mn);
-        mrun = mn;
-        f32x4 pv[4];
-#pragma unroll
-        for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float lw = st[kt][i];
-            pv[kt][i] = lw == STILL_NEG_INF ? 0.f : exp_acc<T>(lw - mn);
-          }
-        // weights as H; the running sum uses the same rounded weights
-        const Frag<H> pf0 = frag_from<H>(pv[0], pv[1]);
-        const Frag<H> pf1 = frag_from<H>(pv[2], pv[3]);
-        lrun = lrun * al + frag_sum(pf0) + frag_sum(pf1);
-#pragma unroll
-        for (int dt = 0; dt < D / 16; ++dt) {
-          O[dt] *= al;
-          mma(O[dt], ld_frag(P.VTs + (16 * dt + r16) * B_::VS + 8 * g4), pf0);
-          mma(O[dt], ld_frag(P.VTs + (16 * dt + r16) * B_::VS + 32 + 8 * g4), pf1);
-        }
+      if (act) attend_block(false, blo, min(64, band_hi - blo), la_blk);  // wave-uniform
+    }
+    if (n_pool_blk > 0) {
+      issue_pool(0);
+      __syncthreads();
+      commit_block<T, D, 512>(P, R, 0, 0);
+    }
+    for (int pb = 0; pb < n_pool_blk; ++pb) {
+      __syncthreads();  // pool block pb is in LDS
+      if (pb + 1 < n_pool_blk) issue_pool(pb + 1);
+      if (act) attend_block(true, 64 * pb, min(64, n_oob - 64 * pb), false);
+      if (pb + 1 < n_pool_blk) {
+        __syncthreads();  // every wave is done with block pb
+        commit_block<T, D, 512>(P, R, 0, 0);
       }
     }
 
