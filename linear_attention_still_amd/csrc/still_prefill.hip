@@ -931,6 +931,10 @@ __global__ __launch_bounds__(512) void attend_kernel(PrefillArgs a) {
     for (int kb = 0; kb < D / 32; ++kb)
       qf[kb] = ld_frag_buf<T>(qr, act ? (uint32_t)(t * D + 8 * g4) * sizeof(T) : kv_bytes,
                               32 * kb * sizeof(T));
+    // the first band block's loads are in flight during the readout (issued
+    // after the query loads: waits on those then leave them outstanding)
+    BlkRegs<T, D, 512> R;
+    issue_block<T, D, 512>(R, kr, vr, kv_bytes, sf, nullptr, 0, band_lo, band_hi);
     f32x4 O[D / 16];
     float mrun, lrun;
     {
@@ -1076,7 +1080,6 @@ __global__ __launch_bounds__(512) void attend_kernel(PrefillArgs a) {
         mma(O[dt], ld_frag(P.VTs + (16 * dt + r16) * B_::VS + 32 + 8 * g4), pf1);
       }
     };
-    BlkRegs<T, D, 512> R;
     auto issue_pool = [&](int pb) {
       const int blo = 64 * pb;
       if (blo + 64 <= B_::PCAP)  // positions staged in LDS
@@ -1088,7 +1091,7 @@ __global__ __launch_bounds__(512) void attend_kernel(PrefillArgs a) {
       const int blo = band_lo + 64 * bb;
       const bool la_blk = blo < cC;
       const bool do_fold = fold && blo < fold_hi;
-      issue_block<T, D, 512>(R, kr, vr, kv_bytes, sf, nullptr, 0, blo, band_hi);
+      if (bb > 0) issue_block<T, D, 512>(R, kr, vr, kv_bytes, sf, nullptr, 0, blo, band_hi);
       __syncthreads();  // the previous block (or the readout) is done with LDS
       commit_block<T, D, 512>(P, R, fold_lo, fold_hi);
       __syncthreads();
