@@ -312,15 +312,52 @@ __device__ __forceinline__ float from_f32<float>(float x) { return x; }
 template <>
 __device__ __forceinline__ f16 from_f32<f16>(float x) { return (f16)x; }
 
+// Cross-lane exchange on the VALU: DPP within a row of 16 lanes and the
+// gfx950 permlane swaps across rows, instead of LDS permutes.
+template <int CTRL>
+__device__ __forceinline__ float dppf(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+// value of lane ^ 16
+__device__ __forceinline__ float xor16f(float x) {
+  const auto q = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(unsigned, x),
+                                                  __builtin_bit_cast(unsigned, x), false, false);
+  return __builtin_bit_cast(float, (threadIdx.x & 16) ? q[0] : q[1]);
+}
+// value of lane ^ 32
+__device__ __forceinline__ float xor32f(float x) {
+  const auto p = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, x),
+                                                  __builtin_bit_cast(unsigned, x), false, false);
+  return __builtin_bit_cast(float, (threadIdx.x & 32) ? p[0] : p[1]);
+}
+// Sum / max over N consecutive aligned lanes (N = 1, 2, 4, 8, 16), every
+// lane of the group receiving the result.
+template <int N>
+__device__ __forceinline__ float row_sum(float x) {
+  if constexpr (N >= 2) x += dppf<0xB1>(x);   // quad_perm [1,0,3,2]
+  if constexpr (N >= 4) x += dppf<0x4E>(x);   // quad_perm [2,3,0,1]
+  if constexpr (N >= 8) x += dppf<0x141>(x);  // row_half_mirror
+  if constexpr (N >= 16) x += dppf<0x140>(x); // row_mirror
+  return x;
+}
+template <int N>
+__device__ __forceinline__ float row_max(float x) {
+  if constexpr (N >= 2) x = fmaxf(x, dppf<0xB1>(x));
+  if constexpr (N >= 4) x = fmaxf(x, dppf<0x4E>(x));
+  if constexpr (N >= 8) x = fmaxf(x, dppf<0x141>(x));
+  if constexpr (N >= 16) x = fmaxf(x, dppf<0x140>(x));
+  return x;
+}
+
 // Sum / max over the four lanes sharing r (lanes r, r+16, r+32, r+48).
 __device__ __forceinline__ float sum_over_g(float x) {
-  x += __shfl_xor(x, 16);
-  x += __shfl_xor(x, 32);
+  x += xor16f(x);
+  x += xor32f(x);
   return x;
 }
 __device__ __forceinline__ float max_over_g(float x) {
-  x = fmaxf(x, __shfl_xor(x, 16));
-  x = fmaxf(x, __shfl_xor(x, 32));
+  x = fmaxf(x, xor16f(x));
+  x = fmaxf(x, xor32f(x));
   return x;
 }
 

@@ -170,8 +170,8 @@ __global__ __launch_bounds__(256) void score_kernel(PrefillArgs a) {
     }
 #pragma unroll
     for (int off = 16; off <= 32; off <<= 1) {
-      const float m2 = __shfl_xor(mrun, off), za2 = __shfl_xor(zall, off),
-                  zo2 = __shfl_xor(zoth, off), ss2 = __shfl_xor(sself, off);
+      auto px = [&](float x) { return off == 16 ? xor16f(x) : xor32f(x); };
+      const float m2 = px(mrun), za2 = px(zall), zo2 = px(zoth), ss2 = px(sself);
       const float mn = fmaxf(mrun, m2);
       if (mn != STILL_NEG_INF) {
         const float f1 = (mrun == STILL_NEG_INF) ? 0.f : __expf(mrun - mn);
@@ -536,8 +536,7 @@ __device__ __forceinline__ void commit_block(const BlkPtr<T, D>& P, const BlkReg
     float q2 = 0.f;
 #pragma unroll
     for (int e = 0; e < VEC; ++e) q2 += to_f32(ke[e]) * to_f32(ke[e]);
-#pragma unroll
-    for (int o = 1; o < CPR; o <<= 1) q2 += __shfl_xor(q2, o);
+    q2 = row_sum<CPR>(q2);
     if (col == 0) P.kstat[128 + kk] = q2;
   }
 #pragma unroll
@@ -598,17 +597,11 @@ __device__ __forceinline__ void np_map_tile(const BlkPtr<T, D>& P, const Frag<T>
 
 // Max / sum over the 16 lanes sharing g (the 16 columns of a C tile).
 __device__ __forceinline__ float max_over_r(float x) {
-  x = fmaxf(x, __shfl_xor(x, 1));
-  x = fmaxf(x, __shfl_xor(x, 2));
-  x = fmaxf(x, __shfl_xor(x, 4));
-  x = fmaxf(x, __shfl_xor(x, 8));
+  x = row_max<16>(x);
   return x;
 }
 __device__ __forceinline__ float sum_over_r(float x) {
-  x += __shfl_xor(x, 1);
-  x += __shfl_xor(x, 2);
-  x += __shfl_xor(x, 4);
-  x += __shfl_xor(x, 8);
+  x = row_sum<16>(x);
   return x;
 }
 
