@@ -102,9 +102,16 @@ __device__ __forceinline__ uint2 ld8(const void* p) { return *reinterpret_cast<c
 // Sum over the n consecutive lanes (n a power of two) that hold one row.
 template <int N>
 __device__ __forceinline__ float sum_lanes(float x) {
-#pragma unroll
-  for (int o = 1; o < N; o <<= 1) x += __shfl_xor(x, o);
+  x = row_sum<(N < 16 ? N : 16)>(x);
+  if constexpr (N >= 32) x += xor16f(x);
+  if constexpr (N >= 64) x += xor32f(x);
   return x;
+}
+// partner value at lane ^ o, o = 16 or 32
+template <int O>
+__device__ __forceinline__ float xorf(float x) {
+  static_assert(O == 16 || O == 32, "row-group exchange");
+  return O == 16 ? xor16f(x) : xor32f(x);
 }
 template <int N>
 __device__ __forceinline__ double sum_lanes_f64(double x) {
@@ -113,15 +120,11 @@ __device__ __forceinline__ double sum_lanes_f64(double x) {
   return x;
 }
 __device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) x = fmaxf(x, __shfl_xor(x, o));
-  return x;
+  x = row_max<16>(x);
+  x = fmaxf(x, xor16f(x));
+  return fmaxf(x, xor32f(x));
 }
-__device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) x += __shfl_xor(x, o);
-  return x;
-}
+__device__ __forceinline__ float wave_sum(float x) { return sum_lanes<64>(x); }
 
 // NP-Map [P3 "NP-Map: Norm-Preserving Feature Map"] of NR <= 9 rows, reading:
 // ||x|| * softmax(x F) / ||softmax(x F)|| with exact expf. u = x F with the rows
@@ -163,8 +166,10 @@ __device__ __forceinline__ void np_map_vec(const T* F, const float* xs, float* r
   for (int r = 0; r < NR; ++r)
 #pragma unroll
     for (int e = 0; e < VEC; ++e)
-#pragma unroll
-      for (int o = LPK; o < 64; o <<= 1) acc[r][e] += __shfl_xor(acc[r][e], o);
+    {
+      if constexpr (LPK <= 16) acc[r][e] += xorf<16>(acc[r][e]);
+      acc[r][e] += xorf<32>(acc[r][e]);
+    }
   if (grp == 0)
 #pragma unroll
     for (int r = 0; r < NR; ++r)
@@ -448,8 +453,10 @@ void decode_kernel(DecodeArgs a) {
     for (int h = 0; h < G; ++h)
 #pragma unroll
       for (int e = 0; e < 4; ++e)
-#pragma unroll
-        for (int o = SL; o < 64; o <<= 1) accS[h][e] += __shfl_xor(accS[h][e], o);
+      {
+        if constexpr (SL <= 16) accS[h][e] += xorf<16>(accS[h][e]);
+        accS[h][e] += xorf<32>(accS[h][e]);
+      }
     if (sg == 0)
 #pragma unroll
       for (int h = 0; h < G; ++h)
@@ -577,20 +584,21 @@ void decode_kernel(DecodeArgs a) {
     }
   }
   // merge the row groups of each wave, then publish per wave
-#pragma unroll
-  for (int o = LPK; o < 64; o <<= 1) {
+  auto merge = [&](auto px) {
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      const float m2 = __shfl_xor(m[h], o), l2 = __shfl_xor(l[h], o);
+      const float m2 = px(m[h]), l2 = px(l[h]);
       const float mm = fmaxf(m[h], m2);
       const float a1 = m[h] == STILL_NEG_INF ? 0.f : __expf(m[h] - mm);
       const float a2 = m2 == STILL_NEG_INF ? 0.f : __expf(m2 - mm);
       l[h] = l[h] * a1 + l2 * a2;
 #pragma unroll
-      for (int e = 0; e < VEC; ++e) acc[h][e] = acc[h][e] * a1 + __shfl_xor(acc[h][e], o) * a2;
+      for (int e = 0; e < VEC; ++e) acc[h][e] = acc[h][e] * a1 + px(acc[h][e]) * a2;
       m[h] = mm;
     }
-  }
+  };
+  if constexpr (LPK <= 16) merge([](float x) { return xorf<16>(x); });
+  merge([](float x) { return xorf<32>(x); });
   if (grp == 0) {
 #pragma unroll
     for (int h = 0; h < G; ++h) {
