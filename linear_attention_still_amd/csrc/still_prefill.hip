@@ -101,22 +101,26 @@ __global__ __launch_bounds__(256) void score_kernel(PrefillArgs a) {
   constexpr int VEC = 16 / sizeof(T);
   const int nvec = nkt * 16 * (D / VEC);
   if (tid == 0) kmax[0] = 0.f;
-  for (int idx = tid; idx < nvec; idx += 256) {
+  __syncthreads();
+  // keys into LDS; the largest squared key norm (for the error bound) from
+  // the same vectors: D / VEC consecutive lanes hold one row
+  float kmx = 0.f;
+  for (int idx = tid; idx < nvec; idx += 256) {  // whole rows per lane group
     const int row = idx / (D / VEC), col = (idx % (D / VEC)) * VEC;
     const int j = kbase + row;
     uint4 val = {0, 0, 0, 0};
     if (j >= 0 && j < L && j < cC + C) val = *reinterpret_cast<const uint4*>(kg + (size_t)j * D + col);
     *reinterpret_cast<uint4*>(Ks + row * KS + col) = val;
+    const T* e = reinterpret_cast<const T*>(&val);
+    float q2 = 0.f;
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) q2 += to_f32(e[i]) * to_f32(e[i]);
+    kmx = fmaxf(kmx, row_sum<D / VEC>(q2));
   }
-  __syncthreads();
-  for (int row = tid; row < nkt * 16; row += 256) {
-    float s = 0.f;
-    for (int i = 0; i < D; ++i) {
-      const float x = to_f32(Ks[row * KS + i]);
-      s += x * x;
-    }
-    atomicMax(reinterpret_cast<int*>(kmax), __float_as_int(s));  // s >= 0
-  }
+  kmx = row_max<16>(kmx);
+  kmx = fmaxf(kmx, xor16f(kmx));
+  kmx = fmaxf(kmx, xor32f(kmx));
+  if (lane == 0) atomicMax(reinterpret_cast<int*>(kmax), __float_as_int(kmx));  // >= 0
   __syncthreads();
   const float kn_max = sqrtf(kmax[0]);
 
@@ -225,36 +229,59 @@ __global__ __launch_bounds__(256) void score_kernel(PrefillArgs a) {
 template <typename T, int D>
 __device__ __forceinline__ double score_f64(const PrefillArgs& a, int b, int kv, int t, double* lg,
                             double* red) {
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int W = a.W, G = a.G, L = a.L;
   const int lo = t - W + 1 > 0 ? t - W + 1 : 0;
   const int n = t - lo + 1;
+  constexpr int VEC = 16 / sizeof(T);
   const T* kg = reinterpret_cast<const T*>(a.k) + (size_t)(b * a.Hkv + kv) * L * D;
+  // window logits in float64 (products of bf16/f32 values are exact), each
+  // accumulated in index order from 16-byte row vectors
   for (int p = tid; p < G * n; p += 256) {
     const int hl = p / n, jj = p % n;
     const T* qr = reinterpret_cast<const T*>(a.q) +
                   ((size_t)(b * a.Hq + kv * G + hl) * L + t) * D;
     const T* kr = kg + (size_t)(lo + jj) * D;
     double s = 0.0;
-    for (int i = 0; i < D; ++i) s += (double)to_f32(qr[i]) * (double)to_f32(kr[i]);
+    for (int c = 0; c < D; c += VEC) {
+      const uint4 qv = *reinterpret_cast<const uint4*>(qr + c);
+      const uint4 kv4 = *reinterpret_cast<const uint4*>(kr + c);
+      const T* qe = reinterpret_cast<const T*>(&qv);
+      const T* ke = reinterpret_cast<const T*>(&kv4);
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) s += (double)to_f32(qe[e]) * (double)to_f32(ke[e]);
+    }
     lg[hl * W + jj] = a.scale64 * s;
   }
   __syncthreads();
-  if (tid < G) {
-    const double* x = lg + tid * W;
-    double mx = x[0];
-    for (int j = 1; j < n; ++j) mx = x[j] > mx ? x[j] : mx;
+  // one wave per head: max, the two sums, the KL form
+  for (int h = wave; h < G; h += 4) {
+    const double* x = lg + h * W;
+    double mx = -__builtin_huge_val();
+    for (int j = lane; j < n; j += 64) mx = x[j] > mx ? x[j] : mx;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const double y = __shfl_xor(mx, o);
+      mx = y > mx ? y : mx;
+    }
     double za = 0.0, zo = 0.0;
-    for (int j = 0; j < n; ++j) {
+    for (int j = lane; j < n; j += 64) {
       const double e = exp(x[j] - mx);
       za += e;
       if (j != n - 1) zo += e;
     }
-    const double p = exp(x[n - 1] - mx) / za, pn = zo / za;
-    double sc = 0.0;
-    if (p > 0.0) sc += p * log(p / a.eps64);
-    if (pn > 0.0) sc += pn * log(pn / (1.0 - a.eps64));
-    red[tid] = sc;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      za += __shfl_xor(za, o);
+      zo += __shfl_xor(zo, o);
+    }
+    if (lane == 0) {
+      const double p = exp(x[n - 1] - mx) / za, pn = zo / za;
+      double sc = 0.0;
+      if (p > 0.0) sc += p * log(p / a.eps64);
+      if (pn > 0.0) sc += pn * log(pn / (1.0 - a.eps64));
+      red[h] = sc;
+    }
   }
   __syncthreads();
   double tot = 0.0;
