@@ -859,12 +859,19 @@ __global__ __launch_bounds__(512) void state_delta_kernel(PrefillArgs a) {
 __global__ __launch_bounds__(256) void state_scan_kernel(float* dS, int NS, int n_elem) {
   const int e = blockIdx.x * 256 + threadIdx.x;
   if (e >= n_elem) return;
-  float* base = dS + (size_t)(blockIdx.y + gridDim.y * blockIdx.z) * NS * n_elem;
+  float* base = dS + (size_t)(blockIdx.y + gridDim.y * blockIdx.z) * NS * n_elem + e;
   double run = 0.0;  // float64 running sum: one float32 rounding per start
-  for (int s = 0; s < NS; ++s) {
-    const float x = base[(size_t)s * n_elem + e];
-    base[(size_t)s * n_elem + e] = (float)run;
-    if (s + 1 < NS) run += (double)x;
+  constexpr int B8 = 8;  // loads of a batch in flight together
+  for (int s0 = 0; s0 < NS; s0 += B8) {
+    float x[B8];
+#pragma unroll
+    for (int i = 0; i < B8; ++i) x[i] = s0 + i < NS ? base[(size_t)(s0 + i) * n_elem] : 0.f;
+#pragma unroll
+    for (int i = 0; i < B8; ++i) {
+      if (s0 + i >= NS) break;
+      base[(size_t)(s0 + i) * n_elem] = (float)run;
+      run += (double)x[i];
+    }
   }
 }
 
@@ -1203,10 +1210,16 @@ __global__ __launch_bounds__(256) void export_kernel(PrefillArgs a) {
   const int ring_lo = L - R > 0 ? L - R : 0;
   const int n_ring_grp = (L - ring_lo + 15) / 16;
   if (x < n_ring_grp) {
+    // NP-Map of 16 ring keys [P3 "NP-Map: Norm-Preserving Feature Map"]
+    // with F staged in LDS; per-row statistics by one wave per row
+    __shared__ __align__(16) T Fs[D * D];
     __shared__ float xs[16][D];
     __shared__ float us[16][D];
-    __shared__ float red[16][3];
+    __shared__ float red[16][2];
+    const int lane = tid & 63, wave = tid >> 6;
     const T* F = reinterpret_cast<const T*>(a.fmap_w) + (size_t)kv * D * D;
+    for (int e = tid; e < D * D * (int)sizeof(T) / 16; e += 256)
+      reinterpret_cast<uint4*>(Fs)[e] = reinterpret_cast<const uint4*>(F)[e];
     for (int e = tid; e < 16 * D; e += 256) {
       const int r = e / D, i = e % D, p = ring_lo + 16 * x + r;
       xs[r][i] = p < L ? to_f32(kg[(size_t)p * D + i]) : 0.f;
@@ -1215,21 +1228,31 @@ __global__ __launch_bounds__(256) void export_kernel(PrefillArgs a) {
     for (int e = tid; e < 16 * D; e += 256) {
       const int r = e / D, j = e % D;
       float u = 0.f;
-      for (int i = 0; i < D; ++i) u += xs[r][i] * to_f32(F[(size_t)i * D + j]);
+#pragma unroll 8
+      for (int i = 0; i < D; ++i) u += xs[r][i] * to_f32(Fs[i * D + j]);
       us[r][j] = u;
     }
     __syncthreads();
-    if (tid < 16) {
+    for (int r = wave; r < 16; r += 4) {
       float mx = STILL_NEG_INF, xn = 0.f;
-      for (int j = 0; j < D; ++j) mx = fmaxf(mx, us[tid][j]);
-      for (int i = 0; i < D; ++i) xn += xs[tid][i] * xs[tid][i];
+      for (int j = lane; j < D; j += 64) {
+        mx = fmaxf(mx, us[r][j]);
+        xn += xs[r][j] * xs[r][j];
+      }
+      mx = row_max<16>(mx);
+      mx = fmaxf(mx, xor16f(mx));
+      mx = fmaxf(mx, xor32f(mx));
       float ss = 0.f;
-      for (int j = 0; j < D; ++j) {
-        const float e = exp_acc<T>(us[tid][j] - mx);
+      for (int j = lane; j < D; j += 64) {
+        const float e = exp_acc<T>(us[r][j] - mx);
         ss += e * e;
       }
-      red[tid][0] = mx;
-      red[tid][1] = sqrtf(xn) / sqrtf(ss);
+      xn = sum_over_g(row_sum<16>(xn));
+      ss = sum_over_g(row_sum<16>(ss));
+      if (lane == 0) {
+        red[r][0] = mx;
+        red[r][1] = sqrtf(xn) / sqrtf(ss);
+      }
     }
     __syncthreads();
     T* rk = reinterpret_cast<T*>(st + a.st_ring_k);
