@@ -62,22 +62,23 @@ def algorithmic_work(wl, sel):
 
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-TRAFFIC_SOURCES = ("linear_attention_still_amd/csrc/still_prefill.hip",
-                   "linear_attention_still_amd/csrc/still_common.h",
-                   "linear_attention_still_amd/csrc/still_api.hip")
+COMMON = ("linear_attention_still_amd/csrc/still_common.h", "linear_attention_still_amd/csrc/still_api.hip")
+PREFILL_SOURCES = ("linear_attention_still_amd/csrc/still_prefill.hip",) + COMMON
+DECODE_SOURCES = ("linear_attention_still_amd/csrc/still_decode.hip",) + COMMON
 
 
-def measured_traffic(kernel="attend_kernel"):
-    """HBM bytes per launch from the committed rocprofv3 counter summary,
-    or None when the kernel sources changed since the counters were taken."""
+def measured_traffic(kernel, profile, sources):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
+    summary `profiles/<profile>`, or None when the kernel sources changed
+    since the counters were taken."""
     import hashlib
     h = hashlib.sha256()
-    for f in TRAFFIC_SOURCES:
+    for f in sources:
         with open(os.path.join(HERE, f), "rb") as fh:
             h.update(fh.read())
     sha = h.hexdigest()[:16]
     try:
-        with open(os.path.join(HERE, "profiles", "prefill_llama8b_L16K.md")) as fh:
+        with open(os.path.join(HERE, "profiles", profile)) as fh:
             for line in fh:
                 if line.startswith("traffic %s " % kernel):
                     kv = dict(x.split("=") for x in line.split()[2:])
@@ -153,7 +154,9 @@ def run_decode_bench(torch, still, inputs, n_steps):
             "ms_per_step": step_ms, "tokens_per_s": wl.batch / (step_ms * 1e-3),
             "wall_s": wall, "algorithmic_bytes_per_step": step_bytes,
             "hbm_gbs": step_bytes / (step_ms * 1e-3) / 1e9,
-            "hbm_frac": step_bytes / (step_ms * 1e-3) / 1e9 / PEAK_HBM_GBS}
+            "hbm_frac": step_bytes / (step_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+            "traffic": measured_traffic("decode_kernel", "decode_llama8b_B64_ctx16K.md",
+                                        DECODE_SOURCES)}
 
 
 def run_cpu_baseline(wl, x):
@@ -224,7 +227,9 @@ def main():
                    "budget": wl.budget, "t_max": wl.t_max},
         "roofline": {"bound": "mfma", "kernel": "attend", "achieved": achieved,
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": achieved / PEAK_BF16_TFLOPS, "traffic": measured_traffic(),
+                     "frac": achieved / PEAK_BF16_TFLOPS,
+                     "traffic": measured_traffic("attend_kernel", "prefill_llama8b_L16K.md",
+                                                 PREFILL_SOURCES),
                      "flops_per_launch": work["attend"]},
         "layer": {"algorithmic_tflop": work["total"] / 1e12,
                   "tflops": work["total"] / (elapsed / args.steps) / 1e12,
