@@ -635,10 +635,11 @@ __device__ __forceinline__ float sum_over_r(float x) {
 // NP-Map features of the block's 64 keys, computed once by the waves
 // w < D/16, wave w holding feature tile w of every key in the accumulator
 // layout of K F: ph[kt][i] = phi(k_{16kt+4g+i})[16w + r]. Per-key softmax
-// statistics are combined across waves through LDS. With want_w the
-// features are also written as H hi/lo A fragments (rows = keys) to WF.
-// Four workgroup barriers (five with want_w); every thread must call it with
-// the same want_w.
+// statistics are combined across waves through LDS: each wave's max and sum
+// of squares relative to it, then one factor per (wave, key). With want_w
+// the features are also written as H A fragments (rows = keys) to WF. Two
+// workgroup barriers (three with want_w); every thread must call it with the
+// same want_w.
 template <typename T, int D>
 __device__ __forceinline__ void block_phi(const BlkPtr<T, D>& P, f32x4 (&ph)[4],
                                           bool want_w) {
@@ -656,36 +657,30 @@ __device__ __forceinline__ void block_phi(const BlkPtr<T, D>& P, f32x4 (&ph)[4],
 #pragma unroll
       for (int kb = 0; kb < D / 32; ++kb)
         mma(ph[kt], ld_frag(P.Ks + (16 * kt + r16) * B_::KS + 32 * kb + 8 * g4), fb[kb]);
+      // per key: this wave's max over its 16 features and its sum of
+      // squared exponentials relative to that max
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const float m = max_over_r(ph[kt][i]);
-        if (r16 == 0) P.kmax[wave * 64 + 16 * kt + 4 * g4 + i] = m;
+        const float e = exp_acc<T>(ph[kt][i] - m);
+        ph[kt][i] = e;
+        const float s2 = sum_over_r(e * e);
+        if (r16 == 0) {
+          P.kmax[wave * 64 + 16 * kt + 4 * g4 + i] = m;
+          P.ksum[wave * 64 + 16 * kt + 4 * g4 + i] = s2;
+        }
       }
     }
   }
   __syncthreads();
-  if (tid < 64) {
-    float m = STILL_NEG_INF;
-    for (int w = 0; w < B_::NFT; ++w) m = fmaxf(m, P.kmax[w * 64 + tid]);
-    P.kstat[tid] = m;
-  }
-  __syncthreads();
-  if (mine) {
-#pragma unroll
-    for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float e = exp_acc<T>(ph[kt][i] - P.kstat[16 * kt + 4 * g4 + i]);
-        ph[kt][i] = e;
-        const float s2 = sum_over_r(e * e);
-        if (r16 == 0) P.ksum[wave * 64 + 16 * kt + 4 * g4 + i] = s2;
-      }
-  }
-  __syncthreads();
-  if (tid < 64) {
-    float s2 = 0.f;
-    for (int w = 0; w < B_::NFT; ++w) s2 += P.ksum[w * 64 + tid];
-    P.kstat[64 + tid] = sqrtf(P.kstat[128 + tid]) / sqrtf(s2);
+  if (tid < 64) {  // combine the waves: global max M, sum S, then per-wave factors
+    float M = STILL_NEG_INF;
+    for (int w = 0; w < B_::NFT; ++w) M = fmaxf(M, P.kmax[w * 64 + tid]);
+    float S = 0.f;
+    for (int w = 0; w < B_::NFT; ++w)
+      S += P.ksum[w * 64 + tid] * exp_acc<T>(2.f * (P.kmax[w * 64 + tid] - M));
+    const float base = sqrtf(P.kstat[128 + tid]) / sqrtf(S);
+    for (int w = 0; w < B_::NFT; ++w) P.kmax[w * 64 + tid] = exp_acc<T>(P.kmax[w * 64 + tid] - M) * base;
   }
   __syncthreads();
   if (mine) {
@@ -696,7 +691,7 @@ __device__ __forceinline__ void block_phi(const BlkPtr<T, D>& P, f32x4 (&ph)[4],
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int key = 16 * kt + 4 * g4 + i;
-        const float v = ph[kt][i] * P.kstat[64 + key];
+        const float v = ph[kt][i] * P.kmax[wave * 64 + key];
         ph[kt][i] = v;
         if (want_w) P.wf(kt, bb)[(16 * gp + (key & 15)) * 8 + sl] = from_f32<H>(v);
       }
