@@ -28,6 +28,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 typedef _Float16 f16;
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
 
 template <typename T>
 struct Frag;
@@ -91,6 +92,24 @@ __device__ __forceinline__ X* lds_opaque(X* p) {
   unsigned a = (unsigned)(__UINTPTR_TYPE__)(lds_char*)(char*)p;
   asm volatile("" : "+s"(a));
   return (X*)(char*)(lds_char*)(__UINTPTR_TYPE__)a;
+}
+
+// A 16-bit MFMA fragment read transposed from LDS (gfx950
+// ds_read_b64_tr_b16): within each 16-lane group, lane i receives element
+// i & 3 of the 8-byte chunks addressed by lanes (i >> 2) + 4k, k = 0..3.
+// With lane c of group g addressing row R0 + 4g + (c >> 2), columns
+// C0 + 4 (c & 3), lane (r, g) gets column C0 + r of rows R0 + 4g + k; a
+// second read `step` elements further gives rows + 16: together the depth
+// slots perm(g, 0..7) of a fragment whose depth runs along the rows.
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+__device__ __forceinline__ Frag<f16> tr_frag(const f16* p, int step) {
+  const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(lds_char*)(char*)p);
+  const i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(lds_char*)(char*)(p + step));
+  Frag<f16> f;
+  const f16x4_t a4 = __builtin_bit_cast(f16x4_t, a), b4 = __builtin_bit_cast(f16x4_t, b);
+  f.v = f16x8{a4[0], a4[1], a4[2], a4[3], b4[0], b4[1], b4[2], b4[3]};
+  return f;
 }
 
 // Buffer-resource loads: the lane-dependent part of an address is a 32-bit

@@ -404,13 +404,18 @@ template <typename T, int D>
 struct Blk {
   typedef typename HalfOf<T>::type H;
   static constexpr int KS = D + Pad<T>::v;
-  static constexpr int VS = 64 + Pad<H>::v;
+  static constexpr int VS = 64 + Pad<H>::v;  // float data: values transposed
+  // 16-bit H: values row-major [64][VR] and phi(K) feature-major [D][FKS],
+  // read as MFMA fragments with transposing LDS reads
+  static constexpr bool TR = sizeof(H) == 2;
+  static constexpr int VR = D + 8;
+  static constexpr int FKS = 64 + 8;
   static constexpr int NFT = D / 16;  // feature (and d_v) tiles
   static constexpr int NPAIR = (D / 16) * (D / 32);
   static constexpr int PCAP = 1024;   // pool positions staged in LDS per chunk
   static constexpr size_t ks_bytes = 64 * KS * sizeof(T);
-  static constexpr size_t vs_bytes = (size_t)D * VS * sizeof(H);
-  static constexpr size_t wf_bytes = (size_t)4 * (D / 32) * 64 * 8 * sizeof(H);
+  static constexpr size_t vs_bytes = TR ? (size_t)64 * VR * sizeof(H) : (size_t)D * VS * sizeof(H);
+  static constexpr size_t wf_bytes = TR ? (size_t)D * FKS * sizeof(H) : (size_t)4 * (D / 32) * 64 * 8 * sizeof(H);
   // readout fragments of half the d_v tiles: [NPAIR / 2][hi, lo][64][8]
   static constexpr size_t rs_bytes = (size_t)(NPAIR / 2) * 2 * 64 * 8 * sizeof(T);
   static constexpr size_t lo_bytes =
@@ -458,6 +463,30 @@ struct BlkPtr {
   }
   __device__ float* pair(int p) const { return SP + ((size_t)p * 64 + (threadIdx.x & 63)) * 8; }
   __device__ H* wf(int kt, int bb) const { return WF + ((size_t)(kt * (D / 32) + bb) * 64) * 8; }
+  // Fragment of V^T for d_v tile dt and key half kb2: lane (r, g) holds
+  // V[32 kb2 + perm(g, s)][16 dt + r], s = 0..7 (A operand of O^T += V^T P^T,
+  // B operand of the fold).
+  __device__ Frag<H> ld_v(int dt, int kb2) const {
+    using B_ = Blk<T, D>;
+    const int lane = threadIdx.x & 63, r16 = lane & 15, g4 = lane >> 4;
+    if constexpr (B_::TR) {
+      const H* p = VTs + (32 * kb2 + 4 * g4 + (r16 >> 2)) * B_::VR + 16 * dt + 4 * (r16 & 3);
+      return tr_frag(p, 16 * B_::VR);
+    } else {
+      return ld_frag(VTs + (16 * dt + r16) * B_::VS + 32 * kb2 + 8 * g4);
+    }
+  }
+  // A fragment of phi(K) (rows = keys 16 kt + r, depth = features 32 bb + perm(g, s)).
+  __device__ Frag<H> ld_wk(int kt, int bb) const {
+    using B_ = Blk<T, D>;
+    const int lane = threadIdx.x & 63, r16 = lane & 15, g4 = lane >> 4;
+    if constexpr (B_::TR) {
+      const H* p = WF + (32 * bb + 4 * g4 + (r16 >> 2)) * B_::FKS + 16 * kt + 4 * (r16 & 3);
+      return tr_frag(p, 16 * B_::FKS);
+    } else {
+      return ld_frag(wf(kt, bb) + lane * 8);
+    }
+  }
   // fragment (feature tile ft, d block kb) of F^T: B operand of X F
   __device__ const T* ft(int ftile, int kb) const {
     return FT + ((size_t)(ftile * (D / 32) + kb) * 64 + (threadIdx.x & 63)) * 8;
@@ -482,8 +511,10 @@ struct BlkRegs {
   static constexpr int VEC = 16 / sizeof(T), CPR = D / VEC;  // 16-byte chunks per row
   static constexpr int KIT = (64 * CPR + NT - 1) / NT;       // key chunks per thread
   static constexpr int VIT = (32 * CPR + NT - 1) / NT;       // value chunk pairs per thread
+  static constexpr bool TR = sizeof(typename HalfOf<T>::type) == 2;
   uint4 k[KIT];
-  uint4 v[VIT][2];
+  uint4 vr[TR ? KIT : 1];     // values, same row chunks as the keys
+  uint4 v[TR ? 1 : VIT][2];   // values as key pairs (transposed layout)
   int pos;  // threads < 64: position of key tid (-1: none)
   int sel;  // threads < 64: kept flag of key tid
 };
@@ -513,7 +544,7 @@ __device__ __forceinline__ void issue_block(BlkRegs<T, D, NT>& R, __amdgpu_buffe
     koff[it] = idx < 64 * CPR ? row_off(pos_of(idx / CPR)) + (idx % CPR) * VEC * sizeof(T) : kv_bytes;
   }
 #pragma unroll
-  for (int it = 0; it < BR::VIT; ++it) {
+  for (int it = 0; it < (BR::TR ? 0 : BR::VIT); ++it) {
     const int idx = tid + it * NT;
 #pragma unroll
     for (int i = 0; i < 2; ++i)
@@ -526,10 +557,15 @@ __device__ __forceinline__ void issue_block(BlkRegs<T, D, NT>& R, __amdgpu_buffe
   }
 #pragma unroll
   for (int it = 0; it < BR::KIT; ++it) R.k[it] = ld_u4_buf(kr, koff[it], 0);
+  if constexpr (BR::TR) {
 #pragma unroll
-  for (int it = 0; it < BR::VIT; ++it)
+    for (int it = 0; it < BR::KIT; ++it) R.vr[it] = ld_u4_buf(vr, koff[it], 0);
+  } else {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) R.v[it][i] = ld_u4_buf(vr, voff[it][i], 0);
+    for (int it = 0; it < BR::VIT; ++it)
+#pragma unroll
+      for (int i = 0; i < 2; ++i) R.v[it][i] = ld_u4_buf(vr, voff[it][i], 0);
+  }
 }
 
 // Writes an issued block to LDS: keys row-major into Ks, values transposed
@@ -565,6 +601,20 @@ __device__ __forceinline__ void commit_block(const BlkPtr<T, D>& P, const BlkReg
     for (int e = 0; e < VEC; ++e) q2 += to_f32(ke[e]) * to_f32(ke[e]);
     q2 = row_sum<CPR>(q2);
     if (col == 0) P.kstat[128 + kk] = q2;
+  }
+  if constexpr (B_::TR) {  // values row-major as H, 16-byte writes
+#pragma unroll
+    for (int it = 0; it < BR::KIT; ++it) {
+      const int idx = tid + it * NT;
+      if (BR::KIT * NT > 64 * CPR && idx >= 64 * CPR) break;
+      const int kk = idx / CPR, col = (idx % CPR) * VEC;
+      const T* ve = reinterpret_cast<const T*>(&R.vr[it]);
+      H w[VEC];
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) w[e] = from_f32<H>(to_f32(ve[e]));
+      *reinterpret_cast<uint4*>(P.VTs + kk * B_::VR + col) = *reinterpret_cast<uint4*>(w);
+    }
+    return;
   }
 #pragma unroll
   for (int it = 0; it < BR::VIT; ++it) {
@@ -687,14 +737,21 @@ __device__ __forceinline__ void block_phi(const BlkPtr<T, D>& P, f32x4 (&ph)[4],
     const int f = 16 * wave + r16, bb = f >> 5, o = f & 31;
     const int gp = (o & 15) >> 2, sl = (o & 3) + ((o >> 4) << 2);
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt)
+    for (int kt = 0; kt < 4; ++kt) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int key = 16 * kt + 4 * g4 + i;
-        const float v = ph[kt][i] * P.kmax[wave * 64 + key];
-        ph[kt][i] = v;
-        if (want_w) P.wf(kt, bb)[(16 * gp + (key & 15)) * 8 + sl] = from_f32<H>(v);
+      for (int i = 0; i < 4; ++i) ph[kt][i] *= P.kmax[wave * 64 + 16 * kt + 4 * g4 + i];
+      if (want_w) {
+        if constexpr (B_::TR) {  // feature-major: 4 keys of feature f, 8 bytes
+          H w4[4] = {from_f32<H>(ph[kt][0]), from_f32<H>(ph[kt][1]), from_f32<H>(ph[kt][2]),
+                     from_f32<H>(ph[kt][3])};
+          *reinterpret_cast<uint2*>(P.WF + f * B_::FKS + 16 * kt + 4 * g4) = *reinterpret_cast<uint2*>(w4);
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            P.wf(kt, bb)[(16 * gp + ((4 * g4 + i) & 15)) * 8 + sl] = from_f32<H>(ph[kt][i]);
+        }
       }
+    }
   }
   if (want_w) __syncthreads();  // WF is read by every wave
 }
@@ -722,7 +779,7 @@ __device__ __forceinline__ void fold_tile(const BlkPtr<T, D>& P, const f32x4 (&p
     split2_frag<H>(x0, x1, hi, lo);
 #pragma unroll
     for (int vt = 0; vt < D / 16; ++vt) {
-      const Frag<H> bv = ld_frag(P.VTs + (16 * vt + r16) * B_::VS + 32 * kb2 + 8 * g4);
+      const Frag<H> bv = P.ld_v(vt, kb2);
       mma(acc[vt], hi, bv);
       if constexpr (sizeof(H) == 2) mma(acc[vt], lo, bv);
     }
@@ -1055,7 +1112,7 @@ __global__ __launch_bounds__(512) void attend_kernel(PrefillArgs a) {
           for (int kt = 0; kt < 4; ++kt) {
             wt[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int bb = 0; bb < D / 32; ++bb) mma(wt[kt], ld_frag(P.wf(kt, bb) + lane * 8), pq[bb]);
+            for (int bb = 0; bb < D / 32; ++bb) mma(wt[kt], P.ld_wk(kt, bb), pq[bb]);
           }
         }
         const int vis_lo = min(t - W + 1, cC);  // softmax-visible from here
@@ -1098,8 +1155,8 @@ __global__ __launch_bounds__(512) void attend_kernel(PrefillArgs a) {
 #pragma unroll
       for (int dt = 0; dt < D / 16; ++dt) {
         O[dt] *= al;
-        mma(O[dt], ld_frag(P.VTs + (16 * dt + r16) * B_::VS + 8 * g4), pf0);
-        mma(O[dt], ld_frag(P.VTs + (16 * dt + r16) * B_::VS + 32 + 8 * g4), pf1);
+        mma(O[dt], P.ld_v(dt, 0), pf0);
+        mma(O[dt], P.ld_v(dt, 1), pf1);
       }
     };
     auto issue_pool = [&](int pb) {
