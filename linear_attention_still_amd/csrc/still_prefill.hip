@@ -394,9 +394,10 @@ __global__ __launch_bounds__(256) void select_kernel(PrefillArgs a) {
 //                               A fragments (rows = keys) of <phi(k),phi(q)>
 //   SP    float32 linear state S (d_k x d_v), fragment-linear: pair
 //         p = (d_v tile vt, d_k 32-block bb) holds, per lane, the 8 values
-//         {S[32bb + 4g + i][16vt + r], S[32bb + 16 + 4g + i][16vt + r]},
-//         i.e. the accumulators of tiles (2bb, vt), (2bb+1, vt) and, read as
-//         one fragment, the A operand of S^T for the readout.
+//         {S[32bb + 4g + i][16vt + r], S[32bb + 16 + 4g + i][16vt + r]} as two
+//         halves [p][h][lane][4] (the accumulators of tiles (2bb, vt) and
+//         (2bb+1, vt)); read together they are the A operand of S^T for the
+//         readout.
 //   stat  per-key softmax statistics of the feature map
 // At the start of a chunk the first region (Ks..WF) holds the state split
 // into hi/lo bf16 fragments for the readout (RS).
@@ -461,7 +462,10 @@ struct BlkPtr {
     zs = lds_opaque(reinterpret_cast<double*>(st + 20 * 64 * 4 + 16));
     pidx = lds_opaque(reinterpret_cast<int32_t*>(st + 20 * 64 * 4 + 16 + D * 8));
   }
-  __device__ float* pair(int p) const { return SP + ((size_t)p * 64 + (threadIdx.x & 63)) * 8; }
+  // half h (0: d_k rows 32bb + 4g + i, 1: rows 32bb + 16 + 4g + i) of pair p
+  __device__ float* pair(int p, int h) const {
+    return SP + ((size_t)(2 * p + h) * 64 + (threadIdx.x & 63)) * 4;
+  }
   __device__ H* wf(int kt, int bb) const { return WF + ((size_t)(kt * (D / 32) + bb) * 64) * 8; }
   // Fragment of V^T for d_v tile dt and key half kb2: lane (r, g) holds
   // V[32 kb2 + perm(g, s)][16 dt + r], s = 0..7 (A operand of O^T += V^T P^T,
@@ -811,7 +815,7 @@ __device__ __forceinline__ void block_fold(const BlkPtr<T, D>& P, const f32x4 (&
   fold_tile<T, D>(P, ph, 0, 2, acc);
 #pragma unroll
   for (int vt = 0; vt < D / 16; ++vt) {
-    float* sp = P.pair(vt * (D / 32) + (wave >> 1)) + 4 * (wave & 1);
+    float* sp = P.pair(vt * (D / 32) + (wave >> 1), wave & 1);
     *reinterpret_cast<f32x4*>(sp) += acc[vt];
   }
   const float z = fold_zsum<T, D>(P, ph);
@@ -834,12 +838,13 @@ __device__ __forceinline__ void store_state_rowmajor(const BlkPtr<T, D>& P, floa
   for (int e = threadIdx.x; e < B_::NPAIR * 64; e += 512) {
     const int p = e >> 6, ln = e & 63, g4 = ln >> 4;
     const int vt = p / (D / 32), bb = p % (D / 32);
-    const float* sp = P.SP + (size_t)e * 8;
 #pragma unroll
-    for (int q = 0; q < 2; ++q)
+    for (int q = 0; q < 2; ++q) {
+      const float* sp = P.SP + ((size_t)(2 * p + q) * 64 + ln) * 4;
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        S[(size_t)(32 * bb + 16 * q + 4 * g4 + i) * D + 16 * vt + (ln & 15)] = sp[4 * q + i];
+        S[(size_t)(32 * bb + 16 * q + 4 * g4 + i) * D + 16 * vt + (ln & 15)] = sp[i];
+    }
   }
   (void)r16;
 }
@@ -899,7 +904,7 @@ __global__ __launch_bounds__(512) void state_delta_kernel(PrefillArgs a) {
   if (wave < B_::NFT) {
 #pragma unroll
     for (int vt = 0; vt < D / 16; ++vt) {
-      float* o = dst + ((size_t)(vt * (D / 32) + (wave >> 1)) * 64 + lane) * 8 + 4 * (wave & 1);
+      float* o = dst + ((size_t)(2 * (vt * (D / 32) + (wave >> 1)) + (wave & 1)) * 64 + lane) * 4;
 #pragma unroll
       for (int i = 0; i < 4; ++i) o[i] = (float)sum[vt][i];
     }
@@ -1037,10 +1042,10 @@ __global__ __launch_bounds__(512) void attend_kernel(PrefillArgs a) {
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
         for (int e = tid; e < HP * 64; e += 512) {
-          const float* sp = P.SP + ((size_t)half * HP * 64 + e) * 8;
-          Frag<T> sh, sl;
-          split2_frag<T>(*reinterpret_cast<const f32x4*>(sp), *reinterpret_cast<const f32x4*>(sp + 4), sh, sl);
           const int pl = e >> 6, ln = e & 63;
+          const float* sp = P.SP + ((size_t)2 * (half * HP + pl) * 64 + ln) * 4;
+          Frag<T> sh, sl;
+          split2_frag<T>(*reinterpret_cast<const f32x4*>(sp), *reinterpret_cast<const f32x4*>(sp + 256), sh, sl);
           st_frag(P.RS + ((size_t)(2 * pl) * 64 + ln) * 8, sh);
           st_frag(P.RS + ((size_t)(2 * pl + 1) * 64 + ln) * 8, sl);
         }
