@@ -273,6 +273,37 @@ __device__ __forceinline__ float log_acc(float x) {
   if constexpr (sizeof(T) == 4) return logf(x);
   else return __logf(x);
 }
+// base-2 forms (v_exp_f32 / v_log_f32 are base 2)
+constexpr float STILL_LOG2E = 1.4426950408889634f;
+template <typename T>
+__device__ __forceinline__ float exp2_acc(float x) {
+  if constexpr (sizeof(T) == 4) return exp2f(x);
+  else return __builtin_amdgcn_exp2f(x);
+}
+template <typename T>
+__device__ __forceinline__ float log2_acc(float x) {
+  if constexpr (sizeof(T) == 4) return log2f(x);
+  else return __builtin_amdgcn_logf(x);
+}
+// 64-bit mask of the n lowest bits (n clamped to [0, 64])
+__device__ __forceinline__ uint64_t low_bits(int n) {
+  return n <= 0 ? 0ull : (n >= 64 ? ~0ull : ((1ull << n) - 1ull));
+}
+template <typename T>
+__device__ __forceinline__ Frag<T> ones_frag();
+template <>
+__device__ __forceinline__ Frag<f16> ones_frag<f16>() {
+  Frag<f16> f;
+  for (int i = 0; i < 8; ++i) f.v[i] = (f16)1.0f;
+  return f;
+}
+template <>
+__device__ __forceinline__ Frag<float> ones_frag<float>() {
+  Frag<float> f;
+  f.lo = f32x4{1.f, 1.f, 1.f, 1.f};
+  f.hi = f.lo;
+  return f;
+}
 
 template <typename T>
 __device__ __forceinline__ float frag_sumsq(const Frag<T>& f);

@@ -983,7 +983,10 @@ __global__ __launch_bounds__(512) void attend_kernel(PrefillArgs a) {
   const int hl = act ? wave / n_qt : 0, qt = act ? wave % n_qt : 0;
   const int h = kv * a.G + hg * a.Gs + hl;
   const float g = a.gate[h];
-  const float lgate = g > 0.f ? log_acc<T>(g) : STILL_NEG_INF;
+  // log-weights are kept in base 2: logits times scale * log2(e), linear
+  // weights log2(g) + log2 <phi(q), phi(k)>
+  const float lgate2 = g > 0.f ? log2_acc<T>(g) : STILL_NEG_INF;
+  const float scale2 = a.scale * STILL_LOG2E;
   const __amdgpu_buffer_rsrc_t qr =
       make_rsrc(reinterpret_cast<const T*>(a.q) + ((size_t)(b * a.Hq + h) * L) * D, kv_bytes);
 
@@ -1020,7 +1023,8 @@ __global__ __launch_bounds__(512) void attend_kernel(PrefillArgs a) {
     BlkRegs<T, D, 512> R;
     issue_block<T, D, 512>(R, kr, vr, kv_bytes, sf, nullptr, 0, band_lo, band_hi);
     f32x4 O[D / 16];
-    float mrun, lrun;
+    float mrun;
+    f32x4 lacc;  // running sum, the same in all four entries (ones-row MFMA)
     {
       f32x4 ph[D / 16];
       np_map_tile<T, D>(P, qf, ph);
@@ -1070,14 +1074,14 @@ __global__ __launch_bounds__(512) void attend_kernel(PrefillArgs a) {
         if (half == 0) __syncthreads();  // the region is split into again
       }
       if (g > 0.f && dz > 0.f) {
-        mrun = log_acc<T>(g * dz);
-        lrun = g4 == 0 ? 1.f : 0.f;
+        mrun = log2_acc<T>(g * dz);
+        lacc = f32x4{1.f, 1.f, 1.f, 1.f};
         const float inv = 1.f / dz;
 #pragma unroll
         for (int dt = 0; dt < D / 16; ++dt) O[dt] *= inv;
       } else {
         mrun = STILL_NEG_INF;
-        lrun = 0.f;
+        lacc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int dt = 0; dt < D / 16; ++dt) O[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
       }
@@ -1101,15 +1105,21 @@ __global__ __launch_bounds__(512) void attend_kernel(PrefillArgs a) {
       }
       float mx = STILL_NEG_INF;
       if (is_pool) {
+        if (nvalid < 64) {  // uniform: only a last, partial pool block is masked
+          const uint64_t v_s = low_bits(nvalid) >> (4 * g4);
+#pragma unroll
+          for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              st[kt][i] = ((v_s >> (16 * kt + i)) & 1ull) ? st[kt][i] * scale2 : STILL_NEG_INF;
+        } else {
+#pragma unroll
+          for (int kt = 0; kt < 4; ++kt) st[kt] *= scale2;
+        }
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int kk = 16 * kt + 4 * g4 + i;
-            const float lw = kk < nvalid ? st[kt][i] * a.scale : STILL_NEG_INF;
-            st[kt][i] = lw;
-            mx = fmaxf(mx, lw);
-          }
+          for (int i = 0; i < 4; ++i) mx = fmaxf(mx, st[kt][i]);
       } else {
         f32x4 wt[4];
         if (la_blk) {
@@ -1120,21 +1130,21 @@ __global__ __launch_bounds__(512) void attend_kernel(PrefillArgs a) {
             for (int bb = 0; bb < D / 32; ++bb) mma(wt[kt], P.ld_wk(kt, bb), pq[bb]);
           }
         }
-        const int vis_lo = min(t - W + 1, cC);  // softmax-visible from here
+        // per-lane key masks (bit kk = key blo + kk): visible keys are those
+        // up to the query; softmax-visible ones are in the window / own
+        // chunk or kept; the rest of the visible ones are linear
+        const uint64_t valid_m = low_bits(min(nvalid, t - blo + 1));
+        const uint64_t sa_m = valid_m & (~low_bits(min(t - W + 1, cC) - blo) | selbits);
+        const uint64_t sa_s = sa_m >> (4 * g4), la_s = (valid_m & ~sa_m) >> (4 * g4);
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const int kk = 16 * kt + 4 * g4 + i;
-            const int j = blo + kk;
-            const bool sel = (selbits >> kk) & 1ull;
-            const bool valid = kk < nvalid && j <= t;
-            const bool sa = valid && (j >= vis_lo || sel);
-            float lw = sa ? st[kt][i] * a.scale : STILL_NEG_INF;
+            float lw = ((sa_s >> (16 * kt + i)) & 1ull) ? st[kt][i] * scale2 : STILL_NEG_INF;
             if (la_blk) {
               const float w = wt[kt][i];
-              const bool la = valid && !sa && w > 0.f;
-              lw = la ? lgate + log_acc<T>(fmaxf(w, 1e-37f)) : lw;
+              const bool la = ((la_s >> (16 * kt + i)) & 1ull) && w > 0.f;
+              lw = la ? lgate2 + log2_acc<T>(fmaxf(w, 1e-37f)) : lw;
             }
             st[kt][i] = lw;
             mx = fmaxf(mx, lw);
@@ -1143,7 +1153,7 @@ __global__ __launch_bounds__(512) void attend_kernel(PrefillArgs a) {
       mx = max_over_g(mx);
       const float mn = fmaxf(mrun, mx);
       // rows with nothing visible so far keep m = -inf, O = 0, l = 0
-      const float al = mrun == STILL_NEG_INF ? 0.f : exp_acc<T>(mrun - mn);
+      const float al = mrun == STILL_NEG_INF ? 0.f : exp2_acc<T>(mrun - mn);
       mrun = mn;
       f32x4 pv[4];
 #pragma unroll
@@ -1151,15 +1161,22 @@ __global__ __launch_bounds__(512) void attend_kernel(PrefillArgs a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const float lw = st[kt][i];
-          pv[kt][i] = lw == STILL_NEG_INF ? 0.f : exp_acc<T>(lw - mn);
+          pv[kt][i] = lw == STILL_NEG_INF ? 0.f : exp2_acc<T>(lw - mn);
         }
-      // weights as H; the running sum uses the same rounded weights
+      // weights as H; the running sum comes from the same rounded weights
+      // through a ones-row MFMA
       const Frag<H> pf0 = frag_from<H>(pv[0], pv[1]);
       const Frag<H> pf1 = frag_from<H>(pv[2], pv[3]);
-      lrun = lrun * al + frag_sum(pf0) + frag_sum(pf1);
+      if (__builtin_amdgcn_ballot_w64(al != 1.f)) {  // wave-uniform: some max moved
+        lacc *= al;
+#pragma unroll
+        for (int dt = 0; dt < D / 16; ++dt) O[dt] *= al;
+      }
+      const Frag<H> one = ones_frag<H>();
+      mma(lacc, one, pf0);
+      mma(lacc, one, pf1);
 #pragma unroll
       for (int dt = 0; dt < D / 16; ++dt) {
-        O[dt] *= al;
         mma(O[dt], P.ld_v(dt, 0), pf0);
         mma(O[dt], P.ld_v(dt, 1), pf1);
       }
@@ -1203,7 +1220,7 @@ __global__ __launch_bounds__(512) void attend_kernel(PrefillArgs a) {
     }
 
     // outputs: normalise; bf16 rows go through LDS for full-line stores
-    const float l = sum_over_g(lrun);
+    const float l = lacc[0];
     const float inv = 1.f / l;
     const size_t ob = ((size_t)(b * a.Hq + h) * L) * D;
     if constexpr (sizeof(T) == 2) {
