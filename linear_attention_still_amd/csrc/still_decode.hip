@@ -22,7 +22,7 @@
 //      not yet folded, and the state S, z as one virtual key; all weights
 //      share one normaliser (reading of the branch merge);
 //   4. the new token's float64 score joins the undecided chunk's scores
-//      (its window logits come from the same pass over the ring keys).
+//      (its window logits from a second, cached pass over the window rows).
 //
 // The step is bound by HBM reads (pool and ring K/V, S): rows are read as
 // 8-byte vectors, D * sizeof(T) / 8 consecutive lanes per row, several rows
@@ -377,6 +377,29 @@ void decode_kernel(DecodeArgs a) {
   if (a.sel_new && !a.boundary)
     for (int i = tid; i < a.lam; i += DEC_THREADS) a.sel_new[(size_t)unit * a.lam + i] = -1;
 
+  // key sets [P3 "Content-Aware Routing ..."]: kept tokens below lo, the ring
+  // from lo to t (window and own chunk), ring tokens [la_lo, la_hi] that are
+  // out of the window and unkept (linear), then S, z.
+  int lo = t - W + 1 < cC ? t - W + 1 : cC;
+  if (lo < 0) lo = 0;
+  const int n_win = t - lo + 1;
+  const int la_lo = full_chunks_before(c, W, C) * C;
+  const int la_hi = min(t - W, cC - 1);  // inclusive
+  const int n_la = la_hi >= la_lo ? la_hi - la_lo + 1 : 0;
+  const int sc_lo = t - W + 1 > 0 ? t - W + 1 : 0;  // score window
+  const int part = lane % LPK, grp = lane / LPK;
+
+  // the pool positions first: the first key batch, issued before the
+  // NP-Map, needs their count
+  const int sp = lane % SL, sg = lane / SL;
+  constexpr int ROUNDS = D / (DEC_WAVES * RPW);
+  {
+    int cnt = 0;  // pool positions ascend: count those below lo
+    for (int i = tid; i < n_pool; i += DEC_THREADS) cnt += pool_pos[i] < lo ? 1 : 0;
+    cnt = (int)wave_sum((float)cnt);
+    if (lane == 0) ibuf[1 + wave] = cnt;
+  }
+
   // ---- 2. the new token enters the ring; phi(q_h), phi(k_t) ---------------
   const T* kin = reinterpret_cast<const T*>(a.k) + (size_t)unit * D;
   const T* vin = reinterpret_cast<const T*>(a.v) + (size_t)unit * D;
@@ -393,52 +416,47 @@ void decode_kernel(DecodeArgs a) {
     xs[e] = x;
   }
   __syncthreads();
+  int n_oob = 0;
+#pragma unroll
+  for (int w = 0; w < DEC_WAVES; ++w) n_oob += ibuf[1 + w];
+  const int n_sa = n_oob + n_win;
+
+  // softmax keys in batches of U rows per lane, two batches in flight
+  constexpr int STRIDE = DEC_WAVES * KPW * U;
+  auto load_sa = [&](int k0, uint2 (&rk)[U], uint2 (&rv)[U]) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int kk = k0 + u * KPW + grp;
+      const bool ok = kk < n_sa;
+      const size_t row = kk < n_oob ? (size_t)kk : (size_t)((lo + kk - n_oob) % R);
+      rk[u] = ok ? ld8((kk < n_oob ? pool_k : ring_k) + row * D + part * VEC) : uint2{0, 0};
+      rv[u] = ok ? ld8((kk < n_oob ? pool_v : ring_v) + row * D + part * VEC) : uint2{0, 0};
+    }
+  };
+  uint2 rkA[U], rvA[U], rkB[U], rvB[U];
+  const int k_first = wave * KPW * U;
+  load_sa(k_first, rkA, rvA);  // the new token's ring row is read back: ordered by the barrier above
+
   np_map_vec<T, D, G + 1>(F, xs, red8, us, ph, rowst);
   for (int e = tid; e < G * D; e += DEC_THREADS) phq[e] = ph[e];
   for (int i = tid; i < D; i += DEC_THREADS) ring_phi[(size_t)slot_t * D + i] = from_f32<T>(ph[G * D + i]);
 
-  // key sets [P3 "Content-Aware Routing ..."]: kept tokens below lo, the ring
-  // from lo to t (window and own chunk), ring tokens [la_lo, la_hi] that are
-  // out of the window and unkept (linear), then S, z.
-  int lo = t - W + 1 < cC ? t - W + 1 : cC;
-  if (lo < 0) lo = 0;
-  if (tid == 0) ibuf[0] = 0;
-  __syncthreads();
-  {
-    int cnt = 0;  // pool positions ascend: count those below lo
-    for (int i = tid; i < n_pool; i += DEC_THREADS) cnt += pool_pos[i] < lo ? 1 : 0;
-    cnt = (int)wave_sum((float)cnt);
-    if (lane == 0 && cnt) atomicAdd(&ibuf[0], cnt);
-  }
-  __syncthreads();
-  const int n_oob = ibuf[0];
-  const int n_win = t - lo + 1;
-  const int n_sa = n_oob + n_win;
-  const int la_lo = full_chunks_before(c, W, C) * C;
-  const int la_hi = min(t - W, cC - 1);  // inclusive
-  const int n_la = la_hi >= la_lo ? la_hi - la_lo + 1 : 0;
-  const int sc_lo = t - W + 1 > 0 ? t - W + 1 : 0;  // score window
-
   float* redA = red;                                          // [waves][G][D]
   float* redS = red + DEC_WAVES * G * D;                      // [waves][G][D]
   float* mlw = reinterpret_cast<float*>(smem + LD::ml);       // [waves][G][2]
-  const int part = lane % LPK, grp = lane / LPK;
+  __syncthreads();  // phq complete; the NP-Map scratch (aliased by red) is free
 
   // ---- 3a. state readout partials: sum_i phi_h[i] S[i][f] ----------------
   {
+    f32x4 sv[ROUNDS];
+#pragma unroll
+    for (int rr = 0; rr < ROUNDS; ++rr)
+      sv[rr] = *reinterpret_cast<const f32x4*>(S + (size_t)((rr * DEC_WAVES + wave) * RPW + sg) * D + sp * 4);
     float accS[G][4];
 #pragma unroll
     for (int h = 0; h < G; ++h)
 #pragma unroll
       for (int e = 0; e < 4; ++e) accS[h][e] = 0.f;
-    const int sp = lane % SL, sg = lane / SL;
-    constexpr int ROUNDS = D / (DEC_WAVES * RPW);
-    f32x4 sv[ROUNDS];
-#pragma unroll
-    for (int rr = 0; rr < ROUNDS; ++rr) {
-      const int i = (rr * DEC_WAVES + wave) * RPW + sg;
-      sv[rr] = *reinterpret_cast<const f32x4*>(S + (size_t)i * D + sp * 4);
-    }
 #pragma unroll
     for (int rr = 0; rr < ROUNDS; ++rr) {
       const int i = (rr * DEC_WAVES + wave) * RPW + sg;
@@ -509,24 +527,13 @@ void decode_kernel(DecodeArgs a) {
     for (int h = 0; h < G; ++h)
 #pragma unroll
       for (int e = 0; e < VEC; ++e) qv[h][e] = qs[h * D + part * VEC + e];
-    for (int k0 = wave * KPW * U; k0 < n_sa; k0 += DEC_WAVES * KPW * U) {
-      uint2 rk[U], rv[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int kk = k0 + u * KPW + grp;
-        const bool ok = kk < n_sa;
-        const size_t row = kk < n_oob ? (size_t)kk : (size_t)((lo + kk - n_oob) % R);
-        rk[u] = ok ? ld8((kk < n_oob ? pool_k : ring_k) + row * D + part * VEC) : uint2{0, 0};
-        rv[u] = ok ? ld8((kk < n_oob ? pool_v : ring_v) + row * D + part * VEC) : uint2{0, 0};
-      }
+    auto compute_sa = [&](int k0, const uint2 (&rk)[U], const uint2 (&rv)[U]) {
       float s[U][G];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int kk = k0 + u * KPW + grp;
         float x[VEC];
         RowVec<T>::get(rk[u], x);
-        const int pos = kk < n_oob ? -1 : lo + kk - n_oob;
-        const bool in_sc = kk < n_sa && pos >= sc_lo;  // uniform over the row's lanes
 #pragma unroll
         for (int h = 0; h < G; ++h) {
           float d = 0.f;
@@ -534,16 +541,35 @@ void decode_kernel(DecodeArgs a) {
           for (int e = 0; e < VEC; ++e) d += qv[h][e] * x[e];
           d = sum_lanes<LPK>(d);
           s[u][h] = kk < n_sa ? d * a.scale : STILL_NEG_INF;
-          if (in_sc) {  // products of bf16/f32 values are exact in float64
-            double d64s = 0.0;
-#pragma unroll
-            for (int e = 0; e < VEC; ++e) d64s += (double)qv[h][e] * (double)x[e];
-            d64s = sum_lanes_f64<LPK>(d64s);
-            if (part == 0) lg[h * W + (pos - sc_lo)] = a.scale64 * d64s;
-          }
         }
       }
       absorb(s, rv);
+    };
+    for (int k0 = k_first; k0 < n_sa; k0 += 2 * STRIDE) {  // wave-uniform bounds
+      load_sa(k0 + STRIDE, rkB, rvB);
+      compute_sa(k0, rkA, rvA);
+      if (k0 + STRIDE >= n_sa) break;
+      load_sa(k0 + 2 * STRIDE, rkA, rvA);
+      compute_sa(k0 + STRIDE, rkB, rvB);
+    }
+    // float64 window logits of the new token (its score), from the window's
+    // ring rows (just read, so cached); products of bf16/f32 values are
+    // exact in float64
+    const int n_sc = t - sc_lo + 1;
+    for (int k0 = wave * KPW; k0 < n_sc; k0 += DEC_WAVES * KPW) {
+      const int jj = k0 + grp;
+      const bool ok = jj < n_sc;  // uniform over the row's lanes
+      const uint2 raw = ok ? ld8(ring_k + (size_t)((sc_lo + jj) % R) * D + part * VEC) : uint2{0, 0};
+      float x[VEC];
+      RowVec<T>::get(raw, x);
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        double d64s = 0.0;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) d64s += (double)qv[h][e] * (double)x[e];
+        d64s = sum_lanes_f64<LPK>(d64s);
+        if (ok && part == 0) lg[h * W + jj] = a.scale64 * d64s;
+      }
     }
   }
   if (n_la > 0) {
