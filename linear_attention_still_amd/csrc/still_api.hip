@@ -216,7 +216,7 @@ int launch_decode(const Derived& d, still::DecodeArgs a, hipStream_t s) {
   using namespace still;
   if (a.boundary) {
     const size_t lds = DecLds<T, D, 1>::uni + DecLds<T, D, 1>::fold_bytes;
-    decode_boundary_kernel<T, D><<<dim3(d.Hkv, d.B), dim3(DEC_THREADS), lds, s>>>(a);
+    decode_boundary_kernel<T, D><<<dim3(d.Hkv, d.B), dim3(BND_THREADS), lds, s>>>(a);
     if (hipGetLastError() != hipSuccess) return STILL_EHIP;
   }
   switch (d.G) {

@@ -10,8 +10,9 @@
 //        "NP-Map: Norm-Preserving Feature Map"
 //
 // The step applies the same routing and memory update as the prefill
-// [P3 "Delayed Chunk-Level Selection ..."]. One workgroup (8 waves) per
-// (kv head, batch row) unit:
+// [P3 "Delayed Chunk-Level Selection ..."]. One workgroup (4 waves) per
+// (kv head, batch row) unit, two per CU; chunk-boundary work runs in its own
+// kernel (8 waves) before the step:
 //   1. when a new chunk begins: Top-lambda of the finished chunk over its
 //      float64 scores, kept tokens appended to the pool [P2 固定预算路由];
 //      the chunk(s) now wholly before the window folded into S, z;
@@ -25,10 +26,10 @@
 //      (its window logits from a second, cached pass over the window rows).
 //
 // The step is bound by HBM reads (pool and ring K/V, S): rows are read as
-// 8-byte vectors, D * sizeof(T) / 8 consecutive lanes per row, several rows
-// in flight per lane, and partial sums are combined through LDS once. Two
-// workgroups fit on a CU (at most 128 VGPRs, small LDS), so every unit of a
-// 512-unit step is resident at once.
+// tiles of 16 keys per wave, two tiles in flight; logits by MFMA, values by
+// per-lane column slices; partial sums are combined through LDS once. Two
+// 4-wave workgroups fit on a CU, so every unit of a 512-unit step is
+// resident at once.
 #include "still_common.h"
 
 namespace still {
@@ -49,8 +50,10 @@ struct DecodeArgs {
       st_ring_phi, st_ring_flag, st_pending, st_meta;
 };
 
-constexpr int DEC_THREADS = 512;
+constexpr int DEC_THREADS = 256;  // per-token kernel: 4 waves, two workgroups per CU
 constexpr int DEC_WAVES = DEC_THREADS / 64;
+constexpr int BND_THREADS = 512;  // chunk-boundary kernel
+constexpr int BND_WAVES = BND_THREADS / 64;
 
 // LDS carve-up of the decode kernel, in bytes from the base.
 template <typename T, int D, int G>
@@ -59,14 +62,15 @@ struct DecLds {
   static constexpr size_t phq = qs + (size_t)G * D * 4;            // f32 [G][D]
   static constexpr size_t hv = phq + (size_t)G * D * 4;            // f32 [G][12]
   static constexpr size_t ml = hv + (size_t)G * 12 * 4;            // f32 [waves][G][2]
-  static constexpr size_t ibuf = ml + (size_t)DEC_WAVES * G * 2 * 4;  // int [2 + 130]
+  static constexpr size_t pw = ml + (size_t)DEC_WAVES * G * 2 * 4;  // f32 [waves][17][8]
+  static constexpr size_t ibuf = pw + (size_t)DEC_WAVES * 17 * 8 * 4;  // int [2 + 130]
   static constexpr size_t d64 = ibuf + (2 + 130) * 4;              // f64 [128 + 8]
   static constexpr size_t rowst = d64 + (128 + 8) * 8;             // f32 [16][2]
   static constexpr size_t uni = rowst + 16 * 2 * 4;                // union below
   // union member 1 (NP-Map and fold): xs, us, ph, vs [8][D] and red8
   // [waves][8][D] f32 in the boundary kernel; xs, us, ph [G+1][D] and red8
   // [waves][G+1][D] per token
-  static constexpr size_t fold_bytes = (size_t)(4 + DEC_WAVES) * 8 * D * 4;
+  static constexpr size_t fold_bytes = (size_t)(4 + BND_WAVES) * 8 * D * 4;
   static constexpr size_t mapg_bytes = (size_t)(3 + DEC_WAVES) * (G + 1) * D * 4;
   // union member 2 (value and state partial sums): f32 [2][waves][G][D]
   static constexpr size_t red_bytes = (size_t)2 * DEC_WAVES * G * D * 4;
@@ -128,15 +132,16 @@ __device__ __forceinline__ float wave_sum(float x) { return sum_lanes<64>(x); }
 
 // NP-Map [P3 "NP-Map: Norm-Preserving Feature Map"] of NR <= 9 rows, reading:
 // ||x|| * softmax(x F) / ||softmax(x F)|| with exact expf. u = x F with the rows
-// of F read once as 16-byte vectors (all loads of a lane in flight at once),
+// of F read once as 8-byte vectors (all loads of a lane in flight at once),
 // partial sums over the F rows reduced across lanes and then across waves
 // through red8 [waves][NR][D]. xs, us, ph are [NR][D] float32 in LDS. All
 // threads; ends with a barrier.
-template <typename T, int D, int NR>
+template <typename T, int D, int NR, int NT>
 __device__ __forceinline__ void np_map_vec(const T* F, const float* xs, float* red8, float* us,
                                            float* ph, float* rowst) {
+  constexpr int NW = NT / 64;
   constexpr int VEC = RowVec<T>::N, LPK = D / VEC, KPW = 64 / LPK;
-  constexpr int ITS = D / (DEC_WAVES * KPW);  // F rows per lane
+  constexpr int ITS = D / (NW * KPW);  // F rows per lane
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int part = lane % LPK, grp = lane / LPK;
   float acc[NR][VEC];
@@ -147,12 +152,12 @@ __device__ __forceinline__ void np_map_vec(const T* F, const float* xs, float* r
   uint2 raw[ITS];
 #pragma unroll
   for (int it = 0; it < ITS; ++it) {
-    const int i = (it * DEC_WAVES + wave) * KPW + grp;
+    const int i = (it * NW + wave) * KPW + grp;
     raw[it] = ld8(F + (size_t)i * D + part * VEC);
   }
 #pragma unroll
   for (int it = 0; it < ITS; ++it) {
-    const int i = (it * DEC_WAVES + wave) * KPW + grp;
+    const int i = (it * NW + wave) * KPW + grp;
     float f[VEC];
     RowVec<T>::get(raw[it], f);
 #pragma unroll
@@ -176,14 +181,14 @@ __device__ __forceinline__ void np_map_vec(const T* F, const float* xs, float* r
 #pragma unroll
       for (int e = 0; e < VEC; ++e) red8[(wave * NR + r) * D + part * VEC + e] = acc[r][e];
   __syncthreads();
-  for (int e = tid; e < NR * D; e += DEC_THREADS) {
+  for (int e = tid; e < NR * D; e += NT) {
     float u = 0.f;
 #pragma unroll
-    for (int w = 0; w < DEC_WAVES; ++w) u += red8[w * NR * D + e];
+    for (int w = 0; w < NW; ++w) u += red8[w * NR * D + e];
     us[e] = u;
   }
   __syncthreads();
-  for (int r = wave; r < NR; r += DEC_WAVES) {
+  for (int r = wave; r < NR; r += NW) {
     float mx = STILL_NEG_INF, xn = 0.f;
     for (int j = lane; j < D; j += 64) {
       mx = fmaxf(mx, us[r * D + j]);
@@ -203,7 +208,7 @@ __device__ __forceinline__ void np_map_vec(const T* F, const float* xs, float* r
     }
   }
   __syncthreads();
-  for (int e = tid; e < NR * D; e += DEC_THREADS) {
+  for (int e = tid; e < NR * D; e += NT) {
     const int r = e / D;
     ph[e] = expf(us[e] - rowst[2 * r]) * rowst[2 * r + 1];
   }
@@ -216,7 +221,7 @@ __device__ __forceinline__ void np_map_vec(const T* F, const float* xs, float* r
 // before decode_kernel of the same step; on a position mismatch it does
 // nothing (decode_kernel then flags the error).
 template <typename T, int D>
-__global__ __launch_bounds__(DEC_THREADS) void decode_boundary_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(BND_THREADS) void decode_boundary_kernel(DecodeArgs a) {
   using LD = DecLds<T, D, 1>;
   constexpr int VEC = RowVec<T>::N;
   constexpr int LPK = D / VEC;
@@ -250,10 +255,10 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_boundary_kernel(DecodeArgs
   const int c = t / C, cC = c * C;
   double* ps = d64;      // [C] scores of the finished chunk
   int* kept = ibuf + 2;  // [C] rank among kept, or -1
-  for (int j = tid; j < C; j += DEC_THREADS) ps[j] = pend[j];
+  for (int j = tid; j < C; j += BND_THREADS) ps[j] = pend[j];
   __syncthreads();
   const int lam_c = (n_pool + a.lam <= a.m - W) ? a.lam : 0;
-  for (int j = tid; j < C; j += DEC_THREADS) {
+  for (int j = tid; j < C; j += BND_THREADS) {
     int r = 0;  // rank by (score desc, position asc)
     for (int i = 0; i < C; ++i) r += (ps[i] > ps[j] || (ps[i] == ps[j] && i < j)) ? 1 : 0;
     kept[j] = r < lam_c ? 1 : 0;
@@ -265,7 +270,7 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_boundary_kernel(DecodeArgs
   }
   __syncthreads();
   const int base = cC - C;
-  for (int e = tid; e < C * LPK; e += DEC_THREADS) {
+  for (int e = tid; e < C * LPK; e += BND_THREADS) {
     const int j = e / LPK, part = e % LPK;
     if (kept[j] < 0) continue;
     const int pos = base + j, slot = pos % R, row = n_pool + kept[j];
@@ -279,8 +284,8 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_boundary_kernel(DecodeArgs
     }
   }
   if (a.sel_new)
-    for (int i = lam_c + tid; i < a.lam; i += DEC_THREADS) a.sel_new[(size_t)unit * a.lam + i] = -1;
-  for (int j = tid; j < C; j += DEC_THREADS) pend[j] = __builtin_nan("");
+    for (int i = lam_c + tid; i < a.lam; i += BND_THREADS) a.sel_new[(size_t)unit * a.lam + i] = -1;
+  for (int j = tid; j < C; j += BND_THREADS) pend[j] = __builtin_nan("");
   n_pool += lam_c;
   __syncthreads();
   if (tid == 0) meta[1] = n_pool;
@@ -288,14 +293,14 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_boundary_kernel(DecodeArgs
   // fold chunks [cf(c-1), cf(c)) into S, z (float32 features, exact expf)
   const int f_lo = full_chunks_before(c - 1, W, C) * C;
   const int f_hi = full_chunks_before(c, W, C) * C;
-  constexpr int PER = D * D / DEC_THREADS;
+  constexpr int PER = D * D / BND_THREADS;
   float dacc[PER];
 #pragma unroll
   for (int q2 = 0; q2 < PER; ++q2) dacc[q2] = 0.f;
   float dz = 0.f;
   for (int g0 = f_lo; g0 < f_hi; g0 += FR) {
     const int n = min(FR, f_hi - g0);
-    for (int e = tid; e < FR * D; e += DEC_THREADS) {
+    for (int e = tid; e < FR * D; e += BND_THREADS) {
       const int r = e / D, i = e % D, pos = g0 + r;
       const int slot = pos % R;
       const bool use = r < n && ring_flag[slot] == 0;
@@ -303,14 +308,14 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_boundary_kernel(DecodeArgs
       vs[e] = use ? to_f32(ring_v[(size_t)slot * D + i]) : 0.f;
     }
     __syncthreads();
-    np_map_vec<T, D, FR>(F, xs, red8, us, ph, rowst);
+    np_map_vec<T, D, FR, BND_THREADS>(F, xs, red8, us, ph, rowst);
     // thread tid owns S[i][jv] for jv = tid % D and i = tid / D + q2 * (512 / D)
 #pragma unroll 1
     for (int r = 0; r < FR; ++r) {
       const float vr = vs[r * D + tid % D];
       const float* pr = ph + r * D + tid / D;
 #pragma unroll
-      for (int q2 = 0; q2 < PER; ++q2) dacc[q2] += pr[q2 * (DEC_THREADS / D)] * vr;
+      for (int q2 = 0; q2 < PER; ++q2) dacc[q2] += pr[q2 * (BND_THREADS / D)] * vr;
     }
     if (tid < D)
       for (int r = 0; r < FR; ++r) dz += ph[r * D + tid];
@@ -318,14 +323,14 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_boundary_kernel(DecodeArgs
   }
   if (f_hi > f_lo) {
 #pragma unroll
-    for (int q2 = 0; q2 < PER; ++q2) S[tid + DEC_THREADS * q2] += dacc[q2];
+    for (int q2 = 0; q2 < PER; ++q2) S[tid + BND_THREADS * q2] += dacc[q2];
     if (tid < D) z[tid] += dz;
   }
   __syncthreads();
 }
 
 template <typename T, int D, int G>
-__global__ __launch_bounds__(DEC_THREADS) __attribute__((amdgpu_waves_per_eu(G >= 8 ? 2 : 4)))
+__global__ __launch_bounds__(DEC_THREADS) __attribute__((amdgpu_waves_per_eu(2)))
 void decode_kernel(DecodeArgs a) {
   using LD = DecLds<T, D, G>;
   constexpr int VEC = RowVec<T>::N;  // elements per 8-byte vector
@@ -421,23 +426,27 @@ void decode_kernel(DecodeArgs a) {
   for (int w = 0; w < DEC_WAVES; ++w) n_oob += ibuf[1 + w];
   const int n_sa = n_oob + n_win;
 
-  // softmax keys in batches of U rows per lane, two batches in flight
-  constexpr int STRIDE = DEC_WAVES * KPW * U;
-  auto load_sa = [&](int k0, uint2 (&rk)[U], uint2 (&rv)[U]) {
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int kk = k0 + u * KPW + grp;
-      const bool ok = kk < n_sa;
-      const size_t row = kk < n_oob ? (size_t)kk : (size_t)((lo + kk - n_oob) % R);
-      rk[u] = ok ? ld8((kk < n_oob ? pool_k : ring_k) + row * D + part * VEC) : uint2{0, 0};
-      rv[u] = ok ? ld8((kk < n_oob ? pool_v : ring_v) + row * D + part * VEC) : uint2{0, 0};
-    }
+  const int r16 = lane & 15, g4 = lane >> 4;
+  constexpr int DV = D / 64;  // value columns per lane
+  auto krow_sa = [&](int kk) -> const T* {
+    return kk < n_oob ? pool_k + (size_t)kk * D : ring_k + (size_t)((lo + kk - n_oob) % R) * D;
   };
-  uint2 rkA[U], rvA[U], rkB[U], rvB[U];
-  const int k_first = wave * KPW * U;
-  load_sa(k_first, rkA, rvA);  // the new token's ring row is read back: ordered by the barrier above
+  const __amdgpu_buffer_rsrc_t pv_r = make_rsrc(pool_v, (uint32_t)((a.m - W) * D * sizeof(T)));
+  const __amdgpu_buffer_rsrc_t rv_r = make_rsrc(ring_v, (uint32_t)(R * D * sizeof(T)));
+  struct RRow {
+    __amdgpu_buffer_rsrc_t first;
+    int second;
+  };
+  auto vrow_sa = [&](int kk) -> RRow {
+    return kk < n_oob ? RRow{pv_r, kk} : RRow{rv_r, (lo + kk - n_oob) % R};
+  };
+  struct TileRegs0 {
+    Frag<T> af[D / 32];
+    uint32_t vw[16];
+  };
+  TileRegs0 TA0;
 
-  np_map_vec<T, D, G + 1>(F, xs, red8, us, ph, rowst);
+  np_map_vec<T, D, G + 1, DEC_THREADS>(F, xs, red8, us, ph, rowst);
   for (int e = tid; e < G * D; e += DEC_THREADS) phq[e] = ph[e];
   for (int i = tid; i < D; i += DEC_THREADS) ring_phi[(size_t)slot_t * D + i] = from_f32<T>(ph[G * D + i]);
 
@@ -482,80 +491,151 @@ void decode_kernel(DecodeArgs a) {
         for (int e = 0; e < 4; ++e) redS[(wave * G + h) * D + sp * 4 + e] = accS[h][e];
   }
 
-  // ---- 3b. one streaming pass over the keys: running max m, sum l and
-  //         weighted values per (row group, head); softmax keys take
-  //         logits, linear keys log(g) + log <phi(q), phi(k)> -------------
-  float m[G], l[G], acc[G][VEC];
+  // ---- 3b. the keys in 16-key tiles, one tile per wave at a time: logits by
+  //         MFMA (keys as A rows against the heads' query columns), a running
+  //         max m and sum l per head in lanes r = h, the tile's weights
+  //         through a per-wave LDS slot to every lane, which owns D/64 value
+  //         columns; softmax keys take logits, linear keys log(g) +
+  //         log <phi(q), phi(k)> -------------------------------------------
+  float* pwv = reinterpret_cast<float*>(smem + LD::pw) + wave * 17 * 8;  // [16 keys + al][8]
+  float mh = STILL_NEG_INF, lh = 0.f;  // lanes r16 = h < G
+  float acc[G][DV];
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
-    m[h] = STILL_NEG_INF;
-    l[h] = 0.f;
+  for (int h = 0; h < G; ++h)
 #pragma unroll
-    for (int e = 0; e < VEC; ++e) acc[h][e] = 0.f;
-  }
-  // folds U keys of log-weights s[u][h] and values rv[u] into (m, l, acc)
-  auto absorb = [&](const float (&s)[U][G], const uint2 (&rv)[U]) {
-    float al[G];
+    for (int e = 0; e < DV; ++e) acc[h][e] = 0.f;
+  auto wave_sync = [] {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  };
+  // query-side B fragments: lane (r, g) holds x_r[32 kb + 8 g .. + 8] for
+  // rows r < G of src (float32 in LDS), zero above; with a split, the part
+  // the first rounding lost
+  auto qfrag = [&](const float* src, int kb, bool lo_part) {
+    float v[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float x = r16 < G ? src[r16 * D + 32 * kb + 8 * g4 + e] : 0.f;
+      v[e] = lo_part ? x - to_f32(from_f32<T>(x)) : x;
+    }
+    return frag_from<T>(f32x4{v[0], v[1], v[2], v[3]}, f32x4{v[4], v[5], v[6], v[7]});
+  };
+  // a tile in flight: A fragments of its 16 key rows and, per row, this
+  // lane's DV value columns (DV * sizeof(T) <= 4 bytes)
+  using TileRegs = TileRegs0;
+  TileRegs& TA = TA0;
+  TileRegs TB;
+  // key rows: flat loads (a tile may span the pool and the ring); value
+  // columns: buffer loads with the row in the scalar offset, so the 16 rows
+  // of a tile need no per-row address registers
+  auto load_tile = [&](TileRegs& X, int kk0, int n, auto krow, auto vrow) {
+    const int kr_ = kk0 + r16;
+    const T* kp = kr_ < n ? krow(kr_) : nullptr;
+#pragma unroll
+    for (int kb = 0; kb < D / 32; ++kb) X.af[kb] = kp ? ld_frag(kp + 32 * kb + 8 * g4) : zero_frag<T>();
+    const uint32_t voff = lane * DV * sizeof(T);
+#pragma unroll
+    for (int jj = 0; jj < 16; ++jj) {
+      const int kk = kk0 + jj;  // uniform
+      uint32_t w = 0;
+      if (kk < n) {
+        const auto rv = vrow(kk);  // (resource, row)
+        const uint32_t soff = (uint32_t)rv.second * D * sizeof(T);
+        if constexpr (DV * sizeof(T) == 4) w = __builtin_amdgcn_raw_buffer_load_b32(rv.first, voff, soff, 0);
+        else w = __builtin_amdgcn_raw_buffer_load_b16(rv.first, voff, soff, 0);
+      }
+      X.vw[jj] = w;
+    }
+  };
+  // one tile: weight(c, kk) turns a product into a log-weight
+  auto tile = [&](const TileRegs& X, int kk0, int n, const Frag<T>* qb, const Frag<T>* qb2,
+                  auto weight) {
+    f32x4 c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < D / 32; ++kb) {
+      mma(c, X.af[kb], qb[kb]);
+      if (qb2) mma(c, X.af[kb], qb2[kb]);
+    }
+    // c[i] = <key kk0 + 4g + i, query-side column r>
+    float mx = STILL_NEG_INF;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int kk = kk0 + 4 * g4 + i;
+      c[i] = (r16 < G && kk < n) ? weight(c[i], kk) : STILL_NEG_INF;
+      mx = fmaxf(mx, c[i]);
+    }
+    mx = fmaxf(mx, xor16f(mx));
+    mx = fmaxf(mx, xor32f(mx));
+    const float mn = fmaxf(mh, mx);
+    const float al = (mh == STILL_NEG_INF || mn == STILL_NEG_INF) ? 0.f : __expf(mh - mn);
+    float ls = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      c[i] = c[i] == STILL_NEG_INF ? 0.f : __expf(c[i] - mn);
+      ls += c[i];
+    }
+    ls += xor16f(ls);
+    ls += xor32f(ls);
+    lh = lh * al + ls;
+    mh = mn;
+    if (r16 < 8) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pwv[(4 * g4 + i) * 8 + r16] = c[i];
+      if (g4 == 0) pwv[128 + r16] = al;
+    }
+    wave_sync();
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      float mb = m[h];
+      const float a_h = pwv[128 + h];
 #pragma unroll
-      for (int u = 0; u < U; ++u) mb = fmaxf(mb, s[u][h]);
-      // rows with nothing visible yet keep m = -inf and zero sums
-      al[h] = (m[h] == STILL_NEG_INF || mb == STILL_NEG_INF) ? 0.f : __expf(m[h] - mb);
-      m[h] = mb;
-      l[h] *= al[h];
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) acc[h][e] *= al[h];
+      for (int e = 0; e < DV; ++e) acc[h][e] *= a_h;
     }
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      float x[VEC];
-      RowVec<T>::get(rv[u], x);
+    for (int jj = 0; jj < 16; ++jj) {
+      float v[DV];
+      const T* ve = reinterpret_cast<const T*>(&X.vw[jj]);
+#pragma unroll
+      for (int e = 0; e < DV; ++e) v[e] = to_f32(ve[e]);
 #pragma unroll
       for (int h = 0; h < G; ++h) {
-        const float p = s[u][h] == STILL_NEG_INF ? 0.f : __expf(s[u][h] - m[h]);
-        l[h] += p;
+        const float pj = pwv[jj * 8 + h];
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) acc[h][e] += p * x[e];
+        for (int e = 0; e < DV; ++e) acc[h][e] += pj * v[e];
       }
+    }
+    wave_sync();  // the slot is written again by the next tile
+  };
+  // the tiles of wave w: w, w + waves, ...; two in flight
+  auto run_tiles = [&](TileRegs& A, TileRegs& B, bool a_loaded, int n, auto krow, auto vrow,
+                       const Frag<T>* qb, const Frag<T>* qb2, auto weight) {
+    constexpr int STEP = 16 * DEC_WAVES;
+    const int first = 16 * wave;
+    if (!a_loaded) load_tile(A, first, n, krow, vrow);
+    for (int kk0 = first; kk0 < n; kk0 += 2 * STEP) {  // wave-uniform
+      if (kk0 + STEP < n) load_tile(B, kk0 + STEP, n, krow, vrow);
+      tile(A, kk0, n, qb, qb2, weight);
+      if (kk0 + STEP >= n) break;
+      if (kk0 + 2 * STEP < n) load_tile(A, kk0 + 2 * STEP, n, krow, vrow);
+      tile(B, kk0 + STEP, n, qb, qb2, weight);
     }
   };
   {
+    Frag<T> qb[D / 32];
+#pragma unroll
+    for (int kb = 0; kb < D / 32; ++kb) qb[kb] = qfrag(qs, kb, false);
+    const float scale = a.scale;
+    run_tiles(TA, TB, false, n_sa, krow_sa, vrow_sa, qb, (const Frag<T>*)nullptr,
+              [&](float x, int) { return x * scale; });
+    // float64 window logits of the new token (its score), from the window's
+    // ring rows (just read, so cached); products of bf16/f32 values are
+    // exact in float64
+    const int n_sc = t - sc_lo + 1;
     float qv[G][VEC];
 #pragma unroll
     for (int h = 0; h < G; ++h)
 #pragma unroll
       for (int e = 0; e < VEC; ++e) qv[h][e] = qs[h * D + part * VEC + e];
-    auto compute_sa = [&](int k0, const uint2 (&rk)[U], const uint2 (&rv)[U]) {
-      float s[U][G];
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int kk = k0 + u * KPW + grp;
-        float x[VEC];
-        RowVec<T>::get(rk[u], x);
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-          float d = 0.f;
-#pragma unroll
-          for (int e = 0; e < VEC; ++e) d += qv[h][e] * x[e];
-          d = sum_lanes<LPK>(d);
-          s[u][h] = kk < n_sa ? d * a.scale : STILL_NEG_INF;
-        }
-      }
-      absorb(s, rv);
-    };
-    for (int k0 = k_first; k0 < n_sa; k0 += 2 * STRIDE) {  // wave-uniform bounds
-      load_sa(k0 + STRIDE, rkB, rvB);
-      compute_sa(k0, rkA, rvA);
-      if (k0 + STRIDE >= n_sa) break;
-      load_sa(k0 + 2 * STRIDE, rkA, rvA);
-      compute_sa(k0 + STRIDE, rkB, rvB);
-    }
-    // float64 window logits of the new token (its score), from the window's
-    // ring rows (just read, so cached); products of bf16/f32 values are
-    // exact in float64
-    const int n_sc = t - sc_lo + 1;
     for (int k0 = wave * KPW; k0 < n_sc; k0 += DEC_WAVES * KPW) {
       const int jj = k0 + grp;
       const bool ok = jj < n_sc;  // uniform over the row's lanes
@@ -573,75 +653,37 @@ void decode_kernel(DecodeArgs a) {
     }
   }
   if (n_la > 0) {
-    float pv[G][VEC], lgate[G];
+    // phi(q) as T hi + lo parts (float32 data: exact in one part)
+    Frag<T> pb[D / 32], pb2[D / 32];
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      const float g = a.gate[kv * G + h];
-      lgate[h] = g > 0.f ? __logf(g) : STILL_NEG_INF;
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) pv[h][e] = phq[h * D + part * VEC + e];
+    for (int kb = 0; kb < D / 32; ++kb) {
+      pb[kb] = qfrag(phq, kb, false);
+      pb2[kb] = qfrag(phq, kb, true);
     }
-    for (int k0 = wave * KPW * U; k0 < n_la; k0 += DEC_WAVES * KPW * U) {
-      uint2 rk[U], rv[U];
-      bool la[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int kk = k0 + u * KPW + grp;
-        const size_t slot = (size_t)((la_lo + kk) % R);
-        la[u] = kk < n_la && ring_flag[slot] == 0;
-        rk[u] = la[u] ? ld8(ring_phi + slot * D + part * VEC) : uint2{0, 0};
-        rv[u] = la[u] ? ld8(ring_v + slot * D + part * VEC) : uint2{0, 0};
-      }
-      float s[U][G];
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        float x[VEC];
-        RowVec<T>::get(rk[u], x);
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-          float w = 0.f;
-#pragma unroll
-          for (int e = 0; e < VEC; ++e) w += pv[h][e] * x[e];
-          w = sum_lanes<LPK>(w);
-          s[u][h] = (la[u] && w > 0.f) ? lgate[h] + __logf(w) : STILL_NEG_INF;
-        }
-      }
-      absorb(s, rv);
-    }
+    const float g_r = r16 < G ? a.gate[kv * G + r16] : 0.f;
+    const float lgate = g_r > 0.f ? __logf(g_r) : STILL_NEG_INF;
+    auto krow = [&](int kk) -> const T* { return ring_phi + (size_t)((la_lo + kk) % R) * D; };
+    auto vrow = [&](int kk) -> RRow { return RRow{rv_r, (la_lo + kk) % R}; };
+    auto weight = [&](float w, int kk) {
+      const bool la = ring_flag[(la_lo + kk) % R] == 0;
+      return (la && w > 0.f) ? lgate + __logf(w) : STILL_NEG_INF;
+    };
+    run_tiles(TA, TB, false, n_la, krow, vrow, pb, sizeof(T) == 2 ? pb2 : (const Frag<T>*)nullptr, weight);
   }
-  // merge the row groups of each wave, then publish per wave
-  auto merge = [&](auto px) {
+  // publish per wave: (m, l) per head from lanes r = h, the value slices
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      const float m2 = px(m[h]), l2 = px(l[h]);
-      const float mm = fmaxf(m[h], m2);
-      const float a1 = m[h] == STILL_NEG_INF ? 0.f : __expf(m[h] - mm);
-      const float a2 = m2 == STILL_NEG_INF ? 0.f : __expf(m2 - mm);
-      l[h] = l[h] * a1 + l2 * a2;
+  for (int h = 0; h < G; ++h)
 #pragma unroll
-      for (int e = 0; e < VEC; ++e) acc[h][e] = acc[h][e] * a1 + px(acc[h][e]) * a2;
-      m[h] = mm;
-    }
-  };
-  if constexpr (LPK <= 16) merge([](float x) { return xorf<16>(x); });
-  merge([](float x) { return xorf<32>(x); });
-  if (grp == 0) {
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) redA[(wave * G + h) * D + part * VEC + e] = acc[h][e];
-      if (part == 0) {
-        mlw[(wave * G + h) * 2] = m[h];
-        mlw[(wave * G + h) * 2 + 1] = l[h];
-      }
-    }
+    for (int e = 0; e < DV; ++e) redA[(wave * G + h) * D + lane * DV + e] = acc[h][e];
+  if (g4 == 0 && r16 < G) {
+    mlw[(wave * G + r16) * 2] = mh;
+    mlw[(wave * G + r16) * 2 + 1] = lh;
   }
   __syncthreads();
 
   // ---- 4. float64 score of token t [P3 "Self-Saliency Score"] and the
-  //         normaliser of each head (wave h) --------------------------------
-  if (wave < G) {
-    const int h = wave;
+  //         normaliser of each head (one wave per head) ------------------
+  for (int h = wave; h < G; h += DEC_WAVES) {  // wave-uniform
     {  // score: KL(a_diag || (1-eps) a_nodiag + eps delta_t) in float64
       const int n = t - sc_lo + 1;
       const double* x = lg + h * W;
