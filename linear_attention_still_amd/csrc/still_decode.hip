@@ -428,8 +428,11 @@ void decode_kernel(DecodeArgs a) {
 
   const int r16 = lane & 15, g4 = lane >> 4;
   constexpr int DV = D / 64;  // value columns per lane
+  // ring slots of consecutive positions: one modulo each, then a wrap
+  const int lo_slot = lo % R, la_slot = la_lo % R, sc_slot = sc_lo % R;
+  auto wrap = [R](int s_) { return s_ >= R ? s_ - R : s_; };
   auto krow_sa = [&](int kk) -> const T* {
-    return kk < n_oob ? pool_k + (size_t)kk * D : ring_k + (size_t)((lo + kk - n_oob) % R) * D;
+    return kk < n_oob ? pool_k + (size_t)kk * D : ring_k + (size_t)wrap(lo_slot + kk - n_oob) * D;
   };
   const __amdgpu_buffer_rsrc_t pv_r = make_rsrc(pool_v, (uint32_t)((a.m - W) * D * sizeof(T)));
   const __amdgpu_buffer_rsrc_t rv_r = make_rsrc(ring_v, (uint32_t)(R * D * sizeof(T)));
@@ -438,7 +441,7 @@ void decode_kernel(DecodeArgs a) {
     int second;
   };
   auto vrow_sa = [&](int kk) -> RRow {
-    return kk < n_oob ? RRow{pv_r, kk} : RRow{rv_r, (lo + kk - n_oob) % R};
+    return kk < n_oob ? RRow{pv_r, kk} : RRow{rv_r, wrap(lo_slot + kk - n_oob)};
   };
   struct TileRegs0 {
     Frag<T> af[D / 32];
@@ -627,29 +630,26 @@ void decode_kernel(DecodeArgs a) {
     const float scale = a.scale;
     run_tiles(TA, TB, false, n_sa, krow_sa, vrow_sa, qb, (const Frag<T>*)nullptr,
               [&](float x, int) { return x * scale; });
-    // float64 window logits of the new token (its score), from the window's
-    // ring rows (just read, so cached); products of bf16/f32 values are
-    // exact in float64
+    // float64 window logits of the new token (its score): one (head, key)
+    // dot product per lane, from the window's ring rows (just read, so
+    // cached); products of bf16/f32 values are exact in float64
     const int n_sc = t - sc_lo + 1;
-    float qv[G][VEC];
+    constexpr int VE = 16 / sizeof(T);
+    for (int pidx = tid; pidx < G * n_sc; pidx += DEC_THREADS) {
+      const int h = pidx / n_sc, jj = pidx % n_sc;
+      const T* kr = ring_k + (size_t)wrap(sc_slot + jj) * D;
+      const float* qh = qs + h * D;
+      uint4 raw[D / VE];
 #pragma unroll
-    for (int h = 0; h < G; ++h)
+      for (int c = 0; c < D / VE; ++c) raw[c] = *reinterpret_cast<const uint4*>(kr + c * VE);
+      double d64s = 0.0;
 #pragma unroll
-      for (int e = 0; e < VEC; ++e) qv[h][e] = qs[h * D + part * VEC + e];
-    for (int k0 = wave * KPW; k0 < n_sc; k0 += DEC_WAVES * KPW) {
-      const int jj = k0 + grp;
-      const bool ok = jj < n_sc;  // uniform over the row's lanes
-      const uint2 raw = ok ? ld8(ring_k + (size_t)((sc_lo + jj) % R) * D + part * VEC) : uint2{0, 0};
-      float x[VEC];
-      RowVec<T>::get(raw, x);
+      for (int c = 0; c < D / VE; ++c) {
+        const T* ke = reinterpret_cast<const T*>(&raw[c]);
 #pragma unroll
-      for (int h = 0; h < G; ++h) {
-        double d64s = 0.0;
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) d64s += (double)qv[h][e] * (double)x[e];
-        d64s = sum_lanes_f64<LPK>(d64s);
-        if (ok && part == 0) lg[h * W + jj] = a.scale64 * d64s;
+        for (int e = 0; e < VE; ++e) d64s += (double)qh[c * VE + e] * (double)to_f32(ke[e]);
       }
+      lg[h * W + jj] = a.scale64 * d64s;
     }
   }
   if (n_la > 0) {
@@ -662,10 +662,10 @@ void decode_kernel(DecodeArgs a) {
     }
     const float g_r = r16 < G ? a.gate[kv * G + r16] : 0.f;
     const float lgate = g_r > 0.f ? __logf(g_r) : STILL_NEG_INF;
-    auto krow = [&](int kk) -> const T* { return ring_phi + (size_t)((la_lo + kk) % R) * D; };
-    auto vrow = [&](int kk) -> RRow { return RRow{rv_r, (la_lo + kk) % R}; };
+    auto krow = [&](int kk) -> const T* { return ring_phi + (size_t)wrap(la_slot + kk) * D; };
+    auto vrow = [&](int kk) -> RRow { return RRow{rv_r, wrap(la_slot + kk)}; };
     auto weight = [&](float w, int kk) {
-      const bool la = ring_flag[(la_lo + kk) % R] == 0;
+      const bool la = ring_flag[wrap(la_slot + kk)] == 0;
       return (la && w > 0.f) ? lgate + __logf(w) : STILL_NEG_INF;
     };
     run_tiles(TA, TB, false, n_la, krow, vrow, pb, sizeof(T) == 2 ? pb2 : (const Frag<T>*)nullptr, weight);
