@@ -341,7 +341,7 @@ void decode_kernel(DecodeArgs a) {
   constexpr int U = 4;               // rows in flight per lane
   extern __shared__ __align__(16) char smem[];
   const int kv = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;  // wave index in an SGPR
   const int unit = b * a.Hkv + kv;
   const int W = a.W, C = a.C, R = a.R, t = a.t;
   char* st = a.state + (size_t)unit * a.st_unit;
@@ -431,17 +431,17 @@ void decode_kernel(DecodeArgs a) {
   // ring slots of consecutive positions: one modulo each, then a wrap
   const int lo_slot = lo % R, la_slot = la_lo % R, sc_slot = sc_lo % R;
   auto wrap = [R](int s_) { return s_ >= R ? s_ - R : s_; };
-  auto krow_sa = [&](int kk) -> const T* {
-    return kk < n_oob ? pool_k + (size_t)kk * D : ring_k + (size_t)wrap(lo_slot + kk - n_oob) * D;
+  auto krow_sa = [&](int kk) -> uint32_t {  // byte offset of key row kk in the state blob
+    return kk < n_oob ? (uint32_t)a.st_pool_k + (uint32_t)kk * (D * sizeof(T))
+                      : (uint32_t)a.st_ring_k + (uint32_t)wrap(lo_slot + kk - n_oob) * (D * sizeof(T));
   };
-  const __amdgpu_buffer_rsrc_t pv_r = make_rsrc(pool_v, (uint32_t)((a.m - W) * D * sizeof(T)));
-  const __amdgpu_buffer_rsrc_t rv_r = make_rsrc(ring_v, (uint32_t)(R * D * sizeof(T)));
-  struct RRow {
-    __amdgpu_buffer_rsrc_t first;
-    int second;
-  };
-  auto vrow_sa = [&](int kk) -> RRow {
-    return kk < n_oob ? RRow{pv_r, kk} : RRow{rv_r, wrap(lo_slot + kk - n_oob)};
+  // value rows as byte offsets into this unit's state blob (one buffer
+  // resource, the row offset a scalar)
+  const __amdgpu_buffer_rsrc_t st_r = make_rsrc(st, (uint32_t)a.st_unit);
+  const uint32_t pv_off = (uint32_t)a.st_pool_v, rv_off = (uint32_t)a.st_ring_v;
+  auto vrow_sa = [&](int kk) -> uint32_t {
+    return kk < n_oob ? pv_off + (uint32_t)kk * (D * sizeof(T))
+                      : rv_off + (uint32_t)wrap(lo_slot + kk - n_oob) * (D * sizeof(T));
   };
   struct TileRegs0 {
     Frag<T> af[D / 32];
@@ -533,22 +533,19 @@ void decode_kernel(DecodeArgs a) {
   // columns: buffer loads with the row in the scalar offset, so the 16 rows
   // of a tile need no per-row address registers
   auto load_tile = [&](TileRegs& X, int kk0, int n, auto krow, auto vrow) {
+    // absent rows read at the end of the blob, past the range: zeros
+    const uint32_t oob = (uint32_t)a.st_unit;
     const int kr_ = kk0 + r16;
-    const T* kp = kr_ < n ? krow(kr_) : nullptr;
+    const uint32_t koff = (kr_ < n ? krow(kr_) : oob) + 8 * g4 * sizeof(T);
 #pragma unroll
-    for (int kb = 0; kb < D / 32; ++kb) X.af[kb] = kp ? ld_frag(kp + 32 * kb + 8 * g4) : zero_frag<T>();
+    for (int kb = 0; kb < D / 32; ++kb) X.af[kb] = ld_frag_buf<T>(st_r, koff, 32 * kb * sizeof(T));
     const uint32_t voff = lane * DV * sizeof(T);
 #pragma unroll
     for (int jj = 0; jj < 16; ++jj) {
       const int kk = kk0 + jj;  // uniform
-      uint32_t w = 0;
-      if (kk < n) {
-        const auto rv = vrow(kk);  // (resource, row)
-        const uint32_t soff = (uint32_t)rv.second * D * sizeof(T);
-        if constexpr (DV * sizeof(T) == 4) w = __builtin_amdgcn_raw_buffer_load_b32(rv.first, voff, soff, 0);
-        else w = __builtin_amdgcn_raw_buffer_load_b16(rv.first, voff, soff, 0);
-      }
-      X.vw[jj] = w;
+      const uint32_t soff = __builtin_amdgcn_readfirstlane(kk < n ? vrow(kk) : oob);
+      if constexpr (DV * sizeof(T) == 4) X.vw[jj] = __builtin_amdgcn_raw_buffer_load_b32(st_r, voff, soff, 0);
+      else X.vw[jj] = __builtin_amdgcn_raw_buffer_load_b16(st_r, voff, soff, 0);
     }
   };
   // one tile: weight(c, kk) turns a product into a log-weight
@@ -662,8 +659,10 @@ void decode_kernel(DecodeArgs a) {
     }
     const float g_r = r16 < G ? a.gate[kv * G + r16] : 0.f;
     const float lgate = g_r > 0.f ? __logf(g_r) : STILL_NEG_INF;
-    auto krow = [&](int kk) -> const T* { return ring_phi + (size_t)wrap(la_slot + kk) * D; };
-    auto vrow = [&](int kk) -> RRow { return RRow{rv_r, wrap(la_slot + kk)}; };
+    auto krow = [&](int kk) -> uint32_t {
+      return (uint32_t)a.st_ring_phi + (uint32_t)wrap(la_slot + kk) * (D * sizeof(T));
+    };
+    auto vrow = [&](int kk) -> uint32_t { return rv_off + (uint32_t)wrap(la_slot + kk) * (D * sizeof(T)); };
     auto weight = [&](float w, int kk) {
       const bool la = ring_flag[wrap(la_slot + kk)] == 0;
       return (la && w > 0.f) ? lgate + __logf(w) : STILL_NEG_INF;
