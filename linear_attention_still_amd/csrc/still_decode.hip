@@ -136,9 +136,29 @@ __device__ __forceinline__ float wave_sum(float x) { return sum_lanes<64>(x); }
 // partial sums over the F rows reduced across lanes and then across waves
 // through red8 [waves][NR][D]. xs, us, ph are [NR][D] float32 in LDS. All
 // threads; ends with a barrier.
+// The rows of F one lane reads for np_map_vec (issued early by callers).
+template <typename T, int D, int NT>
+struct FRows {
+  static constexpr int NW = NT / 64;
+  static constexpr int VEC = RowVec<T>::N, LPK = D / VEC, KPW = 64 / LPK;
+  static constexpr int ITS = D / (NW * KPW);  // F rows per lane
+  uint2 raw[ITS];
+  __device__ __forceinline__ void load(const T* F) {
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int part = lane % LPK, grp = lane / LPK;
+#pragma unroll
+    for (int it = 0; it < ITS; ++it) raw[it] = ld8(F + (size_t)((it * NW + wave) * KPW + grp) * D + part * VEC);
+  }
+};
+
+// element e of the 8 consecutive columns a fragment holds, as float32
+__device__ __forceinline__ float frag_at(const Frag<bf16>& f, int e) { return (float)f.v[e]; }
+__device__ __forceinline__ float frag_at(const Frag<f16>& f, int e) { return (float)f.v[e]; }
+__device__ __forceinline__ float frag_at(const Frag<float>& f, int e) { return e < 4 ? f.lo[e] : f.hi[e - 4]; }
+
 template <typename T, int D, int NR, int NT>
-__device__ __forceinline__ void np_map_vec(const T* F, const float* xs, float* red8, float* us,
-                                           float* ph, float* rowst) {
+__device__ __forceinline__ void np_map_vec(const FRows<T, D, NT>& FR_, const float* xs, float* red8,
+                                           float* us, float* ph, float* rowst) {
   constexpr int NW = NT / 64;
   constexpr int VEC = RowVec<T>::N, LPK = D / VEC, KPW = 64 / LPK;
   constexpr int ITS = D / (NW * KPW);  // F rows per lane
@@ -149,12 +169,7 @@ __device__ __forceinline__ void np_map_vec(const T* F, const float* xs, float* r
   for (int r = 0; r < NR; ++r)
 #pragma unroll
     for (int e = 0; e < VEC; ++e) acc[r][e] = 0.f;
-  uint2 raw[ITS];
-#pragma unroll
-  for (int it = 0; it < ITS; ++it) {
-    const int i = (it * NW + wave) * KPW + grp;
-    raw[it] = ld8(F + (size_t)i * D + part * VEC);
-  }
+  const uint2* raw = FR_.raw;
 #pragma unroll
   for (int it = 0; it < ITS; ++it) {
     const int i = (it * NW + wave) * KPW + grp;
@@ -308,7 +323,9 @@ __global__ __launch_bounds__(BND_THREADS) void decode_boundary_kernel(DecodeArgs
       vs[e] = use ? to_f32(ring_v[(size_t)slot * D + i]) : 0.f;
     }
     __syncthreads();
-    np_map_vec<T, D, FR, BND_THREADS>(F, xs, red8, us, ph, rowst);
+    FRows<T, D, BND_THREADS> fr;
+    fr.load(F);
+    np_map_vec<T, D, FR, BND_THREADS>(fr, xs, red8, us, ph, rowst);
     // thread tid owns S[i][jv] for jv = tid % D and i = tid / D + q2 * (512 / D)
 #pragma unroll 1
     for (int r = 0; r < FR; ++r) {
@@ -371,6 +388,34 @@ void decode_kernel(DecodeArgs a) {
   float* red = reinterpret_cast<float*>(smem + LD::uni);  // [2][waves][G][D]
   double* lg = reinterpret_cast<double*>(smem + LD::lg);
 
+  // loads that depend on nothing else go first, so their latencies overlap:
+  // the S rows of this lane's readout share, the F rows of the NP-Map, the
+  // queries and the new key / value
+  const int sp = lane % SL, sg = lane / SL;
+  constexpr int ROUNDS = D / (DEC_WAVES * RPW);
+  f32x4 sv[ROUNDS];
+#pragma unroll
+  for (int rr = 0; rr < ROUNDS; ++rr)
+    sv[rr] = *reinterpret_cast<const f32x4*>(S + (size_t)((rr * DEC_WAVES + wave) * RPW + sg) * D + sp * 4);
+  FRows<T, D, DEC_THREADS> frows;
+  frows.load(F);
+  constexpr int QPT = (G * D + DEC_THREADS - 1) / DEC_THREADS;
+  float qreg[QPT];
+#pragma unroll
+  for (int u = 0; u < QPT; ++u) {
+    const int e = tid + u * DEC_THREADS;
+    qreg[u] = e < G * D ? to_f32(reinterpret_cast<const T*>(a.q)[((size_t)b * a.Hq + kv * G) * D + e]) : 0.f;
+  }
+  const T* kin = reinterpret_cast<const T*>(a.k) + (size_t)unit * D;
+  const T* vin = reinterpret_cast<const T*>(a.v) + (size_t)unit * D;
+  T kreg[(D + DEC_THREADS - 1) / DEC_THREADS], vreg[(D + DEC_THREADS - 1) / DEC_THREADS];
+#pragma unroll
+  for (int u = 0; u < (D + DEC_THREADS - 1) / DEC_THREADS; ++u) {
+    const int i = tid + u * DEC_THREADS;
+    kreg[u] = i < D ? kin[i] : T(0);
+    vreg[u] = i < D ? vin[i] : T(0);
+  }
+
   if (meta[0] != t || meta[2] != 0) {
     __syncthreads();
     if (tid == 0 && meta[2] == 0) meta[2] = -5;
@@ -394,10 +439,6 @@ void decode_kernel(DecodeArgs a) {
   const int sc_lo = t - W + 1 > 0 ? t - W + 1 : 0;  // score window
   const int part = lane % LPK, grp = lane / LPK;
 
-  // the pool positions first: the first key batch, issued before the
-  // NP-Map, needs their count
-  const int sp = lane % SL, sg = lane / SL;
-  constexpr int ROUNDS = D / (DEC_WAVES * RPW);
   {
     int cnt = 0;  // pool positions ascend: count those below lo
     for (int i = tid; i < n_pool; i += DEC_THREADS) cnt += pool_pos[i] < lo ? 1 : 0;
@@ -406,19 +447,24 @@ void decode_kernel(DecodeArgs a) {
   }
 
   // ---- 2. the new token enters the ring; phi(q_h), phi(k_t) ---------------
-  const T* kin = reinterpret_cast<const T*>(a.k) + (size_t)unit * D;
-  const T* vin = reinterpret_cast<const T*>(a.v) + (size_t)unit * D;
   const int slot_t = t % R;
-  for (int i = tid; i < D; i += DEC_THREADS) {
-    xs[G * D + i] = to_f32(kin[i]);
-    ring_k[(size_t)slot_t * D + i] = kin[i];
-    ring_v[(size_t)slot_t * D + i] = vin[i];
+#pragma unroll
+  for (int u = 0; u < (D + DEC_THREADS - 1) / DEC_THREADS; ++u) {
+    const int i = tid + u * DEC_THREADS;
+    if (i < D) {
+      xs[G * D + i] = to_f32(kreg[u]);
+      ring_k[(size_t)slot_t * D + i] = kreg[u];
+      ring_v[(size_t)slot_t * D + i] = vreg[u];
+    }
   }
   if (tid == 0) ring_flag[slot_t] = 0;
-  for (int e = tid; e < G * D; e += DEC_THREADS) {
-    const float x = to_f32(reinterpret_cast<const T*>(a.q)[((size_t)b * a.Hq + kv * G) * D + e]);
-    qs[e] = x;
-    xs[e] = x;
+#pragma unroll
+  for (int u = 0; u < QPT; ++u) {
+    const int e = tid + u * DEC_THREADS;
+    if (e < G * D) {
+      qs[e] = qreg[u];
+      xs[e] = qreg[u];
+    }
   }
   __syncthreads();
   int n_oob = 0;
@@ -429,7 +475,7 @@ void decode_kernel(DecodeArgs a) {
   const int r16 = lane & 15, g4 = lane >> 4;
   constexpr int DV = D / 64;  // value columns per lane
   // ring slots of consecutive positions: one modulo each, then a wrap
-  const int lo_slot = lo % R, la_slot = la_lo % R, sc_slot = sc_lo % R;
+  const int lo_slot = lo % R, la_slot = la_lo % R;
   auto wrap = [R](int s_) { return s_ >= R ? s_ - R : s_; };
   auto krow_sa = [&](int kk) -> uint32_t {  // byte offset of key row kk in the state blob
     return kk < n_oob ? (uint32_t)a.st_pool_k + (uint32_t)kk * (D * sizeof(T))
@@ -448,51 +494,6 @@ void decode_kernel(DecodeArgs a) {
     uint32_t vw[16];
   };
   TileRegs0 TA0;
-
-  np_map_vec<T, D, G + 1, DEC_THREADS>(F, xs, red8, us, ph, rowst);
-  for (int e = tid; e < G * D; e += DEC_THREADS) phq[e] = ph[e];
-  for (int i = tid; i < D; i += DEC_THREADS) ring_phi[(size_t)slot_t * D + i] = from_f32<T>(ph[G * D + i]);
-
-  float* redA = red;                                          // [waves][G][D]
-  float* redS = red + DEC_WAVES * G * D;                      // [waves][G][D]
-  float* mlw = reinterpret_cast<float*>(smem + LD::ml);       // [waves][G][2]
-  __syncthreads();  // phq complete; the NP-Map scratch (aliased by red) is free
-
-  // ---- 3a. state readout partials: sum_i phi_h[i] S[i][f] ----------------
-  {
-    f32x4 sv[ROUNDS];
-#pragma unroll
-    for (int rr = 0; rr < ROUNDS; ++rr)
-      sv[rr] = *reinterpret_cast<const f32x4*>(S + (size_t)((rr * DEC_WAVES + wave) * RPW + sg) * D + sp * 4);
-    float accS[G][4];
-#pragma unroll
-    for (int h = 0; h < G; ++h)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) accS[h][e] = 0.f;
-#pragma unroll
-    for (int rr = 0; rr < ROUNDS; ++rr) {
-      const int i = (rr * DEC_WAVES + wave) * RPW + sg;
-#pragma unroll
-      for (int h = 0; h < G; ++h) {
-        const float p = phq[h * D + i];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) accS[h][e] += p * sv[rr][e];
-      }
-    }
-#pragma unroll
-    for (int h = 0; h < G; ++h)
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-      {
-        if constexpr (SL <= 16) accS[h][e] += xorf<16>(accS[h][e]);
-        accS[h][e] += xorf<32>(accS[h][e]);
-      }
-    if (sg == 0)
-#pragma unroll
-      for (int h = 0; h < G; ++h)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) redS[(wave * G + h) * D + sp * 4 + e] = accS[h][e];
-  }
 
   // ---- 3b. the keys in 16-key tiles, one tile per wave at a time: logits by
   //         MFMA (keys as A rows against the heads' query columns), a running
@@ -550,7 +551,28 @@ void decode_kernel(DecodeArgs a) {
   };
   // one tile: weight(c, kk) turns a product into a log-weight
   auto tile = [&](const TileRegs& X, int kk0, int n, const Frag<T>* qb, const Frag<T>* qb2,
-                  auto weight) {
+                  auto weight, int sc_first) {
+    if (kk0 + 16 > sc_first) {  // wave-uniform: score-window keys in the tile
+      // float64 logits of the new token's score: the products of bf16/f32
+      // values are exact in float64; lane (r, g) sums its 8 columns per
+      // block, then the four g lanes of row r combine
+      const int kk = kk0 + r16;
+#pragma unroll 1
+      for (int h = 0; h < G; ++h) {  // one head at a time keeps few registers live
+        const float* qh = lds_opaque(qs) + h * D + 8 * g4;
+        double d = 0.0;
+#pragma unroll
+        for (int kb = 0; kb < D / 32; ++kb) {
+          const f32x4 q0 = *reinterpret_cast<const f32x4*>(qh + 32 * kb);
+          const f32x4 q1 = *reinterpret_cast<const f32x4*>(qh + 32 * kb + 4);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) d += (double)(e < 4 ? q0[e] : q1[e - 4]) * (double)frag_at(X.af[kb], e);
+        }
+        d += __shfl_xor(d, 16);
+        d += __shfl_xor(d, 32);
+        if (g4 == 0 && kk >= sc_first && kk < n) lg[h * W + kk - sc_first] = a.scale64 * d;
+      }
+    }
     f32x4 c = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kb = 0; kb < D / 32; ++kb) {
@@ -608,46 +630,70 @@ void decode_kernel(DecodeArgs a) {
   };
   // the tiles of wave w: w, w + waves, ...; two in flight
   auto run_tiles = [&](TileRegs& A, TileRegs& B, bool a_loaded, int n, auto krow, auto vrow,
-                       const Frag<T>* qb, const Frag<T>* qb2, auto weight) {
+                       const Frag<T>* qb, const Frag<T>* qb2, auto weight, int sc_first) {
     constexpr int STEP = 16 * DEC_WAVES;
     const int first = 16 * wave;
     if (!a_loaded) load_tile(A, first, n, krow, vrow);
     for (int kk0 = first; kk0 < n; kk0 += 2 * STEP) {  // wave-uniform
       if (kk0 + STEP < n) load_tile(B, kk0 + STEP, n, krow, vrow);
-      tile(A, kk0, n, qb, qb2, weight);
+      tile(A, kk0, n, qb, qb2, weight, sc_first);
       if (kk0 + STEP >= n) break;
       if (kk0 + 2 * STEP < n) load_tile(A, kk0 + 2 * STEP, n, krow, vrow);
-      tile(B, kk0 + STEP, n, qb, qb2, weight);
+      tile(B, kk0 + STEP, n, qb, qb2, weight, sc_first);
     }
   };
+  // the wave's first key tile is in flight during the NP-Map
+  load_tile(TA0, 16 * wave, n_sa, krow_sa, vrow_sa);
+
+  np_map_vec<T, D, G + 1, DEC_THREADS>(frows, xs, red8, us, ph, rowst);
+  for (int e = tid; e < G * D; e += DEC_THREADS) phq[e] = ph[e];
+  for (int i = tid; i < D; i += DEC_THREADS) ring_phi[(size_t)slot_t * D + i] = from_f32<T>(ph[G * D + i]);
+
+  float* redA = red;                                          // [waves][G][D]
+  float* redS = red + DEC_WAVES * G * D;                      // [waves][G][D]
+  float* mlw = reinterpret_cast<float*>(smem + LD::ml);       // [waves][G][2]
+  __syncthreads();  // phq complete; the NP-Map scratch (aliased by red) is free
+
+  // ---- 3a. state readout partials: sum_i phi_h[i] S[i][f] ----------------
+  {
+    float accS[G][4];
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) accS[h][e] = 0.f;
+#pragma unroll
+    for (int rr = 0; rr < ROUNDS; ++rr) {
+      const int i = (rr * DEC_WAVES + wave) * RPW + sg;
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const float p = phq[h * D + i];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) accS[h][e] += p * sv[rr][e];
+      }
+    }
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+      {
+        if constexpr (SL <= 16) accS[h][e] += xorf<16>(accS[h][e]);
+        accS[h][e] += xorf<32>(accS[h][e]);
+      }
+    if (sg == 0)
+#pragma unroll
+      for (int h = 0; h < G; ++h)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) redS[(wave * G + h) * D + sp * 4 + e] = accS[h][e];
+  }
+
   {
     Frag<T> qb[D / 32];
 #pragma unroll
     for (int kb = 0; kb < D / 32; ++kb) qb[kb] = qfrag(qs, kb, false);
     const float scale = a.scale;
-    run_tiles(TA, TB, false, n_sa, krow_sa, vrow_sa, qb, (const Frag<T>*)nullptr,
-              [&](float x, int) { return x * scale; });
-    // float64 window logits of the new token (its score): one (head, key)
-    // dot product per lane, from the window's ring rows (just read, so
-    // cached); products of bf16/f32 values are exact in float64
-    const int n_sc = t - sc_lo + 1;
-    constexpr int VE = 16 / sizeof(T);
-    for (int pidx = tid; pidx < G * n_sc; pidx += DEC_THREADS) {
-      const int h = pidx / n_sc, jj = pidx % n_sc;
-      const T* kr = ring_k + (size_t)wrap(sc_slot + jj) * D;
-      const float* qh = qs + h * D;
-      uint4 raw[D / VE];
-#pragma unroll
-      for (int c = 0; c < D / VE; ++c) raw[c] = *reinterpret_cast<const uint4*>(kr + c * VE);
-      double d64s = 0.0;
-#pragma unroll
-      for (int c = 0; c < D / VE; ++c) {
-        const T* ke = reinterpret_cast<const T*>(&raw[c]);
-#pragma unroll
-        for (int e = 0; e < VE; ++e) d64s += (double)qh[c * VE + e] * (double)to_f32(ke[e]);
-      }
-      lg[h * W + jj] = a.scale64 * d64s;
-    }
+    const int n_sc = t - sc_lo + 1;  // the score window: the last n_sc keys
+    run_tiles(TA, TB, true, n_sa, krow_sa, vrow_sa, qb, (const Frag<T>*)nullptr,
+              [&](float x, int) { return x * scale; }, n_sa - n_sc);
   }
   if (n_la > 0) {
     // phi(q) as T hi + lo parts (float32 data: exact in one part)
@@ -667,7 +713,8 @@ void decode_kernel(DecodeArgs a) {
       const bool la = ring_flag[wrap(la_slot + kk)] == 0;
       return (la && w > 0.f) ? lgate + __logf(w) : STILL_NEG_INF;
     };
-    run_tiles(TA, TB, false, n_la, krow, vrow, pb, sizeof(T) == 2 ? pb2 : (const Frag<T>*)nullptr, weight);
+    run_tiles(TA, TB, false, n_la, krow, vrow, pb, sizeof(T) == 2 ? pb2 : (const Frag<T>*)nullptr, weight,
+              INT_MAX);
   }
   // publish per wave: (m, l) per head from lanes r = h, the value slices
 #pragma unroll
