@@ -76,7 +76,9 @@ struct DecLds {
   static constexpr size_t red_bytes = (size_t)2 * DEC_WAVES * G * D * 4;
   static constexpr size_t uni_bytes = mapg_bytes > red_bytes ? mapg_bytes : red_bytes;
   static constexpr size_t lg = uni + uni_bytes;                    // f64 [G][W] (runtime W)
-  __host__ __device__ static size_t bytes(int W) { return lg + (size_t)G * W * 8; }
+  // then int [W + 256]: ring flags of the linear keys (at most R = W + 2C)
+  __host__ __device__ static size_t lfl(int W) { return lg + (size_t)G * W * 8; }
+  __host__ __device__ static size_t bytes(int W) { return lfl(W) + (size_t)(W + 256) * 4; }
 };
 
 // 8 bytes of a row as floats: rows are read as 8-byte vectors, so a row of
@@ -150,6 +152,13 @@ struct FRows {
     for (int it = 0; it < ITS; ++it) raw[it] = ld8(F + (size_t)((it * NW + wave) * KPW + grp) * D + part * VEC);
   }
 };
+
+// one element through a buffer resource (zero past its range)
+template <typename T>
+__device__ __forceinline__ T ld_elem_buf(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
+  if constexpr (sizeof(T) == 2) return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b16(r, voff, 0, 0));
+  else return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b32(r, voff, 0, 0));
+}
 
 // element e of the 8 consecutive columns a fragment holds, as float32
 __device__ __forceinline__ float frag_at(const Frag<bf16>& f, int e) { return (float)f.v[e]; }
@@ -353,8 +362,6 @@ void decode_kernel(DecodeArgs a) {
   constexpr int VEC = RowVec<T>::N;  // elements per 8-byte vector
   constexpr int LPK = D / VEC;       // lanes per K/V row
   constexpr int KPW = 64 / LPK;      // rows per wave and vector load
-  constexpr int SL = D / 4;          // lanes per S row (float4)
-  constexpr int RPW = 64 / SL;       // S rows per wave and vector load
   constexpr int U = 4;               // rows in flight per lane
   extern __shared__ __align__(16) char smem[];
   const int kv = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
@@ -388,48 +395,39 @@ void decode_kernel(DecodeArgs a) {
   float* red = reinterpret_cast<float*>(smem + LD::uni);  // [2][waves][G][D]
   double* lg = reinterpret_cast<double*>(smem + LD::lg);
 
-  // loads that depend on nothing else go first, so their latencies overlap:
-  // the S rows of this lane's readout share, the F rows of the NP-Map, the
-  // queries and the new key / value
-  const int sp = lane % SL, sg = lane / SL;
-  constexpr int ROUNDS = D / (DEC_WAVES * RPW);
-  f32x4 sv[ROUNDS];
+  // loads that depend on nothing else go first, so their latencies overlap,
+  // in the order they are needed (a wait for one is a wait for all issued
+  // before it): the position and pool count, the first pool positions, the
+  // queries and the new key / value, the F rows of the NP-Map, the S rows of
+  // this lane's readout share. Buffer loads return zero past their range,
+  // so none of them needs a branch.
+  const __amdgpu_buffer_rsrc_t st_r = make_rsrc(st, (uint32_t)a.st_unit);
+  const u32x4 mv = __builtin_amdgcn_raw_buffer_load_b128(st_r, 0, (uint32_t)a.st_meta, 0);
+  const u32x4 me = __builtin_amdgcn_raw_buffer_load_b128(st_r, 0, (uint32_t)a.st_meta + 16, 0);
+  constexpr int PPT = 2;  // pool positions per thread read ahead
+  int ppos[PPT];
 #pragma unroll
-  for (int rr = 0; rr < ROUNDS; ++rr)
-    sv[rr] = *reinterpret_cast<const f32x4*>(S + (size_t)((rr * DEC_WAVES + wave) * RPW + sg) * D + sp * 4);
-  FRows<T, D, DEC_THREADS> frows;
-  frows.load(F);
+  for (int u = 0; u < PPT; ++u)
+    ppos[u] = (int)__builtin_amdgcn_raw_buffer_load_b32(st_r, (uint32_t)(tid + u * DEC_THREADS) * 4,
+                                                          (uint32_t)a.st_pool_pos, 0);
+  const __amdgpu_buffer_rsrc_t q_r =
+      make_rsrc(reinterpret_cast<const T*>(a.q) + ((size_t)b * a.Hq + kv * G) * D, G * D * sizeof(T));
+  const __amdgpu_buffer_rsrc_t k_r = make_rsrc(reinterpret_cast<const T*>(a.k) + (size_t)unit * D, D * sizeof(T));
+  const __amdgpu_buffer_rsrc_t v_r = make_rsrc(reinterpret_cast<const T*>(a.v) + (size_t)unit * D, D * sizeof(T));
   constexpr int QPT = (G * D + DEC_THREADS - 1) / DEC_THREADS;
-  float qreg[QPT];
+  constexpr int KPT = (D + DEC_THREADS - 1) / DEC_THREADS;
+  T qraw[QPT], kreg[KPT], vreg[KPT];
 #pragma unroll
-  for (int u = 0; u < QPT; ++u) {
-    const int e = tid + u * DEC_THREADS;
-    qreg[u] = e < G * D ? to_f32(reinterpret_cast<const T*>(a.q)[((size_t)b * a.Hq + kv * G) * D + e]) : 0.f;
-  }
-  const T* kin = reinterpret_cast<const T*>(a.k) + (size_t)unit * D;
-  const T* vin = reinterpret_cast<const T*>(a.v) + (size_t)unit * D;
-  T kreg[(D + DEC_THREADS - 1) / DEC_THREADS], vreg[(D + DEC_THREADS - 1) / DEC_THREADS];
+  for (int u = 0; u < QPT; ++u) qraw[u] = ld_elem_buf<T>(q_r, (uint32_t)(tid + u * DEC_THREADS) * sizeof(T));
 #pragma unroll
-  for (int u = 0; u < (D + DEC_THREADS - 1) / DEC_THREADS; ++u) {
-    const int i = tid + u * DEC_THREADS;
-    kreg[u] = i < D ? kin[i] : T(0);
-    vreg[u] = i < D ? vin[i] : T(0);
+  for (int u = 0; u < KPT; ++u) {
+    kreg[u] = ld_elem_buf<T>(k_r, (uint32_t)(tid + u * DEC_THREADS) * sizeof(T));
+    vreg[u] = ld_elem_buf<T>(v_r, (uint32_t)(tid + u * DEC_THREADS) * sizeof(T));
   }
-
-  if (meta[0] != t || meta[2] != 0) {
-    __syncthreads();
-    if (tid == 0 && meta[2] == 0) meta[2] = -5;
-    return;
-  }
-  int n_pool = (int)meta[1];
-  const int c = t / C, cC = c * C;
-
-  if (a.sel_new && !a.boundary)
-    for (int i = tid; i < a.lam; i += DEC_THREADS) a.sel_new[(size_t)unit * a.lam + i] = -1;
-
   // key sets [P3 "Content-Aware Routing ..."]: kept tokens below lo, the ring
   // from lo to t (window and own chunk), ring tokens [la_lo, la_hi] that are
   // out of the window and unkept (linear), then S, z.
+  const int c = t / C, cC = c * C;
   int lo = t - W + 1 < cC ? t - W + 1 : cC;
   if (lo < 0) lo = 0;
   const int n_win = t - lo + 1;
@@ -437,11 +435,62 @@ void decode_kernel(DecodeArgs a) {
   const int la_hi = min(t - W, cC - 1);  // inclusive
   const int n_la = la_hi >= la_lo ? la_hi - la_lo + 1 : 0;
   const int sc_lo = t - W + 1 > 0 ? t - W + 1 : 0;  // score window
+  // ring slots of consecutive positions: one modulo each, then a wrap
+  const int lo_slot = lo % R, la_slot = la_lo % R;
+  auto wrap = [R](int s_) { return s_ >= R ? s_ - R : s_; };
+  // the gate of head r = lane % 16 (zero for r >= G) and this lane's
+  // entries l, l + 64, ... of z
+  const float g_lane = __builtin_bit_cast(
+      float, __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(a.gate + kv * G, G * 4), (lane & 15) * 4, 0, 0));
+  float zreg[D / 64];
+#pragma unroll
+  for (int u = 0; u < D / 64; ++u)
+    zreg[u] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(st_r, (lane + 64 * u) * 4,
+                                                                              (uint32_t)a.st_z, 0));
+  // the ring flags of the linear keys (n_la < R <= W + 256)
+  constexpr int FPT = 2;
+  int flg[FPT];
+#pragma unroll
+  for (int u = 0; u < FPT; ++u) {
+    const int i = tid + u * DEC_THREADS;
+    flg[u] = (int)__builtin_amdgcn_raw_buffer_load_b32(st_r, (uint32_t)((la_slot + i) % R) * 4,
+                                                         (uint32_t)a.st_ring_flag, 0);
+  }
+
+  // meta: position, pool count, error (int64 each)
+  const uint32_t pos_lo = __builtin_amdgcn_readfirstlane(mv[0]), pos_hi = __builtin_amdgcn_readfirstlane(mv[1]);
+  const uint32_t err_or = __builtin_amdgcn_readfirstlane(me[0] | me[1]);
+  if (pos_lo != (uint32_t)t || pos_hi != 0u || err_or != 0u) {
+    // the loads above are used on this path too, so the compiler keeps them
+    // ahead of the branch instead of moving them behind it (where they
+    // would wait for the meta data)
+#pragma unroll
+    for (int u = 0; u < PPT; ++u) asm volatile("" ::"v"(ppos[u]));
+#pragma unroll
+    for (int u = 0; u < QPT; ++u) asm volatile("" ::"v"(to_f32(qraw[u])));
+#pragma unroll
+    for (int u = 0; u < KPT; ++u) asm volatile("" ::"v"(to_f32(kreg[u])), "v"(to_f32(vreg[u])));
+#pragma unroll
+    for (int u = 0; u < FPT; ++u) asm volatile("" ::"v"(flg[u]));
+#pragma unroll
+    for (int u = 0; u < D / 64; ++u) asm volatile("" ::"v"(zreg[u]));
+    asm volatile("" ::"v"(g_lane));
+    __syncthreads();
+    if (tid == 0 && err_or == 0u) meta[2] = -5;
+    return;
+  }
+  int n_pool = (int)__builtin_amdgcn_readfirstlane(mv[2]);
+
+  if (a.sel_new && !a.boundary)
+    for (int i = tid; i < a.lam; i += DEC_THREADS) a.sel_new[(size_t)unit * a.lam + i] = -1;
+
   const int part = lane % LPK, grp = lane / LPK;
 
   {
     int cnt = 0;  // pool positions ascend: count those below lo
-    for (int i = tid; i < n_pool; i += DEC_THREADS) cnt += pool_pos[i] < lo ? 1 : 0;
+#pragma unroll
+    for (int u = 0; u < PPT; ++u) cnt += (tid + u * DEC_THREADS < n_pool && ppos[u] < lo) ? 1 : 0;
+    for (int i = tid + PPT * DEC_THREADS; i < n_pool; i += DEC_THREADS) cnt += pool_pos[i] < lo ? 1 : 0;
     cnt = (int)wave_sum((float)cnt);
     if (lane == 0) ibuf[1 + wave] = cnt;
   }
@@ -462,10 +511,14 @@ void decode_kernel(DecodeArgs a) {
   for (int u = 0; u < QPT; ++u) {
     const int e = tid + u * DEC_THREADS;
     if (e < G * D) {
-      qs[e] = qreg[u];
-      xs[e] = qreg[u];
+      qs[e] = to_f32(qraw[u]);
+      xs[e] = to_f32(qraw[u]);
     }
   }
+  int* lfl = reinterpret_cast<int*>(smem + LD::lfl(W));
+#pragma unroll
+  for (int u = 0; u < FPT; ++u)
+    if (tid + u * DEC_THREADS < n_la) lfl[tid + u * DEC_THREADS] = flg[u];
   __syncthreads();
   int n_oob = 0;
 #pragma unroll
@@ -474,16 +527,12 @@ void decode_kernel(DecodeArgs a) {
 
   const int r16 = lane & 15, g4 = lane >> 4;
   constexpr int DV = D / 64;  // value columns per lane
-  // ring slots of consecutive positions: one modulo each, then a wrap
-  const int lo_slot = lo % R, la_slot = la_lo % R;
-  auto wrap = [R](int s_) { return s_ >= R ? s_ - R : s_; };
   auto krow_sa = [&](int kk) -> uint32_t {  // byte offset of key row kk in the state blob
     return kk < n_oob ? (uint32_t)a.st_pool_k + (uint32_t)kk * (D * sizeof(T))
                       : (uint32_t)a.st_ring_k + (uint32_t)wrap(lo_slot + kk - n_oob) * (D * sizeof(T));
   };
   // value rows as byte offsets into this unit's state blob (one buffer
   // resource, the row offset a scalar)
-  const __amdgpu_buffer_rsrc_t st_r = make_rsrc(st, (uint32_t)a.st_unit);
   const uint32_t pv_off = (uint32_t)a.st_pool_v, rv_off = (uint32_t)a.st_ring_v;
   auto vrow_sa = [&](int kk) -> uint32_t {
     return kk < n_oob ? pv_off + (uint32_t)kk * (D * sizeof(T))
@@ -633,17 +682,57 @@ void decode_kernel(DecodeArgs a) {
                        const Frag<T>* qb, const Frag<T>* qb2, auto weight, int sc_first) {
     constexpr int STEP = 16 * DEC_WAVES;
     const int first = 16 * wave;
+    // loads are issued whether or not their tile exists (absent rows read
+    // zeros past the range): a load on one side of a branch only would make
+    // the next wait one for every load in flight
     if (!a_loaded) load_tile(A, first, n, krow, vrow);
     for (int kk0 = first; kk0 < n; kk0 += 2 * STEP) {  // wave-uniform
-      if (kk0 + STEP < n) load_tile(B, kk0 + STEP, n, krow, vrow);
+      load_tile(B, kk0 + STEP, n, krow, vrow);
       tile(A, kk0, n, qb, qb2, weight, sc_first);
       if (kk0 + STEP >= n) break;
-      if (kk0 + 2 * STEP < n) load_tile(A, kk0 + 2 * STEP, n, krow, vrow);
+      load_tile(A, kk0 + 2 * STEP, n, krow, vrow);
       tile(B, kk0 + STEP, n, qb, qb2, weight, sc_first);
     }
   };
-  // the wave's first key tile is in flight during the NP-Map
-  load_tile(TA0, 16 * wave, n_sa, krow_sa, vrow_sa);
+  // ---- 3b. softmax keys: logits q.k scaled; the float64 score-window
+  //         logits come from the same key fragments ---------------------
+  {
+    Frag<T> qb[D / 32];
+#pragma unroll
+    for (int kb = 0; kb < D / 32; ++kb) qb[kb] = qfrag(qs, kb, false);
+    const float scale = a.scale;
+    const int n_sc = t - sc_lo + 1;  // the score window: the last n_sc keys
+    run_tiles(TA, TB, false, n_sa, krow_sa, vrow_sa, qb, (const Frag<T>*)nullptr,
+              [&](float x, int) { return x * scale; }, n_sa - n_sc);
+  }
+
+  // ---- 3c. NP-Map phi(q_h), phi(k_t), with the wave's state rows and its
+  //         first linear-key tile in flight ------------------------------
+  auto krow_la = [&](int kk) -> uint32_t {
+    return (uint32_t)a.st_ring_phi + (uint32_t)wrap(la_slot + kk) * (D * sizeof(T));
+  };
+  auto vrow_la = [&](int kk) -> uint32_t { return rv_off + (uint32_t)wrap(la_slot + kk) * (D * sizeof(T)); };
+  FRows<T, D, DEC_THREADS> frows;
+  frows.load(F);
+  // state rows 16 j .. 16 j + 15 for j = wave, wave + waves, ...: lane l
+  // holds columns l * DV .. + DV of each
+  constexpr int SJ = D / (16 * DEC_WAVES);
+  using SRow = typename std::conditional<DV == 2, uint2, uint32_t>::type;
+  SRow srow[SJ][16];
+#pragma unroll
+  for (int j = 0; j < SJ; ++j)
+#pragma unroll
+    for (int jj = 0; jj < 16; ++jj) {
+      const uint32_t soff = (uint32_t)a.st_S + (uint32_t)((16 * (j * DEC_WAVES + wave) + jj) * D * 4);
+      if constexpr (DV == 2) {
+        const auto x = __builtin_amdgcn_raw_buffer_load_b64(st_r, lane * 8, soff, 0);
+        srow[j][jj] = uint2{x[0], x[1]};
+      } else {
+        srow[j][jj] = __builtin_amdgcn_raw_buffer_load_b32(st_r, lane * 4, soff, 0);
+      }
+    }
+  constexpr bool LA_EARLY = G <= 4;  // with 8 heads the registers do not hold it
+  if (LA_EARLY) load_tile(TA, 16 * wave, n_la, krow_la, vrow_la);
 
   np_map_vec<T, D, G + 1, DEC_THREADS>(frows, xs, red8, us, ph, rowst);
   for (int e = tid; e < G * D; e += DEC_THREADS) phq[e] = ph[e];
@@ -654,47 +743,34 @@ void decode_kernel(DecodeArgs a) {
   float* mlw = reinterpret_cast<float*>(smem + LD::ml);       // [waves][G][2]
   __syncthreads();  // phq complete; the NP-Map scratch (aliased by red) is free
 
-  // ---- 3a. state readout partials: sum_i phi_h[i] S[i][f] ----------------
+  // ---- 3d. state readout partials: sum_i phi_h[i] S[i][f] over the wave's
+  //         rows -----------------------------------------------------------
   {
-    float accS[G][4];
+    float accS[G][DV];
 #pragma unroll
     for (int h = 0; h < G; ++h)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) accS[h][e] = 0.f;
+      for (int e = 0; e < DV; ++e) accS[h][e] = 0.f;
 #pragma unroll
-    for (int rr = 0; rr < ROUNDS; ++rr) {
-      const int i = (rr * DEC_WAVES + wave) * RPW + sg;
+    for (int j = 0; j < SJ; ++j)
 #pragma unroll
-      for (int h = 0; h < G; ++h) {
-        const float p = phq[h * D + i];
+      for (int jj = 0; jj < 16; ++jj) {
+        const int i = 16 * (j * DEC_WAVES + wave) + jj;
+        const float* sr = reinterpret_cast<const float*>(&srow[j][jj]);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) accS[h][e] += p * sv[rr][e];
+        for (int h = 0; h < G; ++h) {
+          const float p = phq[h * D + i];
+#pragma unroll
+          for (int e = 0; e < DV; ++e) accS[h][e] += p * sr[e];
+        }
       }
-    }
 #pragma unroll
     for (int h = 0; h < G; ++h)
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-      {
-        if constexpr (SL <= 16) accS[h][e] += xorf<16>(accS[h][e]);
-        accS[h][e] += xorf<32>(accS[h][e]);
-      }
-    if (sg == 0)
-#pragma unroll
-      for (int h = 0; h < G; ++h)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) redS[(wave * G + h) * D + sp * 4 + e] = accS[h][e];
+      for (int e = 0; e < DV; ++e) redS[(wave * G + h) * D + lane * DV + e] = accS[h][e];
   }
 
-  {
-    Frag<T> qb[D / 32];
-#pragma unroll
-    for (int kb = 0; kb < D / 32; ++kb) qb[kb] = qfrag(qs, kb, false);
-    const float scale = a.scale;
-    const int n_sc = t - sc_lo + 1;  // the score window: the last n_sc keys
-    run_tiles(TA, TB, true, n_sa, krow_sa, vrow_sa, qb, (const Frag<T>*)nullptr,
-              [&](float x, int) { return x * scale; }, n_sa - n_sc);
-  }
+  // ---- 3e. linear keys: log-weight log(g) + log <phi(q), phi(k)> --------
   if (n_la > 0) {
     // phi(q) as T hi + lo parts (float32 data: exact in one part)
     Frag<T> pb[D / 32], pb2[D / 32];
@@ -703,17 +779,13 @@ void decode_kernel(DecodeArgs a) {
       pb[kb] = qfrag(phq, kb, false);
       pb2[kb] = qfrag(phq, kb, true);
     }
-    const float g_r = r16 < G ? a.gate[kv * G + r16] : 0.f;
+    const float g_r = g_lane;  // zero for r >= G
     const float lgate = g_r > 0.f ? __logf(g_r) : STILL_NEG_INF;
-    auto krow = [&](int kk) -> uint32_t {
-      return (uint32_t)a.st_ring_phi + (uint32_t)wrap(la_slot + kk) * (D * sizeof(T));
-    };
-    auto vrow = [&](int kk) -> uint32_t { return rv_off + (uint32_t)wrap(la_slot + kk) * (D * sizeof(T)); };
     auto weight = [&](float w, int kk) {
-      const bool la = ring_flag[wrap(la_slot + kk)] == 0;
+      const bool la = lfl[kk] == 0;
       return (la && w > 0.f) ? lgate + __logf(w) : STILL_NEG_INF;
     };
-    run_tiles(TA, TB, false, n_la, krow, vrow, pb, sizeof(T) == 2 ? pb2 : (const Frag<T>*)nullptr, weight,
+    run_tiles(TA, TB, LA_EARLY, n_la, krow_la, vrow_la, pb, sizeof(T) == 2 ? pb2 : (const Frag<T>*)nullptr, weight,
               INT_MAX);
   }
   // publish per wave: (m, l) per head from lanes r = h, the value slices
@@ -762,9 +834,10 @@ void decode_kernel(DecodeArgs a) {
     // the state as a virtual key: log-weight log(g * phi(q).z), value
     // S^T phi(q) / phi(q).z; one normaliser over the waves' partials
     float dz = 0.f;
-    for (int i = lane; i < D; i += 64) dz += phq[h * D + i] * z[i];
+#pragma unroll
+    for (int u = 0; u < D / 64; ++u) dz += phq[h * D + lane + 64 * u] * zreg[u];
     dz = wave_sum(dz);
-    const float g = a.gate[kv * G + h];
+    const float g = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, g_lane), h));
     const float lws = (g > 0.f && dz > 0.f) ? __logf(g * dz) : STILL_NEG_INF;
     float mx = lws;
 #pragma unroll
