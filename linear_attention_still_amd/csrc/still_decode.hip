@@ -398,9 +398,9 @@ void decode_kernel(DecodeArgs a) {
   // loads that depend on nothing else go first, so their latencies overlap,
   // in the order they are needed (a wait for one is a wait for all issued
   // before it): the position and pool count, the first pool positions, the
-  // queries and the new key / value, the F rows of the NP-Map, the S rows of
-  // this lane's readout share. Buffer loads return zero past their range,
-  // so none of them needs a branch.
+  // queries and the new key / value, the gate, z and the ring flags of the
+  // linear keys. Buffer loads return zero past their range, so none of them
+  // needs a branch.
   const __amdgpu_buffer_rsrc_t st_r = make_rsrc(st, (uint32_t)a.st_unit);
   const u32x4 mv = __builtin_amdgcn_raw_buffer_load_b128(st_r, 0, (uint32_t)a.st_meta, 0);
   const u32x4 me = __builtin_amdgcn_raw_buffer_load_b128(st_r, 0, (uint32_t)a.st_meta + 16, 0);
@@ -694,28 +694,12 @@ void decode_kernel(DecodeArgs a) {
       tile(B, kk0 + STEP, n, qb, qb2, weight, sc_first);
     }
   };
-  // ---- 3b. softmax keys: logits q.k scaled; the float64 score-window
-  //         logits come from the same key fragments ---------------------
-  {
-    Frag<T> qb[D / 32];
-#pragma unroll
-    for (int kb = 0; kb < D / 32; ++kb) qb[kb] = qfrag(qs, kb, false);
-    const float scale = a.scale;
-    const int n_sc = t - sc_lo + 1;  // the score window: the last n_sc keys
-    run_tiles(TA, TB, false, n_sa, krow_sa, vrow_sa, qb, (const Frag<T>*)nullptr,
-              [&](float x, int) { return x * scale; }, n_sa - n_sc);
-  }
-
-  // ---- 3c. NP-Map phi(q_h), phi(k_t), with the wave's state rows and its
-  //         first linear-key tile in flight ------------------------------
-  auto krow_la = [&](int kk) -> uint32_t {
-    return (uint32_t)a.st_ring_phi + (uint32_t)wrap(la_slot + kk) * (D * sizeof(T));
-  };
-  auto vrow_la = [&](int kk) -> uint32_t { return rv_off + (uint32_t)wrap(la_slot + kk) * (D * sizeof(T)); };
-  FRows<T, D, DEC_THREADS> frows;
-  frows.load(F);
+  // ---- 3b. NP-Map phi(q_h), phi(k_t) (F read at the start), with the
+  //         wave's state rows and its first softmax-key tile in flight ----
   // state rows 16 j .. 16 j + 15 for j = wave, wave + waves, ...: lane l
   // holds columns l * DV .. + DV of each
+  FRows<T, D, DEC_THREADS> frows;
+  frows.load(F);
   constexpr int SJ = D / (16 * DEC_WAVES);
   using SRow = typename std::conditional<DV == 2, uint2, uint32_t>::type;
   SRow srow[SJ][16];
@@ -731,8 +715,7 @@ void decode_kernel(DecodeArgs a) {
         srow[j][jj] = __builtin_amdgcn_raw_buffer_load_b32(st_r, lane * 4, soff, 0);
       }
     }
-  constexpr bool LA_EARLY = G <= 4;  // with 8 heads the registers do not hold it
-  if (LA_EARLY) load_tile(TA, 16 * wave, n_la, krow_la, vrow_la);
+  load_tile(TA, 16 * wave, n_sa, krow_sa, vrow_sa);
 
   np_map_vec<T, D, G + 1, DEC_THREADS>(frows, xs, red8, us, ph, rowst);
   for (int e = tid; e < G * D; e += DEC_THREADS) phq[e] = ph[e];
@@ -743,7 +726,7 @@ void decode_kernel(DecodeArgs a) {
   float* mlw = reinterpret_cast<float*>(smem + LD::ml);       // [waves][G][2]
   __syncthreads();  // phq complete; the NP-Map scratch (aliased by red) is free
 
-  // ---- 3d. state readout partials: sum_i phi_h[i] S[i][f] over the wave's
+  // ---- 3c. state readout partials: sum_i phi_h[i] S[i][f] over the wave's
   //         rows -----------------------------------------------------------
   {
     float accS[G][DV];
@@ -770,8 +753,24 @@ void decode_kernel(DecodeArgs a) {
       for (int e = 0; e < DV; ++e) redS[(wave * G + h) * D + lane * DV + e] = accS[h][e];
   }
 
+  // ---- 3d. softmax keys: logits q.k scaled; the float64 score-window
+  //         logits come from the same key fragments ---------------------
+  {
+    Frag<T> qb[D / 32];
+#pragma unroll
+    for (int kb = 0; kb < D / 32; ++kb) qb[kb] = qfrag(qs, kb, false);
+    const float scale = a.scale;
+    const int n_sc = t - sc_lo + 1;  // the score window: the last n_sc keys
+    run_tiles(TA, TB, true, n_sa, krow_sa, vrow_sa, qb, (const Frag<T>*)nullptr,
+              [&](float x, int) { return x * scale; }, n_sa - n_sc);
+  }
+
   // ---- 3e. linear keys: log-weight log(g) + log <phi(q), phi(k)> --------
   if (n_la > 0) {
+    auto krow_la = [&](int kk) -> uint32_t {
+      return (uint32_t)a.st_ring_phi + (uint32_t)wrap(la_slot + kk) * (D * sizeof(T));
+    };
+    auto vrow_la = [&](int kk) -> uint32_t { return rv_off + (uint32_t)wrap(la_slot + kk) * (D * sizeof(T)); };
     // phi(q) as T hi + lo parts (float32 data: exact in one part)
     Frag<T> pb[D / 32], pb2[D / 32];
 #pragma unroll
@@ -785,7 +784,7 @@ void decode_kernel(DecodeArgs a) {
       const bool la = lfl[kk] == 0;
       return (la && w > 0.f) ? lgate + __logf(w) : STILL_NEG_INF;
     };
-    run_tiles(TA, TB, LA_EARLY, n_la, krow_la, vrow_la, pb, sizeof(T) == 2 ? pb2 : (const Frag<T>*)nullptr, weight,
+    run_tiles(TA, TB, false, n_la, krow_la, vrow_la, pb, sizeof(T) == 2 ? pb2 : (const Frag<T>*)nullptr, weight,
               INT_MAX);
   }
   // publish per wave: (m, l) per head from lanes r = h, the value slices
