@@ -88,7 +88,7 @@ void layout(const Derived& d, still_state_layout* s) {
 
 // Prefill launch geometry.
 struct Plan {
-  int L, T, n_dec, n_pend, K, NS, Gs, nHG, TPW;
+  int L, T, n_dec, n_pend, K, NS, Gs, nHG, HPW;
   int64_t ws_ft, ws_score, ws_delta, ws_flag, ws_dS, ws_total;
 };
 
@@ -98,15 +98,29 @@ Plan plan(const Derived& d, int64_t L) {
   pl.T = (int)((L + d.C - 1) / d.C);
   pl.n_dec = (int)((L - 1) / d.C);
   pl.n_pend = (int)(L - (int64_t)pl.n_dec * d.C);
-  int gs = 128 / d.C;  // at most 8 row tiles of 16 queries per workgroup
-  if (gs < 1) gs = 1;
-  if (gs > d.G) gs = d.G;
-  pl.Gs = gs;
-  pl.nHG = d.G / gs;
-  pl.TPW = 1;
-  // chunks walked per workgroup: enough workgroups to fill the chip
+  // 8 waves per attend workgroup, each one 16-query tile of HPW heads: two
+  // heads per wave where that fills the 8 waves (the heads share every
+  // key / value read and the workgroup's per-block work), else one
+  const int n_qt = d.C / 16;
+  int gs2 = 256 / d.C;
+  if (gs2 > d.G) gs2 = d.G;
+  bool two = gs2 >= 2 && (gs2 / 2) * n_qt == 8;
+  if (const char* e = getenv("STILL_HEADS_PER_WAVE")) two = two && atoi(e) != 1;
+  if (two) {
+    pl.HPW = 2;
+    pl.Gs = gs2;
+  } else {
+    int gs = 128 / d.C;  // at most 8 row tiles of 16 queries per workgroup
+    if (gs < 1) gs = 1;
+    if (gs > d.G) gs = d.G;
+    pl.HPW = 1;
+    pl.Gs = gs;
+  }
+  pl.nHG = d.G / pl.Gs;
+  // chunks walked per workgroup: enough workgroups to fill the chip (about
+  // four chunks each measured best at 16K, with one or two heads per wave)
   const int64_t units = (int64_t)d.B * d.Hkv * pl.nHG;
-  int K = (int)((int64_t)pl.T * units / 1024);
+  int K = (int)((int64_t)pl.T * units * pl.HPW / 1024);
   if (K < 1) K = 1;
   if (K > 8) K = 8;
   if (const char* e = getenv("STILL_CHUNKS_PER_WG")) {
@@ -138,7 +152,10 @@ template <typename T, int D>
 void set_lds_attr() {
   static bool done = false;
   if (done) return;
-  (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&still::attend_kernel<T, D>),
+  (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&still::attend_kernel<T, D, 1>),
+                      hipFuncAttributeMaxDynamicSharedMemorySize,
+                      (int)still::Blk<T, D>::bytes);
+  (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&still::attend_kernel<T, D, 2>),
                       hipFuncAttributeMaxDynamicSharedMemorySize,
                       (int)still::Blk<T, D>::bytes);
   (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&still::state_delta_kernel<T, D>),
@@ -184,7 +201,10 @@ int launch_prefill(const Derived& d, const Plan& pl, still::PrefillArgs a, hipSt
       a.dS, pl.NS, D * D + D);
   mk.at(4, 1);
   mk.at(5, 0);
-  attend_kernel<T, D><<<dim3(pl.NS * d.Hkv * pl.nHG * d.B), dim3(512), Blk<T, D>::bytes, s>>>(a);
+  if (pl.HPW == 2)
+    attend_kernel<T, D, 2><<<dim3(pl.NS * d.Hkv * pl.nHG * d.B), dim3(512), Blk<T, D>::bytes, s>>>(a);
+  else
+    attend_kernel<T, D, 1><<<dim3(pl.NS * d.Hkv * pl.nHG * d.B), dim3(512), Blk<T, D>::bytes, s>>>(a);
   mk.at(5, 1);
   const int ring_lo = pl.L - d.R > 0 ? pl.L - d.R : 0;
   const int n_ring_grp = (pl.L - ring_lo + 15) / 16;

@@ -86,7 +86,22 @@ __device__ __forceinline__ Frag<float> ld_frag(const float* p) {
 // LDS instruction; without this, offsets from a known base above 64 KiB each
 // take an address register of their own, which the compiler hoists out of
 // loops.
+// threadIdx.x through an empty asm: values derived from it are recomputed
+// where they are used instead of being hoisted out of loops and kept live
+__device__ __forceinline__ int opaque_tid() {
+  int x = threadIdx.x;
+  asm volatile("" : "+v"(x));
+  return x;
+}
 typedef __attribute__((address_space(3))) char lds_char;
+// The same through a VGPR, for code the compiler may place under divergent
+// control flow.
+template <typename X>
+__device__ __forceinline__ X* lds_opaque_v(X* p) {
+  unsigned a = (unsigned)(__UINTPTR_TYPE__)(lds_char*)(char*)p;
+  asm volatile("" : "+v"(a));
+  return (X*)(char*)(lds_char*)(__UINTPTR_TYPE__)a;
+}
 template <typename X>
 __device__ __forceinline__ X* lds_opaque(X* p) {
   unsigned a = (unsigned)(__UINTPTR_TYPE__)(lds_char*)(char*)p;

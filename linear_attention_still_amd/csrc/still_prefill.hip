@@ -464,7 +464,7 @@ struct BlkPtr {
   }
   // half h (0: d_k rows 32bb + 4g + i, 1: rows 32bb + 16 + 4g + i) of pair p
   __device__ float* pair(int p, int h) const {
-    return SP + ((size_t)(2 * p + h) * 64 + (threadIdx.x & 63)) * 4;
+    return SP + ((size_t)(2 * p + h) * 64 + (opaque_tid() & 63)) * 4;
   }
   __device__ H* wf(int kt, int bb) const { return WF + ((size_t)(kt * (D / 32) + bb) * 64) * 8; }
   // Fragment of V^T for d_v tile dt and key half kb2: lane (r, g) holds
@@ -472,7 +472,7 @@ struct BlkPtr {
   // B operand of the fold).
   __device__ Frag<H> ld_v(int dt, int kb2) const {
     using B_ = Blk<T, D>;
-    const int lane = threadIdx.x & 63, r16 = lane & 15, g4 = lane >> 4;
+    const int lane = opaque_tid() & 63, r16 = lane & 15, g4 = lane >> 4;
     if constexpr (B_::TR) {
       const H* p = VTs + (32 * kb2 + 4 * g4 + (r16 >> 2)) * B_::VR + 16 * dt + 4 * (r16 & 3);
       return tr_frag(p, 16 * B_::VR);
@@ -483,7 +483,7 @@ struct BlkPtr {
   // A fragment of phi(K) (rows = keys 16 kt + r, depth = features 32 bb + perm(g, s)).
   __device__ Frag<H> ld_wk(int kt, int bb) const {
     using B_ = Blk<T, D>;
-    const int lane = threadIdx.x & 63, r16 = lane & 15, g4 = lane >> 4;
+    const int lane = opaque_tid() & 63, r16 = lane & 15, g4 = lane >> 4;
     if constexpr (B_::TR) {
       const H* p = WF + (32 * bb + 4 * g4 + (r16 >> 2)) * B_::FKS + 16 * kt + 4 * (r16 & 3);
       return tr_frag(p, 16 * B_::FKS);
@@ -493,7 +493,7 @@ struct BlkPtr {
   }
   // fragment (feature tile ft, d block kb) of F^T: B operand of X F
   __device__ const T* ft(int ftile, int kb) const {
-    return FT + ((size_t)(ftile * (D / 32) + kb) * 64 + (threadIdx.x & 63)) * 8;
+    return FT + ((size_t)(ftile * (D / 32) + kb) * 64 + (opaque_tid() & 63)) * 8;
   }
 };
 
@@ -501,7 +501,7 @@ struct BlkPtr {
 template <typename T, int D, int NT>
 __device__ __forceinline__ void load_ft(const BlkPtr<T, D>& P, const T* ftg) {
   constexpr int N16 = D * D * (int)sizeof(T) / 16;
-  for (int e = threadIdx.x; e < N16; e += NT)
+  for (int e = opaque_tid(); e < N16; e += NT)
     reinterpret_cast<uint4*>(P.FT)[e] = reinterpret_cast<const uint4*>(ftg)[e];
 }
 
@@ -523,23 +523,40 @@ struct BlkRegs {
   int sel;  // threads < 64: kept flag of key tid
 };
 
+// Where the positions of a block's keys come from: a range [lo, hi), a
+// list in LDS or a list in global memory (entries from `first`).
+struct BlkSrc {
+  int mode;  // 0 range, 1 LDS list, 2 global list
+  int lo, hi;
+  const int32_t* lds;             // mode 1
+  __amdgpu_buffer_rsrc_t glist;   // mode 2
+  int first, n;                   // list entries first .. first + n
+};
+__device__ __forceinline__ BlkSrc blk_range(int lo, int hi) {
+  BlkSrc s{};
+  s.mode = 0; s.lo = lo; s.hi = hi;
+  return s;
+}
+
 template <typename T, int D, int NT>
 __device__ __forceinline__ void issue_block(BlkRegs<T, D, NT>& R, __amdgpu_buffer_rsrc_t kr,
                                             __amdgpu_buffer_rsrc_t vr, uint32_t kv_bytes,
-                                            const uint8_t* sf, const int32_t* gather,
-                                            int n_gather, int range_lo, int range_hi) {
+                                            __amdgpu_buffer_rsrc_t sfr, const BlkSrc& src) {
   using BR = BlkRegs<T, D, NT>;
   constexpr int VEC = BR::VEC, CPR = BR::CPR;
   // lane-dependent addresses are recomputed here rather than kept live
   // across the caller's loop (they would be hoisted out of it and spilled)
   int tid = threadIdx.x;
   asm volatile("" : "+v"(tid));
-  auto pos_of = [&](int kk) {
-    if (gather) return kk < n_gather ? gather[kk] : -1;
-    return range_lo + kk < range_hi ? range_lo + kk : -1;
+  auto pos_of = [&](int kk) -> int {
+    if (src.mode == 0) return src.lo + kk < src.hi ? src.lo + kk : -1;
+    if (kk >= src.n) return -1;
+    if (src.mode == 1)
+      return ((const __attribute__((address_space(3))) int32_t*)(lds_char*)(char*)src.lds)[src.first + kk];
+    return (int)__builtin_amdgcn_raw_buffer_load_b32(src.glist, (uint32_t)(src.first + kk) * 4, 0, 0);
   };
   auto row_off = [&](int j) { return j >= 0 ? (uint32_t)j * (uint32_t)(D * sizeof(T)) : kv_bytes; };
-  // all row positions first (gather lists are read before any row load is
+  // all row positions first (list entries are read before any row load is
   // issued, so waiting for them does not wait for the row loads)
   uint32_t koff[BR::KIT], voff[BR::VIT][2];
 #pragma unroll
@@ -555,10 +572,11 @@ __device__ __forceinline__ void issue_block(BlkRegs<T, D, NT>& R, __amdgpu_buffe
       voff[it][i] = idx < 32 * CPR ? row_off(pos_of(2 * (idx / CPR) + i)) + (idx % CPR) * VEC * sizeof(T)
                                    : kv_bytes;
   }
-  if (tid < 64) {
-    R.pos = pos_of(tid);
-    R.sel = R.pos >= 0 ? (gather ? 1 : (int)sf[R.pos]) : 0;
-  }
+  // threads < 64: position and kept flag of key tid (the flag byte is read
+  // by every thread, past the range where there is no key: no branch)
+  R.pos = pos_of(tid & 63);
+  const int flag = (int)__builtin_amdgcn_raw_buffer_load_b8(sfr, R.pos >= 0 ? (uint32_t)R.pos : 0xffffffffu, 0, 0);
+  R.sel = src.mode == 0 ? flag : (R.pos >= 0 ? 1 : 0);
 #pragma unroll
   for (int it = 0; it < BR::KIT; ++it) R.k[it] = ld_u4_buf(kr, koff[it], 0);
   if constexpr (BR::TR) {
@@ -645,7 +663,7 @@ __device__ __forceinline__ void commit_block(const BlkPtr<T, D>& P, const BlkReg
 // accumulator layout of (X F)^T: out[ft][i] = phi(x_r)[16 ft + 4g + i].
 template <typename T, int D>
 __device__ __forceinline__ void np_map_tile(const BlkPtr<T, D>& P, const Frag<T>* xf, f32x4* out) {
-  const int lane = threadIdx.x & 63, r16 = lane & 15, g4 = lane >> 4;
+  const int lane = opaque_tid() & 63, r16 = lane & 15, g4 = lane >> 4;
   float xn2 = 0.f;
 #pragma unroll
   for (int kb = 0; kb < D / 32; ++kb) xn2 += frag_sumsq(xf[kb]);
@@ -676,6 +694,54 @@ __device__ __forceinline__ void np_map_tile(const BlkPtr<T, D>& P, const Frag<T>
   for (int ft = 0; ft < D / 16; ++ft) out[ft] *= f;
 }
 
+// np_map_tile for NX tiles at once: each F^T fragment read from LDS serves
+// every tile.
+template <typename T, int D, int NX>
+__device__ __forceinline__ void np_map_tiles(const BlkPtr<T, D>& P, const Frag<T> (&xf)[NX][D / 32],
+                                             f32x4 (&out)[NX][D / 16]) {
+  float xn2[NX], mx[NX], ss[NX];
+#pragma unroll
+  for (int x = 0; x < NX; ++x) {
+    xn2[x] = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < D / 32; ++kb) xn2[x] += frag_sumsq(xf[x][kb]);
+    xn2[x] = sum_over_g(xn2[x]);
+    mx[x] = STILL_NEG_INF;
+    ss[x] = 0.f;
+  }
+#pragma unroll
+  for (int ft = 0; ft < D / 16; ++ft) {
+#pragma unroll
+    for (int x = 0; x < NX; ++x) out[x][ft] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < D / 32; ++kb) {
+      const Frag<T> f = ld_frag(P.ft(ft, kb));
+#pragma unroll
+      for (int x = 0; x < NX; ++x) mma(out[x][ft], f, xf[x][kb]);
+    }
+#pragma unroll
+    for (int x = 0; x < NX; ++x)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) mx[x] = fmaxf(mx[x], out[x][ft][i]);
+  }
+#pragma unroll
+  for (int x = 0; x < NX; ++x) {
+    mx[x] = max_over_g(mx[x]);
+#pragma unroll
+    for (int ft = 0; ft < D / 16; ++ft)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float e = exp_acc<T>(out[x][ft][i] - mx[x]);
+        out[x][ft][i] = e;
+        ss[x] += e * e;
+      }
+    ss[x] = sum_over_g(ss[x]);
+    const float f = sqrtf(xn2[x]) / sqrtf(ss[x]);
+#pragma unroll
+    for (int ft = 0; ft < D / 16; ++ft) out[x][ft] *= f;
+  }
+}
+
 // Max / sum over the 16 lanes sharing g (the 16 columns of a C tile).
 __device__ __forceinline__ float max_over_r(float x) {
   x = row_max<16>(x);
@@ -699,7 +765,7 @@ __device__ __forceinline__ void block_phi(const BlkPtr<T, D>& P, f32x4 (&ph)[4],
                                           bool want_w) {
   using B_ = Blk<T, D>;
   typedef typename HalfOf<T>::type H;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, r16 = lane & 15, g4 = lane >> 4;
+  const int tid = opaque_tid(), wave = tid >> 6, lane = tid & 63, r16 = lane & 15, g4 = lane >> 4;
   const bool mine = wave < B_::NFT;  // wave-uniform
   if (mine) {
     Frag<T> fb[D / 32];
@@ -769,7 +835,7 @@ __device__ __forceinline__ void fold_tile(const BlkPtr<T, D>& P, const f32x4 (&p
                                           int kb_hi, f32x4 (&acc)[D / 16]) {
   using B_ = Blk<T, D>;
   typedef typename HalfOf<T>::type H;
-  const int lane = threadIdx.x & 63, r16 = lane & 15, g4 = lane >> 4;
+  const int lane = opaque_tid() & 63, r16 = lane & 15, g4 = lane >> 4;
 #pragma unroll
   for (int kb2 = 0; kb2 < 2; ++kb2) {
     if (kb2 < kb_lo || kb2 >= kb_hi) continue;
@@ -793,7 +859,7 @@ __device__ __forceinline__ void fold_tile(const BlkPtr<T, D>& P, const f32x4 (&p
 // The block's contribution to z for feature 16w + r (lanes with g == 0).
 template <typename T, int D>
 __device__ __forceinline__ float fold_zsum(const BlkPtr<T, D>& P, const f32x4 (&ph)[4]) {
-  const int lane = threadIdx.x & 63, g4 = lane >> 4;
+  const int lane = opaque_tid() & 63, g4 = lane >> 4;
   float z = 0.f;
 #pragma unroll
   for (int kt = 0; kt < 4; ++kt)
@@ -807,7 +873,7 @@ __device__ __forceinline__ float fold_zsum(const BlkPtr<T, D>& P, const f32x4 (&
 template <typename T, int D>
 __device__ __forceinline__ void block_fold(const BlkPtr<T, D>& P, const f32x4 (&ph)[4]) {
   using B_ = Blk<T, D>;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, r16 = lane & 15, g4 = lane >> 4;
+  const int wave = opaque_tid() >> 6, lane = opaque_tid() & 63, r16 = lane & 15, g4 = lane >> 4;
   if (wave >= B_::NFT) return;
   f32x4 acc[D / 16];
 #pragma unroll
@@ -827,15 +893,15 @@ __device__ __forceinline__ void block_fold(const BlkPtr<T, D>& P, const f32x4 (&
 // exported state is row-major S[d_k][d_v].
 template <typename T, int D>
 __device__ __forceinline__ void load_state(const BlkPtr<T, D>& P, const float* Sfl) {
-  for (int e = threadIdx.x * 4; e < D * D; e += 512 * 4)
+  for (int e = opaque_tid() * 4; e < D * D; e += 512 * 4)
     *reinterpret_cast<f32x4*>(P.SP + e) = *reinterpret_cast<const f32x4*>(Sfl + e);
 }
 
 template <typename T, int D>
 __device__ __forceinline__ void store_state_rowmajor(const BlkPtr<T, D>& P, float* S) {
   using B_ = Blk<T, D>;
-  const int r16 = threadIdx.x & 15;
-  for (int e = threadIdx.x; e < B_::NPAIR * 64; e += 512) {
+  const int r16 = opaque_tid() & 15;
+  for (int e = opaque_tid(); e < B_::NPAIR * 64; e += 512) {
     const int p = e >> 6, ln = e & 63, g4 = ln >> 4;
     const int vt = p / (D / 32), bb = p % (D / 32);
 #pragma unroll
@@ -867,7 +933,7 @@ __global__ __launch_bounds__(512) void state_delta_kernel(PrefillArgs a) {
   const uint32_t kv_bytes = (uint32_t)((size_t)a.L * D * sizeof(T));
   const __amdgpu_buffer_rsrc_t kr = make_rsrc(reinterpret_cast<const T*>(a.k) + (size_t)unit * a.L * D, kv_bytes);
   const __amdgpu_buffer_rsrc_t vr = make_rsrc(reinterpret_cast<const T*>(a.v) + (size_t)unit * a.L * D, kv_bytes);
-  const uint8_t* sf = a.selflag + (size_t)unit * a.L;
+  const __amdgpu_buffer_rsrc_t sfr = make_rsrc(a.selflag + (size_t)unit * a.L, (uint32_t)a.L);
   load_ft<T, D, 512>(P, reinterpret_cast<const T*>(a.ft) + (size_t)kv * D * D);
   double sum[D / 16][4];
 #pragma unroll
@@ -879,7 +945,7 @@ __global__ __launch_bounds__(512) void state_delta_kernel(PrefillArgs a) {
   const int hi = full_chunks_before(s * a.K + a.K, a.W, a.C) * a.C;
   for (int blo = lo; blo < hi; blo += 64) {
     BlkRegs<T, D, 512> R;
-    issue_block<T, D, 512>(R, kr, vr, kv_bytes, sf, nullptr, 0, blo, hi);
+    issue_block<T, D, 512>(R, kr, vr, kv_bytes, sfr, blk_range(blo, hi));
     __syncthreads();
     commit_block<T, D, 512>(P, R, lo, hi);
     __syncthreads();
@@ -955,7 +1021,9 @@ __global__ __launch_bounds__(256) void state_scan_kernel(float* dS, int NS, int 
 // splits of S and phi(q); <phi(k),phi(q)> with both features in fp16 (all
 // terms are positive, so the relative error stays within 2^-11); softmax
 // weights and values in fp16 (11-bit significands, bf16 values exact).
-template <typename T, int D>
+// A wave holds HPW heads of one 16-query tile: the key, value and phi(K)
+// fragments it reads from LDS serve every head it holds.
+template <typename T, int D, int HPW>
 __global__ __launch_bounds__(512) void attend_kernel(PrefillArgs a) {
   using B_ = Blk<T, D>;
   typedef typename HalfOf<T>::type H;
@@ -969,26 +1037,33 @@ __global__ __launch_bounds__(512) void attend_kernel(PrefillArgs a) {
   const int s = id % a.NS;
   const int u3 = id / a.NS;  // (b, kv, hg)
   const int hg = u3 % a.nHG, kv = (u3 / a.nHG) % a.Hkv, b = u3 / (a.nHG * a.Hkv);
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, r16 = lane & 15, g4 = lane >> 4;
+  const int tid = threadIdx.x, lane = tid & 63, r16 = lane & 15, g4 = lane >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // in an SGPR
   const int L = a.L, C = a.C, W = a.W;
   const int unit = b * a.Hkv + kv;
   const uint32_t kv_bytes = (uint32_t)((size_t)L * D * sizeof(T));
   const __amdgpu_buffer_rsrc_t kr = make_rsrc(reinterpret_cast<const T*>(a.k) + (size_t)unit * L * D, kv_bytes);
   const __amdgpu_buffer_rsrc_t vr = make_rsrc(reinterpret_cast<const T*>(a.v) + (size_t)unit * L * D, kv_bytes);
-  const uint8_t* sf = a.selflag + (size_t)unit * L;
+  const __amdgpu_buffer_rsrc_t sfr = make_rsrc(a.selflag + (size_t)unit * L, (uint32_t)L);
   const int32_t* selu = a.sel + (size_t)unit * a.n_dec * a.lam;
+  const __amdgpu_buffer_rsrc_t selr = make_rsrc(selu, (uint32_t)((size_t)a.n_dec * a.lam * 4));
   load_ft<T, D, 512>(P, reinterpret_cast<const T*>(a.ft) + (size_t)kv * D * D);
   const int n_qt = C / 16;
-  const bool act = wave < a.Gs * n_qt;  // wave-uniform
+  const bool act = wave < (a.Gs / HPW) * n_qt;  // wave-uniform
   const int hl = act ? wave / n_qt : 0, qt = act ? wave % n_qt : 0;
-  const int h = kv * a.G + hg * a.Gs + hl;
-  const float g = a.gate[h];
   // log-weights are kept in base 2: logits times scale * log2(e), linear
   // weights log2(g) + log2 <phi(q), phi(k)>
-  const float lgate2 = g > 0.f ? log2_acc<T>(g) : STILL_NEG_INF;
   const float scale2 = a.scale * STILL_LOG2E;
-  const __amdgpu_buffer_rsrc_t qr =
-      make_rsrc(reinterpret_cast<const T*>(a.q) + ((size_t)(b * a.Hq + h) * L) * D, kv_bytes);
+  int hh[HPW];
+  float gg[HPW], lgate2[HPW];
+  __amdgpu_buffer_rsrc_t qr[HPW];
+#pragma unroll
+  for (int j = 0; j < HPW; ++j) {
+    hh[j] = kv * a.G + hg * a.Gs + hl * HPW + j;
+    gg[j] = a.gate[hh[j]];
+    lgate2[j] = gg[j] > 0.f ? log2_acc<T>(gg[j]) : STILL_NEG_INF;
+    qr[j] = make_rsrc(reinterpret_cast<const T*>(a.q) + ((size_t)(b * a.Hq + hh[j]) * L) * D, kv_bytes);
+  }
 
   const float* Sst = a.dS + ((size_t)unit * a.NS + s) * (D * D + D);
   load_state<T, D>(P, Sst);
@@ -998,6 +1073,7 @@ __global__ __launch_bounds__(512) void attend_kernel(PrefillArgs a) {
   const int c_end = min(c_begin + a.K, a.T);
   for (int c = c_begin; c < c_end; ++c) {
     __syncthreads();
+    const int lane = opaque_tid() & 63, r16 = lane & 15, g4 = lane >> 4;  // see opaque_tid
     const int cC = c * C;
     const bool fold = c + 1 < c_end;
     const int cf = full_chunks_before(c, W, C);
@@ -1012,33 +1088,41 @@ __global__ __launch_bounds__(512) void attend_kernel(PrefillArgs a) {
     for (int i = tid; i < min(n_oob, B_::PCAP); i += 512) P.pidx[i] = selu[i];
 
     // query fragments, phi(q) (F^T from LDS), state readout
-    Frag<T> qf[D / 32];
-    Frag<H> pq[D / 32];  // phi(q) as H for <phi(k), phi(q)>
+    Frag<T> qf[HPW][D / 32];
+    Frag<H> pq[HPW][D / 32];  // phi(q) as H for <phi(k), phi(q)> (linear blocks)
 #pragma unroll
-    for (int kb = 0; kb < D / 32; ++kb)
-      qf[kb] = ld_frag_buf<T>(qr, act ? (uint32_t)(t * D + 8 * g4) * sizeof(T) : kv_bytes,
-                              32 * kb * sizeof(T));
+    for (int j = 0; j < HPW; ++j)
+#pragma unroll
+      for (int kb = 0; kb < D / 32; ++kb)
+        qf[j][kb] = ld_frag_buf<T>(qr[j], act ? (uint32_t)(t * D + 8 * g4) * sizeof(T) : kv_bytes,
+                                   32 * kb * sizeof(T));
     // the first band block's loads are in flight during the readout (issued
     // after the query loads: waits on those then leave them outstanding)
     BlkRegs<T, D, 512> R;
-    issue_block<T, D, 512>(R, kr, vr, kv_bytes, sf, nullptr, 0, band_lo, band_hi);
-    f32x4 O[D / 16];
-    float mrun;
-    f32x4 lacc;  // running sum, the same in all four entries (ones-row MFMA)
+    issue_block<T, D, 512>(R, kr, vr, kv_bytes, sfr, blk_range(band_lo, band_hi));
+    f32x4 O[HPW][D / 16];
+    float mrun[HPW];
+    f32x4 lacc[HPW];  // running sums, the same in all four entries (ones-row MFMA)
     {
-      f32x4 ph[D / 16];
-      np_map_tile<T, D>(P, qf, ph);
-      float dz = 0.f;
+      Frag<T> phq[HPW][D / 32], phl[HPW][D / 32];
+      float dz[HPW];
+      {
+        f32x4 ph[HPW][D / 16];
+        np_map_tiles<T, D, HPW>(P, qf, ph);
 #pragma unroll
-      for (int ft = 0; ft < D / 16; ++ft)
+        for (int j = 0; j < HPW; ++j) {
+          float z_ = 0.f;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) dz += ph[ft][i] * (float)P.zs[16 * ft + 4 * g4 + i];
-      dz = sum_over_g(dz);
-      Frag<T> phq[D / 32], phl[D / 32];
+          for (int ft = 0; ft < D / 16; ++ft)
 #pragma unroll
-      for (int bb = 0; bb < D / 32; ++bb) {
-        split2_frag<T>(ph[2 * bb], ph[2 * bb + 1], phq[bb], phl[bb]);
-        pq[bb] = frag_from<H>(ph[2 * bb], ph[2 * bb + 1]);
+            for (int i = 0; i < 4; ++i) z_ += ph[j][ft][i] * (float)P.zs[16 * ft + 4 * g4 + i];
+          dz[j] = sum_over_g(z_);
+#pragma unroll
+          for (int bb = 0; bb < D / 32; ++bb) {
+            split2_frag<T>(ph[j][2 * bb], ph[j][2 * bb + 1], phq[j][bb], phl[j][bb]);
+            pq[j][bb] = frag_from<H>(ph[j][2 * bb], ph[j][2 * bb + 1]);
+          }
+        }
       }
       // S as hi/lo bf16 fragments, split once and shared by every wave, in
       // two halves of the d_v tiles (the split region holds one half)
@@ -1057,209 +1141,255 @@ __global__ __launch_bounds__(512) void attend_kernel(PrefillArgs a) {
 #pragma unroll
         for (int dh = 0; dh < D / 32; ++dh) {
           const int dt = half * (D / 32) + dh;
-          O[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int j = 0; j < HPW; ++j) O[j][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int bb = 0; bb < D / 32; ++bb) {
             // S^T phi(q) to ~2^-16 relative: hi*hi + lo*hi + hi*lo
             const int pl = dh * (D / 32) + bb;
             const Frag<T> sh = ld_frag(P.RS + ((size_t)(2 * pl) * 64 + lane) * 8);
-            mma(O[dt], sh, phq[bb]);
+#pragma unroll
+            for (int j = 0; j < HPW; ++j) mma(O[j][dt], sh, phq[j][bb]);
             if constexpr (sizeof(T) == 2) {
               const Frag<T> sl = ld_frag(P.RS + ((size_t)(2 * pl + 1) * 64 + lane) * 8);
-              mma(O[dt], sl, phq[bb]);
-              mma(O[dt], sh, phl[bb]);
+#pragma unroll
+              for (int j = 0; j < HPW; ++j) {
+                mma(O[j][dt], sl, phq[j][bb]);
+                mma(O[j][dt], sh, phl[j][bb]);
+              }
             }
           }
         }
         if (half == 0) __syncthreads();  // the region is split into again
       }
-      if (g > 0.f && dz > 0.f) {
-        mrun = log2_acc<T>(g * dz);
-        lacc = f32x4{1.f, 1.f, 1.f, 1.f};
-        const float inv = 1.f / dz;
 #pragma unroll
-        for (int dt = 0; dt < D / 16; ++dt) O[dt] *= inv;
-      } else {
-        mrun = STILL_NEG_INF;
-        lacc = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int j = 0; j < HPW; ++j) {
+        if (gg[j] > 0.f && dz[j] > 0.f) {
+          mrun[j] = log2_acc<T>(gg[j] * dz[j]);
+          lacc[j] = f32x4{1.f, 1.f, 1.f, 1.f};
+          const float inv = 1.f / dz[j];
 #pragma unroll
-        for (int dt = 0; dt < D / 16; ++dt) O[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+          for (int dt = 0; dt < D / 16; ++dt) O[j][dt] *= inv;
+        } else {
+          mrun[j] = STILL_NEG_INF;
+          lacc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int dt = 0; dt < D / 16; ++dt) O[j][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
       }
     }
 
     // key blocks: the band first (linear-attention weights, fold), then the
-    // kept pool below the band, whose global loads for block i+1 are in
-    // flight while block i is used
+    // kept pool below the band
     const int n_pool_blk = (n_oob + 63) / 64;
     const int n_band_blk = (band_hi - band_lo + 63) / 64;
     // softmax / linear weights of one block in LDS folded into (m, l, O)
-    auto attend_block = [&](const bool is_pool, const int blo, const int nvalid, const bool la_blk) {
+    auto attend_block = [&](const bool is_pool, const int blo, const int nvalid, const bool la_blk)
+                            __attribute__((always_inline)) {
+      // region bases made opaque again per block: the per-lane fragment
+      // addresses are then recomputed here instead of held across the loop
+      const int lane = opaque_tid() & 63, r16 = lane & 15, g4 = lane >> 4;
+      BlkPtr<T, D> Pb = P;
+      Pb.Ks = lds_opaque_v(P.Ks);
+      Pb.VTs = lds_opaque_v(P.VTs);
+      Pb.WF = lds_opaque_v(P.WF);
       const uint64_t selbits = ((uint64_t)P.selw[1] << 32) | P.selw[0];
-      f32x4 st[4];
+      f32x4 st[HPW][4];
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt) {
-        st[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int kb = 0; kb < D / 32; ++kb)
-          mma(st[kt], ld_frag(P.Ks + (16 * kt + r16) * B_::KS + 32 * kb + 8 * g4), qf[kb]);
+        for (int j = 0; j < HPW; ++j) st[j][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < D / 32; ++kb) {
+          const Frag<T> kf = ld_frag(Pb.Ks + (16 * kt + r16) * B_::KS + 32 * kb + 8 * g4);
+#pragma unroll
+          for (int j = 0; j < HPW; ++j) mma(st[j][kt], kf, qf[j][kb]);
+        }
       }
-      float mx = STILL_NEG_INF;
+      // st holds raw logits (scaled into the base-2 domain inside the
+      // exponential); linear keys hold their log-weight / scale2, masked
+      // keys -inf. scale2 > 0, so the row maximum commutes with the scaling.
+      float mx[HPW];
+#pragma unroll
+      for (int j = 0; j < HPW; ++j) mx[j] = STILL_NEG_INF;
       if (is_pool) {
         if (nvalid < 64) {  // uniform: only a last, partial pool block is masked
           const uint64_t v_s = low_bits(nvalid) >> (4 * g4);
 #pragma unroll
-          for (int kt = 0; kt < 4; ++kt)
+          for (int j = 0; j < HPW; ++j)
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-              st[kt][i] = ((v_s >> (16 * kt + i)) & 1ull) ? st[kt][i] * scale2 : STILL_NEG_INF;
-        } else {
+            for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-          for (int kt = 0; kt < 4; ++kt) st[kt] *= scale2;
+              for (int i = 0; i < 4; ++i)
+                st[j][kt][i] = ((v_s >> (16 * kt + i)) & 1ull) ? st[j][kt][i] : STILL_NEG_INF;
         }
-#pragma unroll
-        for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) mx = fmaxf(mx, st[kt][i]);
       } else {
-        f32x4 wt[4];
-        if (la_blk) {
-#pragma unroll
-          for (int kt = 0; kt < 4; ++kt) {
-            wt[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int bb = 0; bb < D / 32; ++bb) mma(wt[kt], P.ld_wk(kt, bb), pq[bb]);
-          }
-        }
         // per-lane key masks (bit kk = key blo + kk): visible keys are those
         // up to the query; softmax-visible ones are in the window / own
         // chunk or kept; the rest of the visible ones are linear
         const uint64_t valid_m = low_bits(min(nvalid, t - blo + 1));
         const uint64_t sa_m = valid_m & (~low_bits(min(t - W + 1, cC) - blo) | selbits);
         const uint64_t sa_s = sa_m >> (4 * g4), la_s = (valid_m & ~sa_m) >> (4 * g4);
+        const float inv_scale2 = 1.f / scale2;
+#pragma unroll
+        for (int j = 0; j < HPW; ++j) {
+          f32x4 wt[4];
+          if (la_blk) {
+#pragma unroll
+            for (int kt = 0; kt < 4; ++kt) {
+              wt[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+              for (int bb = 0; bb < D / 32; ++bb) mma(wt[kt], Pb.ld_wk(kt, bb), pq[j][bb]);
+            }
+          }
+#pragma unroll
+          for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              float x = ((sa_s >> (16 * kt + i)) & 1ull) ? st[j][kt][i] : STILL_NEG_INF;
+              if (la_blk) {
+                const float w = wt[kt][i];
+                const bool la = ((la_s >> (16 * kt + i)) & 1ull) && w > 0.f;
+                x = la ? (lgate2[j] + log2_acc<T>(fmaxf(w, 1e-37f))) * inv_scale2 : x;
+              }
+              st[j][kt][i] = x;
+            }
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < HPW; ++j)
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt)
+          mx[j] = fmaxf(mx[j], fmaxf(fmaxf(st[j][kt][0], st[j][kt][1]), fmaxf(st[j][kt][2], st[j][kt][3])));
+      Frag<H> pf[HPW][2];
+#pragma unroll
+      for (int j = 0; j < HPW; ++j) {
+        const float mxj = max_over_g(mx[j]) * scale2;
+        const float mn = fmaxf(mrun[j], mxj);
+        // rows with nothing visible so far keep m = -inf, O = 0, l = 0; the
+        // exponent's offset is finite either way (exp2(-inf) = 0)
+        const float al = mrun[j] == STILL_NEG_INF ? 0.f : exp2_acc<T>(mrun[j] - mn);
+        const float nmn = mn == STILL_NEG_INF ? 0.f : -mn;
+        mrun[j] = mn;
+        f32x4 pv[4];
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            float lw = ((sa_s >> (16 * kt + i)) & 1ull) ? st[kt][i] * scale2 : STILL_NEG_INF;
-            if (la_blk) {
-              const float w = wt[kt][i];
-              const bool la = ((la_s >> (16 * kt + i)) & 1ull) && w > 0.f;
-              lw = la ? lgate2 + log2_acc<T>(fmaxf(w, 1e-37f)) : lw;
-            }
-            st[kt][i] = lw;
-            mx = fmaxf(mx, lw);
-          }
-      }
-      mx = max_over_g(mx);
-      const float mn = fmaxf(mrun, mx);
-      // rows with nothing visible so far keep m = -inf, O = 0, l = 0
-      const float al = mrun == STILL_NEG_INF ? 0.f : exp2_acc<T>(mrun - mn);
-      mrun = mn;
-      f32x4 pv[4];
+          for (int i = 0; i < 4; ++i) pv[kt][i] = exp2_acc<T>(fmaf(st[j][kt][i], scale2, nmn));
+        // weights as H; the running sum comes from the same rounded weights
+        // through a ones-row MFMA
+        pf[j][0] = frag_from<H>(pv[0], pv[1]);
+        pf[j][1] = frag_from<H>(pv[2], pv[3]);
+        if (__builtin_amdgcn_ballot_w64(al != 1.f)) {  // wave-uniform: some max moved
+          lacc[j] *= al;
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float lw = st[kt][i];
-          pv[kt][i] = lw == STILL_NEG_INF ? 0.f : exp2_acc<T>(lw - mn);
+          for (int dt = 0; dt < D / 16; ++dt) O[j][dt] *= al;
         }
-      // weights as H; the running sum comes from the same rounded weights
-      // through a ones-row MFMA
-      const Frag<H> pf0 = frag_from<H>(pv[0], pv[1]);
-      const Frag<H> pf1 = frag_from<H>(pv[2], pv[3]);
-      if (__builtin_amdgcn_ballot_w64(al != 1.f)) {  // wave-uniform: some max moved
-        lacc *= al;
-#pragma unroll
-        for (int dt = 0; dt < D / 16; ++dt) O[dt] *= al;
+        const Frag<H> one = ones_frag<H>();
+        mma(lacc[j], one, pf[j][0]);
+        mma(lacc[j], one, pf[j][1]);
       }
-      const Frag<H> one = ones_frag<H>();
-      mma(lacc, one, pf0);
-      mma(lacc, one, pf1);
 #pragma unroll
       for (int dt = 0; dt < D / 16; ++dt) {
-        mma(O[dt], P.ld_v(dt, 0), pf0);
-        mma(O[dt], P.ld_v(dt, 1), pf1);
+        const Frag<H> v0 = Pb.ld_v(dt, 0), v1 = Pb.ld_v(dt, 1);
+#pragma unroll
+        for (int j = 0; j < HPW; ++j) {
+          mma(O[j][dt], v0, pf[j][0]);
+          mma(O[j][dt], v1, pf[j][1]);
+        }
       }
     };
-    auto issue_pool = [&](int pb) {
+    auto issue_pool = [&](int pb) __attribute__((always_inline)) {
       const int blo = 64 * pb;
-      if (blo + 64 <= B_::PCAP)  // positions staged in LDS
-        issue_block<T, D, 512>(R, kr, vr, kv_bytes, sf, P.pidx + blo, min(64, n_oob - blo), 0, 0);
-      else
-        issue_block<T, D, 512>(R, kr, vr, kv_bytes, sf, selu + blo, min(64, n_oob - blo), 0, 0);
+      BlkSrc src{};
+      src.mode = blo + 64 <= B_::PCAP ? 1 : 2;  // positions staged in LDS, else global
+      src.lds = P.pidx;
+      src.glist = selr;
+      src.first = blo;
+      src.n = min(64, n_oob - blo);
+      issue_block<T, D, 512>(R, kr, vr, kv_bytes, sfr, src);
     };
-    for (int bb = 0; bb < n_band_blk; ++bb) {
-      const int blo = band_lo + 64 * bb;
-      const bool la_blk = blo < cC;
-      const bool do_fold = fold && blo < fold_hi;
-      if (bb > 0) issue_block<T, D, 512>(R, kr, vr, kv_bytes, sf, nullptr, 0, blo, band_hi);
+    // one stream of blocks, the band's then the pool's: block i + 1 is
+    // issued as soon as block i is in LDS, so its loads are in flight while
+    // block i is used. The band blocks below the chunk (linear weights, the
+    // only users of phi(q) after the readout) come first, in a loop of their
+    // own, so phi(q) is not held through the rest.
+    const int nblk = n_band_blk + n_pool_blk;
+    const int n_la_blk = min(n_band_blk, max(0, (cC - band_lo + 63) / 64));
+    auto process = [&](int i, auto la_phase) __attribute__((always_inline)) {
+      constexpr bool LA = decltype(la_phase)::value;
+      const bool band = i < n_band_blk;  // uniform
+      const int blo = band ? band_lo + 64 * i : 64 * (i - n_band_blk);
       __syncthreads();  // the previous block (or the readout) is done with LDS
-      commit_block<T, D, 512>(P, R, fold_lo, fold_hi);
+      commit_block<T, D, 512>(P, R, band ? fold_lo : 0, band ? fold_hi : 0);
+      if (i + 1 < n_band_blk)
+        issue_block<T, D, 512>(R, kr, vr, kv_bytes, sfr, blk_range(blo + 64, band_hi));
+      else if (i + 1 < nblk)
+        issue_pool(i + 1 - n_band_blk);
       __syncthreads();
+      const bool la_blk = LA && band && blo < cC;
+      const bool do_fold = band && fold && blo < fold_hi;
       if (la_blk || do_fold) {
         f32x4 phk[4];
         block_phi<T, D>(P, phk, la_blk);  // ends with a barrier
         // the fold writes only SP / zs, which this chunk no longer reads
         if (do_fold) block_fold<T, D>(P, phk);
       }
-      if (act) attend_block(false, blo, min(64, band_hi - blo), la_blk);  // wave-uniform
-    }
-    if (n_pool_blk > 0) {
-      issue_pool(0);
-      __syncthreads();
-      commit_block<T, D, 512>(P, R, 0, 0);
-    }
-    for (int pb = 0; pb < n_pool_blk; ++pb) {
-      __syncthreads();  // pool block pb is in LDS
-      if (pb + 1 < n_pool_blk) issue_pool(pb + 1);
-      if (act) attend_block(true, 64 * pb, min(64, n_oob - 64 * pb), false);
-      if (pb + 1 < n_pool_blk) {
-        __syncthreads();  // every wave is done with block pb
-        commit_block<T, D, 512>(P, R, 0, 0);
-      }
-    }
+      // one call site, whatever the block (the accumulators then stay in
+      // place); idle waves run it too on a copy of wave 0's rows and store
+      // nothing
+      attend_block(!band, blo, min(64, (band ? band_hi : n_oob) - blo), la_blk);
+    };
+    for (int i = 0; i < n_la_blk; ++i) process(i, std::true_type{});
+    for (int i = n_la_blk; i < nblk; ++i) process(i, std::false_type{});
 
     // outputs: normalise; bf16 rows go through LDS for full-line stores
-    const float l = lacc[0];
-    const float inv = 1.f / l;
-    const size_t ob = ((size_t)(b * a.Hq + h) * L) * D;
-    if constexpr (sizeof(T) == 2) {
-      if (!a.fp32_out) {
-        __syncthreads();  // Ks / VTs are free again
-        constexpr int OS = D + 8;  // padded row, elements
-        bf16* tile = reinterpret_cast<bf16*>(smem) + (size_t)wave * 16 * OS;
-        if (act) {
 #pragma unroll
-          for (int dt = 0; dt < D / 16; ++dt) {
-            const f32x4 y = O[dt] * inv;
-            bf16 y4[4] = {(bf16)y[0], (bf16)y[1], (bf16)y[2], (bf16)y[3]};
-            *reinterpret_cast<uint2*>(tile + r16 * OS + 16 * dt + 4 * g4) = *reinterpret_cast<uint2*>(y4);
-          }
-          // wave-local: the tile is written and read by this wave only
-          __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-          __builtin_amdgcn_wave_barrier();
-          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-          constexpr int CPR = D / 8;  // 16-byte chunks per row
+    for (int j = 0; j < HPW; ++j) {
+      const float inv = 1.f / lacc[j][0];
+      const size_t ob = ((size_t)(b * a.Hq + hh[j]) * L) * D;
+      if constexpr (sizeof(T) == 2) {
+        if (!a.fp32_out) {
+          if (j == 0) __syncthreads();  // Ks / VTs are free again
+          constexpr int OS = D + 8;  // padded row, elements
+          bf16* tile = reinterpret_cast<bf16*>(smem) + (size_t)wave * 16 * OS;
+          if (act) {
+            // wave-local: the tile is written and read by this wave only
+            auto wave_sync = [] {
+              __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+              __builtin_amdgcn_wave_barrier();
+              __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            };
+            if (j > 0) wave_sync();  // the previous head's rows are read
 #pragma unroll
-          for (int it = 0; it < 16 * CPR / 64; ++it) {
-            const int e = it * 64 + lane, row = e / CPR, ch = e % CPR;
-            const int tr = cC + 16 * qt + row;
-            if (tr < L)
-              *reinterpret_cast<uint4*>(reinterpret_cast<bf16*>(a.out) + ob + (size_t)tr * D + 8 * ch) =
-                  *reinterpret_cast<const uint4*>(tile + row * OS + 8 * ch);
+            for (int dt = 0; dt < D / 16; ++dt) {
+              const f32x4 y = O[j][dt] * inv;
+              bf16 y4[4] = {(bf16)y[0], (bf16)y[1], (bf16)y[2], (bf16)y[3]};
+              *reinterpret_cast<uint2*>(tile + r16 * OS + 16 * dt + 4 * g4) = *reinterpret_cast<uint2*>(y4);
+            }
+            wave_sync();
+            constexpr int CPR = D / 8;  // 16-byte chunks per row
+#pragma unroll
+            for (int it = 0; it < 16 * CPR / 64; ++it) {
+              const int e = it * 64 + lane, row = e / CPR, ch = e % CPR;
+              const int tr = cC + 16 * qt + row;
+              if (tr < L)
+                *reinterpret_cast<uint4*>(reinterpret_cast<bf16*>(a.out) + ob + (size_t)tr * D + 8 * ch) =
+                    *reinterpret_cast<const uint4*>(tile + row * OS + 8 * ch);
+            }
           }
+        } else if (act && t < L) {
+#pragma unroll
+          for (int dt = 0; dt < D / 16; ++dt)
+            *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.out) + ob + (size_t)t * D + 16 * dt + 4 * g4) =
+                O[j][dt] * inv;
         }
       } else if (act && t < L) {
 #pragma unroll
         for (int dt = 0; dt < D / 16; ++dt)
           *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.out) + ob + (size_t)t * D + 16 * dt + 4 * g4) =
-              O[dt] * inv;
+              O[j][dt] * inv;
       }
-    } else if (act && t < L) {
-#pragma unroll
-      for (int dt = 0; dt < D / 16; ++dt)
-        *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.out) + ob + (size_t)t * D + 16 * dt + 4 * g4) =
-            O[dt] * inv;
     }
     if (c == a.T - 1 && hg == 0) {
       __syncthreads();
