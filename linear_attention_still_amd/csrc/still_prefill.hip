@@ -943,11 +943,14 @@ __global__ __launch_bounds__(512) void state_delta_kernel(PrefillArgs a) {
   double zsum = 0.0;
   const int lo = full_chunks_before(s * a.K, a.W, a.C) * a.C;
   const int hi = full_chunks_before(s * a.K + a.K, a.W, a.C) * a.C;
+  // block blo + 64 is issued as soon as block blo is in LDS (past hi the
+  // loads read zeros past the buffer range)
+  BlkRegs<T, D, 512> R;
+  issue_block<T, D, 512>(R, kr, vr, kv_bytes, sfr, blk_range(lo, hi));
   for (int blo = lo; blo < hi; blo += 64) {
-    BlkRegs<T, D, 512> R;
-    issue_block<T, D, 512>(R, kr, vr, kv_bytes, sfr, blk_range(blo, hi));
     __syncthreads();
     commit_block<T, D, 512>(P, R, lo, hi);
+    issue_block<T, D, 512>(R, kr, vr, kv_bytes, sfr, blk_range(blo + 64, hi));
     __syncthreads();
     f32x4 ph[4];
     block_phi<T, D>(P, ph, false);
