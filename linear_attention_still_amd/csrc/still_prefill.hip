@@ -86,7 +86,8 @@ __global__ __launch_bounds__(256) void score_kernel(PrefillArgs a) {
   extern __shared__ __align__(16) char smem[];
   const int c = blockIdx.x, kv = blockIdx.y, b = blockIdx.z;
   const int L = a.L, C = a.C, W = a.W, G = a.G;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // in an SGPR
   const int r16 = lane & 15, g4 = lane >> 4;
   constexpr int KS = D + Pad<T>::v;
   const int cC = c * C;
@@ -100,22 +101,52 @@ __global__ __launch_bounds__(256) void score_kernel(PrefillArgs a) {
   const T* kg = reinterpret_cast<const T*>(a.k) + (size_t)(b * a.Hkv + kv) * L * D;
   constexpr int VEC = 16 / sizeof(T);
   const int nvec = nkt * 16 * (D / VEC);
+  const int n_qt = C / 16;
+  const int n_rt = G * n_qt;
+  // query fragments of row tile rt (zeros past the sequence or the tiles):
+  // the next tile's are loaded while this one is used
+  const uint32_t qbytes = (uint32_t)((size_t)L * D * sizeof(T));
+  auto load_q = [&](Frag<T>* f, int rt) {
+    const int hl = rt / n_qt, qt = rt % n_qt;
+    const int t = cC + 16 * qt + r16;
+    const __amdgpu_buffer_rsrc_t qrs = make_rsrc(
+        reinterpret_cast<const T*>(a.q) + ((size_t)(b * a.Hq + kv * G + (rt < n_rt ? hl : 0)) * L) * D, qbytes);
+    const uint32_t off = (rt < n_rt && t < L) ? (uint32_t)((t * D + 8 * g4) * sizeof(T)) : qbytes;
+#pragma unroll
+    for (int kb = 0; kb < D / 32; ++kb) f[kb] = ld_frag_buf<T>(qrs, off, 32 * kb * sizeof(T));
+  };
+  Frag<T> qnext[D / 32];
+  load_q(qnext, wave);  // in flight while the keys are staged
   if (tid == 0) kmax[0] = 0.f;
   __syncthreads();
   // keys into LDS; the largest squared key norm (for the error bound) from
   // the same vectors: D / VEC consecutive lanes hold one row
   float kmx = 0.f;
-  for (int idx = tid; idx < nvec; idx += 256) {  // whole rows per lane group
-    const int row = idx / (D / VEC), col = (idx % (D / VEC)) * VEC;
-    const int j = kbase + row;
-    uint4 val = {0, 0, 0, 0};
-    if (j >= 0 && j < L && j < cC + C) val = *reinterpret_cast<const uint4*>(kg + (size_t)j * D + col);
-    *reinterpret_cast<uint4*>(Ks + row * KS + col) = val;
-    const T* e = reinterpret_cast<const T*>(&val);
-    float q2 = 0.f;
+  // up to eight 16-byte loads per thread in flight at a time; rows outside
+  // [0, min(L, cC + C)) read past the buffer range (zeros)
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(kg, qbytes);
+  constexpr int NB = 8;
+  for (int base = 0; base < nvec; base += NB * 256) {  // whole rows per lane group
+    uint4 val[NB];
 #pragma unroll
-    for (int i = 0; i < VEC; ++i) q2 += to_f32(e[i]) * to_f32(e[i]);
-    kmx = fmaxf(kmx, row_sum<D / VEC>(q2));
+    for (int u = 0; u < NB; ++u) {
+      const int idx = base + u * 256 + tid;
+      const int row = idx / (D / VEC), col = (idx % (D / VEC)) * VEC;
+      const int j = kbase + row;
+      const bool ok = idx < nvec && j >= 0 && j < L && j < cC + C;
+      val[u] = ld_u4_buf(krs, ok ? (uint32_t)(((size_t)j * D + col) * sizeof(T)) : qbytes, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < NB; ++u) {
+      const int idx = base + u * 256 + tid;
+      const int row = idx / (D / VEC), col = (idx % (D / VEC)) * VEC;
+      if (idx < nvec) *reinterpret_cast<uint4*>(Ks + row * KS + col) = val[u];
+      const T* e = reinterpret_cast<const T*>(&val[u]);
+      float q2 = 0.f;
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) q2 += to_f32(e[i]) * to_f32(e[i]);
+      kmx = fmaxf(kmx, row_sum<D / VEC>(q2));
+    }
   }
   kmx = row_max<16>(kmx);
   kmx = fmaxf(kmx, xor16f(kmx));
@@ -124,20 +155,16 @@ __global__ __launch_bounds__(256) void score_kernel(PrefillArgs a) {
   __syncthreads();
   const float kn_max = sqrtf(kmax[0]);
 
-  const int n_qt = C / 16;
-  const int n_rt = G * n_qt;
   for (int rt = wave; rt < n_rt; rt += 4) {
     const int hl = rt / n_qt, qt = rt % n_qt;
-    const int h = kv * G + hl;
     const int t = cC + 16 * qt + r16;
-    const T* qg = reinterpret_cast<const T*>(a.q) + ((size_t)(b * a.Hq + h) * L) * D;
     Frag<T> qf[D / 32];
+#pragma unroll
+    for (int kb = 0; kb < D / 32; ++kb) qf[kb] = qnext[kb];
+    load_q(qnext, rt + 4);
     float qn2 = 0.f;
 #pragma unroll
-    for (int kb = 0; kb < D / 32; ++kb) {
-      qf[kb] = (t < L) ? ld_frag(qg + (size_t)t * D + 32 * kb + 8 * g4) : zero_frag<T>();
-      qn2 += frag_sumsq(qf[kb]);
-    }
+    for (int kb = 0; kb < D / 32; ++kb) qn2 += frag_sumsq(qf[kb]);
     qn2 = sum_over_g(qn2);
     float mrun = STILL_NEG_INF, zall = 0.f, zoth = 0.f, sself = STILL_NEG_INF;
     const int kt_lo = qt, kt_hi = qt + (W + 14) / 16;
