@@ -1014,17 +1014,18 @@ __global__ __launch_bounds__(256) void state_scan_kernel(float* dS, int NS, int 
   if (e >= n_elem) return;
   float* base = dS + (size_t)(blockIdx.y + gridDim.y * blockIdx.z) * NS * n_elem + e;
   double run = 0.0;  // float64 running sum: one float32 rounding per start
-  constexpr int B8 = 8;  // loads of a batch in flight together
-  for (int s0 = 0; s0 < NS; s0 += B8) {
-    float x[B8];
+  constexpr int NB = 32;  // loads of a batch in flight together (indices
+                          // past the end re-read the last entry, unused)
+  for (int s0 = 0; s0 < NS; s0 += NB) {
+    float x[NB];
 #pragma unroll
-    for (int i = 0; i < B8; ++i) x[i] = s0 + i < NS ? base[(size_t)(s0 + i) * n_elem] : 0.f;
+    for (int i = 0; i < NB; ++i) x[i] = base[(size_t)min(s0 + i, NS - 1) * n_elem];
 #pragma unroll
-    for (int i = 0; i < B8; ++i) {
-      if (s0 + i >= NS) break;
-      base[(size_t)(s0 + i) * n_elem] = (float)run;
-      run += (double)x[i];
-    }
+    for (int i = 0; i < NB; ++i)
+      if (s0 + i < NS) {
+        base[(size_t)(s0 + i) * n_elem] = (float)run;
+        run += (double)x[i];
+      }
   }
 }
 
@@ -1435,72 +1436,58 @@ __global__ __launch_bounds__(512) void attend_kernel(PrefillArgs a) {
 // values, NP-Map features, kept flags), the kept pool, and the position.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void export_kernel(PrefillArgs a) {
+  extern __shared__ __align__(16) char smem[];
   const int x = blockIdx.x, kv = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, L = a.L, R = a.R;
   const int unit = b * a.Hkv + kv;
   char* st = a.state + (size_t)unit * a.st_unit;
   const T* kg = reinterpret_cast<const T*>(a.k) + (size_t)unit * L * D;
   const T* vg = reinterpret_cast<const T*>(a.v) + (size_t)unit * L * D;
+  constexpr int VEC = 16 / sizeof(T), CPR = D / VEC;  // 16-byte chunks per row
   const int ring_lo = L - R > 0 ? L - R : 0;
-  const int n_ring_grp = (L - ring_lo + 15) / 16;
+  const int n_ring_grp = (L - ring_lo + 63) / 64;
   if (x < n_ring_grp) {
-    // NP-Map of 16 ring keys [P3 "NP-Map: Norm-Preserving Feature Map"]
-    // with F staged in LDS; per-row statistics by one wave per row
-    __shared__ __align__(16) T Fs[D * D];
-    __shared__ float xs[16][D];
-    __shared__ float us[16][D];
-    __shared__ float red[16][2];
-    const int lane = tid & 63, wave = tid >> 6;
-    const T* F = reinterpret_cast<const T*>(a.fmap_w) + (size_t)kv * D * D;
-    for (int e = tid; e < D * D * (int)sizeof(T) / 16; e += 256)
-      reinterpret_cast<uint4*>(Fs)[e] = reinterpret_cast<const uint4*>(F)[e];
-    for (int e = tid; e < 16 * D; e += 256) {
-      const int r = e / D, i = e % D, p = ring_lo + 16 * x + r;
-      xs[r][i] = p < L ? to_f32(kg[(size_t)p * D + i]) : 0.f;
-    }
-    __syncthreads();
-    for (int e = tid; e < 16 * D; e += 256) {
-      const int r = e / D, j = e % D;
-      float u = 0.f;
-#pragma unroll 8
-      for (int i = 0; i < D; ++i) u += xs[r][i] * to_f32(Fs[i * D + j]);
-      us[r][j] = u;
-    }
-    __syncthreads();
-    for (int r = wave; r < 16; r += 4) {
-      float mx = STILL_NEG_INF, xn = 0.f;
-      for (int j = lane; j < D; j += 64) {
-        mx = fmaxf(mx, us[r][j]);
-        xn += xs[r][j] * xs[r][j];
-      }
-      mx = row_max<16>(mx);
-      mx = fmaxf(mx, xor16f(mx));
-      mx = fmaxf(mx, xor32f(mx));
-      float ss = 0.f;
-      for (int j = lane; j < D; j += 64) {
-        const float e = exp_acc<T>(us[r][j] - mx);
-        ss += e * e;
-      }
-      xn = sum_over_g(row_sum<16>(xn));
-      ss = sum_over_g(row_sum<16>(ss));
-      if (lane == 0) {
-        red[r][0] = mx;
-        red[r][1] = sqrtf(xn) / sqrtf(ss);
-      }
-    }
-    __syncthreads();
+    // 64 ring keys per workgroup, 16 per wave: NP-Map [P3 "NP-Map:
+    // Norm-Preserving Feature Map"] by MFMA against F^T (fragment order, in
+    // LDS), keys, values and kept flags copied to their slots
+    BlkPtr<T, D> P(smem);
+    P.FT = lds_opaque(reinterpret_cast<T*>(smem));
+    load_ft<T, D, 256>(P, reinterpret_cast<const T*>(a.ft) + (size_t)kv * D * D);
+    const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int r16 = lane & 15, g4 = lane >> 4;
+    const uint32_t kv_bytes = (uint32_t)((size_t)L * D * sizeof(T));
+    const __amdgpu_buffer_rsrc_t kr = make_rsrc(kg, kv_bytes);
+    const int p = ring_lo + 64 * x + 16 * wave + r16;  // key row of lane (r, g)
+    Frag<T> xf[D / 32];
+#pragma unroll
+    for (int kb = 0; kb < D / 32; ++kb)
+      xf[kb] = ld_frag_buf<T>(kr, p < L ? (uint32_t)((p * D + 8 * g4) * sizeof(T)) : kv_bytes,
+                              32 * kb * sizeof(T));
+    __syncthreads();  // F^T in LDS
+    f32x4 ph[D / 16];
+    np_map_tile<T, D>(P, xf, ph);
     T* rk = reinterpret_cast<T*>(st + a.st_ring_k);
     T* rv = reinterpret_cast<T*>(st + a.st_ring_v);
     T* rp = reinterpret_cast<T*>(st + a.st_ring_phi);
     int32_t* rf = reinterpret_cast<int32_t*>(st + a.st_ring_flag);
-    for (int e = tid; e < 16 * D; e += 256) {
-      const int r = e / D, j = e % D, p = ring_lo + 16 * x + r;
-      if (p >= L) continue;
+    if (p < L) {
       const int slot = p % R;
-      rk[(size_t)slot * D + j] = kg[(size_t)p * D + j];
-      rv[(size_t)slot * D + j] = vg[(size_t)p * D + j];
-      rp[(size_t)slot * D + j] = from_f32<T>(exp_acc<T>(us[r][j] - red[r][0]) * red[r][1]);
-      if (j == 0) rf[slot] = a.selflag[(size_t)unit * L + p];
+#pragma unroll
+      for (int ft = 0; ft < D / 16; ++ft) {
+        T w4[4] = {from_f32<T>(ph[ft][0]), from_f32<T>(ph[ft][1]), from_f32<T>(ph[ft][2]),
+                   from_f32<T>(ph[ft][3])};
+        T* dst = rp + (size_t)slot * D + 16 * ft + 4 * g4;
+        if constexpr (sizeof(T) == 2) *reinterpret_cast<uint2*>(dst) = *reinterpret_cast<uint2*>(w4);
+        else *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<uint4*>(w4);
+      }
+      if (g4 == 0) rf[slot] = a.selflag[(size_t)unit * L + p];
+    }
+    for (int e = tid; e < 64 * CPR; e += 256) {
+      const int r = e / CPR, c = (e % CPR) * VEC, q = ring_lo + 64 * x + r;
+      if (q >= L) continue;
+      const int slot = q % R;
+      *reinterpret_cast<uint4*>(rk + (size_t)slot * D + c) = *reinterpret_cast<const uint4*>(kg + (size_t)q * D + c);
+      *reinterpret_cast<uint4*>(rv + (size_t)slot * D + c) = *reinterpret_cast<const uint4*>(vg + (size_t)q * D + c);
     }
     return;
   }
@@ -1511,13 +1498,13 @@ __global__ __launch_bounds__(256) void export_kernel(PrefillArgs a) {
   T* pk = reinterpret_cast<T*>(st + a.st_pool_k);
   T* pvv = reinterpret_cast<T*>(st + a.st_pool_v);
   int32_t* pp = reinterpret_cast<int32_t*>(st + a.st_pool_pos);
-  for (int e = tid; e < 16 * D; e += 256) {
-    const int r = e / D, j = e % D, i = i0 + r;
+  for (int e = tid; e < 16 * CPR; e += 256) {
+    const int r = e / CPR, c = (e % CPR) * VEC, i = i0 + r;
     if (i >= n_pool) continue;
-    const int p = selu[i];
-    pk[(size_t)i * D + j] = kg[(size_t)p * D + j];
-    pvv[(size_t)i * D + j] = vg[(size_t)p * D + j];
-    if (j == 0) pp[i] = p;
+    const int q = selu[i];
+    *reinterpret_cast<uint4*>(pk + (size_t)i * D + c) = *reinterpret_cast<const uint4*>(kg + (size_t)q * D + c);
+    *reinterpret_cast<uint4*>(pvv + (size_t)i * D + c) = *reinterpret_cast<const uint4*>(vg + (size_t)q * D + c);
+    if (c == 0) pp[i] = q;
   }
   if (x == n_ring_grp && tid == 0) {
     int64_t* meta = reinterpret_cast<int64_t*>(st + a.st_meta);
