@@ -395,6 +395,46 @@ __device__ __forceinline__ float xor32f(float x) {
                                                   __builtin_bit_cast(unsigned, x), false, false);
   return __builtin_bit_cast(float, (threadIdx.x & 32) ? p[0] : p[1]);
 }
+// float64 forms, each 32-bit half moved on its own
+template <int CTRL>
+__device__ __forceinline__ double dppd(double x) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, x);
+  const unsigned lo = (unsigned)__builtin_amdgcn_mov_dpp((int)(unsigned)u, CTRL, 0xF, 0xF, false);
+  const unsigned hi = (unsigned)__builtin_amdgcn_mov_dpp((int)(unsigned)(u >> 32), CTRL, 0xF, 0xF, false);
+  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+__device__ __forceinline__ double xor16d(double x) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, x);
+  const auto ql = __builtin_amdgcn_permlane16_swap((unsigned)u, (unsigned)u, false, false);
+  const auto qh = __builtin_amdgcn_permlane16_swap((unsigned)(u >> 32), (unsigned)(u >> 32), false, false);
+  const bool up = threadIdx.x & 16;
+  return __builtin_bit_cast(double, ((uint64_t)(up ? qh[0] : qh[1]) << 32) | (up ? ql[0] : ql[1]));
+}
+__device__ __forceinline__ double xor32d(double x) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, x);
+  const auto pl = __builtin_amdgcn_permlane32_swap((unsigned)u, (unsigned)u, false, false);
+  const auto ph = __builtin_amdgcn_permlane32_swap((unsigned)(u >> 32), (unsigned)(u >> 32), false, false);
+  const bool up = threadIdx.x & 32;
+  return __builtin_bit_cast(double, ((uint64_t)(up ? ph[0] : ph[1]) << 32) | (up ? pl[0] : pl[1]));
+}
+// sum / max over the 64 lanes of a wave, every lane receiving the same value
+__device__ __forceinline__ double wave_sum_d(double x) {
+  x += dppd<0xB1>(x);   // quad_perm [1,0,3,2]
+  x += dppd<0x4E>(x);   // quad_perm [2,3,0,1]
+  x += dppd<0x141>(x);  // row_half_mirror
+  x += dppd<0x140>(x);  // row_mirror
+  x += xor16d(x);
+  return x + xor32d(x);
+}
+__device__ __forceinline__ double wave_max_d(double x) {
+  auto mx = [](double a, double b) { return b > a ? b : a; };
+  x = mx(x, dppd<0xB1>(x));
+  x = mx(x, dppd<0x4E>(x));
+  x = mx(x, dppd<0x141>(x));
+  x = mx(x, dppd<0x140>(x));
+  x = mx(x, xor16d(x));
+  return mx(x, xor32d(x));
+}
 // Sum / max over N consecutive aligned lanes (N = 1, 2, 4, 8, 16), every
 // lane of the group receiving the result.
 template <int N>

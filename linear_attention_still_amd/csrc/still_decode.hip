@@ -119,12 +119,6 @@ __device__ __forceinline__ float xorf(float x) {
   static_assert(O == 16 || O == 32, "row-group exchange");
   return O == 16 ? xor16f(x) : xor32f(x);
 }
-template <int N>
-__device__ __forceinline__ double sum_lanes_f64(double x) {
-#pragma unroll
-  for (int o = 1; o < N; o <<= 1) x += __shfl_xor(x, o);
-  return x;
-}
 __device__ __forceinline__ float wave_max(float x) {
   x = row_max<16>(x);
   x = fmaxf(x, xor16f(x));
@@ -617,8 +611,8 @@ void decode_kernel(DecodeArgs a) {
 #pragma unroll
           for (int e = 0; e < 8; ++e) d += (double)(e < 4 ? q0[e] : q1[e - 4]) * (double)frag_at(X.af[kb], e);
         }
-        d += __shfl_xor(d, 16);
-        d += __shfl_xor(d, 32);
+        d += xor16d(d);
+        d += xor32d(d);
         if (g4 == 0 && kk >= sc_first && kk < n) lg[h * W + kk - sc_first] = a.scale64 * d;
       }
     }
@@ -694,12 +688,12 @@ void decode_kernel(DecodeArgs a) {
       tile(B, kk0 + STEP, n, qb, qb2, weight, sc_first);
     }
   };
-  // ---- 3b. NP-Map phi(q_h), phi(k_t) (F read at the start), with the
-  //         wave's state rows and its first softmax-key tile in flight ----
-  // state rows 16 j .. 16 j + 15 for j = wave, wave + waves, ...: lane l
-  // holds columns l * DV .. + DV of each
+  // ---- 3b. NP-Map phi(q_h), phi(k_t), with the wave's state rows and its
+  //         first softmax-key tile in flight --------------------------------
   FRows<T, D, DEC_THREADS> frows;
   frows.load(F);
+  // state rows 16 j .. 16 j + 15 for j = wave, wave + waves, ...: lane l
+  // holds columns l * DV .. + DV of each
   constexpr int SJ = D / (16 * DEC_WAVES);
   using SRow = typename std::conditional<DV == 2, uint2, uint32_t>::type;
   SRow srow[SJ][16];
@@ -754,7 +748,16 @@ void decode_kernel(DecodeArgs a) {
   }
 
   // ---- 3d. softmax keys: logits q.k scaled; the float64 score-window
-  //         logits come from the same key fragments ---------------------
+  //         logits come from the same key fragments; the wave's first
+  //         linear-key tile is loaded meanwhile (up to four heads: with
+  //         eight the registers do not hold it) -----------------------------
+  auto krow_la = [&](int kk) -> uint32_t {
+    return (uint32_t)a.st_ring_phi + (uint32_t)wrap(la_slot + kk) * (D * sizeof(T));
+  };
+  auto vrow_la = [&](int kk) -> uint32_t { return rv_off + (uint32_t)wrap(la_slot + kk) * (D * sizeof(T)); };
+  constexpr bool LA_EARLY = G <= 4;
+  TileRegs TC;
+  if constexpr (LA_EARLY) load_tile(TC, 16 * wave, n_la, krow_la, vrow_la);
   {
     Frag<T> qb[D / 32];
 #pragma unroll
@@ -767,10 +770,6 @@ void decode_kernel(DecodeArgs a) {
 
   // ---- 3e. linear keys: log-weight log(g) + log <phi(q), phi(k)> --------
   if (n_la > 0) {
-    auto krow_la = [&](int kk) -> uint32_t {
-      return (uint32_t)a.st_ring_phi + (uint32_t)wrap(la_slot + kk) * (D * sizeof(T));
-    };
-    auto vrow_la = [&](int kk) -> uint32_t { return rv_off + (uint32_t)wrap(la_slot + kk) * (D * sizeof(T)); };
     // phi(q) as T hi + lo parts (float32 data: exact in one part)
     Frag<T> pb[D / 32], pb2[D / 32];
 #pragma unroll
@@ -784,8 +783,8 @@ void decode_kernel(DecodeArgs a) {
       const bool la = lfl[kk] == 0;
       return (la && w > 0.f) ? lgate + __logf(w) : STILL_NEG_INF;
     };
-    run_tiles(TA, TB, false, n_la, krow_la, vrow_la, pb, sizeof(T) == 2 ? pb2 : (const Frag<T>*)nullptr, weight,
-              INT_MAX);
+    run_tiles(LA_EARLY ? TC : TA, TB, LA_EARLY, n_la, krow_la, vrow_la, pb,
+              sizeof(T) == 2 ? pb2 : (const Frag<T>*)nullptr, weight, INT_MAX);
   }
   // publish per wave: (m, l) per head from lanes r = h, the value slices
 #pragma unroll
@@ -806,22 +805,15 @@ void decode_kernel(DecodeArgs a) {
       const double* x = lg + h * W;
       double mx = -__builtin_huge_val();
       for (int j = lane; j < n; j += 64) mx = x[j] > mx ? x[j] : mx;
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const double y = __shfl_xor(mx, o);
-        mx = y > mx ? y : mx;
-      }
+      mx = wave_max_d(mx);
       double za = 0.0, zo = 0.0;
       for (int j = lane; j < n; j += 64) {
         const double e = exp(x[j] - mx);
         za += e;
         if (j != n - 1) zo += e;
       }
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        za += __shfl_xor(za, o);
-        zo += __shfl_xor(zo, o);
-      }
+      za = wave_sum_d(za);
+      zo = wave_sum_d(zo);
       if (lane == 0) {
         const double p = exp(x[n - 1] - mx) / za, pn = zo / za;
         double sc = 0.0;

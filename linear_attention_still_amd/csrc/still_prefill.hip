@@ -286,22 +286,15 @@ __device__ __forceinline__ double score_f64(const PrefillArgs& a, int b, int kv,
     const double* x = lg + h * W;
     double mx = -__builtin_huge_val();
     for (int j = lane; j < n; j += 64) mx = x[j] > mx ? x[j] : mx;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const double y = __shfl_xor(mx, o);
-      mx = y > mx ? y : mx;
-    }
+    mx = wave_max_d(mx);
     double za = 0.0, zo = 0.0;
     for (int j = lane; j < n; j += 64) {
       const double e = exp(x[j] - mx);
       za += e;
       if (j != n - 1) zo += e;
     }
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      za += __shfl_xor(za, o);
-      zo += __shfl_xor(zo, o);
-    }
+    za = wave_sum_d(za);
+    zo = wave_sum_d(zo);
     if (lane == 0) {
       const double p = exp(x[n - 1] - mx) / za, pn = zo / za;
       double sc = 0.0;
