@@ -560,10 +560,14 @@ void decode_kernel(DecodeArgs a) {
   // rows r < G of src (float32 in LDS), zero above; with a split, the part
   // the first rounding lost
   auto qfrag = [&](const float* src, int kb, bool lo_part) {
+    // every lane reads (rows past G read row 0, then drop it): no branch
+    // around the LDS reads
+    const float* row = src + (r16 < G ? r16 : 0) * D + 32 * kb + 8 * g4;
+    const f32x4 x0 = *reinterpret_cast<const f32x4*>(row), x1 = *reinterpret_cast<const f32x4*>(row + 4);
     float v[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const float x = r16 < G ? src[r16 * D + 32 * kb + 8 * g4 + e] : 0.f;
+      const float x = r16 < G ? (e < 4 ? x0[e] : x1[e - 4]) : 0.f;
       v[e] = lo_part ? x - to_f32(from_f32<T>(x)) : x;
     }
     return frag_from<T>(f32x4{v[0], v[1], v[2], v[3]}, f32x4{v[4], v[5], v[6], v[7]});
@@ -627,7 +631,9 @@ void decode_kernel(DecodeArgs a) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int kk = kk0 + 4 * g4 + i;
-      c[i] = (r16 < G && kk < n) ? weight(c[i], kk) : STILL_NEG_INF;
+      const bool ok = r16 < G && kk < n;
+      const float w = weight(c[i], ok ? kk : kk0);  // evaluated in every lane: no branch
+      c[i] = ok ? w : STILL_NEG_INF;
       mx = fmaxf(mx, c[i]);
     }
     mx = fmaxf(mx, xor16f(mx));
