@@ -70,7 +70,8 @@ struct DecLds {
   // union member 1 (NP-Map and fold): xs, us, ph, vs [8][D] and red8
   // [waves][8][D] f32 in the boundary kernel; xs, us, ph [G+1][D] and red8
   // [waves][G+1][D] per token
-  static constexpr size_t fold_bytes = (size_t)(4 + BND_WAVES) * 8 * D * 4;
+  static constexpr int FOLD_ROWS = 8;  // rows per fold group of the boundary kernel
+  static constexpr size_t fold_bytes = (size_t)(4 + BND_WAVES) * FOLD_ROWS * D * 4;
   static constexpr size_t mapg_bytes = (size_t)(3 + DEC_WAVES) * (G + 1) * D * 4;
   // union member 2 (value and state partial sums): f32 [2][waves][G][D]
   static constexpr size_t red_bytes = (size_t)2 * DEC_WAVES * G * D * 4;
@@ -126,7 +127,7 @@ __device__ __forceinline__ float wave_max(float x) {
 }
 __device__ __forceinline__ float wave_sum(float x) { return sum_lanes<64>(x); }
 
-// NP-Map [P3 "NP-Map: Norm-Preserving Feature Map"] of NR <= 9 rows, reading:
+// NP-Map [P3 "NP-Map: Norm-Preserving Feature Map"] of NR <= 16 rows, reading:
 // ||x|| * softmax(x F) / ||softmax(x F)|| with exact expf. u = x F with the rows
 // of F read once as 8-byte vectors (all loads of a lane in flight at once),
 // partial sums over the F rows reduced across lanes and then across waves
@@ -262,7 +263,7 @@ __global__ __launch_bounds__(BND_THREADS) void decode_boundary_kernel(DecodeArgs
   int* ibuf = reinterpret_cast<int*>(smem + LD::ibuf);
   double* d64 = reinterpret_cast<double*>(smem + LD::d64);
   float* rowst = reinterpret_cast<float*>(smem + LD::rowst);
-  constexpr int FR = 8;  // rows per fold group
+  constexpr int FR = LD::FOLD_ROWS;  // rows per fold group
   float* xs = reinterpret_cast<float*>(smem + LD::uni);  // [FR][D]
   float* us = xs + FR * D;
   float* ph = us + FR * D;
@@ -316,18 +317,30 @@ __global__ __launch_bounds__(BND_THREADS) void decode_boundary_kernel(DecodeArgs
 #pragma unroll
   for (int q2 = 0; q2 < PER; ++q2) dacc[q2] = 0.f;
   float dz = 0.f;
+  FRows<T, D, BND_THREADS> fr;  // F rows, read once for every group
+  fr.load(F);
+  const __amdgpu_buffer_rsrc_t st_r = make_rsrc(st, (uint32_t)a.st_unit);
   for (int g0 = f_lo; g0 < f_hi; g0 += FR) {
     const int n = min(FR, f_hi - g0);
-    for (int e = tid; e < FR * D; e += BND_THREADS) {
-      const int r = e / D, i = e % D, pos = g0 + r;
+    // rows of the group (unkept ones; absent or kept rows read zeros past
+    // the state's range): buffer loads, all issued before any is used
+    constexpr int PT = FR * D / BND_THREADS;
+    T kx[PT], vx[PT];
+#pragma unroll
+    for (int u = 0; u < PT; ++u) {
+      const int e = tid + u * BND_THREADS, r = e / D, i = e % D, pos = g0 + r;
       const int slot = pos % R;
-      const bool use = r < n && ring_flag[slot] == 0;
-      xs[e] = use ? to_f32(ring_k[(size_t)slot * D + i]) : 0.f;
-      vs[e] = use ? to_f32(ring_v[(size_t)slot * D + i]) : 0.f;
+      const bool use = (ring_flag[slot] == 0) & (r < n);  // slot is in range: no branch
+      const uint32_t off = (uint32_t)(slot * D + i) * sizeof(T);
+      kx[u] = ld_elem_buf<T>(st_r, use ? (uint32_t)a.st_ring_k + off : (uint32_t)a.st_unit);
+      vx[u] = ld_elem_buf<T>(st_r, use ? (uint32_t)a.st_ring_v + off : (uint32_t)a.st_unit);
+    }
+#pragma unroll
+    for (int u = 0; u < PT; ++u) {
+      xs[tid + u * BND_THREADS] = to_f32(kx[u]);
+      vs[tid + u * BND_THREADS] = to_f32(vx[u]);
     }
     __syncthreads();
-    FRows<T, D, BND_THREADS> fr;
-    fr.load(F);
     np_map_vec<T, D, FR, BND_THREADS>(fr, xs, red8, us, ph, rowst);
     // thread tid owns S[i][jv] for jv = tid % D and i = tid / D + q2 * (512 / D)
 #pragma unroll 1
