@@ -454,6 +454,11 @@ __device__ __forceinline__ float row_max(float x) {
   return x;
 }
 
+// Maximum without the quieting of signalling NaN inputs that fmaxf costs
+// (an extra v_max per operand not known to be canonical, e.g. an MFMA
+// result); a NaN operand gives NaN. For values that are never NaN.
+__device__ __forceinline__ float fmax_nn(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+
 // Sum / max over the four lanes sharing r (lanes r, r+16, r+32, r+48).
 __device__ __forceinline__ float sum_over_g(float x) {
   x += xor16f(x);
@@ -461,8 +466,8 @@ __device__ __forceinline__ float sum_over_g(float x) {
   return x;
 }
 __device__ __forceinline__ float max_over_g(float x) {
-  x = fmaxf(x, xor16f(x));
-  x = fmaxf(x, xor32f(x));
+  x = fmax_nn(x, xor16f(x));
+  x = fmax_nn(x, xor32f(x));
   return x;
 }
 

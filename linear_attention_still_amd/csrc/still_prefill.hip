@@ -490,9 +490,12 @@ struct BlkPtr {
   // Fragment of V^T for d_v tile dt and key half kb2: lane (r, g) holds
   // V[32 kb2 + perm(g, s)][16 dt + r], s = 0..7 (A operand of O^T += V^T P^T,
   // B operand of the fold).
-  __device__ Frag<H> ld_v(int dt, int kb2) const {
+  // (lane: the caller's lane index, so that the lane-dependent part of the
+  // address is computed once where the caller reads many fragments)
+  __device__ Frag<H> ld_v(int dt, int kb2) const { return ld_v(dt, kb2, opaque_tid() & 63); }
+  __device__ Frag<H> ld_v(int dt, int kb2, int lane) const {
     using B_ = Blk<T, D>;
-    const int lane = opaque_tid() & 63, r16 = lane & 15, g4 = lane >> 4;
+    const int r16 = lane & 15, g4 = lane >> 4;
     if constexpr (B_::TR) {
       const H* p = VTs + (32 * kb2 + 4 * g4 + (r16 >> 2)) * B_::VR + 16 * dt + 4 * (r16 & 3);
       return tr_frag(p, 16 * B_::VR);
@@ -501,9 +504,10 @@ struct BlkPtr {
     }
   }
   // A fragment of phi(K) (rows = keys 16 kt + r, depth = features 32 bb + perm(g, s)).
-  __device__ Frag<H> ld_wk(int kt, int bb) const {
+  __device__ Frag<H> ld_wk(int kt, int bb) const { return ld_wk(kt, bb, opaque_tid() & 63); }
+  __device__ Frag<H> ld_wk(int kt, int bb, int lane) const {
     using B_ = Blk<T, D>;
-    const int lane = opaque_tid() & 63, r16 = lane & 15, g4 = lane >> 4;
+    const int r16 = lane & 15, g4 = lane >> 4;
     if constexpr (B_::TR) {
       const H* p = WF + (32 * bb + 4 * g4 + (r16 >> 2)) * B_::FKS + 16 * kt + 4 * (r16 & 3);
       return tr_frag(p, 16 * B_::FKS);
@@ -1255,24 +1259,31 @@ __global__ __launch_bounds__(512) void attend_kernel(PrefillArgs a) {
         const uint64_t sa_m = valid_m & (~low_bits(min(t - W + 1, cC) - blo) | selbits);
         const uint64_t sa_s = sa_m >> (4 * g4), la_s = (valid_m & ~sa_m) >> (4 * g4);
         const float inv_scale2 = 1.f / scale2;
+        f32x4 wt[HPW][4];
+        if (la_blk) {
+          // <phi(k), phi(q)> of every key and row: each phi(K) fragment read
+          // serves all heads of the wave
 #pragma unroll
-        for (int j = 0; j < HPW; ++j) {
-          f32x4 wt[4];
-          if (la_blk) {
+          for (int kt = 0; kt < 4; ++kt) {
 #pragma unroll
-            for (int kt = 0; kt < 4; ++kt) {
-              wt[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int j = 0; j < HPW; ++j) wt[j][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-              for (int bb = 0; bb < D / 32; ++bb) mma(wt[kt], Pb.ld_wk(kt, bb), pq[j][bb]);
+            for (int bb = 0; bb < D / 32; ++bb) {
+              const Frag<H> wk = Pb.ld_wk(kt, bb, lane);
+#pragma unroll
+              for (int j = 0; j < HPW; ++j) mma(wt[j][kt], wk, pq[j][bb]);
             }
           }
+        }
+#pragma unroll
+        for (int j = 0; j < HPW; ++j) {
 #pragma unroll
           for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
               float x = ((sa_s >> (16 * kt + i)) & 1ull) ? st[j][kt][i] : STILL_NEG_INF;
               if (la_blk) {
-                const float w = wt[kt][i];
+                const float w = wt[j][kt][i];
                 const bool la = ((la_s >> (16 * kt + i)) & 1ull) && w > 0.f;
                 x = la ? (lgate2[j] + log2_acc<T>(fmaxf(w, 1e-37f))) * inv_scale2 : x;
               }
@@ -1284,17 +1295,27 @@ __global__ __launch_bounds__(512) void attend_kernel(PrefillArgs a) {
       for (int j = 0; j < HPW; ++j)
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt)
-          mx[j] = fmaxf(mx[j], fmaxf(fmaxf(st[j][kt][0], st[j][kt][1]), fmaxf(st[j][kt][2], st[j][kt][3])));
+          mx[j] = fmax_nn(mx[j], fmax_nn(fmax_nn(st[j][kt][0], st[j][kt][1]), fmax_nn(st[j][kt][2], st[j][kt][3])));
       Frag<H> pf[HPW][2];
 #pragma unroll
       for (int j = 0; j < HPW; ++j) {
         const float mxj = max_over_g(mx[j]) * scale2;
-        const float mn = fmaxf(mrun[j], mxj);
-        // rows with nothing visible so far keep m = -inf, O = 0, l = 0; the
-        // exponent's offset is finite either way (exp2(-inf) = 0)
-        const float al = mrun[j] == STILL_NEG_INF ? 0.f : exp2_acc<T>(mrun[j] - mn);
-        const float nmn = mn == STILL_NEG_INF ? 0.f : -mn;
-        mrun[j] = mn;
+        // The offset m is moved only when some row's block maximum passes it
+        // by more than 2^RESCALE_SLACK (wave-uniform test): weights then stay
+        // below 2^8, well inside fp16, and O and l are rescaled on few blocks
+        // instead of on almost every one. y = O / l does not depend on m.
+        // Rows with nothing visible so far keep m = -inf, O = 0, l = 0; the
+        // exponent's offset is finite either way (exp2(-inf) = 0).
+        constexpr float RESCALE_SLACK = 8.f;
+        if (__builtin_amdgcn_ballot_w64(mxj > mrun[j] + RESCALE_SLACK)) {
+          const float mn = fmax_nn(mrun[j], mxj);
+          const float al = mrun[j] == STILL_NEG_INF ? 0.f : exp2_acc<T>(mrun[j] - mn);
+          mrun[j] = mn;
+          lacc[j] *= al;
+#pragma unroll
+          for (int dt = 0; dt < D / 16; ++dt) O[j][dt] *= al;
+        }
+        const float nmn = mrun[j] == STILL_NEG_INF ? 0.f : -mrun[j];
         f32x4 pv[4];
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt)
@@ -1304,18 +1325,13 @@ __global__ __launch_bounds__(512) void attend_kernel(PrefillArgs a) {
         // through a ones-row MFMA
         pf[j][0] = frag_from<H>(pv[0], pv[1]);
         pf[j][1] = frag_from<H>(pv[2], pv[3]);
-        if (__builtin_amdgcn_ballot_w64(al != 1.f)) {  // wave-uniform: some max moved
-          lacc[j] *= al;
-#pragma unroll
-          for (int dt = 0; dt < D / 16; ++dt) O[j][dt] *= al;
-        }
         const Frag<H> one = ones_frag<H>();
         mma(lacc[j], one, pf[j][0]);
         mma(lacc[j], one, pf[j][1]);
       }
 #pragma unroll
       for (int dt = 0; dt < D / 16; ++dt) {
-        const Frag<H> v0 = Pb.ld_v(dt, 0), v1 = Pb.ld_v(dt, 1);
+        const Frag<H> v0 = Pb.ld_v(dt, 0, lane), v1 = Pb.ld_v(dt, 1, lane);
 #pragma unroll
         for (int j = 0; j < HPW; ++j) {
           mma(O[j][dt], v0, pf[j][0]);
