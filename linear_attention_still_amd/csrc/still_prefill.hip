@@ -516,8 +516,9 @@ struct BlkPtr {
     }
   }
   // fragment (feature tile ft, d block kb) of F^T: B operand of X F
-  __device__ const T* ft(int ftile, int kb) const {
-    return FT + ((size_t)(ftile * (D / 32) + kb) * 64 + (opaque_tid() & 63)) * 8;
+  __device__ const T* ft(int ftile, int kb) const { return ft(ftile, kb, opaque_tid() & 63); }
+  __device__ const T* ft(int ftile, int kb, int lane) const {
+    return FT + ((size_t)(ftile * (D / 32) + kb) * 64 + lane) * 8;
   }
 };
 
@@ -698,7 +699,7 @@ __device__ __forceinline__ void np_map_tile(const BlkPtr<T, D>& P, const Frag<T>
     out[ft] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kb = 0; kb < D / 32; ++kb)
-      mma(out[ft], ld_frag(P.ft(ft, kb)), xf[kb]);
+      mma(out[ft], ld_frag(P.ft(ft, kb, lane)), xf[kb]);
 #pragma unroll
     for (int i = 0; i < 4; ++i) mx = fmaxf(mx, out[ft][i]);
   }
@@ -723,6 +724,7 @@ __device__ __forceinline__ void np_map_tile(const BlkPtr<T, D>& P, const Frag<T>
 template <typename T, int D, int NX>
 __device__ __forceinline__ void np_map_tiles(const BlkPtr<T, D>& P, const Frag<T> (&xf)[NX][D / 32],
                                              f32x4 (&out)[NX][D / 16]) {
+  const int lane = opaque_tid() & 63;
   float xn2[NX], mx[NX], ss[NX];
 #pragma unroll
   for (int x = 0; x < NX; ++x) {
@@ -739,7 +741,7 @@ __device__ __forceinline__ void np_map_tiles(const BlkPtr<T, D>& P, const Frag<T
     for (int x = 0; x < NX; ++x) out[x][ft] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kb = 0; kb < D / 32; ++kb) {
-      const Frag<T> f = ld_frag(P.ft(ft, kb));
+      const Frag<T> f = ld_frag(P.ft(ft, kb, lane));
 #pragma unroll
       for (int x = 0; x < NX; ++x) mma(out[x][ft], f, xf[x][kb]);
     }
@@ -873,7 +875,7 @@ __device__ __forceinline__ void fold_tile(const BlkPtr<T, D>& P, const f32x4 (&p
     split2_frag<H>(x0, x1, hi, lo);
 #pragma unroll
     for (int vt = 0; vt < D / 16; ++vt) {
-      const Frag<H> bv = P.ld_v(vt, kb2);
+      const Frag<H> bv = P.ld_v(vt, kb2, lane);
       mma(acc[vt], hi, bv);
       if constexpr (sizeof(H) == 2) mma(acc[vt], lo, bv);
     }
@@ -1132,72 +1134,109 @@ __global__ __launch_bounds__(512) void attend_kernel(PrefillArgs a) {
     float mrun[HPW];
     f32x4 lacc[HPW];  // running sums, the same in all four entries (ones-row MFMA)
     {
-      Frag<T> phq[HPW][D / 32], phl[HPW][D / 32];
+      // Readout o = S^T phi(q) / dz, dz = z . phi(q). 16-bit data: one fp16
+      // MFMA per tile on a rescaled pair, row i of S times 1/z_i and phi(q)_i
+      // times z_i / dz. |S_ij| <= z_i max|v| (S and z sum the same
+      // non-negative features), so the scaled state is bounded by the largest
+      // value magnitude and the scaled features are weights in [0, 1] that
+      // sum to 1: both sit well inside fp16, and each product carries about
+      // 2^-10 relative error. float32 data: the float32 MFMA on S and phi(q).
+      [[maybe_unused]] Frag<H> pz[HPW][D / 32];
+      [[maybe_unused]] Frag<T> phq[HPW][D / 32];
       float dz[HPW];
       {
         f32x4 ph[HPW][D / 16];
         np_map_tiles<T, D, HPW>(P, qf, ph);
 #pragma unroll
-        for (int j = 0; j < HPW; ++j) {
-          float z_ = 0.f;
-#pragma unroll
-          for (int ft = 0; ft < D / 16; ++ft)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) z_ += ph[j][ft][i] * (float)P.zs[16 * ft + 4 * g4 + i];
-          dz[j] = sum_over_g(z_);
+        for (int j = 0; j < HPW; ++j)
 #pragma unroll
           for (int bb = 0; bb < D / 32; ++bb) {
-            split2_frag<T>(ph[j][2 * bb], ph[j][2 * bb + 1], phq[j][bb], phl[j][bb]);
             pq[j][bb] = frag_from<H>(ph[j][2 * bb], ph[j][2 * bb + 1]);
+            if constexpr (sizeof(T) == 4) phq[j][bb] = frag_from<T>(ph[j][2 * bb], ph[j][2 * bb + 1]);
+          }
+        float z_[HPW];
+#pragma unroll
+        for (int j = 0; j < HPW; ++j) z_[j] = 0.f;
+#pragma unroll
+        for (int ft = 0; ft < D / 16; ++ft)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float zi = (float)P.zs[16 * ft + 4 * g4 + i];
+#pragma unroll
+            for (int j = 0; j < HPW; ++j) {
+              ph[j][ft][i] *= zi;  // z_i phi(q)_i
+              z_[j] += ph[j][ft][i];
+            }
+          }
+#pragma unroll
+        for (int j = 0; j < HPW; ++j) {
+          dz[j] = sum_over_g(z_[j]);
+          if constexpr (sizeof(T) == 2) {
+            const float inv = dz[j] > 0.f ? 1.f / dz[j] : 0.f;
+#pragma unroll
+            for (int bb = 0; bb < D / 32; ++bb) pz[j][bb] = frag_from<H>(ph[j][2 * bb] * inv, ph[j][2 * bb + 1] * inv);
           }
         }
       }
-      // S as hi/lo bf16 fragments, split once and shared by every wave, in
-      // two halves of the d_v tiles (the split region holds one half)
-      constexpr int HP = B_::NPAIR / 2;
+      if constexpr (sizeof(T) == 2) {
+        // 1/z_i per state row (kmax is scratch of block_phi, free here)
+        if (tid < D) {
+          const double z = P.zs[tid];
+          P.kmax[tid] = z > 0.0 ? (float)(1.0 / z) : 0.f;
+        }
+        __syncthreads();
+        // the scaled state as fp16 fragments, split once and shared by
+        // every wave (the region of the key / value blocks is free here)
+        H* RSh = reinterpret_cast<H*>(P.RS);
+        for (int e = tid; e < B_::NPAIR * 64; e += 512) {
+          const int pl = e >> 6, ln = e & 63, g = ln >> 4, bb = pl % (D / 32);
+          const float* sp = P.SP + ((size_t)2 * pl * 64 + ln) * 4;
+          f32x4 x0 = *reinterpret_cast<const f32x4*>(sp), x1 = *reinterpret_cast<const f32x4*>(sp + 256);
 #pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        for (int e = tid; e < HP * 64; e += 512) {
-          const int pl = e >> 6, ln = e & 63;
-          const float* sp = P.SP + ((size_t)2 * (half * HP + pl) * 64 + ln) * 4;
-          Frag<T> sh, sl;
-          split2_frag<T>(*reinterpret_cast<const f32x4*>(sp), *reinterpret_cast<const f32x4*>(sp + 256), sh, sl);
-          st_frag(P.RS + ((size_t)(2 * pl) * 64 + ln) * 8, sh);
-          st_frag(P.RS + ((size_t)(2 * pl + 1) * 64 + ln) * 8, sl);
+          for (int i = 0; i < 4; ++i) {
+            x0[i] *= P.kmax[32 * bb + 4 * g + i];
+            x1[i] *= P.kmax[32 * bb + 16 + 4 * g + i];
+          }
+          st_frag(RSh + ((size_t)pl * 64 + ln) * 8, frag_from<H>(x0, x1));
         }
         __syncthreads();
 #pragma unroll
-        for (int dh = 0; dh < D / 32; ++dh) {
-          const int dt = half * (D / 32) + dh;
+        for (int dt = 0; dt < D / 16; ++dt) {
 #pragma unroll
           for (int j = 0; j < HPW; ++j) O[j][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int bb = 0; bb < D / 32; ++bb) {
-            // S^T phi(q) to ~2^-16 relative: hi*hi + lo*hi + hi*lo
-            const int pl = dh * (D / 32) + bb;
-            const Frag<T> sh = ld_frag(P.RS + ((size_t)(2 * pl) * 64 + lane) * 8);
+            const Frag<H> sf = ld_frag(RSh + ((size_t)(dt * (D / 32) + bb) * 64 + lane) * 8);
 #pragma unroll
-            for (int j = 0; j < HPW; ++j) mma(O[j][dt], sh, phq[j][bb]);
-            if constexpr (sizeof(T) == 2) {
-              const Frag<T> sl = ld_frag(P.RS + ((size_t)(2 * pl + 1) * 64 + lane) * 8);
-#pragma unroll
-              for (int j = 0; j < HPW; ++j) {
-                mma(O[j][dt], sl, phq[j][bb]);
-                mma(O[j][dt], sh, phl[j][bb]);
-              }
-            }
+            for (int j = 0; j < HPW; ++j) mma(O[j][dt], sf, pz[j][bb]);
           }
         }
-        if (half == 0) __syncthreads();  // the region is split into again
+      } else {
+        // float32 S fragments straight from the state region
+#pragma unroll
+        for (int dt = 0; dt < D / 16; ++dt) {
+#pragma unroll
+          for (int j = 0; j < HPW; ++j) O[j][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int bb = 0; bb < D / 32; ++bb) {
+            const int pl = dt * (D / 32) + bb;
+            const Frag<T> sf = frag_from<T>(*reinterpret_cast<const f32x4*>(P.pair(pl, 0)),
+                                            *reinterpret_cast<const f32x4*>(P.pair(pl, 1)));
+#pragma unroll
+            for (int j = 0; j < HPW; ++j) mma(O[j][dt], sf, phq[j][bb]);
+          }
+        }
       }
 #pragma unroll
       for (int j = 0; j < HPW; ++j) {
         if (gg[j] > 0.f && dz[j] > 0.f) {
           mrun[j] = log2_acc<T>(gg[j] * dz[j]);
           lacc[j] = f32x4{1.f, 1.f, 1.f, 1.f};
-          const float inv = 1.f / dz[j];
+          if constexpr (sizeof(T) == 4) {
+            const float inv = 1.f / dz[j];
 #pragma unroll
-          for (int dt = 0; dt < D / 16; ++dt) O[j][dt] *= inv;
+            for (int dt = 0; dt < D / 16; ++dt) O[j][dt] *= inv;
+          }
         } else {
           mrun[j] = STILL_NEG_INF;
           lacc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
