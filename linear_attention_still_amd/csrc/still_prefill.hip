@@ -122,10 +122,11 @@ __global__ __launch_bounds__(256) void score_kernel(PrefillArgs a) {
   // keys into LDS; the largest squared key norm (for the error bound) from
   // the same vectors: D / VEC consecutive lanes hold one row
   float kmx = 0.f;
-  // up to eight 16-byte loads per thread in flight at a time; rows outside
+  // up to nine 16-byte loads per thread in flight at a time (all of them for
+  // a 64-key window and chunk at d = 128); rows outside
   // [0, min(L, cC + C)) read past the buffer range (zeros)
   const __amdgpu_buffer_rsrc_t krs = make_rsrc(kg, qbytes);
-  constexpr int NB = 8;
+  constexpr int NB = 9;
   for (int base = 0; base < nvec; base += NB * 256) {  // whole rows per lane group
     uint4 val[NB];
 #pragma unroll
@@ -168,36 +169,47 @@ __global__ __launch_bounds__(256) void score_kernel(PrefillArgs a) {
     qn2 = sum_over_g(qn2);
     float mrun = STILL_NEG_INF, zall = 0.f, zoth = 0.f, sself = STILL_NEG_INF;
     const int kt_lo = qt, kt_hi = qt + (W + 14) / 16;
-    for (int kt = kt_lo; kt <= kt_hi; ++kt) {
-      f32x4 s = {0.f, 0.f, 0.f, 0.f};
+    // key tiles in groups of NG: the group's logits first (its MFMAs back
+    // to back), then one running-max update and the exponentials
+    constexpr int NG = 5;
+    for (int k0 = kt_lo; k0 <= kt_hi; k0 += NG) {
+      f32x4 sg[NG];
 #pragma unroll
-      for (int kb = 0; kb < D / 32; ++kb)
-        mma(s, ld_frag(Ks + (16 * kt + r16) * KS + 32 * kb + 8 * g4), qf[kb]);
-      float lv[4];
+      for (int u = 0; u < NG; ++u) {
+        sg[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (k0 + u <= kt_hi) {  // uniform
+#pragma unroll
+          for (int kb = 0; kb < D / 32; ++kb)
+            mma(sg[u], ld_frag(Ks + (16 * (k0 + u) + r16) * KS + 32 * kb + 8 * g4), qf[kb]);
+        }
+      }
       float mx = STILL_NEG_INF;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int j = kbase + 16 * kt + 4 * g4 + i;
-        const bool ok = j >= 0 && j <= t && j >= t - W + 1;
-        lv[i] = ok ? s[i] * a.scale : STILL_NEG_INF;
-        if (ok && j == t) sself = lv[i];
-        mx = fmaxf(mx, lv[i]);
-      }
-      const float mn = fmaxf(mrun, mx);
-      if (mn != STILL_NEG_INF) {
-        const float al = (mrun == STILL_NEG_INF) ? 0.f : __expf(mrun - mn);
-        zall *= al;
-        zoth *= al;
+      for (int u = 0; u < NG; ++u)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          if (lv[i] == STILL_NEG_INF) continue;
-          const float e = __expf(lv[i] - mn);
-          zall += e;
-          const int j = kbase + 16 * kt + 4 * g4 + i;
-          if (j != t) zoth += e;
+          const int j = kbase + 16 * (k0 + u) + 4 * g4 + i;
+          const bool ok = k0 + u <= kt_hi && j >= 0 && j <= t && j >= t - W + 1;
+          sg[u][i] = ok ? sg[u][i] * a.scale : STILL_NEG_INF;
+          sself = ok && j == t ? sg[u][i] : sself;
+          mx = fmaxf(mx, sg[u][i]);
         }
-        mrun = mn;
-      }
+      const float mn = fmaxf(mrun, mx);
+      // rows with nothing visible so far keep m = -inf and zero sums
+      const float al = mrun == STILL_NEG_INF ? 0.f : __expf(mrun - mn);
+      const float mo = mn == STILL_NEG_INF ? 0.f : mn;
+      float ea = 0.f, eo = 0.f;
+#pragma unroll
+      for (int u = 0; u < NG; ++u)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float e = __expf(sg[u][i] - mo);  // 0 for masked keys
+          ea += e;
+          eo += kbase + 16 * (k0 + u) + 4 * g4 + i != t ? e : 0.f;
+        }
+      zall = zall * al + ea;
+      zoth = zoth * al + eo;
+      mrun = mn;
     }
 #pragma unroll
     for (int off = 16; off <= 32; off <<= 1) {
