@@ -629,10 +629,11 @@ __device__ __forceinline__ void issue_block(BlkRegs<T, D, NT>& R, __amdgpu_buffe
 
 // Writes an issued block to LDS: keys row-major into Ks, values transposed
 // (as H) into VTs with keys 2a, 2a+1 in adjacent permuted columns, the kept
-// flags as a 64-bit mask, the fold mask and the keys' squared norms.
+// flags as a 64-bit mask, the fold mask and (with want_norm, uniform: for
+// blocks whose NP-Map features are computed) the keys' squared norms.
 template <typename T, int D, int NT>
 __device__ __forceinline__ void commit_block(const BlkPtr<T, D>& P, const BlkRegs<T, D, NT>& R,
-                                             int fold_lo, int fold_hi) {
+                                             int fold_lo, int fold_hi, bool want_norm = true) {
   using B_ = Blk<T, D>;
   using BR = BlkRegs<T, D, NT>;
   typedef typename HalfOf<T>::type H;
@@ -653,6 +654,7 @@ __device__ __forceinline__ void commit_block(const BlkPtr<T, D>& P, const BlkReg
     if (BR::KIT * NT > 64 * CPR && idx >= 64 * CPR) break;  // uniform per wave
     const int kk = idx / CPR, col = (idx % CPR) * VEC;
     *reinterpret_cast<uint4*>(P.Ks + kk * B_::KS + col) = R.k[it];
+    if (!want_norm) continue;
     // |k|^2 for the feature map: CPR consecutive lanes hold one row
     const T* ke = reinterpret_cast<const T*>(&R.k[it]);
     float q2 = 0.f;
@@ -1412,7 +1414,7 @@ __global__ __launch_bounds__(512) void attend_kernel(PrefillArgs a) {
       const bool band = i < n_band_blk;  // uniform
       const int blo = band ? band_lo + 64 * i : 64 * (i - n_band_blk);
       __syncthreads();  // the previous block (or the readout) is done with LDS
-      commit_block<T, D, 512>(P, R, band ? fold_lo : 0, band ? fold_hi : 0);
+      commit_block<T, D, 512>(P, R, band ? fold_lo : 0, band ? fold_hi : 0, band);
       if (i + 1 < n_band_blk)
         issue_block<T, D, 512>(R, kr, vr, kv_bytes, sfr, blk_range(blo + 64, band_hi));
       else if (i + 1 < nblk)
