@@ -437,6 +437,11 @@ __device__ __forceinline__ double wave_max_d(double x) {
 }
 // Sum / max over N consecutive aligned lanes (N = 1, 2, 4, 8, 16), every
 // lane of the group receiving the result.
+// Maximum without the quieting of signalling NaN inputs that fmaxf costs
+// (an extra v_max per operand not known to be canonical, e.g. an MFMA
+// result); a NaN operand gives NaN. For values that are never NaN.
+__device__ __forceinline__ float fmax_nn(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+
 template <int N>
 __device__ __forceinline__ float row_sum(float x) {
   if constexpr (N >= 2) x += dppf<0xB1>(x);   // quad_perm [1,0,3,2]
@@ -447,17 +452,12 @@ __device__ __forceinline__ float row_sum(float x) {
 }
 template <int N>
 __device__ __forceinline__ float row_max(float x) {
-  if constexpr (N >= 2) x = fmaxf(x, dppf<0xB1>(x));
-  if constexpr (N >= 4) x = fmaxf(x, dppf<0x4E>(x));
-  if constexpr (N >= 8) x = fmaxf(x, dppf<0x141>(x));
-  if constexpr (N >= 16) x = fmaxf(x, dppf<0x140>(x));
+  if constexpr (N >= 2) x = fmax_nn(x, dppf<0xB1>(x));
+  if constexpr (N >= 4) x = fmax_nn(x, dppf<0x4E>(x));
+  if constexpr (N >= 8) x = fmax_nn(x, dppf<0x141>(x));
+  if constexpr (N >= 16) x = fmax_nn(x, dppf<0x140>(x));
   return x;
 }
-
-// Maximum without the quieting of signalling NaN inputs that fmaxf costs
-// (an extra v_max per operand not known to be canonical, e.g. an MFMA
-// result); a NaN operand gives NaN. For values that are never NaN.
-__device__ __forceinline__ float fmax_nn(float a, float b) { return __builtin_elementwise_maximum(a, b); }
 
 // Sum / max over the four lanes sharing r (lanes r, r+16, r+32, r+48).
 __device__ __forceinline__ float sum_over_g(float x) {

@@ -122,8 +122,8 @@ __device__ __forceinline__ float xorf(float x) {
 }
 __device__ __forceinline__ float wave_max(float x) {
   x = row_max<16>(x);
-  x = fmaxf(x, xor16f(x));
-  return fmaxf(x, xor32f(x));
+  x = fmax_nn(x, xor16f(x));
+  return fmax_nn(x, xor32f(x));
 }
 __device__ __forceinline__ float wave_sum(float x) { return sum_lanes<64>(x); }
 
@@ -210,7 +210,7 @@ __device__ __forceinline__ void np_map_vec(const FRows<T, D, NT>& FR_, const flo
   for (int r = wave; r < NR; r += NW) {
     float mx = STILL_NEG_INF, xn = 0.f;
     for (int j = lane; j < D; j += 64) {
-      mx = fmaxf(mx, us[r * D + j]);
+      mx = fmax_nn(mx, us[r * D + j]);
       xn += xs[r * D + j] * xs[r * D + j];
     }
     mx = wave_max(mx);
@@ -647,11 +647,11 @@ void decode_kernel(DecodeArgs a) {
       const bool ok = r16 < G && kk < n;
       const float w = weight(c[i], ok ? kk : kk0);  // evaluated in every lane: no branch
       c[i] = ok ? w : STILL_NEG_INF;
-      mx = fmaxf(mx, c[i]);
+      mx = fmax_nn(mx, c[i]);
     }
-    mx = fmaxf(mx, xor16f(mx));
-    mx = fmaxf(mx, xor32f(mx));
-    const float mn = fmaxf(mh, mx);
+    mx = fmax_nn(mx, xor16f(mx));
+    mx = fmax_nn(mx, xor32f(mx));
+    const float mn = fmax_nn(mh, mx);
     const float al = (mh == STILL_NEG_INF || mn == STILL_NEG_INF) ? 0.f : __expf(mh - mn);
     float ls = 0.f;
 #pragma unroll
@@ -851,7 +851,7 @@ void decode_kernel(DecodeArgs a) {
     const float lws = (g > 0.f && dz > 0.f) ? __logf(g * dz) : STILL_NEG_INF;
     float mx = lws;
 #pragma unroll
-    for (int w = 0; w < DEC_WAVES; ++w) mx = fmaxf(mx, mlw[(w * G + h) * 2]);
+    for (int w = 0; w < DEC_WAVES; ++w) mx = fmax_nn(mx, mlw[(w * G + h) * 2]);
     if (lane < DEC_WAVES) {
       const float mw = mlw[(lane * G + h) * 2];
       hv[h * 12 + 4 + lane] = mw == STILL_NEG_INF ? 0.f : __expf(mw - mx);

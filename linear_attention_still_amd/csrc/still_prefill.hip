@@ -192,9 +192,9 @@ __global__ __launch_bounds__(256) void score_kernel(PrefillArgs a) {
           const bool ok = k0 + u <= kt_hi && j >= 0 && j <= t && j >= t - W + 1;
           sg[u][i] = ok ? sg[u][i] * a.scale : STILL_NEG_INF;
           sself = ok && j == t ? sg[u][i] : sself;
-          mx = fmaxf(mx, sg[u][i]);
+          mx = fmax_nn(mx, sg[u][i]);
         }
-      const float mn = fmaxf(mrun, mx);
+      const float mn = fmax_nn(mrun, mx);
       // rows with nothing visible so far keep m = -inf and zero sums
       const float al = mrun == STILL_NEG_INF ? 0.f : __expf(mrun - mn);
       const float mo = mn == STILL_NEG_INF ? 0.f : mn;
@@ -215,7 +215,7 @@ __global__ __launch_bounds__(256) void score_kernel(PrefillArgs a) {
     for (int off = 16; off <= 32; off <<= 1) {
       auto px = [&](float x) { return off == 16 ? xor16f(x) : xor32f(x); };
       const float m2 = px(mrun), za2 = px(zall), zo2 = px(zoth), ss2 = px(sself);
-      const float mn = fmaxf(mrun, m2);
+      const float mn = fmax_nn(mrun, m2);
       if (mn != STILL_NEG_INF) {
         const float f1 = (mrun == STILL_NEG_INF) ? 0.f : __expf(mrun - mn);
         const float f2 = (m2 == STILL_NEG_INF) ? 0.f : __expf(m2 - mn);
@@ -223,7 +223,7 @@ __global__ __launch_bounds__(256) void score_kernel(PrefillArgs a) {
         zoth = zoth * f1 + zo2 * f2;
       }
       mrun = mn;
-      sself = fmaxf(sself, ss2);
+      sself = fmax_nn(sself, ss2);
     }
     float sc = 0.f, dl = 0.f;
     if (t < L) {
@@ -715,7 +715,7 @@ __device__ __forceinline__ void np_map_tile(const BlkPtr<T, D>& P, const Frag<T>
     for (int kb = 0; kb < D / 32; ++kb)
       mma(out[ft], ld_frag(P.ft(ft, kb, lane)), xf[kb]);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) mx = fmaxf(mx, out[ft][i]);
+    for (int i = 0; i < 4; ++i) mx = fmax_nn(mx, out[ft][i]);
   }
   mx = max_over_g(mx);
   float ss = 0.f;
@@ -762,7 +762,7 @@ __device__ __forceinline__ void np_map_tiles(const BlkPtr<T, D>& P, const Frag<T
 #pragma unroll
     for (int x = 0; x < NX; ++x)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) mx[x] = fmaxf(mx[x], out[x][ft][i]);
+      for (int i = 0; i < 4; ++i) mx[x] = fmax_nn(mx[x], out[x][ft][i]);
   }
 #pragma unroll
   for (int x = 0; x < NX; ++x) {
@@ -835,7 +835,7 @@ __device__ __forceinline__ void block_phi(const BlkPtr<T, D>& P, f32x4 (&ph)[4],
   __syncthreads();
   if (tid < 64) {  // combine the waves: global max M, sum S, then per-wave factors
     float M = STILL_NEG_INF;
-    for (int w = 0; w < B_::NFT; ++w) M = fmaxf(M, P.kmax[w * 64 + tid]);
+    for (int w = 0; w < B_::NFT; ++w) M = fmax_nn(M, P.kmax[w * 64 + tid]);
     float S = 0.f;
     for (int w = 0; w < B_::NFT; ++w)
       S += P.ksum[w * 64 + tid] * exp_acc<T>(2.f * (P.kmax[w * 64 + tid] - M));
@@ -1338,7 +1338,7 @@ __global__ __launch_bounds__(512) void attend_kernel(PrefillArgs a) {
               if (la_blk) {
                 const float w = wt[j][kt][i];
                 const bool la = ((la_s >> (16 * kt + i)) & 1ull) && w > 0.f;
-                x = la ? (lgate2[j] + log2_acc<T>(fmaxf(w, 1e-37f))) * inv_scale2 : x;
+                x = la ? (lgate2[j] + log2_acc<T>(fmax_nn(w, 1e-37f))) * inv_scale2 : x;
               }
               st[j][kt][i] = x;
             }
