@@ -797,8 +797,8 @@ __device__ __forceinline__ float sum_over_r(float x) {
 // layout of K F: ph[kt][i] = phi(k_{16kt+4g+i})[16w + r]. Per-key softmax
 // statistics are combined across waves through LDS: each wave's max and sum
 // of squares relative to it, then one factor per (wave, key). With want_w
-// the features are also written as H A fragments (rows = keys) to WF. Two
-// workgroup barriers (three with want_w); every thread must call it with the
+// the features are also written as H A fragments (rows = keys) to WF. One
+// workgroup barrier (two with want_w); every thread must call it with the
 // same want_w.
 template <typename T, int D>
 __device__ __forceinline__ void block_phi(const BlkPtr<T, D>& P, f32x4 (&ph)[4],
@@ -833,23 +833,27 @@ __device__ __forceinline__ void block_phi(const BlkPtr<T, D>& P, f32x4 (&ph)[4],
     }
   }
   __syncthreads();
-  if (tid < 64) {  // combine the waves: global max M, sum S, then per-wave factors
-    float M = STILL_NEG_INF;
-    for (int w = 0; w < B_::NFT; ++w) M = fmax_nn(M, P.kmax[w * 64 + tid]);
-    float S = 0.f;
-    for (int w = 0; w < B_::NFT; ++w)
-      S += P.ksum[w * 64 + tid] * exp_acc<T>(2.f * (P.kmax[w * 64 + tid] - M));
-    const float base = sqrtf(P.kstat[128 + tid]) / sqrtf(S);
-    for (int w = 0; w < B_::NFT; ++w) P.kmax[w * 64 + tid] = exp_acc<T>(P.kmax[w * 64 + tid] - M) * base;
-  }
-  __syncthreads();
   if (mine) {
+    // Combine the waves per key (lane = key): the maximum M of the waves'
+    // maxima, the sum S of squares relative to it, and this wave's factor
+    // exp(m_w - M) |k| / sqrt(S). Every wave computes the key statistics
+    // itself, so no further workgroup barrier is needed; each lane then
+    // takes the factors of its 16 keys from the lanes that hold them.
+    float M = STILL_NEG_INF;
+#pragma unroll
+    for (int w = 0; w < B_::NFT; ++w) M = fmax_nn(M, P.kmax[w * 64 + lane]);
+    float S = 0.f;
+#pragma unroll
+    for (int w = 0; w < B_::NFT; ++w)
+      S += P.ksum[w * 64 + lane] * exp_acc<T>(2.f * (P.kmax[w * 64 + lane] - M));
+    const float base = sqrtf(P.kstat[128 + lane]) / sqrtf(S);
+    const float fac = exp_acc<T>(P.kmax[wave * 64 + lane] - M) * base;
     const int f = 16 * wave + r16, bb = f >> 5, o = f & 31;
     const int gp = (o & 15) >> 2, sl = (o & 3) + ((o >> 4) << 2);
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) ph[kt][i] *= P.kmax[wave * 64 + 16 * kt + 4 * g4 + i];
+      for (int i = 0; i < 4; ++i) ph[kt][i] *= __shfl(fac, 16 * kt + 4 * g4 + i);
       if (want_w) {
         if constexpr (B_::TR) {  // feature-major: 4 keys of feature f, 8 bytes
           H w4[4] = {from_f32<H>(ph[kt][0]), from_f32<H>(ph[kt][1]), from_f32<H>(ph[kt][2]),
@@ -1424,7 +1428,7 @@ __global__ __launch_bounds__(512) void attend_kernel(PrefillArgs a) {
       const bool do_fold = band && fold && blo < fold_hi;
       if (la_blk || do_fold) {
         f32x4 phk[4];
-        block_phi<T, D>(P, phk, la_blk);  // ends with a barrier
+        block_phi<T, D>(P, phk, la_blk);  // WF is complete on return
         // the fold writes only SP / zs, which this chunk no longer reads
         if (do_fold) block_fold<T, D>(P, phk);
       }
