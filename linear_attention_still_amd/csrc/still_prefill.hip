@@ -420,10 +420,12 @@ __global__ __launch_bounds__(256) void select_kernel(PrefillArgs a) {
 // ----------------------------------------- shared block machinery (4-6) ----
 // A workgroup of 8 waves streams 64-key blocks through LDS:
 //   Ks    [64][D+pad] T         keys, row-major (A fragments of K)
-//   VTs   [D][64+pad] H         values transposed, keys permuted (perm_col);
-//                               H = fp16 next to bf16 data, float otherwise
-//   WF    [4 kt][D/32][hi,lo]   NP-Map features of the block's keys as H
-//                               A fragments (rows = keys) of <phi(k),phi(q)>
+//   VTs   values as H (fp16 next to bf16 data, float otherwise): for fp16
+//         row-major [64][D+8], read as fragments by transposing LDS reads;
+//         for float transposed [D][64+pad], keys permuted (perm_col)
+//   WF    NP-Map features of the block's keys as H, the A fragments (rows =
+//         keys) of <phi(k),phi(q)>: for fp16 feature-major [D][64+8] read
+//         by transposing LDS reads; for float [4 kt][D/32] fragments
 //   SP    float32 linear state S (d_k x d_v), fragment-linear: pair
 //         p = (d_v tile vt, d_k 32-block bb) holds, per lane, the 8 values
 //         {S[32bb + 4g + i][16vt + r], S[32bb + 16 + 4g + i][16vt + r]} as two
@@ -431,8 +433,8 @@ __global__ __launch_bounds__(256) void select_kernel(PrefillArgs a) {
 //         (2bb+1, vt)); read together they are the A operand of S^T for the
 //         readout.
 //   stat  per-key softmax statistics of the feature map
-// At the start of a chunk the first region (Ks..WF) holds the state split
-// into hi/lo bf16 fragments for the readout (RS).
+// At the start of a chunk the first region (Ks..WF) holds the state's
+// fp16 readout fragments (RS; rows scaled by 1/z).
 template <typename T, int D>
 struct Blk {
   typedef typename HalfOf<T>::type H;
@@ -1068,10 +1070,12 @@ __global__ __launch_bounds__(256) void state_scan_kernel(float* dS, int NS, int 
 //  * every weight enters one running max / sum in the log domain (reading:
 //    a single normaliser over softmax and gated linear weights);
 //  * the next chunk's newly folded tokens are added to the state.
-// Precision: logits from exact bf16 products; the readout with hi/lo bf16
-// splits of S and phi(q); <phi(k),phi(q)> with both features in fp16 (all
-// terms are positive, so the relative error stays within 2^-11); softmax
-// weights and values in fp16 (11-bit significands, bf16 values exact).
+// Precision: logits from exact bf16 products; the readout as one fp16
+// product of S with rows scaled by 1/z_i against z_i phi(q)_i / z.phi(q)
+// (both bounded, see the readout); <phi(k),phi(q)> with both features in
+// fp16 (all terms are positive, so the relative error stays within 2^-11);
+// softmax weights and values in fp16 (11-bit significands, bf16 values
+// exact), the weights below 2^8 by the lazily moved offset.
 // A wave holds HPW heads of one 16-query tile: the key, value and phi(K)
 // fragments it reads from LDS serve every head it holds.
 template <typename T, int D, int HPW>
