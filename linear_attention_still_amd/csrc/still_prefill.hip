@@ -822,18 +822,32 @@ __device__ __forceinline__ void block_phi(const BlkPtr<T, D>& P, f32x4 (&ph)[4],
 #pragma unroll
       for (int kb = 0; kb < D / 32; ++kb)
         mma(ph[kt], ld_frag(P.Ks + (16 * kt + r16) * B_::KS + 32 * kb + 8 * g4), fb[kb]);
-      // per key: this wave's max over its 16 features and its sum of
-      // squared exponentials relative to that max
+    }
+    // per key: this wave's max over its 16 features and its sum of squared
+    // exponentials relative to that max; the 16 keys of a lane are reduced
+    // side by side (independent chains), then one lane per row stores them
+    f32x4 mk[4], sk[4];
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) mk[kt][i] = max_over_r(ph[kt][i]);
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float m = max_over_r(ph[kt][i]);
-        const float e = exp_acc<T>(ph[kt][i] - m);
+        const float e = exp_acc<T>(ph[kt][i] - mk[kt][i]);
         ph[kt][i] = e;
-        const float s2 = sum_over_r(e * e);
-        if (r16 == 0) {
-          P.kmax[wave * 64 + 16 * kt + 4 * g4 + i] = m;
-          P.ksum[wave * 64 + 16 * kt + 4 * g4 + i] = s2;
-        }
+        sk[kt][i] = e * e;
+      }
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sk[kt][i] = sum_over_r(sk[kt][i]);
+    if (r16 == 0) {
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) {
+        *reinterpret_cast<f32x4*>(P.kmax + wave * 64 + 16 * kt + 4 * g4) = mk[kt];
+        *reinterpret_cast<f32x4*>(P.ksum + wave * 64 + 16 * kt + 4 * g4) = sk[kt];
       }
     }
   }
