@@ -1103,7 +1103,9 @@ __global__ __launch_bounds__(512) void attend_kernel(PrefillArgs a) {
   const int n_wg = a.NS * n_units;
   int id = blockIdx.x;
   if ((n_wg & 7) == 0) id = (id & 7) * (n_wg >> 3) + (id >> 3);
-  const int s = id % a.NS;
+  // super-chunks in descending order: later ones walk larger kept pools and
+  // take longer, so the longest start first and the short ones fill in
+  const int s = a.NS - 1 - id % a.NS;
   const int u3 = id / a.NS;  // (b, kv, hg)
   const int hg = u3 % a.nHG, kv = (u3 / a.nHG) % a.Hkv, b = u3 / (a.nHG * a.Hkv);
   const int tid = threadIdx.x, lane = tid & 63, r16 = lane & 15, g4 = lane >> 4;
