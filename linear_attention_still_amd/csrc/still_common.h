@@ -137,18 +137,29 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint3
 }
 template <typename T>
 __device__ __forceinline__ Frag<T> ld_frag_buf(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff);
+// (POL: the cache policy bits of the load; CPOL_NT marks data read once,
+// which the caches may evict first)
+constexpr int CPOL_NT = 2;
+template <typename T, int POL = 0>
+__device__ __forceinline__ Frag<T> ld_frag_buf_p(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  if constexpr (sizeof(T) == 2) {
+    Frag<T> f;
+    f.v = __builtin_bit_cast(decltype(f.v), __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, POL));
+    return f;
+  } else {
+    Frag<T> f;
+    f.lo = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, POL));
+    f.hi = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff + 16, POL));
+    return f;
+  }
+}
 template <>
 __device__ __forceinline__ Frag<bf16> ld_frag_buf<bf16>(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
-  Frag<bf16> f;
-  f.v = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
-  return f;
+  return ld_frag_buf_p<bf16>(r, voff, soff);
 }
 template <>
 __device__ __forceinline__ Frag<float> ld_frag_buf<float>(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
-  Frag<float> f;
-  f.lo = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
-  f.hi = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff + 16, 0));
-  return f;
+  return ld_frag_buf_p<float>(r, voff, soff);
 }
 __device__ __forceinline__ uint4 ld_u4_buf(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
   const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);

@@ -1165,8 +1165,8 @@ __global__ __launch_bounds__(512) void attend_kernel(PrefillArgs a) {
     for (int j = 0; j < HPW; ++j)
 #pragma unroll
       for (int kb = 0; kb < D / 32; ++kb)
-        qf[j][kb] = ld_frag_buf<T>(qr[j], act ? (uint32_t)(t * D + 8 * g4) * sizeof(T) : kv_bytes,
-                                   32 * kb * sizeof(T));
+        qf[j][kb] = ld_frag_buf_p<T, CPOL_NT>(qr[j], act ? (uint32_t)(t * D + 8 * g4) * sizeof(T) : kv_bytes,
+                                              32 * kb * sizeof(T));  // read once
     // the first band block's loads are in flight during the readout (issued
     // after the query loads: waits on those then leave them outstanding)
     BlkRegs<T, D, 512> R;
@@ -1494,8 +1494,9 @@ __global__ __launch_bounds__(512) void attend_kernel(PrefillArgs a) {
               const int e = it * 64 + lane, row = e / CPR, ch = e % CPR;
               const int tr = cC + 16 * qt + row;
               if (tr < L)
-                *reinterpret_cast<uint4*>(reinterpret_cast<bf16*>(a.out) + ob + (size_t)tr * D + 8 * ch) =
-                    *reinterpret_cast<const uint4*>(tile + row * OS + 8 * ch);
+                __builtin_nontemporal_store(  // written once
+                    *reinterpret_cast<const u32x4*>(tile + row * OS + 8 * ch),
+                    reinterpret_cast<u32x4*>(reinterpret_cast<bf16*>(a.out) + ob + (size_t)tr * D + 8 * ch));
             }
           }
         } else if (act && t < L) {
