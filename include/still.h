@@ -135,8 +135,11 @@ int still_prefill(const still_params* p, int64_t seq_len, const void* q, const v
 
 /* still_prefill with per-kernel timing, for benchmarks: for i < n_pairs it
  * records events[2i] before and events[2i+1] after the i-th kernel of the
- * prefill on `stream` (events are caller-created hipEvent_t handles). Kernel
- * order: 0 F^T copy, 1 score, 2 select, 3 state deltas, 4 state scan,
+ * prefill on `stream` (events are caller-created hipEvent_t handles; a NULL
+ * handle is not recorded, so a caller can time some kernels only: every
+ * recorded event costs the stream a drain). Kernel order: 0 F^T copy (made
+ * by extra workgroups of the score launch, so its two events are recorded
+ * back to back), 1 score, 2 select, 3 state deltas, 4 state scan,
  * 5 attention walk, 6 state export; a kernel not launched for a given
  * length gets its two events recorded back to back. n_pairs <= 7. Same
  * results and errors as still_prefill. */

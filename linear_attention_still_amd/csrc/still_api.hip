@@ -169,8 +169,9 @@ struct Marks {
   void* const* ev;
   int n;
   hipStream_t s;
-  void at(int i, int which) const {
-    if (ev && i < n) (void)hipEventRecord(reinterpret_cast<hipEvent_t>(ev[2 * i + which]), s);
+  void at(int i, int which) const {  // a null handle is skipped
+    if (ev && i < n && ev[2 * i + which])
+      (void)hipEventRecord(reinterpret_cast<hipEvent_t>(ev[2 * i + which]), s);
   }
 };
 
@@ -183,11 +184,12 @@ int launch_prefill(const Derived& d, const Plan& pl, still::PrefillArgs a, hipSt
       (size_t)nkt * 16 * (D + Pad<T>::v) * sizeof(T) + (size_t)(2 * d.G * d.C + 4) * 4;
   const size_t lds_sel = (size_t)(d.G * d.W + 8 + d.C) * 8 + (size_t)(3 * d.C + 4) * 4;
   set_lds_attr<T, D>();
+  // F^T is made by D*D/2048 extra workgroups of the score launch (its
+  // events are recorded back to back)
   mk.at(0, 0);
-  fmap_transpose_kernel<T, D><<<dim3(D * D / 2048, d.Hkv), dim3(256), 0, s>>>(a);
   mk.at(0, 1);
   mk.at(1, 0);
-  score_kernel<T, D><<<dim3(pl.T, d.Hkv, d.B), dim3(256), lds_score, s>>>(a);
+  score_kernel<T, D><<<dim3(pl.T + D * D / 2048, d.Hkv, d.B), dim3(256), lds_score, s>>>(a);
   mk.at(1, 1);
   mk.at(2, 0);
   select_kernel<T, D><<<dim3(pl.n_dec + pl.n_pend, d.Hkv, d.B), dim3(256), lds_sel, s>>>(a);

@@ -10,7 +10,8 @@
 //        "NP-Map: Norm-Preserving Feature Map"
 //
 // Launch sequence on one stream (host side in still_api.hip):
-//   1. fmap_transpose   F^T copy so MFMA fragments of F^T are 16-byte reads
+//   1. F^T copy         so MFMA fragments of F^T are 16-byte reads (extra
+//                       workgroups of the score launch)
 //   2. score            windowed Self-Saliency Score, float32, + error bound
 //   3. select           per decided chunk: Top-lambda, float64 refinement of
 //                       candidates the float32 bound cannot separate; float64
@@ -55,14 +56,16 @@ struct Pad {
 };
 
 // ------------------------------------------------------------ 1. F^T ----
+// Part bx (of D*D/2048) of F^T for kv head kv, by 256 threads; run by extra
+// workgroups of the score launch (the score kernel does not read it).
 template <typename T, int D>
-__global__ __launch_bounds__(256) void fmap_transpose_kernel(PrefillArgs a) {
+__device__ __forceinline__ void fmap_transpose_part(const PrefillArgs& a, int bx, int kv) {
   // F^T in fragment order: element ((ft * D/32 + kb) * 64 + lane) * 8 + s
   // holds F[32 kb + 8 g + s][16 ft + r], lane = 16 g + r, i.e. the B operand
   // fragments of X F for feature tile ft and d block kb, 8 per lane.
-  const T* F = reinterpret_cast<const T*>(a.fmap_w) + (size_t)blockIdx.y * D * D;
-  T* Ft = reinterpret_cast<T*>(a.ft) + (size_t)blockIdx.y * D * D;
-  const int base = blockIdx.x * 256 * 8;
+  const T* F = reinterpret_cast<const T*>(a.fmap_w) + (size_t)kv * D * D;
+  T* Ft = reinterpret_cast<T*>(a.ft) + (size_t)kv * D * D;
+  const int base = bx * 256 * 8;
 #pragma unroll
   for (int q = 0; q < 8; ++q) {
     const int e = base + q * 256 + threadIdx.x;
@@ -84,6 +87,10 @@ __global__ __launch_bounds__(256) void fmap_transpose_kernel(PrefillArgs a) {
 template <typename T, int D>
 __global__ __launch_bounds__(256) void score_kernel(PrefillArgs a) {
   extern __shared__ __align__(16) char smem[];
+  if ((int)blockIdx.x >= a.T) {  // the extra workgroups: F^T (batch row 0's)
+    if (blockIdx.z == 0) fmap_transpose_part<T, D>(a, (int)blockIdx.x - a.T, (int)blockIdx.y);
+    return;
+  }
   const int c = blockIdx.x, kv = blockIdx.y, b = blockIdx.z;
   const int L = a.L, C = a.C, W = a.W, G = a.G;
   const int tid = threadIdx.x, lane = tid & 63;

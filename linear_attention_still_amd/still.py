@@ -163,10 +163,11 @@ PREFILL_KERNELS = ("fmap_transpose", "score", "select", "state_delta", "state_sc
 def still_prefill_timed(p: still_params, seq_len: int, q, k, v, fmap_w, gate, out, sel_idx,
                         score, state, workspace, events, stream=None) -> None:
     """events: flat list of 2*n torch.cuda.Event (enable_timing=True), already
-    recorded once so their handles exist; kernel i is bracketed by
-    events[2i], events[2i+1]."""
+    recorded once so their handles exist, or None (not recorded); kernel i is
+    bracketed by events[2i], events[2i+1]."""
     n = len(events) // 2
-    arr = (ctypes.c_void_p * (2 * n))(*[ctypes.c_void_p(e.cuda_event) for e in events])
+    arr = (ctypes.c_void_p * (2 * n))(*[ctypes.c_void_p(e.cuda_event if e is not None else None)
+                                        for e in events])
     rc = lib().still_prefill_timed(ctypes.byref(p), int(seq_len), _ptr(q), _ptr(k), _ptr(v),
                                    _ptr(fmap_w), _ptr(gate), _ptr(out), _ptr(sel_idx),
                                    _ptr(score), _ptr(state), _ptr(workspace),
