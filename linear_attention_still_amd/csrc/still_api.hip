@@ -179,7 +179,7 @@ template <typename T, int D>
 int launch_prefill(const Derived& d, const Plan& pl, still::PrefillArgs a, hipStream_t s,
                    const Marks& mk) {
   using namespace still;
-  const int nkt = d.C / 16 + (d.W + 14) / 16 + 1;
+  const int nkt = d.C / 16 + (d.W + 14) / 16;  // key tiles of the score kernel
   const size_t lds_score =
       (size_t)nkt * 16 * (D + Pad<T>::v) * sizeof(T) + (size_t)(2 * d.G * d.C + 4) * 4;
   const size_t lds_sel = (size_t)(d.G * d.W + 8 + d.C) * 8 + (size_t)(3 * d.C + 4) * 4;

@@ -99,7 +99,9 @@ __global__ __launch_bounds__(256) void score_kernel(PrefillArgs a) {
   constexpr int KS = D + Pad<T>::v;
   const int cC = c * C;
   const int kbase = cC - W + 1;
-  const int nkt = C / 16 + (W + 14) / 16 + 1;
+  // key tiles: row tile qt reads tiles qt .. qt + (W + 14) / 16 (its rows'
+  // windows start at 16 qt + r - W + 1 relative to the chunk)
+  const int nkt = C / 16 + (W + 14) / 16;
   T* Ks = reinterpret_cast<T*>(smem);
   float* part = reinterpret_cast<float*>(smem + (size_t)nkt * 16 * KS * sizeof(T));
   float* pdel = part + G * C;
