@@ -376,19 +376,66 @@ __global__ __launch_bounds__(256) void select_kernel(PrefillArgs a) {
     for (int i = tid; i < lam; i += 256) selrow[i] = lam_c == C ? base + i : -1;
     return;
   }
-  for (int j = tid; j < C; j += 256) {
-    const float s = a.score[ub_off + base + j], d = a.delta[ub_off + base + j];
-    lb[j] = s - d;
-    ub[j] = s + d;
+  if (C <= 64) {
+    // One wave, token j in lane j: the lam_c-th largest lower bound by
+    // (lb desc, index asc), taken by lam_c rounds of removing the largest;
+    // the candidates are the tokens whose upper bound reaches it. With
+    // exactly lam_c of them (the usual case) they are the kept tokens and
+    // the chunk is done here; otherwise the bounds go to LDS for the
+    // float64 ranking below.
+    if (tid < 64) {
+      const int lane = tid;
+      float lbj = STILL_NEG_INF, ubj = STILL_NEG_INF;
+      if (lane < C) {
+        const float sc = a.score[ub_off + base + lane], d = a.delta[ub_off + base + lane];
+        lbj = sc - d;
+        ubj = sc + d;
+      }
+      float x = lane < C ? lbj : STILL_NEG_INF, LBv = STILL_NEG_INF;
+      bool gone = lane >= C;
+      for (int k = 0; k < lam_c; ++k) {
+        float m = row_max<16>(gone ? STILL_NEG_INF : x);
+        m = fmax_nn(m, xor16f(m));
+        m = fmax_nn(m, xor32f(m));
+        const uint64_t at = __builtin_amdgcn_ballot_w64(!gone && x == m);
+        const int first = (int)__builtin_ctzll(at);  // lowest index among the maxima
+        if (lane == first) gone = true;
+        LBv = m;
+      }
+      const bool cand = lane < C && ubj >= LBv;
+      const uint64_t cm = __builtin_amdgcn_ballot_w64(cand);
+      if ((int)__builtin_popcountll(cm) == lam_c) {
+        if (lane < C) a.selflag[ub_off + base + lane] = cand ? 1 : 0;
+        if (cand) selrow[__builtin_popcountll(cm & ((1ull << lane) - 1ull))] = base + lane;
+        if (lane == 0) misc[2] = 0;
+      } else {
+        if (lane < C) {
+          lb[lane] = lbj;
+          ub[lane] = ubj;
+        }
+        if (lane == 0) {
+          misc[0] = __float_as_int(LBv);
+          misc[2] = 1;
+        }
+      }
+    }
+    __syncthreads();
+    if (misc[2] == 0) return;  // uniform
+  } else {
+    for (int j = tid; j < C; j += 256) {
+      const float s = a.score[ub_off + base + j], d = a.delta[ub_off + base + j];
+      lb[j] = s - d;
+      ub[j] = s + d;
+    }
+    __syncthreads();
+    // lambda-th largest lower bound (rank by (lb desc, index asc))
+    for (int j = tid; j < C; j += 256) {
+      int r = 0;
+      for (int i = 0; i < C; ++i) r += (lb[i] > lb[j] || (lb[i] == lb[j] && i < j)) ? 1 : 0;
+      if (r == lam_c - 1) misc[0] = __float_as_int(lb[j]);
+    }
   }
   if (tid == 0) misc[1] = 0;
-  __syncthreads();
-  // lambda-th largest lower bound (rank by (lb desc, index asc))
-  for (int j = tid; j < C; j += 256) {
-    int r = 0;
-    for (int i = 0; i < C; ++i) r += (lb[i] > lb[j] || (lb[i] == lb[j] && i < j)) ? 1 : 0;
-    if (r == lam_c - 1) misc[0] = __float_as_int(lb[j]);
-  }
   __syncthreads();
   const float LB = __int_as_float(misc[0]);
   for (int j = tid; j < C; j += 256) {
