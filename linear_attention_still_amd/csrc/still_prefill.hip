@@ -398,7 +398,7 @@ __global__ __launch_bounds__(256) void select_kernel(PrefillArgs a) {
         m = fmax_nn(m, xor16f(m));
         m = fmax_nn(m, xor32f(m));
         const uint64_t at = __builtin_amdgcn_ballot_w64(!gone && x == m);
-        const int first = (int)__builtin_ctzll(at);  // lowest index among the maxima
+        const int first = at ? (int)__builtin_ctzll(at) : 64;  // lowest index among the maxima
         if (lane == first) gone = true;
         LBv = m;
       }
