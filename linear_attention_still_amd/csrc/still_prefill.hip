@@ -794,6 +794,21 @@ __device__ __forceinline__ void np_map_tile(const BlkPtr<T, D>& P, const Frag<T>
   for (int ft = 0; ft < D / 16; ++ft) out[ft] *= f;
 }
 
+// Orders the LDS reads and MFMAs of the enclosing scheduling region (one
+// basic block): AHEAD reads first, then N times M MFMAs followed by R reads,
+// then TAIL MFMAs. The reads then run that far ahead of the MFMAs that use
+// them and their latency is covered; other instructions are placed freely.
+template <int AHEAD, int N, int M, int R, int TAIL>
+__device__ __forceinline__ void lds_mfma_pipeline() {
+  __builtin_amdgcn_sched_group_barrier(0x100, AHEAD, 0);  // LDS reads
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, M, 0);  // MFMAs
+    __builtin_amdgcn_sched_group_barrier(0x100, R, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, TAIL, 0);
+}
+
 // np_map_tile for NX tiles at once: each F^T fragment read from LDS serves
 // every tile.
 template <typename T, int D, int NX>
@@ -825,6 +840,8 @@ __device__ __forceinline__ void np_map_tiles(const BlkPtr<T, D>& P, const Frag<T
 #pragma unroll
       for (int i = 0; i < 4; ++i) mx[x] = fmax_nn(mx[x], out[x][ft][i]);
   }
+  if constexpr (sizeof(T) == 2)  // F^T reads two feature tiles ahead
+    lds_mfma_pipeline<2 * (D / 32), (D / 16 - 2) * (D / 32), NX, 1, 2 * (D / 32) * NX>();
 #pragma unroll
   for (int x = 0; x < NX; ++x) {
     mx[x] = max_over_g(mx[x]);
@@ -879,6 +896,8 @@ __device__ __forceinline__ void block_phi(const BlkPtr<T, D>& P, f32x4 (&ph)[4],
       for (int kb = 0; kb < D / 32; ++kb)
         mma(ph[kt], ld_frag(P.Ks + (16 * kt + r16) * B_::KS + 32 * kb + 8 * g4), fb[kb]);
     }
+    if constexpr (sizeof(T) == 2)  // F^T and two key tiles ahead
+      lds_mfma_pipeline<3 * (D / 32), 2 * (D / 32), 1, 1, 2 * (D / 32)>();
     // per key: this wave's max over its 16 features and its sum of squared
     // exponentials relative to that max; the 16 keys of a lane are reduced
     // side by side (independent chains), then one lane per row stores them
@@ -1308,6 +1327,7 @@ __global__ __launch_bounds__(512) void attend_kernel(PrefillArgs a) {
             for (int j = 0; j < HPW; ++j) mma(O[j][dt], sf, pz[j][bb]);
           }
         }
+        lds_mfma_pipeline<2 * (D / 32), (D / 16 - 2) * (D / 32), HPW, 1, 2 * (D / 32) * HPW>();
       } else {
         // float32 S fragments straight from the state region
 #pragma unroll
@@ -1358,18 +1378,25 @@ __global__ __launch_bounds__(512) void attend_kernel(PrefillArgs a) {
       Pb.VTs = lds_opaque_v(P.VTs);
       Pb.WF = lds_opaque_v(P.WF);
       const uint64_t selbits = ((uint64_t)P.selw[1] << 32) | P.selw[0];
+      // QK^T of the block; the schedule keeps the key fragment reads two
+      // 16-key tiles ahead of their MFMAs, so their LDS latency is covered
       f32x4 st[HPW][4];
+      Frag<T> kf[4][D / 32];
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) {
+#pragma unroll
+        for (int kb = 0; kb < D / 32; ++kb) kf[kt][kb] = ld_frag(Pb.Ks + (16 * kt + r16) * B_::KS + 32 * kb + 8 * g4);
+      }
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt) {
 #pragma unroll
         for (int j = 0; j < HPW; ++j) st[j][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int kb = 0; kb < D / 32; ++kb) {
-          const Frag<T> kf = ld_frag(Pb.Ks + (16 * kt + r16) * B_::KS + 32 * kb + 8 * g4);
+        for (int kb = 0; kb < D / 32; ++kb)
 #pragma unroll
-          for (int j = 0; j < HPW; ++j) mma(st[j][kt], kf, qf[j][kb]);
-        }
+          for (int j = 0; j < HPW; ++j) mma(st[j][kt], kf[kt][kb], qf[j][kb]);
       }
+      if constexpr (sizeof(T) == 2) lds_mfma_pipeline<2 * (D / 32), 2 * (D / 32), HPW, 1, 2 * HPW * (D / 32)>();
       // st holds raw logits (scaled into the base-2 domain inside the
       // exponential); linear keys hold their log-weight / scale2, masked
       // keys -inf. scale2 > 0, so the row maximum commutes with the scaling.
@@ -1410,6 +1437,8 @@ __global__ __launch_bounds__(512) void attend_kernel(PrefillArgs a) {
               for (int j = 0; j < HPW; ++j) mma(wt[j][kt], wk, pq[j][bb]);
             }
           }
+          // one key tile ahead (two transposing reads per fragment)
+          if constexpr (sizeof(T) == 2) lds_mfma_pipeline<2 * (D / 32), 3 * (D / 32), HPW, 2, HPW * (D / 32)>();
         }
 #pragma unroll
         for (int j = 0; j < HPW; ++j) {
@@ -1432,6 +1461,10 @@ __global__ __launch_bounds__(512) void attend_kernel(PrefillArgs a) {
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt)
           mx[j] = fmax_nn(mx[j], fmax_nn(fmax_nn(st[j][kt][0], st[j][kt][1]), fmax_nn(st[j][kt][2], st[j][kt][3])));
+      // the first value tile is read while the weights are formed
+      Frag<H> vf[D / 16][2];
+      vf[0][0] = Pb.ld_v(0, 0, lane);
+      vf[0][1] = Pb.ld_v(0, 1, lane);
       Frag<H> pf[HPW][2];
 #pragma unroll
       for (int j = 0; j < HPW; ++j) {
@@ -1466,14 +1499,21 @@ __global__ __launch_bounds__(512) void attend_kernel(PrefillArgs a) {
         mma(lacc[j], one, pf[j][1]);
       }
 #pragma unroll
-      for (int dt = 0; dt < D / 16; ++dt) {
-        const Frag<H> v0 = Pb.ld_v(dt, 0, lane), v1 = Pb.ld_v(dt, 1, lane);
+      for (int dt = 1; dt < D / 16; ++dt) {
+        vf[dt][0] = Pb.ld_v(dt, 0, lane);
+        vf[dt][1] = Pb.ld_v(dt, 1, lane);
+      }
+#pragma unroll
+      for (int dt = 0; dt < D / 16; ++dt)
 #pragma unroll
         for (int j = 0; j < HPW; ++j) {
-          mma(O[j][dt], v0, pf[j][0]);
-          mma(O[j][dt], v1, pf[j][1]);
+          mma(O[j][dt], vf[dt][0], pf[j][0]);
+          mma(O[j][dt], vf[dt][1], pf[j][1]);
         }
-      }
+      // value tiles 1 and 2 first (tile 0 is in flight), then each tile's
+      // MFMAs with the reads of the tile three ahead (two transposing reads
+      // per fragment)
+      if constexpr (sizeof(T) == 2) lds_mfma_pipeline<8, 2 * (D / 16 - 3), HPW, 2, 3 * 2 * HPW>();
     };
     auto issue_pool = [&](int pb) __attribute__((always_inline)) {
       const int blo = 64 * pb;
