@@ -181,8 +181,8 @@ int launch_prefill(const Derived& d, const Plan& pl, still::PrefillArgs a, hipSt
   using namespace still;
   const int nkt = d.C / 16 + (d.W + 14) / 16;  // key tiles of the score kernel
   const size_t lds_score =
-      (size_t)nkt * 16 * (D + Pad<T>::v) * sizeof(T) + (size_t)(2 * d.G * d.C + 4) * 4;
-  const size_t lds_sel = (size_t)(d.G * d.W + 8 + d.C) * 8 + (size_t)(3 * d.C + 4) * 4;
+      (size_t)nkt * 16 * (D + Pad<T>::v) * sizeof(T) + (size_t)(3 * d.G * d.C + nkt * 16 + 80) * 4;
+  const size_t lds_sel = (size_t)4 * d.G * D * 4 + (size_t)d.C * 8 + (size_t)(5 * d.C + 4) * 4;
   set_lds_attr<T, D>();
   // F^T is made by D*D/2048 extra workgroups of the score launch (its
   // events are recorded back to back)
@@ -192,15 +192,14 @@ int launch_prefill(const Derived& d, const Plan& pl, still::PrefillArgs a, hipSt
   score_kernel<T, D><<<dim3(pl.T + D * D / 2048, d.Hkv, d.B), dim3(256), lds_score, s>>>(a);
   mk.at(1, 1);
   mk.at(2, 0);
-  select_kernel<T, D><<<dim3(pl.n_dec + pl.n_pend, d.Hkv, d.B), dim3(256), lds_sel, s>>>(a);
+  select_kernel<T, D><<<dim3(pl.n_dec + (pl.n_pend + 3) / 4, d.Hkv, d.B), dim3(256), lds_sel, s>>>(a);
   mk.at(2, 1);
   mk.at(3, 0);
-  if (pl.NS > 1)
-    state_delta_kernel<T, D><<<dim3(pl.NS - 1, d.Hkv, d.B), dim3(512), Blk<T, D>::bytes, s>>>(a);
+  state_delta_kernel<T, D><<<dim3(pl.NS, d.Hkv, d.B), dim3(512), Blk<T, D>::bytes, s>>>(a);
   mk.at(3, 1);
   mk.at(4, 0);
-  state_scan_kernel<<<dim3((D * D + D + 255) / 256, d.Hkv, d.B), dim3(256), 0, s>>>(
-      a.dS, pl.NS, D * D + D);
+  state_scan_kernel<D><<<dim3((D * D + D + 255) / 256, d.Hkv, d.B), dim3(256), 0, s>>>(
+      a.dS, pl.NS, a.state, a.st_unit, a.st_S, a.st_z);
   mk.at(4, 1);
   mk.at(5, 0);
   if (pl.HPW == 2)
@@ -336,6 +335,7 @@ static int prefill_impl(const still_params* p, int64_t seq_len, const void* q, c
   a.out = out;
   a.sel = sel_idx;
   a.score = score ? score : reinterpret_cast<float*>(ws + pl.ws_score);
+  a.score_out = score ? 1 : 0;
   a.delta = reinterpret_cast<float*>(ws + pl.ws_delta);
   a.selflag = reinterpret_cast<uint8_t*>(ws + pl.ws_flag);
   a.ft = ws + pl.ws_ft;

@@ -199,6 +199,19 @@ __device__ __forceinline__ Frag<float> zero_frag<float>() {
   return f;
 }
 
+// Element-wise magnitude of a fragment (sign bits cleared).
+__device__ __forceinline__ Frag<bf16> frag_abs(const Frag<bf16>& f) {
+  Frag<bf16> r;
+  r.v = __builtin_bit_cast(bf16x8, __builtin_bit_cast(u32x4, f.v) & 0x7fff7fffu);
+  return r;
+}
+__device__ __forceinline__ Frag<float> frag_abs(const Frag<float>& f) {
+  Frag<float> r;
+  r.lo = __builtin_bit_cast(f32x4, __builtin_bit_cast(u32x4, f.lo) & 0x7fffffffu);
+  r.hi = __builtin_bit_cast(f32x4, __builtin_bit_cast(u32x4, f.hi) & 0x7fffffffu);
+  return r;
+}
+
 // Fragment from two accumulator tiles (slots 0..3 from x0, 4..7 from x1).
 template <typename T>
 __device__ __forceinline__ Frag<T> frag_from(const f32x4& x0, const f32x4& x1);

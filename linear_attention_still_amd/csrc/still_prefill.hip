@@ -17,8 +17,10 @@
 //                       candidates the float32 bound cannot separate; float64
 //                       scores of the undecided chunk (decode state)
 //   4. state_delta      per super-chunk: sum of phi(k) v^T over the chunks it
-//                       folds into the linear state
-//   5. state_scan       exclusive prefix over super-chunks (in place)
+//                       folds into the linear state (float64 for the rare
+//                       keys whose float32 features are not accurate enough)
+//   5. state_scan       exclusive prefix over super-chunks (in place) and the
+//                       exported S, z (their total)
 //   6. attend           per super-chunk, chunk by chunk: softmax over window
 //                       + own chunk + kept pool, NP-Map linear attention over
 //                       the state and the not-yet-folded band, one softmax-
@@ -43,6 +45,7 @@ struct PrefillArgs {
   float* dS;         // [B][Hkv][NS][D*D + D]
   char* state;
   int B, Hq, Hkv, G, L, W, C, m, T, n_dec, lam, cap_chunks, K, NS, nHG, Gs, fp32_out;
+  int score_out;  // the caller asked for the scores (score is theirs)
   float scale, eps;
   double scale64, eps64;  // the same parameters for the float64 paths
   long st_unit, st_S, st_z, st_pool_k, st_pool_v, st_pool_pos, st_ring_k, st_ring_v,
@@ -105,7 +108,8 @@ __global__ __launch_bounds__(256) void score_kernel(PrefillArgs a) {
   T* Ks = reinterpret_cast<T*>(smem);
   float* part = reinterpret_cast<float*>(smem + (size_t)nkt * 16 * KS * sizeof(T));
   float* pdel = part + G * C;
-  float* kmax = pdel + G * C;
+  float* pest = pdel + G * C;
+  float* knrm = pest + G * C;  // [nkt * 16 + 80] key norms (tiles past the last of a group of five read zeros)
 
   const T* kg = reinterpret_cast<const T*>(a.k) + (size_t)(b * a.Hkv + kv) * L * D;
   constexpr int VEC = 16 / sizeof(T);
@@ -126,12 +130,7 @@ __global__ __launch_bounds__(256) void score_kernel(PrefillArgs a) {
   };
   Frag<T> qnext[D / 32];
   load_q(qnext, wave);  // in flight while the keys are staged
-  if (tid == 0) kmax[0] = 0.f;
-  __syncthreads();
-  // keys into LDS; the largest squared key norm (for the error bound) from
-  // the same vectors: D / VEC consecutive lanes hold one row
-  float kmx = 0.f;
-  // up to nine 16-byte loads per thread in flight at a time (all of them for
+  // keys into LDS: up to nine 16-byte loads per thread in flight at a time (all of them for
   // a 64-key window and chunk at d = 128); rows outside
   // [0, min(L, cC + C)) read past the buffer range (zeros)
   const __amdgpu_buffer_rsrc_t krs = make_rsrc(kg, qbytes);
@@ -151,19 +150,17 @@ __global__ __launch_bounds__(256) void score_kernel(PrefillArgs a) {
       const int idx = base + u * 256 + tid;
       const int row = idx / (D / VEC), col = (idx % (D / VEC)) * VEC;
       if (idx < nvec) *reinterpret_cast<uint4*>(Ks + row * KS + col) = val[u];
+      // the key norm from the same vectors: D / VEC consecutive lanes hold a row
       const T* e = reinterpret_cast<const T*>(&val[u]);
       float q2 = 0.f;
 #pragma unroll
       for (int i = 0; i < VEC; ++i) q2 += to_f32(e[i]) * to_f32(e[i]);
-      kmx = fmaxf(kmx, row_sum<D / VEC>(q2));
+      q2 = row_sum<D / VEC>(q2);
+      if (idx < nvec && col == 0) knrm[row] = sqrtf(q2);
     }
   }
-  kmx = row_max<16>(kmx);
-  kmx = fmaxf(kmx, xor16f(kmx));
-  kmx = fmaxf(kmx, xor32f(kmx));
-  if (lane == 0) atomicMax(reinterpret_cast<int*>(kmax), __float_as_int(kmx));  // >= 0
+  for (int i = nkt * 16 + tid; i < nkt * 16 + 80; i += 256) knrm[i] = 0.f;
   __syncthreads();
-  const float kn_max = sqrtf(kmax[0]);
 
   for (int rt = wave; rt < n_rt; rt += 4) {
     const int hl = rt / n_qt, qt = rt % n_qt;
@@ -175,8 +172,11 @@ __global__ __launch_bounds__(256) void score_kernel(PrefillArgs a) {
     float qn2 = 0.f;
 #pragma unroll
     for (int kb = 0; kb < D / 32; ++kb) qn2 += frag_sumsq(qf[kb]);
-    qn2 = sum_over_g(qn2);
+    const float qn = sqrtf(sum_over_g(qn2));
     float mrun = STILL_NEG_INF, zall = 0.f, zoth = 0.f, sself = STILL_NEG_INF;
+    // key-norm sums for the error bound: sum_j e_j |k_j| over the other keys
+    // (same running rescale as zoth) and the self key's norm
+    float zabs = 0.f, tself = 0.f;
     const int kt_lo = qt, kt_hi = qt + (W + 14) / 16;
     // key tiles in groups of NG: the group's logits first (its MFMAs back
     // to back), then one running-max update and the exponentials
@@ -207,127 +207,161 @@ __global__ __launch_bounds__(256) void score_kernel(PrefillArgs a) {
       // rows with nothing visible so far keep m = -inf and zero sums
       const float al = mrun == STILL_NEG_INF ? 0.f : __expf(mrun - mn);
       const float mo = mn == STILL_NEG_INF ? 0.f : mn;
-      float ea = 0.f, eo = 0.f;
+      float ea = 0.f, eo = 0.f, et = 0.f;
 #pragma unroll
-      for (int u = 0; u < NG; ++u)
+      for (int u = 0; u < NG; ++u) {
+        const f32x4 kn = *reinterpret_cast<const f32x4*>(knrm + 16 * (k0 + u) + 4 * g4);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const float e = __expf(sg[u][i] - mo);  // 0 for masked keys
+          const bool oth = kbase + 16 * (k0 + u) + 4 * g4 + i != t;
           ea += e;
-          eo += kbase + 16 * (k0 + u) + 4 * g4 + i != t ? e : 0.f;
+          eo += oth ? e : 0.f;
+          et += oth ? e * kn[i] : 0.f;
+          tself = oth ? tself : kn[i];
         }
+      }
       zall = zall * al + ea;
       zoth = zoth * al + eo;
+      zabs = zabs * al + et;
       mrun = mn;
     }
 #pragma unroll
     for (int off = 16; off <= 32; off <<= 1) {
       auto px = [&](float x) { return off == 16 ? xor16f(x) : xor32f(x); };
-      const float m2 = px(mrun), za2 = px(zall), zo2 = px(zoth), ss2 = px(sself);
+      const float m2 = px(mrun), za2 = px(zall), zo2 = px(zoth), zt2 = px(zabs), ss2 = px(sself),
+                  ts2 = px(tself);
       const float mn = fmax_nn(mrun, m2);
       if (mn != STILL_NEG_INF) {
         const float f1 = (mrun == STILL_NEG_INF) ? 0.f : __expf(mrun - mn);
         const float f2 = (m2 == STILL_NEG_INF) ? 0.f : __expf(m2 - mn);
         zall = zall * f1 + za2 * f2;
         zoth = zoth * f1 + zo2 * f2;
+        zabs = zabs * f1 + zt2 * f2;
       }
       mrun = mn;
       sself = fmax_nn(sself, ss2);
+      tself = fmax_nn(tself, ts2);
     }
-    float sc = 0.f, dl = 0.f;
+    float sc = 0.f, dl = 0.f, es = 0.f;
     if (t < L) {
       const float p = __expf(sself - mrun) / zall;
       const float pn = zoth / zall;
       const float lp = p > 0.f ? logf(p / a.eps) : 0.f;
       const float lpn = pn > 0.f ? logf(pn / (1.f - a.eps)) : 0.f;
       sc = (p > 0.f ? p * lp : 0.f) + (pn > 0.f ? pn * lpn : 0.f);
-      // Bound on the float32 evaluation error of this head's score: logit
-      // error <= 4e-6 * scale * |q| * max|k| (a wide margin over the MFMA
-      // accumulation error), propagated through d score / d p, plus
-      // rounding of exp/log at a few float32 ulps.
-      const float ds = 4e-6f * a.scale * sqrtf(qn2) * kn_max + 1e-6f * fabsf(mrun);
-      const float dp = 2.f * p * pn * ds + 2e-6f * p;
-      dl = 4.f * (fabsf(lp - lpn) * dp + 2e-6f * (fabsf(sc) + 1.f));
+      // Bound on the float32 evaluation error of this head's score. Each
+      // logit s_j carries at most ~2^-24 sum_i |q_i k_ji| <= 2^-24 |q| |k_j|
+      // of MFMA accumulation error (measured on gfx950: at most 1.3x that;
+      // taken as 4x with the scale), so p = a_t moves by at most p ((1-p)
+      // ds_t + sum_{j!=t} a_j ds_j). The exponentials (argument rounding |x| 2^-24,
+      // 2 ulps each) and the sums (one rounding per add: the lane's tiles,
+      // two lane merges) move p and 1-p by rho relative. d score / d p =
+      // lp - lpn, d score / d(p, pn) at most |lp| + |lpn| + 2. Doubled.
+      const float cs = 4.f * 5.9604645e-8f * a.scale * qn;  // 4 * 2^-24 * scale * |q|
+      const float dp = p * cs * ((1.f - p) * tself + zabs / zall);
+      const float n_add = (float)(4 * (kt_hi - kt_lo + 1) + 2);
+      const float rho = (fabsf(sself - mrun) + 2.f + n_add) * 5.9604645e-8f;
+      dl = 2.f * (fabsf(lp - lpn) * dp + (fabsf(lp) + fabsf(lpn) + 2.f) * fmaxf(p, pn) * rho +
+                  2.3841858e-7f * (fabsf(sc) + 1.f));
+      // The typical size of the logit term (1x instead of 4x the MFMA
+      // error scale, no doubling): measured against the float64 scores of
+      // the workloads here it stays above the actual error, and the tokens
+      // where it exceeds 3e-6 of the score (a few %) hold every error
+      // above ~1e-6.
+      es = fabsf(lp - lpn) * dp * 0.25f;
     }
     if (g4 == 0) {
       part[hl * C + 16 * qt + r16] = sc;
       pdel[hl * C + 16 * qt + r16] = dl;
+      pest[hl * C + 16 * qt + r16] = es;
     }
   }
   __syncthreads();
   for (int qi = tid; qi < C; qi += 256) {
     const int t = cC + qi;
     if (t >= L) continue;
-    float s = 0.f, d = 0.f;
+    float s = 0.f, d = 0.f, e = 0.f;
     for (int hl = 0; hl < G; ++hl) {
       s += part[hl * C + qi];
       d += pdel[hl * C + qi];
+      e += pest[hl * C + qi];
     }
     const size_t o = (size_t)(b * a.Hkv + kv) * L + t;
     a.score[o] = s;
-    a.delta[o] = d;
+    // the bound, negative where the exported score is to be recomputed in
+    // float64 (its typical error may come near 1e-5 of the score)
+    a.delta[o] = e > 3e-6f * fmaxf(1.f, fabsf(s)) ? -d : d;
   }
 }
 
 // ---------------------------------------------------------- 3. select ----
-// Score of token t in float64 [P3 "Self-Saliency Score"], cooperatively by
-// the 256 threads of a workgroup: logits over the window of each of the
-// group's heads (bf16 / f32 products are exact in float64), then per head the
-// two-point KL form with 1-p summed from the other entries.
+// Score of token t in float64 [P3 "Self-Saliency Score"] by one wave: lane j
+// takes the window keys lo + j, lo + j + 64, ...; per head the logits are
+// float64 dot products (products of bf16 / float32 values are exact in
+// float64) against the query row staged in LDS (qs: this wave's [G][D]
+// floats), then the window softmax and the two-point KL form with 1-p
+// summed from the other keys. Every lane returns the sum over the heads.
 template <typename T, int D>
-__device__ __forceinline__ double score_f64(const PrefillArgs& a, int b, int kv, int t, double* lg,
-                            double* red) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+__device__ double score_f64_wave(const PrefillArgs& a, int b, int kv, int t, float* qs) {
+  const int lane = threadIdx.x & 63;
   const int W = a.W, G = a.G, L = a.L;
   const int lo = t - W + 1 > 0 ? t - W + 1 : 0;
   const int n = t - lo + 1;
   constexpr int VEC = 16 / sizeof(T);
+  auto wave_sync = [] {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  };
+  wave_sync();  // the previous token's reads of qs are done
+  const T* q = reinterpret_cast<const T*>(a.q);
+  for (int e = lane; e < G * D; e += 64)
+    qs[e] = to_f32(q[((size_t)(b * a.Hq + kv * G + e / D) * L + t) * D + e % D]);
+  wave_sync();
   const T* kg = reinterpret_cast<const T*>(a.k) + (size_t)(b * a.Hkv + kv) * L * D;
-  // window logits in float64 (products of bf16/f32 values are exact), each
-  // accumulated in index order from 16-byte row vectors
-  for (int p = tid; p < G * n; p += 256) {
-    const int hl = p / n, jj = p % n;
-    const T* qr = reinterpret_cast<const T*>(a.q) +
-                  ((size_t)(b * a.Hq + kv * G + hl) * L + t) * D;
-    const T* kr = kg + (size_t)(lo + jj) * D;
-    double s = 0.0;
-    for (int c = 0; c < D; c += VEC) {
-      const uint4 qv = *reinterpret_cast<const uint4*>(qr + c);
-      const uint4 kv4 = *reinterpret_cast<const uint4*>(kr + c);
-      const T* qe = reinterpret_cast<const T*>(&qv);
-      const T* ke = reinterpret_cast<const T*>(&kv4);
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) s += (double)to_f32(qe[e]) * (double)to_f32(ke[e]);
-    }
-    lg[hl * W + jj] = a.scale64 * s;
-  }
-  __syncthreads();
-  // one wave per head: max, the two sums, the KL form
-  for (int h = wave; h < G; h += 4) {
-    const double* x = lg + h * W;
+  double tot = 0.0;
+  for (int h = 0; h < G; ++h) {
+    double x[4];  // window of at most 256 keys
     double mx = -__builtin_huge_val();
-    for (int j = lane; j < n; j += 64) mx = x[j] > mx ? x[j] : mx;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int j = lane + 64 * s;
+      x[s] = -__builtin_huge_val();
+      if (j < n) {
+        const T* kr = kg + (size_t)(lo + j) * D;
+        double acc = 0.0;
+        for (int c = 0; c < D; c += VEC) {
+          const uint4 k4 = *reinterpret_cast<const uint4*>(kr + c);
+          const T* ke = reinterpret_cast<const T*>(&k4);
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) acc += (double)qs[h * D + c + e] * (double)to_f32(ke[e]);
+        }
+        x[s] = a.scale64 * acc;
+        mx = x[s] > mx ? x[s] : mx;
+      }
+    }
     mx = wave_max_d(mx);
-    double za = 0.0, zo = 0.0;
-    for (int j = lane; j < n; j += 64) {
-      const double e = exp(x[j] - mx);
-      za += e;
-      if (j != n - 1) zo += e;
+    double za = 0.0, zo = 0.0, es = 0.0;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int j = lane + 64 * s;
+      if (j < n) {
+        const double e = exp(x[s] - mx);
+        za += e;
+        if (j != n - 1) zo += e;
+        else es = e;
+      }
     }
     za = wave_sum_d(za);
     zo = wave_sum_d(zo);
-    if (lane == 0) {
-      const double p = exp(x[n - 1] - mx) / za, pn = zo / za;
-      double sc = 0.0;
-      if (p > 0.0) sc += p * log(p / a.eps64);
-      if (pn > 0.0) sc += pn * log(pn / (1.0 - a.eps64));
-      red[h] = sc;
-    }
+    es = wave_sum_d(es);
+    const double p = es / za, pn = zo / za;
+    double sc = 0.0;
+    if (p > 0.0) sc += p * log(p / a.eps64);
+    if (pn > 0.0) sc += pn * log(pn / (1.0 - a.eps64));
+    tot += sc;
   }
-  __syncthreads();
-  double tot = 0.0;
-  for (int h = 0; h < G; ++h) tot += red[h];
-  __syncthreads();
   return tot;
 }
 
@@ -336,141 +370,143 @@ __device__ __forceinline__ double score_f64(const PrefillArgs& a, int b, int kv,
 // [P2 固定预算路由], ranked by (score desc, position asc). The float32 scores
 // with their error bounds give, for every token, an interval; tokens whose
 // upper end is below the lambda-th largest lower end cannot be kept. If more
-// than lambda tokens remain, their scores are recomputed in float64 and the
-// ranking is made on those. Workgroups x >= n_dec compute the float64 score
-// of one token of the undecided last chunk into the decode state.
+// than lambda tokens remain, their scores are recomputed in float64 (one
+// wave per token) and the ranking is made on those. When the caller asked
+// for the scores, the tokens the score kernel marked (sign of the bound:
+// their estimated float32 error is above 2e-6 of the score) are recomputed
+// in float64 as well and their exported scores are the float64 values
+// rounded once. Workgroups x >= n_dec compute the float64
+// scores of the undecided last chunk (four tokens each, one per wave) into
+// the decode state.
+// The selection's intervals are [score - m dl, score + m dl] with the score
+// kernel's bound dl widened by SEL_MARGIN: a wider interval only sends more
+// tokens to the float64 ranking, a too narrow one could drop a token the
+// float64 ranking keeps.
+constexpr float SEL_MARGIN = 2.f;
+
 template <typename T, int D>
 __global__ __launch_bounds__(256) void select_kernel(PrefillArgs a) {
   extern __shared__ __align__(16) char smem[];
-  double* lg = reinterpret_cast<double*>(smem);     // [G * W]
-  double* red = lg + (size_t)a.G * a.W;             // [8]
-  double* s64 = red + 8;                            // [C]
-  float* lb = reinterpret_cast<float*>(s64 + a.C);  // [C]
-  float* ub = lb + a.C;                             // [C]
-  int* flag = reinterpret_cast<int*>(ub + a.C);     // [C] candidate / kept
-  int* misc = flag + a.C;                           // [4]
   const int x = blockIdx.x, kv = blockIdx.y, b = blockIdx.z;
-  const int tid = threadIdx.x, C = a.C, L = a.L, lam = a.lam;
-  const size_t ub_off = (size_t)(b * a.Hkv + kv) * L;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int C = a.C, L = a.L, lam = a.lam, G = a.G;
+  float* qs = reinterpret_cast<float*>(smem) + (size_t)wave * G * D;       // [4][G][D]
+  double* s64 = reinterpret_cast<double*>(smem + (size_t)4 * G * D * 4);  // [C]
+  float* sc = reinterpret_cast<float*>(s64 + C);                          // [C]
+  float* dl = sc + C;                                                      // [C]
+  int* flag = reinterpret_cast<int*>(dl + C);                             // [C] candidate
+  int* keep = flag + C;                                                    // [C]
+  int* list = keep + C;                                                    // [C] float64 tokens
+  int* misc = list + C;                                                    // [4]
+  const int unit = b * a.Hkv + kv;
+  const size_t ub_off = (size_t)unit * L;
 
   if (x >= a.n_dec) {
     const int c_last = (L - 1) / C;
-    const int j = x - a.n_dec, t = c_last * C + j;
-    double* pend = reinterpret_cast<double*>(a.state + (size_t)(b * a.Hkv + kv) * a.st_unit +
-                                             a.st_pending);
-    const double s = score_f64<T, D>(a, b, kv, t, lg, red);
-    if (tid == 0) {
-      pend[j] = s;
-      a.selflag[ub_off + t] = 0;
-      if (j == 0)
-        for (int i = L - c_last * C; i < C; ++i) pend[i] = __builtin_nan("");
+    const int j = (x - a.n_dec) * 4 + wave, t = c_last * C + j;
+    double* pend = reinterpret_cast<double*>(a.state + (size_t)unit * a.st_unit + a.st_pending);
+    if (t < L) {  // wave-uniform
+      const double s = score_f64_wave<T, D>(a, b, kv, t, qs);
+      if (lane == 0) {
+        pend[j] = s;
+        a.selflag[ub_off + t] = 0;
+        if (a.score_out) a.score[ub_off + t] = (float)s;
+      }
     }
+    if (x == a.n_dec && tid == 0)
+      for (int i = L - c_last * C; i < C; ++i) pend[i] = __builtin_nan("");
     return;
   }
 
   const int c = x, base = c * C;
   const int lam_c = ((c + 1) * lam <= a.m - a.W) ? lam : 0;
-  int32_t* selrow = a.sel + ((size_t)(b * a.Hkv + kv) * a.n_dec + c) * lam;
-  if (lam_c == 0 || lam_c == C) {
-    for (int j = tid; j < C; j += 256) a.selflag[ub_off + base + j] = lam_c == C ? 1 : 0;
-    for (int i = tid; i < lam; i += 256) selrow[i] = lam_c == C ? base + i : -1;
-    return;
-  }
-  if (C <= 64) {
-    // One wave, token j in lane j: the lam_c-th largest lower bound by
-    // (lb desc, index asc), taken by lam_c rounds of removing the largest;
-    // the candidates are the tokens whose upper bound reaches it. With
-    // exactly lam_c of them (the usual case) they are the kept tokens and
-    // the chunk is done here; otherwise the bounds go to LDS for the
-    // float64 ranking below.
-    if (tid < 64) {
-      const int lane = tid;
-      float lbj = STILL_NEG_INF, ubj = STILL_NEG_INF;
-      if (lane < C) {
-        const float sc = a.score[ub_off + base + lane], d = a.delta[ub_off + base + lane];
-        lbj = sc - d;
-        ubj = sc + d;
-      }
-      float x = lane < C ? lbj : STILL_NEG_INF, LBv = STILL_NEG_INF;
-      bool gone = lane >= C;
-      for (int k = 0; k < lam_c; ++k) {
-        float m = row_max<16>(gone ? STILL_NEG_INF : x);
-        m = fmax_nn(m, xor16f(m));
-        m = fmax_nn(m, xor32f(m));
-        const uint64_t at = __builtin_amdgcn_ballot_w64(!gone && x == m);
-        const int first = at ? (int)__builtin_ctzll(at) : 64;  // lowest index among the maxima
-        if (lane == first) gone = true;
-        LBv = m;
-      }
-      const bool cand = lane < C && ubj >= LBv;
-      const uint64_t cm = __builtin_amdgcn_ballot_w64(cand);
-      if ((int)__builtin_popcountll(cm) == lam_c) {
-        if (lane < C) a.selflag[ub_off + base + lane] = cand ? 1 : 0;
-        if (cand) selrow[__builtin_popcountll(cm & ((1ull << lane) - 1ull))] = base + lane;
-        if (lane == 0) misc[2] = 0;
-      } else {
-        if (lane < C) {
-          lb[lane] = lbj;
-          ub[lane] = ubj;
-        }
-        if (lane == 0) {
-          misc[0] = __float_as_int(LBv);
-          misc[2] = 1;
-        }
-      }
-    }
-    __syncthreads();
-    if (misc[2] == 0) return;  // uniform
-  } else {
-    for (int j = tid; j < C; j += 256) {
-      const float s = a.score[ub_off + base + j], d = a.delta[ub_off + base + j];
-      lb[j] = s - d;
-      ub[j] = s + d;
-    }
-    __syncthreads();
-    // lambda-th largest lower bound (rank by (lb desc, index asc))
-    for (int j = tid; j < C; j += 256) {
-      int r = 0;
-      for (int i = 0; i < C; ++i) r += (lb[i] > lb[j] || (lb[i] == lb[j] && i < j)) ? 1 : 0;
-      if (r == lam_c - 1) misc[0] = __float_as_int(lb[j]);
-    }
-  }
-  if (tid == 0) misc[1] = 0;
-  __syncthreads();
-  const float LB = __int_as_float(misc[0]);
+  const bool partial = lam_c > 0 && lam_c < C;  // else none or all are kept
+  int32_t* selrow = a.sel + ((size_t)unit * a.n_dec + c) * lam;
   for (int j = tid; j < C; j += 256) {
-    flag[j] = ub[j] >= LB ? 1 : 0;
-    if (flag[j]) atomicAdd(&misc[1], 1);
+    sc[j] = a.score[ub_off + base + j];
+    dl[j] = a.delta[ub_off + base + j];  // sign: export refinement wanted
+  }
+  if (tid == 0) {
+    misc[0] = 0;  // candidates
+    misc[1] = 0;  // float64 list
   }
   __syncthreads();
-  const int n_cand = misc[1];
-  if (n_cand > lam_c) {
-    for (int j = 0; j < C; ++j) {
-      if (!flag[j]) continue;  // uniform: flag is in LDS
-      const double s = score_f64<T, D>(a, b, kv, base + j, lg, red);
-      if (tid == 0) s64[j] = s;
-      __syncthreads();
+  // the lam_c-th largest lower bound, ranked by (lower bound desc, index asc)
+  if (partial) {
+    if (C <= 64) {  // one wave, token j in lane j: lam_c rounds of removing the largest
+      if (tid < 64) {
+        float xl = lane < C ? sc[lane] - SEL_MARGIN * fabsf(dl[lane]) : STILL_NEG_INF, LBv = STILL_NEG_INF;
+        bool gone = lane >= C;
+        for (int k = 0; k < lam_c; ++k) {
+          float m = row_max<16>(gone ? STILL_NEG_INF : xl);
+          m = fmax_nn(m, xor16f(m));
+          m = fmax_nn(m, xor32f(m));
+          const uint64_t at = __builtin_amdgcn_ballot_w64(!gone && xl == m);
+          const int first = at ? (int)__builtin_ctzll(at) : 64;  // lowest index among the maxima
+          if (lane == first) gone = true;
+          LBv = m;
+        }
+        if (lane == 0) misc[2] = __float_as_int(LBv);
+      }
+    } else {
+      for (int j = tid; j < C; j += 256) {
+        const float lj = sc[j] - SEL_MARGIN * fabsf(dl[j]);
+        int r = 0;
+        for (int i = 0; i < C; ++i) {
+          const float li = sc[i] - SEL_MARGIN * fabsf(dl[i]);
+          r += (li > lj || (li == lj && i < j)) ? 1 : 0;
+        }
+        if (r == lam_c - 1) misc[2] = __float_as_int(lj);
+      }
     }
-    for (int j = tid; j < C; j += 256) {
-      int r = 0;
-      if (flag[j])
+  }
+  __syncthreads();
+  const float LB = __int_as_float(misc[2]);
+  for (int j = tid; j < C; j += 256) {
+    const bool cand = partial && sc[j] + SEL_MARGIN * fabsf(dl[j]) >= LB;
+    flag[j] = cand ? 1 : 0;
+    if (cand) atomicAdd(&misc[0], 1);
+  }
+  __syncthreads();
+  const bool rank64 = partial && misc[0] > lam_c;  // uniform
+  for (int j = tid; j < C; j += 256) {
+    const bool exported = a.score_out && __builtin_signbit(dl[j]);
+    if ((rank64 && flag[j]) || exported) list[atomicAdd(&misc[1], 1)] = j;
+  }
+  __syncthreads();
+  const int n_list = misc[1];
+  for (int i = wave; i < n_list; i += 4) {  // wave-uniform
+    const int j = list[i];
+    const double s = score_f64_wave<T, D>(a, b, kv, base + j, qs);
+    if (lane == 0) {
+      s64[j] = s;
+      if (a.score_out) a.score[ub_off + base + j] = (float)s;
+    }
+  }
+  __syncthreads();
+  for (int j = tid; j < C; j += 256) {
+    bool kept = lam_c == C;
+    if (partial) {
+      kept = flag[j] != 0;
+      if (rank64 && kept) {
+        int r = 0;
         for (int i = 0; i < C; ++i)
           r += (flag[i] && (s64[i] > s64[j] || (s64[i] == s64[j] && i < j))) ? 1 : 0;
-      lb[j] = (flag[j] && r < lam_c) ? 1.f : 0.f;
+        kept = r < lam_c;
+      }
     }
-  } else {
-    for (int j = tid; j < C; j += 256) lb[j] = flag[j] ? 1.f : 0.f;
+    keep[j] = kept ? 1 : 0;
   }
   __syncthreads();
   for (int j = tid; j < C; j += 256) {
-    const bool kept = lb[j] != 0.f;
-    a.selflag[ub_off + base + j] = kept ? 1 : 0;
-    if (kept) {
+    a.selflag[ub_off + base + j] = (uint8_t)keep[j];
+    if (keep[j]) {
       int k = 0;
-      for (int i = 0; i < j; ++i) k += lb[i] != 0.f ? 1 : 0;
+      for (int i = 0; i < j; ++i) k += keep[i];
       selrow[k] = base + j;
     }
   }
+  for (int i = lam_c + tid; i < lam; i += 256) selrow[i] = -1;
 }
 
 // ----------------------------------------- shared block machinery (4-6) ----
@@ -1035,36 +1071,151 @@ __device__ __forceinline__ void load_state(const BlkPtr<T, D>& P, const float* S
     *reinterpret_cast<f32x4*>(P.SP + e) = *reinterpret_cast<const f32x4*>(Sfl + e);
 }
 
-template <typename T, int D>
-__device__ __forceinline__ void store_state_rowmajor(const BlkPtr<T, D>& P, float* S) {
-  using B_ = Blk<T, D>;
-  const int r16 = opaque_tid() & 15;
-  for (int e = opaque_tid(); e < B_::NPAIR * 64; e += 512) {
-    const int p = e >> 6, ln = e & 63, g4 = ln >> 4;
-    const int vt = p / (D / 32), bb = p % (D / 32);
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const float* sp = P.SP + ((size_t)(2 * p + q) * 64 + ln) * 4;
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        S[(size_t)(32 * bb + 16 * q + 4 * g4 + i) * D + 16 * vt + (ln & 15)] = sp[i];
-    }
-  }
-  (void)r16;
-}
-
 // ---------------------------------------------------- 4. state_delta ----
 // Super-chunk s folds the chunks [cf(sK), cf(sK+K)) into the state, cf(c) =
-// chunks wholly before the window of chunk c. This kernel sums their
-// unkept tokens' phi(k) v^T (and phi(k)) so the scan can give every
-// super-chunk its starting state. Every 32-key group lands in float64 sums on
-// its own: a single 8x-norm token can make a group's sum ~1e4, where one
-// float32 rounding is already ~5e-4.
+// chunks wholly before the window of chunk c; the last super-chunk's delta
+// runs to cf(T-1), so that the sum of all deltas is the exported state. This
+// kernel sums their unkept tokens' phi(k) v^T (and phi(k)) so the scan can
+// give every super-chunk its starting state and the decode state its S, z.
+// Every 32-key group lands in float64 sums on its own: a single 8x-norm token
+// can make a group's sum ~1e4, where one float32 rounding is already ~5e-4.
+//
+// Keys with |k|^2 max|v| >= BIG_KV fold through a float64 path instead of
+// the MFMAs: the bf16 MFMA accumulates the 128 products of a feature logit
+// x.F with an error of up to about 2^-24 times the sum of their magnitudes
+// (measured on gfx950), i.e. ~1e-5 absolute for a key of norm ~300, which
+// moves phi(k) by ~1e-5 relative and the state entry it dominates (~1e4) by
+// ~1e-1. Such keys are rare (the largest 1-2 % of |k|^2 max|v| in the
+// workloads here); their logits, NP-Map and rank-1 update are float64.
+constexpr float BIG_KV = 16384.f;
+
+template <typename T, int D>
+struct BigScratch {  // in the state region SP, which state_delta does not use
+  double* part;  // [512 / D][D] partial logits
+  double* phi;   // [D]
+  double* red;   // [8]
+  float* vmx;    // [64] max |v| per key
+  uint32_t* bits;  // [2] big keys of the block
+  __device__ BigScratch(const BlkPtr<T, D>& P) {
+    char* b = reinterpret_cast<char*>(P.SP);
+    part = reinterpret_cast<double*>(b);
+    phi = part + 512;
+    red = phi + D;
+    vmx = reinterpret_cast<float*>(red + 8);
+    bits = reinterpret_cast<uint32_t*>(vmx + 64);
+  }
+};
+
+// value c of key kk of the block in LDS, as float
+template <typename T, int D>
+__device__ __forceinline__ float blk_v(const BlkPtr<T, D>& P, int kk, int c) {
+  using B_ = Blk<T, D>;
+  if constexpr (B_::TR) return to_f32(P.VTs[kk * B_::VR + c]);
+  else return to_f32(P.VTs[c * B_::VS + perm_col(kk)]);
+}
+
+// Marks the block's fold keys with |k|^2 max|v| >= BIG_KV: clears their
+// fmask (the MFMA fold skips them) and returns them as a bit mask (same in
+// every thread). Ends with a barrier.
+template <typename T, int D>
+__device__ __forceinline__ uint64_t mark_big_keys(const BlkPtr<T, D>& P, const BigScratch<T, D>& Z) {
+  const int tid = threadIdx.x;
+  {  // 8 threads per key, D/8 values each
+    const int kk = tid >> 3, part = tid & 7;
+    float m = 0.f;
+#pragma unroll
+    for (int c = 0; c < D / 8; ++c) m = fmaxf(m, fabsf(blk_v<T, D>(P, kk, part * (D / 8) + c)));
+    m = row_max<8>(m);
+    if (part == 0) Z.vmx[kk] = m;
+  }
+  __syncthreads();
+  if (tid < 64) {
+    const bool big = P.fmask[tid] != 0.f && P.kstat[128 + tid] * Z.vmx[tid] >= BIG_KV;
+    const uint64_t bits = __builtin_amdgcn_ballot_w64(big);
+    if (big) P.fmask[tid] = 0.f;
+    if (tid == 0) {
+      Z.bits[0] = (uint32_t)bits;
+      Z.bits[1] = (uint32_t)(bits >> 32);
+    }
+  }
+  __syncthreads();
+  return ((uint64_t)Z.bits[1] << 32) | Z.bits[0];
+}
+
+// Float64 fold of key kk of the block: logits x.F (every product of bf16 /
+// float32 inputs is exact in float64), NP-Map [P3 "NP-Map: Norm-Preserving
+// Feature Map"] and the rank-1 update of the calling thread's state entries
+// sum[vt][i] = S[16w + 4g + i][16vt + r] (waves w < D/16) and z[16w + r]
+// (lanes g == 0). Every thread calls it; it contains barriers.
+template <typename T, int D>
+__device__ __forceinline__ void big_key_fold(const BlkPtr<T, D>& P, const BigScratch<T, D>& Z, int kk,
+                                             double (&sum)[D / 16][4], double& zsum) {
+  using B_ = Blk<T, D>;
+  constexpr int NPART = 512 / D, TP = D / NPART;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, r16 = lane & 15, g4 = lane >> 4;
+  {
+    const int j = tid % D, part = tid / D;
+    double u = 0.0;
+#pragma unroll 8
+    for (int ii = 0; ii < TP; ++ii) {
+      const int i = part * TP + ii;
+      const int kb = i >> 5, g = (i & 31) >> 3, s = i & 7;
+      const float f = to_f32(P.FT[(((j >> 4) * (D / 32) + kb) * 64 + 16 * g + (j & 15)) * 8 + s]);
+      u += (double)to_f32(P.Ks[kk * B_::KS + i]) * (double)f;
+    }
+    Z.part[part * D + j] = u;
+  }
+  __syncthreads();
+  double uj = 0.0, e = 0.0, k2 = 0.0;
+  if (tid < D) {
+#pragma unroll
+    for (int p = 0; p < NPART; ++p) uj += Z.part[p * D + tid];
+    const double kx = (double)to_f32(P.Ks[kk * B_::KS + tid]);
+    const double mx = wave_max_d(uj);
+    k2 = wave_sum_d(kx * kx);
+    if (lane == 0) {
+      Z.red[2 * wave] = mx;
+      Z.red[2 * wave + 1] = k2;
+    }
+  }
+  __syncthreads();
+  if (tid < D) {
+    double mx = Z.red[0];
+    k2 = Z.red[1];
+#pragma unroll
+    for (int w = 1; w < D / 64; ++w) {
+      mx = Z.red[2 * w] > mx ? Z.red[2 * w] : mx;
+      k2 += Z.red[2 * w + 1];
+    }
+    e = exp(uj - mx);
+    const double ss = wave_sum_d(e * e);
+    if (lane == 0) Z.red[4 + wave] = ss;
+  }
+  __syncthreads();
+  if (tid < D) {
+    double ss = 0.0;
+#pragma unroll
+    for (int w = 0; w < D / 64; ++w) ss += Z.red[4 + w];
+    Z.phi[tid] = sqrt(k2) * e / sqrt(ss);
+  }
+  __syncthreads();
+  if (wave < B_::NFT) {
+#pragma unroll
+    for (int vt = 0; vt < D / 16; ++vt) {
+      const double vv = (double)blk_v<T, D>(P, kk, 16 * vt + r16);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sum[vt][i] += Z.phi[16 * wave + 4 * g4 + i] * vv;
+    }
+    if (g4 == 0) zsum += Z.phi[16 * wave + r16];
+  }
+}
+
 template <typename T, int D>
 __global__ __launch_bounds__(512) void state_delta_kernel(PrefillArgs a) {
   using B_ = Blk<T, D>;
   extern __shared__ __align__(16) char smem[];
   const BlkPtr<T, D> P(smem);
+  const BigScratch<T, D> Z(P);
   const int s = blockIdx.x, kv = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, r16 = lane & 15, g4 = lane >> 4;
   const int unit = b * a.Hkv + kv;
@@ -1080,7 +1231,8 @@ __global__ __launch_bounds__(512) void state_delta_kernel(PrefillArgs a) {
     for (int i = 0; i < 4; ++i) sum[vt][i] = 0.0;
   double zsum = 0.0;
   const int lo = full_chunks_before(s * a.K, a.W, a.C) * a.C;
-  const int hi = full_chunks_before(s * a.K + a.K, a.W, a.C) * a.C;
+  const int hi = (s == a.NS - 1 ? full_chunks_before(a.T - 1, a.W, a.C)
+                                : full_chunks_before(s * a.K + a.K, a.W, a.C)) * a.C;
   // block blo + 64 is issued as soon as block blo is in LDS (past hi the
   // loads read zeros past the buffer range)
   BlkRegs<T, D, 512> R;
@@ -1090,6 +1242,7 @@ __global__ __launch_bounds__(512) void state_delta_kernel(PrefillArgs a) {
     commit_block<T, D, 512>(P, R, lo, hi);
     issue_block<T, D, 512>(R, kr, vr, kv_bytes, sfr, blk_range(blo + 64, hi));
     __syncthreads();
+    const uint64_t big = mark_big_keys<T, D>(P, Z);
     f32x4 ph[4];
     block_phi<T, D>(P, ph, false);
     if (wave < B_::NFT) {
@@ -1106,6 +1259,8 @@ __global__ __launch_bounds__(512) void state_delta_kernel(PrefillArgs a) {
       }
       zsum += (double)fold_zsum<T, D>(P, ph);
     }
+    for (uint64_t m = big; m; m &= m - 1)  // uniform
+      big_key_fold<T, D>(P, Z, (int)__builtin_ctzll(m), sum, zsum);
   }
   float* dst = a.dS + ((size_t)unit * a.NS + s) * (D * D + D);
   if (wave < B_::NFT) {
@@ -1120,10 +1275,17 @@ __global__ __launch_bounds__(512) void state_delta_kernel(PrefillArgs a) {
 }
 
 // ----------------------------------------------------- 5. state_scan ----
-__global__ __launch_bounds__(256) void state_scan_kernel(float* dS, int NS, int n_elem) {
+// Exclusive prefix over the super-chunk deltas, in place (the starting state
+// of every super-chunk), and their total, the exported state S (row-major)
+// and z, each rounded to float32 once from a float64 running sum.
+template <int D>
+__global__ __launch_bounds__(256) void state_scan_kernel(float* dS, int NS, char* state, long st_unit,
+                                                         long st_S, long st_z) {
+  constexpr int n_elem = D * D + D;
   const int e = blockIdx.x * 256 + threadIdx.x;
   if (e >= n_elem) return;
-  float* base = dS + (size_t)(blockIdx.y + gridDim.y * blockIdx.z) * NS * n_elem + e;
+  const int unit = blockIdx.y + gridDim.y * blockIdx.z;
+  float* base = dS + (size_t)unit * NS * n_elem + e;
   double run = 0.0;  // float64 running sum: one float32 rounding per start
   constexpr int NB = 32;  // loads of a batch in flight together (indices
                           // past the end re-read the last entry, unused)
@@ -1137,6 +1299,17 @@ __global__ __launch_bounds__(256) void state_scan_kernel(float* dS, int NS, int 
         base[(size_t)(s0 + i) * n_elem] = (float)run;
         run += (double)x[i];
       }
+  }
+  char* st = state + (size_t)unit * st_unit;
+  if (e < D * D) {
+    // fragment-linear index ((2p + h) * 64 + lane) * 4 + i, pair p = vt *
+    // (D/32) + bb, lane = 16g + r: S[32bb + 16h + 4g + i][16vt + r]
+    const int i = e & 3, ln = (e >> 2) & 63, ph = e >> 8;
+    const int h = ph & 1, p = ph >> 1, vt = p / (D / 32), bb = p % (D / 32);
+    const int row = 32 * bb + 16 * h + 4 * (ln >> 4) + i, col = 16 * vt + (ln & 15);
+    reinterpret_cast<float*>(st + st_S)[row * D + col] = (float)run;
+  } else {
+    reinterpret_cast<float*>(st + st_z)[e - D * D] = (float)run;
   }
 }
 
@@ -1465,7 +1638,9 @@ __global__ __launch_bounds__(512) void attend_kernel(PrefillArgs a) {
       Frag<H> vf[D / 16][2];
       vf[0][0] = Pb.ld_v(0, 0, lane);
       vf[0][1] = Pb.ld_v(0, 1, lane);
-      Frag<H> pf[HPW][2];
+      // weights as H hi + lo parts (fp16: ~22 significant bits; one fp16
+      // part alone moves y by up to 2^-12 of the value spread)
+      Frag<H> pf[HPW][2], pl[HPW][2];
 #pragma unroll
       for (int j = 0; j < HPW; ++j) {
         const float mxj = max_over_g(mx[j]) * scale2;
@@ -1492,11 +1667,15 @@ __global__ __launch_bounds__(512) void attend_kernel(PrefillArgs a) {
           for (int i = 0; i < 4; ++i) pv[kt][i] = exp2_acc<T>(fmaf(st[j][kt][i], scale2, nmn));
         // weights as H; the running sum comes from the same rounded weights
         // through a ones-row MFMA
-        pf[j][0] = frag_from<H>(pv[0], pv[1]);
-        pf[j][1] = frag_from<H>(pv[2], pv[3]);
+        split2_frag<H>(pv[0], pv[1], pf[j][0], pl[j][0]);
+        split2_frag<H>(pv[2], pv[3], pf[j][1], pl[j][1]);
         const Frag<H> one = ones_frag<H>();
         mma(lacc[j], one, pf[j][0]);
         mma(lacc[j], one, pf[j][1]);
+        if constexpr (sizeof(H) == 2) {
+          mma(lacc[j], one, pl[j][0]);
+          mma(lacc[j], one, pl[j][1]);
+        }
       }
 #pragma unroll
       for (int dt = 1; dt < D / 16; ++dt) {
@@ -1509,11 +1688,15 @@ __global__ __launch_bounds__(512) void attend_kernel(PrefillArgs a) {
         for (int j = 0; j < HPW; ++j) {
           mma(O[j][dt], vf[dt][0], pf[j][0]);
           mma(O[j][dt], vf[dt][1], pf[j][1]);
+          if constexpr (sizeof(H) == 2) {
+            mma(O[j][dt], vf[dt][0], pl[j][0]);
+            mma(O[j][dt], vf[dt][1], pl[j][1]);
+          }
         }
       // value tiles 1 and 2 first (tile 0 is in flight), then each tile's
       // MFMAs with the reads of the tile three ahead (two transposing reads
       // per fragment)
-      if constexpr (sizeof(T) == 2) lds_mfma_pipeline<8, 2 * (D / 16 - 3), HPW, 2, 3 * 2 * HPW>();
+      if constexpr (sizeof(T) == 2) lds_mfma_pipeline<8, 2 * (D / 16 - 3), 2 * HPW, 2, 3 * 4 * HPW>();
     };
     auto issue_pool = [&](int pb) __attribute__((always_inline)) {
       const int blo = 64 * pb;
@@ -1607,12 +1790,6 @@ __global__ __launch_bounds__(512) void attend_kernel(PrefillArgs a) {
           *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.out) + ob + (size_t)t * D + 16 * dt + 4 * g4) =
               O[j][dt] * inv;
       }
-    }
-    if (c == a.T - 1 && hg == 0) {
-      __syncthreads();
-      char* st = a.state + (size_t)unit * a.st_unit;
-      store_state_rowmajor<T, D>(P, reinterpret_cast<float*>(st + a.st_S));
-      if (tid < D) reinterpret_cast<float*>(st + a.st_z)[tid] = (float)P.zs[tid];
     }
   }
 }

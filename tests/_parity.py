@@ -4,8 +4,9 @@ oracle on the same seeded inputs, and compare them to the stated bars.
 Bars: selected indices bit-exact; float32 workloads within 1e-4 max-abs
 (outputs and state); bfloat16 workloads within 2e-2 max-abs on the float32
 output of the same kernels, and on the bfloat16 output within 2e-2 plus half
-a bfloat16 ulp of the reference, with relative L2 <= 1e-2; state (float32 in
-both cases) within the same max-abs bar.
+a bfloat16 ulp of the reference, with relative L2 <= 1e-2; the state (float32
+in both cases) within the dtype's max-abs bar; float32 scores within 1e-5
+relative to max(1, |score|).
 """
 from __future__ import annotations
 
@@ -72,25 +73,27 @@ def check_outputs(y_gpu: np.ndarray, y_ref: np.ndarray, dtype: str, out_fp32: bo
         assert rel <= 1e-2, (what, rel)
 
 
-# The state is float32 and its entries reach 1e4 or more (sums over
-# thousands of tokens, 8x-norm tokens contribute products of ~1e4). float32
-# storage alone has an ulp of ~4e-3 at 3.9e4, and the float32 feature logits
-# x F of an 8x-norm key carry ~2e-6 absolute error, i.e. ~2e-6 relative error
-# in phi(k) and ~2e-2 on one product of 1e4. The state bar is therefore the
-# max-abs bar at unit scale plus 16 float32 ulps of the reference value.
-STATE_RTOL = 16 * 2.0 ** -23
-
-
 def check_state(got: np.ndarray, ref: np.ndarray, dtype: str, what=""):
+    """State (float32 in both dtypes) against the float64 oracle: the
+    max-abs bar of the dtype (1e-4 float32, 2e-2 bfloat16) and its relative
+    L2 bar (1e-6 float32, 1e-2 bfloat16)."""
     atol = 1e-4 if dtype == "f32" else 2e-2
-    diff = np.abs(got.astype(np.float64) - ref)
-    err = float(diff.max()) if ref.size else 0.0
-    excess = float((diff - STATE_RTOL * np.abs(ref)).max()) if ref.size else 0.0
+    err = float(np.abs(got.astype(np.float64) - ref).max()) if ref.size else 0.0
     rel = float(np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-30)) if ref.size else 0.0
-    print("    %s max_abs=%.3e (|ref| max %.3g) beyond-rtol %.3e rel_l2=%.2e"
-          % (what, err, float(np.abs(ref).max()) if ref.size else 0, excess, rel), flush=True)
-    assert excess <= atol, (what, err, excess)
+    print("    %s max_abs=%.3e (|ref| max %.3g) rel_l2=%.2e"
+          % (what, err, float(np.abs(ref).max()) if ref.size else 0, rel), flush=True)
+    assert err <= atol, (what, err)
     assert rel <= (1e-6 if dtype == "f32" else 1e-2), (what, rel)
+
+
+SCORE_RTOL = 1e-5  # float32 score vs the float64 oracle, relative to max(1, |score|)
+
+
+def check_scores(got: np.ndarray, ref: np.ndarray, what="score"):
+    serr = np.abs(got.astype(np.float64) - ref) / np.maximum(1.0, np.abs(ref))
+    worst = float(serr.max()) if serr.size else 0.0
+    print("    %s max rel err %.3e" % (what, worst), flush=True)
+    assert worst <= SCORE_RTOL, (what, worst)
 
 
 def unit_rows(wl: Workload, units: Sequence[Tuple[int, int]]):
@@ -113,10 +116,7 @@ def compare_prefill(wl: Workload, g: Dict[str, torch.Tensor], o: Dict[str, np.nd
         mism = np.argwhere(sg != o["sel"])
         assert mism.size == 0, "selection mismatch at %s" % (mism[:5].tolist(),)
     # scores: float32 evaluation vs float64
-    sc = np.stack([g["score"][b, kv].numpy() for b, kv in units]).astype(np.float64)
-    serr = np.abs(sc - o["score"]) / np.maximum(1.0, np.abs(o["score"]))
-    print("    score max rel err %.3e" % float(serr.max()), flush=True)
-    assert float(serr.max()) <= 1e-3
+    check_scores(np.stack([g["score"][b, kv].numpy() for b, kv in units]), o["score"])
     if not check_state_too:
         return
     check_state(g["S"][idx].numpy(), o["S"], wl.dtype, "S")

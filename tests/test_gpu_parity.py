@@ -43,6 +43,11 @@ SHAPES = [
     small("bf16_one_token", "bf16", 1, 4, 1, 64, 1, 16, 32, 64, 4),
     small("bf16_one_chunk", "bf16", 1, 4, 1, 64, 64, 16, 64, 64, 1),
     small("bf16_one_decided", "bf16", 1, 4, 1, 64, 65, 16, 64, 80, 1),
+    # more than 1024 kept tokens: the walk reads pool positions from the
+    # global list instead of LDS (m - W = 36 * 32 = 1152, lambda = 36)
+    small("bf16_pool_global_list", "bf16", 1, 4, 1, 64, 2048, 64, 64, 64 + 36 * 32, 32),
+    # the widest window (W = 256) with the widest chunk
+    small("bf16_W256_C128", "bf16", 1, 4, 1, 128, 900, 256, 128, 256 + 8 * 6, 8),
 ]
 
 
@@ -82,13 +87,27 @@ def test_llama8b_L16K_workload():
 
 
 @pytest.mark.timeout(900)
-def test_llama8b_L64K_workload_sampled_units():
-    """All 8 kv heads run on the GPU; the oracle checks kv heads 0 and 5."""
+def test_llama8b_L64K_workload():
+    """Every (batch row, kv head) unit of the 64K workload against the oracle."""
     wl = WORKLOADS["llama8b_bf16_L64K"]
     x = make_inputs(wl)
-    units = [(0, 0), (0, 5)]
-    o = P.oracle(wl, x, units=units)
-    P.compare_prefill(wl, P.gpu_prefill(wl, x, fp32_out=True), o, units=units, out_fp32=True)
+    o = P.oracle(wl, x)
+    P.compare_prefill(wl, P.gpu_prefill(wl, x, fp32_out=True), o, out_fp32=True)
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name", ["llama8b_bf16_L16K", "llama8b_bf16_L64K"])
+def test_softmax_branch_alone_full_size(name):
+    """With every gate at 0 the output is the softmax branch alone over the
+    window, own-chunk prefix and kept pool (no linear weight enters), so the
+    kept-pool gather path is checked at full size without being diluted by
+    the linear branch's mass."""
+    wl = WORKLOADS[name]
+    x = make_inputs(wl)
+    x["gate"] = torch.zeros_like(x["gate"])
+    o = P.oracle(wl, x)
+    P.compare_prefill(wl, P.gpu_prefill(wl, x, fp32_out=True), o, out_fp32=True,
+                      check_state_too=False)
 
 
 def test_prefill_deterministic():
@@ -133,6 +152,9 @@ DECODE_SHAPES = [
     (small("dec_bf16_W_lt_C", "bf16", 1, 4, 1, 64, 100, 16, 32, 16 + 3 * 10, 10), 100, 75),
     (small("dec_bf16_W_gt_C", "bf16", 1, 2, 1, 64, 70, 48, 16, 48 + 2 * 12, 12), 70, 60),
     (small("dec_bf16_fill", "bf16", 1, 4, 1, 64, 96, 8, 16, 8 + 2 * 4, 4), 96, 80),
+    (small("dec_bf16_G1", "bf16", 2, 2, 2, 128, 150, 32, 32, 32 + 7 * 3, 7), 150, 70),
+    (small("dec_bf16_G8", "bf16", 1, 8, 1, 128, 200, 64, 64, 64 + 5 * 4, 5), 200, 70),
+    (small("dec_bf16_W256_C128", "bf16", 1, 4, 1, 128, 400, 256, 128, 256 + 5 * 8, 5), 400, 140),
 ]
 
 
@@ -177,7 +199,8 @@ def test_decode_matches_prefill_of_extended_sequence(case):
 @pytest.mark.timeout(900)
 def test_decode_workload_sampled_units():
     """Batch 64 at 16K context: prefill on the GPU, 64 decode steps (one
-    chunk-boundary decision); the oracle checks two sampled units."""
+    chunk-boundary decision); the oracle checks 16 units spread over the
+    batch rows and kv heads."""
     wl = WORKLOADS["decode_bf16_B64_ctx16K"]
     L0, n = wl.seq_len, wl.decode_steps
     x = make_inputs(wl, device="cuda")
@@ -187,9 +210,10 @@ def test_decode_workload_sampled_units():
     bufs = still.PrefillBuffers(p, L0)
     still.run_prefill(p, x, bufs)
     outs, sels = P.run_decode(wl, bufs.state, p, x, toks, L0, fp32_out=True)
-    units = [(0, 0), (37, 5)]
+    units = [(b, (3 * i) % wl.n_kv_heads) for i, b in
+             enumerate([0, 4, 9, 13, 17, 21, 26, 30, 33, 37, 42, 46, 50, 55, 59, 63])]
     qs, ks, vs, Fs, gs = P.concat_units(x, toks, wl, units)
-    print("  oracle 2 units, %d tokens" % (L0 + n), flush=True)
+    print("  oracle %d units, %d tokens" % (len(units), L0 + n), flush=True)
     o = rec.run_units(qs, ks, vs, Fs, gs, window=wl.window, chunk=wl.chunk, budget=wl.budget,
                       t_max=wl.t_max, n_threads=P.n_threads())
     G = wl.group
@@ -222,3 +246,52 @@ def test_prefill_then_decode_equals_longer_prefill():
     sv = still.state_views(p, g["_state"])
     assert torch.equal(sv["pool_pos"].cpu(), full["pool_pos"])
     assert (sv["S"].cpu() - full["S"]).abs().max().item() <= 2e-2
+
+
+def test_decode_position_mismatch_sets_error_word():
+    """A decode step whose position does not follow the state sets the
+    state's error word (meta[2] = STILL_ESTATE), writes nothing else, and
+    later steps are skipped until the state is reset."""
+    wl = small("dec_err", "bf16", 1, 4, 1, 64, 100, 16, 32, 16 + 3 * 10, 10)
+    x = make_inputs(wl)
+    toks = make_decode_tokens(wl, 2)
+    g = P.gpu_prefill(wl, x, keep_device=True)
+    p = g["_params"]
+    before = g["_state"].clone()
+    xd = {k: v.cuda() for k, v in x.items()}
+    out = torch.full((wl.batch, wl.n_q_heads, wl.head_dim), 7.0, dtype=torch.bfloat16, device="cuda")
+    still.still_decode_step(p, 101, toks["q"][0].cuda(), toks["k"][0].cuda(), toks["v"][0].cuda(),
+                            xd["fmap_w"], xd["gate"], g["_state"], out)  # the state holds 100
+    torch.cuda.synchronize()
+    sv = still.state_views(p, g["_state"])
+    assert int(sv["meta"][0, 2]) == still.STILL_ESTATE
+    assert int(sv["meta"][0, 0]) == 100
+    lay = still.still_state_layout_get(p)
+    changed = (g["_state"].cpu() != before.cpu()).nonzero().flatten().tolist()
+    assert all(lay.meta + 16 <= i < lay.meta + 24 for i in changed), changed
+    assert torch.all(out.float() == 7.0)
+    # a step at the right position is refused too while the error word is set
+    still.still_decode_step(p, 100, toks["q"][1].cuda(), toks["k"][1].cuda(), toks["v"][1].cuda(),
+                            xd["fmap_w"], xd["gate"], g["_state"], out)
+    torch.cuda.synchronize()
+    assert int(still.state_views(p, g["_state"])["meta"][0, 0]) == 100
+
+
+def test_state_save_restore_resumes_exactly():
+    """The decode state is plain device memory: copied to the host and back
+    into a fresh buffer, decoding resumes exactly as it would have without
+    the interruption (same outputs and kept positions, same final state)."""
+    wl = small("dec_resume", "bf16", 2, 8, 2, 128, 190, 64, 64, 64 + 5 * 2, 5)
+    x = make_inputs(wl)
+    toks = make_decode_tokens(wl, 90)
+    g = P.gpu_prefill(wl, x, keep_device=True)
+    p = still.params_for(wl)
+    xd = {k: v.cuda() for k, v in x.items()}
+    td = {k: v.cuda() for k, v in toks.items()}
+    saved = g["_state"].cpu()  # the checkpoint, in host memory
+    outs_a, sels_a = P.run_decode(wl, g["_state"], p, xd, td, 190)
+    restored = saved.cuda()
+    outs_b, sels_b = P.run_decode(wl, restored, p, xd, td, 190)
+    assert torch.equal(outs_a, outs_b)
+    assert torch.equal(sels_a, sels_b)
+    assert torch.equal(g["_state"].cpu(), restored.cpu())
