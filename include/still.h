@@ -46,6 +46,21 @@
  *     budget >= window; t_max >= 1; n_q_heads a multiple of n_kv_heads
  *     with G = n_q_heads / n_kv_heads <= 8. All sequences of a batch share
  *     one length / position.
+ *   - Thread safety: every entry point may be called from several host
+ *     threads at once (on different buffers). The only shared host state is
+ *     a mutex-protected table of per-device kernel attributes.
+ *   - Value range (bf16): values and NP-Map features enter their products
+ *     as fp16, so every |v_i| and every key / query norm |x| (the NP-Map
+ *     feature of x has norm |x|) must stay below 65504; larger inputs give
+ *     undefined outputs (inf / NaN). This is not checked.
+ *   - Accuracy: bf16 outputs and the float32 state follow the float64
+ *     definition to about 2e-3 max-abs on the 16K and 64K workloads (state
+ *     entries up to 4e4); float32 scores to 1e-6 of max(1, |score|) (tokens
+ *     whose estimated float32 error is larger are recomputed in float64).
+ *     float32 data: logits, features and weights are float32 products, so
+ *     the error grows with |q| |k| scale max|v|; it stays below 1e-4 for
+ *     inputs of the small float32 workload's range (norms ~ sqrt(d) times a
+ *     LogNormal(0, 0.5) factor, no outliers).
  */
 #ifndef STILL_H
 #define STILL_H

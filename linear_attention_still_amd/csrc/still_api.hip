@@ -5,6 +5,8 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "still.h"
 #include "still_decode.hip"
 #include "still_prefill.hip"
@@ -148,20 +150,45 @@ Plan plan(const Derived& d, int64_t L) {
 
 bool misaligned(const void* p) { return ((uintptr_t)p & 15u) != 0; }
 
+// LDS-size attributes of the kernels that use more than 64 KiB of dynamic
+// LDS, set once per (kernel family, device). The table is the library's only
+// mutable host state; a mutex makes concurrent first calls safe.
+constexpr int kMaxDevices = 64;
+std::mutex g_attr_mu;
+uint64_t g_attr_done[kMaxDevices];  // bit f: family f set on that device
+
 template <typename T, int D>
-void set_lds_attr() {
-  static bool done = false;
-  if (done) return;
+void set_prefill_attrs(int family) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) dev = 0;
+  std::lock_guard<std::mutex> lk(g_attr_mu);
+  if (g_attr_done[dev] & (1ull << family)) return;
   (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&still::attend_kernel<T, D, 1>),
-                      hipFuncAttributeMaxDynamicSharedMemorySize,
-                      (int)still::Blk<T, D>::bytes);
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)still::Blk<T, D>::bytes);
   (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&still::attend_kernel<T, D, 2>),
-                      hipFuncAttributeMaxDynamicSharedMemorySize,
-                      (int)still::Blk<T, D>::bytes);
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)still::Blk<T, D>::bytes);
   (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&still::state_delta_kernel<T, D>),
-                      hipFuncAttributeMaxDynamicSharedMemorySize,
-                      (int)still::Blk<T, D>::bytes);
-  done = true;
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)still::Blk<T, D>::bytes);
+  g_attr_done[dev] |= 1ull << family;
+}
+
+template <typename T, int D, int G>
+void set_decode_attr(int family) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) dev = 0;
+  std::lock_guard<std::mutex> lk(g_attr_mu);
+  if (g_attr_done[dev] & (1ull << family)) return;
+  (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&still::decode_kernel<T, D, G>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+  g_attr_done[dev] |= 1ull << family;
+}
+
+// kernel family index of (element type, head dim[, group]) for the table
+template <typename T, int D>
+constexpr int prefill_family() { return (sizeof(T) == 4 ? 0 : 1) * 2 + (D == 128 ? 1 : 0); }
+template <typename T, int D, int G>
+constexpr int decode_family() {
+  return 4 + ((sizeof(T) == 4 ? 0 : 1) * 2 + (D == 128 ? 1 : 0)) * 4 + (G == 1 ? 0 : G == 2 ? 1 : G == 4 ? 2 : 3);
 }
 
 // Optional per-kernel events (still_prefill_timed).
@@ -183,7 +210,7 @@ int launch_prefill(const Derived& d, const Plan& pl, still::PrefillArgs a, hipSt
   const size_t lds_score =
       (size_t)nkt * 16 * (D + Pad<T>::v) * sizeof(T) + (size_t)(3 * d.G * d.C + nkt * 16 + 80) * 4;
   const size_t lds_sel = (size_t)4 * d.G * D * 4 + (size_t)d.C * 8 + (size_t)(5 * d.C + 4) * 4;
-  set_lds_attr<T, D>();
+  set_prefill_attrs<T, D>(prefill_family<T, D>());
   // F^T is made by D*D/2048 extra workgroups of the score launch (its
   // events are recorded back to back)
   mk.at(0, 0);
@@ -222,12 +249,7 @@ int launch_decode_g(const Derived& d, still::DecodeArgs a, hipStream_t s) {
   using namespace still;
   const size_t lds = DecLds<T, D, G>::bytes(d.W);
   if (lds > 160 * 1024) return STILL_EUNSUPPORTED;
-  static bool attr = false;
-  if (!attr) {
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_kernel<T, D, G>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-    attr = true;
-  }
+  set_decode_attr<T, D, G>(decode_family<T, D, G>());
   decode_kernel<T, D, G><<<dim3(d.Hkv, d.B), dim3(DEC_THREADS), lds, s>>>(a);
   return hipGetLastError() == hipSuccess ? STILL_OK : STILL_EHIP;
 }
