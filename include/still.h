@@ -86,6 +86,7 @@ enum { STILL_DTYPE_F32 = 0, STILL_DTYPE_BF16 = 1 };
 #define STILL_EWORKSPACE (-3)   /* workspace smaller than still_workspace_bytes */
 #define STILL_EHIP (-4)         /* a HIP launch failed */
 #define STILL_ESTATE (-5)       /* decode position does not follow the state */
+#define STILL_ESCRATCH (-6)     /* needs more than still_prefill_noalloc's scratch */
 
 typedef struct still_params {
   int32_t abi_version; /* STILL_ABI_VERSION */
@@ -162,6 +163,24 @@ int still_prefill_timed(const still_params* p, int64_t seq_len, const void* q, c
                         const void* v, const void* fmap_w, const float* gate, void* out,
                         int32_t* sel_idx, float* score, void* state, void* workspace,
                         size_t ws_bytes, void* stream, void* const* events, int n_pairs);
+
+/* still_prefill without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): the workspace is a static device array
+ * of still_noalloc_scratch_bytes() bytes (64 MiB) inside the library, one per
+ * GPU, held until the process ends. The call allocates nothing. Problems
+ * whose still_workspace_bytes exceeds that size return STILL_ESCRATCH (e.g.
+ * batch 1 at 32/8 heads, d = 128 fits up to L = 64K). Every call on a GPU
+ * uses that GPU's one array: calls that overlap on one GPU (other streams,
+ * other threads) race and give undefined results; serialise them. Same
+ * outputs, errors and stream semantics as still_prefill otherwise (the
+ * array needs no initialisation; nothing in it must start at zero). */
+int still_prefill_noalloc(const still_params* p, int64_t seq_len, const void* q, const void* k,
+                          const void* v, const void* fmap_w, const float* gate, void* out,
+                          int32_t* sel_idx, float* score, void* state, void* stream);
+
+/* Size in bytes of still_prefill_noalloc's static scratch. */
+int64_t still_noalloc_scratch_bytes(void);
 
 /* Decode one token per sequence at position pos (the state must hold
  * position pos, i.e. pos tokens already processed), [P3 "Delayed

@@ -287,6 +287,31 @@ void fill_state_offsets(const still_state_layout& L, long* unit, long* S, long* 
   *meta = L.meta;
 }
 
+// Scratch of still_prefill_noalloc: a static device array, so that the call
+// allocates nothing. Each GPU the library runs on holds its own copy until
+// the process ends. In host code `scratch` only names the symbol; its device
+// address comes from hipGetSymbolAddress, taken once per device (with that
+// device current) on the first call there and kept in g_scratch_ptr.
+constexpr size_t kNoAllocScratchBytes = (size_t)64 << 20;
+__device__ __align__(256) char scratch[kNoAllocScratchBytes];
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+int scratch_address(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return STILL_EHIP;
+  if (dev < 0 || dev >= kMaxDevices) return STILL_EUNSUPPORTED;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return STILL_EHIP;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return STILL_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -414,6 +439,23 @@ int still_prefill_timed(const still_params* p, int64_t seq_len, const void* q, c
                       ws_bytes, stream, events, n_pairs);
 }
 
+int still_prefill_noalloc(const still_params* p, int64_t seq_len, const void* q, const void* k,
+                          const void* v, const void* fmap_w, const float* gate, void* out,
+                          int32_t* sel_idx, float* score, void* state, void* stream) {
+  Derived d;
+  const int rc = derive(p, &d);
+  if (rc != STILL_OK) return rc;
+  if (seq_len < 1 || seq_len > ((int64_t)1 << 30)) return STILL_EINVAL;
+  if (plan(d, seq_len).ws_total > (int64_t)kNoAllocScratchBytes) return STILL_ESCRATCH;
+  void* ws = nullptr;
+  const int rs = scratch_address(&ws);
+  if (rs != STILL_OK) return rs;
+  return prefill_impl(p, seq_len, q, k, v, fmap_w, gate, out, sel_idx, score, state, ws,
+                      kNoAllocScratchBytes, stream, nullptr, 0);
+}
+
+int64_t still_noalloc_scratch_bytes(void) { return (int64_t)kNoAllocScratchBytes; }
+
 int still_decode_step(const still_params* p, int64_t pos, const void* q, const void* k,
                       const void* v, const void* fmap_w, const float* gate, void* state,
                       void* out, int32_t* sel_new, void* workspace, size_t ws_bytes,
@@ -475,6 +517,7 @@ const char* still_status_str(int status) {
     case STILL_EWORKSPACE: return "workspace too small";
     case STILL_EHIP: return "HIP launch failed";
     case STILL_ESTATE: return "decode position does not match the state";
+    case STILL_ESCRATCH: return "problem needs more scratch than still_prefill_noalloc's static buffer";
     default: return "unknown status";
   }
 }

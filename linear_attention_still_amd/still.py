@@ -21,8 +21,8 @@ STILL_ABI_VERSION = 1
 STILL_DTYPE_F32 = 0
 STILL_DTYPE_BF16 = 1
 STILL_FLAG_FP32_OUT = 1
-STILL_OK, STILL_EINVAL, STILL_EUNSUPPORTED, STILL_EWORKSPACE, STILL_EHIP, STILL_ESTATE = \
-    0, -1, -2, -3, -4, -5
+STILL_OK, STILL_EINVAL, STILL_EUNSUPPORTED, STILL_EWORKSPACE, STILL_EHIP, STILL_ESTATE, \
+    STILL_ESCRATCH = 0, -1, -2, -3, -4, -5, -6
 
 
 class still_params(ctypes.Structure):
@@ -72,6 +72,10 @@ def lib() -> ctypes.CDLL:
         L.still_prefill.restype = I32
         L.still_prefill_timed.argtypes = [pp, I64] + [P] * 10 + [ctypes.c_size_t, P, P, I32]
         L.still_prefill_timed.restype = I32
+        L.still_prefill_noalloc.argtypes = [pp, I64] + [P] * 10
+        L.still_prefill_noalloc.restype = I32
+        L.still_noalloc_scratch_bytes.argtypes = []
+        L.still_noalloc_scratch_bytes.restype = I64
         L.still_decode_step.argtypes = [pp, I64] + [P] * 9 + [ctypes.c_size_t, P]
         L.still_decode_step.restype = I32
         L.still_status_str.argtypes = [I32]
@@ -154,6 +158,19 @@ def still_prefill(p: still_params, seq_len: int, q, k, v, fmap_w, gate, out, sel
                              _stream(stream))
     if rc != STILL_OK:
         raise StillError("still_prefill", rc)
+
+
+def still_prefill_noalloc(p: still_params, seq_len: int, q, k, v, fmap_w, gate, out, sel_idx,
+                          score, state, stream=None) -> None:
+    rc = lib().still_prefill_noalloc(ctypes.byref(p), int(seq_len), _ptr(q), _ptr(k), _ptr(v),
+                                     _ptr(fmap_w), _ptr(gate), _ptr(out), _ptr(sel_idx),
+                                     _ptr(score), _ptr(state), _stream(stream))
+    if rc != STILL_OK:
+        raise StillError("still_prefill_noalloc", rc)
+
+
+def still_noalloc_scratch_bytes() -> int:
+    return int(lib().still_noalloc_scratch_bytes())
 
 
 PREFILL_KERNELS = ("fmap_transpose", "score", "select", "state_delta", "state_scan", "attend",

@@ -124,3 +124,14 @@ def test_status_strings():
     for rc in (0, -1, -2, -3, -4, -5):
         assert still.still_status_str(rc) != "unknown status"
     assert still.still_status_str(42) == "unknown status"
+
+
+def test_noalloc_rejects_oversize_before_any_hip_call():
+    """still_prefill_noalloc refuses a problem whose workspace exceeds its
+    static scratch before touching the device (runs without a GPU)."""
+    p = still.make_params(dtype="bf16", batch=4, n_q_heads=32, n_kv_heads=8, head_dim=128,
+                          window=128, chunk=128, budget=1024, t_max=512)
+    assert still.still_workspace_bytes(p, 65536) > still.still_noalloc_scratch_bytes()
+    rc = still.lib().still_prefill_noalloc(ctypes.byref(p), 65536, *([ctypes.c_void_p(256)] * 10))
+    assert rc == still.STILL_ESCRATCH
+    assert "scratch" in still.still_status_str(rc)
