@@ -91,7 +91,7 @@ void layout(const Derived& d, still_state_layout* s) {
 // Prefill launch geometry.
 struct Plan {
   int L, T, n_dec, n_pend, K, NS, Gs, nHG, HPW;
-  int64_t ws_ft, ws_score, ws_delta, ws_flag, ws_dS, ws_total;
+  int64_t ws_ft, ws_score, ws_delta, ws_flag, ws_dS, ws_rl, ws_total;
 };
 
 Plan plan(const Derived& d, int64_t L) {
@@ -144,6 +144,7 @@ Plan plan(const Derived& d, int64_t L) {
   pl.ws_delta = take(nu * L * 4);
   pl.ws_flag = take(nu * L);
   pl.ws_dS = take(nu * pl.NS * ((int64_t)d.D * d.D + d.D) * 4);
+  pl.ws_rl = take(nu * pl.T * (int64_t)(d.C + 1) * 4);
   pl.ws_total = o;
   return pl;
 }
@@ -209,7 +210,13 @@ int launch_prefill(const Derived& d, const Plan& pl, still::PrefillArgs a, hipSt
   const int nkt = d.C / 16 + (d.W + 14) / 16;  // key tiles of the score kernel
   const size_t lds_score =
       (size_t)nkt * 16 * (D + Pad<T>::v) * sizeof(T) + (size_t)(3 * d.G * d.C + nkt * 16 + 80) * 4;
-  const size_t lds_sel = (size_t)4 * d.G * D * 4 + (size_t)d.C * 8 + (size_t)(5 * d.C + 4) * 4;
+  // select: query rows, chunk arrays, per-head float64 results (near ties);
+  // refine: key rows, query rows, per-head results, sums, token list
+  const size_t krows = (size_t)(d.W + d.C - 1) * (D + Pad<T>::v) * sizeof(T);
+  const size_t f64s = (size_t)4 * D * 8 + (size_t)d.C * d.G * 8 + (size_t)d.C * 8;
+  const size_t lds_sel = (size_t)4 * D * 8 + (size_t)d.C * 8 + (size_t)(5 * d.C + 4) * 4 +
+                         (size_t)d.C * d.G * 8 + (size_t)d.C * 8;
+  const size_t lds_ref = krows + f64s + (size_t)d.C * 4;
   set_prefill_attrs<T, D>(prefill_family<T, D>());
   // F^T is made by D*D/2048 extra workgroups of the score launch (its
   // events are recorded back to back)
@@ -217,9 +224,13 @@ int launch_prefill(const Derived& d, const Plan& pl, still::PrefillArgs a, hipSt
   mk.at(0, 1);
   mk.at(1, 0);
   score_kernel<T, D><<<dim3(pl.T + D * D / 2048, d.Hkv, d.B), dim3(256), lds_score, s>>>(a);
+  // float64 scores: the undecided chunk's tokens first, then (exported
+  // scores only) the chunks' listed tokens
+  score_refine_kernel<T, D><<<dim3(pl.n_pend + (a.score_out ? pl.T : 0), d.Hkv, d.B), dim3(256), lds_ref, s>>>(a);
   mk.at(1, 1);
   mk.at(2, 0);
-  select_kernel<T, D><<<dim3(pl.n_dec + (pl.n_pend + 3) / 4, d.Hkv, d.B), dim3(256), lds_sel, s>>>(a);
+  if (pl.n_dec > 0)
+    select_kernel<T, D><<<dim3(pl.n_dec, d.Hkv, d.B), dim3(256), lds_sel, s>>>(a);
   mk.at(2, 1);
   mk.at(3, 0);
   state_delta_kernel<T, D><<<dim3(pl.NS, d.Hkv, d.B), dim3(512), Blk<T, D>::bytes, s>>>(a);
@@ -387,6 +398,7 @@ static int prefill_impl(const still_params* p, int64_t seq_len, const void* q, c
   a.selflag = reinterpret_cast<uint8_t*>(ws + pl.ws_flag);
   a.ft = ws + pl.ws_ft;
   a.dS = reinterpret_cast<float*>(ws + pl.ws_dS);
+  a.rlist = reinterpret_cast<int*>(ws + pl.ws_rl);
   a.state = reinterpret_cast<char*>(state);
   a.B = d.B;
   a.Hq = d.Hq;

@@ -46,6 +46,7 @@ struct PrefillArgs {
   char* state;
   int B, Hq, Hkv, G, L, W, C, m, T, n_dec, lam, cap_chunks, K, NS, nHG, Gs, fp32_out;
   int score_out;  // the caller asked for the scores (score is theirs)
+  int* rlist;     // [B][Hkv][T][C + 1] tokens whose exported score is refined
   float scale, eps;
   double scale64, eps64;  // the same parameters for the float64 paths
   long st_unit, st_S, st_z, st_pool_k, st_pool_v, st_pool_pos, st_ring_k, st_ring_v,
@@ -277,6 +278,13 @@ __global__ __launch_bounds__(256) void score_kernel(PrefillArgs a) {
       pest[hl * C + 16 * qt + r16] = es;
     }
   }
+  // tokens whose exported score is recomputed in float64 by the refine
+  // kernel (their estimated float32 error comes near 1e-5 of the score):
+  // the chunk's list rlist[unit][c] = {count, positions in the chunk}
+  int* rl = a.rlist + ((size_t)(b * a.Hkv + kv) * a.T + c) * (C + 1);
+  int* n_list = reinterpret_cast<int*>(knrm);
+  __syncthreads();  // every wave is done with the key norms
+  if (tid == 0) *n_list = 0;
   __syncthreads();
   for (int qi = tid; qi < C; qi += 256) {
     const int t = cC + qi;
@@ -289,95 +297,205 @@ __global__ __launch_bounds__(256) void score_kernel(PrefillArgs a) {
     }
     const size_t o = (size_t)(b * a.Hkv + kv) * L + t;
     a.score[o] = s;
-    // the bound, negative where the exported score is to be recomputed in
-    // float64 (its typical error may come near 1e-5 of the score)
-    a.delta[o] = e > 3e-6f * fmaxf(1.f, fabsf(s)) ? -d : d;
+    a.delta[o] = d;
+    if (a.score_out && c * C + C < L && e > 6e-6f * fmaxf(1.f, fabsf(s)))
+      rl[1 + atomicAdd(n_list, 1)] = qi;  // (the last chunk's are all recomputed)
+  }
+  __syncthreads();
+  if (tid == 0) rl[0] = *n_list;  // 0 unless the scores are exported
+}
+
+// Key rows [r0, r0 + n) of unit (b, kv) into LDS (row stride KS elements),
+// rows outside [0, L) as zeros; 16-byte loads, all of a thread's in flight.
+template <typename T, int D>
+__device__ __forceinline__ void stage_rows(const PrefillArgs& a, int b, int kv, int r0, int n, T* Kst,
+                                           int KS, int tid, int nthr) {
+  constexpr int VEC = 16 / sizeof(T), NV = D / VEC;
+  const uint32_t bytes = (uint32_t)((size_t)a.L * D * sizeof(T));
+  const __amdgpu_buffer_rsrc_t kr =
+      make_rsrc(reinterpret_cast<const T*>(a.k) + (size_t)(b * a.Hkv + kv) * a.L * D, bytes);
+  constexpr int NB = 8;
+  for (int base = 0; base < n * NV; base += NB * nthr) {
+    uint4 v[NB];
+#pragma unroll
+    for (int u = 0; u < NB; ++u) {
+      const int idx = base + u * nthr + tid, row = idx / NV, c = idx % NV, j = r0 + row;
+      const bool ok = idx < n * NV && j >= 0 && j < a.L;
+      v[u] = ld_u4_buf(kr, ok ? (uint32_t)(((size_t)j * D + c * VEC) * sizeof(T)) : bytes, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < NB; ++u) {
+      const int idx = base + u * nthr + tid;
+      if (idx < n * NV) *reinterpret_cast<uint4*>(Kst + (idx / NV) * KS + (idx % NV) * VEC) = v[u];
+    }
   }
 }
 
-// ---------------------------------------------------------- 3. select ----
-// Score of token t in float64 [P3 "Self-Saliency Score"] by one wave: lane j
-// takes the window keys lo + j, lo + j + 64, ...; per head the logits are
-// float64 dot products (products of bf16 / float32 values are exact in
-// float64) against the query row staged in LDS (qs: this wave's [G][D]
-// floats), then the window softmax and the two-point KL form with 1-p
-// summed from the other keys. Every lane returns the sum over the heads.
-template <typename T, int D>
-__device__ double score_f64_wave(const PrefillArgs& a, int b, int kv, int t, float* qs) {
+// Float64 score of head h (of the kv group) for token t [P3 "Self-Saliency
+// Score"] by one wave. The window keys are the LDS rows row_t - n + 1 ..
+// row_t of Kst (stride KS) when LDSK, else the rows of global memory, lane j
+// taking rows j, j + 64, ...; the query row
+// is staged in LDS as float64 (qd: this wave's [D]); the logits are float64
+// dot products (products of bf16 / float32 values are exact in float64);
+// the softmax sums run online over the 64-key slots and the two-point KL
+// form takes 1-p from the other keys. Every lane returns the head's score.
+template <typename T, int D, bool LDSK>
+__device__ double score_f64_head(const PrefillArgs& a, int b, int kv, int h, int t, const T* Kst,
+                                 int KS, int row_t, double* qd) {
   const int lane = threadIdx.x & 63;
   const int W = a.W, G = a.G, L = a.L;
-  const int lo = t - W + 1 > 0 ? t - W + 1 : 0;
-  const int n = t - lo + 1;
-  constexpr int VEC = 16 / sizeof(T);
+  const int n = t - W + 1 > 0 ? W : t + 1;
+  constexpr int VEC = 16 / sizeof(T), NV = D / VEC;
   auto wave_sync = [] {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   };
-  wave_sync();  // the previous token's reads of qs are done
-  const T* q = reinterpret_cast<const T*>(a.q);
-  for (int e = lane; e < G * D; e += 64)
-    qs[e] = to_f32(q[((size_t)(b * a.Hq + kv * G + e / D) * L + t) * D + e % D]);
-  wave_sync();
-  const T* kg = reinterpret_cast<const T*>(a.k) + (size_t)(b * a.Hkv + kv) * L * D;
-  double tot = 0.0;
-  for (int h = 0; h < G; ++h) {
-    double x[4];  // window of at most 256 keys
-    double mx = -__builtin_huge_val();
+  const T* qrow = reinterpret_cast<const T*>(a.q) + ((size_t)(b * a.Hq + kv * G + h) * L + t) * D;
+  wave_sync();  // the previous call's reads of qd are done
+  for (int c = lane; c < NV; c += 64) {
+    const uint4 q4 = *reinterpret_cast<const uint4*>(qrow + c * VEC);
+    const T* qe = reinterpret_cast<const T*>(&q4);
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const int j = lane + 64 * s;
-      x[s] = -__builtin_huge_val();
-      if (j < n) {
-        const T* kr = kg + (size_t)(lo + j) * D;
-        double acc = 0.0;
-        for (int c = 0; c < D; c += VEC) {
-          const uint4 k4 = *reinterpret_cast<const uint4*>(kr + c);
-          const T* ke = reinterpret_cast<const T*>(&k4);
-#pragma unroll
-          for (int e = 0; e < VEC; ++e) acc += (double)qs[h * D + c + e] * (double)to_f32(ke[e]);
-        }
-        x[s] = a.scale64 * acc;
-        mx = x[s] > mx ? x[s] : mx;
-      }
-    }
-    mx = wave_max_d(mx);
-    double za = 0.0, zo = 0.0, es = 0.0;
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const int j = lane + 64 * s;
-      if (j < n) {
-        const double e = exp(x[s] - mx);
-        za += e;
-        if (j != n - 1) zo += e;
-        else es = e;
-      }
-    }
-    za = wave_sum_d(za);
-    zo = wave_sum_d(zo);
-    es = wave_sum_d(es);
-    const double p = es / za, pn = zo / za;
-    double sc = 0.0;
-    if (p > 0.0) sc += p * log(p / a.eps64);
-    if (pn > 0.0) sc += pn * log(pn / (1.0 - a.eps64));
-    tot += sc;
+    for (int i = 0; i < VEC; ++i) qd[c * VEC + i] = (double)to_f32(qe[i]);
   }
-  return tot;
+  wave_sync();
+  double m = -__builtin_huge_val(), za = 0.0, zo = 0.0, zt = 0.0;  // uniform
+  for (int s = 0; 64 * s < n; ++s) {  // uniform
+    const int j = lane + 64 * s;
+    // the key row: staged in LDS, or straight from global memory
+    const T* krow = LDSK ? lds_opaque_v(Kst) + (size_t)(row_t - n + 1 + (j < n ? j : 0)) * KS
+                         : reinterpret_cast<const T*>(a.k) +
+                               ((size_t)(b * a.Hkv + kv) * L + (t - n + 1 + (j < n ? j : 0))) * D;
+    // query doubles as 16-byte pairs (read here, not hoisted out of the loop)
+    typedef double f64x2 __attribute__((ext_vector_type(2)));
+    const f64x2* q2 = reinterpret_cast<const f64x2*>(lds_opaque_v(qd));
+    double acc[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = 0.0;
+    // one 16-byte key vector and its VEC query doubles per step; the next
+    // step's LDS reads are issued before this step's products
+    uint4 kc = *reinterpret_cast<const uint4*>(krow);
+    f64x2 qc[VEC / 2];
+#pragma unroll
+    for (int i = 0; i < VEC / 2; ++i) qc[i] = q2[i];
+#pragma unroll 1
+    for (int c = 0; c < NV; ++c) {
+      const uint4 kx = kc;
+      f64x2 qx[VEC / 2];
+#pragma unroll
+      for (int i = 0; i < VEC / 2; ++i) qx[i] = qc[i];
+      if (c + 1 < NV) {
+        kc = *reinterpret_cast<const uint4*>(krow + (c + 1) * VEC);
+#pragma unroll
+        for (int i = 0; i < VEC / 2; ++i) qc[i] = q2[(c + 1) * (VEC / 2) + i];
+      }
+      const T* ke = reinterpret_cast<const T*>(&kx);
+#pragma unroll
+      for (int i = 0; i < VEC; ++i)
+        acc[i & 7] = fma(qx[i / 2][i & 1], (double)to_f32(ke[i]), acc[i & 7]);
+    }
+    const double dot = ((acc[0] + acc[1]) + (acc[2] + acc[3])) + ((acc[4] + acc[5]) + (acc[6] + acc[7]));
+    const double xv = j < n ? a.scale64 * dot : -__builtin_huge_val();
+    const double mx = wave_max_d(xv);
+    const double mn = mx > m ? mx : m;
+    const double al = m == -__builtin_huge_val() ? 0.0 : exp(m - mn);
+    const double e = j < n ? exp(xv - mn) : 0.0;
+    za = za * al + wave_sum_d(e);
+    zo = zo * al + wave_sum_d(j == n - 1 ? 0.0 : e);
+    zt = zt * al + wave_sum_d(j == n - 1 ? e : 0.0);
+    m = mn;
+  }
+  const double p = zt / za, pn = zo / za;
+  double sc = 0.0;
+  if (p > 0.0) sc += p * log(p / a.eps64);
+  if (pn > 0.0) sc += pn * log(pn / (1.0 - a.eps64));
+  return sc;
 }
 
+// Float64 scores of a list of tokens by a 4-wave workgroup: the (token,
+// head) pairs are dealt to the waves, each head's score lands in res[i][h]
+// and every token's sum is taken in head order (tok_t: the tokens; rows:
+// key rows staged in Kst from row r0; qd: [4][D] float64). Ends with a
+// barrier; the sums are left in sum[i].
+template <typename T, int D, bool LDSK>
+__device__ void score_f64_list(const PrefillArgs& a, int b, int kv, const int* tok_t, int n_tok,
+                               const T* Kst, int KS, int r0, double* qd, double* res, double* sum) {
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, G = a.G;
+  for (int pi = wave; pi < n_tok * G; pi += 4) {  // wave-uniform
+    const int i = pi / G, h = pi % G, t = tok_t[i];
+    const double s = score_f64_head<T, D, LDSK>(a, b, kv, h, t, Kst, KS, t - r0, qd + wave * D);
+    if (lane == 0) res[pi] = s;
+  }
+  __syncthreads();
+  for (int i = tid; i < n_tok; i += 256) {
+    double s = 0.0;
+    for (int h = 0; h < G; ++h) s += res[i * G + h];
+    sum[i] = s;
+  }
+  __syncthreads();
+}
+
+// Float64 scores (4-wave workgroups, keys staged in LDS, then the query rows,
+// the token list and the per-head results):
+//   x < n_pend: token x of the undecided last chunk (its heads dealt to the
+//          waves): the score goes to the decode state (and the exported
+//          scores); the token's kept flag is 0;
+//   x >= n_pend (launched only when the scores are exported): the listed
+//          tokens of chunk x - n_pend, their exported scores rounded once to
+//          float32 (chunks other than the undecided last one).
+template <typename T, int D>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void score_refine_kernel(PrefillArgs a) {
+  extern __shared__ __align__(16) char smem[];
+  constexpr int KS = D + Pad<T>::v;
+  const int x = blockIdx.x, kv = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x;
+  const int C = a.C, W = a.W, L = a.L;
+  const int unit = b * a.Hkv + kv;
+  const int c_last = (L - 1) / C, n_pend = L - c_last * C;
+  T* Kst = reinterpret_cast<T*>(smem);
+  const size_t krows = (size_t)(W + C - 1) * KS * sizeof(T);
+  double* qd = reinterpret_cast<double*>(smem + krows);  // [4][D]
+  double* res = qd + 4 * D;                             // [C][G]
+  double* sum = res + (size_t)C * a.G;                  // [C]
+  int* tok = reinterpret_cast<int*>(sum + C);           // [C]
+  if (x < n_pend) {
+    const int t = c_last * C + x, r0 = t - W + 1;
+    if (tid == 0) tok[0] = t;
+    stage_rows<T, D>(a, b, kv, r0, W, Kst, KS, tid, 256);
+    __syncthreads();
+    score_f64_list<T, D, true>(a, b, kv, tok, 1, Kst, KS, r0, qd, res, sum);
+    if (tid == 0) {
+      double* pend = reinterpret_cast<double*>(a.state + (size_t)unit * a.st_unit + a.st_pending);
+      pend[x] = sum[0];
+      a.selflag[(size_t)unit * L + t] = 0;
+      if (a.score_out) a.score[(size_t)unit * L + t] = (float)sum[0];
+      if (x == 0)
+        for (int i = n_pend; i < C; ++i) pend[i] = __builtin_nan("");
+    }
+    return;
+  }
+  const int c = x - n_pend;
+  const int* rl = a.rlist + ((size_t)unit * a.T + c) * (C + 1);
+  const int n = min(rl[0], C);
+  if (n <= 0) return;  // uniform
+  const int r0 = c * C - W + 1;
+  for (int i = tid; i < n; i += 256) tok[i] = c * C + rl[1 + i];
+  stage_rows<T, D>(a, b, kv, r0, W + C - 1, Kst, KS, tid, 256);
+  __syncthreads();
+  score_f64_list<T, D, true>(a, b, kv, tok, n, Kst, KS, r0, qd, res, sum);
+  for (int i = tid; i < n; i += 256) a.score[(size_t)unit * L + tok[i]] = (float)sum[i];
+}
+
+// ---------------------------------------------------------- 3. select ----
 // Workgroup x < n_dec decides chunk x [P3 "Delayed Chunk-Level Selection"]:
 // keep lambda_c = lambda tokens while the pool of m - W slots has room
 // [P2 固定预算路由], ranked by (score desc, position asc). The float32 scores
 // with their error bounds give, for every token, an interval; tokens whose
 // upper end is below the lambda-th largest lower end cannot be kept. If more
 // than lambda tokens remain, their scores are recomputed in float64 (one
-// wave per token) and the ranking is made on those. When the caller asked
-// for the scores, the tokens the score kernel marked (sign of the bound:
-// their estimated float32 error is above 2e-6 of the score) are recomputed
-// in float64 as well and their exported scores are the float64 values
-// rounded once. Workgroups x >= n_dec compute the float64
-// scores of the undecided last chunk (four tokens each, one per wave) into
-// the decode state.
+// wave per token) and the ranking is made on those (their exported scores
+// become the float64 values rounded once).
 // The selection's intervals are [score - m dl, score + m dl] with the score
 // kernel's bound dl widened by SEL_MARGIN: a wider interval only sends more
 // tokens to the float64 ranking, a too narrow one could drop a token the
@@ -385,38 +503,21 @@ __device__ double score_f64_wave(const PrefillArgs& a, int b, int kv, int t, flo
 constexpr float SEL_MARGIN = 2.f;
 
 template <typename T, int D>
-__global__ __launch_bounds__(256) void select_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void select_kernel(PrefillArgs a) {
   extern __shared__ __align__(16) char smem[];
   const int x = blockIdx.x, kv = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int C = a.C, L = a.L, lam = a.lam, G = a.G;
-  float* qs = reinterpret_cast<float*>(smem) + (size_t)wave * G * D;       // [4][G][D]
-  double* s64 = reinterpret_cast<double*>(smem + (size_t)4 * G * D * 4);  // [C]
+  double* qd = reinterpret_cast<double*>(smem);  // [4][D] float64 query rows (one per wave)
+  double* s64 = qd + 4 * D;                        // [C]
   float* sc = reinterpret_cast<float*>(s64 + C);                          // [C]
   float* dl = sc + C;                                                      // [C]
   int* flag = reinterpret_cast<int*>(dl + C);                             // [C] candidate
   int* keep = flag + C;                                                    // [C]
   int* list = keep + C;                                                    // [C] float64 tokens
-  int* misc = list + C;                                                    // [4]
+  int* misc = list + C;  // [4], then (16-byte aligned) the per-head float64 results
   const int unit = b * a.Hkv + kv;
   const size_t ub_off = (size_t)unit * L;
-
-  if (x >= a.n_dec) {
-    const int c_last = (L - 1) / C;
-    const int j = (x - a.n_dec) * 4 + wave, t = c_last * C + j;
-    double* pend = reinterpret_cast<double*>(a.state + (size_t)unit * a.st_unit + a.st_pending);
-    if (t < L) {  // wave-uniform
-      const double s = score_f64_wave<T, D>(a, b, kv, t, qs);
-      if (lane == 0) {
-        pend[j] = s;
-        a.selflag[ub_off + t] = 0;
-        if (a.score_out) a.score[ub_off + t] = (float)s;
-      }
-    }
-    if (x == a.n_dec && tid == 0)
-      for (int i = L - c_last * C; i < C; ++i) pend[i] = __builtin_nan("");
-    return;
-  }
 
   const int c = x, base = c * C;
   const int lam_c = ((c + 1) * lam <= a.m - a.W) ? lam : 0;
@@ -424,7 +525,7 @@ __global__ __launch_bounds__(256) void select_kernel(PrefillArgs a) {
   int32_t* selrow = a.sel + ((size_t)unit * a.n_dec + c) * lam;
   for (int j = tid; j < C; j += 256) {
     sc[j] = a.score[ub_off + base + j];
-    dl[j] = a.delta[ub_off + base + j];  // sign: export refinement wanted
+    dl[j] = a.delta[ub_off + base + j];
   }
   if (tid == 0) {
     misc[0] = 0;  // candidates
@@ -435,7 +536,7 @@ __global__ __launch_bounds__(256) void select_kernel(PrefillArgs a) {
   if (partial) {
     if (C <= 64) {  // one wave, token j in lane j: lam_c rounds of removing the largest
       if (tid < 64) {
-        float xl = lane < C ? sc[lane] - SEL_MARGIN * fabsf(dl[lane]) : STILL_NEG_INF, LBv = STILL_NEG_INF;
+        float xl = lane < C ? sc[lane] - SEL_MARGIN * dl[lane] : STILL_NEG_INF, LBv = STILL_NEG_INF;
         bool gone = lane >= C;
         for (int k = 0; k < lam_c; ++k) {
           float m = row_max<16>(gone ? STILL_NEG_INF : xl);
@@ -450,10 +551,10 @@ __global__ __launch_bounds__(256) void select_kernel(PrefillArgs a) {
       }
     } else {
       for (int j = tid; j < C; j += 256) {
-        const float lj = sc[j] - SEL_MARGIN * fabsf(dl[j]);
+        const float lj = sc[j] - SEL_MARGIN * dl[j];
         int r = 0;
         for (int i = 0; i < C; ++i) {
-          const float li = sc[i] - SEL_MARGIN * fabsf(dl[i]);
+          const float li = sc[i] - SEL_MARGIN * dl[i];
           r += (li > lj || (li == lj && i < j)) ? 1 : 0;
         }
         if (r == lam_c - 1) misc[2] = __float_as_int(lj);
@@ -463,24 +564,26 @@ __global__ __launch_bounds__(256) void select_kernel(PrefillArgs a) {
   __syncthreads();
   const float LB = __int_as_float(misc[2]);
   for (int j = tid; j < C; j += 256) {
-    const bool cand = partial && sc[j] + SEL_MARGIN * fabsf(dl[j]) >= LB;
+    const bool cand = partial && sc[j] + SEL_MARGIN * dl[j] >= LB;
     flag[j] = cand ? 1 : 0;
     if (cand) atomicAdd(&misc[0], 1);
   }
   __syncthreads();
   const bool rank64 = partial && misc[0] > lam_c;  // uniform
-  for (int j = tid; j < C; j += 256) {
-    const bool exported = a.score_out && __builtin_signbit(dl[j]);
-    if ((rank64 && flag[j]) || exported) list[atomicAdd(&misc[1], 1)] = j;
-  }
+  for (int j = tid; j < C; j += 256)
+    if (rank64 && flag[j]) list[atomicAdd(&misc[1], 1)] = j;
   __syncthreads();
   const int n_list = misc[1];
-  for (int i = wave; i < n_list; i += 4) {  // wave-uniform
-    const int j = list[i];
-    const double s = score_f64_wave<T, D>(a, b, kv, base + j, qs);
-    if (lane == 0) {
-      s64[j] = s;
-      if (a.score_out) a.score[ub_off + base + j] = (float)s;
+  if (n_list > 0) {  // uniform: float64 scores, key rows read from global memory
+    double* res = reinterpret_cast<double*>(misc + 4);  // [C][G]
+    double* sum = res + (size_t)C * G;                  // [C]
+    for (int i = tid; i < n_list; i += 256) list[i] += base;  // positions
+    __syncthreads();
+    score_f64_list<T, D, false>(a, b, kv, list, n_list, nullptr, 0, 0, qd, res, sum);
+    for (int i = tid; i < n_list; i += 256) {
+      const int j = list[i] - base;
+      s64[j] = sum[i];
+      if (a.score_out) a.score[ub_off + base + j] = (float)sum[i];
     }
   }
   __syncthreads();
