@@ -210,13 +210,9 @@ int launch_prefill(const Derived& d, const Plan& pl, still::PrefillArgs a, hipSt
   const int nkt = d.C / 16 + (d.W + 14) / 16;  // key tiles of the score kernel
   const size_t lds_score =
       (size_t)nkt * 16 * (D + Pad<T>::v) * sizeof(T) + (size_t)(3 * d.G * d.C + nkt * 16 + 80) * 4;
-  // select: query rows, chunk arrays, per-head float64 results (near ties);
-  // refine: key rows, query rows, per-head results, sums, token list
-  const size_t krows = (size_t)(d.W + d.C - 1) * (D + Pad<T>::v) * sizeof(T);
-  const size_t f64s = (size_t)4 * D * 8 + (size_t)d.C * d.G * 8 + (size_t)d.C * 8;
+  // select: query rows, chunk arrays, per-head float64 results and sums
   const size_t lds_sel = (size_t)4 * D * 8 + (size_t)d.C * 8 + (size_t)(5 * d.C + 4) * 4 +
                          (size_t)d.C * d.G * 8 + (size_t)d.C * 8;
-  const size_t lds_ref = krows + f64s + (size_t)d.C * 4;
   set_prefill_attrs<T, D>(prefill_family<T, D>());
   // F^T is made by D*D/2048 extra workgroups of the score launch (its
   // events are recorded back to back)
@@ -224,13 +220,9 @@ int launch_prefill(const Derived& d, const Plan& pl, still::PrefillArgs a, hipSt
   mk.at(0, 1);
   mk.at(1, 0);
   score_kernel<T, D><<<dim3(pl.T + D * D / 2048, d.Hkv, d.B), dim3(256), lds_score, s>>>(a);
-  // float64 scores: the undecided chunk's tokens first, then (exported
-  // scores only) the chunks' listed tokens
-  score_refine_kernel<T, D><<<dim3(pl.n_pend + (a.score_out ? pl.T : 0), d.Hkv, d.B), dim3(256), lds_ref, s>>>(a);
   mk.at(1, 1);
   mk.at(2, 0);
-  if (pl.n_dec > 0)
-    select_kernel<T, D><<<dim3(pl.n_dec, d.Hkv, d.B), dim3(256), lds_sel, s>>>(a);
+  select_kernel<T, D><<<dim3(pl.n_pend + pl.n_dec, d.Hkv, d.B), dim3(256), lds_sel, s>>>(a);
   mk.at(2, 1);
   mk.at(3, 0);
   state_delta_kernel<T, D><<<dim3(pl.NS, d.Hkv, d.B), dim3(512), Blk<T, D>::bytes, s>>>(a);

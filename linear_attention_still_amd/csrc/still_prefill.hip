@@ -305,43 +305,16 @@ __global__ __launch_bounds__(256) void score_kernel(PrefillArgs a) {
   if (tid == 0) rl[0] = *n_list;  // 0 unless the scores are exported
 }
 
-// Key rows [r0, r0 + n) of unit (b, kv) into LDS (row stride KS elements),
-// rows outside [0, L) as zeros; 16-byte loads, all of a thread's in flight.
-template <typename T, int D>
-__device__ __forceinline__ void stage_rows(const PrefillArgs& a, int b, int kv, int r0, int n, T* Kst,
-                                           int KS, int tid, int nthr) {
-  constexpr int VEC = 16 / sizeof(T), NV = D / VEC;
-  const uint32_t bytes = (uint32_t)((size_t)a.L * D * sizeof(T));
-  const __amdgpu_buffer_rsrc_t kr =
-      make_rsrc(reinterpret_cast<const T*>(a.k) + (size_t)(b * a.Hkv + kv) * a.L * D, bytes);
-  constexpr int NB = 8;
-  for (int base = 0; base < n * NV; base += NB * nthr) {
-    uint4 v[NB];
-#pragma unroll
-    for (int u = 0; u < NB; ++u) {
-      const int idx = base + u * nthr + tid, row = idx / NV, c = idx % NV, j = r0 + row;
-      const bool ok = idx < n * NV && j >= 0 && j < a.L;
-      v[u] = ld_u4_buf(kr, ok ? (uint32_t)(((size_t)j * D + c * VEC) * sizeof(T)) : bytes, 0);
-    }
-#pragma unroll
-    for (int u = 0; u < NB; ++u) {
-      const int idx = base + u * nthr + tid;
-      if (idx < n * NV) *reinterpret_cast<uint4*>(Kst + (idx / NV) * KS + (idx % NV) * VEC) = v[u];
-    }
-  }
-}
-
 // Float64 score of head h (of the kv group) for token t [P3 "Self-Saliency
-// Score"] by one wave. The window keys are the LDS rows row_t - n + 1 ..
-// row_t of Kst (stride KS) when LDSK, else the rows of global memory, lane j
-// taking rows j, j + 64, ...; the query row
+// Score"] by one wave. Lane j takes the window keys t - n + 1 + j, + 64, ...
+// (rows read from global memory, 16 bytes at a time, the next read in flight
+// while one is used); the query row
 // is staged in LDS as float64 (qd: this wave's [D]); the logits are float64
 // dot products (products of bf16 / float32 values are exact in float64);
 // the softmax sums run online over the 64-key slots and the two-point KL
 // form takes 1-p from the other keys. Every lane returns the head's score.
-template <typename T, int D, bool LDSK>
-__device__ double score_f64_head(const PrefillArgs& a, int b, int kv, int h, int t, const T* Kst,
-                                 int KS, int row_t, double* qd) {
+template <typename T, int D>
+__device__ double score_f64_head(const PrefillArgs& a, int b, int kv, int h, int t, double* qd) {
   const int lane = threadIdx.x & 63;
   const int W = a.W, G = a.G, L = a.L;
   const int n = t - W + 1 > 0 ? W : t + 1;
@@ -363,10 +336,8 @@ __device__ double score_f64_head(const PrefillArgs& a, int b, int kv, int h, int
   double m = -__builtin_huge_val(), za = 0.0, zo = 0.0, zt = 0.0;  // uniform
   for (int s = 0; 64 * s < n; ++s) {  // uniform
     const int j = lane + 64 * s;
-    // the key row: staged in LDS, or straight from global memory
-    const T* krow = LDSK ? lds_opaque_v(Kst) + (size_t)(row_t - n + 1 + (j < n ? j : 0)) * KS
-                         : reinterpret_cast<const T*>(a.k) +
-                               ((size_t)(b * a.Hkv + kv) * L + (t - n + 1 + (j < n ? j : 0))) * D;
+    const T* krow =
+        reinterpret_cast<const T*>(a.k) + ((size_t)(b * a.Hkv + kv) * L + (t - n + 1 + (j < n ? j : 0))) * D;
     // query doubles as 16-byte pairs (read here, not hoisted out of the loop)
     typedef double f64x2 __attribute__((ext_vector_type(2)));
     const f64x2* q2 = reinterpret_cast<const f64x2*>(lds_opaque_v(qd));
@@ -415,16 +386,15 @@ __device__ double score_f64_head(const PrefillArgs& a, int b, int kv, int h, int
 
 // Float64 scores of a list of tokens by a 4-wave workgroup: the (token,
 // head) pairs are dealt to the waves, each head's score lands in res[i][h]
-// and every token's sum is taken in head order (tok_t: the tokens; rows:
-// key rows staged in Kst from row r0; qd: [4][D] float64). Ends with a
-// barrier; the sums are left in sum[i].
-template <typename T, int D, bool LDSK>
+// and every token's sum is taken in head order (tok_t: the tokens; qd: [4][D]
+// float64). Ends with a barrier; the sums are left in sum[i].
+template <typename T, int D>
 __device__ void score_f64_list(const PrefillArgs& a, int b, int kv, const int* tok_t, int n_tok,
-                               const T* Kst, int KS, int r0, double* qd, double* res, double* sum) {
+                               double* qd, double* res, double* sum) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, G = a.G;
   for (int pi = wave; pi < n_tok * G; pi += 4) {  // wave-uniform
     const int i = pi / G, h = pi % G, t = tok_t[i];
-    const double s = score_f64_head<T, D, LDSK>(a, b, kv, h, t, Kst, KS, t - r0, qd + wave * D);
+    const double s = score_f64_head<T, D>(a, b, kv, h, t, qd + wave * D);
     if (lane == 0) res[pi] = s;
   }
   __syncthreads();
@@ -436,57 +406,6 @@ __device__ void score_f64_list(const PrefillArgs& a, int b, int kv, const int* t
   __syncthreads();
 }
 
-// Float64 scores (4-wave workgroups, keys staged in LDS, then the query rows,
-// the token list and the per-head results):
-//   x < n_pend: token x of the undecided last chunk (its heads dealt to the
-//          waves): the score goes to the decode state (and the exported
-//          scores); the token's kept flag is 0;
-//   x >= n_pend (launched only when the scores are exported): the listed
-//          tokens of chunk x - n_pend, their exported scores rounded once to
-//          float32 (chunks other than the undecided last one).
-template <typename T, int D>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void score_refine_kernel(PrefillArgs a) {
-  extern __shared__ __align__(16) char smem[];
-  constexpr int KS = D + Pad<T>::v;
-  const int x = blockIdx.x, kv = blockIdx.y, b = blockIdx.z;
-  const int tid = threadIdx.x;
-  const int C = a.C, W = a.W, L = a.L;
-  const int unit = b * a.Hkv + kv;
-  const int c_last = (L - 1) / C, n_pend = L - c_last * C;
-  T* Kst = reinterpret_cast<T*>(smem);
-  const size_t krows = (size_t)(W + C - 1) * KS * sizeof(T);
-  double* qd = reinterpret_cast<double*>(smem + krows);  // [4][D]
-  double* res = qd + 4 * D;                             // [C][G]
-  double* sum = res + (size_t)C * a.G;                  // [C]
-  int* tok = reinterpret_cast<int*>(sum + C);           // [C]
-  if (x < n_pend) {
-    const int t = c_last * C + x, r0 = t - W + 1;
-    if (tid == 0) tok[0] = t;
-    stage_rows<T, D>(a, b, kv, r0, W, Kst, KS, tid, 256);
-    __syncthreads();
-    score_f64_list<T, D, true>(a, b, kv, tok, 1, Kst, KS, r0, qd, res, sum);
-    if (tid == 0) {
-      double* pend = reinterpret_cast<double*>(a.state + (size_t)unit * a.st_unit + a.st_pending);
-      pend[x] = sum[0];
-      a.selflag[(size_t)unit * L + t] = 0;
-      if (a.score_out) a.score[(size_t)unit * L + t] = (float)sum[0];
-      if (x == 0)
-        for (int i = n_pend; i < C; ++i) pend[i] = __builtin_nan("");
-    }
-    return;
-  }
-  const int c = x - n_pend;
-  const int* rl = a.rlist + ((size_t)unit * a.T + c) * (C + 1);
-  const int n = min(rl[0], C);
-  if (n <= 0) return;  // uniform
-  const int r0 = c * C - W + 1;
-  for (int i = tid; i < n; i += 256) tok[i] = c * C + rl[1 + i];
-  stage_rows<T, D>(a, b, kv, r0, W + C - 1, Kst, KS, tid, 256);
-  __syncthreads();
-  score_f64_list<T, D, true>(a, b, kv, tok, n, Kst, KS, r0, qd, res, sum);
-  for (int i = tid; i < n; i += 256) a.score[(size_t)unit * L + tok[i]] = (float)sum[i];
-}
-
 // ---------------------------------------------------------- 3. select ----
 // Workgroup x < n_dec decides chunk x [P3 "Delayed Chunk-Level Selection"]:
 // keep lambda_c = lambda tokens while the pool of m - W slots has room
@@ -495,7 +414,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void s
 // upper end is below the lambda-th largest lower end cannot be kept. If more
 // than lambda tokens remain, their scores are recomputed in float64 (one
 // wave per token) and the ranking is made on those (their exported scores
-// become the float64 values rounded once).
+// become the float64 values rounded once); then the tokens the score kernel
+// listed for export are recomputed in float64. Workgroups x < n_pend (first,
+// so they start early) compute the float64 score of one token of the
+// undecided last chunk each, into the decode state.
 // The selection's intervals are [score - m dl, score + m dl] with the score
 // kernel's bound dl widened by SEL_MARGIN: a wider interval only sends more
 // tokens to the float64 ranking, a too narrow one could drop a token the
@@ -518,8 +440,28 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void s
   int* misc = list + C;  // [4], then (16-byte aligned) the per-head float64 results
   const int unit = b * a.Hkv + kv;
   const size_t ub_off = (size_t)unit * L;
+  double* res = reinterpret_cast<double*>(misc + 4);  // [C][G] per-head float64 scores
+  double* sum = res + (size_t)C * G;                  // [C]
 
-  const int c = x, base = c * C;
+  const int c_last = (L - 1) / C, n_pend = L - c_last * C;
+  if (x < n_pend) {
+    // token x of the undecided last chunk: float64 score into the decode
+    // state (and the exported scores); its kept flag is 0
+    const int t = c_last * C + x;
+    if (tid == 0) list[0] = t;
+    __syncthreads();
+    score_f64_list<T, D>(a, b, kv, list, 1, qd, res, sum);
+    if (tid == 0) {
+      double* pend = reinterpret_cast<double*>(a.state + (size_t)unit * a.st_unit + a.st_pending);
+      pend[x] = sum[0];
+      a.selflag[ub_off + t] = 0;
+      if (a.score_out) a.score[ub_off + t] = (float)sum[0];
+      if (x == 0)
+        for (int i = n_pend; i < C; ++i) pend[i] = __builtin_nan("");
+    }
+    return;
+  }
+  const int c = x - n_pend, base = c * C;
   const int lam_c = ((c + 1) * lam <= a.m - a.W) ? lam : 0;
   const bool partial = lam_c > 0 && lam_c < C;  // else none or all are kept
   int32_t* selrow = a.sel + ((size_t)unit * a.n_dec + c) * lam;
@@ -575,11 +517,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void s
   __syncthreads();
   const int n_list = misc[1];
   if (n_list > 0) {  // uniform: float64 scores, key rows read from global memory
-    double* res = reinterpret_cast<double*>(misc + 4);  // [C][G]
-    double* sum = res + (size_t)C * G;                  // [C]
     for (int i = tid; i < n_list; i += 256) list[i] += base;  // positions
     __syncthreads();
-    score_f64_list<T, D, false>(a, b, kv, list, n_list, nullptr, 0, 0, qd, res, sum);
+    score_f64_list<T, D>(a, b, kv, list, n_list, qd, res, sum);
     for (int i = tid; i < n_list; i += 256) {
       const int j = list[i] - base;
       s64[j] = sum[i];
@@ -610,6 +550,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void s
     }
   }
   for (int i = lam_c + tid; i < lam; i += 256) selrow[i] = -1;
+  // exported scores the score kernel listed (estimated float32 error near
+  // 1e-5 of the score): recomputed in float64, rounded once
+  if (!a.score_out) return;
+  const int* rl = a.rlist + ((size_t)unit * a.T + c) * (C + 1);
+  const int nr = min(rl[0], C);
+  if (nr <= 0) return;  // uniform
+  __syncthreads();  // the ranking's reads of list are done
+  for (int i = tid; i < nr; i += 256) list[i] = base + rl[1 + i];
+  __syncthreads();
+  score_f64_list<T, D>(a, b, kv, list, nr, qd, res, sum);
+  for (int i = tid; i < nr; i += 256) a.score[ub_off + list[i]] = (float)sum[i];
 }
 
 // ----------------------------------------- shared block machinery (4-6) ----
