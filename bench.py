@@ -6,11 +6,15 @@ kept softmax -> NP-Map linear attention + merge, plus the decode-state
 export) over one batch of seeded synthetic inputs shaped like a
 Llama-3-8B layer at 16K context (32 query / 8 kv heads, head dim 128,
 W = C = 64, budget m = 512). Inputs are resident in HBM before the timed
-region. The decode leg (batch 64 at 16K context, 64 steps including one
-chunk-boundary decision) and the oracle's CPU baseline are reported in the
-same JSON line.
+region. The same JSON line reports the other workloads (the batch-2 4K GQA
+prefill, the 64K prefill with its per-token time against the 16K one, and
+the latency of the small float32 workload), measured ceilings of the chip
+(a device copy and a large bf16 GEMM), the decode leg (batch 64 at 16K
+context, 64 steps including one chunk-boundary decision) and the float64
+oracle's CPU baseline (all usable cores, and one thread).
 
   python bench.py [--steps K] [--warmup W] [--no-cpu-baseline] [--no-decode]
+                  [--no-workloads]
 
 One GPU only: --gpus above 1 exits with a message.
 """
@@ -89,19 +93,22 @@ def measured_traffic(kernel, profile, sources):
     return None
 
 
-def run_prefill_bench(args, torch, still, inputs):
-    wl = inputs.WORKLOADS["llama8b_bf16_L16K"]
+def run_prefill_bench(torch, still, inputs, name, steps, warmup, breakdown=True):
+    """Times `steps` prefills of workload `name` (inputs resident in HBM),
+    with HIP events around the attention kernel only; then, if breakdown,
+    a second set of steps with events around every kernel."""
+    wl = inputs.WORKLOADS[name]
     p = still.params_for(wl)
     x = inputs.make_inputs(wl, device="cuda")
     bufs = still.PrefillBuffers(p, wl.seq_len)
     nk = len(still.PREFILL_KERNELS)
     ai = still.PREFILL_KERNELS.index("attend")
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         still.run_prefill(p, x, bufs)
     torch.cuda.synchronize()
 
     def events(n):
-        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(n)] for _ in range(args.steps)]
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(n)] for _ in range(steps)]
         for evs in ev:  # create the handles
             for e in evs:
                 e.record()
@@ -109,7 +116,8 @@ def run_prefill_bench(args, torch, still, inputs):
 
     def run(evs):
         still.still_prefill_timed(p, wl.seq_len, x["q"], x["k"], x["v"], x["fmap_w"], x["gate"],
-                                  bufs.out, bufs.sel, bufs.score, bufs.state, bufs.workspace, evs)
+                                  bufs.out, bufs.sel if bufs.sel.numel() else None, bufs.score,
+                                  bufs.state, bufs.workspace, evs)
 
     # timed region: the prefill with HIP events around the attention kernel
     # only (each recorded event drains the stream, so events around every
@@ -117,25 +125,95 @@ def run_prefill_bench(args, torch, still, inputs):
     ev_a = events(2)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for s in range(args.steps):
+    for s in range(steps):
         run([None] * (2 * ai) + ev_a[s])
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    attend_ms = sum(e0.elapsed_time(e1) for e0, e1 in ev_a) / args.steps
-    # per-kernel breakdown, after the timed region: events around every kernel
-    ev = events(2 * nk)
-    torch.cuda.synchronize()
-    for s in range(args.steps):
-        run(ev[s])
-    torch.cuda.synchronize()
-    ms = {k: sum(ev[s][2 * i].elapsed_time(ev[s][2 * i + 1]) for s in range(args.steps)) / args.steps
-          for i, k in enumerate(still.PREFILL_KERNELS)}
-    ms["attend"] = attend_ms  # the timed region's own measurement
-    # F^T is made by extra workgroups of the score launch: its pair of
-    # events is recorded back to back and times nothing
-    ms.pop("fmap_transpose", None)
+    attend_ms = sum(e0.elapsed_time(e1) for e0, e1 in ev_a) / steps
+    ms = None
+    if breakdown:
+        # per-kernel breakdown, after the timed region: events around every kernel
+        ev = events(2 * nk)
+        torch.cuda.synchronize()
+        for s in range(steps):
+            run(ev[s])
+        torch.cuda.synchronize()
+        ms = {k: sum(ev[s][2 * i].elapsed_time(ev[s][2 * i + 1]) for s in range(steps)) / steps
+              for i, k in enumerate(still.PREFILL_KERNELS)}
+        ms["attend"] = attend_ms  # the timed region's own measurement
+        # F^T is made by extra workgroups of the score launch: its pair of
+        # events is recorded back to back and times nothing
+        ms.pop("fmap_transpose", None)
     work = algorithmic_work(wl, bufs.sel.cpu().numpy())
-    return wl, x, bufs, elapsed, ms, work
+    step_s = elapsed / steps
+    att_tf = work["attend"] / (attend_ms * 1e-3) / 1e12
+    out = {"workload": wl.name, "batch": wl.batch, "seq_len": wl.seq_len, "steps": steps,
+           "ms_per_step": step_s * 1e3, "tokens_per_s": wl.batch * wl.seq_len / step_s,
+           "attend_ms": attend_ms, "attend_tflops": att_tf,
+           "attend_mfma_frac": att_tf / PEAK_BF16_TFLOPS,
+           "layer_tflop": work["total"] / 1e12,
+           "layer_mfma_frac": work["total"] / step_s / 1e12 / PEAK_BF16_TFLOPS,
+           "hbm_floor_mb": (2 * wl.batch * wl.n_q_heads + 2 * wl.batch * wl.n_kv_heads) *
+           wl.seq_len * wl.head_dim * 2 / 1e6}
+    if ms is not None:
+        out["kernels_ms"] = ms
+    return wl, x, bufs, out, work
+
+
+def run_latency_bench(torch, still, inputs, name, reps=50):
+    """Wall time of one synchronised prefill of a small workload (median)."""
+    wl = inputs.WORKLOADS[name]
+    p = still.params_for(wl)
+    x = inputs.make_inputs(wl, device="cuda")
+    bufs = still.PrefillBuffers(p, wl.seq_len)
+    for _ in range(5):
+        still.run_prefill(p, x, bufs)
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        still.run_prefill(p, x, bufs)
+        torch.cuda.synchronize()
+        ts.append(time.perf_counter() - t0)
+    ts.sort()
+    return {"workload": wl.name, "reps": reps, "median_ms": ts[len(ts) // 2] * 1e3,
+            "min_ms": ts[0] * 1e3}
+
+
+def measured_ceilings(torch):
+    """What the chip reaches on plain work: a device copy (HBM read + write)
+    and a large bf16 GEMM (hipBLASLt through torch)."""
+    n = 1 << 30
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(10):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    copy_gbs = 2 * n * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del src, dst
+    m = 8192
+    a = torch.randn(m, m, device="cuda").to(torch.bfloat16)
+    b = torch.randn(m, m, device="cuda").to(torch.bfloat16)
+    for _ in range(3):
+        c = a @ b
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(10):
+        c = a @ b
+    e1.record()
+    torch.cuda.synchronize()
+    gemm_tf = 2 * m ** 3 * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e12
+    del a, b, c
+    torch.cuda.empty_cache()
+    return {"copy_gbs": copy_gbs, "copy_frac_of_spec": copy_gbs / PEAK_HBM_GBS,
+            "gemm_bf16_tflops": gemm_tf, "gemm_frac_of_spec": gemm_tf / PEAK_BF16_TFLOPS,
+            "gemm_shape": [m, m, m]}
 
 
 def run_decode_bench(torch, still, inputs, n_steps):
@@ -182,15 +260,24 @@ def run_decode_bench(torch, still, inputs, n_steps):
 
 
 def run_cpu_baseline(wl, x):
+    """The float64 recurrent oracle on the host cores: the whole 16K layer
+    on every usable core (one (batch row, kv head) unit per thread), and two
+    units on one thread, scaled to the layer."""
     from oracle import rec
     cores = len(os.sched_getaffinity(0))
     units = [(b, kv) for b in range(wl.batch) for kv in range(wl.n_kv_heads)]
     threads = max(1, min(cores, len(units)))
     xc = {k: v.cpu() for k, v in x.items()}
-    t0 = time.perf_counter()
-    rec.prefill(xc["q"], xc["k"], xc["v"], xc["fmap_w"], xc["gate"], window=wl.window,
-                chunk=wl.chunk, budget=wl.budget, t_max=wl.t_max, units=units, n_threads=threads)
-    wall = time.perf_counter() - t0
+
+    def timed(us, n_threads):
+        t0 = time.perf_counter()
+        rec.prefill(xc["q"], xc["k"], xc["v"], xc["fmap_w"], xc["gate"], window=wl.window,
+                    chunk=wl.chunk, budget=wl.budget, t_max=wl.t_max, units=us, n_threads=n_threads)
+        return time.perf_counter() - t0
+
+    wall_all = timed(units, threads)
+    one = units[:2]
+    wall_one = timed(one, 1) * len(units) / len(one)
     model = ""
     try:
         with open("/proc/cpuinfo") as fh:
@@ -200,10 +287,14 @@ def run_cpu_baseline(wl, x):
                     break
     except OSError:
         pass
-    return {"value": wl.batch * wl.seq_len / wall, "unit": "tokens/s/layer", "cores": threads,
-            "kind": "oracle",
-            "sample": "whole 16K layer (%d kv-head units, one per thread), float64 recurrent "
-                      "oracle, %.1f s wall on %s" % (len(units), wall, model or "host CPU")}
+    tokens = wl.batch * wl.seq_len
+    return {"value": tokens / wall_all, "unit": "tokens/s/layer", "cores": threads,
+            "kind": "oracle", "usable_cores": cores, "cpu_model": model or "unknown",
+            "wall_s_all_threads": wall_all, "wall_s_one_thread_est": wall_one,
+            "one_thread_tokens_per_s": tokens / wall_one,
+            "sample": "whole 16K layer (%d kv-head units, %d threads), float64 recurrent oracle "
+                      "(%.1f s); one thread: 2 units timed, scaled to %d (%.1f s)"
+                      % (len(units), threads, wall_all, len(units), wall_one)}
 
 
 def main():
@@ -214,6 +305,9 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=64)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-workloads", action="store_true",
+                    help="skip the 4K / 64K prefill lines, the small-workload latency and the "
+                         "measured ceilings")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="only run a plain device copy of this many bytes (HBM counter "
                          "calibration for rocprofv3 --pmc)")
@@ -233,15 +327,15 @@ def main():
         return
     from linear_attention_still_amd import inputs, still
 
-    wl, x, bufs, elapsed, ms, work = run_prefill_bench(args, torch, still, inputs)
+    wl, x, bufs, c3, work = run_prefill_bench(torch, still, inputs, "llama8b_bf16_L16K",
+                                              args.steps, args.warmup)
     tokens = wl.batch * wl.seq_len
-    value = tokens * args.steps / elapsed
-    att_s = ms["attend"] * 1e-3
-    achieved = work["attend"] / att_s / 1e12
+    step_s = c3["ms_per_step"] * 1e-3
+    achieved = work["attend"] / (c3["attend_ms"] * 1e-3) / 1e12
     res = {
-        "metric": METRIC, "value": value, "unit": "tokens/s/layer", "n_gpus": 1,
+        "metric": METRIC, "value": tokens / step_s, "unit": "tokens/s/layer", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup,
-        "ms_per_step": elapsed * 1e3 / args.steps, "higher_is_better": True, "scaling": "weak",
+        "ms_per_step": c3["ms_per_step"], "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": wl.name, "batch": wl.batch, "seq_len": wl.seq_len,
                    "q_heads": wl.n_q_heads, "kv_heads": wl.n_kv_heads,
@@ -254,13 +348,29 @@ def main():
                                                  PREFILL_SOURCES),
                      "flops_per_launch": work["attend"]},
         "layer": {"algorithmic_tflop": work["total"] / 1e12,
-                  "tflops": work["total"] / (elapsed / args.steps) / 1e12,
-                  "mfma_frac": work["total"] / (elapsed / args.steps) / 1e12 / PEAK_BF16_TFLOPS},
-        "kernels_ms": ms,
+                  "tflops": work["total"] / step_s / 1e12,
+                  "mfma_frac": work["total"] / step_s / 1e12 / PEAK_BF16_TFLOPS,
+                  "hbm_floor_mb": c3["hbm_floor_mb"]},
+        "kernels_ms": c3["kernels_ms"],
     }
+    del x, bufs
+    torch.cuda.empty_cache()
+    if not args.no_workloads:
+        others = {}
+        for name, steps, warmup in (("gqa_bf16_L4K", args.steps, 5),
+                                    ("llama8b_bf16_L64K", max(3, args.steps // 4), 3)):
+            _, xo, bo, r, _ = run_prefill_bench(torch, still, inputs, name, steps, warmup,
+                                                breakdown=(name == "llama8b_bf16_L64K"))
+            others[name] = r
+            del xo, bo
+            torch.cuda.empty_cache()
+        c5 = others["llama8b_bf16_L64K"]
+        c5["per_token_time_vs_16K"] = (c5["ms_per_step"] / c5["seq_len"]) / (
+            c3["ms_per_step"] / c3["seq_len"])
+        others["small_f32_L256"] = run_latency_bench(torch, still, inputs, "small_f32_L256")
+        res["workloads"] = others
+        res["ceilings"] = measured_ceilings(torch)
     if not args.no_decode:
-        del x, bufs
-        torch.cuda.empty_cache()
         res["decode"] = run_decode_bench(torch, still, inputs, args.decode_steps)
     if not args.no_cpu_baseline:
         xc = inputs.make_inputs(wl, device="cuda")
