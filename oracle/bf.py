@@ -94,7 +94,7 @@ def np_map(x: np.ndarray, F: np.ndarray) -> np.ndarray:
 
 def prefill(q, k, v, fmap_w, gate, *, window: int, chunk: int, budget: int,
             t_max: int, eps: float = 1e-6, sm_scale: Optional[float] = None,
-            partials: bool = False) -> Dict[str, np.ndarray]:
+            partials: bool = False, merge: str = "one") -> Dict[str, np.ndarray]:
     """One STILL layer over a whole sequence, every query by brute force.
 
     q [B,Hq,L,d], k/v [B,Hkv,L,d], fmap_w [Hkv,d,d], gate [Hq] (any array
@@ -104,9 +104,18 @@ def prefill(q, k, v, fmap_w, gate, *, window: int, chunk: int, budget: int,
     positions, -1 where a chunk kept fewer), n_pool [B,Hkv], the exported
     state S [B,Hkv,d,d], z [B,Hkv,d], and pending [B,Hkv,C] (scores of the
     undecided chunk's tokens, NaN beyond the sequence end). With
-    partials=True also y_sa, lse_sa, y_la, lse_la (NaN where a branch is
-    empty or the gate is 0).
+    partials=True also y_sa, lse_sa, y_la, lse_la: each branch normalised
+    on its own, lse the natural log of its weight sum, the linear branch
+    without the gate (y_la = 0 and lse_la = -inf where B(t) is empty).
+
+    merge (reading where the pages leave it open): "one" = one normaliser
+    over exp(logit) and gate * <phi(q), phi(k)>; "sum" = y_SA + gate * y_LA,
+    each normalised on its own [P4 §4]; "softmax_only" = y_SA, the linear
+    branch dropped and unkept tokens discarded ([P3 "Problems with Existing
+    Intra-Layer Hybrid Attention"]: the sparse-attention-only alternative).
     """
+    if merge not in ("one", "sum", "softmax_only"):
+        raise ValueError("merge must be one, sum or softmax_only")
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
@@ -130,8 +139,8 @@ def prefill(q, k, v, fmap_w, gate, *, window: int, chunk: int, budget: int,
     if partials:
         y_sa = np.full((B, Hq, L, d), np.nan)
         lse_sa = np.full((B, Hq, L), np.nan)
-        y_la = np.full((B, Hq, L, d), np.nan)
-        lse_la = np.full((B, Hq, L), np.nan)
+        y_la = np.zeros((B, Hq, L, d))
+        lse_la = np.full((B, Hq, L), -np.inf)
 
     pos = np.arange(L)
     chunk_of = pos // C
@@ -173,20 +182,28 @@ def prefill(q, k, v, fmap_w, gate, *, window: int, chunk: int, budget: int,
                 ia, ib = np.nonzero(in_a)[0], np.nonzero(in_b)[0]
                 for h in heads:
                     s = scale * (K[ia] @ q[b, h, t])
-                    w = g_all[h] * (phik[ib] @ np_map(q[b, h, t], F))
-                    with np.errstate(divide="ignore"):
-                        logw = np.concatenate([s, np.log(w)])
-                    mx = logw.max()
-                    e = np.exp(logw - mx)
-                    vals = np.concatenate([V[ia], V[ib]])
-                    y[b, h, t] = (e @ vals) / e.sum()
+                    w0 = phik[ib] @ np_map(q[b, h, t], F)  # linear weights, no gate
+                    ea = np.exp(s - s.max())
+                    ysa = (ea @ V[ia]) / ea.sum()
+                    yla = (w0 @ V[ib]) / w0.sum() if len(ib) and w0.sum() > 0 else np.zeros(d)
+                    if merge == "one":
+                        w = g_all[h] * w0
+                        with np.errstate(divide="ignore"):
+                            logw = np.concatenate([s, np.log(w)])
+                        mx = logw.max()
+                        e = np.exp(logw - mx)
+                        vals = np.concatenate([V[ia], V[ib]])
+                        y[b, h, t] = (e @ vals) / e.sum()
+                    elif merge == "sum":
+                        y[b, h, t] = ysa + g_all[h] * yla
+                    else:
+                        y[b, h, t] = ysa
                     if partials:
-                        ea = np.exp(s - s.max())
-                        y_sa[b, h, t] = (ea @ V[ia]) / ea.sum()
+                        y_sa[b, h, t] = ysa
                         lse_sa[b, h, t] = s.max() + math.log(ea.sum())
-                        if len(ib) and w.sum() > 0:
-                            y_la[b, h, t] = (w @ V[ib]) / w.sum()
-                            lse_la[b, h, t] = math.log(w.sum())
+                        y_la[b, h, t] = yla
+                        if len(ib) and w0.sum() > 0:
+                            lse_la[b, h, t] = math.log(w0.sum())
 
             if L:
                 c_last = (L - 1) // C

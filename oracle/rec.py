@@ -20,6 +20,10 @@ _OUT_DIR = os.path.join(_HERE, "_build")
 _LIB_PATH = os.path.join(_OUT_DIR, "liboracle.so")
 _lib = None
 
+# merge of the two branches (still_oracle.c): one normaliser, the sum of
+# separately normalised branches, or the softmax branch alone
+MERGES = {"one": 0, "sum": 1, "softmax_only": 2}
+
 
 def build(force: bool = True) -> str:
     """Compile the oracle with gcc (fp64, strict evaluation order)."""
@@ -43,7 +47,7 @@ def _load():
         f = lib.still_oracle_run
         P = ctypes.c_void_p
         f.argtypes = [ctypes.c_int] * 8 + [ctypes.c_double] * 2 + [P] * 5 + \
-            [ctypes.c_int] + [P] * 7
+            [ctypes.c_int] + [P] * 7 + [ctypes.c_int] + [P] * 4
         f.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -62,13 +66,17 @@ def units_of(B: int, Hkv: int) -> Sequence[Tuple[int, int]]:
 def prefill(q, k, v, fmap_w, gate, *, window: int, chunk: int, budget: int,
             t_max: int, eps: float = 1e-6, sm_scale: Optional[float] = None,
             units: Optional[Sequence[Tuple[int, int]]] = None,
-            n_threads: int = 1) -> Dict[str, np.ndarray]:
+            n_threads: int = 1, merge: str = "one",
+            partials: bool = False) -> Dict[str, np.ndarray]:
     """Run the recurrent oracle on the listed (batch, kv head) units.
 
     q [B,Hq,L,d], k/v [B,Hkv,L,d], fmap_w [Hkv,d,d], gate [Hq]. Outputs
     are per unit, in the order of `units` (default: every unit, batch-major):
     y [U,G,L,d], score [U,L], sel [U,n_dec,lam], S [U,d,d], z [U,d],
-    pending [U,C], n_pool [U].
+    pending [U,C], n_pool [U]; with partials=True also y_sa, y_la [U,G,L,d]
+    and lse_sa, lse_la [U,G,L] (each branch normalised on its own, the
+    linear one without the gate; y_la = 0 and lse_la = -inf where the state
+    is empty). merge: "one", "sum" or "softmax_only" (see MERGES).
     """
     B, Hq, L, d = q.shape
     Hkv = k.shape[1]
@@ -83,12 +91,14 @@ def prefill(q, k, v, fmap_w, gate, *, window: int, chunk: int, budget: int,
     gs = np.stack([_f32(gate[kv * G:(kv + 1) * G]) for _, kv in units]) if U else \
         np.zeros((0, G), np.float32)
     return run_units(qs, ks, vs, Fs, gs, window=window, chunk=chunk, budget=budget,
-                     t_max=t_max, eps=eps, sm_scale=sm_scale, n_threads=n_threads)
+                     t_max=t_max, eps=eps, sm_scale=sm_scale, n_threads=n_threads,
+                     merge=merge, partials=partials)
 
 
 def run_units(qs, ks, vs, Fs, gs, *, window: int, chunk: int, budget: int, t_max: int,
               eps: float = 1e-6, sm_scale: Optional[float] = None,
-              n_threads: int = 1) -> Dict[str, np.ndarray]:
+              n_threads: int = 1, merge: str = "one",
+              partials: bool = False) -> Dict[str, np.ndarray]:
     """Run on pre-gathered per-unit arrays (see still_oracle_run)."""
     qs, ks, vs, Fs, gs = (_f32(a) for a in (qs, ks, vs, Fs, gs))
     U, G, L, d = qs.shape
@@ -102,13 +112,21 @@ def run_units(qs, ks, vs, Fs, gs, *, window: int, chunk: int, budget: int, t_max
     z = np.zeros((U, d))
     pending = np.zeros((U, chunk))
     n_pool = np.zeros((U,), dtype=np.int32)
+    part = None
+    if partials:
+        part = {"y_sa": np.zeros((U, G, L, d)), "lse_sa": np.zeros((U, G, L)),
+                "y_la": np.zeros((U, G, L, d)), "lse_la": np.zeros((U, G, L))}
     lib = _load()
     ptr = lambda a: a.ctypes.data_as(ctypes.c_void_p)
+    pp = [None] * 4 if part is None else [ptr(part[n]) for n in ("y_sa", "lse_sa", "y_la", "lse_la")]
     rc = lib.still_oracle_run(U, L, d, G, window, chunk, budget, t_max, float(eps), scale,
                               ptr(qs), ptr(ks), ptr(vs), ptr(Fs), ptr(gs), int(n_threads),
                               ptr(y), ptr(score), ptr(sel), ptr(S), ptr(z), ptr(pending),
-                              ptr(n_pool))
+                              ptr(n_pool), MERGES[merge], *pp)
     if rc != 0:
         raise ValueError("still_oracle_run rejected its arguments (rc=%d)" % rc)
-    return {"y": y, "score": score, "sel": sel, "S": S, "z": z, "pending": pending,
-            "n_pool": n_pool, "lam": lam, "n_dec": n_dec}
+    out = {"y": y, "score": score, "sel": sel, "S": S, "z": z, "pending": pending,
+           "n_pool": n_pool, "lam": lam, "n_dec": n_dec}
+    if part is not None:
+        out.update(part)
+    return out

@@ -12,7 +12,10 @@
  *        LLM Linearization", sections "Content-Aware Routing with Fixed
  *        Budget", "Delayed Chunk-Level Selection for Unified
  *        Training-Inference Parallelism", "Self-Saliency Score",
- *        "NP-Map: Norm-Preserving Feature Map"
+ *        "NP-Map: Norm-Preserving Feature Map", "Problems with Existing
+ *        Intra-Layer Hybrid Attention"
+ *   [P4] "Synergizing Linear and Sparse Attention: A Deep Dive into Hybrid
+ *        LLM Architectures", §4 (gating; the separately normalised merge)
  *
  * The loop follows the recurrent (decoding) form the pages describe: tokens
  * arrive one by one; when a new chunk begins the previous chunk is decided
@@ -32,12 +35,22 @@
 #include <stdlib.h>
 #include <string.h>
 
+/* Merge of the two branches (reading where the pages leave it open):
+ *   MERGE_ONE: one normaliser over exp(logit) and gate * <phi(q), phi(k)>;
+ *   MERGE_SUM: each branch normalised on its own, y = y_SA + gate * y_LA
+ *     [P4 §4 Gating];
+ *   MERGE_SOFTMAX_ONLY: the linear branch dropped, y = y_SA (the sparse
+ *     attention alternative [P3 "Problems with Existing Intra-Layer Hybrid
+ *     Attention"]); the state is still maintained. */
+enum { MERGE_ONE = 0, MERGE_SUM = 1, MERGE_SOFTMAX_ONLY = 2 };
+
 typedef struct {
-  int L, d, G, W, C, m, t_max, lam, n_dec;
+  int L, d, G, W, C, m, t_max, lam, n_dec, merge;
   double eps, scale;
   const float *q, *k, *v, *F, *gate;
   double *y, *score, *S, *z, *pending;
   int32_t *sel, *n_pool;
+  double *y_sa, *lse_sa, *y_la, *lse_la; /* branch partials, or all null */
 } oracle_job;
 
 typedef struct {
@@ -123,6 +136,7 @@ static void run_unit(const oracle_job* J, int u) {
   unsigned char* selected = calloc((size_t)L, 1);
   int* pool = malloc(sizeof(int) * (size_t)(J->m > 0 ? J->m : 1));
   int n_pool = 0, n_la = 0;
+  const int want_la = J->y_la != NULL;
   const float* qs = J->q + (size_t)u * G * Ld;
   const float* ks = J->k + (size_t)u * Ld;
   const float* vs = J->v + (size_t)u * Ld;
@@ -225,8 +239,11 @@ static void run_unit(const oracle_job* J, int u) {
         for (int b2 = 0; b2 < d; ++b2) num[b2] += w * vj[b2];
       }
       double* yt = yu + (size_t)h * Ld + (size_t)t * d;
+      /* linear branch without the gate: den_la = <phi(q), z_B>,
+       * lnum = phi(q)^T S_B */
       double den_la = 0.0;
-      if (n_la > 0 && g > 0.0) {
+      const int use_la = J->merge != MERGE_SOFTMAX_ONLY && g > 0.0;
+      if (n_la > 0 && (use_la || want_la)) {
         np_map(qh, F, d, phq, tmp);
         for (int b2 = 0; b2 < d; ++b2) lnum[b2] = 0.0;
         for (int a = 0; a < d; ++a) {
@@ -236,15 +253,26 @@ static void run_unit(const oracle_job* J, int u) {
           for (int b2 = 0; b2 < d; ++b2) lnum[b2] += pa * row[b2];
         }
       }
-      if (den_la > 0.0) {
-        const double lse_sa = mx + log(l);
+      const double lse_sa = mx + log(l);
+      if (use_la && den_la > 0.0 && J->merge == MERGE_ONE) {
         const double lse_la = log(g * den_la);
         const double top = lse_sa > lse_la ? lse_sa : lse_la;
         const double wa = exp(lse_sa - top), wb = exp(lse_la - top);
         for (int b2 = 0; b2 < d; ++b2)
           yt[b2] = (wa * (num[b2] / l) + wb * (lnum[b2] / den_la)) / (wa + wb);
+      } else if (use_la && den_la > 0.0) { /* MERGE_SUM */
+        for (int b2 = 0; b2 < d; ++b2) yt[b2] = num[b2] / l + g * (lnum[b2] / den_la);
       } else {
         for (int b2 = 0; b2 < d; ++b2) yt[b2] = num[b2] / l;
+      }
+      if (want_la) {
+        const size_t row = ((size_t)u * G + h) * L + t;
+        for (int b2 = 0; b2 < d; ++b2) {
+          J->y_sa[row * d + b2] = num[b2] / l;
+          J->y_la[row * d + b2] = den_la > 0.0 ? lnum[b2] / den_la : 0.0;
+        }
+        J->lse_sa[row] = lse_sa;
+        J->lse_la[row] = den_la > 0.0 ? log(den_la) : -INFINITY;
       }
     }
   }
@@ -290,19 +318,28 @@ static void* worker(void* p) {
  * Outputs (host, caller-allocated):
  *   y [n_units, G, L, d], score [n_units, L], sel [n_units, n_dec, lam],
  *   S [n_units, d, d], z [n_units, d], pending [n_units, C], n_pool [n_units].
+ * merge: MERGE_ONE, MERGE_SUM or MERGE_SOFTMAX_ONLY. y_sa, lse_sa, y_la,
+ * lse_la: all null, or the branch partials [n_units, G, L, d] / [n_units,
+ * G, L]: each branch normalised on its own, the linear one without the
+ * gate (y_la = 0, lse_la = -inf where the state is empty), lse = natural
+ * log of the branch's weight sum.
  * Returns 0, or -1 on invalid sizes. */
 int still_oracle_run(int n_units, int L, int d, int G, int W, int C, int m, int t_max,
                      double eps, double scale, const float* q, const float* k,
                      const float* v, const float* F, const float* gate, int n_threads,
                      double* y, double* score, int32_t* sel, double* S, double* z,
-                     double* pending, int32_t* n_pool) {
+                     double* pending, int32_t* n_pool, int merge, double* y_sa,
+                     double* lse_sa, double* y_la, double* lse_la) {
   if (n_units < 0 || L < 0 || d < 1 || G < 1 || W < 1 || C < 1 || m < W || t_max < 1)
     return -1;
+  if (merge < MERGE_ONE || merge > MERGE_SOFTMAX_ONLY) return -1;
+  if (!(y_sa && lse_sa && y_la && lse_la) && (y_sa || lse_sa || y_la || lse_la)) return -1;
   int lam = (m - W) / t_max;
   if (lam > C) lam = C;
   if (lam > 1024) return -1;
-  oracle_job J = {L, d, G, W, C, m, t_max, lam, L > 0 ? (L - 1) / C : 0, eps, scale,
-                  q, k, v, F, gate, y, score, S, z, pending, sel, n_pool};
+  oracle_job J = {L, d, G, W, C, m, t_max, lam, L > 0 ? (L - 1) / C : 0, merge, eps, scale,
+                  q, k, v, F, gate, y, score, S, z, pending, sel, n_pool,
+                  y_sa, lse_sa, y_la, lse_la};
   if (n_threads < 1) n_threads = 1;
   if (n_threads > n_units) n_threads = n_units > 0 ? n_units : 1;
   pthread_t th[256];

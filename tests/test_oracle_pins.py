@@ -199,11 +199,14 @@ def test_nothing_kept_gate_zero_is_sliding_window(W, C):
 def test_linear_branch_is_masked_linear_attention():
     """With nothing kept, the linear branch is the textbook quadratic form
     of (NP-Map) linear attention over keys outside the window and chunk:
-    (M * phi(Q) phi(K)^T) V / row sums."""
+    (M * phi(Q) phi(K)^T) V / row sums, taken without the gate; the default
+    output merges it with the softmax branch under one normaliser and the
+    sum merge [P4 §4] adds it scaled by the gate."""
     rng = np.random.default_rng(7)
     L, C, W, d = 40, 8, 6, 16
     q, k, v, F, g = rand_inputs(rng, 1, 1, 1, L, d)
-    o = bf.prefill(q, k, v, F, g, window=W, chunk=C, budget=W, t_max=5, partials=True)
+    kw = dict(window=W, chunk=C, budget=W, t_max=5, partials=True)
+    o = bf.prefill(q, k, v, F, g, **kw)
     pq, pk = phi_torch(q[0, 0], F[0]), phi_torch(k[0, 0], F[0])
     i, j = np.indices((L, L))
     M = (j <= i - W) & (j // C < i // C)
@@ -211,11 +214,58 @@ def test_linear_branch_is_masked_linear_attention():
     rows = M.any(1)
     want = (Wm @ v[0, 0])[rows] / Wm.sum(1, keepdims=True)[rows]
     np.testing.assert_allclose(o["y_la"][0, 0][rows], want, rtol=1e-11, atol=1e-12)
-    assert np.all(np.isnan(o["y_la"][0, 0][~rows]))
+    np.testing.assert_allclose(o["lse_la"][0, 0][rows], np.log(Wm.sum(1)[rows]), rtol=1e-13)
+    assert np.all(o["y_la"][0, 0][~rows] == 0) and np.all(o["lse_la"][0, 0][~rows] == -np.inf)
     # the merge: one normaliser over exp(logits) and g * <phi, phi>
     za, zl = np.exp(o["lse_sa"][0, 0][rows]), g[0] * Wm.sum(1)[rows]
     mix = (za[:, None] * o["y_sa"][0, 0][rows] + zl[:, None] * want) / (za + zl)[:, None]
     np.testing.assert_allclose(o["y"][0, 0][rows], mix, rtol=1e-10, atol=1e-12)
+    # the sum merge: y_SA + g y_LA, y_SA alone where the linear set is empty
+    for run in (bf.prefill, rec.prefill):
+        s_ = run(q, k, v, F, g, merge="sum", **kw)
+        y_s = s_["y"].reshape(L, d)
+        np.testing.assert_allclose(y_s[rows], o["y_sa"][0, 0][rows] + g[0] * want,
+                                   rtol=1e-10, atol=1e-12)
+        np.testing.assert_allclose(y_s[~rows], o["y_sa"][0, 0][~rows], rtol=1e-12, atol=1e-13)
+
+
+@pytest.mark.parametrize("form", ["bf", "rec"])
+def test_softmax_only_is_masked_softmax(form):
+    """The sparse-attention-only variant ([P3 "Problems with Existing
+    Intra-Layer Hybrid Attention"]) with a non-zero gate: torch's masked SDPA
+    over A(t) (window, own chunk, kept tokens), and the softmax partial's
+    log-normaliser is torch's logsumexp of the masked logits; the exported
+    state is the same as the default merge's."""
+    rng = np.random.default_rng(17)
+    L, C, W, d = 56, 8, 5, 16
+    q, k, v, F, g = rand_inputs(rng, 1, 2, 1, L, d)
+    kw = dict(window=W, chunk=C, budget=W + 12, t_max=6, partials=True)
+    run = bf.prefill if form == "bf" else rec.prefill
+    o = run(q, k, v, F, g, merge="softmax_only", **kw)
+    d1 = run(q, k, v, F, g, **kw)
+    sel = o["sel"][0, 0] if form == "bf" else o["sel"][0]
+    A, _ = bf.key_sets(L, W, C, sel.tolist())
+    want = sdpa(q, np.repeat(k, 2, 1), np.repeat(v, 2, 1), A, 1 / 4.0)
+    np.testing.assert_allclose(o["y"].reshape(want.shape), want, atol=1e-12)
+    np.testing.assert_allclose(o["y_sa"].reshape(want.shape), want, atol=1e-12)
+    logits = torch.as_tensor(q[0]) @ torch.as_tensor(k[0, 0]).T / 4.0
+    lse = torch.logsumexp(logits.masked_fill(~torch.as_tensor(A), -math.inf), -1).numpy()
+    np.testing.assert_allclose(o["lse_sa"].reshape(lse.shape), lse, rtol=1e-13, atol=1e-13)
+    for key in ("S", "z", "score", "sel", "y_la", "lse_la"):
+        np.testing.assert_array_equal(o[key], d1[key])
+    assert not np.allclose(o["y"], d1["y"])  # the gate is not 0: the variants differ
+
+
+def test_gate_zero_merges_coincide():
+    """g = 0 turns the linear branch off in every merge: the default, the
+    sum and the softmax-only outputs are equal."""
+    rng = np.random.default_rng(23)
+    q, k, v, F, _ = rand_inputs(rng, 1, 2, 1, 45, 8, outliers=2)
+    kw = dict(window=6, chunk=8, budget=6 + 8, t_max=4)
+    ys = [rec.prefill(q, k, v, F, np.zeros(2), merge=mg, **kw)["y"]
+          for mg in ("one", "sum", "softmax_only")]
+    np.testing.assert_array_equal(ys[0], ys[1])
+    np.testing.assert_array_equal(ys[0], ys[2])
 
 
 # ------------------------------------------------------------ invariants ----
@@ -367,3 +417,24 @@ def test_recurrent_matches_brute_force(case):
     np.testing.assert_allclose(r["pending"], a["pending"].reshape(U, C), rtol=1e-12, atol=1e-12)
     np.testing.assert_array_equal(r["n_pool"], a["n_pool"].reshape(U))
     _check_selection(a, L, W, C, m)
+
+
+@pytest.mark.parametrize("merge", ["one", "sum", "softmax_only"])
+@pytest.mark.parametrize("case", CASES[:5] + CASES[7:])
+def test_variants_recurrent_matches_brute_force(case, merge):
+    """Both oracle forms agree on the three merges and on the branch
+    partials (recurrence over the state vs. explicit sets)."""
+    B, Hq, Hkv, L, d, W, C, m, tm, nout = case
+    rng = np.random.default_rng(sum(case) + 1)
+    q, k, v, F, g = rand_inputs(rng, B, Hq, Hkv, L, d, outliers=nout)
+    kw = dict(window=W, chunk=C, budget=m, t_max=tm, merge=merge, partials=True)
+    a = bf.prefill(q, k, v, F, g, **kw)
+    r = rec.prefill(q, k, v, F, g, **kw)
+    G = Hq // Hkv
+    U = B * Hkv
+    for key in ("y", "y_sa", "y_la"):
+        np.testing.assert_allclose(r[key], a[key].reshape(B, Hkv, G, L, d).reshape(U, G, L, d),
+                                   rtol=1e-11, atol=1e-12, err_msg=key)
+    for key in ("lse_sa", "lse_la"):
+        np.testing.assert_allclose(r[key], a[key].reshape(U, G, L), rtol=1e-12, atol=1e-12,
+                                   err_msg=key)
