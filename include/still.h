@@ -78,6 +78,19 @@ enum { STILL_DTYPE_F32 = 0, STILL_DTYPE_BF16 = 1 };
 
 /* flags */
 #define STILL_FLAG_FP32_OUT 1u /* write `out` as float32 whatever the dtype */
+/* Branch variants (the pages' ablation axes; the default is one normaliser
+ * over exp(logit) and gate * <phi(q), phi(k)>):
+ *   SOFTMAX_ONLY: the linear branch is dropped, unkept tokens are discarded
+ *     (the "sparse attention only" alternative [P3 "Problems with Existing
+ *     Intra-Layer Hybrid Attention"]); y = softmax over A(t). The state is
+ *     still maintained. Prefill and decode.
+ *   MERGE_SUM: y = y_SA + gate * y_LA, each branch normalised on its own (a
+ *     merge of separately normalised branches, [P4 §4 Gating]). Prefill
+ *     only (decode returns STILL_EUNSUPPORTED). */
+#define STILL_FLAG_SOFTMAX_ONLY 2u
+#define STILL_FLAG_MERGE_SUM 4u
+/* Any other bit, or SOFTMAX_ONLY and MERGE_SUM together, makes every entry
+ * that takes the params return STILL_EINVAL. */
 
 /* status codes */
 #define STILL_OK 0
@@ -163,6 +176,22 @@ int still_prefill_timed(const still_params* p, int64_t seq_len, const void* q, c
                         const void* v, const void* fmap_w, const float* gate, void* out,
                         int32_t* sel_idx, float* score, void* state, void* workspace,
                         size_t ws_bytes, void* stream, void* const* events, int n_pairs);
+
+/* still_prefill that also returns the two branches apart, per (batch row,
+ * query head, position), float32, [B, Hq, L, d] and [B, Hq, L]:
+ *   y_sa   softmax-branch output sum_A e^s v / Z,  lse_sa = ln Z, Z = sum_A e^s
+ *   y_la   linear-branch output  sum_B w v / D,    lse_la = ln D, D = sum_B w,
+ *          w = <phi(q), phi(k)> without the gate (y_la = 0, lse_la = -inf
+ *          where B(t) is empty)
+ * so that the default output is (Z y_sa + g D y_la) / (Z + g D). out, sel_idx,
+ * score and state are written as by still_prefill (with the params' merge);
+ * the walk keeps the branches apart (slower). All four pointers are
+ * required (16-byte aligned); STILL_FLAG_SOFTMAX_ONLY is rejected. */
+int still_prefill_partials(const still_params* p, int64_t seq_len, const void* q, const void* k,
+                           const void* v, const void* fmap_w, const float* gate, void* out,
+                           int32_t* sel_idx, float* score, void* state, void* workspace,
+                           size_t ws_bytes, void* stream, float* y_sa, float* lse_sa, float* y_la,
+                           float* lse_la);
 
 /* still_prefill without a workspace argument, for callers that cannot
  * allocate device memory (code under HIP graph capture, tight serving loops,

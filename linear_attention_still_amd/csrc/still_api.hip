@@ -28,6 +28,10 @@ int derive(const still_params* p, Derived* d) {
   if (!p) return STILL_EINVAL;
   if (p->abi_version != STILL_ABI_VERSION) return STILL_EINVAL;
   if (p->dtype != STILL_DTYPE_F32 && p->dtype != STILL_DTYPE_BF16) return STILL_EINVAL;
+  if (p->flags & ~(STILL_FLAG_FP32_OUT | STILL_FLAG_SOFTMAX_ONLY | STILL_FLAG_MERGE_SUM))
+    return STILL_EINVAL;  // unknown flag bits
+  if ((p->flags & STILL_FLAG_SOFTMAX_ONLY) && (p->flags & STILL_FLAG_MERGE_SUM))
+    return STILL_EINVAL;  // two merges at once
   if (p->batch < 1 || p->n_q_heads < 1 || p->n_kv_heads < 1) return STILL_EINVAL;
   if (p->n_q_heads % p->n_kv_heads != 0) return STILL_EINVAL;
   if (p->window < 1 || p->chunk < 1 || p->budget < p->window || p->t_max < 1) return STILL_EINVAL;
@@ -91,10 +95,13 @@ void layout(const Derived& d, still_state_layout* s) {
 // Prefill launch geometry.
 struct Plan {
   int L, T, n_dec, n_pend, K, NS, Gs, nHG, HPW;
+  bool part;
   int64_t ws_ft, ws_score, ws_delta, ws_flag, ws_dS, ws_rl, ws_total;
 };
 
-Plan plan(const Derived& d, int64_t L) {
+// part: the walk keeps the two branches apart (one query head per wave,
+// held in both head slots of the two-head walk).
+Plan plan(const Derived& d, int64_t L, bool part) {
   Plan pl;
   pl.L = (int)L;
   pl.T = (int)((L + d.C - 1) / d.C);
@@ -108,6 +115,7 @@ Plan plan(const Derived& d, int64_t L) {
   if (gs2 > d.G) gs2 = d.G;
   bool two = gs2 >= 2 && (gs2 / 2) * n_qt == 8;
   if (const char* e = getenv("STILL_HEADS_PER_WAVE")) two = two && atoi(e) != 1;
+  if (part) two = false;
   if (two) {
     pl.HPW = 2;
     pl.Gs = gs2;
@@ -143,10 +151,17 @@ Plan plan(const Derived& d, int64_t L) {
   pl.ws_score = take(nu * L * 4);
   pl.ws_delta = take(nu * L * 4);
   pl.ws_flag = take(nu * L);
-  pl.ws_dS = take(nu * pl.NS * ((int64_t)d.D * d.D + d.D) * 4);
   pl.ws_rl = take(nu * pl.T * (int64_t)(d.C + 1) * 4);
+  pl.ws_dS = take(nu * pl.NS * ((int64_t)d.D * d.D + d.D) * 4);  // last: its size depends on NS
   pl.ws_total = o;
+  pl.part = part;
   return pl;
+}
+
+// Workspace bytes that serve both walks (the separate-branch one included).
+int64_t ws_bytes_any(const Derived& d, int64_t L) {
+  const int64_t a = plan(d, L, false).ws_total, b = plan(d, L, true).ws_total;
+  return a > b ? a : b;
 }
 
 bool misaligned(const void* p) { return ((uintptr_t)p & 15u) != 0; }
@@ -167,6 +182,8 @@ void set_prefill_attrs(int family) {
   (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&still::attend_kernel<T, D, 1>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)still::Blk<T, D>::bytes);
   (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&still::attend_kernel<T, D, 2>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)still::Blk<T, D>::bytes);
+  (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&still::attend_kernel<T, D, 2, true>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)still::Blk<T, D>::bytes);
   (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&still::state_delta_kernel<T, D>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)still::Blk<T, D>::bytes);
@@ -232,7 +249,9 @@ int launch_prefill(const Derived& d, const Plan& pl, still::PrefillArgs a, hipSt
       a.dS, pl.NS, a.state, a.st_unit, a.st_S, a.st_z);
   mk.at(4, 1);
   mk.at(5, 0);
-  if (pl.HPW == 2)
+  if (pl.part)
+    attend_kernel<T, D, 2, true><<<dim3(pl.NS * d.Hkv * pl.nHG * d.B), dim3(512), Blk<T, D>::bytes, s>>>(a);
+  else if (pl.HPW == 2)
     attend_kernel<T, D, 2><<<dim3(pl.NS * d.Hkv * pl.nHG * d.B), dim3(512), Blk<T, D>::bytes, s>>>(a);
   else
     attend_kernel<T, D, 1><<<dim3(pl.NS * d.Hkv * pl.nHG * d.B), dim3(512), Blk<T, D>::bytes, s>>>(a);
@@ -349,13 +368,20 @@ int64_t still_workspace_bytes(const still_params* p, int64_t seq_len) {
   if (rc != STILL_OK) return rc;
   if (seq_len <= 0) return 0;
   if (seq_len > (int64_t)1 << 30) return STILL_EINVAL;
-  return plan(d, seq_len).ws_total;
+  return ws_bytes_any(d, seq_len);
 }
+
+// Branch partials of still_prefill_partials (all null for the other entries).
+struct Partials {
+  float *y_sa, *lse_sa, *y_la, *lse_la;
+  bool any() const { return y_sa || lse_sa || y_la || lse_la; }
+};
 
 static int prefill_impl(const still_params* p, int64_t seq_len, const void* q, const void* k,
                         const void* v, const void* fmap_w, const float* gate, void* out,
                         int32_t* sel_idx, float* score, void* state, void* workspace,
-                        size_t ws_bytes, void* stream, void* const* events, int n_pairs) {
+                        size_t ws_bytes, void* stream, void* const* events, int n_pairs,
+                        Partials parts = Partials{nullptr, nullptr, nullptr, nullptr}) {
   Derived d;
   int rc = derive(p, &d);
   if (rc != STILL_OK) return rc;
@@ -369,7 +395,12 @@ static int prefill_impl(const still_params* p, int64_t seq_len, const void* q, c
   if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(fmap_w) || misaligned(out) ||
       misaligned(state) || misaligned(workspace) || misaligned(gate))
     return STILL_EINVAL;
-  const Plan pl = plan(d, seq_len);
+  if (misaligned(parts.y_sa) || misaligned(parts.y_la)) return STILL_EINVAL;
+  const bool merge_sum = (p->flags & STILL_FLAG_MERGE_SUM) != 0;
+  const bool softmax_only = (p->flags & STILL_FLAG_SOFTMAX_ONLY) != 0;
+  if (merge_sum && softmax_only) return STILL_EINVAL;
+  // the branches are kept apart for the sum merge and for the partials
+  const Plan pl = plan(d, seq_len, merge_sum || parts.any());
   if ((int64_t)ws_bytes < pl.ws_total) return STILL_EWORKSPACE;
   still_state_layout SL;
   layout(d, &SL);
@@ -409,6 +440,12 @@ static int prefill_impl(const still_params* p, int64_t seq_len, const void* q, c
   a.nHG = pl.nHG;
   a.Gs = pl.Gs;
   a.fp32_out = (p->flags & STILL_FLAG_FP32_OUT) ? 1 : 0;
+  a.softmax_only = softmax_only ? 1 : 0;
+  a.merge_sum = merge_sum ? 1 : 0;
+  a.y_sa = parts.y_sa;
+  a.lse_sa = parts.lse_sa;
+  a.y_la = parts.y_la;
+  a.lse_la = parts.lse_la;
   a.scale = d.scale;
   a.eps = d.eps;
   a.scale64 = d.scale64;
@@ -443,6 +480,17 @@ int still_prefill_timed(const still_params* p, int64_t seq_len, const void* q, c
                       ws_bytes, stream, events, n_pairs);
 }
 
+int still_prefill_partials(const still_params* p, int64_t seq_len, const void* q, const void* k,
+                           const void* v, const void* fmap_w, const float* gate, void* out,
+                           int32_t* sel_idx, float* score, void* state, void* workspace,
+                           size_t ws_bytes, void* stream, float* y_sa, float* lse_sa, float* y_la,
+                           float* lse_la) {
+  if (!y_sa || !lse_sa || !y_la || !lse_la) return STILL_EINVAL;
+  if (p && (p->flags & STILL_FLAG_SOFTMAX_ONLY)) return STILL_EINVAL;
+  return prefill_impl(p, seq_len, q, k, v, fmap_w, gate, out, sel_idx, score, state, workspace,
+                      ws_bytes, stream, nullptr, 0, Partials{y_sa, lse_sa, y_la, lse_la});
+}
+
 int still_prefill_noalloc(const still_params* p, int64_t seq_len, const void* q, const void* k,
                           const void* v, const void* fmap_w, const float* gate, void* out,
                           int32_t* sel_idx, float* score, void* state, void* stream) {
@@ -450,7 +498,7 @@ int still_prefill_noalloc(const still_params* p, int64_t seq_len, const void* q,
   const int rc = derive(p, &d);
   if (rc != STILL_OK) return rc;
   if (seq_len < 1 || seq_len > ((int64_t)1 << 30)) return STILL_EINVAL;
-  if (plan(d, seq_len).ws_total > (int64_t)kNoAllocScratchBytes) return STILL_ESCRATCH;
+  if (ws_bytes_any(d, seq_len) > (int64_t)kNoAllocScratchBytes) return STILL_ESCRATCH;
   void* ws = nullptr;
   const int rs = scratch_address(&ws);
   if (rs != STILL_OK) return rs;
@@ -469,6 +517,7 @@ int still_decode_step(const still_params* p, int64_t pos, const void* q, const v
   Derived d;
   int rc = derive(p, &d);
   if (rc != STILL_OK) return rc;
+  if (p->flags & STILL_FLAG_MERGE_SUM) return STILL_EUNSUPPORTED;  // decode keeps one normaliser
   if (pos < 1 || pos > ((int64_t)1 << 30)) return STILL_EINVAL;
   if (!q || !k || !v || !fmap_w || !gate || !state || !out) return STILL_EINVAL;
   if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(fmap_w) || misaligned(out) ||
@@ -497,6 +546,7 @@ int still_decode_step(const still_params* p, int64_t pos, const void* q, const v
   a.R = d.R;
   a.t = (int)pos;
   a.boundary = (pos % d.C) == 0 ? 1 : 0;
+  a.softmax_only = (p->flags & STILL_FLAG_SOFTMAX_ONLY) ? 1 : 0;
   a.fp32_out = (p->flags & STILL_FLAG_FP32_OUT) ? 1 : 0;
   a.scale = d.scale;
   a.eps = d.eps;

@@ -44,6 +44,7 @@ struct DecodeArgs {
   void* out;         // [B][Hq][D]
   int32_t* sel_new;  // [B][Hkv][lam] or null
   int B, Hq, Hkv, G, W, C, m, lam, R, t, boundary, fp32_out;
+  int softmax_only;  // the linear branch dropped (every gate taken as 0)
   float scale, eps;
   double scale64, eps64;  // the same parameters for the float64 score
   long st_unit, st_S, st_z, st_pool_k, st_pool_v, st_pool_pos, st_ring_k, st_ring_v,
@@ -447,8 +448,9 @@ void decode_kernel(DecodeArgs a) {
   auto wrap = [R](int s_) { return s_ >= R ? s_ - R : s_; };
   // the gate of head r = lane % 16 (zero for r >= G) and this lane's
   // entries l, l + 64, ... of z
-  const float g_lane = __builtin_bit_cast(
+  const float g_load = __builtin_bit_cast(
       float, __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(a.gate + kv * G, G * 4), (lane & 15) * 4, 0, 0));
+  const float g_lane = a.softmax_only ? 0.f : g_load;
   float zreg[D / 64];
 #pragma unroll
   for (int u = 0; u < D / 64; ++u)

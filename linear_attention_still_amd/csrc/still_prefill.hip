@@ -46,6 +46,11 @@ struct PrefillArgs {
   char* state;
   int B, Hq, Hkv, G, L, W, C, m, T, n_dec, lam, cap_chunks, K, NS, nHG, Gs, fp32_out;
   int score_out;  // the caller asked for the scores (score is theirs)
+  int softmax_only, merge_sum;  // branch variants (linear branch dropped / sum merge)
+  float* y_sa;    // [B][Hq][L][D] softmax-branch output, or null (separate walk)
+  float* lse_sa;  // [B][Hq][L] natural log of its normaliser, or null
+  float* y_la;    // [B][Hq][L][D] linear-branch output (no gate), or null
+  float* lse_la;  // [B][Hq][L] natural log of sum <phi(q), phi(k)>, or null
   int* rlist;     // [B][Hkv][T][C + 1] tokens whose exported score is refined
   float scale, eps;
   double scale64, eps64;  // the same parameters for the float64 paths
@@ -1394,8 +1399,15 @@ __global__ __launch_bounds__(256) void state_scan_kernel(float* dS, int NS, char
 // exact), the weights below 2^8 by the lazily moved offset.
 // A wave holds HPW heads of one 16-query tile: the key, value and phi(K)
 // fragments it reads from LDS serve every head it holds.
-template <typename T, int D, int HPW>
+// PART: the two branches kept apart. The wave's two head slots then hold one
+// query head twice: slot 0 accumulates the softmax branch alone (the kept,
+// window and own-chunk keys), slot 1 the linear branch alone (linear keys and
+// the state, without the gate); the output is their merge (the single
+// normaliser, or the sum y_SA + g y_LA), and the branch partials (normalised
+// outputs and natural-log normalisers) are written when asked for.
+template <typename T, int D, int HPW, bool PART = false>
 __global__ __launch_bounds__(512) void attend_kernel(PrefillArgs a) {
+  static_assert(!PART || HPW == 2, "the separate-branch walk uses both head slots");
   using B_ = Blk<T, D>;
   typedef typename HalfOf<T>::type H;
   extern __shared__ __align__(16) char smem[];
@@ -1422,7 +1434,8 @@ __global__ __launch_bounds__(512) void attend_kernel(PrefillArgs a) {
   const __amdgpu_buffer_rsrc_t selr = make_rsrc(selu, (uint32_t)((size_t)a.n_dec * a.lam * 4));
   load_ft<T, D, 512>(P, reinterpret_cast<const T*>(a.ft) + (size_t)kv * D * D);
   const int n_qt = C / 16;
-  const bool act = wave < (a.Gs / HPW) * n_qt;  // wave-uniform
+  constexpr int RH = PART ? 1 : HPW;  // query heads per wave
+  const bool act = wave < (a.Gs / RH) * n_qt;  // wave-uniform
   const int hl = act ? wave / n_qt : 0, qt = act ? wave % n_qt : 0;
   // log-weights are kept in base 2: logits times scale * log2(e), linear
   // weights log2(g) + log2 <phi(q), phi(k)>
@@ -1432,8 +1445,9 @@ __global__ __launch_bounds__(512) void attend_kernel(PrefillArgs a) {
   __amdgpu_buffer_rsrc_t qr[HPW];
 #pragma unroll
   for (int j = 0; j < HPW; ++j) {
-    hh[j] = kv * a.G + hg * a.Gs + hl * HPW + j;
-    gg[j] = a.gate[hh[j]];
+    hh[j] = kv * a.G + hg * a.Gs + (PART ? hl : hl * HPW + j);
+    gg[j] = a.softmax_only ? 0.f : a.gate[hh[j]];
+    if constexpr (PART) gg[j] = j == 0 ? 0.f : 1.f;  // slot 0: no linear key; slot 1: gate-free
     lgate2[j] = gg[j] > 0.f ? log2_acc<T>(gg[j]) : STILL_NEG_INF;
     qr[j] = make_rsrc(reinterpret_cast<const T*>(a.q) + ((size_t)(b * a.Hq + hh[j]) * L) * D, kv_bytes);
   }
@@ -1630,6 +1644,11 @@ __global__ __launch_bounds__(512) void attend_kernel(PrefillArgs a) {
       float mx[HPW];
 #pragma unroll
       for (int j = 0; j < HPW; ++j) mx[j] = STILL_NEG_INF;
+      if constexpr (PART) {  // slot 1 (the linear branch) takes no kept key
+        if (is_pool)
+#pragma unroll
+          for (int kt = 0; kt < 4; ++kt) st[1][kt] = f32x4{STILL_NEG_INF, STILL_NEG_INF, STILL_NEG_INF, STILL_NEG_INF};
+      }
       if (is_pool) {
         if (nvalid < 64) {  // uniform: only a last, partial pool block is masked
           const uint64_t v_s = low_bits(nvalid) >> (4 * g4);
@@ -1673,7 +1692,7 @@ __global__ __launch_bounds__(512) void attend_kernel(PrefillArgs a) {
           for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-              float x = ((sa_s >> (16 * kt + i)) & 1ull) ? st[j][kt][i] : STILL_NEG_INF;
+              float x = ((sa_s >> (16 * kt + i)) & 1ull) && !(PART && j == 1) ? st[j][kt][i] : STILL_NEG_INF;
               if (la_blk) {
                 const float w = wt[j][kt][i];
                 const bool la = ((la_s >> (16 * kt + i)) & 1ull) && w > 0.f;
@@ -1796,6 +1815,48 @@ __global__ __launch_bounds__(512) void attend_kernel(PrefillArgs a) {
     for (int i = 0; i < n_la_blk; ++i) process(i, std::true_type{});
     for (int i = n_la_blk; i < nblk; ++i) process(i, std::false_type{});
 
+    if constexpr (PART) {
+      // the branch outputs and their natural-log normalisers (base-2 log of
+      // the weight sum plus the offset, times ln 2), then the merge
+      const float l0 = lacc[0][0], l1 = lacc[1][0];
+      const float lse_sa = l0 > 0.f ? (mrun[0] + log2_acc<T>(l0)) * 0.6931471805599453f : STILL_NEG_INF;
+      const float lse_la = l1 > 0.f ? (mrun[1] + log2_acc<T>(l1)) * 0.6931471805599453f : STILL_NEG_INF;
+      const float i0 = l0 > 0.f ? 1.f / l0 : 0.f, i1 = l1 > 0.f ? 1.f / l1 : 0.f;
+      const float g = a.gate[hh[0]];
+      // single normaliser: y = a y_SA + (1 - a) y_LA, a = Z / (Z + g D);
+      // sum merge: y = y_SA + g y_LA
+      float w_sa = 1.f, w_la = 0.f;
+      if (a.merge_sum) {
+        w_la = g;
+      } else if (g > 0.f && lse_la != STILL_NEG_INF) {
+        const float r = exp_acc<T>(log_acc<T>(g) + lse_la - lse_sa);  // g D / Z
+        w_sa = 1.f / (1.f + r);
+        w_la = r * w_sa;
+      }
+      if (act && t < L) {
+        const size_t ob = ((size_t)(b * a.Hq + hh[0]) * L + t) * D;
+        const size_t orow = (size_t)(b * a.Hq + hh[0]) * L + t;
+#pragma unroll
+        for (int dt = 0; dt < D / 16; ++dt) {
+          const f32x4 ys = O[0][dt] * i0, yl = O[1][dt] * i1;
+          const f32x4 y = ys * w_sa + yl * w_la;
+          const int col = 16 * dt + 4 * g4;
+          if (sizeof(T) == 4 || a.fp32_out) {
+            *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.out) + ob + col) = y;
+          } else {
+            bf16 y4[4] = {(bf16)y[0], (bf16)y[1], (bf16)y[2], (bf16)y[3]};
+            *reinterpret_cast<uint2*>(reinterpret_cast<bf16*>(a.out) + ob + col) = *reinterpret_cast<uint2*>(y4);
+          }
+          if (a.y_sa) *reinterpret_cast<f32x4*>(a.y_sa + ob + col) = ys;
+          if (a.y_la) *reinterpret_cast<f32x4*>(a.y_la + ob + col) = yl;
+        }
+        if (g4 == 0) {
+          if (a.lse_sa) a.lse_sa[orow] = lse_sa;
+          if (a.lse_la) a.lse_la[orow] = lse_la;
+        }
+      }
+      continue;
+    }
     // outputs: normalise; bf16 rows go through LDS for full-line stores
 #pragma unroll
     for (int j = 0; j < HPW; ++j) {

@@ -21,6 +21,8 @@ STILL_ABI_VERSION = 1
 STILL_DTYPE_F32 = 0
 STILL_DTYPE_BF16 = 1
 STILL_FLAG_FP32_OUT = 1
+STILL_FLAG_SOFTMAX_ONLY = 2
+STILL_FLAG_MERGE_SUM = 4
 STILL_OK, STILL_EINVAL, STILL_EUNSUPPORTED, STILL_EWORKSPACE, STILL_EHIP, STILL_ESTATE, \
     STILL_ESCRATCH = 0, -1, -2, -3, -4, -5, -6
 
@@ -72,6 +74,8 @@ def lib() -> ctypes.CDLL:
         L.still_prefill.restype = I32
         L.still_prefill_timed.argtypes = [pp, I64] + [P] * 10 + [ctypes.c_size_t, P, P, I32]
         L.still_prefill_timed.restype = I32
+        L.still_prefill_partials.argtypes = [pp, I64] + [P] * 10 + [ctypes.c_size_t, P] + [P] * 4
+        L.still_prefill_partials.restype = I32
         L.still_prefill_noalloc.argtypes = [pp, I64] + [P] * 10
         L.still_prefill_noalloc.restype = I32
         L.still_noalloc_scratch_bytes.argtypes = []
@@ -86,20 +90,21 @@ def lib() -> ctypes.CDLL:
 
 def make_params(*, dtype: str, batch: int, n_q_heads: int, n_kv_heads: int, head_dim: int,
                 window: int, chunk: int, budget: int, t_max: int, eps: float = 0.0,
-                sm_scale: float = 0.0, fp32_out: bool = False) -> still_params:
+                sm_scale: float = 0.0, fp32_out: bool = False, flags: int = 0) -> still_params:
     """eps <= 0 and sm_scale <= 0 select the library defaults (1e-6 and
-    1/sqrt(head_dim))."""
+    1/sqrt(head_dim)); flags are further STILL_FLAG_* bits."""
     return still_params(STILL_ABI_VERSION,
                         STILL_DTYPE_F32 if dtype in ("f32", torch.float32) else STILL_DTYPE_BF16,
                         batch, n_q_heads, n_kv_heads, head_dim, window, chunk, budget, t_max,
-                        eps, sm_scale, STILL_FLAG_FP32_OUT if fp32_out else 0)
+                        eps, sm_scale, (STILL_FLAG_FP32_OUT if fp32_out else 0) | flags)
 
 
-def params_for(wl, fp32_out: bool = False) -> still_params:
+def params_for(wl, fp32_out: bool = False, flags: int = 0) -> still_params:
     """Parameters of a Workload (linear_attention_still_amd.inputs)."""
     return make_params(dtype=wl.dtype, batch=wl.batch, n_q_heads=wl.n_q_heads,
                        n_kv_heads=wl.n_kv_heads, head_dim=wl.head_dim, window=wl.window,
-                       chunk=wl.chunk, budget=wl.budget, t_max=wl.t_max, fp32_out=fp32_out)
+                       chunk=wl.chunk, budget=wl.budget, t_max=wl.t_max, fp32_out=fp32_out,
+                       flags=flags)
 
 
 def still_status_str(rc: int) -> str:
@@ -158,6 +163,19 @@ def still_prefill(p: still_params, seq_len: int, q, k, v, fmap_w, gate, out, sel
                              _stream(stream))
     if rc != STILL_OK:
         raise StillError("still_prefill", rc)
+
+
+def still_prefill_partials(p: still_params, seq_len: int, q, k, v, fmap_w, gate, out, sel_idx,
+                           score, state, workspace, y_sa, lse_sa, y_la, lse_la,
+                           stream=None) -> None:
+    rc = lib().still_prefill_partials(ctypes.byref(p), int(seq_len), _ptr(q), _ptr(k), _ptr(v),
+                                      _ptr(fmap_w), _ptr(gate), _ptr(out), _ptr(sel_idx),
+                                      _ptr(score), _ptr(state), _ptr(workspace),
+                                      workspace.numel() * workspace.element_size(),
+                                      _stream(stream), _ptr(y_sa), _ptr(lse_sa), _ptr(y_la),
+                                      _ptr(lse_la))
+    if rc != STILL_OK:
+        raise StillError("still_prefill_partials", rc)
 
 
 def still_prefill_noalloc(p: still_params, seq_len: int, q, k, v, fmap_w, gate, out, sel_idx,

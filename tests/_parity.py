@@ -27,15 +27,31 @@ def n_threads() -> int:
 
 
 def gpu_prefill(wl: Workload, x: Dict[str, torch.Tensor], fp32_out: bool = False,
-                keep_device: bool = False) -> Dict[str, torch.Tensor]:
-    p = still.params_for(wl, fp32_out=fp32_out)
+                keep_device: bool = False, flags: int = 0,
+                partials: bool = False) -> Dict[str, torch.Tensor]:
+    """still_prefill (or still_prefill_partials) on the GPU; flags are the
+    branch-variant flags."""
+    p = still.params_for(wl, fp32_out=fp32_out, flags=flags)
     xd = {k: v.cuda() for k, v in x.items()}
     L = xd["q"].shape[2]
-    print("  gpu prefill %s L=%d fp32_out=%s" % (wl.name, L, fp32_out), flush=True)
+    print("  gpu prefill %s L=%d fp32_out=%s flags=%d partials=%s"
+          % (wl.name, L, fp32_out, flags, partials), flush=True)
     bufs = still.PrefillBuffers(p, L)
-    still.run_prefill(p, xd, bufs)
+    out = {}
+    if partials:
+        B, Hq, d = wl.batch, wl.n_q_heads, wl.head_dim
+        out["y_sa"] = torch.full((B, Hq, L, d), float("nan"), device="cuda")
+        out["y_la"] = torch.full((B, Hq, L, d), float("nan"), device="cuda")
+        out["lse_sa"] = torch.full((B, Hq, L), float("nan"), device="cuda")
+        out["lse_la"] = torch.full((B, Hq, L), float("nan"), device="cuda")
+        still.still_prefill_partials(p, L, xd["q"], xd["k"], xd["v"], xd["fmap_w"], xd["gate"],
+                                     bufs.out, bufs.sel if bufs.sel.numel() else None,
+                                     bufs.score, bufs.state, bufs.workspace, out["y_sa"],
+                                     out["lse_sa"], out["y_la"], out["lse_la"])
+    else:
+        still.run_prefill(p, xd, bufs)
     torch.cuda.synchronize()
-    out = {"y": bufs.out, "sel": bufs.sel, "score": bufs.score}
+    out.update({"y": bufs.out, "sel": bufs.sel, "score": bufs.score})
     out.update(still.state_views(p, bufs.state))
     if keep_device:
         out["_state"] = bufs.state
@@ -44,12 +60,13 @@ def gpu_prefill(wl: Workload, x: Dict[str, torch.Tensor], fp32_out: bool = False
     return {k: v.cpu() for k, v in out.items()}
 
 
-def oracle(wl: Workload, x: Dict[str, torch.Tensor], units=None) -> Dict[str, np.ndarray]:
-    print("  oracle %s units=%s threads=%d" % (wl.name, "all" if units is None else len(units),
-                                              n_threads()), flush=True)
+def oracle(wl: Workload, x: Dict[str, torch.Tensor], units=None, merge: str = "one",
+           partials: bool = False) -> Dict[str, np.ndarray]:
+    print("  oracle %s units=%s threads=%d merge=%s" % (
+        wl.name, "all" if units is None else len(units), n_threads(), merge), flush=True)
     return rec.prefill(x["q"], x["k"], x["v"], x["fmap_w"], x["gate"], window=wl.window,
                        chunk=wl.chunk, budget=wl.budget, t_max=wl.t_max, units=units,
-                       n_threads=n_threads())
+                       n_threads=n_threads(), merge=merge, partials=partials)
 
 
 def bf16_half_ulp(ref: np.ndarray) -> np.ndarray:

@@ -135,3 +135,27 @@ def test_noalloc_rejects_oversize_before_any_hip_call():
     rc = still.lib().still_prefill_noalloc(ctypes.byref(p), 65536, *([ctypes.c_void_p(256)] * 10))
     assert rc == still.STILL_ESCRATCH
     assert "scratch" in still.still_status_str(rc)
+
+
+def test_branch_flags_validated_before_any_hip_call():
+    """Unknown flag bits and the two merges at once are rejected by every
+    entry; the separate-branch partials refuse the softmax-only variant; the
+    decode step refuses the sum merge (it keeps one normaliser)."""
+    L = still.lib()
+    fake = ctypes.c_void_p(1 << 20)
+    wl = WORKLOADS["small_f32_L256"]
+    for bad in (still.STILL_FLAG_SOFTMAX_ONLY | still.STILL_FLAG_MERGE_SUM, 8, 1 << 31):
+        p = still.params_for(wl, flags=bad)
+        assert L.still_lambda(ctypes.byref(p)) == still.STILL_EINVAL
+        assert L.still_workspace_bytes(ctypes.byref(p), 256) == still.STILL_EINVAL
+        assert L.still_prefill(ctypes.byref(p), 256, *([fake] * 10), 1 << 30, None) == still.STILL_EINVAL
+    p = still.params_for(wl, flags=still.STILL_FLAG_SOFTMAX_ONLY)
+    ws = still.still_workspace_bytes(p, 256)
+    rc = L.still_prefill_partials(ctypes.byref(p), 256, *([fake] * 10), ws, None, *([fake] * 4))
+    assert rc == still.STILL_EINVAL
+    p = still.params_for(wl)
+    rc = L.still_prefill_partials(ctypes.byref(p), 256, *([fake] * 10), ws, None, fake, None, fake, fake)
+    assert rc == still.STILL_EINVAL  # all four partial outputs are required
+    p = still.params_for(WORKLOADS["decode_bf16_B64_ctx16K"], flags=still.STILL_FLAG_MERGE_SUM)
+    rc = L.still_decode_step(ctypes.byref(p), 16384, *([fake] * 9), 0, None)
+    assert rc == still.STILL_EUNSUPPORTED

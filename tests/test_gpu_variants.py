@@ -1,0 +1,162 @@
+"""Parity of the branch variants and the branch partials with the oracle,
+on the GPU (through the C ABI).
+
+The variants are the ablation axes the pages discuss: the softmax branch
+alone (unkept tokens dropped, the sparse-attention-only alternative of the
+STILL article, "Problems with Existing Intra-Layer Hybrid Attention"), the
+sum of separately normalised branches (the hybrid-architecture survey, §4
+on gating) and the default single normaliser. The partials are the two
+branches apart: each normalised output and the natural log of its
+normaliser, the linear one without the gate.
+
+Bars: those of the default path (tests/_parity.py) for the outputs, the
+selections, scores and state; the branch outputs (float32) within the
+dtype's float32-output bar; the log-normalisers within the dtype's max-abs
+bar (1e-4 float32, 2e-2 bfloat16: a relative bar on the normaliser), with
+-inf exactly where the linear key set is empty.
+"""
+import numpy as np
+import pytest
+import torch
+
+from linear_attention_still_amd import still
+from linear_attention_still_amd.inputs import WORKLOADS, Workload, make_decode_tokens, make_inputs
+from oracle import rec
+from tests import _parity as P
+
+pytestmark = pytest.mark.gpu
+
+
+def small(name, dtype, B, Hq, Hkv, d, L, W, C, m, t_max, out=0.01, seed=13):
+    return Workload(name, dtype, B, Hq, Hkv, d, L, W, C, m, t_max, sigma=0.5,
+                    outlier_frac=out, seed=seed)
+
+
+SHAPES = [
+    small("f32_gqa_ragged", "f32", 2, 4, 2, 64, 333, 40, 64, 40 + 6 * 3, 6, out=0.0),
+    small("bf16_d128_gqa", "bf16", 1, 8, 2, 128, 1000, 64, 64, 64 + 16 * 3, 16),
+    small("bf16_C16_W8", "bf16", 1, 2, 1, 64, 300, 8, 16, 8 + 19 * 2, 19),
+    small("bf16_G8_C32", "bf16", 1, 8, 1, 64, 300, 32, 32, 32 + 10 * 2, 10),
+    small("bf16_G1", "bf16", 2, 3, 3, 64, 260, 32, 32, 32 + 9 * 2, 9),
+    small("bf16_W256_C128", "bf16", 1, 4, 1, 128, 900, 256, 128, 256 + 8 * 6, 8),
+    small("bf16_pool_global_list", "bf16", 1, 4, 1, 64, 2048, 64, 64, 64 + 36 * 32, 32),
+    small("bf16_one_chunk", "bf16", 1, 4, 1, 64, 64, 16, 64, 64, 1),
+]
+IDS = [w.name for w in SHAPES]
+
+
+def _units_rows(wl, t):
+    """[U, G, ...] of a [B, Hq, ...] tensor, in the oracle's unit order."""
+    G = wl.group
+    a = t.float().cpu().numpy()
+    return np.stack([a[b, kv * G:(kv + 1) * G] for b in range(wl.batch)
+                     for kv in range(wl.n_kv_heads)])
+
+
+def check_lse(got, ref, dtype, what):
+    assert np.array_equal(np.isneginf(got), np.isneginf(ref)), what
+    fin = np.isfinite(ref)
+    assert np.all(np.isfinite(got[fin])), what
+    err = float(np.abs(got[fin] - ref[fin]).max()) if fin.any() else 0.0
+    print("    %s max_abs=%.3e" % (what, err), flush=True)
+    assert err <= (1e-4 if dtype == "f32" else 2e-2), (what, err)
+
+
+@pytest.mark.parametrize("wl", SHAPES, ids=IDS)
+def test_prefill_partials(wl):
+    x = make_inputs(wl)
+    o = P.oracle(wl, x, partials=True)
+    g = P.gpu_prefill(wl, x, fp32_out=(wl.dtype == "bf16"), partials=True)
+    P.compare_prefill(wl, g, o, out_fp32=(wl.dtype == "bf16"))
+    for key in ("y_sa", "y_la"):
+        P.check_outputs(_units_rows(wl, g[key]), o[key], wl.dtype, True, key)
+    la_empty = np.isneginf(o["lse_la"])
+    assert np.all(_units_rows(wl, g["y_la"])[la_empty] == 0)
+    for key in ("lse_sa", "lse_la"):
+        check_lse(_units_rows(wl, g[key]), o[key], wl.dtype, key)
+    # the default walk gives the same merged output as the separate one; the
+    # selection work is the same, the state scan may group chunks otherwise
+    d = P.gpu_prefill(wl, x, fp32_out=(wl.dtype == "bf16"))
+    P.check_outputs(d["y"].float().numpy(), g["y"].float().numpy().astype(np.float64), wl.dtype,
+                    True, "two walks")
+    for k in ("sel", "score", "pool_k"):
+        assert torch.equal(d[k], g[k]), k
+    assert np.array_equal(d["pending"].numpy(), g["pending"].numpy(), equal_nan=True)
+    for k in ("S", "z"):
+        diff = (d[k] - g[k]).abs().max().item()
+        assert diff <= 1e-5 * max(1.0, d[k].abs().max().item()), (k, diff)
+
+
+@pytest.mark.parametrize("variant", ["sum", "softmax_only"])
+@pytest.mark.parametrize("wl", SHAPES, ids=IDS)
+def test_prefill_merge_variants(wl, variant):
+    flags = still.STILL_FLAG_MERGE_SUM if variant == "sum" else still.STILL_FLAG_SOFTMAX_ONLY
+    x = make_inputs(wl)
+    o = P.oracle(wl, x, merge=variant)
+    g = P.gpu_prefill(wl, x, fp32_out=(wl.dtype == "bf16"), flags=flags)
+    P.compare_prefill(wl, g, o, out_fp32=(wl.dtype == "bf16"))
+    if wl.dtype == "bf16":
+        g2 = P.gpu_prefill(wl, x, fp32_out=False, flags=flags)
+        P.compare_prefill(wl, g2, o, out_fp32=False, check_state_too=False)
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("variant", ["partials", "sum", "softmax_only"])
+def test_llama8b_L16K_variants_sampled_units(variant):
+    """The 16K workload (batch 1, 32 query / 8 kv heads, d = 128) in each
+    variant; the oracle checks two kv-head units."""
+    wl = WORKLOADS["llama8b_bf16_L16K"]
+    x = make_inputs(wl)
+    units = [(0, 2), (0, 7)]
+    merge = "one" if variant == "partials" else variant
+    flags = {"partials": 0, "sum": still.STILL_FLAG_MERGE_SUM,
+             "softmax_only": still.STILL_FLAG_SOFTMAX_ONLY}[variant]
+    o = P.oracle(wl, x, units=units, merge=merge, partials=variant == "partials")
+    g = P.gpu_prefill(wl, x, fp32_out=True, flags=flags, partials=variant == "partials")
+    P.compare_prefill(wl, g, o, units=units, out_fp32=True)
+    if variant == "partials":
+        rows = P.unit_rows(wl, units)
+        for key in ("y_sa", "y_la"):
+            got = np.stack([g[key][b, h0:h1].numpy() for b, h0, h1 in rows])
+            P.check_outputs(got, o[key], "bf16", True, key)
+        for key in ("lse_sa", "lse_la"):
+            got = np.stack([g[key][b, h0:h1].numpy() for b, h0, h1 in rows])
+            check_lse(got, o[key], "bf16", key)
+
+
+DECODE_SHAPES = [
+    (small("dec_f32", "f32", 1, 2, 1, 64, 90, 16, 32, 16 + 4 * 6, 6, out=0.0), 90, 70),
+    (small("dec_bf16_d128", "bf16", 2, 8, 2, 128, 256, 64, 64, 64 + 8 * 2, 8), 256, 130),
+    (small("dec_bf16_W_gt_C", "bf16", 1, 2, 1, 64, 70, 48, 16, 48 + 2 * 12, 12), 70, 60),
+]
+
+
+@pytest.mark.parametrize("case", DECODE_SHAPES, ids=[c[0].name for c in DECODE_SHAPES])
+def test_decode_softmax_only(case):
+    """Prefill and decode with the softmax branch alone; the oracle runs the
+    same variant over all L0 + n tokens (the state is still maintained)."""
+    wl, L0, n = case
+    x = make_inputs(wl, seq_len=L0)
+    toks = make_decode_tokens(wl, n)
+    flags = still.STILL_FLAG_SOFTMAX_ONLY
+    g = P.gpu_prefill(wl, x, keep_device=True, flags=flags)
+    p = still.params_for(wl, fp32_out=True, flags=flags)
+    xd = {k: v.cuda() for k, v in x.items()}
+    td = {k: v.cuda() for k, v in toks.items()}
+    outs, sels = P.run_decode(wl, g["_state"], p, xd, td, L0, fp32_out=True)
+    units = [(b, kv) for b in range(wl.batch) for kv in range(wl.n_kv_heads)]
+    qs, ks, vs, Fs, gs = P.concat_units(x, toks, wl, units)
+    o = rec.run_units(qs, ks, vs, Fs, gs, window=wl.window, chunk=wl.chunk, budget=wl.budget,
+                      t_max=wl.t_max, n_threads=P.n_threads(), merge="softmax_only")
+    G = wl.group
+    yg = np.stack([outs[:, b, kv * G:(kv + 1) * G].numpy().transpose(1, 0, 2) for b, kv in units])
+    P.check_outputs(yg, o["y"][:, :, L0:], wl.dtype, True, "decode y")
+    for s in range(n):
+        t = L0 + s
+        if t % wl.chunk == 0 and o["lam"] > 0:
+            got = np.stack([sels[s, b, kv].numpy() for b, kv in units])
+            assert np.array_equal(got, o["sel"][:, t // wl.chunk - 1]), s
+    sv = still.state_views(p, g["_state"])
+    P.check_state(sv["S"].cpu().numpy(), o["S"], wl.dtype, "decode S")
+    P.check_state(sv["z"].cpu().numpy(), o["z"], wl.dtype, "decode z")
+
