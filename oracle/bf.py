@@ -94,7 +94,8 @@ def np_map(x: np.ndarray, F: np.ndarray) -> np.ndarray:
 
 def prefill(q, k, v, fmap_w, gate, *, window: int, chunk: int, budget: int,
             t_max: int, eps: float = 1e-6, sm_scale: Optional[float] = None,
-            partials: bool = False, merge: str = "one") -> Dict[str, np.ndarray]:
+            partials: bool = False, merge: str = "one", route: str = "saliency",
+            ext_score=None) -> Dict[str, np.ndarray]:
     """One STILL layer over a whole sequence, every query by brute force.
 
     q [B,Hq,L,d], k/v [B,Hkv,L,d], fmap_w [Hkv,d,d], gate [Hq] (any array
@@ -113,9 +114,21 @@ def prefill(q, k, v, fmap_w, gate, *, window: int, chunk: int, budget: int,
     each normalised on its own [P4 §4]; "softmax_only" = y_SA, the linear
     branch dropped and unkept tokens discarded ([P3 "Problems with Existing
     Intra-Layer Hybrid Attention"]: the sparse-attention-only alternative).
+
+    route: the score that ranks a chunk's tokens, the Self-Saliency Score
+    ("saliency") or an alternative of the pages' routing-metric ablation
+    [P3 "Ablation Studies"]: "diag" (the window softmax's weight on the
+    token itself, summed over the group's heads), "qk" (the scaled self
+    logit, summed over the heads), "keynorm" (||k_t||), "uniform" (reading:
+    evenly spaced offsets floor(i C / lambda) of each chunk score 1, the rest
+    0) or "external" (ext_score [B,Hkv,L], e.g. random routing's draws).
     """
     if merge not in ("one", "sum", "softmax_only"):
         raise ValueError("merge must be one, sum or softmax_only")
+    if route not in ("saliency", "diag", "qk", "keynorm", "uniform", "external"):
+        raise ValueError("unknown route")
+    if route == "external" and ext_score is None:
+        raise ValueError("route external needs ext_score")
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
@@ -151,11 +164,24 @@ def prefill(q, k, v, fmap_w, gate, *, window: int, chunk: int, budget: int,
             # Score of every token, summed over the query heads of the group
             # (reading: routing is per kv head).
             sc = np.zeros(L)
+            marks = {(i * C) // lam for i in range(lam)} if lam > 0 else set()
             for t in range(L):
                 lo = max(0, t - W + 1)
-                for h in heads:
+                if route == "keynorm":
+                    sc[t] = math.sqrt(float(K[t] @ K[t]))
+                elif route == "uniform":
+                    sc[t] = 1.0 if t % C in marks else 0.0
+                elif route == "external":
+                    sc[t] = float(np.float32(ext_score[b, kv, t]))
+                for h in heads if route in ("saliency", "diag", "qk") else ():
                     logits = scale * (K[lo:t + 1] @ q[b, h, t])
-                    sc[t] += saliency_kl(logits, t - lo, eps)
+                    if route == "saliency":
+                        sc[t] += saliency_kl(logits, t - lo, eps)
+                    elif route == "diag":
+                        e = np.exp(logits - logits.max())
+                        sc[t] += e[-1] / e.sum()
+                    else:
+                        sc[t] += logits[-1]
             score[b, kv] = sc
 
             # Delayed chunk-level Top-lambda: chunk c is decided when chunk

@@ -23,6 +23,9 @@ _lib = None
 # merge of the two branches (still_oracle.c): one normaliser, the sum of
 # separately normalised branches, or the softmax branch alone
 MERGES = {"one": 0, "sum": 1, "softmax_only": 2}
+# routing metric (still_oracle.c): the Self-Saliency Score or one of the
+# alternatives of the routing ablation; "external" takes the caller's scores
+ROUTES = {"saliency": 0, "diag": 1, "qk": 2, "keynorm": 3, "uniform": 4, "external": 5}
 
 
 def build(force: bool = True) -> str:
@@ -47,7 +50,7 @@ def _load():
         f = lib.still_oracle_run
         P = ctypes.c_void_p
         f.argtypes = [ctypes.c_int] * 8 + [ctypes.c_double] * 2 + [P] * 5 + \
-            [ctypes.c_int] + [P] * 7 + [ctypes.c_int] + [P] * 4
+            [ctypes.c_int] + [P] * 7 + [ctypes.c_int] + [P] * 4 + [ctypes.c_int, P]
         f.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -67,7 +70,8 @@ def prefill(q, k, v, fmap_w, gate, *, window: int, chunk: int, budget: int,
             t_max: int, eps: float = 1e-6, sm_scale: Optional[float] = None,
             units: Optional[Sequence[Tuple[int, int]]] = None,
             n_threads: int = 1, merge: str = "one",
-            partials: bool = False) -> Dict[str, np.ndarray]:
+            partials: bool = False, route: str = "saliency",
+            ext_score=None) -> Dict[str, np.ndarray]:
     """Run the recurrent oracle on the listed (batch, kv head) units.
 
     q [B,Hq,L,d], k/v [B,Hkv,L,d], fmap_w [Hkv,d,d], gate [Hq]. Outputs
@@ -76,7 +80,8 @@ def prefill(q, k, v, fmap_w, gate, *, window: int, chunk: int, budget: int,
     pending [U,C], n_pool [U]; with partials=True also y_sa, y_la [U,G,L,d]
     and lse_sa, lse_la [U,G,L] (each branch normalised on its own, the
     linear one without the gate; y_la = 0 and lse_la = -inf where the state
-    is empty). merge: "one", "sum" or "softmax_only" (see MERGES).
+    is empty). merge: "one", "sum" or "softmax_only" (see MERGES). route:
+    a key of ROUTES; ext_score [B,Hkv,L] the caller's scores for "external".
     """
     B, Hq, L, d = q.shape
     Hkv = k.shape[1]
@@ -90,17 +95,26 @@ def prefill(q, k, v, fmap_w, gate, *, window: int, chunk: int, budget: int,
     Fs = np.stack([_f32(fmap_w[kv]) for _, kv in units]) if U else np.zeros((0, d, d), np.float32)
     gs = np.stack([_f32(gate[kv * G:(kv + 1) * G]) for _, kv in units]) if U else \
         np.zeros((0, G), np.float32)
+    ext = None
+    if ext_score is not None:
+        ext = np.stack([_f32(ext_score[b, kv]) for b, kv in units]) if U else \
+            np.zeros((0, L), np.float32)
     return run_units(qs, ks, vs, Fs, gs, window=window, chunk=chunk, budget=budget,
                      t_max=t_max, eps=eps, sm_scale=sm_scale, n_threads=n_threads,
-                     merge=merge, partials=partials)
+                     merge=merge, partials=partials, route=route, ext=ext)
 
 
 def run_units(qs, ks, vs, Fs, gs, *, window: int, chunk: int, budget: int, t_max: int,
               eps: float = 1e-6, sm_scale: Optional[float] = None,
-              n_threads: int = 1, merge: str = "one",
-              partials: bool = False) -> Dict[str, np.ndarray]:
-    """Run on pre-gathered per-unit arrays (see still_oracle_run)."""
+              n_threads: int = 1, merge: str = "one", partials: bool = False,
+              route: str = "saliency", ext=None) -> Dict[str, np.ndarray]:
+    """Run on pre-gathered per-unit arrays (see still_oracle_run); ext
+    [U, L]: the caller's scores for route "external"."""
     qs, ks, vs, Fs, gs = (_f32(a) for a in (qs, ks, vs, Fs, gs))
+    if route == "external":
+        if ext is None:
+            raise ValueError("route external needs the caller's scores")
+        ext = _f32(ext)
     U, G, L, d = qs.shape
     lam = min(chunk, (budget - window) // t_max) if budget >= window else 0
     n_dec = (L - 1) // chunk if L > 0 else 0
@@ -122,7 +136,8 @@ def run_units(qs, ks, vs, Fs, gs, *, window: int, chunk: int, budget: int, t_max
     rc = lib.still_oracle_run(U, L, d, G, window, chunk, budget, t_max, float(eps), scale,
                               ptr(qs), ptr(ks), ptr(vs), ptr(Fs), ptr(gs), int(n_threads),
                               ptr(y), ptr(score), ptr(sel), ptr(S), ptr(z), ptr(pending),
-                              ptr(n_pool), MERGES[merge], *pp)
+                              ptr(n_pool), MERGES[merge], *pp, ROUTES[route],
+                              ptr(ext) if route == "external" else None)
     if rc != 0:
         raise ValueError("still_oracle_run rejected its arguments (rc=%d)" % rc)
     out = {"y": y, "score": score, "sel": sel, "S": S, "z": z, "pending": pending,

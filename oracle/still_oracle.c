@@ -44,8 +44,22 @@
  *     Attention"]); the state is still maintained. */
 enum { MERGE_ONE = 0, MERGE_SUM = 1, MERGE_SOFTMAX_ONLY = 2 };
 
+/* Routing metric: the score that ranks a chunk's tokens. The default is
+ * the Self-Saliency Score; the others are the alternatives the pages'
+ * routing-metric ablation compares it with [P3 "Ablation Studies"]:
+ *   ROUTE_DIAG     the diagonal attention weight a_diag_t of the window
+ *                  softmax, summed over the group's query heads;
+ *   ROUTE_QK       the scaled self logit q_t . k_t, summed over the heads;
+ *   ROUTE_KEYNORM  ||k_t|| (one value per kv head);
+ *   ROUTE_UNIFORM  reading: evenly spaced positions, score 1 at the offsets
+ *                  floor(i C / lambda), i < lambda, of each chunk, else 0;
+ *   ROUTE_EXTERNAL scores supplied by the caller (random routing draws
+ *                  them outside the layer). */
+enum { ROUTE_SALIENCY = 0, ROUTE_DIAG, ROUTE_QK, ROUTE_KEYNORM, ROUTE_UNIFORM, ROUTE_EXTERNAL };
+
 typedef struct {
-  int L, d, G, W, C, m, t_max, lam, n_dec, merge;
+  int L, d, G, W, C, m, t_max, lam, n_dec, merge, route;
+  const float* ext; /* [n_units, L] caller scores (ROUTE_EXTERNAL), else null */
   double eps, scale;
   const float *q, *k, *v, *F, *gate;
   double *y, *score, *S, *z, *pending;
@@ -111,6 +125,33 @@ static double saliency(const double* qh, const double* K, int t, int W, int d,
   if (p > 0.0) sc += p * log(p / eps);
   if (pn > 0.0) sc += pn * log(pn / (1.0 - eps));
   return sc;
+}
+
+/* Diagonal attention weight of token t for one head: the window softmax's
+ * weight on the token itself. buf holds W doubles. */
+static double diag_weight(const double* qh, const double* K, int t, int W, int d, double scale,
+                          double* buf) {
+  const int lo = t - W + 1 > 0 ? t - W + 1 : 0;
+  const int n = t - lo + 1;
+  for (int j = 0; j < n; ++j) {
+    const double* kj = K + (size_t)(lo + j) * d;
+    double s = 0.0;
+    for (int i = 0; i < d; ++i) s += qh[i] * kj[i];
+    buf[j] = scale * s;
+  }
+  double mx = buf[0];
+  for (int j = 1; j < n; ++j) mx = buf[j] > mx ? buf[j] : mx;
+  double z = 0.0;
+  for (int j = 0; j < n; ++j) z += exp(buf[j] - mx);
+  return exp(buf[n - 1] - mx) / z;
+}
+
+/* ROUTE_UNIFORM: 1 if offset r of a chunk of C is one of floor(i C / lam),
+ * i = 0 .. lam - 1, else 0. */
+static double uniform_mark(int r, int C, int lam) {
+  for (int i = 0; i < lam; ++i)
+    if ((int)(((long)i * C) / lam) == r) return 1.0;
+  return 0.0;
 }
 
 static int full_chunks_out_of_window(int c, int W, int C) {
@@ -197,10 +238,30 @@ static void run_unit(const oracle_job* J, int u) {
       }
       ++n_la;
     }
-    /* Score of token t, summed over the group's query heads. */
+    /* Routing score of token t (summed over the group's query heads where
+     * the metric is per query head). */
     double st = 0.0;
-    for (int h = 0; h < G; ++h)
-      st += saliency(Q + (size_t)h * Ld + (size_t)t * d, K, t, W, d, J->scale, J->eps, logit);
+    if (J->route == ROUTE_KEYNORM) {
+      for (int i = 0; i < d; ++i) st += K[(size_t)t * d + i] * K[(size_t)t * d + i];
+      st = sqrt(st);
+    } else if (J->route == ROUTE_UNIFORM) {
+      st = uniform_mark(t % C, C, J->lam);
+    } else if (J->route == ROUTE_EXTERNAL) {
+      st = J->ext[(size_t)u * L + t];
+    } else {
+      for (int h = 0; h < G; ++h) {
+        const double* qh = Q + (size_t)h * Ld + (size_t)t * d;
+        if (J->route == ROUTE_DIAG) {
+          st += diag_weight(qh, K, t, W, d, J->scale, logit);
+        } else if (J->route == ROUTE_QK) {
+          double s = 0.0;
+          for (int i = 0; i < d; ++i) s += qh[i] * K[(size_t)t * d + i];
+          st += J->scale * s;
+        } else {
+          st += saliency(qh, K, t, W, d, J->scale, J->eps, logit);
+        }
+      }
+    }
     score[t] = st;
 
     /* Softmax keys: every j in [lo, t] (window or own chunk) plus kept
@@ -318,7 +379,9 @@ static void* worker(void* p) {
  * Outputs (host, caller-allocated):
  *   y [n_units, G, L, d], score [n_units, L], sel [n_units, n_dec, lam],
  *   S [n_units, d, d], z [n_units, d], pending [n_units, C], n_pool [n_units].
- * merge: MERGE_ONE, MERGE_SUM or MERGE_SOFTMAX_ONLY. y_sa, lse_sa, y_la,
+ * merge: MERGE_ONE, MERGE_SUM or MERGE_SOFTMAX_ONLY. route: a ROUTE_*
+ * metric; ext [n_units, L]: the caller's scores for ROUTE_EXTERNAL (else
+ * ignored, may be null). y_sa, lse_sa, y_la,
  * lse_la: all null, or the branch partials [n_units, G, L, d] / [n_units,
  * G, L]: each branch normalised on its own, the linear one without the
  * gate (y_la = 0, lse_la = -inf where the state is empty), lse = natural
@@ -329,15 +392,19 @@ int still_oracle_run(int n_units, int L, int d, int G, int W, int C, int m, int 
                      const float* v, const float* F, const float* gate, int n_threads,
                      double* y, double* score, int32_t* sel, double* S, double* z,
                      double* pending, int32_t* n_pool, int merge, double* y_sa,
-                     double* lse_sa, double* y_la, double* lse_la) {
+                     double* lse_sa, double* y_la, double* lse_la, int route,
+                     const float* ext) {
   if (n_units < 0 || L < 0 || d < 1 || G < 1 || W < 1 || C < 1 || m < W || t_max < 1)
     return -1;
   if (merge < MERGE_ONE || merge > MERGE_SOFTMAX_ONLY) return -1;
+  if (route < ROUTE_SALIENCY || route > ROUTE_EXTERNAL) return -1;
+  if (route == ROUTE_EXTERNAL && !ext) return -1;
   if (!(y_sa && lse_sa && y_la && lse_la) && (y_sa || lse_sa || y_la || lse_la)) return -1;
   int lam = (m - W) / t_max;
   if (lam > C) lam = C;
   if (lam > 1024) return -1;
-  oracle_job J = {L, d, G, W, C, m, t_max, lam, L > 0 ? (L - 1) / C : 0, merge, eps, scale,
+  oracle_job J = {L, d, G, W, C, m, t_max, lam, L > 0 ? (L - 1) / C : 0, merge, route, ext,
+                  eps, scale,
                   q, k, v, F, gate, y, score, S, z, pending, sel, n_pool,
                   y_sa, lse_sa, y_la, lse_la};
   if (n_threads < 1) n_threads = 1;

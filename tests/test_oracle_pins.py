@@ -438,3 +438,88 @@ def test_variants_recurrent_matches_brute_force(case, merge):
     for key in ("lse_sa", "lse_la"):
         np.testing.assert_allclose(r[key], a[key].reshape(U, G, L), rtol=1e-12, atol=1e-12,
                                    err_msg=key)
+
+
+# ------------------------------------------------------ routing metrics ----
+
+def _topk_selection(score_t, L, C, lam):
+    """Per decided chunk, the lam positions with the largest scores by
+    torch.topk (distinct scores), ascending."""
+    n_dec = (L - 1) // C
+    out = []
+    for c in range(n_dec):
+        _, idx = torch.topk(score_t[c * C:(c + 1) * C], lam)
+        out.append(sorted((idx + c * C).tolist()))
+    return np.array(out).reshape(n_dec, lam)
+
+
+@pytest.mark.parametrize("route", ["diag", "qk", "keynorm", "external"])
+@pytest.mark.parametrize("form", ["bf", "rec"])
+def test_routing_metric_scores_and_selection(route, form):
+    """The routing-metric alternatives [P3 "Ablation Studies"]: the scores
+    are torch's window softmax weight on the token itself (diag), torch's
+    scaled self dot product (qk), torch's vector norm (keynorm) or the given
+    draws (external), summed over the group's heads where per query head;
+    each decided chunk keeps torch.topk of them (the budget never fills)."""
+    rng = np.random.default_rng(31)
+    B, Hq, Hkv, L, d, W, C = 1, 2, 1, 50, 8, 6, 8
+    q, k, v, F, g = rand_inputs(rng, B, Hq, Hkv, L, d)
+    m = W + 6 * 3  # lambda = 18 / 6 = 3 for each of the six decided chunks
+    ext = rng.uniform(0, 1, (B, Hkv, L)).astype(np.float32)
+    kw = dict(window=W, chunk=C, budget=m, t_max=6, route=route, ext_score=ext)
+    o = (bf.prefill if form == "bf" else rec.prefill)(q, k, v, F, g, **kw)
+    lam = o["lam"]
+    assert lam == 3
+    qt, kt = torch.as_tensor(q[0]), torch.as_tensor(k[0, 0])
+    scale = 1 / math.sqrt(d)
+    if route == "diag":
+        i, j = np.indices((L, L))
+        band = torch.as_tensor((j <= i) & (j >= i - W + 1))
+        p = torch.softmax((qt @ kt.T * scale).masked_fill(~band, -math.inf), -1)
+        want = torch.diagonal(p, dim1=-2, dim2=-1).sum(0)
+    elif route == "qk":
+        want = (qt * kt).sum(-1).sum(0) * scale
+    elif route == "keynorm":
+        want = torch.linalg.vector_norm(kt, dim=-1)
+    else:
+        want = torch.as_tensor(ext[0, 0], dtype=torch.float64)
+    np.testing.assert_allclose(o["score"].reshape(L), want.numpy(), rtol=1e-12, atol=1e-14)
+    np.testing.assert_array_equal(o["sel"].reshape(-1, lam), _topk_selection(want, L, C, lam))
+    # the state holds the unselected tokens whatever ranked them
+    _check_selection(o if form == "bf" else bf.prefill(q, k, v, F, g, **kw), L, W, C, m)
+
+
+def test_uniform_routing_hand_example():
+    """Uniform routing, C = 16, lambda = 6: every decided chunk keeps the
+    offsets floor(16 i / 6) = 0, 2, 5, 8, 10, 13; the last chunk's scores are
+    1 at those offsets and 0 elsewhere."""
+    rng = np.random.default_rng(3)
+    L, C, W = 60, 16, 4
+    q, k, v, F, g = rand_inputs(rng, 1, 1, 1, L, 8)
+    offs = [0, 2, 5, 8, 10, 13]
+    for run in (bf.prefill, rec.prefill):
+        o = run(q, k, v, F, g, window=W, chunk=C, budget=W + 6 * 3, t_max=3, route="uniform")
+        assert o["lam"] == 6
+        sel = o["sel"].reshape(3, 6)
+        for c in range(3):
+            assert sel[c].tolist() == [c * C + x for x in offs]
+        pend = o["pending"].reshape(-1)[:L - 3 * C]
+        assert pend.tolist() == [1.0 if x in offs else 0.0 for x in range(L - 3 * C)]
+
+
+@pytest.mark.parametrize("route", ["diag", "qk", "keynorm", "uniform", "external"])
+@pytest.mark.parametrize("case", CASES[:5] + CASES[7:])
+def test_routes_recurrent_matches_brute_force(case, route):
+    B, Hq, Hkv, L, d, W, C, m, tm, nout = case
+    rng = np.random.default_rng(sum(case) + 2)
+    q, k, v, F, g = rand_inputs(rng, B, Hq, Hkv, L, d, outliers=nout)
+    ext = rng.uniform(0, 1, (B, Hkv, L)).astype(np.float32)
+    kw = dict(window=W, chunk=C, budget=m, t_max=tm, route=route, ext_score=ext)
+    a = bf.prefill(q, k, v, F, g, **kw)
+    r = rec.prefill(q, k, v, F, g, **kw)
+    G, U = Hq // Hkv, B * Hkv
+    np.testing.assert_allclose(r["score"], a["score"].reshape(U, L), rtol=1e-12, atol=1e-13)
+    np.testing.assert_array_equal(r["sel"], a["sel"].reshape(U, a["n_dec"], a["lam"]))
+    np.testing.assert_allclose(r["y"], a["y"].reshape(U, G, L, d), rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(r["S"], a["S"].reshape(U, d, d), rtol=1e-11, atol=1e-11)
+    _check_selection(a, L, W, C, m)
