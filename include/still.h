@@ -89,8 +89,32 @@ enum { STILL_DTYPE_F32 = 0, STILL_DTYPE_BF16 = 1 };
  *     only (decode returns STILL_EUNSUPPORTED). */
 #define STILL_FLAG_SOFTMAX_ONLY 2u
 #define STILL_FLAG_MERGE_SUM 4u
-/* Any other bit, or SOFTMAX_ONLY and MERGE_SUM together, makes every entry
- * that takes the params return STILL_EINVAL. */
+/* Routing metric, flags bits 8..11 (STILL_FLAG_ROUTE(r)): the score that
+ * ranks a chunk's tokens for the delayed Top-lambda. The default is the
+ * Self-Saliency Score; the others are the alternatives of the STILL
+ * article's routing-metric ablation [P3 "Ablation Studies"], each computed
+ * in float64 and summed over the group's query heads where it is per head:
+ *   DIAG      the window softmax's weight on the token itself;
+ *   QK        the scaled self logit scale * q_t . k_t;
+ *   KEYNORM   ||k_t|| (per kv head);
+ *   UNIFORM   1 at the chunk offsets floor(i C / lambda), i < lambda, else
+ *             0 (evenly spaced picks);
+ *   EXTERNAL  the caller's scores: still_prefill's `score` argument becomes
+ *             a required input [B, Hkv, L] float32 (e.g. random draws for
+ *             random routing) and is not written. Prefill only (decode
+ *             returns STILL_EUNSUPPORTED).
+ * Ties rank the lower position first, as for the default score. */
+#define STILL_ROUTE_SALIENCY 0u
+#define STILL_ROUTE_DIAG 1u
+#define STILL_ROUTE_QK 2u
+#define STILL_ROUTE_KEYNORM 3u
+#define STILL_ROUTE_UNIFORM 4u
+#define STILL_ROUTE_EXTERNAL 5u
+#define STILL_FLAG_ROUTE(r) ((uint32_t)(r) << 8)
+#define STILL_ROUTE_OF(flags) (((uint32_t)(flags) >> 8) & 15u)
+/* Any other bit, a routing metric above STILL_ROUTE_EXTERNAL, or
+ * SOFTMAX_ONLY and MERGE_SUM together make every entry that takes the
+ * params return STILL_EINVAL. */
 
 /* status codes */
 #define STILL_OK 0
@@ -152,7 +176,9 @@ int64_t still_workspace_bytes(const still_params* p, int64_t seq_len);
  *   out     [B, Hq, L, d]   outputs,
  *   sel_idx int32 [B, Hkv, n_dec, lambda], n_dec = (L-1)/C: positions kept
  *           from each decided chunk, ascending, -1 where the budget was full,
- *   score   float32 [B, Hkv, L] or NULL: scores (float32 evaluation),
+ *   score   float32 [B, Hkv, L] or NULL: scores (float32 evaluation; the
+ *           routing metric's scores rounded once from float64 for the
+ *           alternative metrics; an input for STILL_ROUTE_EXTERNAL),
  *   state   still_state_bytes(p) bytes: the decode state after token L-1.
  * q, k, v, fmap_w ([Hkv, d, d], phi uses x @ fmap_w[k]) and gate are read
  * only. workspace: ws_bytes >= still_workspace_bytes(p, seq_len), device

@@ -28,8 +28,10 @@ int derive(const still_params* p, Derived* d) {
   if (!p) return STILL_EINVAL;
   if (p->abi_version != STILL_ABI_VERSION) return STILL_EINVAL;
   if (p->dtype != STILL_DTYPE_F32 && p->dtype != STILL_DTYPE_BF16) return STILL_EINVAL;
-  if (p->flags & ~(STILL_FLAG_FP32_OUT | STILL_FLAG_SOFTMAX_ONLY | STILL_FLAG_MERGE_SUM))
+  if (p->flags & ~(STILL_FLAG_FP32_OUT | STILL_FLAG_SOFTMAX_ONLY | STILL_FLAG_MERGE_SUM |
+                   STILL_FLAG_ROUTE(15u)))
     return STILL_EINVAL;  // unknown flag bits
+  if (STILL_ROUTE_OF(p->flags) > STILL_ROUTE_EXTERNAL) return STILL_EINVAL;
   if ((p->flags & STILL_FLAG_SOFTMAX_ONLY) && (p->flags & STILL_FLAG_MERGE_SUM))
     return STILL_EINVAL;  // two merges at once
   if (p->batch < 1 || p->n_q_heads < 1 || p->n_kv_heads < 1) return STILL_EINVAL;
@@ -91,6 +93,11 @@ void layout(const Derived& d, still_state_layout* s) {
   s->ring_slots = d.R;
   s->pool_slots = d.P;
 }
+
+static_assert(still::ROUTE_SALIENCY == STILL_ROUTE_SALIENCY && still::ROUTE_DIAG == STILL_ROUTE_DIAG &&
+                  still::ROUTE_QK == STILL_ROUTE_QK && still::ROUTE_KEYNORM == STILL_ROUTE_KEYNORM &&
+                  still::ROUTE_UNIFORM == STILL_ROUTE_UNIFORM && still::ROUTE_EXTERNAL == STILL_ROUTE_EXTERNAL,
+              "routing metric numbers of the ABI and the kernels agree");
 
 // Prefill launch geometry.
 struct Plan {
@@ -236,7 +243,10 @@ int launch_prefill(const Derived& d, const Plan& pl, still::PrefillArgs a, hipSt
   mk.at(0, 0);
   mk.at(0, 1);
   mk.at(1, 0);
-  score_kernel<T, D><<<dim3(pl.T + D * D / 2048, d.Hkv, d.B), dim3(256), lds_score, s>>>(a);
+  if (a.route == ROUTE_SALIENCY)
+    score_kernel<T, D><<<dim3(pl.T + D * D / 2048, d.Hkv, d.B), dim3(256), lds_score, s>>>(a);
+  else
+    route_kernel<T, D><<<dim3(pl.T + D * D / 2048, d.Hkv, d.B), dim3(256), 4 * D * 8, s>>>(a);
   mk.at(1, 1);
   mk.at(2, 0);
   select_kernel<T, D><<<dim3(pl.n_pend + pl.n_dec, d.Hkv, d.B), dim3(256), lds_sel, s>>>(a);
@@ -392,6 +402,7 @@ static int prefill_impl(const still_params* p, int64_t seq_len, const void* q, c
   if (!q || !k || !v || !fmap_w || !gate || !out || !state || !workspace) return STILL_EINVAL;
   const int n_dec = (int)((seq_len - 1) / d.C);
   if (!sel_idx && n_dec > 0 && d.lam > 0) return STILL_EINVAL;
+  if (STILL_ROUTE_OF(p->flags) == STILL_ROUTE_EXTERNAL && !score) return STILL_EINVAL;
   if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(fmap_w) || misaligned(out) ||
       misaligned(state) || misaligned(workspace) || misaligned(gate))
     return STILL_EINVAL;
@@ -415,6 +426,11 @@ static int prefill_impl(const still_params* p, int64_t seq_len, const void* q, c
   a.gate = gate;
   a.out = out;
   a.sel = sel_idx;
+  a.route = (int)STILL_ROUTE_OF(p->flags);
+  if (a.route == still::ROUTE_EXTERNAL) {  // the caller's scores are an input here
+    a.ext_score = score;
+    score = nullptr;
+  }
   a.score = score ? score : reinterpret_cast<float*>(ws + pl.ws_score);
   a.score_out = score ? 1 : 0;
   a.delta = reinterpret_cast<float*>(ws + pl.ws_delta);
@@ -518,6 +534,8 @@ int still_decode_step(const still_params* p, int64_t pos, const void* q, const v
   int rc = derive(p, &d);
   if (rc != STILL_OK) return rc;
   if (p->flags & STILL_FLAG_MERGE_SUM) return STILL_EUNSUPPORTED;  // decode keeps one normaliser
+  // the caller's scores are a prefill input only
+  if (STILL_ROUTE_OF(p->flags) == STILL_ROUTE_EXTERNAL) return STILL_EUNSUPPORTED;
   if (pos < 1 || pos > ((int64_t)1 << 30)) return STILL_EINVAL;
   if (!q || !k || !v || !fmap_w || !gate || !state || !out) return STILL_EINVAL;
   if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(fmap_w) || misaligned(out) ||
@@ -547,6 +565,7 @@ int still_decode_step(const still_params* p, int64_t pos, const void* q, const v
   a.t = (int)pos;
   a.boundary = (pos % d.C) == 0 ? 1 : 0;
   a.softmax_only = (p->flags & STILL_FLAG_SOFTMAX_ONLY) ? 1 : 0;
+  a.route = (int)STILL_ROUTE_OF(p->flags);
   a.fp32_out = (p->flags & STILL_FLAG_FP32_OUT) ? 1 : 0;
   a.scale = d.scale;
   a.eps = d.eps;

@@ -459,6 +459,34 @@ __device__ __forceinline__ double wave_max_d(double x) {
   x = mx(x, xor16d(x));
   return mx(x, xor32d(x));
 }
+
+
+// Routing metric: the score that ranks a chunk's tokens. The Self-Saliency
+// Score, or an alternative of the STILL article's routing-metric ablation
+// ("Ablation Studies"): the diagonal attention weight, the scaled self
+// logit q.k, the key norm, evenly spaced offsets (uniform), or scores the
+// caller supplies (random routing draws them outside the layer).
+enum { ROUTE_SALIENCY = 0, ROUTE_DIAG, ROUTE_QK, ROUTE_KEYNORM, ROUTE_UNIFORM, ROUTE_EXTERNAL };
+
+// Uniform routing: is offset r of a chunk of C one of floor(i C / lam),
+// i < lam? The only candidate is i = ceil(r lam / C) (lam <= C: the range
+// [r lam / C, (r + 1) lam / C) holds at most one integer).
+__device__ __forceinline__ int uniform_mark(int r, int C, int lam) {
+  if (lam <= 0) return 0;
+  const int i = (r * lam + C - 1) / C;
+  return (i < lam && (i * C) / lam == r) ? 1 : 0;
+}
+
+// Float64 dot product of two rows of D elements by one wave (products of
+// bf16 / float32 values are exact in float64); every lane gets the sum.
+template <typename T, int D>
+__device__ __forceinline__ double row_dot_f64(const T* x, const T* y) {
+  const int lane = threadIdx.x & 63;
+  double s = 0.0;
+#pragma unroll
+  for (int i = lane; i < D; i += 64) s = fma((double)to_f32(x[i]), (double)to_f32(y[i]), s);
+  return wave_sum_d(s);
+}
 // Sum / max over N consecutive aligned lanes (N = 1, 2, 4, 8, 16), every
 // lane of the group receiving the result.
 // Maximum without the quieting of signalling NaN inputs that fmaxf costs

@@ -45,6 +45,7 @@ struct DecodeArgs {
   int32_t* sel_new;  // [B][Hkv][lam] or null
   int B, Hq, Hkv, G, W, C, m, lam, R, t, boundary, fp32_out;
   int softmax_only;  // the linear branch dropped (every gate taken as 0)
+  int route;         // routing metric (ROUTE_*; not ROUTE_EXTERNAL)
   float scale, eps;
   double scale64, eps64;  // the same parameters for the float64 score
   long st_unit, st_S, st_z, st_pool_k, st_pool_v, st_pool_pos, st_ring_k, st_ring_v,
@@ -835,11 +836,27 @@ void decode_kernel(DecodeArgs a) {
       }
       za = wave_sum_d(za);
       zo = wave_sum_d(zo);
+      // the routing metric (metrics of the kv head counted on head 0 only)
+      double kn = 0.0;
+      if (a.route == ROUTE_KEYNORM && h == 0) {  // wave-uniform
+        const T* kt = reinterpret_cast<const T*>(a.k) + (size_t)unit * D;
+        kn = sqrt(row_dot_f64<T, D>(kt, kt));
+      }
       if (lane == 0) {
         const double p = exp(x[n - 1] - mx) / za, pn = zo / za;
         double sc = 0.0;
-        if (p > 0.0) sc += p * log(p / a.eps64);
-        if (pn > 0.0) sc += pn * log(pn / (1.0 - a.eps64));
+        if (a.route == ROUTE_DIAG) {
+          sc = p;
+        } else if (a.route == ROUTE_QK) {
+          sc = x[n - 1];
+        } else if (a.route == ROUTE_KEYNORM) {
+          sc = kn;
+        } else if (a.route == ROUTE_UNIFORM) {
+          sc = h == 0 ? (double)uniform_mark(t - cC, C, a.lam) : 0.0;
+        } else {
+          if (p > 0.0) sc += p * log(p / a.eps64);
+          if (pn > 0.0) sc += pn * log(pn / (1.0 - a.eps64));
+        }
         d64[128 + h] = sc;
       }
     }

@@ -52,6 +52,8 @@ struct PrefillArgs {
   float* y_la;    // [B][Hq][L][D] linear-branch output (no gate), or null
   float* lse_la;  // [B][Hq][L] natural log of sum <phi(q), phi(k)>, or null
   int* rlist;     // [B][Hkv][T][C + 1] tokens whose exported score is refined
+  int route;      // routing metric (ROUTE_*)
+  const float* ext_score;  // [B][Hkv][L] the caller's scores (ROUTE_EXTERNAL)
   float scale, eps;
   double scale64, eps64;  // the same parameters for the float64 paths
   long st_unit, st_S, st_z, st_pool_k, st_pool_v, st_pool_pos, st_ring_k, st_ring_v,
@@ -318,8 +320,11 @@ __global__ __launch_bounds__(256) void score_kernel(PrefillArgs a) {
 // dot products (products of bf16 / float32 values are exact in float64);
 // the softmax sums run online over the 64-key slots and the two-point KL
 // form takes 1-p from the other keys. Every lane returns the head's score.
+// diag: return the window softmax's weight on the token itself instead (the
+// diagonal-attention routing metric).
 template <typename T, int D>
-__device__ double score_f64_head(const PrefillArgs& a, int b, int kv, int h, int t, double* qd) {
+__device__ double score_f64_head(const PrefillArgs& a, int b, int kv, int h, int t, double* qd,
+                                 bool diag = false) {
   const int lane = threadIdx.x & 63;
   const int W = a.W, G = a.G, L = a.L;
   const int n = t - W + 1 > 0 ? W : t + 1;
@@ -383,10 +388,71 @@ __device__ double score_f64_head(const PrefillArgs& a, int b, int kv, int h, int
     m = mn;
   }
   const double p = zt / za, pn = zo / za;
+  if (diag) return p;
   double sc = 0.0;
   if (p > 0.0) sc += p * log(p / a.eps64);
   if (pn > 0.0) sc += pn * log(pn / (1.0 - a.eps64));
   return sc;
+}
+
+// Float64 routing score of head h for token t by one wave (every lane gets
+// it): the Self-Saliency Score or the metric a.route names. Metrics of the
+// kv head (key norm, uniform, the caller's) are returned for h = 0 and 0
+// for the other heads, so a sum over the group's heads is the metric.
+template <typename T, int D>
+__device__ double route_f64_head(const PrefillArgs& a, int b, int kv, int h, int t, double* qd) {
+  const int unit = b * a.Hkv + kv;
+  const T* krow = reinterpret_cast<const T*>(a.k) + ((size_t)unit * a.L + t) * D;
+  switch (a.route) {  // uniform
+    case ROUTE_DIAG:
+      return score_f64_head<T, D>(a, b, kv, h, t, qd, true);
+    case ROUTE_QK: {
+      const T* qrow = reinterpret_cast<const T*>(a.q) + ((size_t)(b * a.Hq + kv * a.G + h) * a.L + t) * D;
+      return a.scale64 * row_dot_f64<T, D>(qrow, krow);
+    }
+    case ROUTE_KEYNORM:
+      return h == 0 ? sqrt(row_dot_f64<T, D>(krow, krow)) : 0.0;
+    case ROUTE_UNIFORM:
+      return h == 0 ? (double)uniform_mark(t % a.C, a.C, a.lam) : 0.0;
+    case ROUTE_EXTERNAL:
+      return h == 0 ? (double)a.ext_score[(size_t)unit * a.L + t] : 0.0;
+    default:
+      return score_f64_head<T, D>(a, b, kv, h, t, qd);
+  }
+}
+
+// Routing scores other than the Self-Saliency Score, in place of the score
+// kernel (same grid, the same extra F^T workgroups): one workgroup of 4
+// waves per (chunk, kv head, batch row), one token per wave at a time, the
+// group's heads summed in head order in float64 and rounded once. The bound
+// written beside the float32 score covers that rounding (the select
+// kernel's float64 ranking of near ties recomputes the same values); no
+// exported score needs refining.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void route_kernel(PrefillArgs a) {
+  extern __shared__ __align__(16) char smem[];
+  if ((int)blockIdx.x >= a.T) {  // the extra workgroups: F^T (batch row 0's)
+    if (blockIdx.z == 0) fmap_transpose_part<T, D>(a, (int)blockIdx.x - a.T, (int)blockIdx.y);
+    return;
+  }
+  const int c = blockIdx.x, kv = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  double* qd = reinterpret_cast<double*>(smem) + wave * D;  // this wave's float64 query row
+  const int unit = b * a.Hkv + kv;
+  for (int i = wave; i < a.C; i += 4) {  // wave-uniform
+    const int t = c * a.C + i;
+    if (t >= a.L) break;
+    double s = 0.0;
+    for (int h = 0; h < a.G; ++h) s += route_f64_head<T, D>(a, b, kv, h, t, qd);
+    if (lane == 0) {
+      const float s32 = (float)s;
+      const size_t o = (size_t)unit * a.L + t;
+      a.score[o] = s32;
+      // |float32 - float64| plus the float64 evaluation error (far below)
+      a.delta[o] = (float)(fabs((double)s32 - s) + fabs(s) * 0x1p-40) * (1.f + 0x1p-20f);
+    }
+  }
+  if (tid == 0) a.rlist[((size_t)unit * a.T + c) * (a.C + 1)] = 0;
 }
 
 // Float64 scores of a list of tokens by a 4-wave workgroup: the (token,
@@ -399,7 +465,7 @@ __device__ void score_f64_list(const PrefillArgs& a, int b, int kv, const int* t
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, G = a.G;
   for (int pi = wave; pi < n_tok * G; pi += 4) {  // wave-uniform
     const int i = pi / G, h = pi % G, t = tok_t[i];
-    const double s = score_f64_head<T, D>(a, b, kv, h, t, qd + wave * D);
+    const double s = route_f64_head<T, D>(a, b, kv, h, t, qd + wave * D);
     if (lane == 0) res[pi] = s;
   }
   __syncthreads();

@@ -129,6 +129,17 @@ def make_inputs(wl: Workload, device="cpu", seq_len: Optional[int] = None,
             "fmap_w": fmap_w.contiguous(), "gate": gate.contiguous()}
 
 
+def make_route_scores(wl: Workload, device="cpu", seq_len: Optional[int] = None,
+                      seed: Optional[int] = None) -> torch.Tensor:
+    """Per-token routing scores [B,Hkv,L] float32, U(0, 1): the draws of
+    random routing, handed to the layer as caller-supplied scores."""
+    L = wl.seq_len if seq_len is None else seq_len
+    gen = torch.Generator(device=device)
+    gen.manual_seed((wl.seed if seed is None else seed) + 7919)
+    return torch.rand((wl.batch, wl.n_kv_heads, L), generator=gen, device=device,
+                      dtype=torch.float32)
+
+
 def make_decode_tokens(wl: Workload, n_steps: int, device="cpu",
                        seed: Optional[int] = None) -> Dict[str, torch.Tensor]:
     """New tokens for n_steps decode steps: q [S,B,Hq,d], k/v [S,B,Hkv,d].

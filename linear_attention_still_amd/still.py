@@ -23,6 +23,13 @@ STILL_DTYPE_BF16 = 1
 STILL_FLAG_FP32_OUT = 1
 STILL_FLAG_SOFTMAX_ONLY = 2
 STILL_FLAG_MERGE_SUM = 4
+# routing metrics (flags bits 8..11)
+ROUTES = {"saliency": 0, "diag": 1, "qk": 2, "keynorm": 3, "uniform": 4, "external": 5}
+
+
+def route_flag(route: str) -> int:
+    """The flags bits that select a routing metric (see ROUTES)."""
+    return ROUTES[route] << 8
 STILL_OK, STILL_EINVAL, STILL_EUNSUPPORTED, STILL_EWORKSPACE, STILL_EHIP, STILL_ESTATE, \
     STILL_ESCRATCH = 0, -1, -2, -3, -4, -5, -6
 

@@ -27,16 +27,19 @@ def n_threads() -> int:
 
 
 def gpu_prefill(wl: Workload, x: Dict[str, torch.Tensor], fp32_out: bool = False,
-                keep_device: bool = False, flags: int = 0,
-                partials: bool = False) -> Dict[str, torch.Tensor]:
+                keep_device: bool = False, flags: int = 0, partials: bool = False,
+                ext_score: Optional[torch.Tensor] = None) -> Dict[str, torch.Tensor]:
     """still_prefill (or still_prefill_partials) on the GPU; flags are the
-    branch-variant flags."""
+    variant flags; ext_score: the caller's routing scores (external route),
+    passed in the score buffer."""
     p = still.params_for(wl, fp32_out=fp32_out, flags=flags)
     xd = {k: v.cuda() for k, v in x.items()}
     L = xd["q"].shape[2]
     print("  gpu prefill %s L=%d fp32_out=%s flags=%d partials=%s"
           % (wl.name, L, fp32_out, flags, partials), flush=True)
     bufs = still.PrefillBuffers(p, L)
+    if ext_score is not None:
+        bufs.score.copy_(ext_score)
     out = {}
     if partials:
         B, Hq, d = wl.batch, wl.n_q_heads, wl.head_dim
@@ -61,12 +64,14 @@ def gpu_prefill(wl: Workload, x: Dict[str, torch.Tensor], fp32_out: bool = False
 
 
 def oracle(wl: Workload, x: Dict[str, torch.Tensor], units=None, merge: str = "one",
-           partials: bool = False) -> Dict[str, np.ndarray]:
-    print("  oracle %s units=%s threads=%d merge=%s" % (
-        wl.name, "all" if units is None else len(units), n_threads(), merge), flush=True)
+           partials: bool = False, route: str = "saliency",
+           ext_score=None) -> Dict[str, np.ndarray]:
+    print("  oracle %s units=%s threads=%d merge=%s route=%s" % (
+        wl.name, "all" if units is None else len(units), n_threads(), merge, route), flush=True)
     return rec.prefill(x["q"], x["k"], x["v"], x["fmap_w"], x["gate"], window=wl.window,
                        chunk=wl.chunk, budget=wl.budget, t_max=wl.t_max, units=units,
-                       n_threads=n_threads(), merge=merge, partials=partials)
+                       n_threads=n_threads(), merge=merge, partials=partials, route=route,
+                       ext_score=ext_score)
 
 
 def bf16_half_ulp(ref: np.ndarray) -> np.ndarray:

@@ -159,3 +159,25 @@ def test_branch_flags_validated_before_any_hip_call():
     p = still.params_for(WORKLOADS["decode_bf16_B64_ctx16K"], flags=still.STILL_FLAG_MERGE_SUM)
     rc = L.still_decode_step(ctypes.byref(p), 16384, *([fake] * 9), 0, None)
     assert rc == still.STILL_EUNSUPPORTED
+
+
+def test_routing_flags_validated_before_any_hip_call():
+    """Routing metrics above the last one are rejected; the caller's scores
+    (external routing) are a required prefill input and are refused by the
+    decode step."""
+    L = still.lib()
+    fake = ctypes.c_void_p(1 << 20)
+    wl = WORKLOADS["small_f32_L256"]
+    for r in range(6):
+        p = still.params_for(wl, flags=still.route_flag(list(still.ROUTES)[r]))
+        assert L.still_lambda(ctypes.byref(p)) >= 0
+    p = still.params_for(wl, flags=6 << 8)
+    assert L.still_lambda(ctypes.byref(p)) == still.STILL_EINVAL
+    p = still.params_for(wl, flags=still.route_flag("external"))
+    ws = still.still_workspace_bytes(p, 256)
+    args = [fake] * 10
+    args[7] = None  # no score buffer
+    assert L.still_prefill(ctypes.byref(p), 256, *args, ws, None) == still.STILL_EINVAL
+    p = still.params_for(WORKLOADS["decode_bf16_B64_ctx16K"], flags=still.route_flag("external"))
+    rc = L.still_decode_step(ctypes.byref(p), 16384, *([fake] * 9), 0, None)
+    assert rc == still.STILL_EUNSUPPORTED

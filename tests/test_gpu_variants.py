@@ -1,5 +1,5 @@
-"""Parity of the branch variants and the branch partials with the oracle,
-on the GPU (through the C ABI).
+"""Parity of the branch variants, the branch partials and the routing
+metrics with the oracle, on the GPU (through the C ABI).
 
 The variants are the ablation axes the pages discuss: the softmax branch
 alone (unkept tokens dropped, the sparse-attention-only alternative of the
@@ -14,13 +14,19 @@ selections, scores and state; the branch outputs (float32) within the
 dtype's float32-output bar; the log-normalisers within the dtype's max-abs
 bar (1e-4 float32, 2e-2 bfloat16: a relative bar on the normaliser), with
 -inf exactly where the linear key set is empty.
+
+The routing metrics are the alternatives of the STILL article's routing
+ablation ("Ablation Studies"): diagonal attention weight, q.k, key norm,
+uniform picks, and caller-supplied scores (random routing's draws, seeded
+U(0, 1)); selections bit-exact, scores within the score bar.
 """
 import numpy as np
 import pytest
 import torch
 
 from linear_attention_still_amd import still
-from linear_attention_still_amd.inputs import WORKLOADS, Workload, make_decode_tokens, make_inputs
+from linear_attention_still_amd.inputs import (WORKLOADS, Workload, make_decode_tokens, make_inputs,
+                                               make_route_scores)
 from oracle import rec
 from tests import _parity as P
 
@@ -160,3 +166,66 @@ def test_decode_softmax_only(case):
     P.check_state(sv["S"].cpu().numpy(), o["S"], wl.dtype, "decode S")
     P.check_state(sv["z"].cpu().numpy(), o["z"], wl.dtype, "decode z")
 
+
+
+ROUTES = ["diag", "qk", "keynorm", "uniform", "external"]
+ROUTE_SHAPES = [SHAPES[0], SHAPES[1], SHAPES[2], SHAPES[5], SHAPES[6]]
+
+
+@pytest.mark.parametrize("route", ROUTES)
+@pytest.mark.parametrize("wl", ROUTE_SHAPES, ids=[w.name for w in ROUTE_SHAPES])
+def test_prefill_routing_metrics(wl, route):
+    x = make_inputs(wl)
+    ext = make_route_scores(wl) if route == "external" else None
+    o = P.oracle(wl, x, route=route, ext_score=ext)
+    g = P.gpu_prefill(wl, x, fp32_out=(wl.dtype == "bf16"), flags=still.route_flag(route),
+                      ext_score=ext)
+    P.compare_prefill(wl, g, o, out_fp32=(wl.dtype == "bf16"))
+    if ext is not None:  # an input: not written
+        assert torch.equal(g["score"], ext)
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("route", ROUTES)
+def test_llama8b_L16K_routing_sampled_units(route):
+    wl = WORKLOADS["llama8b_bf16_L16K"]
+    x = make_inputs(wl)
+    ext = make_route_scores(wl) if route == "external" else None
+    units = [(0, 1), (0, 6)]
+    o = P.oracle(wl, x, units=units, route=route, ext_score=ext)
+    g = P.gpu_prefill(wl, x, fp32_out=True, flags=still.route_flag(route), ext_score=ext)
+    P.compare_prefill(wl, g, o, units=units, out_fp32=True)
+
+
+@pytest.mark.parametrize("route", ["diag", "qk", "keynorm", "uniform"])
+@pytest.mark.parametrize("case", DECODE_SHAPES[:2], ids=[c[0].name for c in DECODE_SHAPES[:2]])
+def test_decode_routing_metrics(case, route):
+    """Prefill and decode under an alternative routing metric; the oracle
+    runs the same metric over all L0 + n tokens."""
+    wl, L0, n = case
+    x = make_inputs(wl, seq_len=L0)
+    toks = make_decode_tokens(wl, n)
+    flags = still.route_flag(route)
+    g = P.gpu_prefill(wl, x, keep_device=True, flags=flags)
+    p = still.params_for(wl, fp32_out=True, flags=flags)
+    xd = {k: v.cuda() for k, v in x.items()}
+    td = {k: v.cuda() for k, v in toks.items()}
+    outs, sels = P.run_decode(wl, g["_state"], p, xd, td, L0, fp32_out=True)
+    units = [(b, kv) for b in range(wl.batch) for kv in range(wl.n_kv_heads)]
+    qs, ks, vs, Fs, gs = P.concat_units(x, toks, wl, units)
+    o = rec.run_units(qs, ks, vs, Fs, gs, window=wl.window, chunk=wl.chunk, budget=wl.budget,
+                      t_max=wl.t_max, n_threads=P.n_threads(), route=route)
+    G = wl.group
+    yg = np.stack([outs[:, b, kv * G:(kv + 1) * G].numpy().transpose(1, 0, 2) for b, kv in units])
+    P.check_outputs(yg, o["y"][:, :, L0:], wl.dtype, True, "decode y")
+    for s in range(n):
+        t = L0 + s
+        if t % wl.chunk == 0 and o["lam"] > 0:
+            got = np.stack([sels[s, b, kv].numpy() for b, kv in units])
+            assert np.array_equal(got, o["sel"][:, t // wl.chunk - 1]), s
+    sv = still.state_views(p, g["_state"])
+    P.check_state(sv["S"].cpu().numpy(), o["S"], wl.dtype, "decode S")
+    pend = sv["pending"].cpu().numpy()
+    assert np.array_equal(np.isnan(pend), np.isnan(o["pending"]))
+    ok = ~np.isnan(pend)
+    assert np.allclose(pend[ok], o["pending"][ok], rtol=1e-12, atol=1e-12)
