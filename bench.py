@@ -9,7 +9,8 @@ W = C = 64, budget m = 512). Inputs are resident in HBM before the timed
 region. The same JSON line reports the other workloads (the batch-2 4K GQA
 prefill, the 64K prefill with its per-token time against the 16K one, and
 the latency of the small float32 workload), measured ceilings of the chip
-(a device copy and a large bf16 GEMM), the decode leg (batch 64 at 16K
+(a device copy and a large bf16 GEMM), a chunk-size sweep of the 16K
+workload (C = 16 .. 128, all else unchanged), the decode leg (batch 64 at 16K
 context, 64 steps including one chunk-boundary decision) and the float64
 oracle's CPU baseline (all usable cores, and one thread).
 
@@ -97,7 +98,7 @@ def run_prefill_bench(torch, still, inputs, name, steps, warmup, breakdown=True)
     """Times `steps` prefills of workload `name` (inputs resident in HBM),
     with HIP events around the attention kernel only; then, if breakdown,
     a second set of steps with events around every kernel."""
-    wl = inputs.WORKLOADS[name]
+    wl = inputs.WORKLOADS[name] if isinstance(name, str) else name
     p = still.params_for(wl)
     x = inputs.make_inputs(wl, device="cuda")
     bufs = still.PrefillBuffers(p, wl.seq_len)
@@ -370,6 +371,18 @@ def main():
         others["small_f32_L256"] = run_latency_bench(torch, still, inputs, "small_f32_L256")
         res["workloads"] = others
         res["ceilings"] = measured_ceilings(torch)
+        # chunk-size sweep of the 16K workload (window, budget, T_max and
+        # inputs unchanged; lambda = min(C, (m - W) / T_max))
+        sweep = {}
+        for C, wc in inputs.chunk_sweep().items():
+            _, xs, bs, r, _ = run_prefill_bench(torch, still, inputs, wc, args.steps, 5)
+            sweep[str(C)] = {"ms_per_step": r["ms_per_step"], "tokens_per_s": r["tokens_per_s"],
+                             "lambda": still.still_lambda(still.params_for(wc)),
+                             "attend_mfma_frac": r["attend_mfma_frac"],
+                             "kernels_ms": r["kernels_ms"]}
+            del xs, bs
+            torch.cuda.empty_cache()
+        res["chunk_sweep"] = sweep
     if not args.no_decode:
         res["decode"] = run_decode_bench(torch, still, inputs, args.decode_steps)
     if not args.no_cpu_baseline:

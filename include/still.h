@@ -253,6 +253,42 @@ int still_decode_step(const still_params* p, int64_t pos, const void* q, const v
                       void* out, int32_t* sel_new, void* workspace, size_t ws_bytes,
                       void* stream);
 
+/* Ragged batches [P3 "Delayed Chunk-Level Selection ..."]: prefill and
+ * decode keep one routing and memory-update rule per sequence, so each row
+ * of a batch may be at its own length.
+ *
+ * still_prefill_varlen: rows of their own lengths seq_lens[b] >= 1 (host
+ * array of p->batch entries). Every array is packed row after row: row b
+ * starts after the tokens of rows 0 .. b-1 and is laid out as for a batch
+ * of one ([H][L_b][d] for q, k, v and out; [Hkv][n_dec_b][lambda] for
+ * sel_idx, n_dec_b = (L_b - 1) / C; [Hkv][L_b] for score). state is the
+ * batch's state (still_state_bytes(p)); row b's units are b * Hkv .. b * Hkv
+ * + Hkv - 1. workspace: ws_bytes >= still_workspace_bytes_varlen(p,
+ * seq_lens). The rows run one after another on the stream (each one a
+ * whole prefill). Same flags, results and errors as still_prefill; all
+ * arguments are checked before the first row runs. */
+int64_t still_workspace_bytes_varlen(const still_params* p, const int64_t* seq_lens);
+int still_prefill_varlen(const still_params* p, const int64_t* seq_lens, const void* q,
+                         const void* k, const void* v, const void* fmap_w, const float* gate,
+                         void* out, int32_t* sel_idx, float* score, void* state, void* workspace,
+                         size_t ws_bytes, void* stream);
+
+/* n_tokens decode steps in one call (multi-token decode), each row at its
+ * own position if asked. Token s of every row is q[s], k[s], v[s] ([n_tokens]
+ * [B][H][d]) and writes out[s] ([n_tokens][B][Hq][d]) and, if sel_new is
+ * not NULL, sel_new[s] ([n_tokens][B][Hkv][lambda], as for
+ * still_decode_step). Positions: row_pos NULL: every row's token s is at pos
+ * + s (pos >= 1, checked on the host); else row_pos is a device array of B
+ * int32 and row b's token s is at row_pos[b] + s (pos is ignored). Positions
+ * are checked against each unit's state on the device: a unit whose
+ * position does not follow its state gets the error word (meta[2] =
+ * STILL_ESTATE) and is skipped from then on; other rows go on. Steps run in
+ * order on the stream. */
+int still_decode_tokens(const still_params* p, int64_t pos, const int32_t* row_pos, int n_tokens,
+                        const void* q, const void* k, const void* v, const void* fmap_w,
+                        const float* gate, void* state, void* out, int32_t* sel_new,
+                        void* stream);
+
 /* Human-readable text of a status code (static storage). */
 const char* still_status_str(int status);
 

@@ -289,7 +289,7 @@ int launch_decode_g(const Derived& d, still::DecodeArgs a, hipStream_t s) {
 template <typename T, int D>
 int launch_decode(const Derived& d, still::DecodeArgs a, hipStream_t s) {
   using namespace still;
-  if (a.boundary) {
+  if (a.boundary || a.pos) {  // per-row positions: every row's workgroups look
     const size_t lds = DecLds<T, D, 1>::uni + DecLds<T, D, 1>::fold_bytes;
     decode_boundary_kernel<T, D><<<dim3(d.Hkv, d.B), dim3(BND_THREADS), lds, s>>>(a);
     if (hipGetLastError() != hipSuccess) return STILL_EHIP;
@@ -507,6 +507,67 @@ int still_prefill_partials(const still_params* p, int64_t seq_len, const void* q
                       ws_bytes, stream, nullptr, 0, Partials{y_sa, lse_sa, y_la, lse_la});
 }
 
+// Varlen prefill: the rows are prefilled one after another on the stream,
+// each as a batch of one over its own length (row b's arrays start after
+// the rows before it; its state units are b * Hkv .. b * Hkv + Hkv - 1 of
+// the batch's state), sharing one workspace.
+int64_t still_workspace_bytes_varlen(const still_params* p, const int64_t* seq_lens) {
+  Derived d;
+  const int rc = derive(p, &d);
+  if (rc != STILL_OK) return rc;
+  if (!seq_lens) return STILL_EINVAL;
+  still_params p1 = *p;
+  p1.batch = 1;
+  Derived d1;
+  derive(&p1, &d1);
+  int64_t ws = 0;
+  for (int b = 0; b < d.B; ++b) {
+    if (seq_lens[b] < 1 || seq_lens[b] > ((int64_t)1 << 30)) return STILL_EINVAL;
+    const int64_t w = ws_bytes_any(d1, seq_lens[b]);
+    ws = w > ws ? w : ws;
+  }
+  return ws;
+}
+
+int still_prefill_varlen(const still_params* p, const int64_t* seq_lens, const void* q,
+                         const void* k, const void* v, const void* fmap_w, const float* gate,
+                         void* out, int32_t* sel_idx, float* score, void* state, void* workspace,
+                         size_t ws_bytes, void* stream) {
+  const int64_t need = still_workspace_bytes_varlen(p, seq_lens);
+  if (need < 0) return (int)need;
+  if ((int64_t)ws_bytes < need) return STILL_EWORKSPACE;
+  if (!q || !k || !v || !out || !state) return STILL_EINVAL;
+  Derived d;
+  derive(p, &d);
+  still_params p1 = *p;
+  p1.batch = 1;
+  still_state_layout SL;
+  layout(d, &SL);
+  // checks that could fail on a later row are made before the first runs
+  for (int b = 0; b < d.B; ++b) {
+    if (seq_lens[b] * d.D * (int64_t)d.esz >= ((int64_t)1 << 31)) return STILL_EUNSUPPORTED;
+    if (!sel_idx && d.lam > 0 && seq_lens[b] > d.C) return STILL_EINVAL;
+  }
+  const size_t osz = (p->flags & STILL_FLAG_FP32_OUT) ? 4 : d.esz;
+  int64_t tok = 0, dec = 0;  // tokens and decided chunks of the rows before b
+  for (int b = 0; b < d.B; ++b) {
+    const int64_t L = seq_lens[b], n_dec = (L - 1) / d.C;
+    const int rc = prefill_impl(
+        &p1, L, reinterpret_cast<const char*>(q) + (size_t)tok * d.Hq * d.D * d.esz,
+        reinterpret_cast<const char*>(k) + (size_t)tok * d.Hkv * d.D * d.esz,
+        reinterpret_cast<const char*>(v) + (size_t)tok * d.Hkv * d.D * d.esz, fmap_w, gate,
+        reinterpret_cast<char*>(out) + (size_t)tok * d.Hq * d.D * osz,
+        sel_idx ? sel_idx + (size_t)dec * d.Hkv * d.lam : nullptr,
+        score ? score + (size_t)tok * d.Hkv : nullptr,
+        reinterpret_cast<char*>(state) + (size_t)b * d.Hkv * SL.unit_bytes, workspace, ws_bytes,
+        stream, nullptr, 0);
+    if (rc != STILL_OK) return rc;
+    tok += L;
+    dec += n_dec;
+  }
+  return STILL_OK;
+}
+
 int still_prefill_noalloc(const still_params* p, int64_t seq_len, const void* q, const void* k,
                           const void* v, const void* fmap_w, const float* gate, void* out,
                           int32_t* sel_idx, float* score, void* state, void* stream) {
@@ -524,35 +585,31 @@ int still_prefill_noalloc(const still_params* p, int64_t seq_len, const void* q,
 
 int64_t still_noalloc_scratch_bytes(void) { return (int64_t)kNoAllocScratchBytes; }
 
-int still_decode_step(const still_params* p, int64_t pos, const void* q, const void* k,
-                      const void* v, const void* fmap_w, const float* gate, void* state,
-                      void* out, int32_t* sel_new, void* workspace, size_t ws_bytes,
-                      void* stream) {
-  (void)workspace;
-  (void)ws_bytes;
+// n_tokens decode steps: step s takes token s of q, k, v ([n][B][H][d])
+// and writes out[s], sel_new[s]; row b's position is pos + s, or
+// row_pos[b] + s with per-row positions (device array).
+static int decode_impl(const still_params* p, int64_t pos, const int32_t* row_pos, int n_tokens,
+                       const void* q, const void* k, const void* v, const void* fmap_w,
+                       const float* gate, void* state, void* out, int32_t* sel_new, void* stream) {
   Derived d;
   int rc = derive(p, &d);
   if (rc != STILL_OK) return rc;
   if (p->flags & STILL_FLAG_MERGE_SUM) return STILL_EUNSUPPORTED;  // decode keeps one normaliser
   // the caller's scores are a prefill input only
   if (STILL_ROUTE_OF(p->flags) == STILL_ROUTE_EXTERNAL) return STILL_EUNSUPPORTED;
-  if (pos < 1 || pos > ((int64_t)1 << 30)) return STILL_EINVAL;
+  if (n_tokens < 1 || n_tokens > (1 << 20)) return STILL_EINVAL;
+  if (!row_pos && (pos < 1 || pos + n_tokens - 1 > ((int64_t)1 << 30))) return STILL_EINVAL;
   if (!q || !k || !v || !fmap_w || !gate || !state || !out) return STILL_EINVAL;
   if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(fmap_w) || misaligned(out) ||
-      misaligned(state) || misaligned(gate))
+      misaligned(state) || misaligned(gate) || ((uintptr_t)row_pos & 3u))
     return STILL_EINVAL;
   still_state_layout SL;
   layout(d, &SL);
   still::DecodeArgs a;
   memset(&a, 0, sizeof(a));
-  a.q = q;
-  a.k = k;
-  a.v = v;
   a.fmap_w = fmap_w;
   a.gate = gate;
   a.state = reinterpret_cast<char*>(state);
-  a.out = out;
-  a.sel_new = sel_new;
   a.B = d.B;
   a.Hq = d.Hq;
   a.Hkv = d.Hkv;
@@ -562,8 +619,7 @@ int still_decode_step(const still_params* p, int64_t pos, const void* q, const v
   a.m = d.m;
   a.lam = d.lam;
   a.R = d.R;
-  a.t = (int)pos;
-  a.boundary = (pos % d.C) == 0 ? 1 : 0;
+  a.pos = row_pos;
   a.softmax_only = (p->flags & STILL_FLAG_SOFTMAX_ONLY) ? 1 : 0;
   a.route = (int)STILL_ROUTE_OF(p->flags);
   a.fp32_out = (p->flags & STILL_FLAG_FP32_OUT) ? 1 : 0;
@@ -574,12 +630,42 @@ int still_decode_step(const still_params* p, int64_t pos, const void* q, const v
   fill_state_offsets(SL, &a.st_unit, &a.st_S, &a.st_z, &a.st_pool_k, &a.st_pool_v,
                      &a.st_pool_pos, &a.st_ring_k, &a.st_ring_v, &a.st_ring_phi,
                      &a.st_ring_flag, &a.st_pending, &a.st_meta);
+  const size_t qb = (size_t)d.B * d.Hq * d.D * d.esz, kb = (size_t)d.B * d.Hkv * d.D * d.esz;
+  const size_t ob = (size_t)d.B * d.Hq * d.D * (a.fp32_out ? 4 : d.esz);
+  const size_t sb = (size_t)d.B * d.Hkv * d.lam;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  if (p->dtype == STILL_DTYPE_BF16) {
-    if (d.D == 128) return launch_decode<bf16, 128>(d, a, s);
-    return launch_decode<bf16, 64>(d, a, s);
+  for (int i = 0; i < n_tokens; ++i) {
+    a.q = reinterpret_cast<const char*>(q) + i * qb;
+    a.k = reinterpret_cast<const char*>(k) + i * kb;
+    a.v = reinterpret_cast<const char*>(v) + i * kb;
+    a.out = reinterpret_cast<char*>(out) + i * ob;
+    a.sel_new = sel_new ? sel_new + i * sb : nullptr;
+    a.t = row_pos ? i : (int)(pos + i);
+    a.boundary = !row_pos && ((pos + i) % d.C) == 0 ? 1 : 0;
+    if (p->dtype == STILL_DTYPE_BF16)
+      rc = d.D == 128 ? launch_decode<bf16, 128>(d, a, s) : launch_decode<bf16, 64>(d, a, s);
+    else
+      rc = launch_decode<float, 64>(d, a, s);
+    if (rc != STILL_OK) return rc;
   }
-  return launch_decode<float, 64>(d, a, s);
+  return STILL_OK;
+}
+
+int still_decode_step(const still_params* p, int64_t pos, const void* q, const void* k,
+                      const void* v, const void* fmap_w, const float* gate, void* state,
+                      void* out, int32_t* sel_new, void* workspace, size_t ws_bytes,
+                      void* stream) {
+  (void)workspace;
+  (void)ws_bytes;
+  return decode_impl(p, pos, nullptr, 1, q, k, v, fmap_w, gate, state, out, sel_new, stream);
+}
+
+int still_decode_tokens(const still_params* p, int64_t pos, const int32_t* row_pos, int n_tokens,
+                        const void* q, const void* k, const void* v, const void* fmap_w,
+                        const float* gate, void* state, void* out, int32_t* sel_new,
+                        void* stream) {
+  return decode_impl(p, pos, row_pos, n_tokens, q, k, v, fmap_w, gate, state, out, sel_new,
+                     stream);
 }
 
 const char* still_status_str(int status) {

@@ -44,6 +44,10 @@ struct DecodeArgs {
   void* out;         // [B][Hq][D]
   int32_t* sel_new;  // [B][Hkv][lam] or null
   int B, Hq, Hkv, G, W, C, m, lam, R, t, boundary, fp32_out;
+  // per-row positions: row b's token is at pos[b] + t (device [B]), or null
+  // (every row at t); with them the boundary kernel runs for every row and
+  // returns where pos[b] + t is not a chunk start
+  const int32_t* pos;
   int softmax_only;  // the linear branch dropped (every gate taken as 0)
   int route;         // routing metric (ROUTE_*; not ROUTE_EXTERNAL)
   float scale, eps;
@@ -249,7 +253,8 @@ __global__ __launch_bounds__(BND_THREADS) void decode_boundary_kernel(DecodeArgs
   extern __shared__ __align__(16) char smem[];
   const int kv = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
   const int unit = b * a.Hkv + kv;
-  const int W = a.W, C = a.C, R = a.R, t = a.t;
+  const int W = a.W, C = a.C, R = a.R, t = a.pos ? a.pos[b] + a.t : a.t;
+  if (a.pos && (t < 1 || t % C != 0)) return;  // this row is not at a chunk start
   char* st = a.state + (size_t)unit * a.st_unit;
   int64_t* meta = reinterpret_cast<int64_t*>(st + a.st_meta);
   float* S = reinterpret_cast<float*>(st + a.st_S);
@@ -376,7 +381,8 @@ void decode_kernel(DecodeArgs a) {
   const int kv = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;  // wave index in an SGPR
   const int unit = b * a.Hkv + kv;
-  const int W = a.W, C = a.C, R = a.R, t = a.t;
+  const int W = a.W, C = a.C, R = a.R, t = a.pos ? a.pos[b] + a.t : a.t;
+  const bool boundary = t % C == 0;  // row b's token starts a chunk
   char* st = a.state + (size_t)unit * a.st_unit;
   int64_t* meta = reinterpret_cast<int64_t*>(st + a.st_meta);
   float* S = reinterpret_cast<float*>(st + a.st_S);
@@ -491,7 +497,7 @@ void decode_kernel(DecodeArgs a) {
   }
   int n_pool = (int)__builtin_amdgcn_readfirstlane(mv[2]);
 
-  if (a.sel_new && !a.boundary)
+  if (a.sel_new && !boundary)
     for (int i = tid; i < a.lam; i += DEC_THREADS) a.sel_new[(size_t)unit * a.lam + i] = -1;
 
   const int part = lane % LPK, grp = lane / LPK;

@@ -129,6 +129,13 @@ def make_inputs(wl: Workload, device="cpu", seq_len: Optional[int] = None,
             "fmap_w": fmap_w.contiguous(), "gate": gate.contiguous()}
 
 
+def chunk_sweep(base: str = "llama8b_bf16_L16K", chunks=(16, 32, 64, 128)) -> Dict[int, Workload]:
+    """The base workload at other chunk sizes C, everything else (window,
+    budget, T_max, inputs) unchanged: the chunk-size ablation's axis."""
+    wl = WORKLOADS[base]
+    return {C: dataclasses.replace(wl, name="%s_C%d" % (base, C), chunk=C) for C in chunks}
+
+
 def make_route_scores(wl: Workload, device="cpu", seq_len: Optional[int] = None,
                       seed: Optional[int] = None) -> torch.Tensor:
     """Per-token routing scores [B,Hkv,L] float32, U(0, 1): the draws of

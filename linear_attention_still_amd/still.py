@@ -88,6 +88,12 @@ def lib() -> ctypes.CDLL:
         L.still_noalloc_scratch_bytes.argtypes = []
         L.still_noalloc_scratch_bytes.restype = I64
         L.still_decode_step.argtypes = [pp, I64] + [P] * 9 + [ctypes.c_size_t, P]
+        L.still_decode_tokens.argtypes = [pp, I64, P, I32] + [P] * 9
+        L.still_decode_tokens.restype = I32
+        L.still_workspace_bytes_varlen.argtypes = [pp, P]
+        L.still_workspace_bytes_varlen.restype = I64
+        L.still_prefill_varlen.argtypes = [pp, P] + [P] * 10 + [ctypes.c_size_t, P]
+        L.still_prefill_varlen.restype = I32
         L.still_decode_step.restype = I32
         L.still_status_str.argtypes = [I32]
         L.still_status_str.restype = ctypes.c_char_p
@@ -231,6 +237,47 @@ def still_decode_step(p: still_params, pos: int, q, k, v, fmap_w, gate, state, o
 
 
 # ---- allocation helpers (torch memory only) --------------------------------
+
+def _lens(seq_lens):
+    a = (ctypes.c_int64 * len(seq_lens))(*[int(x) for x in seq_lens])
+    return a
+
+
+def still_workspace_bytes_varlen(p: still_params, seq_lens) -> int:
+    if len(seq_lens) != p.batch:
+        raise ValueError("one length per batch row")
+    n = int(lib().still_workspace_bytes_varlen(ctypes.byref(p), _lens(seq_lens)))
+    if n < 0:
+        raise StillError("still_workspace_bytes_varlen", n)
+    return n
+
+
+def still_prefill_varlen(p: still_params, seq_lens, q, k, v, fmap_w, gate, out, sel_idx, score,
+                         state, workspace, stream=None) -> None:
+    """Rows of their own lengths; q, k, v, out, sel_idx and score packed row
+    after row (see include/still.h)."""
+    if len(seq_lens) != p.batch:
+        raise ValueError("one length per batch row")
+    rc = lib().still_prefill_varlen(ctypes.byref(p), _lens(seq_lens), _ptr(q), _ptr(k), _ptr(v),
+                                    _ptr(fmap_w), _ptr(gate), _ptr(out), _ptr(sel_idx),
+                                    _ptr(score), _ptr(state), _ptr(workspace),
+                                    workspace.numel() * workspace.element_size(),
+                                    _stream(stream))
+    if rc != STILL_OK:
+        raise StillError("still_prefill_varlen", rc)
+
+
+def still_decode_tokens(p: still_params, pos: int, row_pos, q, k, v, fmap_w, gate, state, out,
+                        sel_new=None, stream=None) -> None:
+    """len(q) decode steps; row_pos: None (every row at pos + s) or a device
+    int32 tensor [B] of per-row positions of the first token."""
+    n = q.shape[0]
+    rc = lib().still_decode_tokens(ctypes.byref(p), int(pos), _ptr(row_pos), int(n), _ptr(q),
+                                   _ptr(k), _ptr(v), _ptr(fmap_w), _ptr(gate), _ptr(state),
+                                   _ptr(out), _ptr(sel_new), _stream(stream))
+    if rc != STILL_OK:
+        raise StillError("still_decode_tokens", rc)
+
 
 class PrefillBuffers:
     """Device buffers of one prefill: outputs, kept indices, scores, state,

@@ -181,3 +181,35 @@ def test_routing_flags_validated_before_any_hip_call():
     p = still.params_for(WORKLOADS["decode_bf16_B64_ctx16K"], flags=still.route_flag("external"))
     rc = L.still_decode_step(ctypes.byref(p), 16384, *([fake] * 9), 0, None)
     assert rc == still.STILL_EUNSUPPORTED
+
+
+def test_ragged_entries_validate_before_any_hip_call():
+    """Varlen prefill checks every row's length (and the kept-index buffer a
+    later row would need) before the first row runs; multi-token decode
+    checks its token count and host position."""
+    L = still.lib()
+    fake = ctypes.c_void_p(1 << 20)
+    wl = WORKLOADS["small_f32_L256"]
+    p = still.make_params(dtype="bf16", batch=3, n_q_heads=8, n_kv_heads=2, head_dim=128,
+                          window=64, chunk=64, budget=64 + 48, t_max=16)
+    lens = [300, 1, 777]
+    ws = still.still_workspace_bytes_varlen(p, lens)
+    p1 = still.make_params(dtype="bf16", batch=1, n_q_heads=8, n_kv_heads=2, head_dim=128,
+                           window=64, chunk=64, budget=64 + 48, t_max=16)
+    assert ws == still.still_workspace_bytes(p1, 777)
+    for bad in ([300, 0, 777], [300, -5, 1]):
+        assert L.still_workspace_bytes_varlen(ctypes.byref(p), still._lens(bad)) == still.STILL_EINVAL
+        assert L.still_prefill_varlen(ctypes.byref(p), still._lens(bad), *([fake] * 10), ws,
+                                      None) == still.STILL_EINVAL
+    assert L.still_prefill_varlen(ctypes.byref(p), still._lens(lens), *([fake] * 10), ws - 1,
+                                  None) == still.STILL_EWORKSPACE
+    args = [fake] * 10
+    args[6] = None  # no kept-index buffer: row 0 already decides chunks
+    assert L.still_prefill_varlen(ctypes.byref(p), still._lens(lens), *args, ws,
+                                  None) == still.STILL_EINVAL
+    p = still.params_for(WORKLOADS["decode_bf16_B64_ctx16K"])
+    f8 = [fake] * 8  # q, k, v, fmap_w, gate, state, out, sel_new (then the stream)
+    assert L.still_decode_tokens(ctypes.byref(p), 16384, None, 0, *f8, None) == still.STILL_EINVAL
+    assert L.still_decode_tokens(ctypes.byref(p), 0, None, 4, *f8, None) == still.STILL_EINVAL
+    odd = ctypes.c_void_p((1 << 20) + 2)
+    assert L.still_decode_tokens(ctypes.byref(p), 0, odd, 4, *f8, None) == still.STILL_EINVAL

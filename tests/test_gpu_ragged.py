@@ -1,0 +1,197 @@
+"""Ragged batches on the GPU (through the C ABI): rows of their own lengths
+in one prefill call, decode with a position per row, several tokens per
+decode call. Each row is checked against the oracle run on that row alone
+(the pages' rule is per sequence: [P3 "Delayed Chunk-Level Selection for
+Unified Training-Inference Parallelism"]), to the bars of the default path.
+
+Inputs: each row draws its own q, k, v (seeded per row, the workload's
+distribution); the layer's weights (F, gate) are shared by the rows.
+"""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+from linear_attention_still_amd import still
+from linear_attention_still_amd.inputs import Workload, make_decode_tokens, make_inputs
+from oracle import rec
+from tests import _parity as P
+
+pytestmark = pytest.mark.gpu
+
+
+def small(name, dtype, B, Hq, Hkv, d, W, C, m, t_max, out=0.01, seed=29):
+    return Workload(name, dtype, B, Hq, Hkv, d, 0, W, C, m, t_max, sigma=0.5,
+                    outlier_frac=out, seed=seed)
+
+
+def row_inputs(wl, lens):
+    """Per-row inputs (batch of one each) and the shared weights."""
+    one = dataclasses.replace(wl, batch=1)
+    rows = [make_inputs(one, seq_len=L, seed=wl.seed + 101 * b) for b, L in enumerate(lens)]
+    for r in rows[1:]:
+        r["fmap_w"], r["gate"] = rows[0]["fmap_w"], rows[0]["gate"]
+    return rows
+
+
+def pack(rows, key):
+    return torch.cat([r[key][0].reshape(-1) for r in rows]).cuda()
+
+
+def run_varlen(wl, rows, lens, fp32_out=False, flags=0):
+    p = still.params_for(wl, fp32_out=fp32_out, flags=flags)
+    lam = still.still_lambda(p)
+    tot = sum(lens)
+    n_dec = sum((L - 1) // wl.chunk for L in lens)
+    odt = torch.float32 if (fp32_out or wl.dtype == "f32") else torch.bfloat16
+    out = torch.empty(tot * wl.n_q_heads * wl.head_dim, dtype=odt, device="cuda")
+    sel = torch.empty(max(1, n_dec * wl.n_kv_heads * lam), dtype=torch.int32, device="cuda")
+    score = torch.empty(tot * wl.n_kv_heads, dtype=torch.float32, device="cuda")
+    state = torch.zeros(still.still_state_bytes(p), dtype=torch.uint8, device="cuda")
+    ws = torch.empty(still.still_workspace_bytes_varlen(p, lens), dtype=torch.uint8, device="cuda")
+    print("  gpu varlen prefill %s lens=%s" % (wl.name, lens), flush=True)
+    still.still_prefill_varlen(p, lens, pack(rows, "q"), pack(rows, "k"), pack(rows, "v"),
+                               rows[0]["fmap_w"].cuda(), rows[0]["gate"].cuda(), out, sel, score,
+                               state, ws)
+    torch.cuda.synchronize()
+    return p, out, sel, score, state
+
+
+def row_views(wl, p, lens, out, sel, score, state, b):
+    """Row b's results in the batch-of-one layout compare_prefill reads."""
+    lam = still.still_lambda(p)
+    tok = sum(lens[:b])
+    dec = sum((L - 1) // wl.chunk for L in lens[:b])
+    L, H, Hkv, d = lens[b], wl.n_q_heads, wl.n_kv_heads, wl.head_dim
+    n_dec = (L - 1) // wl.chunk
+    g = {"y": out[tok * H * d:(tok + L) * H * d].view(1, H, L, d).cpu(),
+         "sel": sel[dec * Hkv * lam:(dec + n_dec) * Hkv * lam].view(1, Hkv, n_dec, lam).cpu(),
+         "score": score[tok * Hkv:(tok + L) * Hkv].view(1, Hkv, L).cpu()}
+    sv = still.state_views(p, state)
+    for k, v in sv.items():
+        g[k] = v[b * Hkv:(b + 1) * Hkv].cpu()
+    return g
+
+
+CASES = [
+    (small("rag_bf16_d128", "bf16", 4, 8, 2, 128, 64, 64, 64 + 16 * 3, 16), [300, 1, 777, 64]),
+    (small("rag_f32_d64", "f32", 2, 4, 2, 64, 16, 32, 16 + 4 * 6, 6, out=0.0), [90, 200]),
+    (small("rag_bf16_C16", "bf16", 3, 4, 1, 64, 8, 16, 8 + 19 * 2, 19), [33, 250, 17]),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0].name for c in CASES])
+def test_varlen_prefill_rows_match_oracle(case):
+    wl, lens = case
+    rows = row_inputs(wl, lens)
+    p, out, sel, score, state = run_varlen(wl, rows, lens, fp32_out=(wl.dtype == "bf16"))
+    for b, L in enumerate(lens):
+        wr = dataclasses.replace(wl, batch=1, seq_len=L)
+        o = P.oracle(wr, rows[b])
+        g = row_views(wl, p, lens, out, sel, score, state, b)
+        P.compare_prefill(wr, g, o, out_fp32=(wl.dtype == "bf16"))
+
+
+DEC_CASES = [
+    (small("ragdec_bf16_d128", "bf16", 3, 8, 2, 128, 64, 64, 64 + 8 * 2, 8), [256, 300, 129], 140),
+    (small("ragdec_f32", "f32", 2, 2, 1, 64, 16, 32, 16 + 4 * 6, 6, out=0.0), [90, 33], 70),
+]
+
+
+@pytest.mark.parametrize("case", DEC_CASES, ids=[c[0].name for c in DEC_CASES])
+def test_ragged_multi_token_decode_matches_oracle(case):
+    """Varlen prefill, then every row decodes n tokens from its own position
+    in one call (chunk boundaries fall at different steps per row)."""
+    wl, lens, n = case
+    rows = row_inputs(wl, lens)
+    p, _, _, _, state = run_varlen(wl, rows, lens)
+    pd = still.params_for(wl, fp32_out=True)
+    toks = make_decode_tokens(dataclasses.replace(wl, batch=len(lens)), n)
+    lam = still.still_lambda(pd)
+    out = torch.empty((n, len(lens), wl.n_q_heads, wl.head_dim), dtype=torch.float32, device="cuda")
+    sel = torch.empty((n, len(lens), wl.n_kv_heads, max(lam, 1)), dtype=torch.int32, device="cuda")
+    row_pos = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    print("  gpu ragged decode %s n=%d" % (wl.name, n), flush=True)
+    still.still_decode_tokens(pd, 0, row_pos, toks["q"].cuda(), toks["k"].cuda(), toks["v"].cuda(),
+                              rows[0]["fmap_w"].cuda(), rows[0]["gate"].cuda(), state, out,
+                              sel if lam > 0 else None)
+    torch.cuda.synchronize()
+    out, sel = out.cpu(), sel.cpu()
+    sv = still.state_views(pd, state)
+    G, Hkv = wl.group, wl.n_kv_heads
+    for b, L0 in enumerate(lens):
+        units = range(Hkv)
+        qs = np.stack([torch.cat([rows[b]["q"][0, kv * G:(kv + 1) * G].float(),
+                                  toks["q"][:, b, kv * G:(kv + 1) * G].float().permute(1, 0, 2)],
+                                 dim=1).numpy() for kv in units])
+        ks = np.stack([torch.cat([rows[b]["k"][0, kv].float(), toks["k"][:, b, kv].float()]).numpy()
+                       for kv in units])
+        vs = np.stack([torch.cat([rows[b]["v"][0, kv].float(), toks["v"][:, b, kv].float()]).numpy()
+                       for kv in units])
+        Fs = np.stack([rows[0]["fmap_w"][kv].float().numpy() for kv in units])
+        gs = np.stack([rows[0]["gate"][kv * G:(kv + 1) * G].float().numpy() for kv in units])
+        o = rec.run_units(qs, ks, vs, Fs, gs, window=wl.window, chunk=wl.chunk, budget=wl.budget,
+                          t_max=wl.t_max, n_threads=P.n_threads())
+        yg = np.stack([out[:, b, kv * G:(kv + 1) * G].numpy().transpose(1, 0, 2) for kv in units])
+        P.check_outputs(yg, o["y"][:, :, L0:], wl.dtype, True, "row %d decode y" % b)
+        for s in range(n):
+            t = L0 + s
+            if t % wl.chunk == 0 and lam > 0:
+                assert np.array_equal(sel[s, b, :, :lam].numpy(), o["sel"][:, t // wl.chunk - 1]), (b, s)
+            elif lam > 0:
+                assert np.all(sel[s, b, :, :lam].numpy() == -1), (b, s)
+        idx = slice(b * Hkv, (b + 1) * Hkv)
+        P.check_state(sv["S"][idx].cpu().numpy(), o["S"], wl.dtype, "row %d S" % b)
+        P.check_state(sv["z"][idx].cpu().numpy(), o["z"], wl.dtype, "row %d z" % b)
+        meta = sv["meta"][idx].cpu().numpy()
+        assert np.all(meta[:, 0] == L0 + n) and np.all(meta[:, 2] == 0)
+        assert np.array_equal(meta[:, 1], o["n_pool"])
+
+
+def test_multi_token_decode_equals_single_steps():
+    """still_decode_tokens over n tokens at a uniform position gives the
+    bits of n still_decode_step calls."""
+    wl = small("mt_bf16", "bf16", 2, 8, 2, 128, 64, 64, 64 + 8 * 2, 8)
+    wl = dataclasses.replace(wl, seq_len=200)
+    x = make_inputs(wl, device="cuda")
+    n = 70
+    toks = {k: v.cuda() for k, v in make_decode_tokens(wl, n).items()}
+    p = still.params_for(wl)
+    outs = []
+    for mode in ("steps", "tokens"):
+        bufs = still.PrefillBuffers(p, 200)
+        still.run_prefill(p, x, bufs)
+        out = torch.empty((n, 2, 8, 128), dtype=torch.bfloat16, device="cuda")
+        if mode == "steps":
+            for s in range(n):
+                still.still_decode_step(p, 200 + s, toks["q"][s], toks["k"][s], toks["v"][s],
+                                        x["fmap_w"], x["gate"], bufs.state, out[s])
+        else:
+            still.still_decode_tokens(p, 200, None, toks["q"], toks["k"], toks["v"], x["fmap_w"],
+                                      x["gate"], bufs.state, out)
+        torch.cuda.synchronize()
+        outs.append((out.cpu(), bufs.state.cpu()))
+    assert torch.equal(outs[0][0], outs[1][0])
+    assert torch.equal(outs[0][1], outs[1][1])
+
+
+def test_ragged_decode_wrong_row_position_sets_only_its_error_word():
+    wl = small("rag_err", "bf16", 2, 4, 1, 64, 16, 32, 16 + 3 * 10, 10)
+    lens = [100, 70]
+    rows = row_inputs(wl, lens)
+    p, _, _, _, state = run_varlen(wl, rows, lens)
+    before = state.clone()
+    toks = make_decode_tokens(dataclasses.replace(wl, batch=2), 1)
+    out = torch.empty((1, 2, 4, 64), dtype=torch.bfloat16, device="cuda")
+    row_pos = torch.tensor([100, 75], dtype=torch.int32, device="cuda")  # row 1 is at 70
+    still.still_decode_tokens(p, 0, row_pos, toks["q"].cuda(), toks["k"].cuda(), toks["v"].cuda(),
+                              rows[0]["fmap_w"].cuda(), rows[0]["gate"].cuda(), state, out)
+    torch.cuda.synchronize()
+    sv, sb = still.state_views(p, state), still.state_views(p, before)
+    meta = sv["meta"].cpu().numpy()
+    assert meta[0, 0] == 101 and meta[0, 2] == 0
+    assert meta[1, 0] == 70 and meta[1, 2] == still.STILL_ESTATE
+    lay = still.still_state_layout_get(p)
+    u = lay.unit_bytes  # row 1's unit: every byte before its meta words is unchanged
+    assert torch.equal(state[u:u + lay.meta].cpu(), before[u:u + lay.meta].cpu())
