@@ -282,14 +282,18 @@ __device__ __forceinline__ void split2_frag<bf16>(const f32x4& x0, const f32x4& 
     lo.v[i] = (bf16)(x - (float)a);
   }
 }
+// fp16: the high part is x cut to 11 significant bits by clearing the low
+// 13 mantissa bits (exact in fp16 over its normal range), the low part the
+// exact remainder rounded to fp16 (~22 significant bits together); one
+// mask, one subtraction and two packed conversions per pair of values.
 template <>
 __device__ __forceinline__ void split2_frag<f16>(const f32x4& x0, const f32x4& x1,
                                                  Frag<f16>& hi, Frag<f16>& lo) {
   for (int i = 0; i < 8; ++i) {
     const float x = i < 4 ? x0[i] : x1[i - 4];
-    const f16 a = (f16)x;
-    hi.v[i] = a;
-    lo.v[i] = (f16)(x - (float)a);
+    const float h = __uint_as_float(__float_as_uint(x) & 0xFFFFE000u);
+    hi.v[i] = (f16)h;
+    lo.v[i] = (f16)(x - h);
   }
 }
 template <>
