@@ -289,6 +289,27 @@ int still_decode_tokens(const still_params* p, int64_t pos, const int32_t* row_p
                         const float* gate, void* state, void* out, int32_t* sel_new,
                         void* stream);
 
+/* Backward of one layer [P3 "Delayed Chunk-Level Selection for Unified
+ * Training-Inference Parallelism": training runs the same chunk-parallel
+ * form]: gradients of sum(y * dy) with respect to q, k, v, fmap_w and gate,
+ * the routing held fixed (reading: which tokens are kept carries no
+ * gradient; sel_idx is the forward's selection). Inputs: the forward's
+ * inputs, its sel_idx, its float32 output y [B, Hq, L, d] (STILL_FLAG_
+ * FP32_OUT), its branch log-normalisers lse_sa, lse_la [B, Hq, L] (from
+ * still_prefill_partials) and dy [B, Hq, L, d] float32. Outputs (float32,
+ * overwritten): dq [B, Hq, L, d], dk, dv [B, Hkv, L, d], dfmap [Hkv, d, d],
+ * dgate [Hq]. Default merge only (the branch-variant flags return
+ * STILL_EUNSUPPORTED). workspace: ws_bytes >= still_backward_workspace_bytes
+ * (p, seq_len), 16-byte aligned. Dense form: every (query, key) pair on or
+ * below the diagonal is visited, so the cost grows as L^2. Accuracy: float32
+ * arithmetic on top of the forward's y and normalisers. */
+int64_t still_backward_workspace_bytes(const still_params* p, int64_t seq_len);
+int still_backward(const still_params* p, int64_t seq_len, const void* q, const void* k, const void* v,
+                   const void* fmap_w, const float* gate, const int32_t* sel_idx, const float* y,
+                   const float* lse_sa, const float* lse_la, const float* dy, float* dq, float* dk,
+                   float* dv, float* dfmap, float* dgate, void* workspace, size_t ws_bytes,
+                   void* stream);
+
 /* Human-readable text of a status code (static storage). */
 const char* still_status_str(int status);
 

@@ -5,11 +5,13 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <algorithm>
 #include <mutex>
 
 #include "still.h"
 #include "still_decode.hip"
 #include "still_prefill.hip"
+#include "still_backward.hip"
 
 namespace {
 
@@ -216,6 +218,24 @@ constexpr int decode_family() {
   return 4 + ((sizeof(T) == 4 ? 0 : 1) * 2 + (D == 128 ? 1 : 0)) * 4 + (G == 1 ? 0 : G == 2 ? 1 : G == 4 ? 2 : 3);
 }
 
+template <typename T, int D>
+void set_backward_attrs() {
+  const int family = 20 + prefill_family<T, D>();
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) dev = 0;
+  std::lock_guard<std::mutex> lk(g_attr_mu);
+  if (g_attr_done[dev] & (1ull << family)) return;
+  (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&still::bw_phi_kernel<T, D>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, still::BwRowLds<D>::bytes);
+  (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&still::bw_npmap_kernel<T, D>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, still::BwRowLds<D>::bytes);
+  (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&still::bw_query_kernel<T, D>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, still::BwQLds<D>::bytes);
+  (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&still::bw_key_kernel<T, D>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, still::BwKLds<D>::bytes);
+  g_attr_done[dev] |= 1ull << family;
+}
+
 // Optional per-kernel events (still_prefill_timed).
 struct Marks {
   void* const* ev;
@@ -345,6 +365,53 @@ int scratch_address(void** out) {
 }
 
 }  // namespace
+
+// ---------------------------------------------------------------- backward
+struct BwPlan {
+  int64_t phq, phk, dphq, dphk, dz, lnN, delta, kept, total;
+};
+
+static BwPlan bw_plan(const Derived& d, int64_t L) {
+  BwPlan w;
+  int64_t o = 0;
+  auto take = [&](int64_t bytes) {
+    const int64_t at = o;
+    o = align_up(o + bytes);
+    return at;
+  };
+  const int64_t nq = (int64_t)d.B * d.Hq * L, nk = (int64_t)d.B * d.Hkv * L;
+  w.phq = take(nq * d.D * 4);
+  w.phk = take(nk * d.D * 4);
+  w.dphq = take(nq * d.D * 4);
+  w.dphk = take(nk * d.D * 4);
+  w.dz = take((nq + nk) * d.D * 4);
+  w.lnN = take(nq * 4);
+  w.delta = take(nq * 4);
+  w.kept = take(nk);
+  w.total = o;
+  return w;
+}
+
+template <typename T, int D>
+static int launch_backward(const Derived& d, const BwPlan& w, still::BackwardArgs a, hipStream_t s) {
+  using namespace still;
+  set_backward_attrs<T, D>();
+  const int L = a.L;
+  bw_zero_kernel<<<dim3(1), dim3(BW_THREADS), 0, s>>>(a.dgate, d.Hq);
+  bw_zero_kernel<<<dim3(64), dim3(BW_THREADS), 0, s>>>(a.dfmap, (int64_t)d.Hkv * D * D);
+  const int64_t nk = (int64_t)d.B * d.Hkv * L;
+  bw_flags_kernel<<<dim3((unsigned)std::min<int64_t>((nk + BW_THREADS - 1) / BW_THREADS, 4096)),
+                    dim3(BW_THREADS), 0, s>>>(a);
+  const dim3 rows_grid((L + BW_ROWS - 1) / BW_ROWS, d.B * (d.Hq + d.Hkv));
+  bw_phi_kernel<T, D><<<rows_grid, dim3(BW_THREADS), BwRowLds<D>::bytes, s>>>(a);
+  bw_query_kernel<T, D><<<dim3((L + BW_QT - 1) / BW_QT, d.Hq, d.B), dim3(BW_THREADS), BwQLds<D>::bytes, s>>>(a);
+  bw_key_kernel<T, D><<<dim3((L + BW_KT - 1) / BW_KT, d.Hkv, d.B), dim3(BW_THREADS), BwKLds<D>::bytes, s>>>(a);
+  bw_npmap_kernel<T, D><<<rows_grid, dim3(BW_THREADS), BwRowLds<D>::bytes, s>>>(a);
+  const int64_t nrow = (int64_t)d.B * (d.G + 1) * L;
+  bw_dfmap_kernel<T, D><<<dim3((unsigned)((nrow + BW_DF_ROWS - 1) / BW_DF_ROWS), d.Hkv), dim3(BW_THREADS), 0, s>>>(a);
+  (void)w;
+  return hipGetLastError() == hipSuccess ? STILL_OK : STILL_EHIP;
+}
 
 extern "C" {
 
@@ -666,6 +733,79 @@ int still_decode_tokens(const still_params* p, int64_t pos, const int32_t* row_p
                         void* stream) {
   return decode_impl(p, pos, row_pos, n_tokens, q, k, v, fmap_w, gate, state, out, sel_new,
                      stream);
+}
+
+int64_t still_backward_workspace_bytes(const still_params* p, int64_t seq_len) {
+  Derived d;
+  const int rc = derive(p, &d);
+  if (rc != STILL_OK) return rc;
+  if (seq_len < 1 || seq_len > ((int64_t)1 << 24)) return STILL_EINVAL;
+  return bw_plan(d, seq_len).total;
+}
+
+int still_backward(const still_params* p, int64_t seq_len, const void* q, const void* k, const void* v,
+                   const void* fmap_w, const float* gate, const int32_t* sel_idx, const float* y,
+                   const float* lse_sa, const float* lse_la, const float* dy, float* dq, float* dk,
+                   float* dv, float* dfmap, float* dgate, void* workspace, size_t ws_bytes,
+                   void* stream) {
+  Derived d;
+  const int rc = derive(p, &d);
+  if (rc != STILL_OK) return rc;
+  // the gradients are those of the default merge (one normaliser)
+  if (p->flags & (STILL_FLAG_SOFTMAX_ONLY | STILL_FLAG_MERGE_SUM)) return STILL_EUNSUPPORTED;
+  if (seq_len < 1 || seq_len > ((int64_t)1 << 24)) return STILL_EINVAL;
+  if ((int64_t)d.B * (d.Hq + d.Hkv) > 65535) return STILL_EUNSUPPORTED;  // grid rows
+  const int n_dec = (int)((seq_len - 1) / d.C);
+  if (!q || !k || !v || !fmap_w || !gate || !y || !lse_sa || !lse_la || !dy || !dq || !dk || !dv ||
+      !dfmap || !dgate || !workspace)
+    return STILL_EINVAL;
+  if (!sel_idx && n_dec > 0 && d.lam > 0) return STILL_EINVAL;
+  if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(fmap_w) || misaligned(y) ||
+      misaligned(dy) || misaligned(dq) || misaligned(dk) || misaligned(dv) || misaligned(dfmap) ||
+      misaligned(workspace))
+    return STILL_EINVAL;
+  const BwPlan w = bw_plan(d, seq_len);
+  if ((int64_t)ws_bytes < w.total) return STILL_EWORKSPACE;
+  char* ws = reinterpret_cast<char*>(workspace);
+  still::BackwardArgs a;
+  memset(&a, 0, sizeof(a));
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.fmap_w = fmap_w;
+  a.gate = gate;
+  a.sel = sel_idx;
+  a.y = y;
+  a.lse_sa = lse_sa;
+  a.lse_la = lse_la;
+  a.dy = dy;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.dfmap = dfmap;
+  a.dgate = dgate;
+  a.phq = reinterpret_cast<float*>(ws + w.phq);
+  a.phk = reinterpret_cast<float*>(ws + w.phk);
+  a.dphq = reinterpret_cast<float*>(ws + w.dphq);
+  a.dphk = reinterpret_cast<float*>(ws + w.dphk);
+  a.dz = reinterpret_cast<float*>(ws + w.dz);
+  a.lnN = reinterpret_cast<float*>(ws + w.lnN);
+  a.delta = reinterpret_cast<float*>(ws + w.delta);
+  a.kept = reinterpret_cast<uint8_t*>(ws + w.kept);
+  a.B = d.B;
+  a.Hq = d.Hq;
+  a.Hkv = d.Hkv;
+  a.G = d.G;
+  a.L = (int)seq_len;
+  a.W = d.W;
+  a.C = d.C;
+  a.n_dec = d.lam > 0 ? n_dec : 0;
+  a.lam = d.lam;
+  a.scale = d.scale;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (p->dtype == STILL_DTYPE_BF16)
+    return d.D == 128 ? launch_backward<bf16, 128>(d, w, a, s) : launch_backward<bf16, 64>(d, w, a, s);
+  return launch_backward<float, 64>(d, w, a, s);
 }
 
 const char* still_status_str(int status) {

@@ -136,6 +136,16 @@ def chunk_sweep(base: str = "llama8b_bf16_L16K", chunks=(16, 32, 64, 128)) -> Di
     return {C: dataclasses.replace(wl, name="%s_C%d" % (base, C), chunk=C) for C in chunks}
 
 
+def make_grad_output(wl: Workload, device="cpu", seq_len: Optional[int] = None,
+                     seed: Optional[int] = None) -> torch.Tensor:
+    """An upstream gradient dy [B,Hq,L,d] float32, N(0, 1)."""
+    L = wl.seq_len if seq_len is None else seq_len
+    gen = torch.Generator(device=device)
+    gen.manual_seed((wl.seed if seed is None else seed) + 104729)
+    return torch.randn((wl.batch, wl.n_q_heads, L, wl.head_dim), generator=gen, device=device,
+                       dtype=torch.float32)
+
+
 def make_route_scores(wl: Workload, device="cpu", seq_len: Optional[int] = None,
                       seed: Optional[int] = None) -> torch.Tensor:
     """Per-token routing scores [B,Hkv,L] float32, U(0, 1): the draws of

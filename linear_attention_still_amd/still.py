@@ -94,6 +94,10 @@ def lib() -> ctypes.CDLL:
         L.still_workspace_bytes_varlen.restype = I64
         L.still_prefill_varlen.argtypes = [pp, P] + [P] * 10 + [ctypes.c_size_t, P]
         L.still_prefill_varlen.restype = I32
+        L.still_backward_workspace_bytes.argtypes = [pp, I64]
+        L.still_backward_workspace_bytes.restype = I64
+        L.still_backward.argtypes = [pp, I64] + [P] * 15 + [P, ctypes.c_size_t, P]
+        L.still_backward.restype = I32
         L.still_decode_step.restype = I32
         L.still_status_str.argtypes = [I32]
         L.still_status_str.restype = ctypes.c_char_p
@@ -277,6 +281,25 @@ def still_decode_tokens(p: still_params, pos: int, row_pos, q, k, v, fmap_w, gat
                                    _ptr(out), _ptr(sel_new), _stream(stream))
     if rc != STILL_OK:
         raise StillError("still_decode_tokens", rc)
+
+
+def still_backward_workspace_bytes(p: still_params, seq_len: int) -> int:
+    n = int(lib().still_backward_workspace_bytes(ctypes.byref(p), int(seq_len)))
+    if n < 0:
+        raise StillError("still_backward_workspace_bytes", n)
+    return n
+
+
+def still_backward(p: still_params, seq_len: int, q, k, v, fmap_w, gate, sel_idx, y, lse_sa,
+                   lse_la, dy, dq, dk, dv, dfmap, dgate, workspace, stream=None) -> None:
+    """Gradients of sum(y * dy), the routing held fixed (see include/still.h)."""
+    rc = lib().still_backward(ctypes.byref(p), int(seq_len), _ptr(q), _ptr(k), _ptr(v),
+                              _ptr(fmap_w), _ptr(gate), _ptr(sel_idx), _ptr(y), _ptr(lse_sa),
+                              _ptr(lse_la), _ptr(dy), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dfmap),
+                              _ptr(dgate), _ptr(workspace),
+                              workspace.numel() * workspace.element_size(), _stream(stream))
+    if rc != STILL_OK:
+        raise StillError("still_backward", rc)
 
 
 class PrefillBuffers:
