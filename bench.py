@@ -10,7 +10,8 @@ region. The same JSON line reports the other workloads (the batch-2 4K GQA
 prefill, the 64K prefill with its per-token time against the 16K one, and
 the latency of the small float32 workload), measured ceilings of the chip
 (a device copy and a large bf16 GEMM), a chunk-size sweep of the 16K
-workload (C = 16 .. 128, all else unchanged), the decode leg (batch 64 at 16K
+workload (C = 16 .. 128, all else unchanged), the backward on the 4K workload, the
+decode leg (batch 64 at 16K
 context, 64 steps including one chunk-boundary decision) and the float64
 oracle's CPU baseline (all usable cores, and one thread).
 
@@ -159,6 +160,58 @@ def run_prefill_bench(torch, still, inputs, name, steps, warmup, breakdown=True)
     if ms is not None:
         out["kernels_ms"] = ms
     return wl, x, bufs, out, work
+
+
+PEAK_FP32_VECTOR_TFLOPS = 157.3  # MI355X float32 vector
+
+
+def run_backward_bench(torch, still, inputs, name, steps=5):
+    """Time of the backward (gradients of q, k, v, F, gates) after a forward
+    with partials; flops of the dense form it runs: 22 d per (query head,
+    query, key <= query) pair (query side: three dot products and two
+    accumulations; key side: three dot products and three accumulations),
+    8 d^2 per q or k row (features, their recompute, F dz, x^T dz)."""
+    wl = inputs.WORKLOADS[name]
+    p = still.params_for(wl, fp32_out=True)
+    L, B, Hq, Hkv, d = wl.seq_len, wl.batch, wl.n_q_heads, wl.n_kv_heads, wl.head_dim
+    x = inputs.make_inputs(wl, device="cuda")
+    dy = inputs.make_grad_output(wl, device="cuda")
+    bufs = still.PrefillBuffers(p, L)
+    lse_sa = torch.empty((B, Hq, L), device="cuda")
+    lse_la = torch.empty((B, Hq, L), device="cuda")
+    y_sa = torch.empty((B, Hq, L, d), device="cuda")
+    y_la = torch.empty((B, Hq, L, d), device="cuda")
+    still.still_prefill_partials(p, L, x["q"], x["k"], x["v"], x["fmap_w"], x["gate"], bufs.out,
+                                 bufs.sel, bufs.score, bufs.state, bufs.workspace, y_sa, lse_sa,
+                                 y_la, lse_la)
+    del y_sa, y_la
+    g = {"dq": torch.empty((B, Hq, L, d), device="cuda"),
+         "dk": torch.empty((B, Hkv, L, d), device="cuda"),
+         "dv": torch.empty((B, Hkv, L, d), device="cuda"),
+         "dfmap": torch.empty((Hkv, d, d), device="cuda"), "dgate": torch.empty((Hq,), device="cuda")}
+    ws = torch.empty(still.still_backward_workspace_bytes(p, L), dtype=torch.uint8, device="cuda")
+
+    def run():
+        still.still_backward(p, L, x["q"], x["k"], x["v"], x["fmap_w"], x["gate"], bufs.sel,
+                             bufs.out, lse_sa, lse_la, dy, g["dq"], g["dk"], g["dv"], g["dfmap"],
+                             g["dgate"], ws)
+    run()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    pairs = B * Hq * L * (L + 1) / 2
+    flops = pairs * 22 * d + B * (Hq + Hkv) * L * 8 * d * d
+    tf = flops / (ms * 1e-3) / 1e12
+    return {"workload": wl.name, "steps": steps, "ms": ms, "tokens_per_s": B * L / (ms * 1e-3),
+            "form": "dense (every pair on or below the diagonal), float32 vector ALU",
+            "flops_per_launch": flops, "tflops": tf,
+            "roofline": {"bound": "alu", "achieved": tf, "peak": PEAK_FP32_VECTOR_TFLOPS,
+                         "unit": "TFLOP/s", "frac": tf / PEAK_FP32_VECTOR_TFLOPS}}
 
 
 def run_latency_bench(torch, still, inputs, name, reps=50):
@@ -385,6 +438,9 @@ def main():
         res["chunk_sweep"] = sweep
     if not args.no_decode:
         res["decode"] = run_decode_bench(torch, still, inputs, args.decode_steps)
+    if not args.no_workloads:
+        res["backward"] = run_backward_bench(torch, still, inputs, "gqa_bf16_L4K")
+        torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         xc = inputs.make_inputs(wl, device="cuda")
         res["cpu_baseline"] = run_cpu_baseline(wl, xc)
