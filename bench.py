@@ -165,12 +165,30 @@ def run_prefill_bench(torch, still, inputs, name, steps, warmup, breakdown=True)
 PEAK_FP32_VECTOR_TFLOPS = 157.3  # MI355X float32 vector
 
 
+def backward_work(wl, lam, cap_chunks):
+    """Algorithmic flops of still_backward's chunked form: every pair it
+    visits one by one (band pairs, key in [b_c, t], from both sides: 22 d;
+    kept-pool pairs: 10 d from the query side, 8 d from the kept-key pass),
+    the chunk state terms (2 d^2 per head and query, 4 d^2 per kv head and
+    key), the chunk deltas (2 d^2 per key, 2 d^2 per head and query) and the
+    row work (8 d^2 per q or k row: features, their recompute, F dz, x^T dz)."""
+    L, C, W, d = wl.seq_len, wl.chunk, wl.window, wl.head_dim
+    band = pool = 0
+    for c in range((L + C - 1) // C):
+        x = c * C - W + 1
+        cf = x // C if x >= 0 else 0
+        t1 = min(L, c * C + C)
+        n = t1 - c * C
+        band += sum(t - cf * C + 1 for t in range(c * C, t1))
+        pool += n * min(cf, cap_chunks) * lam
+    B, Hq, Hkv = wl.batch, wl.n_q_heads, wl.n_kv_heads
+    return (B * Hq * (band * 22 * d + pool * 18 * d) + B * Hq * L * 4 * d * d
+            + B * Hkv * L * 6 * d * d + B * (Hq + Hkv) * L * 8 * d * d)
+
+
 def run_backward_bench(torch, still, inputs, name, steps=5):
     """Time of the backward (gradients of q, k, v, F, gates) after a forward
-    with partials; flops of the dense form it runs: 22 d per (query head,
-    query, key <= query) pair (query side: three dot products and two
-    accumulations; key side: three dot products and three accumulations),
-    8 d^2 per q or k row (features, their recompute, F dz, x^T dz)."""
+    with partials, against the float32 vector peak (see backward_work)."""
     wl = inputs.WORKLOADS[name]
     p = still.params_for(wl, fp32_out=True)
     L, B, Hq, Hkv, d = wl.seq_len, wl.batch, wl.n_q_heads, wl.n_kv_heads, wl.head_dim
@@ -204,11 +222,13 @@ def run_backward_bench(torch, still, inputs, name, steps=5):
     e1.record()
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / steps
-    pairs = B * Hq * L * (L + 1) / 2
-    flops = pairs * 22 * d + B * (Hq + Hkv) * L * 8 * d * d
+    lam = still.still_lambda(p)
+    cap = (wl.budget - wl.window) // lam if lam > 0 else 0
+    flops = backward_work(wl, lam, cap)
     tf = flops / (ms * 1e-3) / 1e12
     return {"workload": wl.name, "steps": steps, "ms": ms, "tokens_per_s": B * L / (ms * 1e-3),
-            "form": "dense (every pair on or below the diagonal), float32 vector ALU",
+            "form": "chunked (prefix / suffix chunk states, band and kept-pool pairs one by one), "
+                    "float32 vector ALU",
             "flops_per_launch": flops, "tflops": tf,
             "roofline": {"bound": "alu", "achieved": tf, "peak": PEAK_FP32_VECTOR_TFLOPS,
                          "unit": "TFLOP/s", "frac": tf / PEAK_FP32_VECTOR_TFLOPS}}

@@ -300,9 +300,11 @@ int still_decode_tokens(const still_params* p, int64_t pos, const int32_t* row_p
  * overwritten): dq [B, Hq, L, d], dk, dv [B, Hkv, L, d], dfmap [Hkv, d, d],
  * dgate [Hq]. Default merge only (the branch-variant flags return
  * STILL_EUNSUPPORTED). workspace: ws_bytes >= still_backward_workspace_bytes
- * (p, seq_len), 16-byte aligned. Dense form: every (query, key) pair on or
- * below the diagonal is visited, so the cost grows as L^2. Accuracy: float32
- * arithmetic on top of the forward's y and normalisers. */
+ * (p, seq_len), 16-byte aligned. Chunked form, linear in L: the linear
+ * branch through per-chunk prefix states (query side) and suffix states
+ * (key side), the band and kept-pool pairs one by one. Accuracy: float32
+ * arithmetic (float64 chunk scans) on top of the forward's y and
+ * normalisers. */
 int64_t still_backward_workspace_bytes(const still_params* p, int64_t seq_len);
 int still_backward(const still_params* p, int64_t seq_len, const void* q, const void* k, const void* v,
                    const void* fmap_w, const float* gate, const int32_t* sel_idx, const float* y,

@@ -368,7 +368,7 @@ int scratch_address(void** out) {
 
 // ---------------------------------------------------------------- backward
 struct BwPlan {
-  int64_t phq, phk, dphq, dphk, dz, lnN, delta, kept, total;
+  int64_t phq, phk, dphq, dphk, dz, lnN, delta, kept, cS, cR, total;
 };
 
 static BwPlan bw_plan(const Derived& d, int64_t L) {
@@ -388,6 +388,9 @@ static BwPlan bw_plan(const Derived& d, int64_t L) {
   w.lnN = take(nq * 4);
   w.delta = take(nq * 4);
   w.kept = take(nk);
+  const int64_t T = (L + d.C - 1) / d.C;
+  w.cS = take((int64_t)d.B * d.Hkv * T * ((int64_t)d.D * d.D + d.D) * 4);
+  w.cR = take((int64_t)d.B * d.Hkv * T * ((int64_t)d.D * d.D + d.D) * 4);
   w.total = o;
   return w;
 }
@@ -404,8 +407,16 @@ static int launch_backward(const Derived& d, const BwPlan& w, still::BackwardArg
                     dim3(BW_THREADS), 0, s>>>(a);
   const dim3 rows_grid((L + BW_ROWS - 1) / BW_ROWS, d.B * (d.Hq + d.Hkv));
   bw_phi_kernel<T, D><<<rows_grid, dim3(BW_THREADS), BwRowLds<D>::bytes, s>>>(a);
+  const int64_t nq = (int64_t)d.B * d.Hq * L;
+  bw_rowstat_kernel<<<dim3((unsigned)((nq + 3) / 4)), dim3(BW_THREADS), 0, s>>>(a, D);
+  bw_chunk_delta_kernel<T, D><<<dim3(a.T, d.B * d.Hkv, 2), dim3(BW_THREADS), 0, s>>>(a);
+  bw_chunk_scan_kernel<<<dim3((D * D + D + BW_THREADS - 1) / BW_THREADS, 2 * d.B * d.Hkv), dim3(BW_THREADS), 0, s>>>(
+      a, D);
   bw_query_kernel<T, D><<<dim3((L + BW_QT - 1) / BW_QT, d.Hq, d.B), dim3(BW_THREADS), BwQLds<D>::bytes, s>>>(a);
   bw_key_kernel<T, D><<<dim3((L + BW_KT - 1) / BW_KT, d.Hkv, d.B), dim3(BW_THREADS), BwKLds<D>::bytes, s>>>(a);
+  const int n_kept = pool_count_at(a.n_dec, a.lam, a.cap_chunks);
+  if (n_kept > 0)
+    bw_pool_kernel<T, D><<<dim3((n_kept + BW_KT - 1) / BW_KT, d.Hkv, d.B), dim3(BW_THREADS), BwKLds<D>::bytes, s>>>(a);
   bw_npmap_kernel<T, D><<<rows_grid, dim3(BW_THREADS), BwRowLds<D>::bytes, s>>>(a);
   const int64_t nrow = (int64_t)d.B * (d.G + 1) * L;
   bw_dfmap_kernel<T, D><<<dim3((unsigned)((nrow + BW_DF_ROWS - 1) / BW_DF_ROWS), d.Hkv), dim3(BW_THREADS), 0, s>>>(a);
@@ -792,6 +803,10 @@ int still_backward(const still_params* p, int64_t seq_len, const void* q, const 
   a.lnN = reinterpret_cast<float*>(ws + w.lnN);
   a.delta = reinterpret_cast<float*>(ws + w.delta);
   a.kept = reinterpret_cast<uint8_t*>(ws + w.kept);
+  a.cS = reinterpret_cast<float*>(ws + w.cS);
+  a.cR = reinterpret_cast<float*>(ws + w.cR);
+  a.T = (int)((seq_len + d.C - 1) / d.C);
+  a.cap_chunks = d.cap_chunks;
   a.B = d.B;
   a.Hq = d.Hq;
   a.Hkv = d.Hkv;

@@ -24,19 +24,36 @@
 // N_t comes from the forward's log-normalisers (the branch partials), y_t
 // from its float32 output.
 //
-// Dense form: every (query, key) pair on or below the diagonal is visited,
-// in float32 on the vector ALUs, tiles staged in LDS. The cost grows as
-// L^2 (the forward's is linear in L).
+// Chunked form, linear in L like the forward: with the routing fixed, the
+// linear keys of a query t of chunk c are the unkept tokens before the
+// chunk-level boundary b_c = cf(c) C (the forward's folded state) plus some
+// band keys in [b_c, t]; so the linear part of the query side is the chunk's
+// prefix state P_c = sum_{unkept j < b_c} phi(k_j) v_j^T (and z_c):
+//   d phi(q_t) += (g / N_t)(P_c dy_t - z_c delta_t),
+//   dg += (1 / N_t)(phi(q_t)^T P_c dy_t - delta_t phi(q_t) . z_c),
+// and the linear part of the key side, for an unkept key j, is a suffix over
+// the query chunks that hold j in their state, R = sum (g / N_t) phi(q_t)
+// dy_t^T and r = sum (g / N_t) delta_t phi(q_t) (over those chunks' queries
+// and the group's heads):
+//   d phi(k_j) += R v_j - r,  dv_j += R^T phi(k_j).
+// The remaining pairs are visited one by one: the band pairs (key in
+// [b_c, t]) from both sides, and the kept-pool pairs (softmax keys of every
+// later chunk) from the query side and, for dk and dv, from a pass over the
+// kept keys. Float32 on the vector ALUs, tiles in LDS, float64 scans.
 //
 // Kernels, in launch order:
-//   0. zero the accumulated outputs (dgate, dfmap); kept flags from sel
-//   1. NP-Map features of every q and k row
-//   2. query side: per 16-query tile, all earlier keys: the softmax part of
-//      dq, d phi(q), dg; the rows' ln N and delta for step 3
-//   3. key side: per 32-key tile, all later queries of the group's heads:
-//      the softmax part of dk, d phi(k), dv
-//   4. NP-Map backward of every row: dq, dk += J^T d phi; dz = d(x F)
-//   5. dF = sum over rows of x^T dz, per kv head
+//   0. zero dgate, dfmap; kept flags from sel
+//   1. NP-Map features of every q and k row; per query row ln N and delta
+//   2. per chunk: the state delta (unkept keys) and the query-side delta
+//      (R, r); a float64 prefix scan of the first, suffix scan of the second
+//   3. query side, per 16-query tile: band and pool pairs, the state term:
+//      dq (softmax part), d phi(q), dg
+//   4. key side, per 16-key tile: band pairs of the group's heads, the
+//      suffix-state term: dk (softmax part), d phi(k), dv
+//   5. kept keys, per 16 pool entries: their softmax pairs with the later
+//      chunks' queries: dk, dv +=
+//   6. NP-Map backward of every row: dq, dk += J^T d phi; dz = d(x F)
+//   7. dF = sum over rows of x^T dz, per kv head
 #include "still_common.h"
 
 namespace still {
@@ -54,7 +71,9 @@ struct BackwardArgs {
   float *lnN, *delta;              // [B][Hq][L]
   float* dz;                       // [B*Hq*L + B*Hkv*L][D] gradients of x F
   uint8_t* kept;                   // [B][Hkv][L]
-  int B, Hq, Hkv, G, L, W, C, n_dec, lam;
+  float* cS;                       // [B][Hkv][T][D*D + D] chunk state deltas -> prefix
+  float* cR;                       // [B][Hkv][T][D*D + D] chunk query deltas -> suffix
+  int B, Hq, Hkv, G, L, W, C, n_dec, lam, T, cap_chunks;
   float scale;
 };
 
@@ -229,36 +248,188 @@ __device__ __forceinline__ void bw_dots(const float* q, const float* pq, const f
   e = e0;
 }
 
-// 2. query side: one workgroup per (16-query tile, query head, batch row)
-constexpr int BW_QT = 16, BW_KT = 32;
+// per query row: delta = dy . y and ln N = ln(Z + g D) from the branch
+// log-normalisers (one wave per row)
+__global__ __launch_bounds__(BW_THREADS) void bw_rowstat_kernel(BackwardArgs a, int D) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t r = (int64_t)blockIdx.x * 4 + wave, rows = (int64_t)a.B * a.Hq * a.L;
+  if (r >= rows) return;  // wave-uniform
+  const int h = (int)((r / a.L) % a.Hq);
+  float dd = 0.f;
+  for (int d = lane; d < D; d += 64) dd += a.dy[r * D + d] * a.y[r * D + d];
+  dd = wave_sum(dd);
+  if (lane == 0) {
+    const float g = a.gate[h], ls = a.lse_sa[r], ll = a.lse_la[r];
+    a.lnN[r] = (g > 0.f && ll != STILL_NEG_INF) ? ls + log1pf(g * expf(ll - ls)) : ls;
+    a.delta[r] = dd;
+  }
+}
+
+// 2a. per chunk c: cS[c] = sum over its unkept keys of phi(k) v^T (row-major
+// D x D) and phi(k) (D); cR[c] = sum over its queries and the group's heads
+// of (g / N) phi(q) dy^T and (g / N) delta phi(q). Thread (i, part) owns
+// entries [i][part OPT .. + OPT) and, for part 0, the vector entry i.
+template <typename T, int D>
+__global__ __launch_bounds__(BW_THREADS) void bw_chunk_delta_kernel(BackwardArgs a) {
+  __shared__ float xa[16][D];
+  __shared__ float xb[16][D];
+  __shared__ float cf_[16];  // per-row factor
+  constexpr int OPT = D * D / BW_THREADS;
+  const int c = blockIdx.x, kv = blockIdx.y % a.Hkv, b = blockIdx.y / a.Hkv, side = blockIdx.z;
+  const int tid = threadIdx.x, i = tid / (BW_THREADS / D), j0 = (tid % (BW_THREADS / D)) * OPT;
+  const int L = a.L, C = a.C;
+  const size_t unit = (size_t)b * a.Hkv + kv;
+  float acc[OPT], vec = 0.f;
+#pragma unroll
+  for (int e = 0; e < OPT; ++e) acc[e] = 0.f;
+  // side 0: rows = the chunk's keys (factor: unkept); side 1: rows = the
+  // chunk's queries of every head of the group (factor g / N)
+  const int nrows = side == 0 ? C : C * a.G;
+  for (int r0 = 0; r0 < nrows; r0 += 16) {
+    __syncthreads();
+    for (int e = tid; e < 16 * D; e += BW_THREADS) {
+      const int rr = e / D, d = e % D, r = r0 + rr;
+      float va = 0.f, vb = 0.f;
+      if (side == 0) {
+        const int t = c * C + r;
+        if (r < nrows && t < L) {
+          va = a.phk[(unit * L + t) * D + d];
+          vb = to_f32(reinterpret_cast<const T*>(a.v)[(unit * L + t) * D + d]);
+        }
+      } else {
+        const int hl = r / C, t = c * C + r % C;
+        if (r < nrows && t < L) {
+          const size_t row = ((size_t)b * a.Hq + kv * a.G + hl) * L + t;
+          va = a.phq[row * D + d];
+          vb = a.dy[row * D + d];
+        }
+      }
+      xa[rr][d] = va;
+      xb[rr][d] = vb;
+    }
+    if (tid < 16) {
+      const int r = r0 + tid;
+      float f = 0.f;
+      if (side == 0) {
+        const int t = c * C + r;
+        if (r < nrows && t < L) f = a.kept[unit * L + t] ? 0.f : 1.f;
+      } else {
+        const int hl = r / C, t = c * C + r % C;
+        if (r < nrows && t < L) {
+          const int h = kv * a.G + hl;
+          const size_t row = ((size_t)b * a.Hq + h) * L + t;
+          const float g = a.gate[h];
+          f = g > 0.f ? g * expf(-a.lnN[row]) : 0.f;
+        }
+      }
+      cf_[tid] = f;
+    }
+    __syncthreads();
+    for (int rr = 0; rr < 16; ++rr) {
+      const float f = cf_[rr];
+      if (f == 0.f) continue;  // uniform across the workgroup
+      const float xi = f * xa[rr][i];
+#pragma unroll
+      for (int e = 0; e < OPT; ++e) acc[e] = fmaf(xi, xb[rr][j0 + e], acc[e]);
+      if (j0 == 0) {
+        float w = 1.f;
+        if (side == 1) {
+          const int r = r0 + rr, hl = r / C, t = c * C + r % C;
+          w = a.delta[((size_t)b * a.Hq + kv * a.G + hl) * L + t];
+        }
+        vec = fmaf(xi, w, vec);
+      }
+    }
+  }
+  float* dst = (side == 0 ? a.cS : a.cR) + (unit * a.T + c) * (size_t)(D * D + D);
+#pragma unroll
+  for (int e = 0; e < OPT; ++e) dst[(size_t)i * D + j0 + e] = acc[e];
+  if (j0 == 0) dst[D * D + i] = vec;
+}
+
+// 2b. scans over chunks, float64 running sums: cS inclusive prefix (the
+// state of the chunks <= c), cR inclusive suffix (chunks >= c).
+__global__ __launch_bounds__(BW_THREADS) void bw_chunk_scan_kernel(BackwardArgs a, int D) {
+  const int n_elem = D * D + D;
+  const int e = blockIdx.x * BW_THREADS + threadIdx.x;
+  if (e >= n_elem) return;
+  const size_t unit = (size_t)blockIdx.y % (a.B * a.Hkv);
+  const bool suffix = blockIdx.y >= (unsigned)(a.B * a.Hkv);
+  float* base = (suffix ? a.cR : a.cS) + unit * a.T * (size_t)n_elem + e;
+  double run = 0.0;
+  for (int k = 0; k < a.T; ++k) {
+    const int c = suffix ? a.T - 1 - k : k;
+    run += (double)base[(size_t)c * n_elem];
+    base[(size_t)c * n_elem] = (float)run;
+  }
+}
+
+// Tile helpers of the pair kernels (LDS rows of D floats, padded).
+constexpr int BW_QT = 16, BW_KT = 16;
+
+// Loads the rows `pos[i]` (-1: zeros) of a [L][D] array of type S into LDS.
+template <typename S, int D>
+__device__ __forceinline__ void bw_load_rows(float* dst, const S* src, const int* pos, int n) {
+  constexpr int RS = D + BW_PAD;
+  for (int e = threadIdx.x; e < n * D; e += BW_THREADS) {
+    const int i = e / D, d = e % D, p = pos[i];
+    dst[i * RS + d] = p >= 0 ? to_f32(src[(size_t)p * D + d]) : 0.f;
+  }
+}
+
+// Pair gradients of query row t (of head with gate g, ln N, delta) and key
+// j: softmax pair -> (p, ds, 0), linear pair -> (p, 0, dw) and its dg term.
+struct BwPair {
+  float p, ds, dw, dg;
+};
+__device__ __forceinline__ BwPair bw_pair(bool sa, float s, float w, float e, float g, float lnN, float dl,
+                                          float scale) {
+  BwPair r{0.f, 0.f, 0.f, 0.f};
+  if (sa) {
+    r.p = expf(scale * s - lnN);
+    r.ds = r.p * (e - dl);
+  } else {
+    const float rN = expf(-lnN);
+    r.p = g * w * rN;
+    r.dw = g * rN * (e - dl);
+    r.dg = w * rN * (e - dl);
+  }
+  return r;
+}
+
+// 3. query side: one workgroup per (16-query tile, query head, batch row);
+// the tile lies in one chunk c (C is a multiple of 16)
 template <int D>
 struct BwQLds {
   static constexpr int RS = D + BW_PAD;
-  static constexpr int bytes = (3 * BW_QT * RS + 3 * BW_KT * RS + 2 * BW_QT * (BW_KT + 1) + 2 * BW_QT) * 4 + BW_KT;
+  static constexpr int KT = 32;
+  static constexpr int bytes =
+      (3 * BW_QT * RS + 3 * KT * RS + 2 * BW_QT * (KT + 1) + 2 * BW_QT + KT) * 4 + KT * 4;
 };
 
 template <typename T, int D>
 __global__ __launch_bounds__(BW_THREADS) void bw_query_kernel(BackwardArgs a) {
   extern __shared__ __align__(16) char smem[];
-  constexpr int RS = D + BW_PAD, DPT = D / 16;
+  constexpr int RS = D + BW_PAD, DPT = D / 16, KT = BwQLds<D>::KT;
   float* Qs = reinterpret_cast<float*>(smem);
   float* PQs = Qs + BW_QT * RS;
   float* DYs = PQs + BW_QT * RS;
   float* Ks = DYs + BW_QT * RS;
-  float* PKs = Ks + BW_KT * RS;
-  float* Vs = PKs + BW_KT * RS;
-  float* DS = Vs + BW_KT * RS;          // [QT][KT + 1]
-  float* DW = DS + BW_QT * (BW_KT + 1);  // [QT][KT + 1]
-  float* rowN = DW + BW_QT * (BW_KT + 1);  // ln N of the tile's rows
-  float* rowD = rowN + BW_QT;             // delta
-  uint8_t* kp = reinterpret_cast<uint8_t*>(rowD + BW_QT);  // [KT] kept flags
+  float* PKs = Ks + KT * RS;
+  float* Vs = PKs + KT * RS;
+  float* DS = Vs + KT * RS;            // [QT][KT + 1]
+  float* DW = DS + BW_QT * (KT + 1);   // [QT][KT + 1]
+  float* rowN = DW + BW_QT * (KT + 1);
+  float* rowD = rowN + BW_QT;
+  int* kpos = reinterpret_cast<int*>(rowD + BW_QT);  // [KT] key positions (-1: none)
+  int* ksa = kpos + KT;                              // [KT] kept (pool) flags
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int t0 = blockIdx.x * BW_QT, h = blockIdx.y, b = blockIdx.z;
-  const int L = a.L, kv = h / a.G;
+  const int L = a.L, C = a.C, kv = h / a.G;
   const float g = a.gate[h];
-  const size_t qrow0 = ((size_t)b * a.Hq + h) * L;  // row index of (b, h, 0)
-  const size_t krow0 = ((size_t)b * a.Hkv + kv) * L;
-  // query tile: q (as float), phi(q), dy; rows past L are zeros
+  const size_t qrow0 = ((size_t)b * a.Hq + h) * L;
+  const size_t unit = (size_t)b * a.Hkv + kv, krow0 = unit * L;
+  const int c = t0 / C, cf = full_chunks_before(c, a.W, C), bc = cf * C;
   for (int e = tid; e < BW_QT * D; e += BW_THREADS) {
     const int i = e / D, d = e % D, t = t0 + i;
     const bool in = t < L;
@@ -266,84 +437,102 @@ __global__ __launch_bounds__(BW_THREADS) void bw_query_kernel(BackwardArgs a) {
     PQs[i * RS + d] = in ? a.phq[(qrow0 + t) * D + d] : 0.f;
     DYs[i * RS + d] = in ? a.dy[(qrow0 + t) * D + d] : 0.f;
   }
-  // row constants: delta = dy . y, ln N = ln(Z + g D) from the branch
-  // log-normalisers (wave w: rows 4w .. 4w + 3)
-  for (int i = wave * (BW_QT / 4); i < (wave + 1) * (BW_QT / 4); ++i) {
-    const int t = t0 + i;
-    float dd = 0.f;
-    if (t < L)
-      for (int d = lane; d < D; d += 64) dd += a.dy[(qrow0 + t) * D + d] * a.y[(qrow0 + t) * D + d];
-    dd = wave_sum(dd);
-    if (lane == 0) {
-      float ln = 0.f;
-      if (t < L) {
-        const float ls = a.lse_sa[qrow0 + t], ll = a.lse_la[qrow0 + t];
-        ln = (g > 0.f && ll != STILL_NEG_INF) ? ls + log1pf(g * expf(ll - ls)) : ls;
-        a.lnN[qrow0 + t] = ln;
-        a.delta[qrow0 + t] = dd;
-      }
-      rowN[i] = ln;
-      rowD[i] = dd;
-    }
+  if (tid < BW_QT) {
+    const int t = t0 + tid;
+    rowN[tid] = t < L ? a.lnN[qrow0 + t] : 0.f;
+    rowD[tid] = t < L ? a.delta[qrow0 + t] : 0.f;
   }
-  const int qi = tid >> 4, sub = tid & 15;  // row of the tile; key pair / column group
+  const int qi = tid >> 4, sub = tid & 15;
   const int t = t0 + qi;
   float dqa[DPT], dpa[DPT], dg = 0.f;
 #pragma unroll
-  for (int c = 0; c < DPT; ++c) dqa[c] = dpa[c] = 0.f;
-  const int j_end = min(t0 + BW_QT, L);
-  for (int j0 = 0; j0 < j_end; j0 += BW_KT) {
-    __syncthreads();  // the previous tile is done with Ks .. DW
-    for (int e = tid; e < BW_KT * D; e += BW_THREADS) {
-      const int i = e / D, d = e % D, j = j0 + i;
-      const bool in = j < L;
-      Ks[i * RS + d] = in ? to_f32(reinterpret_cast<const T*>(a.k)[(krow0 + j) * D + d]) : 0.f;
-      PKs[i * RS + d] = in ? a.phk[(krow0 + j) * D + d] : 0.f;
-      Vs[i * RS + d] = in ? to_f32(reinterpret_cast<const T*>(a.v)[(krow0 + j) * D + d]) : 0.f;
+  for (int cc = 0; cc < DPT; ++cc) dqa[cc] = dpa[cc] = 0.f;
+  // key tiles: the band [bc, min(t0 + 15, L - 1)] in order, then the kept
+  // pool's entries (sel rows of the chunks before cf, all valid)
+  const int band_hi = min(t0 + BW_QT, L);
+  const int n_band = (band_hi - bc + KT - 1) / KT;
+  const int n_pool = pool_count_at(cf, a.lam, a.cap_chunks);
+  const int32_t* pool = a.sel + unit * (size_t)a.n_dec * a.lam;
+  const int n_tiles = n_band + (n_pool + KT - 1) / KT;
+  for (int it = 0; it < n_tiles; ++it) {
+    __syncthreads();  // the previous tile is done with Ks .. kpos
+    const bool band = it < n_band;
+    if (tid < KT) {
+      int p = -1;
+      if (band) {
+        const int j = bc + it * KT + tid;
+        p = j < band_hi ? j : -1;
+      } else {
+        const int e = (it - n_band) * KT + tid;
+        p = e < n_pool ? pool[e] : -1;
+      }
+      kpos[tid] = p;
+      ksa[tid] = band ? (p >= 0 ? a.kept[krow0 + p] : 0) : 1;
     }
-    if (tid < BW_KT) kp[tid] = j0 + tid < L ? a.kept[krow0 + j0 + tid] : 0;
     __syncthreads();
-    // pair gradients of (t, keys 2 sub, 2 sub + 1)
+    bw_load_rows<T, D>(Ks, reinterpret_cast<const T*>(a.k) + krow0 * D, kpos, KT);
+    bw_load_rows<float, D>(PKs, a.phk + krow0 * D, kpos, KT);
+    bw_load_rows<T, D>(Vs, reinterpret_cast<const T*>(a.v) + krow0 * D, kpos, KT);
+    __syncthreads();
     const float lnN = rowN[qi], dl = rowD[qi];
-    const float rN = expf(-lnN);
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int kk = 2 * sub + u, j = j0 + kk;
+    for (int u = 0; u < KT / 16; ++u) {
+      const int kk = (KT / 16) * sub + u, j = kpos[kk];
       float ds = 0.f, dw = 0.f;
-      if (t < L && j <= t) {
+      if (t < L && j >= 0 && j <= t) {
         float s, w, e;
         bw_dots<D>(Qs + qi * RS, PQs + qi * RS, DYs + qi * RS, Ks + kk * RS, PKs + kk * RS, Vs + kk * RS, s, w,
                    e);
-        if (bw_is_sa(t, j, a.W, a.C, kp[kk] != 0)) {
-          ds = expf(a.scale * s - lnN) * (e - dl);
-        } else {
-          dw = g * rN * (e - dl);
-          dg += w * rN * (e - dl);
-        }
+        const bool sa = band ? bw_is_sa(t, j, a.W, C, ksa[kk] != 0) : true;
+        const BwPair pr = bw_pair(sa, s, w, e, g, lnN, dl, a.scale);
+        ds = pr.ds;
+        dw = pr.dw;
+        dg += pr.dg;
       }
-      DS[qi * (BW_KT + 1) + kk] = ds;
-      DW[qi * (BW_KT + 1) + kk] = dw;
+      DS[qi * (KT + 1) + kk] = ds;
+      DW[qi * (KT + 1) + kk] = dw;
     }
     __syncthreads();
-    // dq += ds K, d phi(q) += dw phi(K) over the tile's keys (columns
-    // sub + 16 c of the row)
-    for (int kk = 0; kk < BW_KT; ++kk) {
-      const float ds = DS[qi * (BW_KT + 1) + kk], dw = DW[qi * (BW_KT + 1) + kk];
+    for (int kk = 0; kk < KT; ++kk) {
+      const float ds = DS[qi * (KT + 1) + kk], dw = DW[qi * (KT + 1) + kk];
 #pragma unroll
-      for (int c = 0; c < DPT; ++c) {
-        dqa[c] = fmaf(ds, Ks[kk * RS + sub + 16 * c], dqa[c]);
-        dpa[c] = fmaf(dw, PKs[kk * RS + sub + 16 * c], dpa[c]);
+      for (int cc = 0; cc < DPT; ++cc) {
+        dqa[cc] = fmaf(ds, Ks[kk * RS + sub + 16 * cc], dqa[cc]);
+        dpa[cc] = fmaf(dw, PKs[kk * RS + sub + 16 * cc], dpa[cc]);
       }
     }
+  }
+  // the state term: P = state of the chunks < cf (prefix entry cf - 1);
+  // dg needs it whatever the gate
+  if (cf > 0 && t < L) {
+    const float* P = a.cS + (unit * a.T + (cf - 1)) * (size_t)(D * D + D);
+    const float lnN = rowN[qi], dl = rowD[qi], rN = expf(-lnN);
+    const float* dyr = DYs + qi * RS;
+    float pu = 0.f, pz = 0.f;
+#pragma unroll
+    for (int cc = 0; cc < DPT; ++cc) {
+      const int i = sub + 16 * cc;
+      const float* Pi = P + (size_t)i * D;
+      float u = 0.f;
+      for (int k = 0; k < D; k += 4) {
+        const f32x4 pv = *reinterpret_cast<const f32x4*>(Pi + k);
+        const f32x4 dv = *reinterpret_cast<const f32x4*>(dyr + k);
+        u = fmaf(pv[0], dv[0], fmaf(pv[1], dv[1], fmaf(pv[2], dv[2], fmaf(pv[3], dv[3], u))));
+      }
+      const float zi = P[D * D + i];
+      dpa[cc] += g * rN * (u - zi * dl);
+      pu += PQs[qi * RS + i] * u;
+      pz += PQs[qi * RS + i] * zi;
+    }
+    dg += rN * (pu - dl * pz);
   }
   if (t < L) {
 #pragma unroll
-    for (int c = 0; c < DPT; ++c) {
-      a.dq[(qrow0 + t) * D + sub + 16 * c] = a.scale * dqa[c];
-      a.dphq[(qrow0 + t) * D + sub + 16 * c] = dpa[c];
+    for (int cc = 0; cc < DPT; ++cc) {
+      a.dq[(qrow0 + t) * D + sub + 16 * cc] = a.scale * dqa[cc];
+      a.dphq[(qrow0 + t) * D + sub + 16 * cc] = dpa[cc];
     }
   }
-  // dg over the workgroup, one atomic add
   dg = wave_sum(dg);
   __syncthreads();
   if (lane == 0) rowN[wave] = dg;
@@ -351,34 +540,44 @@ __global__ __launch_bounds__(BW_THREADS) void bw_query_kernel(BackwardArgs a) {
   if (tid == 0) atomicAdd(a.dgate + h, rowN[0] + rowN[1] + rowN[2] + rowN[3]);
 }
 
-// 3. key side: one workgroup per (32-key tile, kv head, batch row); the
-// group's query heads and every later 16-query tile in turn
+// Last chunk whose queries hold key chunk cj in their band (cf(c) <= cj).
+__device__ __forceinline__ int bw_band_last_chunk(int cj, int W, int C, int T) {
+  int c = cj;
+  while (c + 1 < T && full_chunks_before(c + 1, W, C) <= cj) ++c;
+  return c;
+}
+
+// 4. key side: one workgroup per (16-key tile, kv head, batch row); the
+// tile lies in one chunk cj. Band queries: chunks cj .. c_hi (cf <= cj),
+// every head of the group; then the suffix state of the chunks after c_hi
+// for the unkept keys.
 template <int D>
 struct BwKLds {
   static constexpr int RS = D + BW_PAD;
-  static constexpr int bytes = (3 * BW_KT * RS + 3 * BW_QT * RS + 3 * BW_KT * (BW_QT + 1) + 2 * BW_QT) * 4 + BW_KT;
+  static constexpr int bytes = (3 * BW_KT * RS + 3 * BW_QT * RS + 3 * BW_KT * (BW_QT + 1) + 2 * BW_QT) * 4 + BW_KT * 4;
 };
 
 template <typename T, int D>
 __global__ __launch_bounds__(BW_THREADS) void bw_key_kernel(BackwardArgs a) {
   extern __shared__ __align__(16) char smem[];
-  constexpr int RS = D + BW_PAD, DPT = D / 8;
+  constexpr int RS = D + BW_PAD, DPT = D / 16;
   float* Ks = reinterpret_cast<float*>(smem);
   float* PKs = Ks + BW_KT * RS;
   float* Vs = PKs + BW_KT * RS;
   float* Qs = Vs + BW_KT * RS;
   float* PQs = Qs + BW_QT * RS;
   float* DYs = PQs + BW_QT * RS;
-  float* PS = DYs + BW_QT * RS;          // [KT][QT + 1] weight / N
+  float* PS = DYs + BW_QT * RS;          // [KT][QT + 1]
   float* DS = PS + BW_KT * (BW_QT + 1);  // [KT][QT + 1]
   float* DW = DS + BW_KT * (BW_QT + 1);  // [KT][QT + 1]
   float* rowN = DW + BW_KT * (BW_QT + 1);
   float* rowD = rowN + BW_QT;
-  uint8_t* kp = reinterpret_cast<uint8_t*>(rowD + BW_QT);
+  int* kp = reinterpret_cast<int*>(rowD + BW_QT);  // [KT] kept flags
   const int tid = threadIdx.x;
   const int j0 = blockIdx.x * BW_KT, kv = blockIdx.y, b = blockIdx.z;
-  const int L = a.L;
-  const size_t krow0 = ((size_t)b * a.Hkv + kv) * L;
+  const int L = a.L, C = a.C;
+  const size_t unit = (size_t)b * a.Hkv + kv, krow0 = unit * L;
+  const int cj = j0 / C, c_hi = bw_band_last_chunk(cj, a.W, C, a.T);
   for (int e = tid; e < BW_KT * D; e += BW_THREADS) {
     const int i = e / D, d = e % D, j = j0 + i;
     const bool in = j < L;
@@ -387,22 +586,143 @@ __global__ __launch_bounds__(BW_THREADS) void bw_key_kernel(BackwardArgs a) {
     Vs[i * RS + d] = in ? to_f32(reinterpret_cast<const T*>(a.v)[(krow0 + j) * D + d]) : 0.f;
   }
   if (tid < BW_KT) kp[tid] = j0 + tid < L ? a.kept[krow0 + j0 + tid] : 0;
-  const int qi = tid >> 4, sub = tid & 15;  // phase 1: query row, key pair
-  const int kk2 = tid >> 3, part = tid & 7;  // phase 2: key row, column group
+  const int qi = tid >> 4, sub = tid & 15;   // phase 1: query row, key
+  const int kk2 = tid >> 4, part = tid & 15;  // phase 2: key row, columns part + 16 c
   float dka[DPT], dpa[DPT], dva[DPT];
 #pragma unroll
-  for (int c = 0; c < DPT; ++c) dka[c] = dpa[c] = dva[c] = 0.f;
+  for (int cc = 0; cc < DPT; ++cc) dka[cc] = dpa[cc] = dva[cc] = 0.f;
+  const int t_end = min(L, (c_hi + 1) * C);
   for (int hl = 0; hl < a.G; ++hl) {
     const int h = kv * a.G + hl;
     const float g = a.gate[h];
     const size_t qrow0 = ((size_t)b * a.Hq + h) * L;
-    for (int t0 = (j0 / BW_QT) * BW_QT; t0 < L; t0 += BW_QT) {
+    for (int t0 = j0; t0 < t_end; t0 += BW_QT) {
       __syncthreads();  // the previous query tile is done with Qs .. DW
+      for (int e = tid; e < BW_QT * D; e += BW_THREADS) {
+        const int i = e / D, d = e % D, t = t0 + i;
+        const bool in = t < t_end;
+        Qs[i * RS + d] = in ? to_f32(reinterpret_cast<const T*>(a.q)[(qrow0 + t) * D + d]) : 0.f;
+        PQs[i * RS + d] = in ? a.phq[(qrow0 + t) * D + d] : 0.f;
+        DYs[i * RS + d] = in ? a.dy[(qrow0 + t) * D + d] : 0.f;
+      }
+      if (tid < BW_QT) {
+        const int t = t0 + tid;
+        rowN[tid] = t < t_end ? a.lnN[qrow0 + t] : 0.f;
+        rowD[tid] = t < t_end ? a.delta[qrow0 + t] : 0.f;
+      }
+      __syncthreads();
+      const int t = t0 + qi, kk = sub, j = j0 + kk;
+      BwPair pr{0.f, 0.f, 0.f, 0.f};
+      if (t < t_end && j < L && j <= t) {
+        float s, w, e;
+        bw_dots<D>(Qs + qi * RS, PQs + qi * RS, DYs + qi * RS, Ks + kk * RS, PKs + kk * RS, Vs + kk * RS, s, w,
+                   e);
+        pr = bw_pair(bw_is_sa(t, j, a.W, C, kp[kk] != 0), s, w, e, g, rowN[qi], rowD[qi], a.scale);
+      }
+      PS[kk * (BW_QT + 1) + qi] = pr.p;
+      DS[kk * (BW_QT + 1) + qi] = pr.ds;
+      DW[kk * (BW_QT + 1) + qi] = pr.dw;
+      __syncthreads();
+      for (int i = 0; i < BW_QT; ++i) {
+        const float p = PS[kk2 * (BW_QT + 1) + i], ds = DS[kk2 * (BW_QT + 1) + i], dw = DW[kk2 * (BW_QT + 1) + i];
+#pragma unroll
+        for (int cc = 0; cc < DPT; ++cc) {
+          dka[cc] = fmaf(ds, Qs[i * RS + part + 16 * cc], dka[cc]);
+          dpa[cc] = fmaf(dw, PQs[i * RS + part + 16 * cc], dpa[cc]);
+          dva[cc] = fmaf(p, DYs[i * RS + part + 16 * cc], dva[cc]);
+        }
+      }
+    }
+  }
+  // suffix state of the chunks after c_hi (their queries hold key j in the
+  // state when j is unkept): d phi(k) += R v - r, dv += R^T phi(k)
+  const int j = j0 + kk2;
+  if (c_hi + 1 < a.T && j < L && !kp[kk2]) {
+    const float* R = a.cR + (unit * a.T + (c_hi + 1)) * (size_t)(D * D + D);
+    const float* vr = Vs + kk2 * RS;
+    const float* pr = PKs + kk2 * RS;
+    float u[DPT], w[DPT];
+#pragma unroll
+    for (int cc = 0; cc < DPT; ++cc) u[cc] = w[cc] = 0.f;
+#pragma unroll 2
+    for (int k = 0; k < D; ++k) {
+      const float vk = vr[k], pk = pr[k];
+#pragma unroll
+      for (int cc = 0; cc < DPT; ++cc) {
+        const int i = part + 16 * cc;
+        u[cc] = fmaf(R[(size_t)i * D + k], vk, u[cc]);  // (R v)_i
+        w[cc] = fmaf(R[(size_t)k * D + i], pk, w[cc]);  // (R^T phi(k))_i
+      }
+    }
+#pragma unroll
+    for (int cc = 0; cc < DPT; ++cc) {
+      dpa[cc] += u[cc] - R[D * D + part + 16 * cc];
+      dva[cc] += w[cc];
+    }
+  }
+  if (j < L) {
+#pragma unroll
+    for (int cc = 0; cc < DPT; ++cc) {
+      a.dk[(krow0 + j) * D + part + 16 * cc] = a.scale * dka[cc];
+      a.dphk[(krow0 + j) * D + part + 16 * cc] = dpa[cc];
+      a.dv[(krow0 + j) * D + part + 16 * cc] = dva[cc];
+    }
+  }
+}
+
+// 5. kept keys: one workgroup per (16 consecutive entries of the unit's
+// selection, kv head, batch row). Entry j (kept, chunk cj) is a softmax key
+// of every query of the chunks after bw_band_last_chunk(cj) (the band
+// pairs were taken by the key-side kernel); dk, dv of these pairs are added.
+template <typename T, int D>
+__global__ __launch_bounds__(BW_THREADS) void bw_pool_kernel(BackwardArgs a) {
+  extern __shared__ __align__(16) char smem[];
+  constexpr int RS = D + BW_PAD, DPT = D / 16;
+  float* Ks = reinterpret_cast<float*>(smem);
+  float* PKs = Ks + BW_KT * RS;  // (unused; keeps the key kernel's layout)
+  float* Vs = PKs + BW_KT * RS;
+  float* Qs = Vs + BW_KT * RS;
+  float* PQs = Qs + BW_QT * RS;
+  float* DYs = PQs + BW_QT * RS;
+  float* PS = DYs + BW_QT * RS;
+  float* DS = PS + BW_KT * (BW_QT + 1);
+  float* DW = DS + BW_KT * (BW_QT + 1);
+  float* rowN = DW + BW_KT * (BW_QT + 1);
+  float* rowD = rowN + BW_QT;
+  int* kpos = reinterpret_cast<int*>(rowD + BW_QT);  // [KT]
+  __shared__ int tstart[BW_KT];
+  const int tid = threadIdx.x;
+  const int e0 = blockIdx.x * BW_KT, kv = blockIdx.y, b = blockIdx.z;
+  const int L = a.L, C = a.C;
+  const size_t unit = (size_t)b * a.Hkv + kv, krow0 = unit * L;
+  const int n_kept = pool_count_at(a.n_dec, a.lam, a.cap_chunks);
+  const int32_t* pool = a.sel + unit * (size_t)a.n_dec * a.lam;
+  if (tid < BW_KT) {
+    const int e = e0 + tid;
+    const int j = e < n_kept ? pool[e] : -1;
+    kpos[tid] = j;
+    tstart[tid] = j >= 0 ? (bw_band_last_chunk(j / C, a.W, C, a.T) + 1) * C : L;
+  }
+  __syncthreads();
+  bw_load_rows<T, D>(Ks, reinterpret_cast<const T*>(a.k) + krow0 * D, kpos, BW_KT);
+  bw_load_rows<T, D>(Vs, reinterpret_cast<const T*>(a.v) + krow0 * D, kpos, BW_KT);
+  int t_first = L;
+  for (int i = 0; i < BW_KT; ++i) t_first = min(t_first, tstart[i]);
+  t_first = t_first / BW_QT * BW_QT;
+  const int qi = tid >> 4, sub = tid & 15;
+  const int kk2 = tid >> 4, part = tid & 15;
+  float dka[DPT], dva[DPT];
+#pragma unroll
+  for (int cc = 0; cc < DPT; ++cc) dka[cc] = dva[cc] = 0.f;
+  for (int hl = 0; hl < a.G; ++hl) {
+    const int h = kv * a.G + hl;
+    const size_t qrow0 = ((size_t)b * a.Hq + h) * L;
+    for (int t0 = t_first; t0 < L; t0 += BW_QT) {
+      __syncthreads();
       for (int e = tid; e < BW_QT * D; e += BW_THREADS) {
         const int i = e / D, d = e % D, t = t0 + i;
         const bool in = t < L;
         Qs[i * RS + d] = in ? to_f32(reinterpret_cast<const T*>(a.q)[(qrow0 + t) * D + d]) : 0.f;
-        PQs[i * RS + d] = in ? a.phq[(qrow0 + t) * D + d] : 0.f;
         DYs[i * RS + d] = in ? a.dy[(qrow0 + t) * D + d] : 0.f;
       }
       if (tid < BW_QT) {
@@ -411,48 +731,42 @@ __global__ __launch_bounds__(BW_THREADS) void bw_key_kernel(BackwardArgs a) {
         rowD[tid] = t < L ? a.delta[qrow0 + t] : 0.f;
       }
       __syncthreads();
-      const int t = t0 + qi;
-      const float lnN = rowN[qi], dl = rowD[qi], rN = expf(-lnN);
+      const int t = t0 + qi, kk = sub;
+      float p = 0.f, ds = 0.f;
+      if (t < L && kpos[kk] >= 0 && t >= tstart[kk]) {
+        float s = 0.f, e = 0.f;
+        const float *q = Qs + qi * RS, *k = Ks + kk * RS, *dy = DYs + qi * RS, *v = Vs + kk * RS;
+        for (int d = 0; d < D; d += 4) {
+          const f32x4 qa = *reinterpret_cast<const f32x4*>(q + d), ka = *reinterpret_cast<const f32x4*>(k + d);
+          const f32x4 ya = *reinterpret_cast<const f32x4*>(dy + d), va = *reinterpret_cast<const f32x4*>(v + d);
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int kk = 2 * sub + u, j = j0 + kk;
-        float p = 0.f, ds = 0.f, dw = 0.f;
-        if (t < L && j < L && j <= t) {
-          float s, w, e;
-          bw_dots<D>(Qs + qi * RS, PQs + qi * RS, DYs + qi * RS, Ks + kk * RS, PKs + kk * RS, Vs + kk * RS, s,
-                     w, e);
-          if (bw_is_sa(t, j, a.W, a.C, kp[kk] != 0)) {
-            p = expf(a.scale * s - lnN);
-            ds = p * (e - dl);
-          } else {
-            p = g * w * rN;
-            dw = g * rN * (e - dl);
+          for (int i = 0; i < 4; ++i) {
+            s = fmaf(qa[i], ka[i], s);
+            e = fmaf(ya[i], va[i], e);
           }
         }
-        PS[kk * (BW_QT + 1) + qi] = p;
-        DS[kk * (BW_QT + 1) + qi] = ds;
-        DW[kk * (BW_QT + 1) + qi] = dw;
+        p = expf(a.scale * s - rowN[qi]);
+        ds = p * (e - rowD[qi]);
       }
+      PS[kk * (BW_QT + 1) + qi] = p;
+      DS[kk * (BW_QT + 1) + qi] = ds;
       __syncthreads();
-      // dk += ds q, d phi(k) += dw phi(q), dv += p dy over the tile's queries
       for (int i = 0; i < BW_QT; ++i) {
-        const float p = PS[kk2 * (BW_QT + 1) + i], ds = DS[kk2 * (BW_QT + 1) + i], dw = DW[kk2 * (BW_QT + 1) + i];
+        const float pp = PS[kk2 * (BW_QT + 1) + i], dd = DS[kk2 * (BW_QT + 1) + i];
 #pragma unroll
-        for (int c = 0; c < DPT; ++c) {
-          dka[c] = fmaf(ds, Qs[i * RS + part + 8 * c], dka[c]);
-          dpa[c] = fmaf(dw, PQs[i * RS + part + 8 * c], dpa[c]);
-          dva[c] = fmaf(p, DYs[i * RS + part + 8 * c], dva[c]);
+        for (int cc = 0; cc < DPT; ++cc) {
+          dka[cc] = fmaf(dd, Qs[i * RS + part + 16 * cc], dka[cc]);
+          dva[cc] = fmaf(pp, DYs[i * RS + part + 16 * cc], dva[cc]);
         }
       }
     }
   }
-  const int j = j0 + kk2;
-  if (j < L) {
+  const int j = kpos[kk2];
+  if (j >= 0) {
 #pragma unroll
-    for (int c = 0; c < DPT; ++c) {
-      a.dk[(krow0 + j) * D + part + 8 * c] = a.scale * dka[c];
-      a.dphk[(krow0 + j) * D + part + 8 * c] = dpa[c];
-      a.dv[(krow0 + j) * D + part + 8 * c] = dva[c];
+    for (int cc = 0; cc < DPT; ++cc) {
+      a.dk[(krow0 + j) * D + part + 16 * cc] += a.scale * dka[cc];
+      a.dv[(krow0 + j) * D + part + 16 * cc] += dva[cc];
     }
   }
 }
