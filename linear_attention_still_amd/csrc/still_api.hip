@@ -416,7 +416,9 @@ static int launch_backward(const Derived& d, const BwPlan& w, still::BackwardArg
   bw_key_kernel<T, D><<<dim3((L + BW_KT - 1) / BW_KT, d.Hkv, d.B), dim3(BW_THREADS), BwKLds<D>::bytes, s>>>(a);
   const int n_kept = pool_count_at(a.n_dec, a.lam, a.cap_chunks);
   if (n_kept > 0)
-    bw_pool_kernel<T, D><<<dim3((n_kept + BW_KT - 1) / BW_KT, d.Hkv, d.B), dim3(BW_THREADS), BwKLds<D>::bytes, s>>>(a);
+    bw_pool_kernel<T, D><<<dim3((n_kept + BW_KT - 1) / BW_KT, d.Hkv,
+                                d.B * d.G * ((L + BW_POOL_SEG - 1) / BW_POOL_SEG)),
+                           dim3(BW_THREADS), BwKLds<D>::bytes, s>>>(a);
   bw_npmap_kernel<T, D><<<rows_grid, dim3(BW_THREADS), BwRowLds<D>::bytes, s>>>(a);
   const int64_t nrow = (int64_t)d.B * (d.G + 1) * L;
   bw_dfmap_kernel<T, D><<<dim3((unsigned)((nrow + BW_DF_ROWS - 1) / BW_DF_ROWS), d.Hkv), dim3(BW_THREADS), 0, s>>>(a);

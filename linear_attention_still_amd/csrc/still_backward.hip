@@ -671,9 +671,11 @@ __global__ __launch_bounds__(BW_THREADS) void bw_key_kernel(BackwardArgs a) {
 }
 
 // 5. kept keys: one workgroup per (16 consecutive entries of the unit's
-// selection, kv head, batch row). Entry j (kept, chunk cj) is a softmax key
-// of every query of the chunks after bw_band_last_chunk(cj) (the band
-// pairs were taken by the key-side kernel); dk, dv of these pairs are added.
+// selection, kv head, (batch row, query head of the group, query segment)).
+// Entry j (kept, chunk cj) is a softmax key of every query of the chunks
+// after bw_band_last_chunk(cj) (the band pairs were taken by the key-side
+// kernel); each workgroup adds its segment's share of dk, dv atomically.
+constexpr int BW_POOL_SEG = 512;  // queries per segment
 template <typename T, int D>
 __global__ __launch_bounds__(BW_THREADS) void bw_pool_kernel(BackwardArgs a) {
   extern __shared__ __align__(16) char smem[];
@@ -692,8 +694,10 @@ __global__ __launch_bounds__(BW_THREADS) void bw_pool_kernel(BackwardArgs a) {
   int* kpos = reinterpret_cast<int*>(rowD + BW_QT);  // [KT]
   __shared__ int tstart[BW_KT];
   const int tid = threadIdx.x;
-  const int e0 = blockIdx.x * BW_KT, kv = blockIdx.y, b = blockIdx.z;
   const int L = a.L, C = a.C;
+  const int n_seg = (L + BW_POOL_SEG - 1) / BW_POOL_SEG;
+  const int e0 = blockIdx.x * BW_KT, kv = blockIdx.y;
+  const int seg = blockIdx.z % n_seg, hl = (blockIdx.z / n_seg) % a.G, b = blockIdx.z / (n_seg * a.G);
   const size_t unit = (size_t)b * a.Hkv + kv, krow0 = unit * L;
   const int n_kept = pool_count_at(a.n_dec, a.lam, a.cap_chunks);
   const int32_t* pool = a.sel + unit * (size_t)a.n_dec * a.lam;
@@ -708,32 +712,33 @@ __global__ __launch_bounds__(BW_THREADS) void bw_pool_kernel(BackwardArgs a) {
   bw_load_rows<T, D>(Vs, reinterpret_cast<const T*>(a.v) + krow0 * D, kpos, BW_KT);
   int t_first = L;
   for (int i = 0; i < BW_KT; ++i) t_first = min(t_first, tstart[i]);
-  t_first = t_first / BW_QT * BW_QT;
+  t_first = max(t_first / BW_QT * BW_QT, seg * BW_POOL_SEG);
+  const int t_last = min(L, (seg + 1) * BW_POOL_SEG);
   const int qi = tid >> 4, sub = tid & 15;
   const int kk2 = tid >> 4, part = tid & 15;
   float dka[DPT], dva[DPT];
 #pragma unroll
   for (int cc = 0; cc < DPT; ++cc) dka[cc] = dva[cc] = 0.f;
-  for (int hl = 0; hl < a.G; ++hl) {
+  {
     const int h = kv * a.G + hl;
     const size_t qrow0 = ((size_t)b * a.Hq + h) * L;
-    for (int t0 = t_first; t0 < L; t0 += BW_QT) {
+    for (int t0 = t_first; t0 < t_last; t0 += BW_QT) {
       __syncthreads();
       for (int e = tid; e < BW_QT * D; e += BW_THREADS) {
         const int i = e / D, d = e % D, t = t0 + i;
-        const bool in = t < L;
+        const bool in = t < t_last;
         Qs[i * RS + d] = in ? to_f32(reinterpret_cast<const T*>(a.q)[(qrow0 + t) * D + d]) : 0.f;
         DYs[i * RS + d] = in ? a.dy[(qrow0 + t) * D + d] : 0.f;
       }
       if (tid < BW_QT) {
         const int t = t0 + tid;
-        rowN[tid] = t < L ? a.lnN[qrow0 + t] : 0.f;
-        rowD[tid] = t < L ? a.delta[qrow0 + t] : 0.f;
+        rowN[tid] = t < t_last ? a.lnN[qrow0 + t] : 0.f;
+        rowD[tid] = t < t_last ? a.delta[qrow0 + t] : 0.f;
       }
       __syncthreads();
       const int t = t0 + qi, kk = sub;
       float p = 0.f, ds = 0.f;
-      if (t < L && kpos[kk] >= 0 && t >= tstart[kk]) {
+      if (t < t_last && kpos[kk] >= 0 && t >= tstart[kk]) {
         float s = 0.f, e = 0.f;
         const float *q = Qs + qi * RS, *k = Ks + kk * RS, *dy = DYs + qi * RS, *v = Vs + kk * RS;
         for (int d = 0; d < D; d += 4) {
@@ -762,11 +767,11 @@ __global__ __launch_bounds__(BW_THREADS) void bw_pool_kernel(BackwardArgs a) {
     }
   }
   const int j = kpos[kk2];
-  if (j >= 0) {
+  if (j >= 0 && t_first < t_last) {
 #pragma unroll
     for (int cc = 0; cc < DPT; ++cc) {
-      a.dk[(krow0 + j) * D + part + 16 * cc] += a.scale * dka[cc];
-      a.dv[(krow0 + j) * D + part + 16 * cc] += dva[cc];
+      atomicAdd(a.dk + (krow0 + j) * D + part + 16 * cc, a.scale * dka[cc]);
+      atomicAdd(a.dv + (krow0 + j) * D + part + 16 * cc, dva[cc]);
     }
   }
 }
