@@ -14,7 +14,8 @@ import pytest
 import torch
 
 from linear_attention_still_amd import still
-from linear_attention_still_amd.inputs import Workload, make_decode_tokens, make_inputs
+from linear_attention_still_amd.inputs import (Workload, make_decode_tokens, make_inputs,
+                                               make_route_scores)
 from oracle import rec
 from tests import _parity as P
 
@@ -39,7 +40,7 @@ def pack(rows, key):
     return torch.cat([r[key][0].reshape(-1) for r in rows]).cuda()
 
 
-def run_varlen(wl, rows, lens, fp32_out=False, flags=0):
+def run_varlen(wl, rows, lens, fp32_out=False, flags=0, ext=None):
     p = still.params_for(wl, fp32_out=fp32_out, flags=flags)
     lam = still.still_lambda(p)
     tot = sum(lens)
@@ -48,6 +49,8 @@ def run_varlen(wl, rows, lens, fp32_out=False, flags=0):
     out = torch.empty(tot * wl.n_q_heads * wl.head_dim, dtype=odt, device="cuda")
     sel = torch.empty(max(1, n_dec * wl.n_kv_heads * lam), dtype=torch.int32, device="cuda")
     score = torch.empty(tot * wl.n_kv_heads, dtype=torch.float32, device="cuda")
+    if ext is not None:  # the caller's routing scores, packed row after row
+        score.copy_(torch.cat([e.reshape(-1) for e in ext]))
     state = torch.zeros(still.still_state_bytes(p), dtype=torch.uint8, device="cuda")
     ws = torch.empty(still.still_workspace_bytes_varlen(p, lens), dtype=torch.uint8, device="cuda")
     print("  gpu varlen prefill %s lens=%s" % (wl.name, lens), flush=True)
@@ -195,3 +198,19 @@ def test_ragged_decode_wrong_row_position_sets_only_its_error_word():
     lay = still.still_state_layout_get(p)
     u = lay.unit_bytes  # row 1's unit: every byte before its meta words is unchanged
     assert torch.equal(state[u:u + lay.meta].cpu(), before[u:u + lay.meta].cpu())
+
+
+def test_varlen_with_caller_routing_and_sum_merge():
+    """Row-packed caller scores (random routing's draws) and the sum merge
+    go through the varlen entry unchanged: each row against the oracle."""
+    wl, lens = CASES[0]
+    rows = row_inputs(wl, lens)
+    one = dataclasses.replace(wl, batch=1)
+    ext = [make_route_scores(one, seq_len=L, seed=wl.seed + 7 * b) for b, L in enumerate(lens)]
+    flags = still.route_flag("external") | still.STILL_FLAG_MERGE_SUM
+    p, out, sel, score, state = run_varlen(wl, rows, lens, fp32_out=True, flags=flags, ext=ext)
+    for b, L in enumerate(lens):
+        wr = dataclasses.replace(wl, batch=1, seq_len=L)
+        o = P.oracle(wr, rows[b], merge="sum", route="external", ext_score=ext[b])
+        g = row_views(wl, p, lens, out, sel, score, state, b)
+        P.compare_prefill(wr, g, o, out_fp32=True)
