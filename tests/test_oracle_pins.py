@@ -523,3 +523,29 @@ def test_routes_recurrent_matches_brute_force(case, route):
     np.testing.assert_allclose(r["y"], a["y"].reshape(U, G, L, d), rtol=1e-11, atol=1e-12)
     np.testing.assert_allclose(r["S"], a["S"].reshape(U, d, d), rtol=1e-11, atol=1e-11)
     _check_selection(a, L, W, C, m)
+
+
+@pytest.mark.parametrize("W,C,L", [(5, 8, 70), (8, 8, 61), (20, 4, 45), (1, 16, 50)])
+def test_exported_state_plus_ring_is_last_query_linear_set(W, C, L):
+    """The exported state S, z (the unkept tokens of the chunks wholly before
+    every window of the last chunk) plus the decided, unkept, out-of-window
+    tokens after that boundary (kept explicitly in the recent-token ring) sum
+    to phi(k) v^T over B(L-1), the last query's linear set built by
+    key_sets; the boundary lies on a chunk start at or before the last
+    query's window, i.e. cf C <= L - W (for L > W) and cf C <= (c_last - 1) C."""
+    rng = np.random.default_rng(W * 100 + C + L)
+    q, k, v, F, g = rand_inputs(rng, 1, 2, 1, L, 8)
+    o = bf.prefill(q, k, v, F, g, window=W, chunk=C, budget=W + 3 * 4, t_max=4)
+    c_last = (L - 1) // C
+    cf = bf.full_chunks_out_of_window(c_last, W, C)
+    assert cf * C <= max(0, c_last * C - W + 1) and cf * C % C == 0
+    assert (cf + 1) * C > c_last * C - W + 1  # the largest such chunk boundary
+    _, Bm = bf.key_sets(L, W, C, o["sel"][0, 0].tolist())
+    lin = np.nonzero(Bm[L - 1])[0]
+    pk = phi_torch(k[0, 0], F[0])
+    ring = [j for j in lin if j >= cf * C]
+    want_S = pk[lin].T @ v[0, 0][lin]
+    got_S = o["S"][0, 0] + (pk[ring].T @ v[0, 0][ring] if ring else 0.0)
+    np.testing.assert_allclose(got_S, want_S, rtol=1e-11, atol=1e-11)
+    np.testing.assert_allclose(o["z"][0, 0] + pk[ring].sum(0), pk[lin].sum(0), rtol=1e-12, atol=1e-12)
+    assert all(j < cf * C for j in lin if j not in ring)
