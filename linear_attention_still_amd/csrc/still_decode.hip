@@ -554,9 +554,17 @@ void decode_kernel(DecodeArgs a) {
     return kk < n_oob ? pv_off + (uint32_t)kk * (D * sizeof(T))
                       : rv_off + (uint32_t)wrap(lo_slot + kk - n_oob) * (D * sizeof(T));
   };
+  // 16-bit data: PV on the matrix cores (v_mfma_f32_16x16x16_bf16: the
+  // weights, heads x 16 keys, are the A operand exactly in the lanes the
+  // logit product leaves them in; the B operand of value block (blk, par)
+  // holds, in lane (n, g), keys 4g .. 4g + 3 at dim 32 blk + 2 n + par, so
+  // one 4-byte load per (key, blk) serves both parities). float32 data:
+  // per-lane value columns on the vector ALUs.
+  static constexpr bool PV_MFMA = sizeof(T) == 2;
+  static constexpr int NVW = PV_MFMA ? 4 * (D / 32) : 16;
   struct TileRegs0 {
     Frag<T> af[D / 32];
-    uint32_t vw[16];
+    uint32_t vw[NVW];
   };
   TileRegs0 TA0;
 
@@ -568,11 +576,15 @@ void decode_kernel(DecodeArgs a) {
   //         log <phi(q), phi(k)> -------------------------------------------
   float* pwv = reinterpret_cast<float*>(smem + LD::pw) + wave * 17 * 8;  // [16 keys + al][8]
   float mh = STILL_NEG_INF, lh = 0.f;  // lanes r16 = h < G
-  float acc[G][DV];
+  float acc[PV_MFMA ? 1 : G][DV];  // float32 data: per head, this lane's value columns
+  f32x4 accm[PV_MFMA ? D / 32 : 1][2];  // 16-bit data: O[heads 4g + i][dim 32 blk + 2 r + par]
 #pragma unroll
-  for (int h = 0; h < G; ++h)
+  for (int h = 0; h < (PV_MFMA ? 1 : G); ++h)
 #pragma unroll
     for (int e = 0; e < DV; ++e) acc[h][e] = 0.f;
+#pragma unroll
+  for (int blk = 0; blk < (PV_MFMA ? D / 32 : 1); ++blk)
+    accm[blk][0] = accm[blk][1] = f32x4{0.f, 0.f, 0.f, 0.f};
   auto wave_sync = [] {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
@@ -609,13 +621,26 @@ void decode_kernel(DecodeArgs a) {
     const uint32_t koff = (kr_ < n ? krow(kr_) : oob) + 8 * g4 * sizeof(T);
 #pragma unroll
     for (int kb = 0; kb < D / 32; ++kb) X.af[kb] = ld_frag_buf<T>(st_r, koff, 32 * kb * sizeof(T));
-    const uint32_t voff = lane * DV * sizeof(T);
+    if constexpr (PV_MFMA) {
+      // keys 4g + i of the tile, dims 32 blk + 2 r, + 1 (4 bytes)
 #pragma unroll
-    for (int jj = 0; jj < 16; ++jj) {
-      const int kk = kk0 + jj;  // uniform
-      const uint32_t soff = __builtin_amdgcn_readfirstlane(kk < n ? vrow(kk) : oob);
-      if constexpr (DV * sizeof(T) == 4) X.vw[jj] = __builtin_amdgcn_raw_buffer_load_b32(st_r, voff, soff, 0);
-      else X.vw[jj] = __builtin_amdgcn_raw_buffer_load_b16(st_r, voff, soff, 0);
+      for (int i = 0; i < 4; ++i) {
+        const int kk = kk0 + 4 * g4 + i;
+        const uint32_t roff = kk < n ? vrow(kk) : oob;
+#pragma unroll
+        for (int blk = 0; blk < D / 32; ++blk)
+          X.vw[i * (D / 32) + blk] =
+              __builtin_amdgcn_raw_buffer_load_b32(st_r, roff + (32 * blk + 2 * r16) * sizeof(T), 0, 0);
+      }
+    } else {
+      const uint32_t voff = lane * DV * sizeof(T);
+#pragma unroll
+      for (int jj = 0; jj < 16; ++jj) {
+        const int kk = kk0 + jj;  // uniform
+        const uint32_t soff = __builtin_amdgcn_readfirstlane(kk < n ? vrow(kk) : oob);
+        if constexpr (DV * sizeof(T) == 4) X.vw[jj] = __builtin_amdgcn_raw_buffer_load_b32(st_r, voff, soff, 0);
+        else X.vw[jj] = __builtin_amdgcn_raw_buffer_load_b16(st_r, voff, soff, 0);
+      }
     }
   };
   // one tile: weight(c, kk) turns a product into a log-weight
@@ -672,32 +697,79 @@ void decode_kernel(DecodeArgs a) {
     ls += xor32f(ls);
     lh = lh * al + ls;
     mh = mn;
-    if (r16 < 8) {
+    if constexpr (PV_MFMA) {
+      // rescale factors of the O rows (heads 4g + i) from lanes r = head,
+      // only when some head's maximum moved (wave-uniform)
+      if (__builtin_amdgcn_ballot_w64(r16 < G && al != 1.f)) {
+        if (r16 < 8 && g4 == 0) pwv[128 + r16] = al;
+        wave_sync();
+        float ar[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) pwv[(4 * g4 + i) * 8 + r16] = c[i];
-      if (g4 == 0) pwv[128 + r16] = al;
-    }
-    wave_sync();
+        for (int i = 0; i < 4; ++i) ar[i] = 4 * g4 + i < G ? pwv[128 + 4 * g4 + i] : 0.f;
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      const float a_h = pwv[128 + h];
+        for (int blk = 0; blk < D / 32; ++blk)
 #pragma unroll
-      for (int e = 0; e < DV; ++e) acc[h][e] *= a_h;
-    }
+          for (int par = 0; par < 2; ++par)
 #pragma unroll
-    for (int jj = 0; jj < 16; ++jj) {
-      float v[DV];
-      const T* ve = reinterpret_cast<const T*>(&X.vw[jj]);
+            for (int i = 0; i < 4; ++i) accm[blk][par][i] *= ar[i];
+        wave_sync();  // the slot is written again by the next tile
+      }
+      // weights as bf16 hi (the top 16 bits) + lo (the remainder's top 16
+      // bits): ~16 significant bits; A operand: row = head r, keys 4g + i
+      typedef short s16x4 __attribute__((ext_vector_type(4)));
+      s16x4 ahi, alo;
 #pragma unroll
-      for (int e = 0; e < DV; ++e) v[e] = to_f32(ve[e]);
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t u = __float_as_uint(c[i]) & 0xFFFF0000u;
+        ahi[i] = (short)(u >> 16);
+        alo[i] = (short)(__float_as_uint(c[i] - __uint_as_float(u)) >> 16);
+      }
+#pragma unroll
+      for (int blk = 0; blk < D / 32; ++blk) {
+        const uint32_t w0 = X.vw[blk], w1 = X.vw[(D / 32) + blk];
+        const uint32_t w2 = X.vw[2 * (D / 32) + blk], w3 = X.vw[3 * (D / 32) + blk];
+#pragma unroll
+        for (int par = 0; par < 2; ++par) {
+          // keys 0..3 of the lane's group at dim 32 blk + 2 r + par
+          const uint32_t sel = par ? 0x07060302u : 0x05040100u;
+          const uint32_t b01 = __builtin_amdgcn_perm(w1, w0, sel), b23 = __builtin_amdgcn_perm(w3, w2, sel);
+          s16x4 bv;
+          bv[0] = (short)(b01 & 0xffffu);
+          bv[1] = (short)(b01 >> 16);
+          bv[2] = (short)(b23 & 0xffffu);
+          bv[3] = (short)(b23 >> 16);
+          accm[blk][par] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ahi, bv, accm[blk][par], 0, 0, 0);
+          accm[blk][par] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(alo, bv, accm[blk][par], 0, 0, 0);
+        }
+      }
+    } else {
+      if (r16 < 8) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) pwv[(4 * g4 + i) * 8 + r16] = c[i];
+        if (g4 == 0) pwv[128 + r16] = al;
+      }
+      wave_sync();
 #pragma unroll
       for (int h = 0; h < G; ++h) {
-        const float pj = pwv[jj * 8 + h];
+        const float a_h = pwv[128 + h];
 #pragma unroll
-        for (int e = 0; e < DV; ++e) acc[h][e] += pj * v[e];
+        for (int e = 0; e < DV; ++e) acc[h][e] *= a_h;
       }
+#pragma unroll
+      for (int jj = 0; jj < 16; ++jj) {
+        float v[DV];
+        const T* ve = reinterpret_cast<const T*>(&X.vw[jj]);
+#pragma unroll
+        for (int e = 0; e < DV; ++e) v[e] = to_f32(ve[e]);
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          const float pj = pwv[jj * 8 + h];
+#pragma unroll
+          for (int e = 0; e < DV; ++e) acc[h][e] += pj * v[e];
+        }
+      }
+      wave_sync();  // the slot is written again by the next tile
     }
-    wave_sync();  // the slot is written again by the next tile
   };
   // the tiles of wave w: w, w + waves, ...; two in flight
   auto run_tiles = [&](TileRegs& A, TileRegs& B, bool a_loaded, int n, auto krow, auto vrow,
@@ -815,10 +887,22 @@ void decode_kernel(DecodeArgs a) {
               sizeof(T) == 2 ? pb2 : (const Frag<T>*)nullptr, weight, INT_MAX);
   }
   // publish per wave: (m, l) per head from lanes r = h, the value slices
+  if constexpr (PV_MFMA) {
 #pragma unroll
-  for (int h = 0; h < G; ++h)
+    for (int blk = 0; blk < D / 32; ++blk)
 #pragma unroll
-    for (int e = 0; e < DV; ++e) redA[(wave * G + h) * D + lane * DV + e] = acc[h][e];
+      for (int par = 0; par < 2; ++par)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int h = 4 * g4 + i;
+          if (h < G) redA[(wave * G + h) * D + 32 * blk + 2 * r16 + par] = accm[blk][par][i];
+        }
+  } else {
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int e = 0; e < DV; ++e) redA[(wave * G + h) * D + lane * DV + e] = acc[h][e];
+  }
   if (g4 == 0 && r16 < G) {
     mlw[(wave * G + r16) * 2] = mh;
     mlw[(wave * G + r16) * 2 + 1] = lh;
