@@ -194,8 +194,12 @@ void set_prefill_attrs(int family) {
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)still::Blk<T, D>::bytes);
   (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&still::attend_kernel<T, D, 2, true>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)still::Blk<T, D>::bytes);
-  (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&still::state_delta_kernel<T, D>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)still::Blk<T, D>::bytes);
+  if constexpr (sizeof(T) == 2)
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&still::state_delta_kernel<T, D>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)still::SdLds<T, D>::bytes);
+  else
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&still::state_delta_f32_kernel<D>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)still::Blk<T, D>::bytes);
   g_attr_done[dev] |= 1ull << family;
 }
 
@@ -272,7 +276,10 @@ int launch_prefill(const Derived& d, const Plan& pl, still::PrefillArgs a, hipSt
   select_kernel<T, D><<<dim3(pl.n_pend + pl.n_dec, d.Hkv, d.B), dim3(256), lds_sel, s>>>(a);
   mk.at(2, 1);
   mk.at(3, 0);
-  state_delta_kernel<T, D><<<dim3(pl.NS, d.Hkv, d.B), dim3(512), Blk<T, D>::bytes, s>>>(a);
+  if constexpr (sizeof(T) == 2)
+    state_delta_kernel<T, D><<<dim3(pl.NS, d.Hkv, d.B), dim3(512), SdLds<T, D>::bytes, s>>>(a);
+  else
+    state_delta_f32_kernel<D><<<dim3(pl.NS, d.Hkv, d.B), dim3(512), Blk<T, D>::bytes, s>>>(a);
   mk.at(3, 1);
   mk.at(4, 0);
   state_scan_kernel<D><<<dim3((D * D + D + 255) / 256, d.Hkv, d.B), dim3(256), 0, s>>>(

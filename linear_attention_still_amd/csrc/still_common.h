@@ -406,10 +406,16 @@ template <>
 __device__ __forceinline__ f16 from_f32<f16>(float x) { return (f16)x; }
 
 // Cross-lane exchange on the VALU: DPP within a row of 16 lanes and the
-// gfx950 permlane swaps across rows, instead of LDS permutes.
+// gfx950 permlane swaps across rows, instead of LDS permutes. Every control
+// used here is a full permutation within a row (quad_perm, row_mirror,
+// row_half_mirror), so no source lane is out of range and bound_ctrl does
+// not change the result; with it set the compiler folds the move into the
+// consuming add (v_add_f32_dpp), one instruction per step instead of two.
 template <int CTRL>
 __device__ __forceinline__ float dppf(float x) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+  static_assert(CTRL == 0xB1 || CTRL == 0x4E || CTRL == 0x141 || CTRL == 0x140 || CTRL == 0x1B,
+                "full in-row permutations only");
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xF, 0xF, true));
 }
 // value of lane ^ 16
 __device__ __forceinline__ float xor16f(float x) {

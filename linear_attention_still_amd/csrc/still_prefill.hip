@@ -1335,8 +1335,12 @@ __device__ __forceinline__ void big_key_fold(const BlkPtr<T, D>& P, const BigScr
   }
 }
 
-template <typename T, int D>
-__global__ __launch_bounds__(512) void state_delta_kernel(PrefillArgs a) {
+// float32 data: in blocks of 64 keys through the attention kernel's block
+// helpers (features of feature tile w by wave w, per-key statistics combined
+// across the waves through LDS).
+template <int D>
+__global__ __launch_bounds__(512) void state_delta_f32_kernel(PrefillArgs a) {
+  using T = float;
   using B_ = Blk<T, D>;
   extern __shared__ __align__(16) char smem[];
   const BlkPtr<T, D> P(smem);
@@ -1397,6 +1401,373 @@ __global__ __launch_bounds__(512) void state_delta_kernel(PrefillArgs a) {
     }
     if (g4 == 0) dst[D * D + 16 * wave + r16] = (float)zsum;
   }
+}
+
+// 16-bit data: blocks of SD_BK = 128 keys (eight 16-key tiles), one
+// workgroup of 8 waves per super-chunk.
+//  * Wave w computes phi(k) of key tile w over all D features (X F by MFMA
+//    with the features on the lanes): a key's softmax statistics then reduce
+//    over the wave's own registers and the 16 lanes of a row, with no
+//    exchange between waves. Keys that do not fold (kept, past the range,
+//    or large, see below) get zero features. The features go to LDS
+//    feature-major in float32.
+//  * Wave w then folds feature tile w % (D/16) against the block's values
+//    for its d_v tiles: phi as fp16 hi + lo parts (~22 significant bits),
+//    values exact in fp16; the block's float32 sums are added to float64
+//    ones.
+//  * Large keys (|k|^2 max|v| >= BIG_KV, a few per block) take the float64
+//    path: logits split over all threads (each D / (512 / D) products),
+//    NP-Map and rank-1 update, in rounds of up to SD_NBK keys with two
+//    barriers per round.
+constexpr int SD_BK = 128;
+constexpr int SD_NBK = 8;
+
+template <typename T, int D>
+struct SdLds {
+  static constexpr int VS = D + 8;       // value row (fp16 elements)
+  static constexpr int PS = SD_BK + 4;   // feature row (floats)
+  static constexpr size_t ft_bytes = (size_t)D * D * sizeof(T);
+  static constexpr size_t v_bytes = (size_t)SD_BK * VS * 2;
+  static constexpr size_t ph_bytes = (size_t)D * PS * 4;
+  static constexpr size_t vmx_bytes = SD_BK * 4;
+  static constexpr size_t bits_bytes = 32;
+  static constexpr size_t bst_bytes = (size_t)SD_NBK * (8 * 2 + 1) * 8;
+  static constexpr size_t bphi_bytes = (size_t)SD_NBK * D * 8;
+  static constexpr size_t krow_bytes = (size_t)16 * D * sizeof(T);  // two large-key rows per wave
+  static constexpr size_t kn2_bytes = (size_t)SD_BK * 8;              // float64 |k|^2 of large keys
+  static constexpr size_t bytes =
+      ft_bytes + v_bytes + ph_bytes + vmx_bytes + bits_bytes + bst_bytes + bphi_bytes + krow_bytes + kn2_bytes;
+  static_assert(bytes <= 160 * 1024, "one workgroup's LDS");
+};
+
+// acc + sum of squares of a bf16 fragment, by packed bf16 dot products
+__device__ __forceinline__ float frag_dot2_sumsq(const Frag<bf16>& f, float acc) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const bf16x2_t p = {f.v[2 * i], f.v[2 * i + 1]};
+    acc = __builtin_amdgcn_fdot2_f32_bf16(p, p, acc, false);
+  }
+  return acc;
+}
+
+// sum over groups of N consecutive lanes (N = 4 or 8), float64
+template <int N>
+__device__ __forceinline__ double group_sum_d(double x) {
+  x += dppd<0xB1>(x);
+  x += dppd<0x4E>(x);
+  if constexpr (N >= 8) x += dppd<0x141>(x);
+  static_assert(N == 4 || N == 8, "groups of 4 or 8 lanes");
+  return x;
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(512) void state_delta_kernel(PrefillArgs a) {
+  static_assert(sizeof(T) == 2, "16-bit data");
+  using L_ = SdLds<T, D>;
+  constexpr int NFT = D / 16;            // feature (and d_v) tiles
+  constexpr int VPW = NFT * NFT / 8;     // d_v tiles folded per wave
+  constexpr int CPR = D / 8;             // 16-byte chunks per row
+  constexpr int VIT = SD_BK * CPR / 512; // value chunks per thread
+  constexpr int NP = 512 / D;            // threads per float64 logit
+  constexpr int TPP = D / NP;            // products per thread
+  extern __shared__ __align__(16) char smem[];
+  T* FT = lds_opaque(reinterpret_cast<T*>(smem));
+  f16* VR = lds_opaque(reinterpret_cast<f16*>(smem + L_::ft_bytes));
+  float* PH = lds_opaque(reinterpret_cast<float*>(smem + L_::ft_bytes + L_::v_bytes));
+  char* misc = smem + L_::ft_bytes + L_::v_bytes + L_::ph_bytes;
+  float* vmx = lds_opaque(reinterpret_cast<float*>(misc));
+  uint32_t* bigw = lds_opaque(reinterpret_cast<uint32_t*>(misc + L_::vmx_bytes));
+  double* bst = lds_opaque(reinterpret_cast<double*>(misc + L_::vmx_bytes + L_::bits_bytes));
+  double* bk2 = bst + SD_NBK * 16;
+  double* bphi = lds_opaque(reinterpret_cast<double*>(misc + L_::vmx_bytes + L_::bits_bytes + L_::bst_bytes));
+  T* krows = lds_opaque(reinterpret_cast<T*>(misc + L_::vmx_bytes + L_::bits_bytes + L_::bst_bytes + L_::bphi_bytes));
+  double* kn2d = lds_opaque(
+      reinterpret_cast<double*>(misc + L_::vmx_bytes + L_::bits_bytes + L_::bst_bytes + L_::bphi_bytes + L_::krow_bytes));
+
+  const int s = blockIdx.x, kv = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, r16 = lane & 15, g4 = lane >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int unit = b * a.Hkv + kv;
+  const uint32_t kv_bytes = (uint32_t)((size_t)a.L * D * sizeof(T));
+  const __amdgpu_buffer_rsrc_t kr = make_rsrc(reinterpret_cast<const T*>(a.k) + (size_t)unit * a.L * D, kv_bytes);
+  const __amdgpu_buffer_rsrc_t vr = make_rsrc(reinterpret_cast<const T*>(a.v) + (size_t)unit * a.L * D, kv_bytes);
+  const __amdgpu_buffer_rsrc_t sfr = make_rsrc(a.selflag + (size_t)unit * a.L, (uint32_t)a.L);
+  {
+    const uint4* src = reinterpret_cast<const uint4*>(reinterpret_cast<const T*>(a.ft) + (size_t)kv * D * D);
+    for (int e = tid; e < (int)(L_::ft_bytes / 16); e += 512) reinterpret_cast<uint4*>(FT)[e] = src[e];
+  }
+  const int lo = full_chunks_before(s * a.K, a.W, a.C) * a.C;
+  const int hi = (s == a.NS - 1 ? full_chunks_before(a.T - 1, a.W, a.C)
+                                : full_chunks_before(s * a.K + a.K, a.W, a.C)) * a.C;
+  // fold ownership: feature tile ft, d_v tiles vt0 .. vt0 + VPW - 1
+  const int ft = wave % NFT, vt0 = (wave / NFT) * VPW;
+  double sum[VPW][4];
+#pragma unroll
+  for (int v = 0; v < VPW; ++v)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sum[v][i] = 0.0;
+  double zsum = 0.0;
+
+  // loads of a block: wave w's key tile as MFMA A fragments (row r16), its
+  // keys' kept flags, and the values (every thread VIT row chunks); rows at
+  // or past hi read zeros (keys) or are not folded
+  Frag<T> kn[D / 32];
+  int sn;
+  uint4 vn[VIT];
+  auto issue = [&](int blo) __attribute__((always_inline)) {
+    const int row = blo + 16 * wave + r16;
+    const uint32_t off = row < hi ? (uint32_t)((size_t)row * D * sizeof(T)) : kv_bytes;
+#pragma unroll
+    for (int kb = 0; kb < D / 32; ++kb) kn[kb] = ld_frag_buf<T>(kr, off + 8 * g4 * sizeof(T), 32 * kb * sizeof(T));
+    sn = (int)__builtin_amdgcn_raw_buffer_load_b8(sfr, row < hi ? (uint32_t)row : 0xffffffffu, 0, 0);
+#pragma unroll
+    for (int it = 0; it < VIT; ++it) {
+      const int idx = tid + it * 512, vrow = blo + idx / CPR;
+      vn[it] = ld_u4_buf(vr, vrow < hi ? (uint32_t)(((size_t)vrow * D + (idx % CPR) * 8) * sizeof(T)) : kv_bytes, 0);
+    }
+  };
+  if (lo < hi) issue(lo);
+  for (int blo = lo; blo < hi; blo += SD_BK) {
+    __syncthreads();  // the previous block's fold and large keys are done with VR, PH
+    // values as fp16, row-major, and each key's largest |v|
+#pragma unroll
+    for (int it = 0; it < VIT; ++it) {
+      const int idx = tid + it * 512, row = idx / CPR, col = (idx % CPR) * 8;
+      const T* ve = reinterpret_cast<const T*>(&vn[it]);
+      f16 w[8];
+      float m = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float x = to_f32(ve[e]);
+        w[e] = (f16)x;
+        m = fmaxf(m, fabsf(x));
+      }
+      *reinterpret_cast<uint4*>(VR + row * L_::VS + col) = *reinterpret_cast<uint4*>(w);
+      m = row_max<CPR>(m);
+      if (col == 0) vmx[row] = m;
+    }
+    Frag<T> kc[D / 32];
+#pragma unroll
+    for (int kb = 0; kb < D / 32; ++kb) kc[kb] = kn[kb];
+    const int sc = sn;
+    if (blo + SD_BK < hi) issue(blo + SD_BK);
+    __syncthreads();  // VR, vmx
+
+    // phi of key tile `wave`: ph[f][i] = logit of key 4g + i, feature 16 f + r
+    {
+      f32x4 ph[NFT];
+#pragma unroll
+      for (int f = 0; f < NFT; ++f) {
+        ph[f] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < D / 32; ++kb)
+          mma(ph[f], kc[kb], ld_frag(FT + ((size_t)(f * (D / 32) + kb) * 64 + lane) * 8));
+      }
+      lds_mfma_pipeline<2 * (D / 32), (NFT - 2) * (D / 32), 1, 1, 2 * (D / 32)>();
+      // |k|^2 of key r16 (every g; packed bf16 dot products), and whether
+      // it folds / is large
+      float n2 = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < D / 32; ++kb) n2 = frag_dot2_sumsq(kc[kb], n2);
+      n2 = sum_over_g(n2);
+      const int row = blo + 16 * wave + r16;
+      const bool fold = row < hi && sc == 0;
+      const bool big = fold && n2 * vmx[16 * wave + r16] >= BIG_KV;
+      const uint32_t use16 = (uint32_t)__builtin_amdgcn_ballot_w64(fold && !big) & 0xffffu;
+      const uint32_t big16 = (uint32_t)__builtin_amdgcn_ballot_w64(big) & 0xffffu;
+      if (lane == 0) bigw[wave] = big16;
+      // the rows of the tile's first two large keys and their float64
+      // |k|^2, for the float64 path
+      if (big16) {  // uniform
+        double d2 = 0.0;
+#pragma unroll
+        for (int kb = 0; kb < D / 32; ++kb)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const double x = (double)to_f32(kc[kb].v[e]);
+            d2 += x * x;
+          }
+        d2 += xor16d(d2);
+        d2 += xor32d(d2);
+        const int q = __builtin_popcount(big16 & ((1u << r16) - 1u));
+        if (big && q < 2) {
+#pragma unroll
+          for (int kb = 0; kb < D / 32; ++kb) st_frag(krows + (2 * wave + q) * D + 32 * kb + 8 * g4, kc[kb]);
+        }
+        if (big && g4 == 0) kn2d[16 * wave + r16] = d2;
+      }
+      // softmax over the features in base 2 (exp2(x log2 e - m log2 e): the
+      // offset's rounding is common to a key's features and cancels in the
+      // normalisation), the factor |k| / sqrt(sum e^2) from the hardware
+      // square root and reciprocal square root (~1 ulp each)
+      float nm[4], ss[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float m = ph[0][i];
+#pragma unroll
+        for (int f = 1; f < NFT; ++f) m = fmax_nn(m, ph[f][i]);
+        nm[i] = -row_max<16>(m) * STILL_LOG2E;
+        ss[i] = 0.f;
+      }
+#pragma unroll
+      for (int f = 0; f < NFT; ++f)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float e = __builtin_amdgcn_exp2f(fmaf(ph[f][i], STILL_LOG2E, nm[i]));
+          ph[f][i] = e;
+          ss[i] = fmaf(e, e, ss[i]);
+        }
+      float fac[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float s2 = row_sum<16>(ss[i]);
+        const float k2 = __shfl(n2, 4 * g4 + i);
+        fac[i] = ((use16 >> (4 * g4 + i)) & 1u) ? __builtin_amdgcn_sqrtf(k2) * __builtin_amdgcn_rsqf(s2) : 0.f;
+      }
+#pragma unroll
+      for (int f = 0; f < NFT; ++f) {
+        const f32x4 o = {ph[f][0] * fac[0], ph[f][1] * fac[1], ph[f][2] * fac[2], ph[f][3] * fac[3]};
+        *reinterpret_cast<f32x4*>(PH + (16 * f + r16) * L_::PS + 16 * wave + 4 * g4) = o;
+      }
+    }
+    __syncthreads();  // PH, bigw
+
+    // fold: S[16 ft + 4g + i][16 vt + r] over the block's keys
+    {
+      f32x4 acc[VPW];
+#pragma unroll
+      for (int v = 0; v < VPW; ++v) acc[v] = f32x4{0.f, 0.f, 0.f, 0.f};
+      float zl = 0.f;
+#pragma unroll
+      for (int kb2 = 0; kb2 < SD_BK / 32; ++kb2) {
+        const float* pr = PH + (16 * ft + r16) * L_::PS + 32 * kb2 + 4 * g4;
+        const f32x4 x0 = *reinterpret_cast<const f32x4*>(pr);
+        const f32x4 x1 = *reinterpret_cast<const f32x4*>(pr + 16);
+        zl += ((x0[0] + x0[1]) + (x0[2] + x0[3])) + ((x1[0] + x1[1]) + (x1[2] + x1[3]));
+        Frag<f16> fh, fl;
+        split2_frag<f16>(x0, x1, fh, fl);
+#pragma unroll
+        for (int v = 0; v < VPW; ++v) {
+          const Frag<f16> bv =
+              tr_frag(VR + (32 * kb2 + 4 * g4 + (r16 >> 2)) * L_::VS + 16 * (vt0 + v) + 4 * (r16 & 3), 16 * L_::VS);
+          mma(acc[v], fh, bv);
+          mma(acc[v], fl, bv);
+        }
+      }
+#pragma unroll
+      for (int v = 0; v < VPW; ++v)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sum[v][i] += (double)acc[v][i];
+      if (vt0 == 0) zsum += (double)sum_over_g(zl);
+    }
+
+    // large keys, float64, in rounds of up to SD_NBK
+    uint64_t bl = 0, bh = 0;  // the block's large keys (uniform)
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      bl |= (uint64_t)bigw[w] << (16 * w);
+      bh |= (uint64_t)bigw[4 + w] << (16 * w);
+    }
+    while (bl | bh) {
+      // this round: the first SD_NBK of them (masks rl, rh; key n of the
+      // round is the n-th set bit)
+      uint64_t rl = 0, rh = 0;
+      int nb = 0;
+      for (; nb < SD_NBK && (bl | bh); ++nb) {
+        if (bl) {
+          rl |= bl & (~bl + 1);
+          bl &= bl - 1;
+        } else {
+          rh |= bh & (~bh + 1);
+          bh &= bh - 1;
+        }
+      }
+      auto next_key = [](uint64_t& ml, uint64_t& mh) {
+        int k;
+        if (ml) {
+          k = __builtin_ctzll(ml);
+          ml &= ml - 1;
+        } else {
+          k = 64 + __builtin_ctzll(mh);
+          mh &= mh - 1;
+        }
+        return k;
+      };
+      // logits: thread (j, part) sums TPP products of feature j, the NP
+      // threads of a feature are consecutive lanes; the logit goes to bphi
+      // (turned into the feature after the barrier), the wave's maximum
+      // and sum of exp(2 (u - m)) over its features to bst, |k|^2 to bk2
+      const int j = tid / NP, part = tid % NP;
+      uint64_t ml = rl, mh = rh;
+#pragma unroll 1
+      for (int n = 0; n < nb; ++n) {
+        const int kk = next_key(ml, mh), wo = kk >> 4;
+        const int slot = __builtin_popcount(bigw[wo] & ((1u << (kk & 15)) - 1u));  // uniform
+        const T* krow = krows + (2 * wo + slot) * D;
+        const int row = blo + kk;
+        double u = 0.0;
+#pragma unroll
+        for (int q = 0; q < TPP / 8; ++q) {
+          const int i0 = part * TPP + 8 * q;
+          const uint4 k8 = slot < 2 ? *reinterpret_cast<const uint4*>(krow + i0)
+                                    : ld_u4_buf(kr, (uint32_t)(((size_t)row * D + i0) * sizeof(T)), 0);
+          const T* ke = reinterpret_cast<const T*>(&k8);
+          const Frag<T> f8 =
+              ld_frag(FT + ((size_t)(((j >> 4) * (D / 32) + (i0 >> 5)) * 64) + 16 * ((i0 & 31) >> 3) + (j & 15)) * 8);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) u += (double)to_f32(ke[e]) * (double)to_f32(f8.v[e]);
+        }
+        u = group_sum_d<NP>(u);
+        const double m = wave_max_d(u);
+        const double se = wave_sum_d(part == 0 ? exp(2.0 * (u - m)) : 0.0);
+        if (part == 0) bphi[n * D + j] = u;
+        if (lane == 0) {
+          bst[(n * 8 + wave) * 2] = m;
+          bst[(n * 8 + wave) * 2 + 1] = se;
+          if (wave == 0) bk2[n] = kn2d[kk];
+        }
+      }
+      __syncthreads();
+      // the key's maximum M over the waves' maxima and S = sum of
+      // exp(2 (u - M)): lane w < 8 rescales wave w's sum, a sum over the
+      // row's 8 lanes and a broadcast give S; then phi_j (one exponential
+      // per lane)
+#pragma unroll 1
+      for (int n = 0; n < nb; ++n) {
+        const int w8 = lane & 7;
+        const double mw = bst[(n * 8 + w8) * 2];
+        double M = mw;
+        M = fmax(M, dppd<0xB1>(M));
+        M = fmax(M, dppd<0x4E>(M));
+        M = fmax(M, dppd<0x141>(M));
+        const double S = group_sum_d<8>(bst[(n * 8 + w8) * 2 + 1] * exp(2.0 * (mw - M)));
+        if (part == 0) bphi[n * D + j] = sqrt(bk2[n]) * exp(bphi[n * D + j] - M) / sqrt(S);
+      }
+      __syncthreads();
+      ml = rl;
+      mh = rh;
+#pragma unroll 1
+      for (int n = 0; n < nb; ++n) {
+        const f16* vrow = VR + next_key(ml, mh) * L_::VS;
+#pragma unroll
+        for (int v = 0; v < VPW; ++v) {
+          const double vv = (double)(float)vrow[16 * (vt0 + v) + r16];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) sum[v][i] += bphi[n * D + 16 * ft + 4 * g4 + i] * vv;
+        }
+        if (vt0 == 0) zsum += bphi[n * D + 16 * ft + r16];
+      }
+    }
+  }
+  float* dst = a.dS + ((size_t)unit * a.NS + s) * (D * D + D);
+#pragma unroll
+  for (int v = 0; v < VPW; ++v) {
+    const int vt = vt0 + v;
+    const f32x4 o = {(float)sum[v][0], (float)sum[v][1], (float)sum[v][2], (float)sum[v][3]};
+    *reinterpret_cast<f32x4*>(dst + ((size_t)(2 * (vt * (D / 32) + (ft >> 1)) + (ft & 1)) * 64 + lane) * 4) = o;
+  }
+  if (vt0 == 0 && g4 == 0) dst[D * D + 16 * ft + r16] = (float)zsum;
 }
 
 // ----------------------------------------------------- 5. state_scan ----

@@ -139,10 +139,18 @@ def test_prefill_launch_variants_agree(env, monkeypatch):
         for k in ("y", "S", "z"):
             assert torch.equal(a[k], b[k]), k
     else:
+        # float32-level differences in the state can move a bf16 output
+        # across a rounding boundary: one bf16 step (at most 2^-7 of the
+        # value) per element on top of the float32-level bar
         for k in ("y", "S", "z"):
-            d = (a[k].float() - b[k].float()).abs().max().item()
-            ref = a[k].float().abs().max().item()
-            assert d <= 1e-5 * max(ref, 1.0) + (2e-2 if k == "y" else 0.0), (k, d)
+            af, bf = a[k].float(), b[k].float()
+            ref = af.abs().max().item()
+            tol = 1e-5 * max(ref, 1.0)
+            if k == "y" and a[k].dtype == torch.bfloat16:
+                excess = ((af - bf).abs() - 2.0 ** -7 * af.abs()).max().item()
+            else:
+                excess = (af - bf).abs().max().item()
+            assert excess <= tol, (k, excess)
 
 
 DECODE_SHAPES = [
