@@ -282,8 +282,15 @@ int launch_prefill(const Derived& d, const Plan& pl, still::PrefillArgs a, hipSt
     state_delta_f32_kernel<D><<<dim3(pl.NS, d.Hkv, d.B), dim3(512), Blk<T, D>::bytes, s>>>(a);
   mk.at(3, 1);
   mk.at(4, 0);
-  state_scan_kernel<D><<<dim3((D * D + D + 255) / 256, d.Hkv, d.B), dim3(256), 0, s>>>(
-      a.dS, pl.NS, a.state, a.st_unit, a.st_S, a.st_z);
+  // the scan and, as further workgroups of the same launch, the decode-state
+  // export (its events are recorded back to back)
+  const int n_scan = (D * D + D + 255) / 256;
+  const int ring_lo = pl.L - d.R > 0 ? pl.L - d.R : 0;
+  const int n_ring_grp = (pl.L - ring_lo + 63) / 64;
+  const int n_pool = pool_count_at(pl.n_dec, d.lam, d.cap_chunks);
+  const int n_pool_grp = n_pool > 0 ? (n_pool + 15) / 16 : 1;  // >= 1: it writes the position
+  state_scan_kernel<T, D><<<dim3(n_scan + n_ring_grp + n_pool_grp, d.Hkv, d.B), dim3(256), Blk<T, D>::ft_bytes, s>>>(
+      a, n_scan);
   mk.at(4, 1);
   mk.at(5, 0);
   if (pl.part)
@@ -293,12 +300,7 @@ int launch_prefill(const Derived& d, const Plan& pl, still::PrefillArgs a, hipSt
   else
     attend_kernel<T, D, 1><<<dim3(pl.NS * d.Hkv * pl.nHG * d.B), dim3(512), Blk<T, D>::bytes, s>>>(a);
   mk.at(5, 1);
-  const int ring_lo = pl.L - d.R > 0 ? pl.L - d.R : 0;
-  const int n_ring_grp = (pl.L - ring_lo + 63) / 64;
-  const int n_pool = pool_count_at(pl.n_dec, d.lam, d.cap_chunks);
-  const int n_pool_grp = n_pool > 0 ? (n_pool + 15) / 16 : 1;  // >= 1: it writes the position
   mk.at(6, 0);
-  export_kernel<T, D><<<dim3(n_ring_grp + n_pool_grp, d.Hkv, d.B), dim3(256), Blk<T, D>::ft_bytes, s>>>(a);
   mk.at(6, 1);
   return hipGetLastError() == hipSuccess ? STILL_OK : STILL_EHIP;
 }

@@ -26,6 +26,8 @@
 //                       the state and the not-yet-folded band, one softmax-
 //                       style normaliser over both, then fold the next chunk
 //   7. export           decode state: kept pool, recent-token ring, position
+//                       (extra workgroups of the scan launch: it needs only
+//                       the selection and the inputs)
 #include "still_common.h"
 
 namespace still {
@@ -1774,11 +1776,13 @@ __global__ __launch_bounds__(512) void state_delta_kernel(PrefillArgs a) {
 // Exclusive prefix over the super-chunk deltas, in place (the starting state
 // of every super-chunk), and their total, the exported state S (row-major)
 // and z, each rounded to float32 once from a float64 running sum.
+// Part bx of the scan for unit (blockIdx.y, blockIdx.z): 256 of the D*D + D
+// state entries.
 template <int D>
-__global__ __launch_bounds__(256) void state_scan_kernel(float* dS, int NS, char* state, long st_unit,
-                                                         long st_S, long st_z) {
+__device__ __forceinline__ void state_scan_part(int bx, float* dS, int NS, char* state, long st_unit, long st_S,
+                                                long st_z) {
   constexpr int n_elem = D * D + D;
-  const int e = blockIdx.x * 256 + threadIdx.x;
+  const int e = bx * 256 + threadIdx.x;
   if (e >= n_elem) return;
   const int unit = blockIdx.y + gridDim.y * blockIdx.z;
   float* base = dS + (size_t)unit * NS * n_elem + e;
@@ -1807,6 +1811,20 @@ __global__ __launch_bounds__(256) void state_scan_kernel(float* dS, int NS, char
   } else {
     reinterpret_cast<float*>(st + st_z)[e - D * D] = (float)run;
   }
+}
+
+// The scan (workgroups x < n_scan) and the decode-state export (the rest,
+// x - n_scan as the export's workgroup index) in one launch: the export
+// depends only on the selection and the inputs, so it runs beside the scan
+// instead of after the attention walk.
+template <typename T, int D>
+__device__ void export_part(const PrefillArgs& a, int x);
+template <typename T, int D>
+__global__ __launch_bounds__(256) void state_scan_kernel(PrefillArgs a, int n_scan) {
+  if ((int)blockIdx.x < n_scan)
+    state_scan_part<D>((int)blockIdx.x, a.dS, a.NS, a.state, a.st_unit, a.st_S, a.st_z);
+  else
+    export_part<T, D>(a, (int)blockIdx.x - n_scan);
 }
 
 // ---------------------------------------------------------- 6. attend ----
@@ -2348,11 +2366,12 @@ __global__ __launch_bounds__(512) void attend_kernel(PrefillArgs a) {
 
 // ---------------------------------------------------------- 7. export ----
 // Decode state after the prefill: ring slots of the last R positions (keys,
-// values, NP-Map features, kept flags), the kept pool, and the position.
+// values, NP-Map features, kept flags), the kept pool, and the position
+// (workgroups of the scan launch, see state_scan_kernel).
 template <typename T, int D>
-__global__ __launch_bounds__(256) void export_kernel(PrefillArgs a) {
+__device__ void export_part(const PrefillArgs& a, int x) {
   extern __shared__ __align__(16) char smem[];
-  const int x = blockIdx.x, kv = blockIdx.y, b = blockIdx.z;
+  const int kv = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, L = a.L, R = a.R;
   const int unit = b * a.Hkv + kv;
   char* st = a.state + (size_t)unit * a.st_unit;
