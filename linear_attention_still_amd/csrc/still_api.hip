@@ -214,6 +214,18 @@ void set_decode_attr(int family) {
   g_attr_done[dev] |= 1ull << family;
 }
 
+// the chunk-boundary decode kernel (its fold's LDS passes 64 KiB at d = 128)
+template <typename T, int D>
+void set_boundary_attr(int family) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) dev = 0;
+  std::lock_guard<std::mutex> lk(g_attr_mu);
+  if (g_attr_done[dev] & (1ull << family)) return;
+  (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&still::decode_boundary_kernel<T, D>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+  g_attr_done[dev] |= 1ull << family;
+}
+
 // kernel family index of (element type, head dim[, group]) for the table
 template <typename T, int D>
 constexpr int prefill_family() { return (sizeof(T) == 4 ? 0 : 1) * 2 + (D == 128 ? 1 : 0); }
@@ -319,7 +331,11 @@ template <typename T, int D>
 int launch_decode(const Derived& d, still::DecodeArgs a, hipStream_t s) {
   using namespace still;
   if (a.boundary || a.pos) {  // per-row positions: every row's workgroups look
-    const size_t lds = DecLds<T, D, 1>::uni + DecLds<T, D, 1>::fold_bytes;
+    // the fold's LDS: the float32 path's row groups, or the matrix-core
+    // path's F, value block and features (16-bit data)
+    const size_t fold = sizeof(T) == 2 ? BndFoldLds<D>::bytes : DecLds<T, D, 1>::fold_bytes;
+    const size_t lds = DecLds<T, D, 1>::uni + fold;
+    set_boundary_attr<T, D>(24 + prefill_family<T, D>());
     decode_boundary_kernel<T, D><<<dim3(d.Hkv, d.B), dim3(BND_THREADS), lds, s>>>(a);
     if (hipGetLastError() != hipSuccess) return STILL_EHIP;
   }

@@ -127,6 +127,15 @@ __device__ __forceinline__ Frag<f16> tr_frag(const f16* p, int step) {
   return f;
 }
 
+// The same read for bf16 data (the transposing read moves 16-bit values,
+// whatever their type).
+__device__ __forceinline__ Frag<bf16> tr_frag_bf16(const bf16* p, int step) {
+  const Frag<f16> f = tr_frag(reinterpret_cast<const f16*>(p), step);
+  Frag<bf16> r;
+  r.v = __builtin_bit_cast(bf16x8, f.v);
+  return r;
+}
+
 // Buffer-resource loads: the lane-dependent part of an address is a 32-bit
 // VGPR offset and the uniform part an SGPR offset, so unrolled loops over
 // uniform offsets need no per-iteration 64-bit address registers. Reads at
@@ -364,6 +373,17 @@ __device__ __forceinline__ float frag_sumsq<float>(const Frag<float>& f) {
   float s = 0.f;
   for (int i = 0; i < 4; ++i) s += f.lo[i] * f.lo[i] + f.hi[i] * f.hi[i];
   return s;
+}
+
+// acc + sum of squares of a bf16 fragment, by packed bf16 dot products
+__device__ __forceinline__ float frag_dot2_sumsq(const Frag<bf16>& f, float acc) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const bf16x2_t p = {f.v[2 * i], f.v[2 * i + 1]};
+    acc = __builtin_amdgcn_fdot2_f32_bf16(p, p, acc, false);
+  }
+  return acc;
 }
 
 __device__ __forceinline__ float frag_sum(const Frag<bf16>& f) {

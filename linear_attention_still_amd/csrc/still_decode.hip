@@ -240,6 +240,159 @@ __device__ __forceinline__ void np_map_vec(const FRows<T, D, NT>& FR_, const flo
   __syncthreads();
 }
 
+// Fold of the ring rows [f_lo, f_hi) that are not kept into S, z for 16-bit
+// data, on the matrix cores, in blocks of BFB = 32 keys [P3 "NP-Map:
+// Norm-Preserving Feature Map"]: F staged row-major in LDS (the B fragments
+// of X F by transposing reads); waves 0-1 each compute phi of one 16-key
+// tile over all D features (features on the lanes, so a key's softmax
+// statistics reduce inside the wave), the features go to LDS feature-major
+// in float32; then wave w folds feature tile w % (D/16) against the block's
+// values for its d_v tiles (phi as fp16 hi + lo, ~22 significant bits;
+// values exact in fp16) and adds its float32 sums to S, z once at the end
+// (each entry by one thread). Every thread calls it; barriers inside. The
+// 32-key blocks keep the kernel's LDS under 80 KiB: two workgroups per CU.
+constexpr int BFB = 32;
+template <int D>
+struct BndFoldLds {
+  static constexpr int FS = D + 8, VS = D + 8, PS = BFB + 4;  // row strides (elements)
+  static constexpr size_t f_bytes = (size_t)D * FS * 2;
+  static constexpr size_t v_bytes = (size_t)BFB * VS * 2;
+  static constexpr size_t ph_bytes = (size_t)D * PS * 4;
+  static constexpr size_t bytes = f_bytes + v_bytes + ph_bytes;
+};
+
+template <typename T, int D>
+__device__ __forceinline__ void boundary_fold_mfma(const DecodeArgs& a, char* st, const T* F, int f_lo, int f_hi,
+                                                   char* lds) {
+  static_assert(sizeof(T) == 2, "16-bit data");
+  using BL = BndFoldLds<D>;
+  constexpr int NFT = D / 16, VPW = NFT * NFT / 8, CPR = D / 8;
+  T* Fl = reinterpret_cast<T*>(lds);
+  f16* Vl = reinterpret_cast<f16*>(lds + BL::f_bytes);
+  float* PH = reinterpret_cast<float*>(lds + BL::f_bytes + BL::v_bytes);
+  const int tid = threadIdx.x, lane = tid & 63, r16 = lane & 15, g4 = lane >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int R = a.R;
+  const T* ring_k = reinterpret_cast<const T*>(st + a.st_ring_k);
+  const T* ring_v = reinterpret_cast<const T*>(st + a.st_ring_v);
+  const int32_t* ring_flag = reinterpret_cast<const int32_t*>(st + a.st_ring_flag);
+  float* S = reinterpret_cast<float*>(st + a.st_S);
+  float* z = reinterpret_cast<float*>(st + a.st_z);
+  for (int e = tid; e < D * CPR; e += BND_THREADS) {
+    const int row = e / CPR, c = (e % CPR) * 8;
+    *reinterpret_cast<uint4*>(Fl + row * BL::FS + c) = *reinterpret_cast<const uint4*>(F + (size_t)row * D + c);
+  }
+  // fold ownership: feature tile ft, d_v tiles vt0 .. vt0 + VPW - 1
+  const int ft = wave % NFT, vt0 = (wave / NFT) * VPW;
+  f32x4 acc[VPW];
+#pragma unroll
+  for (int v = 0; v < VPW; ++v) acc[v] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float zl = 0.f;
+  for (int blo = f_lo; blo < f_hi; blo += BFB) {
+    __syncthreads();  // F is staged; the previous block's fold is done with Vl, PH
+    for (int e = tid; e < BFB * CPR; e += BND_THREADS) {
+      const int r = e / CPR, c = (e % CPR) * 8, pos = blo + r;
+      uint4 v8 = {0u, 0u, 0u, 0u};
+      if (pos < f_hi) v8 = *reinterpret_cast<const uint4*>(ring_v + (size_t)(pos % R) * D + c);
+      const T* ve = reinterpret_cast<const T*>(&v8);
+      f16 w[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) w[i] = (f16)to_f32(ve[i]);
+      *reinterpret_cast<uint4*>(Vl + r * BL::VS + c) = *reinterpret_cast<uint4*>(w);
+    }
+    if (wave < BFB / 16) {
+      // key tile `wave`: A fragments of the key rows with the depth order of
+      // the transposing reads (slots 0-3: d = 32kb + 4g + s, slots 4-7: d =
+      // 32kb + 16 + 4g + s - 4)
+      const int pos = blo + 16 * wave + r16;
+      const bool inr = pos < f_hi;
+      const int slot = pos % R;
+      const bool fold = inr && ring_flag[slot] == 0;
+      const T* krow = ring_k + (size_t)slot * D;
+      Frag<T> kf[D / 32];
+#pragma unroll
+      for (int kb = 0; kb < D / 32; ++kb) {
+        const uint2 x0 = inr ? ld8(krow + 32 * kb + 4 * g4) : uint2{0u, 0u};
+        const uint2 x1 = inr ? ld8(krow + 32 * kb + 16 + 4 * g4) : uint2{0u, 0u};
+        const uint4 x = {x0.x, x0.y, x1.x, x1.y};
+        kf[kb].v = __builtin_bit_cast(decltype(kf[kb].v), x);
+      }
+      f32x4 ph[NFT];
+#pragma unroll
+      for (int f = 0; f < NFT; ++f) {
+        ph[f] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < D / 32; ++kb)
+          mma(ph[f], kf[kb],
+              tr_frag_bf16(reinterpret_cast<const bf16*>(Fl) + (32 * kb + 4 * g4 + (r16 >> 2)) * BL::FS + 16 * f +
+                               4 * (r16 & 3),
+                           16 * BL::FS));
+      }
+      // |k|^2 of key r16 (every g); softmax over the features in base 2,
+      // factor |k| / sqrt(sum e^2), zero for keys that do not fold
+      float n2 = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < D / 32; ++kb) n2 = frag_dot2_sumsq(kf[kb], n2);
+      n2 = sum_over_g(n2);
+      const uint32_t use16 = (uint32_t)__builtin_amdgcn_ballot_w64(fold) & 0xffffu;
+      float nm[4], ss[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float m = ph[0][i];
+#pragma unroll
+        for (int f = 1; f < NFT; ++f) m = fmax_nn(m, ph[f][i]);
+        nm[i] = -row_max<16>(m) * STILL_LOG2E;
+        ss[i] = 0.f;
+      }
+#pragma unroll
+      for (int f = 0; f < NFT; ++f)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float e = __builtin_amdgcn_exp2f(fmaf(ph[f][i], STILL_LOG2E, nm[i]));
+          ph[f][i] = e;
+          ss[i] = fmaf(e, e, ss[i]);
+        }
+      float fac[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float s2 = row_sum<16>(ss[i]);
+        const float k2 = __shfl(n2, 4 * g4 + i);
+        fac[i] = ((use16 >> (4 * g4 + i)) & 1u) ? __builtin_amdgcn_sqrtf(k2) * __builtin_amdgcn_rsqf(s2) : 0.f;
+      }
+#pragma unroll
+      for (int f = 0; f < NFT; ++f) {
+        const f32x4 o = {ph[f][0] * fac[0], ph[f][1] * fac[1], ph[f][2] * fac[2], ph[f][3] * fac[3]};
+        *reinterpret_cast<f32x4*>(PH + (16 * f + r16) * BL::PS + 16 * wave + 4 * g4) = o;
+      }
+    }
+    __syncthreads();  // Vl, PH
+#pragma unroll
+    for (int kb2 = 0; kb2 < BFB / 32; ++kb2) {
+      const float* pr = PH + (16 * ft + r16) * BL::PS + 32 * kb2 + 4 * g4;
+      const f32x4 x0 = *reinterpret_cast<const f32x4*>(pr);
+      const f32x4 x1 = *reinterpret_cast<const f32x4*>(pr + 16);
+      zl += ((x0[0] + x0[1]) + (x0[2] + x0[3])) + ((x1[0] + x1[1]) + (x1[2] + x1[3]));
+      Frag<f16> fh, fl;
+      split2_frag<f16>(x0, x1, fh, fl);
+#pragma unroll
+      for (int v = 0; v < VPW; ++v) {
+        const Frag<f16> bv =
+            tr_frag(Vl + (32 * kb2 + 4 * g4 + (r16 >> 2)) * BL::VS + 16 * (vt0 + v) + 4 * (r16 & 3), 16 * BL::VS);
+        mma(acc[v], fh, bv);
+        mma(acc[v], fl, bv);
+      }
+    }
+  }
+#pragma unroll
+  for (int v = 0; v < VPW; ++v)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) S[(size_t)(16 * ft + 4 * g4 + i) * D + 16 * (vt0 + v) + r16] += acc[v][i];
+  if (vt0 == 0) {
+    zl = sum_over_g(zl);
+    if (g4 == 0) z[16 * ft + r16] += zl;
+  }
+}
+
 // Chunk boundary (position t = cC): decide chunk c-1 by Top-lambda over its
 // float64 scores, append the kept tokens to the pool [P2 固定预算路由], and
 // fold the chunks that are now wholly before the window into S, z. Runs
@@ -316,9 +469,15 @@ __global__ __launch_bounds__(BND_THREADS) void decode_boundary_kernel(DecodeArgs
   __syncthreads();
   if (tid == 0) meta[1] = n_pool;
 
-  // fold chunks [cf(c-1), cf(c)) into S, z (float32 features, exact expf)
+  // fold chunks [cf(c-1), cf(c)) into S, z: 16-bit data on the matrix cores,
+  // float32 data with float32 features and exact expf on the VALU
   const int f_lo = full_chunks_before(c - 1, W, C) * C;
   const int f_hi = full_chunks_before(c, W, C) * C;
+  if constexpr (sizeof(T) == 2) {
+    if (f_hi > f_lo) boundary_fold_mfma<T, D>(a, st, F, f_lo, f_hi, smem + LD::uni);  // uniform
+    __syncthreads();
+    return;
+  }
   constexpr int PER = D * D / BND_THREADS;
   float dacc[PER];
 #pragma unroll

@@ -1442,17 +1442,6 @@ struct SdLds {
   static_assert(bytes <= 160 * 1024, "one workgroup's LDS");
 };
 
-// acc + sum of squares of a bf16 fragment, by packed bf16 dot products
-__device__ __forceinline__ float frag_dot2_sumsq(const Frag<bf16>& f, float acc) {
-  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const bf16x2_t p = {f.v[2 * i], f.v[2 * i + 1]};
-    acc = __builtin_amdgcn_fdot2_f32_bf16(p, p, acc, false);
-  }
-  return acc;
-}
-
 // sum over groups of N consecutive lanes (N = 4 or 8), float64
 template <int N>
 __device__ __forceinline__ double group_sum_d(double x) {
