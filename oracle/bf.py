@@ -247,6 +247,23 @@ def prefill(q, k, v, fmap_w, gate, *, window: int, chunk: int, budget: int,
     return out
 
 
+def output_gate(y, gate_out) -> np.ndarray:
+    """Channel-wise sigmoid output gate on the attention output.
+
+    [P4 "Synergizing Linear and Sparse Attention: A Deep Dive into Hybrid LLM
+    Architectures", §4 Gating Mechanism]: the attention output, on its way
+    back to the residual stream, is multiplied element by element by the
+    logistic sigmoid of a gate vector of the same shape. Reading: the gate is
+    a caller-supplied tensor shaped like the output (one value per token and
+    channel, before the sigmoid); the layer's merged output y is gated,
+    float64: y * 1 / (1 + exp(-g)).
+    """
+    g = np.asarray(gate_out, np.float64)
+    with np.errstate(over="ignore"):
+        sig = 1.0 / (1.0 + np.exp(-g))
+    return np.asarray(y, np.float64) * sig
+
+
 def key_sets(L: int, window: int, chunk: int, sel_rows: List[List[int]]):
     """The softmax (A) and linear (B) key sets of every query, for tests.
 

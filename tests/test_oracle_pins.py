@@ -549,3 +549,26 @@ def test_exported_state_plus_ring_is_last_query_linear_set(W, C, L):
     np.testing.assert_allclose(got_S, want_S, rtol=1e-11, atol=1e-11)
     np.testing.assert_allclose(o["z"][0, 0] + pk[ring].sum(0), pk[lin].sum(0), rtol=1e-12, atol=1e-12)
     assert all(j < cf * C for j in lin if j not in ring)
+
+
+# ---- channel-wise sigmoid output gate [P4 §4 Gating Mechanism] -------------
+def test_output_gate_pins():
+    """Pins of the gated output against what the sigmoid fixes, not its
+    formula: a zero gate halves the output exactly; gates g and -g split the
+    output into two parts that add up to it (sigmoid(g) + sigmoid(-g) = 1);
+    a large positive gate leaves it unchanged and a large negative one
+    closes it; one value worked by hand: sigmoid(ln 3) = 3/4."""
+    rng = np.random.default_rng(7)
+    y = rng.standard_normal((2, 3, 5, 8))
+    g = rng.standard_normal(y.shape) * 3.0
+    assert np.array_equal(bf.output_gate(y, np.zeros_like(y)), y / 2)
+    np.testing.assert_allclose(bf.output_gate(y, g) + bf.output_gate(y, -g), y, rtol=0, atol=1e-15)
+    np.testing.assert_allclose(bf.output_gate(y, np.full_like(y, 50.0)), y, rtol=1e-15, atol=0)
+    assert np.abs(bf.output_gate(y, np.full_like(y, -800.0))).max() == 0.0
+    np.testing.assert_allclose(bf.output_gate(np.array([4.0]), np.array([math.log(3.0)])), [3.0], rtol=1e-15)
+    # element by element: each output entry depends on its own gate entry only
+    g2 = g.copy()
+    g2[1, 2, 3, 4] += 1.0
+    d = bf.output_gate(y, g2) - bf.output_gate(y, g)
+    d[1, 2, 3, 4] = 0.0
+    assert np.abs(d).max() == 0.0
