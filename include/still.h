@@ -188,6 +188,20 @@ int still_prefill(const still_params* p, int64_t seq_len, const void* q, const v
                   int32_t* sel_idx, float* score, void* state, void* workspace,
                   size_t ws_bytes, void* stream);
 
+/* still_prefill with a channel-wise sigmoid output gate [P4 "Synergizing
+ * Linear and Sparse Attention: A Deep Dive into Hybrid LLM Architectures",
+ * §4 Gating Mechanism]: out = y * sigmoid(out_gate), y the output
+ * still_prefill writes. out_gate [B, Hq, L, d] holds the gate before the
+ * sigmoid, in the params' dtype (read only, required, 16-byte aligned;
+ * the caller computes it, e.g. as a projection of the layer input). The
+ * gate is applied to the float32 merged output before the one rounding to
+ * the output dtype. sel_idx, score and state are as for still_prefill;
+ * same errors (a NULL out_gate returns STILL_EINVAL). */
+int still_prefill_gated(const still_params* p, int64_t seq_len, const void* q, const void* k,
+                        const void* v, const void* fmap_w, const float* gate,
+                        const void* out_gate, void* out, int32_t* sel_idx, float* score,
+                        void* state, void* workspace, size_t ws_bytes, void* stream);
+
 /* still_prefill with per-kernel timing, for benchmarks: for i < n_pairs it
  * records events[2i] before and events[2i+1] after the i-th kernel of the
  * prefill on `stream` (events are caller-created hipEvent_t handles; a NULL
@@ -252,6 +266,16 @@ int still_decode_step(const still_params* p, int64_t pos, const void* q, const v
                       const void* v, const void* fmap_w, const float* gate, void* state,
                       void* out, int32_t* sel_new, void* workspace, size_t ws_bytes,
                       void* stream);
+
+/* still_decode_step with the channel-wise sigmoid output gate of
+ * still_prefill_gated: out = y * sigmoid(out_gate), out_gate [B, Hq, d] in
+ * the params' dtype (required, 16-byte aligned, read only). Needs no
+ * workspace. Same state update, selection and errors as still_decode_step
+ * (a NULL out_gate returns STILL_EINVAL). */
+int still_decode_step_gated(const still_params* p, int64_t pos, const void* q, const void* k,
+                            const void* v, const void* fmap_w, const float* gate,
+                            const void* out_gate, void* state, void* out, int32_t* sel_new,
+                            void* stream);
 
 /* Ragged batches [P3 "Delayed Chunk-Level Selection ..."]: prefill and
  * decode keep one routing and memory-update rule per sequence, so each row

@@ -496,7 +496,8 @@ static int prefill_impl(const still_params* p, int64_t seq_len, const void* q, c
                         const void* v, const void* fmap_w, const float* gate, void* out,
                         int32_t* sel_idx, float* score, void* state, void* workspace,
                         size_t ws_bytes, void* stream, void* const* events, int n_pairs,
-                        Partials parts = Partials{nullptr, nullptr, nullptr, nullptr}) {
+                        Partials parts = Partials{nullptr, nullptr, nullptr, nullptr},
+                        const void* out_gate = nullptr) {
   Derived d;
   int rc = derive(p, &d);
   if (rc != STILL_OK) return rc;
@@ -511,7 +512,7 @@ static int prefill_impl(const still_params* p, int64_t seq_len, const void* q, c
   if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(fmap_w) || misaligned(out) ||
       misaligned(state) || misaligned(workspace) || misaligned(gate))
     return STILL_EINVAL;
-  if (misaligned(parts.y_sa) || misaligned(parts.y_la)) return STILL_EINVAL;
+  if (misaligned(parts.y_sa) || misaligned(parts.y_la) || misaligned(out_gate)) return STILL_EINVAL;
   const bool merge_sum = (p->flags & STILL_FLAG_MERGE_SUM) != 0;
   const bool softmax_only = (p->flags & STILL_FLAG_SOFTMAX_ONLY) != 0;
   if (merge_sum && softmax_only) return STILL_EINVAL;
@@ -530,6 +531,7 @@ static int prefill_impl(const still_params* p, int64_t seq_len, const void* q, c
   a.fmap_w = fmap_w;
   a.gate = gate;
   a.out = out;
+  a.out_gate = out_gate;
   a.sel = sel_idx;
   a.route = (int)STILL_ROUTE_OF(p->flags);
   if (a.route == still::ROUTE_EXTERNAL) {  // the caller's scores are an input here
@@ -590,6 +592,16 @@ int still_prefill(const still_params* p, int64_t seq_len, const void* q, const v
                   size_t ws_bytes, void* stream) {
   return prefill_impl(p, seq_len, q, k, v, fmap_w, gate, out, sel_idx, score, state, workspace,
                       ws_bytes, stream, nullptr, 0);
+}
+
+int still_prefill_gated(const still_params* p, int64_t seq_len, const void* q, const void* k,
+                        const void* v, const void* fmap_w, const float* gate,
+                        const void* out_gate, void* out, int32_t* sel_idx, float* score,
+                        void* state, void* workspace, size_t ws_bytes, void* stream) {
+  if (!out_gate) return STILL_EINVAL;
+  return prefill_impl(p, seq_len, q, k, v, fmap_w, gate, out, sel_idx, score, state, workspace,
+                      ws_bytes, stream, nullptr, 0, Partials{nullptr, nullptr, nullptr, nullptr},
+                      out_gate);
 }
 
 int still_prefill_timed(const still_params* p, int64_t seq_len, const void* q, const void* k,
@@ -695,7 +707,8 @@ int64_t still_noalloc_scratch_bytes(void) { return (int64_t)kNoAllocScratchBytes
 // row_pos[b] + s with per-row positions (device array).
 static int decode_impl(const still_params* p, int64_t pos, const int32_t* row_pos, int n_tokens,
                        const void* q, const void* k, const void* v, const void* fmap_w,
-                       const float* gate, void* state, void* out, int32_t* sel_new, void* stream) {
+                       const float* gate, void* state, void* out, int32_t* sel_new, void* stream,
+                       const void* out_gate = nullptr) {
   Derived d;
   int rc = derive(p, &d);
   if (rc != STILL_OK) return rc;
@@ -706,7 +719,7 @@ static int decode_impl(const still_params* p, int64_t pos, const int32_t* row_po
   if (!row_pos && (pos < 1 || pos + n_tokens - 1 > ((int64_t)1 << 30))) return STILL_EINVAL;
   if (!q || !k || !v || !fmap_w || !gate || !state || !out) return STILL_EINVAL;
   if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(fmap_w) || misaligned(out) ||
-      misaligned(state) || misaligned(gate) || ((uintptr_t)row_pos & 3u))
+      misaligned(state) || misaligned(gate) || misaligned(out_gate) || ((uintptr_t)row_pos & 3u))
     return STILL_EINVAL;
   still_state_layout SL;
   layout(d, &SL);
@@ -744,6 +757,7 @@ static int decode_impl(const still_params* p, int64_t pos, const int32_t* row_po
     a.k = reinterpret_cast<const char*>(k) + i * kb;
     a.v = reinterpret_cast<const char*>(v) + i * kb;
     a.out = reinterpret_cast<char*>(out) + i * ob;
+    a.out_gate = out_gate ? reinterpret_cast<const char*>(out_gate) + i * qb : nullptr;
     a.sel_new = sel_new ? sel_new + i * sb : nullptr;
     a.t = row_pos ? i : (int)(pos + i);
     a.boundary = !row_pos && ((pos + i) % d.C) == 0 ? 1 : 0;
@@ -763,6 +777,15 @@ int still_decode_step(const still_params* p, int64_t pos, const void* q, const v
   (void)workspace;
   (void)ws_bytes;
   return decode_impl(p, pos, nullptr, 1, q, k, v, fmap_w, gate, state, out, sel_new, stream);
+}
+
+int still_decode_step_gated(const still_params* p, int64_t pos, const void* q, const void* k,
+                            const void* v, const void* fmap_w, const float* gate,
+                            const void* out_gate, void* state, void* out, int32_t* sel_new,
+                            void* stream) {
+  if (!out_gate) return STILL_EINVAL;
+  return decode_impl(p, pos, nullptr, 1, q, k, v, fmap_w, gate, state, out, sel_new, stream,
+                     out_gate);
 }
 
 int still_decode_tokens(const still_params* p, int64_t pos, const int32_t* row_pos, int n_tokens,

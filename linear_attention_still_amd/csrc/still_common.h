@@ -375,6 +375,33 @@ __device__ __forceinline__ float frag_sumsq<float>(const Frag<float>& f) {
   return s;
 }
 
+// The channel-wise sigmoid output gate [P4 "Synergizing Linear and Sparse
+// Attention: A Deep Dive into Hybrid LLM Architectures", §4 Gating
+// Mechanism]: sigmoid(g) = 1 / (1 + exp(-g)) (0 for g -> -inf, 1 for
+// g -> +inf), the hardware exponential and reciprocal (~2 ulp).
+__device__ __forceinline__ float sigmoid_gate(float g) {
+  return __builtin_amdgcn_rcpf(1.f + __expf(-g));
+}
+// sigmoid gates of 4 consecutive elements at byte offset off of a buffer
+// (zeros past its range give 1/2)
+template <typename T>
+__device__ __forceinline__ f32x4 sigmoid_gate4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  // (the loaded vector is cast whole: a bit cast of one element of it
+  // keeps element 0 only)
+  f32x4 g;
+  if constexpr (sizeof(T) == 2) {
+    typedef T t4 __attribute__((ext_vector_type(4)));
+    const t4 x = __builtin_bit_cast(t4, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) g[i] = sigmoid_gate((float)x[i]);
+  } else {
+    const f32x4 x = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) g[i] = sigmoid_gate(x[i]);
+  }
+  return g;
+}
+
 // acc + sum of squares of a bf16 fragment, by packed bf16 dot products
 __device__ __forceinline__ float frag_dot2_sumsq(const Frag<bf16>& f, float acc) {
   typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));

@@ -50,6 +50,7 @@ struct DecodeArgs {
   const int32_t* pos;
   int softmax_only;  // the linear branch dropped (every gate taken as 0)
   int route;         // routing metric (ROUTE_*; not ROUTE_EXTERNAL)
+  const void* out_gate;  // [B][Hq][D] T: channel-wise output gate before the sigmoid, or null
   float scale, eps;
   double scale64, eps64;  // the same parameters for the float64 score
   long st_unit, st_S, st_z, st_pool_k, st_pool_v, st_pool_pos, st_ring_k, st_ring_v,
@@ -1153,8 +1154,9 @@ void decode_kernel(DecodeArgs a) {
     }
     const float dz = hv[h * 12 + 0], es = hv[h * 12 + 1], tot = hv[h * 12 + 2];
     if (es > 0.f) sv += es * ns / dz;
-    const float y = sv / tot;
+    float y = sv / tot;
     const size_t o = ((size_t)b * a.Hq + kv * G + h) * D + f;
+    if (a.out_gate) y *= sigmoid_gate(to_f32(reinterpret_cast<const T*>(a.out_gate)[o]));
     if (a.fp32_out) reinterpret_cast<float*>(a.out)[o] = y;
     else reinterpret_cast<T*>(a.out)[o] = from_f32<T>(y);
   }

@@ -55,6 +55,7 @@ struct PrefillArgs {
   float* lse_la;  // [B][Hq][L] natural log of sum <phi(q), phi(k)>, or null
   int* rlist;     // [B][Hkv][T][C + 1] tokens whose exported score is refined
   int route;      // routing metric (ROUTE_*)
+  const void* out_gate;    // [B][Hq][L][D] T: channel-wise output gate before the sigmoid, or null
   const float* ext_score;  // [B][Hkv][L] the caller's scores (ROUTE_EXTERNAL)
   float scale, eps;
   double scale64, eps64;  // the same parameters for the float64 paths
@@ -1895,6 +1896,13 @@ __global__ __launch_bounds__(512) void attend_kernel(PrefillArgs a) {
     lgate2[j] = gg[j] > 0.f ? log2_acc<T>(gg[j]) : STILL_NEG_INF;
     qr[j] = make_rsrc(reinterpret_cast<const T*>(a.q) + ((size_t)(b * a.Hq + hh[j]) * L) * D, kv_bytes);
   }
+  // the output gates of the wave's heads (only read with a.out_gate)
+  __amdgpu_buffer_rsrc_t gr[HPW];
+#pragma unroll
+  for (int j = 0; j < HPW; ++j)
+    gr[j] = make_rsrc(a.out_gate ? reinterpret_cast<const T*>(a.out_gate) + ((size_t)(b * a.Hq + hh[j]) * L) * D
+                                 : nullptr,
+                      a.out_gate ? kv_bytes : 0u);
 
   const float* Sst = a.dS + ((size_t)unit * a.NS + s) * (D * D + D);
   load_state<T, D>(P, Sst);
@@ -2283,8 +2291,9 @@ __global__ __launch_bounds__(512) void attend_kernel(PrefillArgs a) {
 #pragma unroll
         for (int dt = 0; dt < D / 16; ++dt) {
           const f32x4 ys = O[0][dt] * i0, yl = O[1][dt] * i1;
-          const f32x4 y = ys * w_sa + yl * w_la;
+          f32x4 y = ys * w_sa + yl * w_la;
           const int col = 16 * dt + 4 * g4;
+          if (a.out_gate) y *= sigmoid_gate4<T>(gr[0], (uint32_t)(t * D + col) * sizeof(T));
           if (sizeof(T) == 4 || a.fp32_out) {
             *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.out) + ob + col) = y;
           } else {
@@ -2321,7 +2330,8 @@ __global__ __launch_bounds__(512) void attend_kernel(PrefillArgs a) {
             if (j > 0) wave_sync();  // the previous head's rows are read
 #pragma unroll
             for (int dt = 0; dt < D / 16; ++dt) {
-              const f32x4 y = O[j][dt] * inv;
+              f32x4 y = O[j][dt] * inv;
+              if (a.out_gate) y *= sigmoid_gate4<T>(gr[j], (uint32_t)(t * D + 16 * dt + 4 * g4) * sizeof(T));
               bf16 y4[4] = {(bf16)y[0], (bf16)y[1], (bf16)y[2], (bf16)y[3]};
               *reinterpret_cast<uint2*>(tile + r16 * OS + 16 * dt + 4 * g4) = *reinterpret_cast<uint2*>(y4);
             }
@@ -2339,15 +2349,19 @@ __global__ __launch_bounds__(512) void attend_kernel(PrefillArgs a) {
           }
         } else if (act && t < L) {
 #pragma unroll
-          for (int dt = 0; dt < D / 16; ++dt)
-            *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.out) + ob + (size_t)t * D + 16 * dt + 4 * g4) =
-                O[j][dt] * inv;
+          for (int dt = 0; dt < D / 16; ++dt) {
+            f32x4 y = O[j][dt] * inv;
+            if (a.out_gate) y *= sigmoid_gate4<T>(gr[j], (uint32_t)(t * D + 16 * dt + 4 * g4) * sizeof(T));
+            *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.out) + ob + (size_t)t * D + 16 * dt + 4 * g4) = y;
+          }
         }
       } else if (act && t < L) {
 #pragma unroll
-        for (int dt = 0; dt < D / 16; ++dt)
-          *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.out) + ob + (size_t)t * D + 16 * dt + 4 * g4) =
-              O[j][dt] * inv;
+        for (int dt = 0; dt < D / 16; ++dt) {
+          f32x4 y = O[j][dt] * inv;
+          if (a.out_gate) y *= sigmoid_gate4<T>(gr[j], (uint32_t)(t * D + 16 * dt + 4 * g4) * sizeof(T));
+          *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.out) + ob + (size_t)t * D + 16 * dt + 4 * g4) = y;
+        }
       }
     }
   }

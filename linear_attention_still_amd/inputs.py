@@ -157,6 +157,20 @@ def make_route_scores(wl: Workload, device="cpu", seq_len: Optional[int] = None,
                       dtype=torch.float32)
 
 
+def make_out_gate(wl: Workload, shape, device="cpu", seed: Optional[int] = None) -> torch.Tensor:
+    """Channel-wise output gates before the sigmoid, of the given shape
+    ([B,Hq,L,d] for a prefill, [B,Hq,d] or [n,B,Hq,d] for decode steps), in the
+    workload's dtype: N(0, 2^2), so that the sigmoid takes values across its
+    range, with one entry in 64 at +-40 (saturated open or shut)."""
+    gen = torch.Generator(device=device)
+    gen.manual_seed((wl.seed if seed is None else seed) + 15485863)
+    g = 2.0 * torch.randn(shape, generator=gen, device=device, dtype=torch.float32)
+    sat = torch.rand(shape, generator=gen, device=device) < 1.0 / 64
+    sign = torch.where(torch.rand(shape, generator=gen, device=device) < 0.5, -1.0, 1.0)
+    g = torch.where(sat, 40.0 * sign, g)
+    return g.to(torch.bfloat16 if wl.dtype == "bf16" else torch.float32)
+
+
 def make_decode_tokens(wl: Workload, n_steps: int, device="cpu",
                        seed: Optional[int] = None) -> Dict[str, torch.Tensor]:
     """New tokens for n_steps decode steps: q [S,B,Hq,d], k/v [S,B,Hkv,d].

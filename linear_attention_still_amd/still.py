@@ -79,6 +79,10 @@ def lib() -> ctypes.CDLL:
         L.still_workspace_bytes.restype = I64
         L.still_prefill.argtypes = [pp, I64] + [P] * 10 + [ctypes.c_size_t, P]
         L.still_prefill.restype = I32
+        L.still_prefill_gated.argtypes = [pp, I64] + [P] * 11 + [ctypes.c_size_t, P]
+        L.still_prefill_gated.restype = I32
+        L.still_decode_step_gated.argtypes = [pp, I64] + [P] * 10
+        L.still_decode_step_gated.restype = I32
         L.still_prefill_timed.argtypes = [pp, I64] + [P] * 10 + [ctypes.c_size_t, P, P, I32]
         L.still_prefill_timed.restype = I32
         L.still_prefill_partials.argtypes = [pp, I64] + [P] * 10 + [ctypes.c_size_t, P] + [P] * 4
@@ -182,6 +186,17 @@ def still_prefill(p: still_params, seq_len: int, q, k, v, fmap_w, gate, out, sel
         raise StillError("still_prefill", rc)
 
 
+def still_prefill_gated(p: still_params, seq_len: int, q, k, v, fmap_w, gate, out_gate, out,
+                        sel_idx, score, state, workspace, stream=None) -> None:
+    rc = lib().still_prefill_gated(ctypes.byref(p), int(seq_len), _ptr(q), _ptr(k), _ptr(v),
+                                   _ptr(fmap_w), _ptr(gate), _ptr(out_gate), _ptr(out),
+                                   _ptr(sel_idx), _ptr(score), _ptr(state), _ptr(workspace),
+                                   workspace.numel() * workspace.element_size() if workspace is not None else 0,
+                                   _stream(stream))
+    if rc != STILL_OK:
+        raise StillError("still_prefill_gated", rc)
+
+
 def still_prefill_partials(p: still_params, seq_len: int, q, k, v, fmap_w, gate, out, sel_idx,
                            score, state, workspace, y_sa, lse_sa, y_la, lse_la,
                            stream=None) -> None:
@@ -238,6 +253,15 @@ def still_decode_step(p: still_params, pos: int, q, k, v, fmap_w, gate, state, o
                                  _stream(stream))
     if rc != STILL_OK:
         raise StillError("still_decode_step", rc)
+
+
+def still_decode_step_gated(p: still_params, pos: int, q, k, v, fmap_w, gate, out_gate, state,
+                            out, sel_new=None, stream=None) -> None:
+    rc = lib().still_decode_step_gated(ctypes.byref(p), int(pos), _ptr(q), _ptr(k), _ptr(v),
+                                       _ptr(fmap_w), _ptr(gate), _ptr(out_gate), _ptr(state),
+                                       _ptr(out), _ptr(sel_new), _stream(stream))
+    if rc != STILL_OK:
+        raise StillError("still_decode_step_gated", rc)
 
 
 # ---- allocation helpers (torch memory only) --------------------------------

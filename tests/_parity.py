@@ -28,15 +28,17 @@ def n_threads() -> int:
 
 def gpu_prefill(wl: Workload, x: Dict[str, torch.Tensor], fp32_out: bool = False,
                 keep_device: bool = False, flags: int = 0, partials: bool = False,
-                ext_score: Optional[torch.Tensor] = None) -> Dict[str, torch.Tensor]:
-    """still_prefill (or still_prefill_partials) on the GPU; flags are the
-    variant flags; ext_score: the caller's routing scores (external route),
-    passed in the score buffer."""
+                ext_score: Optional[torch.Tensor] = None,
+                out_gate: Optional[torch.Tensor] = None) -> Dict[str, torch.Tensor]:
+    """still_prefill (or still_prefill_partials, or still_prefill_gated) on
+    the GPU; flags are the variant flags; ext_score: the caller's routing
+    scores (external route), passed in the score buffer; out_gate: the
+    output gate before the sigmoid, [B, Hq, L, d]."""
     p = still.params_for(wl, fp32_out=fp32_out, flags=flags)
     xd = {k: v.cuda() for k, v in x.items()}
     L = xd["q"].shape[2]
-    print("  gpu prefill %s L=%d fp32_out=%s flags=%d partials=%s"
-          % (wl.name, L, fp32_out, flags, partials), flush=True)
+    print("  gpu prefill %s L=%d fp32_out=%s flags=%d partials=%s gated=%s"
+          % (wl.name, L, fp32_out, flags, partials, out_gate is not None), flush=True)
     bufs = still.PrefillBuffers(p, L)
     if ext_score is not None:
         bufs.score.copy_(ext_score)
@@ -51,6 +53,10 @@ def gpu_prefill(wl: Workload, x: Dict[str, torch.Tensor], fp32_out: bool = False
                                      bufs.out, bufs.sel if bufs.sel.numel() else None,
                                      bufs.score, bufs.state, bufs.workspace, out["y_sa"],
                                      out["lse_sa"], out["y_la"], out["lse_la"])
+    elif out_gate is not None:
+        still.still_prefill_gated(p, L, xd["q"], xd["k"], xd["v"], xd["fmap_w"], xd["gate"],
+                                  out_gate.cuda(), bufs.out, bufs.sel if bufs.sel.numel() else None,
+                                  bufs.score, bufs.state, bufs.workspace)
     else:
         still.run_prefill(p, xd, bufs)
     torch.cuda.synchronize()

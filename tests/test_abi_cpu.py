@@ -213,3 +213,28 @@ def test_ragged_entries_validate_before_any_hip_call():
     assert L.still_decode_tokens(ctypes.byref(p), 0, None, 4, *f8, None) == still.STILL_EINVAL
     odd = ctypes.c_void_p((1 << 20) + 2)
     assert L.still_decode_tokens(ctypes.byref(p), 0, odd, 4, *f8, None) == still.STILL_EINVAL
+
+
+def test_gated_entries_validate_before_any_hip_call():
+    """The output-gated prefill and decode step require their gate and a
+    16-byte aligned one; their other checks are those of the plain entries."""
+    L = still.lib()
+    fake = ctypes.c_void_p(1 << 20)
+    odd = ctypes.c_void_p((1 << 20) + 8)
+    p = still.params_for(WORKLOADS["small_f32_L256"])
+    ws = still.still_workspace_bytes(p, 256)
+    args = [fake] * 11  # q, k, v, fmap_w, gate, out_gate, out, sel_idx, score, state, workspace
+    for bad in (None, odd):
+        args[5] = bad
+        assert L.still_prefill_gated(ctypes.byref(p), 256, *args, ws, None) == still.STILL_EINVAL
+    args[5] = fake
+    assert L.still_prefill_gated(ctypes.byref(p), 256, *args, ws - 1, None) == still.STILL_EWORKSPACE
+    p = still.params_for(WORKLOADS["decode_bf16_B64_ctx16K"])
+    f9 = [fake] * 9  # q, k, v, fmap_w, gate, out_gate, state, out, sel_new (then the stream)
+    for bad in (None, odd):
+        f9[5] = bad
+        assert L.still_decode_step_gated(ctypes.byref(p), 16384, *f9, None) == still.STILL_EINVAL
+    f9[5] = fake
+    assert L.still_decode_step_gated(ctypes.byref(p), 0, *f9, None) == still.STILL_EINVAL
+    p = still.params_for(WORKLOADS["decode_bf16_B64_ctx16K"], flags=still.STILL_FLAG_MERGE_SUM)
+    assert L.still_decode_step_gated(ctypes.byref(p), 16384, *f9, None) == still.STILL_EUNSUPPORTED

@@ -19,6 +19,12 @@ The routing metrics are the alternatives of the STILL article's routing
 ablation ("Ablation Studies"): diagonal attention weight, q.k, key norm,
 uniform picks, and caller-supplied scores (random routing's draws, seeded
 U(0, 1)); selections bit-exact, scores within the score bar.
+
+The output gate is the channel-wise sigmoid gate of the hybrid-architecture
+survey (§4, gating): the entries still_prefill_gated and
+still_decode_step_gated against the oracle's output times the sigmoid of the
+same seeded gates; the bars of the ungated outputs (the sigmoid lies in
+[0, 1], so it shrinks the error with the output).
 """
 import numpy as np
 import pytest
@@ -26,8 +32,8 @@ import torch
 
 from linear_attention_still_amd import still
 from linear_attention_still_amd.inputs import (WORKLOADS, Workload, make_decode_tokens, make_inputs,
-                                               make_route_scores)
-from oracle import rec
+                                               make_out_gate, make_route_scores)
+from oracle import bf, rec
 from tests import _parity as P
 
 pytestmark = pytest.mark.gpu
@@ -229,3 +235,81 @@ def test_decode_routing_metrics(case, route):
     assert np.array_equal(np.isnan(pend), np.isnan(o["pending"]))
     ok = ~np.isnan(pend)
     assert np.allclose(pend[ok], o["pending"][ok], rtol=1e-12, atol=1e-12)
+
+
+GATE_SHAPES = [SHAPES[0], SHAPES[1], SHAPES[3], SHAPES[5], SHAPES[6]]
+
+
+@pytest.mark.parametrize("merge", ["one", "sum"])
+@pytest.mark.parametrize("wl", GATE_SHAPES, ids=[w.name for w in GATE_SHAPES])
+def test_prefill_output_gate(wl, merge):
+    """still_prefill_gated: out = y * sigmoid(out_gate), in the walk's output
+    stage (the single-normaliser walk and the kept-apart branches of the sum
+    merge); selections, scores and state as ungated."""
+    x = make_inputs(wl)
+    L = x["q"].shape[2]
+    og = make_out_gate(wl, (wl.batch, wl.n_q_heads, L, wl.head_dim))
+    o = dict(P.oracle(wl, x, merge=merge))
+    o["y"] = bf.output_gate(o["y"], _units_rows(wl, og))
+    flags = still.STILL_FLAG_MERGE_SUM if merge == "sum" else 0
+    g = P.gpu_prefill(wl, x, fp32_out=(wl.dtype == "bf16"), flags=flags, out_gate=og)
+    P.compare_prefill(wl, g, o, out_fp32=(wl.dtype == "bf16"))
+    if wl.dtype == "bf16":
+        g2 = P.gpu_prefill(wl, x, fp32_out=False, flags=flags, out_gate=og)
+        P.compare_prefill(wl, g2, o, out_fp32=False, check_state_too=False)
+
+
+@pytest.mark.timeout(900)
+def test_llama8b_L16K_output_gate_sampled_unit():
+    """The 16K workload (batch 1, 32 query / 8 kv heads, d = 128) gated, bf16
+    output as the walk's tiled store writes it; the oracle checks one unit."""
+    wl = WORKLOADS["llama8b_bf16_L16K"]
+    x = make_inputs(wl)
+    og = make_out_gate(wl, (wl.batch, wl.n_q_heads, wl.seq_len, wl.head_dim))
+    units = [(0, 5)]
+    o = dict(P.oracle(wl, x, units=units))
+    G = wl.group
+    o["y"] = bf.output_gate(o["y"], og[0, 5 * G:6 * G].float().numpy()[None])
+    g = P.gpu_prefill(wl, x, fp32_out=False, out_gate=og)
+    P.compare_prefill(wl, g, o, units=units, out_fp32=False)
+
+
+@pytest.mark.parametrize("case", DECODE_SHAPES, ids=[c[0].name for c in DECODE_SHAPES])
+def test_decode_output_gate(case):
+    """Ungated prefill, then still_decode_step_gated steps (chunk boundaries
+    included); outputs against the oracle's run over all L0 + n tokens, gated."""
+    wl, L0, n = case
+    x = make_inputs(wl, seq_len=L0)
+    toks = make_decode_tokens(wl, n)
+    og = make_out_gate(wl, (n, wl.batch, wl.n_q_heads, wl.head_dim), seed=wl.seed + 1)
+    g = P.gpu_prefill(wl, x, keep_device=True)
+    p = still.params_for(wl, fp32_out=True)
+    xd = {k: v.cuda() for k, v in x.items()}
+    td = {k: v.cuda() for k, v in toks.items()}
+    ogd = og.cuda()
+    lam = still.still_lambda(p)
+    outs, sels = [], []
+    for s in range(n):
+        out = torch.empty((wl.batch, wl.n_q_heads, wl.head_dim), dtype=torch.float32, device="cuda")
+        sel = torch.empty((wl.batch, wl.n_kv_heads, max(lam, 1)), dtype=torch.int32, device="cuda")
+        still.still_decode_step_gated(p, L0 + s, td["q"][s], td["k"][s], td["v"][s], xd["fmap_w"],
+                                      xd["gate"], ogd[s], g["_state"], out,
+                                      sel if lam > 0 else None)
+        outs.append(out)
+        sels.append(sel[..., :lam])
+    torch.cuda.synchronize()
+    outs, sels = torch.stack(outs).cpu(), torch.stack(sels).cpu()
+    units = [(b, kv) for b in range(wl.batch) for kv in range(wl.n_kv_heads)]
+    qs, ks, vs, Fs, gs = P.concat_units(x, toks, wl, units)
+    o = rec.run_units(qs, ks, vs, Fs, gs, window=wl.window, chunk=wl.chunk, budget=wl.budget,
+                      t_max=wl.t_max, n_threads=P.n_threads())
+    G = wl.group
+    gate_u = np.stack([og[:, b, kv * G:(kv + 1) * G].float().numpy().transpose(1, 0, 2)
+                       for b, kv in units])
+    yg = np.stack([outs[:, b, kv * G:(kv + 1) * G].numpy().transpose(1, 0, 2) for b, kv in units])
+    P.check_outputs(yg, bf.output_gate(o["y"][:, :, L0:], gate_u), wl.dtype, True, "gated decode y")
+    for s in range(n):
+        t = L0 + s
+        if t % wl.chunk == 0 and o["lam"] > 0:
+            got = np.stack([sels[s, b, kv].numpy() for b, kv in units])
+            assert np.array_equal(got, o["sel"][:, t // wl.chunk - 1]), s
