@@ -270,9 +270,18 @@ int launch_prefill(const Derived& d, const Plan& pl, still::PrefillArgs a, hipSt
   const int nkt = d.C / 16 + (d.W + 14) / 16;  // key tiles of the score kernel
   const size_t lds_score =
       (size_t)nkt * 16 * (D + Pad<T>::v) * sizeof(T) + (size_t)(3 * d.G * d.C + nkt * 16 + 80) * 4;
-  // select: query rows, chunk arrays, per-head float64 results and sums
-  const size_t lds_sel = (size_t)4 * D * 8 + (size_t)d.C * 8 + (size_t)(5 * d.C + 4) * 4 +
-                         (size_t)d.C * d.G * 8 + (size_t)d.C * 8;
+  // select: float64 query rows, then for the undecided tokens their list,
+  // per-head results and sums; for C <= 64 the per-wave counts, the shared
+  // float64 list, per-head results and sums of SEL_CPW chunks; for C > 64
+  // the chunk arrays, per-head results and sums
+  const size_t lds_sel_pend = (size_t)4 * D * 8 + 16 + (size_t)SEL_PEND * d.G * 8 + (size_t)SEL_PEND * 8;
+  const size_t lds_sel_chunk =
+      d.C <= 64 ? (size_t)16 + 64 + (size_t)SEL_CPW * 64 * 4 + (size_t)SEL_CPW * 64 * d.G * 8 + (size_t)SEL_CPW * 64 * 8
+                : (size_t)d.C * 8 + (size_t)(5 * d.C + 4) * 4 + (size_t)d.C * d.G * 8 + (size_t)d.C * 8;
+  const size_t lds_sel = std::max(lds_sel_pend, (size_t)4 * D * 8 + lds_sel_chunk);
+  const int n_sel = (pl.n_pend + SEL_PEND - 1) / SEL_PEND +
+                    (d.C <= 64 ? (pl.n_dec + SEL_CPW - 1) / SEL_CPW : pl.n_dec) +
+                    (d.C <= 64 && a.score_out ? (pl.n_dec + SEL_RCH - 1) / SEL_RCH : 0);
   set_prefill_attrs<T, D>(prefill_family<T, D>());
   // F^T is made by D*D/2048 extra workgroups of the score launch (its
   // events are recorded back to back)
@@ -285,7 +294,7 @@ int launch_prefill(const Derived& d, const Plan& pl, still::PrefillArgs a, hipSt
     route_kernel<T, D><<<dim3(pl.T + D * D / 2048, d.Hkv, d.B), dim3(256), 4 * D * 8, s>>>(a);
   mk.at(1, 1);
   mk.at(2, 0);
-  select_kernel<T, D><<<dim3(pl.n_pend + pl.n_dec, d.Hkv, d.B), dim3(256), lds_sel, s>>>(a);
+  select_kernel<T, D><<<dim3(n_sel, d.Hkv, d.B), dim3(256), lds_sel, s>>>(a);
   mk.at(2, 1);
   mk.at(3, 0);
   if constexpr (sizeof(T) == 2)

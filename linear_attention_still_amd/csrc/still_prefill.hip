@@ -481,61 +481,199 @@ __device__ void score_f64_list(const PrefillArgs& a, int b, int kv, const int* t
 }
 
 // ---------------------------------------------------------- 3. select ----
-// Workgroup x < n_dec decides chunk x [P3 "Delayed Chunk-Level Selection"]:
-// keep lambda_c = lambda tokens while the pool of m - W slots has room
-// [P2 固定预算路由], ranked by (score desc, position asc). The float32 scores
-// with their error bounds give, for every token, an interval; tokens whose
-// upper end is below the lambda-th largest lower end cannot be kept. If more
-// than lambda tokens remain, their scores are recomputed in float64 (one
-// wave per token) and the ranking is made on those (their exported scores
-// become the float64 values rounded once); then the tokens the score kernel
-// listed for export are recomputed in float64. Workgroups x < n_pend (first,
-// so they start early) compute the float64 score of one token of the
-// undecided last chunk each, into the decode state.
+// Chunk c is decided [P3 "Delayed Chunk-Level Selection"]: keep lambda_c =
+// lambda tokens while the pool of m - W slots has room [P2 固定预算路由],
+// ranked by (score desc, position asc). The float32 scores with their error
+// bounds give, for every token, an interval; tokens whose upper end is
+// below the lambda-th largest lower end cannot be kept. If more than lambda
+// tokens remain, their scores are recomputed in float64 and the ranking is
+// made on those (their exported scores become the float64 values rounded
+// once); the tokens the score kernel listed for export are recomputed in
+// float64 as well. The float64 scores of the undecided last chunk's tokens
+// go to the decode state.
+// Workgroups, in launch order: for C <= 64 and exported scores, the
+// recomputation of the listed exported scores of SEL_RCH chunks each; then
+// SEL_PEND tokens of the undecided chunk each; then the decisions, for
+// C <= 64 one chunk per wave (token j in lane j) and SEL_CPW chunks per
+// workgroup, the four waves sharing the float64 scores their chunks need,
+// so that the few chunks that need them finish within the same round as
+// the others; for C > 64 one chunk per workgroup, which also recomputes its
+// listed exported scores.
 // The selection's intervals are [score - m dl, score + m dl] with the score
 // kernel's bound dl widened by SEL_MARGIN: a wider interval only sends more
 // tokens to the float64 ranking, a too narrow one could drop a token the
 // float64 ranking keeps.
 constexpr float SEL_MARGIN = 2.f;
+constexpr int SEL_PEND = 2;  // undecided tokens per workgroup
+constexpr int SEL_CPW = 4;   // chunks per workgroup for C <= 64 (one per wave)
+constexpr int SEL_RCH = 2;   // chunks per workgroup of the exported-score recomputation
+
+// the lam_c-th largest lower bound of a chunk's scores, ranked by (lower
+// bound desc, index asc): one wave, token j in lane j (C <= 64), lam_c
+// rounds of removing the largest; every lane gets it
+__device__ __forceinline__ float lambda_lower_bound(float xl, bool gone, int lam_c) {
+  const int lane = threadIdx.x & 63;
+  float LBv = STILL_NEG_INF;
+  for (int k = 0; k < lam_c; ++k) {
+    float m = row_max<16>(gone ? STILL_NEG_INF : xl);
+    m = fmax_nn(m, xor16f(m));
+    m = fmax_nn(m, xor32f(m));
+    const uint64_t at = __builtin_amdgcn_ballot_w64(!gone && xl == m);
+    const int first = at ? (int)__builtin_ctzll(at) : 64;  // lowest index among the maxima
+    if (lane == first) gone = true;
+    LBv = m;
+  }
+  return LBv;
+}
 
 template <typename T, int D>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void select_kernel(PrefillArgs a) {
   extern __shared__ __align__(16) char smem[];
-  const int x = blockIdx.x, kv = blockIdx.y, b = blockIdx.z;
+  const int kv = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int C = a.C, L = a.L, lam = a.lam, G = a.G;
-  double* qd = reinterpret_cast<double*>(smem);  // [4][D] float64 query rows (one per wave)
-  double* s64 = qd + 4 * D;                        // [C]
-  float* sc = reinterpret_cast<float*>(s64 + C);                          // [C]
-  float* dl = sc + C;                                                      // [C]
-  int* flag = reinterpret_cast<int*>(dl + C);                             // [C] candidate
-  int* keep = flag + C;                                                    // [C]
-  int* list = keep + C;                                                    // [C] float64 tokens
-  int* misc = list + C;  // [4], then (16-byte aligned) the per-head float64 results
   const int unit = b * a.Hkv + kv;
   const size_t ub_off = (size_t)unit * L;
-  double* res = reinterpret_cast<double*>(misc + 4);  // [C][G] per-head float64 scores
-  double* sum = res + (size_t)C * G;                  // [C]
-
   const int c_last = (L - 1) / C, n_pend = L - c_last * C;
-  if (x < n_pend) {
-    // token x of the undecided last chunk: float64 score into the decode
-    // state (and the exported scores); its kept flag is 0
-    const int t = c_last * C + x;
-    if (tid == 0) list[0] = t;
+  const int n_pgrp = (n_pend + SEL_PEND - 1) / SEL_PEND;
+  const int n_rgrp = C <= 64 && a.score_out ? (a.n_dec + SEL_RCH - 1) / SEL_RCH : 0;
+  double* qd = reinterpret_cast<double*>(smem);  // [4][D] float64 query rows (one per wave)
+
+  if ((int)blockIdx.x < n_rgrp) {
+    // exported scores the score kernel listed for SEL_RCH chunks (estimated
+    // float32 error near 1e-5 of the score): recomputed in float64, rounded
+    // once; in workgroups of their own, first, so that their float64 work
+    // spreads evenly and runs beside the selection's
+    int* cnt = reinterpret_cast<int*>(qd + 4 * D);  // [4] tokens per wave
+    int* list = cnt + 4 + 16;                      // [4 * 64] (after the mask slots)
+    double* res = reinterpret_cast<double*>(list + 4 * 64);
+    double* sum = res + (size_t)4 * 64 * G;
+    const int c = (int)blockIdx.x * SEL_RCH + wave;
+    const size_t rl0 = ((size_t)unit * a.T + c) * (C + 1);
+    const int nr = wave < SEL_RCH && c < a.n_dec ? min(a.rlist[rl0], C) : 0;
+    if (lane == 0) cnt[wave] = nr;
     __syncthreads();
-    score_f64_list<T, D>(a, b, kv, list, 1, qd, res, sum);
-    if (tid == 0) {
-      double* pend = reinterpret_cast<double*>(a.state + (size_t)unit * a.st_unit + a.st_pending);
-      pend[x] = sum[0];
-      a.selflag[ub_off + t] = 0;
-      if (a.score_out) a.score[ub_off + t] = (float)sum[0];
-      if (x == 0)
-        for (int i = n_pend; i < C; ++i) pend[i] = __builtin_nan("");
+    int off = 0, total = 0;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      off += w < wave ? cnt[w] : 0;
+      total += cnt[w];
     }
+    if (lane < nr) list[off + lane] = c * C + a.rlist[rl0 + 1 + lane];
+    __syncthreads();
+    if (total == 0) return;  // uniform
+    score_f64_list<T, D>(a, b, kv, list, total, qd, res, sum);
+    for (int i = tid; i < total; i += 256) a.score[ub_off + list[i]] = (float)sum[i];
     return;
   }
-  const int c = x - n_pend, base = c * C;
+  const int x = (int)blockIdx.x - n_rgrp;
+
+  if (x < n_pgrp) {
+    // tokens of the undecided last chunk: float64 scores into the decode
+    // state (and the exported scores); their kept flags are 0
+    int* list = reinterpret_cast<int*>(qd + 4 * D);            // [SEL_PEND]
+    double* res = reinterpret_cast<double*>(list + 4);          // [SEL_PEND][G]
+    double* sum = res + SEL_PEND * G;                           // [SEL_PEND]
+    const int i0 = x * SEL_PEND, n = min(SEL_PEND, n_pend - i0);
+    if (tid < n) list[tid] = c_last * C + i0 + tid;
+    __syncthreads();
+    score_f64_list<T, D>(a, b, kv, list, n, qd, res, sum);
+    double* pend = reinterpret_cast<double*>(a.state + (size_t)unit * a.st_unit + a.st_pending);
+    if (tid < n) {
+      const int t = list[tid];
+      pend[i0 + tid] = sum[tid];
+      a.selflag[ub_off + t] = 0;
+      if (a.score_out) a.score[ub_off + t] = (float)sum[tid];
+    }
+    if (x == 0)
+      for (int i = n_pend + tid; i < C; i += 256) pend[i] = __builtin_nan("");
+    return;
+  }
+
+  if (C <= 64) {
+    // one chunk per wave
+    int* cnt = reinterpret_cast<int*>(qd + 4 * D);                        // [4] float64 tokens per wave
+    uint64_t* msk = reinterpret_cast<uint64_t*>(cnt + 4);                 // [4][2] candidates, float64 tokens
+    int* list = reinterpret_cast<int*>(msk + 8);                          // [SEL_CPW * 64]
+    double* res = reinterpret_cast<double*>(list + SEL_CPW * 64);         // [SEL_CPW * 64][G]
+    double* sum = res + (size_t)SEL_CPW * 64 * G;                         // [SEL_CPW * 64]
+    const int c = (x - n_pgrp) * SEL_CPW + wave;
+    const bool act = c < a.n_dec;  // wave-uniform
+    const int base = c * C;
+    const int lam_c = ((c + 1) * lam <= a.m - a.W) ? lam : 0;
+    const bool partial = act && lam_c > 0 && lam_c < C;  // else none or all are kept
+    uint64_t cand = 0, need = 0;
+    bool rank64 = false;
+    if (act) {
+      const float sc = lane < C ? a.score[ub_off + base + lane] : 0.f;
+      const float dl = lane < C ? a.delta[ub_off + base + lane] : 0.f;
+      if (partial) {
+        const float LB = lambda_lower_bound(lane < C ? sc - SEL_MARGIN * dl : STILL_NEG_INF, lane >= C, lam_c);
+        cand = __builtin_amdgcn_ballot_w64(lane < C && sc + SEL_MARGIN * dl >= LB);
+        rank64 = __builtin_popcountll(cand) > lam_c;
+      }
+      if (rank64) need = cand;
+    }
+    if (lane == 0) {
+      cnt[wave] = __builtin_popcountll(need);
+      msk[2 * wave] = cand;
+      msk[2 * wave + 1] = need;
+    }
+    __syncthreads();
+    int total = 0;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) total += cnt[w];
+    {
+      int off = 0;
+      for (int w = 0; w < wave; ++w) off += cnt[w];
+      const uint64_t below = lane ? (~0ull >> (64 - lane)) : 0ull;
+      if ((need >> lane) & 1ull) list[off + __builtin_popcountll(need & below)] = base + lane;
+    }
+    __syncthreads();
+    if (total > 0) score_f64_list<T, D>(a, b, kv, list, total, qd, res, sum);  // uniform
+    if (!act) return;
+    // (the masks come back from LDS: fewer registers live across the scores)
+    cand = msk[2 * wave];
+    need = msk[2 * wave + 1];
+    int off = 0;
+    for (int w = 0; w < wave; ++w) off += cnt[w];
+    const uint64_t below = lane ? (~0ull >> (64 - lane)) : 0ull;  // lanes under this one
+    const bool in_list = (need >> lane) & 1ull;
+    const double s64 = in_list ? sum[off + __builtin_popcountll(need & below)] : 0.0;
+    rank64 = partial && __builtin_popcountll(cand) > lam_c;
+    bool kept = lane < C && lam_c == C;
+    if (partial) {
+      kept = (cand >> lane) & 1ull;
+      if (rank64) {  // uniform; every lane takes part in the shuffles
+        int r = 0;
+        for (uint64_t mm = cand; mm; mm &= mm - 1) {  // the candidates, in index order
+          const int i = __builtin_ctzll(mm);
+          const double si = __shfl(s64, i);
+          r += (si > s64 || (si == s64 && i < lane)) ? 1 : 0;
+        }
+        kept = kept && r < lam_c;
+      }
+    }
+    if (lane < C) a.selflag[ub_off + base + lane] = (uint8_t)kept;
+    int32_t* selrow = a.sel + ((size_t)unit * a.n_dec + c) * lam;
+    const uint64_t km = __builtin_amdgcn_ballot_w64(kept);
+    if (kept) selrow[__builtin_popcountll(km & below)] = base + lane;
+    for (int i = lam_c + lane; i < lam; i += 64) selrow[i] = -1;
+    if (a.score_out && in_list) a.score[ub_off + base + lane] = (float)s64;
+    return;
+  }
+
+  // C > 64: one chunk per workgroup
+  double* s64 = qd + 4 * D;                        // [C]
+  float* sc = reinterpret_cast<float*>(s64 + C);   // [C]
+  float* dl = sc + C;                              // [C]
+  int* flag = reinterpret_cast<int*>(dl + C);      // [C] candidate
+  int* keep = flag + C;                            // [C]
+  int* list = keep + C;                            // [C] float64 tokens
+  int* misc = list + C;  // [4], then (16-byte aligned) the per-head float64 results
+  double* res = reinterpret_cast<double*>(misc + 4);  // [C][G] per-head float64 scores
+  double* sum = res + (size_t)C * G;                  // [C]
+  const int c = x - n_pgrp, base = c * C;
   const int lam_c = ((c + 1) * lam <= a.m - a.W) ? lam : 0;
   const bool partial = lam_c > 0 && lam_c < C;  // else none or all are kept
   int32_t* selrow = a.sel + ((size_t)unit * a.n_dec + c) * lam;
@@ -550,31 +688,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void s
   __syncthreads();
   // the lam_c-th largest lower bound, ranked by (lower bound desc, index asc)
   if (partial) {
-    if (C <= 64) {  // one wave, token j in lane j: lam_c rounds of removing the largest
-      if (tid < 64) {
-        float xl = lane < C ? sc[lane] - SEL_MARGIN * dl[lane] : STILL_NEG_INF, LBv = STILL_NEG_INF;
-        bool gone = lane >= C;
-        for (int k = 0; k < lam_c; ++k) {
-          float m = row_max<16>(gone ? STILL_NEG_INF : xl);
-          m = fmax_nn(m, xor16f(m));
-          m = fmax_nn(m, xor32f(m));
-          const uint64_t at = __builtin_amdgcn_ballot_w64(!gone && xl == m);
-          const int first = at ? (int)__builtin_ctzll(at) : 64;  // lowest index among the maxima
-          if (lane == first) gone = true;
-          LBv = m;
-        }
-        if (lane == 0) misc[2] = __float_as_int(LBv);
+    for (int j = tid; j < C; j += 256) {
+      const float lj = sc[j] - SEL_MARGIN * dl[j];
+      int r = 0;
+      for (int i = 0; i < C; ++i) {
+        const float li = sc[i] - SEL_MARGIN * dl[i];
+        r += (li > lj || (li == lj && i < j)) ? 1 : 0;
       }
-    } else {
-      for (int j = tid; j < C; j += 256) {
-        const float lj = sc[j] - SEL_MARGIN * dl[j];
-        int r = 0;
-        for (int i = 0; i < C; ++i) {
-          const float li = sc[i] - SEL_MARGIN * dl[i];
-          r += (li > lj || (li == lj && i < j)) ? 1 : 0;
-        }
-        if (r == lam_c - 1) misc[2] = __float_as_int(lj);
-      }
+      if (r == lam_c - 1) misc[2] = __float_as_int(lj);
     }
   }
   __syncthreads();
@@ -624,8 +745,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void s
     }
   }
   for (int i = lam_c + tid; i < lam; i += 256) selrow[i] = -1;
-  // exported scores the score kernel listed (estimated float32 error near
-  // 1e-5 of the score): recomputed in float64, rounded once
+  // exported scores the score kernel listed: recomputed in float64
   if (!a.score_out) return;
   const int* rl = a.rlist + ((size_t)unit * a.T + c) * (C + 1);
   const int nr = min(rl[0], C);
