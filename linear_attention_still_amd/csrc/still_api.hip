@@ -188,6 +188,8 @@ void set_prefill_attrs(int family) {
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) dev = 0;
   std::lock_guard<std::mutex> lk(g_attr_mu);
   if (g_attr_done[dev] & (1ull << family)) return;
+  (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&still::score_kernel<T, D>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
   (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&still::attend_kernel<T, D, 1>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)still::Blk<T, D>::bytes);
   (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&still::attend_kernel<T, D, 2>),
@@ -268,8 +270,14 @@ int launch_prefill(const Derived& d, const Plan& pl, still::PrefillArgs a, hipSt
                    const Marks& mk) {
   using namespace still;
   const int nkt = d.C / 16 + (d.W + 14) / 16;  // key tiles of the score kernel
+  // the chunks are decided by the score kernel for the Self-Saliency route
+  // with C <= 64 (its LDS then also holds the decision's arrays), else by
+  // the select kernel
+  const bool fuse = a.route == ROUTE_SALIENCY && d.C <= 64;
+  a.fuse_sel = fuse ? 1 : 0;
   const size_t lds_score =
-      (size_t)nkt * 16 * (D + Pad<T>::v) * sizeof(T) + (size_t)(3 * d.G * d.C + nkt * 16 + 80) * 4;
+      (size_t)nkt * 16 * (D + Pad<T>::v) * sizeof(T) + (size_t)(3 * d.G * d.C + nkt * 16 + 80) * 4 +
+      (fuse ? (size_t)3 * d.C * 4 + score_decide_bytes(d.C, d.G, D) : 0);
   // select: float64 query rows, then for the undecided tokens their list,
   // per-head results and sums; for C <= 64 the per-wave counts, the shared
   // float64 list, per-head results and sums of SEL_CPW chunks; for C > 64
@@ -279,6 +287,7 @@ int launch_prefill(const Derived& d, const Plan& pl, still::PrefillArgs a, hipSt
       d.C <= 64 ? (size_t)16 + 64 + (size_t)SEL_CPW * 64 * 4 + (size_t)SEL_CPW * 64 * d.G * 8 + (size_t)SEL_CPW * 64 * 8
                 : (size_t)d.C * 8 + (size_t)(5 * d.C + 4) * 4 + (size_t)d.C * d.G * 8 + (size_t)d.C * 8;
   const size_t lds_sel = std::max(lds_sel_pend, (size_t)4 * D * 8 + lds_sel_chunk);
+  const size_t lds_pend = fuse ? lds_sel_pend : 0;
   const int n_sel = (pl.n_pend + SEL_PEND - 1) / SEL_PEND +
                     (d.C <= 64 ? (pl.n_dec + SEL_CPW - 1) / SEL_CPW : pl.n_dec) +
                     (d.C <= 64 && a.score_out ? (pl.n_dec + SEL_RCH - 1) / SEL_RCH : 0);
@@ -294,7 +303,7 @@ int launch_prefill(const Derived& d, const Plan& pl, still::PrefillArgs a, hipSt
     route_kernel<T, D><<<dim3(pl.T + D * D / 2048, d.Hkv, d.B), dim3(256), 4 * D * 8, s>>>(a);
   mk.at(1, 1);
   mk.at(2, 0);
-  select_kernel<T, D><<<dim3(n_sel, d.Hkv, d.B), dim3(256), lds_sel, s>>>(a);
+  if (!fuse) select_kernel<T, D><<<dim3(n_sel, d.Hkv, d.B), dim3(256), lds_sel, s>>>(a);
   mk.at(2, 1);
   mk.at(3, 0);
   if constexpr (sizeof(T) == 2)
@@ -310,8 +319,9 @@ int launch_prefill(const Derived& d, const Plan& pl, still::PrefillArgs a, hipSt
   const int n_ring_grp = (pl.L - ring_lo + 63) / 64;
   const int n_pool = pool_count_at(pl.n_dec, d.lam, d.cap_chunks);
   const int n_pool_grp = n_pool > 0 ? (n_pool + 15) / 16 : 1;  // >= 1: it writes the position
-  state_scan_kernel<T, D><<<dim3(n_scan + n_ring_grp + n_pool_grp, d.Hkv, d.B), dim3(256), Blk<T, D>::ft_bytes, s>>>(
-      a, n_scan);
+  const int n_pend_grp = fuse ? (pl.n_pend + SEL_PEND - 1) / SEL_PEND : 0;
+  state_scan_kernel<T, D><<<dim3(n_pend_grp + n_scan + n_ring_grp + n_pool_grp, d.Hkv, d.B), dim3(256),
+                            std::max(Blk<T, D>::ft_bytes, lds_pend), s>>>(a, n_pend_grp, n_scan);
   mk.at(4, 1);
   mk.at(5, 0);
   if (pl.part)

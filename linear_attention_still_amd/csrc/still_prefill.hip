@@ -56,6 +56,7 @@ struct PrefillArgs {
   int* rlist;     // [B][Hkv][T][C + 1] tokens whose exported score is refined
   int route;      // routing metric (ROUTE_*)
   const void* out_gate;    // [B][Hq][L][D] T: channel-wise output gate before the sigmoid, or null
+  int fuse_sel;            // the score kernel decides the chunks (Self-Saliency route, C <= 64)
   const float* ext_score;  // [B][Hkv][L] the caller's scores (ROUTE_EXTERNAL)
   float scale, eps;
   double scale64, eps64;  // the same parameters for the float64 paths
@@ -99,7 +100,10 @@ __device__ __forceinline__ void fmap_transpose_part(const PrefillArgs& a, int bx
 // are summed through LDS and the float32 score is written with a bound on
 // its float32 evaluation error.
 template <typename T, int D>
-__global__ __launch_bounds__(256) void score_kernel(PrefillArgs a) {
+__device__ void score_decide(const PrefillArgs& a, int b, int kv, int c, const T* Ks, int kbase, int KS,
+                             const float* sc, const float* dl, const int* rl, int nrl, char* scr);
+template <typename T, int D>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void score_kernel(PrefillArgs a) {
   extern __shared__ __align__(16) char smem[];
   if ((int)blockIdx.x >= a.T) {  // the extra workgroups: F^T (batch row 0's)
     if (blockIdx.z == 0) fmap_transpose_part<T, D>(a, (int)blockIdx.x - a.T, (int)blockIdx.y);
@@ -121,6 +125,11 @@ __global__ __launch_bounds__(256) void score_kernel(PrefillArgs a) {
   float* pdel = part + G * C;
   float* pest = pdel + G * C;
   float* knrm = pest + G * C;  // [nkt * 16 + 80] key norms (tiles past the last of a group of five read zeros)
+  // with the decision in this kernel: the chunk's scores, bounds and listed
+  // positions, then the decision's scratch
+  float* sfin = knrm + nkt * 16 + 80;  // [C]
+  float* dfin = sfin + C;              // [C]
+  int* rll = reinterpret_cast<int*>(dfin + C);  // [C]
 
   const T* kg = reinterpret_cast<const T*>(a.k) + (size_t)(b * a.Hkv + kv) * L * D;
   constexpr int VEC = 16 / sizeof(T);
@@ -308,11 +317,23 @@ __global__ __launch_bounds__(256) void score_kernel(PrefillArgs a) {
     const size_t o = (size_t)(b * a.Hkv + kv) * L + t;
     a.score[o] = s;
     a.delta[o] = d;
-    if (a.score_out && c * C + C < L && e > 6e-6f * fmaxf(1.f, fabsf(s)))
-      rl[1 + atomicAdd(n_list, 1)] = qi;  // (the last chunk's are all recomputed)
+    if (a.fuse_sel) {
+      sfin[qi] = s;
+      dfin[qi] = d;
+    }
+    if (a.score_out && c * C + C < L && e > 6e-6f * fmaxf(1.f, fabsf(s))) {
+      const int k = atomicAdd(n_list, 1);  // (the last chunk's are all recomputed)
+      if (a.fuse_sel) rll[k] = qi;
+      else rl[1 + k] = qi;
+    }
   }
   __syncthreads();
-  if (tid == 0) rl[0] = *n_list;  // 0 unless the scores are exported
+  if (!a.fuse_sel) {
+    if (tid == 0) rl[0] = *n_list;  // 0 unless the scores are exported
+    return;
+  }
+  score_decide<T, D>(a, b, kv, c, Ks, kbase, KS, sfin, dfin, rll, *n_list,
+                     reinterpret_cast<char*>(rll + C));
 }
 
 // Float64 score of head h (of the kv group) for token t [P3 "Self-Saliency
@@ -324,10 +345,12 @@ __global__ __launch_bounds__(256) void score_kernel(PrefillArgs a) {
 // the softmax sums run online over the 64-key slots and the two-point KL
 // form takes 1-p from the other keys. Every lane returns the head's score.
 // diag: return the window softmax's weight on the token itself instead (the
-// diagonal-attention routing metric).
-template <typename T, int D>
+// diagonal-attention routing metric). KL: the key rows come from LDS instead,
+// row j at klds + (j - kbase) * kstride (the score kernel's staged window).
+template <typename T, int D, bool KL = false>
 __device__ double score_f64_head(const PrefillArgs& a, int b, int kv, int h, int t, double* qd,
-                                 bool diag = false) {
+                                 bool diag = false, const T* klds = nullptr, int kbase = 0,
+                                 int kstride = D) {
   const int lane = threadIdx.x & 63;
   const int W = a.W, G = a.G, L = a.L;
   const int n = t - W + 1 > 0 ? W : t + 1;
@@ -349,8 +372,9 @@ __device__ double score_f64_head(const PrefillArgs& a, int b, int kv, int h, int
   double m = -__builtin_huge_val(), za = 0.0, zo = 0.0, zt = 0.0;  // uniform
   for (int s = 0; 64 * s < n; ++s) {  // uniform
     const int j = lane + 64 * s;
-    const T* krow =
-        reinterpret_cast<const T*>(a.k) + ((size_t)(b * a.Hkv + kv) * L + (t - n + 1 + (j < n ? j : 0))) * D;
+    const int kj = t - n + 1 + (j < n ? j : 0);
+    const T* krow = KL ? klds + (size_t)(kj - kbase) * kstride
+                       : reinterpret_cast<const T*>(a.k) + ((size_t)(b * a.Hkv + kv) * L + kj) * D;
     // query doubles as 16-byte pairs (read here, not hoisted out of the loop)
     typedef double f64x2 __attribute__((ext_vector_type(2)));
     const f64x2* q2 = reinterpret_cast<const f64x2*>(lds_opaque_v(qd));
@@ -462,13 +486,17 @@ __global__ __launch_bounds__(256) void route_kernel(PrefillArgs a) {
 // head) pairs are dealt to the waves, each head's score lands in res[i][h]
 // and every token's sum is taken in head order (tok_t: the tokens; qd: [4][D]
 // float64). Ends with a barrier; the sums are left in sum[i].
-template <typename T, int D>
+// KL: the Self-Saliency Score with the key rows from the score kernel's LDS
+// window (klds, kbase, kstride as for score_f64_head).
+template <typename T, int D, bool KL = false>
 __device__ void score_f64_list(const PrefillArgs& a, int b, int kv, const int* tok_t, int n_tok,
-                               double* qd, double* res, double* sum) {
+                               double* qd, double* res, double* sum, const T* klds = nullptr,
+                               int kbase = 0, int kstride = D) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, G = a.G;
   for (int pi = wave; pi < n_tok * G; pi += 4) {  // wave-uniform
     const int i = pi / G, h = pi % G, t = tok_t[i];
-    const double s = route_f64_head<T, D>(a, b, kv, h, t, qd + wave * D);
+    const double s = KL ? score_f64_head<T, D, true>(a, b, kv, h, t, qd + wave * D, false, klds, kbase, kstride)
+                        : route_f64_head<T, D>(a, b, kv, h, t, qd + wave * D);
     if (lane == 0) res[pi] = s;
   }
   __syncthreads();
@@ -526,6 +554,120 @@ __device__ __forceinline__ float lambda_lower_bound(float xl, bool gone, int lam
   return LBv;
 }
 
+// Float64 scores of SEL_PEND tokens (group x) of the undecided last chunk of
+// unit (kv, b) into the decode state's pending scores, and the exported
+// scores; flags: also their kept flags (0). LDS: [4][D] float64 query rows,
+// then the list, per-head results and sums.
+template <typename T, int D>
+__device__ void pending_part(const PrefillArgs& a, int x, int kv, int b, bool flags) {
+  extern __shared__ __align__(16) char smem[];
+  const int tid = threadIdx.x, C = a.C, L = a.L, G = a.G;
+  const int unit = b * a.Hkv + kv;
+  const size_t ub_off = (size_t)unit * L;
+  const int c_last = (L - 1) / C, n_pend = L - c_last * C;
+  double* qd = reinterpret_cast<double*>(smem);               // [4][D]
+  int* list = reinterpret_cast<int*>(qd + 4 * D);            // [SEL_PEND]
+  double* res = reinterpret_cast<double*>(list + 4);          // [SEL_PEND][G]
+  double* sum = res + SEL_PEND * G;                           // [SEL_PEND]
+  const int i0 = x * SEL_PEND, n = min(SEL_PEND, n_pend - i0);
+  if (tid < n) list[tid] = c_last * C + i0 + tid;
+  __syncthreads();
+  score_f64_list<T, D>(a, b, kv, list, n, qd, res, sum);
+  double* pend = reinterpret_cast<double*>(a.state + (size_t)unit * a.st_unit + a.st_pending);
+  if (tid < n) {
+    const int t = list[tid];
+    pend[i0 + tid] = sum[tid];
+    if (flags) a.selflag[ub_off + t] = 0;
+    if (a.score_out) a.score[ub_off + t] = (float)sum[tid];
+  }
+  if (x == 0)
+    for (int i = n_pend + tid; i < C; i += 256) pend[i] = __builtin_nan("");
+}
+
+// Bytes of score_decide's LDS scratch.
+__host__ __device__ constexpr size_t score_decide_bytes(int C, int G, int D) {
+  return (size_t)8 * (4 * D + C * G + C + 2) + (size_t)4 * (C + 4);
+}
+
+// The decision of chunk c inside the score kernel's workgroup (the Self-
+// Saliency route, C <= 64): the select kernel's interval test and float64
+// ranking for one chunk (token j in lane j of wave 0), with the float64
+// scores' key rows read from the window the score kernel staged in LDS
+// (Ks: rows kbase, kbase + 1, ... of stride KS); the chunk's listed
+// exported scores (rl: nrl positions) are recomputed in float64 in the same
+// pass. sc, dl: the chunk's float32 scores and bounds; scr: LDS scratch of
+// score_decide_bytes(C, G, D) bytes. The undecided last chunk only gets its
+// kept flags (0): its float64 scores are made by pending_part. Called by
+// every thread of the workgroup.
+template <typename T, int D>
+__device__ void score_decide(const PrefillArgs& a, int b, int kv, int c, const T* Ks, int kbase, int KS,
+                             const float* sc, const float* dl, const int* rl, int nrl, char* scr) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int C = a.C, L = a.L, lam = a.lam, G = a.G;
+  const int unit = b * a.Hkv + kv;
+  const size_t ub_off = (size_t)unit * L;
+  const int base = c * C;
+  if (c >= a.n_dec) {  // uniform
+    for (int j = tid; j < C && base + j < L; j += 256) a.selflag[ub_off + base + j] = 0;
+    return;
+  }
+  double* qd = reinterpret_cast<double*>(scr);           // [4][D]
+  double* res = qd + 4 * D;                              // [C][G]
+  double* sum = res + (size_t)C * G;                     // [C]
+  uint64_t* msk = reinterpret_cast<uint64_t*>(sum + C);  // candidates, float64 tokens
+  int* list = reinterpret_cast<int*>(msk + 2);           // [C]
+  int* cnt = list + C;
+  const int lam_c = ((c + 1) * lam <= a.m - a.W) ? lam : 0;
+  const bool partial = lam_c > 0 && lam_c < C;  // else none or all are kept
+  const uint64_t below = lane ? (~0ull >> (64 - lane)) : 0ull;  // lanes under this one
+  if (wave == 0) {
+    const float s = lane < C ? sc[lane] : 0.f, d = lane < C ? dl[lane] : 0.f;
+    uint64_t cand = 0;
+    bool rank64 = false;
+    if (partial) {
+      const float LB = lambda_lower_bound(lane < C ? s - SEL_MARGIN * d : STILL_NEG_INF, lane >= C, lam_c);
+      cand = __builtin_amdgcn_ballot_w64(lane < C && s + SEL_MARGIN * d >= LB);
+      rank64 = __builtin_popcountll(cand) > lam_c;
+    }
+    bool mine = false;
+    for (int i = 0; i < nrl; ++i) mine = mine || rl[i] == lane;
+    const uint64_t need = (rank64 ? cand : 0ull) | __builtin_amdgcn_ballot_w64(mine);
+    if ((need >> lane) & 1ull) list[__builtin_popcountll(need & below)] = base + lane;
+    if (lane == 0) {
+      msk[0] = cand;
+      msk[1] = need;
+      *cnt = __builtin_popcountll(need);
+    }
+  }
+  __syncthreads();
+  const int total = *cnt;
+  if (total > 0) score_f64_list<T, D, true>(a, b, kv, list, total, qd, res, sum, Ks, kbase, KS);  // uniform
+  if (wave != 0) return;
+  const uint64_t cand = msk[0], need = msk[1];
+  const bool rank64 = partial && __builtin_popcountll(cand) > lam_c;
+  const bool in_list = (need >> lane) & 1ull;
+  const double s64 = in_list ? sum[__builtin_popcountll(need & below)] : 0.0;
+  bool kept = lane < C && lam_c == C;
+  if (partial) {
+    kept = (cand >> lane) & 1ull;
+    if (rank64) {  // uniform; every lane takes part in the shuffles
+      int r = 0;
+      for (uint64_t mm = cand; mm; mm &= mm - 1) {  // the candidates, in index order
+        const int i = __builtin_ctzll(mm);
+        const double si = __shfl(s64, i);
+        r += (si > s64 || (si == s64 && i < lane)) ? 1 : 0;
+      }
+      kept = kept && r < lam_c;
+    }
+  }
+  if (lane < C) a.selflag[ub_off + base + lane] = (uint8_t)kept;
+  int32_t* selrow = a.sel + ((size_t)unit * a.n_dec + c) * lam;
+  const uint64_t km = __builtin_amdgcn_ballot_w64(kept);
+  if (kept) selrow[__builtin_popcountll(km & below)] = base + lane;
+  for (int i = lam_c + lane; i < lam; i += 64) selrow[i] = -1;
+  if (a.score_out && in_list) a.score[ub_off + base + lane] = (float)s64;
+}
+
 template <typename T, int D>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void select_kernel(PrefillArgs a) {
   extern __shared__ __align__(16) char smem[];
@@ -569,24 +711,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void s
   const int x = (int)blockIdx.x - n_rgrp;
 
   if (x < n_pgrp) {
-    // tokens of the undecided last chunk: float64 scores into the decode
-    // state (and the exported scores); their kept flags are 0
-    int* list = reinterpret_cast<int*>(qd + 4 * D);            // [SEL_PEND]
-    double* res = reinterpret_cast<double*>(list + 4);          // [SEL_PEND][G]
-    double* sum = res + SEL_PEND * G;                           // [SEL_PEND]
-    const int i0 = x * SEL_PEND, n = min(SEL_PEND, n_pend - i0);
-    if (tid < n) list[tid] = c_last * C + i0 + tid;
-    __syncthreads();
-    score_f64_list<T, D>(a, b, kv, list, n, qd, res, sum);
-    double* pend = reinterpret_cast<double*>(a.state + (size_t)unit * a.st_unit + a.st_pending);
-    if (tid < n) {
-      const int t = list[tid];
-      pend[i0 + tid] = sum[tid];
-      a.selflag[ub_off + t] = 0;
-      if (a.score_out) a.score[ub_off + t] = (float)sum[tid];
-    }
-    if (x == 0)
-      for (int i = n_pend + tid; i < C; i += 256) pend[i] = __builtin_nan("");
+    pending_part<T, D>(a, x, kv, b, true);
     return;
   }
 
@@ -1923,18 +2048,23 @@ __device__ __forceinline__ void state_scan_part(int bx, float* dS, int NS, char*
   }
 }
 
-// The scan (workgroups x < n_scan) and the decode-state export (the rest,
-// x - n_scan as the export's workgroup index) in one launch: the export
-// depends only on the selection and the inputs, so it runs beside the scan
-// instead of after the attention walk.
+// The float64 scores of the undecided chunk's tokens when the score kernel
+// made the decisions (workgroups x < n_pend_grp, SEL_PEND tokens each), the
+// scan (the next n_scan) and the decode-state export (the rest) in one
+// launch: none of them depends on another or on the attention walk, so they
+// run side by side.
 template <typename T, int D>
 __device__ void export_part(const PrefillArgs& a, int x);
 template <typename T, int D>
-__global__ __launch_bounds__(256) void state_scan_kernel(PrefillArgs a, int n_scan) {
-  if ((int)blockIdx.x < n_scan)
-    state_scan_part<D>((int)blockIdx.x, a.dS, a.NS, a.state, a.st_unit, a.st_S, a.st_z);
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void state_scan_kernel(
+    PrefillArgs a, int n_pend_grp, int n_scan) {
+  const int x = blockIdx.x;
+  if (x < n_pend_grp)
+    pending_part<T, D>(a, x, blockIdx.y, blockIdx.z, false);
+  else if (x < n_pend_grp + n_scan)
+    state_scan_part<D>(x - n_pend_grp, a.dS, a.NS, a.state, a.st_unit, a.st_S, a.st_z);
   else
-    export_part<T, D>(a, (int)blockIdx.x - n_scan);
+    export_part<T, D>(a, x - n_pend_grp - n_scan);
 }
 
 // ---------------------------------------------------------- 6. attend ----
