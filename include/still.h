@@ -211,8 +211,7 @@ int still_prefill_gated(const still_params* p, int64_t seq_len, const void* q, c
  * back to back), 1 score, 2 select, 3 state deltas, 4 state scan,
  * 5 attention walk, 6 state export; a kernel not launched for a given
  * length gets its two events recorded back to back (so does 2, select, where
- * the score kernel decides the chunks: Self-Saliency routing with C <= 64;
- * the undecided chunk's float64 scores are then made in the scan launch).
+ * the score kernel decides the chunks: Self-Saliency routing with C <= 64).
  * n_pairs <= 7. Same
  * results and errors as still_prefill. */
 int still_prefill_timed(const still_params* p, int64_t seq_len, const void* q, const void* k,

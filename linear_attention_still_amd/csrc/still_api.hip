@@ -275,6 +275,7 @@ int launch_prefill(const Derived& d, const Plan& pl, still::PrefillArgs a, hipSt
   // the select kernel
   const bool fuse = a.route == ROUTE_SALIENCY && d.C <= 64;
   a.fuse_sel = fuse ? 1 : 0;
+  a.n_pend_grp = fuse ? (pl.n_pend + SCORE_PEND - 1) / SCORE_PEND : 0;
   const size_t lds_score =
       (size_t)nkt * 16 * (D + Pad<T>::v) * sizeof(T) + (size_t)(3 * d.G * d.C + nkt * 16 + 80) * 4 +
       (fuse ? (size_t)3 * d.C * 4 + score_decide_bytes(d.C, d.G, D) : 0);
@@ -287,7 +288,6 @@ int launch_prefill(const Derived& d, const Plan& pl, still::PrefillArgs a, hipSt
       d.C <= 64 ? (size_t)16 + 64 + (size_t)SEL_CPW * 64 * 4 + (size_t)SEL_CPW * 64 * d.G * 8 + (size_t)SEL_CPW * 64 * 8
                 : (size_t)d.C * 8 + (size_t)(5 * d.C + 4) * 4 + (size_t)d.C * d.G * 8 + (size_t)d.C * 8;
   const size_t lds_sel = std::max(lds_sel_pend, (size_t)4 * D * 8 + lds_sel_chunk);
-  const size_t lds_pend = fuse ? lds_sel_pend : 0;
   const int n_sel = (pl.n_pend + SEL_PEND - 1) / SEL_PEND +
                     (d.C <= 64 ? (pl.n_dec + SEL_CPW - 1) / SEL_CPW : pl.n_dec) +
                     (d.C <= 64 && a.score_out ? (pl.n_dec + SEL_RCH - 1) / SEL_RCH : 0);
@@ -298,7 +298,7 @@ int launch_prefill(const Derived& d, const Plan& pl, still::PrefillArgs a, hipSt
   mk.at(0, 1);
   mk.at(1, 0);
   if (a.route == ROUTE_SALIENCY)
-    score_kernel<T, D><<<dim3(pl.T + D * D / 2048, d.Hkv, d.B), dim3(256), lds_score, s>>>(a);
+    score_kernel<T, D><<<dim3(a.n_pend_grp + pl.T + D * D / 2048, d.Hkv, d.B), dim3(256), lds_score, s>>>(a);
   else
     route_kernel<T, D><<<dim3(pl.T + D * D / 2048, d.Hkv, d.B), dim3(256), 4 * D * 8, s>>>(a);
   mk.at(1, 1);
@@ -319,9 +319,8 @@ int launch_prefill(const Derived& d, const Plan& pl, still::PrefillArgs a, hipSt
   const int n_ring_grp = (pl.L - ring_lo + 63) / 64;
   const int n_pool = pool_count_at(pl.n_dec, d.lam, d.cap_chunks);
   const int n_pool_grp = n_pool > 0 ? (n_pool + 15) / 16 : 1;  // >= 1: it writes the position
-  const int n_pend_grp = fuse ? (pl.n_pend + SEL_PEND - 1) / SEL_PEND : 0;
-  state_scan_kernel<T, D><<<dim3(n_pend_grp + n_scan + n_ring_grp + n_pool_grp, d.Hkv, d.B), dim3(256),
-                            std::max(Blk<T, D>::ft_bytes, lds_pend), s>>>(a, n_pend_grp, n_scan);
+  state_scan_kernel<T, D><<<dim3(n_scan + n_ring_grp + n_pool_grp, d.Hkv, d.B), dim3(256), Blk<T, D>::ft_bytes, s>>>(
+      a, n_scan);
   mk.at(4, 1);
   mk.at(5, 0);
   if (pl.part)

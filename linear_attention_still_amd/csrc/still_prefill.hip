@@ -57,6 +57,7 @@ struct PrefillArgs {
   int route;      // routing metric (ROUTE_*)
   const void* out_gate;    // [B][Hq][L][D] T: channel-wise output gate before the sigmoid, or null
   int fuse_sel;            // the score kernel decides the chunks (Self-Saliency route, C <= 64)
+  int n_pend_grp;          // with fuse_sel: score workgroups (first) for the undecided chunk's float64 scores
   const float* ext_score;  // [B][Hkv][L] the caller's scores (ROUTE_EXTERNAL)
   float scale, eps;
   double scale64, eps64;  // the same parameters for the float64 paths
@@ -103,13 +104,21 @@ template <typename T, int D>
 __device__ void score_decide(const PrefillArgs& a, int b, int kv, int c, const T* Ks, int kbase, int KS,
                              const float* sc, const float* dl, const int* rl, int nrl, char* scr);
 template <typename T, int D>
+__device__ void score_pending(const PrefillArgs& a, int b, int kv, int x, const T* Ks, int kbase, int KS,
+                              char* scr);
+template <typename T, int D>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void score_kernel(PrefillArgs a) {
   extern __shared__ __align__(16) char smem[];
-  if ((int)blockIdx.x >= a.T) {  // the extra workgroups: F^T (batch row 0's)
-    if (blockIdx.z == 0) fmap_transpose_part<T, D>(a, (int)blockIdx.x - a.T, (int)blockIdx.y);
+  const int npg = a.n_pend_grp;
+  if ((int)blockIdx.x >= npg + a.T) {  // the extra workgroups: F^T (batch row 0's)
+    if (blockIdx.z == 0) fmap_transpose_part<T, D>(a, (int)blockIdx.x - npg - a.T, (int)blockIdx.y);
     return;
   }
-  const int c = blockIdx.x, kv = blockIdx.y, b = blockIdx.z;
+  // workgroups x < npg (first, so their float64 work overlaps the rest):
+  // the undecided last chunk's float64 scores, from its window staged as
+  // for that chunk
+  const bool pend_grp = (int)blockIdx.x < npg;  // uniform
+  const int c = pend_grp ? a.T - 1 : (int)blockIdx.x - npg, kv = blockIdx.y, b = blockIdx.z;
   const int L = a.L, C = a.C, W = a.W, G = a.G;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // in an SGPR
@@ -181,6 +190,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void s
   }
   for (int i = nkt * 16 + tid; i < nkt * 16 + 80; i += 256) knrm[i] = 0.f;
   __syncthreads();
+  if (pend_grp) {
+    score_pending<T, D>(a, b, kv, (int)blockIdx.x, Ks, kbase, KS, reinterpret_cast<char*>(rll + C));
+    return;
+  }
 
   for (int rt = wave; rt < n_rt; rt += 4) {
     const int hl = rt / n_qt, qt = rt % n_qt;
@@ -315,7 +328,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void s
       e += pest[hl * C + qi];
     }
     const size_t o = (size_t)(b * a.Hkv + kv) * L + t;
-    a.score[o] = s;
+    if (!(a.fuse_sel && c >= a.n_dec)) a.score[o] = s;  // (else the float64 score is written)
     a.delta[o] = d;
     if (a.fuse_sel) {
       sfin[qi] = s;
@@ -556,10 +569,10 @@ __device__ __forceinline__ float lambda_lower_bound(float xl, bool gone, int lam
 
 // Float64 scores of SEL_PEND tokens (group x) of the undecided last chunk of
 // unit (kv, b) into the decode state's pending scores, and the exported
-// scores; flags: also their kept flags (0). LDS: [4][D] float64 query rows,
-// then the list, per-head results and sums.
+// scores; their kept flags are 0. LDS: [4][D] float64 query rows, then the
+// list, per-head results and sums.
 template <typename T, int D>
-__device__ void pending_part(const PrefillArgs& a, int x, int kv, int b, bool flags) {
+__device__ void pending_part(const PrefillArgs& a, int x, int kv, int b) {
   extern __shared__ __align__(16) char smem[];
   const int tid = threadIdx.x, C = a.C, L = a.L, G = a.G;
   const int unit = b * a.Hkv + kv;
@@ -577,7 +590,7 @@ __device__ void pending_part(const PrefillArgs& a, int x, int kv, int b, bool fl
   if (tid < n) {
     const int t = list[tid];
     pend[i0 + tid] = sum[tid];
-    if (flags) a.selflag[ub_off + t] = 0;
+    a.selflag[ub_off + t] = 0;
     if (a.score_out) a.score[ub_off + t] = (float)sum[tid];
   }
   if (x == 0)
@@ -668,6 +681,35 @@ __device__ void score_decide(const PrefillArgs& a, int b, int kv, int c, const T
   if (a.score_out && in_list) a.score[ub_off + base + lane] = (float)s64;
 }
 
+// The float64 scores of SCORE_PEND tokens (group x) of the undecided last
+// chunk inside the score launch, with the key rows from the chunk's window
+// staged in LDS (Ks, kbase, KS as for score_decide): into the decode state's
+// pending scores and the exported scores. scr: score_decide's scratch.
+constexpr int SCORE_PEND = 4;
+template <typename T, int D>
+__device__ void score_pending(const PrefillArgs& a, int b, int kv, int x, const T* Ks, int kbase, int KS,
+                              char* scr) {
+  const int tid = threadIdx.x, C = a.C, L = a.L, G = a.G;
+  const int unit = b * a.Hkv + kv;
+  const size_t ub_off = (size_t)unit * L;
+  const int c_last = (L - 1) / C, n_pend = L - c_last * C;
+  double* qd = reinterpret_cast<double*>(scr);           // [4][D]
+  double* res = qd + 4 * D;                              // [SCORE_PEND][G]
+  double* sum = res + SCORE_PEND * G;                    // [SCORE_PEND]
+  int* list = reinterpret_cast<int*>(sum + SCORE_PEND);  // [SCORE_PEND]
+  const int i0 = x * SCORE_PEND, n = min(SCORE_PEND, n_pend - i0);
+  if (tid < n) list[tid] = c_last * C + i0 + tid;
+  __syncthreads();
+  score_f64_list<T, D, true>(a, b, kv, list, n, qd, res, sum, Ks, kbase, KS);
+  double* pend = reinterpret_cast<double*>(a.state + (size_t)unit * a.st_unit + a.st_pending);
+  if (tid < n) {
+    pend[i0 + tid] = sum[tid];
+    a.score[ub_off + list[tid]] = (float)sum[tid];
+  }
+  if (x == 0)
+    for (int i = n_pend + tid; i < C; i += 256) pend[i] = __builtin_nan("");
+}
+
 template <typename T, int D>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void select_kernel(PrefillArgs a) {
   extern __shared__ __align__(16) char smem[];
@@ -711,7 +753,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void s
   const int x = (int)blockIdx.x - n_rgrp;
 
   if (x < n_pgrp) {
-    pending_part<T, D>(a, x, kv, b, true);
+    pending_part<T, D>(a, x, kv, b);
     return;
   }
 
@@ -2048,23 +2090,18 @@ __device__ __forceinline__ void state_scan_part(int bx, float* dS, int NS, char*
   }
 }
 
-// The float64 scores of the undecided chunk's tokens when the score kernel
-// made the decisions (workgroups x < n_pend_grp, SEL_PEND tokens each), the
-// scan (the next n_scan) and the decode-state export (the rest) in one
-// launch: none of them depends on another or on the attention walk, so they
-// run side by side.
+// The scan (workgroups x < n_scan) and the decode-state export (the rest,
+// x - n_scan as the export's workgroup index) in one launch: the export
+// depends only on the selection and the inputs, so it runs beside the scan
+// instead of after the attention walk.
 template <typename T, int D>
 __device__ void export_part(const PrefillArgs& a, int x);
 template <typename T, int D>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void state_scan_kernel(
-    PrefillArgs a, int n_pend_grp, int n_scan) {
-  const int x = blockIdx.x;
-  if (x < n_pend_grp)
-    pending_part<T, D>(a, x, blockIdx.y, blockIdx.z, false);
-  else if (x < n_pend_grp + n_scan)
-    state_scan_part<D>(x - n_pend_grp, a.dS, a.NS, a.state, a.st_unit, a.st_S, a.st_z);
+__global__ __launch_bounds__(256) void state_scan_kernel(PrefillArgs a, int n_scan) {
+  if ((int)blockIdx.x < n_scan)
+    state_scan_part<D>((int)blockIdx.x, a.dS, a.NS, a.state, a.st_unit, a.st_S, a.st_z);
   else
-    export_part<T, D>(a, x - n_pend_grp - n_scan);
+    export_part<T, D>(a, (int)blockIdx.x - n_scan);
 }
 
 // ---------------------------------------------------------- 6. attend ----
