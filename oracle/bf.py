@@ -95,7 +95,7 @@ def np_map(x: np.ndarray, F: np.ndarray) -> np.ndarray:
 def prefill(q, k, v, fmap_w, gate, *, window: int, chunk: int, budget: int,
             t_max: int, eps: float = 1e-6, sm_scale: Optional[float] = None,
             partials: bool = False, merge: str = "one", route: str = "saliency",
-            ext_score=None) -> Dict[str, np.ndarray]:
+            ext_score=None, decay=None) -> Dict[str, np.ndarray]:
     """One STILL layer over a whole sequence, every query by brute force.
 
     q [B,Hq,L,d], k/v [B,Hkv,L,d], fmap_w [Hkv,d,d], gate [Hq] (any array
@@ -122,6 +122,11 @@ def prefill(q, k, v, fmap_w, gate, *, window: int, chunk: int, budget: int,
     logit, summed over the heads), "keynorm" (||k_t||), "uniform" (reading:
     evenly spaced offsets floor(i C / lambda) of each chunk score 1, the rest
     0) or "external" (ext_score [B,Hkv,L], e.g. random routing's draws).
+
+    decay [Hkv] (reading of the forget gate of gated linear attention
+    [P4 §2], write strength 1, applied to the linear state): the linear key j
+    of query t is weighted decay^(t - j); the exported state holds
+    decay^(R - j) with R = cf C, the first position past it. None = 1.
     """
     if merge not in ("one", "sum", "softmax_only"):
         raise ValueError("merge must be one, sum or softmax_only")
@@ -134,6 +139,7 @@ def prefill(q, k, v, fmap_w, gate, *, window: int, chunk: int, budget: int,
     v = np.asarray(v, dtype=np.float64)
     Fw = np.asarray(fmap_w, dtype=np.float64)
     g_all = np.asarray(gate, dtype=np.float64)
+    dec = None if decay is None else np.asarray(np.asarray(decay, dtype=np.float32), dtype=np.float64)
     B, Hq, L, d = q.shape
     Hkv = k.shape[1]
     G = Hq // Hkv
@@ -160,6 +166,7 @@ def prefill(q, k, v, fmap_w, gate, *, window: int, chunk: int, budget: int,
     for b in range(B):
         for kv in range(Hkv):
             K, V, F = k[b, kv], v[b, kv], Fw[kv]
+            gam = 1.0 if dec is None else float(dec[kv])
             heads = range(kv * G, kv * G + G)
             # Score of every token, summed over the query heads of the group
             # (reading: routing is per kv head).
@@ -209,6 +216,8 @@ def prefill(q, k, v, fmap_w, gate, *, window: int, chunk: int, budget: int,
                 for h in heads:
                     s = scale * (K[ia] @ q[b, h, t])
                     w0 = phik[ib] @ np_map(q[b, h, t], F)  # linear weights, no gate
+                    if gam != 1.0:
+                        w0 = w0 * gam ** (t - ib).astype(np.float64)
                     ea = np.exp(s - s.max())
                     ysa = (ea @ V[ia]) / ea.sum()
                     yla = (w0 @ V[ib]) / w0.sum() if len(ib) and w0.sum() > 0 else np.zeros(d)
@@ -235,8 +244,10 @@ def prefill(q, k, v, fmap_w, gate, *, window: int, chunk: int, budget: int,
                 c_last = (L - 1) // C
                 cf = full_chunks_out_of_window(c_last, W, C)
                 folded = (~selected) & (chunk_of < cf)
-                S[b, kv] = phik[folded].T @ V[folded]
-                z[b, kv] = phik[folded].sum(axis=0)
+                wf = gam ** (cf * C - pos[folded]).astype(np.float64) if gam != 1.0 else \
+                    np.ones(int(folded.sum()))
+                S[b, kv] = (phik[folded] * wf[:, None]).T @ V[folded]
+                z[b, kv] = (phik[folded] * wf[:, None]).sum(axis=0)
                 pend = pos[chunk_of == c_last]
                 pending[b, kv, :len(pend)] = sc[pend]
 

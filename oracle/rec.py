@@ -50,7 +50,7 @@ def _load():
         f = lib.still_oracle_run
         P = ctypes.c_void_p
         f.argtypes = [ctypes.c_int] * 8 + [ctypes.c_double] * 2 + [P] * 5 + \
-            [ctypes.c_int] + [P] * 7 + [ctypes.c_int] + [P] * 4 + [ctypes.c_int, P]
+            [ctypes.c_int] + [P] * 7 + [ctypes.c_int] + [P] * 4 + [ctypes.c_int, P, P]
         f.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -71,7 +71,7 @@ def prefill(q, k, v, fmap_w, gate, *, window: int, chunk: int, budget: int,
             units: Optional[Sequence[Tuple[int, int]]] = None,
             n_threads: int = 1, merge: str = "one",
             partials: bool = False, route: str = "saliency",
-            ext_score=None) -> Dict[str, np.ndarray]:
+            ext_score=None, decay=None) -> Dict[str, np.ndarray]:
     """Run the recurrent oracle on the listed (batch, kv head) units.
 
     q [B,Hq,L,d], k/v [B,Hkv,L,d], fmap_w [Hkv,d,d], gate [Hq]. Outputs
@@ -82,6 +82,9 @@ def prefill(q, k, v, fmap_w, gate, *, window: int, chunk: int, budget: int,
     linear one without the gate; y_la = 0 and lse_la = -inf where the state
     is empty). merge: "one", "sum" or "softmax_only" (see MERGES). route:
     a key of ROUTES; ext_score [B,Hkv,L] the caller's scores for "external".
+    decay [Hkv]: forget factors in (0, 1] of the linear state (key j weighted
+    decay^(t - j) at query t), rounded to float32 as the caller holds them;
+    None for the plain layer.
     """
     B, Hq, L, d = q.shape
     Hkv = k.shape[1]
@@ -99,17 +102,22 @@ def prefill(q, k, v, fmap_w, gate, *, window: int, chunk: int, budget: int,
     if ext_score is not None:
         ext = np.stack([_f32(ext_score[b, kv]) for b, kv in units]) if U else \
             np.zeros((0, L), np.float32)
+    dec = None
+    if decay is not None:
+        d32 = _f32(decay)
+        dec = np.array([d32[kv] for _, kv in units], dtype=np.float32)
     return run_units(qs, ks, vs, Fs, gs, window=window, chunk=chunk, budget=budget,
                      t_max=t_max, eps=eps, sm_scale=sm_scale, n_threads=n_threads,
-                     merge=merge, partials=partials, route=route, ext=ext)
+                     merge=merge, partials=partials, route=route, ext=ext, decay=dec)
 
 
 def run_units(qs, ks, vs, Fs, gs, *, window: int, chunk: int, budget: int, t_max: int,
               eps: float = 1e-6, sm_scale: Optional[float] = None,
               n_threads: int = 1, merge: str = "one", partials: bool = False,
-              route: str = "saliency", ext=None) -> Dict[str, np.ndarray]:
+              route: str = "saliency", ext=None, decay=None) -> Dict[str, np.ndarray]:
     """Run on pre-gathered per-unit arrays (see still_oracle_run); ext
-    [U, L]: the caller's scores for route "external"."""
+    [U, L]: the caller's scores for route "external"; decay [U]: the
+    units' forget factors of the linear state (float32 values), or None."""
     qs, ks, vs, Fs, gs = (_f32(a) for a in (qs, ks, vs, Fs, gs))
     if route == "external":
         if ext is None:
@@ -130,6 +138,11 @@ def run_units(qs, ks, vs, Fs, gs, *, window: int, chunk: int, budget: int, t_max
     if partials:
         part = {"y_sa": np.zeros((U, G, L, d)), "lse_sa": np.zeros((U, G, L)),
                 "y_la": np.zeros((U, G, L, d)), "lse_la": np.zeros((U, G, L))}
+    dec64 = None
+    if decay is not None:
+        dec64 = np.ascontiguousarray(_f32(decay).astype(np.float64).reshape(-1))
+        if dec64.shape[0] != U:
+            raise ValueError("decay needs one value per unit")
     lib = _load()
     ptr = lambda a: a.ctypes.data_as(ctypes.c_void_p)
     pp = [None] * 4 if part is None else [ptr(part[n]) for n in ("y_sa", "lse_sa", "y_la", "lse_la")]
@@ -137,7 +150,8 @@ def run_units(qs, ks, vs, Fs, gs, *, window: int, chunk: int, budget: int, t_max
                               ptr(qs), ptr(ks), ptr(vs), ptr(Fs), ptr(gs), int(n_threads),
                               ptr(y), ptr(score), ptr(sel), ptr(S), ptr(z), ptr(pending),
                               ptr(n_pool), MERGES[merge], *pp, ROUTES[route],
-                              ptr(ext) if route == "external" else None)
+                              ptr(ext) if route == "external" else None,
+                              ptr(dec64) if dec64 is not None else None)
     if rc != 0:
         raise ValueError("still_oracle_run rejected its arguments (rc=%d)" % rc)
     out = {"y": y, "score": score, "sel": sel, "S": S, "z": z, "pending": pending,

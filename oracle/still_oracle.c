@@ -15,7 +15,8 @@
  *        "NP-Map: Norm-Preserving Feature Map", "Problems with Existing
  *        Intra-Layer Hybrid Attention"
  *   [P4] "Synergizing Linear and Sparse Attention: A Deep Dive into Hybrid
- *        LLM Architectures", §4 (gating; the separately normalised merge)
+ *        LLM Architectures", §2 (the linear state's forget gate), §4
+ *        (gating; the separately normalised merge)
  *
  * The loop follows the recurrent (decoding) form the pages describe: tokens
  * arrive one by one; when a new chunk begins the previous chunk is decided
@@ -65,6 +66,7 @@ typedef struct {
   double *y, *score, *S, *z, *pending;
   int32_t *sel, *n_pool;
   double *y_sa, *lse_sa, *y_la, *lse_la; /* branch partials, or all null */
+  const double* decay; /* [n_units] forget factor of the linear state, or null (1) */
 } oracle_job;
 
 typedef struct {
@@ -189,9 +191,18 @@ static void run_unit(const oracle_job* J, int u) {
   int32_t* selu = J->sel + (size_t)u * J->n_dec * (J->lam > 0 ? J->lam : 0);
   for (int i = 0; i < J->n_dec * J->lam; ++i) selu[i] = -1;
 
+  /* Forget gate of the linear state (reading of [P4 §2]'s gated linear
+   * attention with write strength 1 applied to the NP-Map state): the state
+   * decays by gam every token, so key j enters the query at t with weight
+   * gam^(t - j); gam = 1 is the plain layer. */
+  const double gam = J->decay ? J->decay[u] : 1.0;
   int next_la = 0; /* every position below this has been routed to B or kept */
   for (int t = 0; t < L; ++t) {
     const int c = t / C;
+    if (gam != 1.0 && t > 0) { /* the state, held at time t - 1, moves to t */
+      for (size_t i = 0; i < (size_t)d * d; ++i) SB[i] *= gam;
+      for (int a = 0; a < d; ++a) zB[a] *= gam;
+    }
     /* Chunk c-1 is decided when chunk c begins [P3 "Delayed Chunk-Level
      * Selection"]: keep its lambda best tokens by (score desc, position
      * asc), while the pool (capacity m - W) has room [P2 固定预算路由]. */
@@ -229,9 +240,10 @@ static void run_unit(const oracle_job* J, int u) {
       const int j = next_la++;
       if (selected[j]) continue;
       np_map(K + (size_t)j * d, F, d, phi, tmp);
+      const double wj = gam == 1.0 ? 1.0 : pow(gam, (double)(t - j));
       for (int a = 0; a < d; ++a) {
-        zB[a] += phi[a];
-        const double pa = phi[a];
+        zB[a] += wj * phi[a];
+        const double pa = wj * phi[a];
         double* row = SB + (size_t)a * d;
         const double* vj = V + (size_t)j * d;
         for (int b2 = 0; b2 < d; ++b2) row[b2] += pa * vj[b2];
@@ -340,7 +352,9 @@ static void run_unit(const oracle_job* J, int u) {
 
   /* Exported state: the unselected tokens of the chunks lying wholly before
    * the window of every query of the last chunk (reading: the state absorbs
-   * whole chunks); pending = scores of the undecided last chunk. */
+   * whole chunks), with the forget gate held at the first position past
+   * them, R = cf C (key j weighted gam^(R - j)); pending = scores of the
+   * undecided last chunk. */
   double* Su = J->S + (size_t)u * d * d;
   double* zu = J->z + (size_t)u * d;
   memset(Su, 0, sizeof(double) * (size_t)d * d);
@@ -353,9 +367,10 @@ static void run_unit(const oracle_job* J, int u) {
     for (int j = 0; j < cf * C; ++j) {
       if (selected[j]) continue;
       np_map(K + (size_t)j * d, F, d, phi, tmp);
+      const double wj = gam == 1.0 ? 1.0 : pow(gam, (double)(cf * C - j));
       for (int a = 0; a < d; ++a) {
-        zu[a] += phi[a];
-        for (int b2 = 0; b2 < d; ++b2) Su[(size_t)a * d + b2] += phi[a] * V[(size_t)j * d + b2];
+        zu[a] += wj * phi[a];
+        for (int b2 = 0; b2 < d; ++b2) Su[(size_t)a * d + b2] += wj * phi[a] * V[(size_t)j * d + b2];
       }
     }
     for (int j = c_last * C; j < L; ++j) pend[j - c_last * C] = score[j];
@@ -385,7 +400,9 @@ static void* worker(void* p) {
  * lse_la: all null, or the branch partials [n_units, G, L, d] / [n_units,
  * G, L]: each branch normalised on its own, the linear one without the
  * gate (y_la = 0, lse_la = -inf where the state is empty), lse = natural
- * log of the branch's weight sum.
+ * log of the branch's weight sum. decay: null, or [n_units] forget factors
+ * in (0, 1] of the linear state (key j weighted decay^(t - j) at query t;
+ * the exported state holds decay^(R - j), R = the first position past it).
  * Returns 0, or -1 on invalid sizes. */
 int still_oracle_run(int n_units, int L, int d, int G, int W, int C, int m, int t_max,
                      double eps, double scale, const float* q, const float* k,
@@ -393,20 +410,22 @@ int still_oracle_run(int n_units, int L, int d, int G, int W, int C, int m, int 
                      double* y, double* score, int32_t* sel, double* S, double* z,
                      double* pending, int32_t* n_pool, int merge, double* y_sa,
                      double* lse_sa, double* y_la, double* lse_la, int route,
-                     const float* ext) {
+                     const float* ext, const double* decay) {
   if (n_units < 0 || L < 0 || d < 1 || G < 1 || W < 1 || C < 1 || m < W || t_max < 1)
     return -1;
   if (merge < MERGE_ONE || merge > MERGE_SOFTMAX_ONLY) return -1;
   if (route < ROUTE_SALIENCY || route > ROUTE_EXTERNAL) return -1;
   if (route == ROUTE_EXTERNAL && !ext) return -1;
   if (!(y_sa && lse_sa && y_la && lse_la) && (y_sa || lse_sa || y_la || lse_la)) return -1;
+  for (int u = 0; decay && u < n_units; ++u)
+    if (!(decay[u] > 0.0 && decay[u] <= 1.0)) return -1;
   int lam = (m - W) / t_max;
   if (lam > C) lam = C;
   if (lam > 1024) return -1;
   oracle_job J = {L, d, G, W, C, m, t_max, lam, L > 0 ? (L - 1) / C : 0, merge, route, ext,
                   eps, scale,
                   q, k, v, F, gate, y, score, S, z, pending, sel, n_pool,
-                  y_sa, lse_sa, y_la, lse_la};
+                  y_sa, lse_sa, y_la, lse_la, decay};
   if (n_threads < 1) n_threads = 1;
   if (n_threads > n_units) n_threads = n_units > 0 ? n_units : 1;
   pthread_t th[256];

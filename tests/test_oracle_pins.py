@@ -572,3 +572,94 @@ def test_output_gate_pins():
     d = bf.output_gate(y, g2) - bf.output_gate(y, g)
     d[1, 2, 3, 4] = 0.0
     assert np.abs(d).max() == 0.0
+
+
+# ---------------------------------------------------------- decay gate ----
+# Reading of the forget gate of gated linear attention (the hybrid-
+# architecture survey, §2: the state decays by gamma every token, write
+# strength 1), applied to STILL's linear state: the linear key j of query t
+# is weighted gamma^(t - j); the exported state holds gamma^(R - j), R the
+# first position past it.
+
+
+@pytest.mark.parametrize("form", ["bf", "rec"])
+def test_decay_one_is_the_plain_layer(form):
+    """gamma = 1 gives the plain layer exactly (outputs and exported state)."""
+    rng = np.random.default_rng(41)
+    q, k, v, F, g = rand_inputs(rng, 1, 4, 2, 70, 8, outliers=1)
+    kw = dict(window=6, chunk=8, budget=6 + 4 * 8, t_max=8)
+    run = bf.prefill if form == "bf" else rec.prefill
+    a = run(q, k, v, F, g, **kw)
+    b = run(q, k, v, F, g, decay=np.ones(2, np.float32), **kw)
+    for key in ("y", "S", "z"):
+        np.testing.assert_array_equal(a[key], b[key])
+
+
+@pytest.mark.parametrize("form", ["bf", "rec"])
+def test_decay_vanishing_is_softmax_only(form):
+    """gamma -> 0: every linear key lies at least W tokens back, so its weight
+    falls below gamma^W and the output is the softmax branch alone."""
+    rng = np.random.default_rng(43)
+    q, k, v, F, g = rand_inputs(rng, 1, 4, 2, 70, 8, outliers=1)
+    kw = dict(window=6, chunk=8, budget=6 + 4 * 8, t_max=8)
+    run = bf.prefill if form == "bf" else rec.prefill
+    a = run(q, k, v, F, g, merge="softmax_only", **kw)
+    b = run(q, k, v, F, g, decay=np.full(2, 1e-6, np.float32), **kw)
+    np.testing.assert_allclose(b["y"], a["y"], rtol=1e-12, atol=1e-14)
+
+
+@pytest.mark.parametrize("case", CASES[:5] + CASES[7:])
+def test_decay_recurrent_matches_brute_force(case):
+    """Both forms agree with a decaying state (the recurrence multiplies its
+    state by gamma every token; the explicit form weights gamma^(t - j))."""
+    B, Hq, Hkv, L, d, W, C, m, tm, nout = case
+    rng = np.random.default_rng(sum(case) + 5)
+    q, k, v, F, g = rand_inputs(rng, B, Hq, Hkv, L, d, outliers=nout)
+    dec = rng.uniform(0.8, 1.0, Hkv).astype(np.float32)
+    kw = dict(window=W, chunk=C, budget=m, t_max=tm, decay=dec)
+    a = bf.prefill(q, k, v, F, g, partials=True, **kw)
+    r = rec.prefill(q, k, v, F, g, partials=True, **kw)
+    G = Hq // Hkv
+    U = B * Hkv
+    np.testing.assert_allclose(r["y"], a["y"].reshape(U, G, L, d), rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(r["y_la"], a["y_la"].reshape(U, G, L, d), rtol=1e-10, atol=1e-11)
+    fin = np.isfinite(a["lse_la"].reshape(U, G, L))
+    np.testing.assert_array_equal(np.isfinite(r["lse_la"]), fin)
+    np.testing.assert_allclose(r["lse_la"][fin], a["lse_la"].reshape(U, G, L)[fin], rtol=1e-11, atol=1e-11)
+    np.testing.assert_allclose(r["S"], a["S"].reshape(U, d, d), rtol=1e-11, atol=1e-11)
+    np.testing.assert_allclose(r["z"], a["z"].reshape(U, d), rtol=1e-12, atol=1e-12)
+
+
+def test_decay_geometric_closed_form():
+    """Identical keys (one feature vector, tied scores: the lower index is
+    kept) and distinct values: the linear branch at query t is the average
+    of its values with weights gamma^(t - j) over B(t) = the unkept tokens
+    below min(t - W + 1, cC), and the exported z is phi(k) times the sum of
+    gamma^(R - j) over the unkept tokens below R = cf C."""
+    rng = np.random.default_rng(47)
+    L, d, W, C, m, tm, gam = 40, 4, 4, 8, 4 + 2 * 8, 8, np.float32(0.75)
+    q, k, v, F, g = rand_inputs(rng, 1, 1, 1, L, d)
+    k[:] = k[0, 0, 0]
+    r = rec.prefill(q, k, v, F, g, window=W, chunk=C, budget=m, t_max=tm,
+                    decay=np.array([gam]), partials=True)
+    lam = bf.budget_lambda(W, C, m, tm)
+    assert lam == 2
+    kept = set()
+    for c in range((L - 1) // C):  # ties: the two lowest positions of each chunk
+        if len(kept) + lam <= m - W:
+            kept.update((c * C, c * C + 1))
+    np.testing.assert_array_equal(np.sort(r["sel"].reshape(-1)[r["sel"].reshape(-1) >= 0]), sorted(kept))
+    G64 = float(gam)
+    for t in range(L):
+        c = t // C
+        B_t = [j for j in range(min(t - W + 1, c * C)) if j not in kept]
+        if not B_t:
+            assert r["lse_la"][0, 0, t] == -np.inf
+            continue
+        w = np.array([G64 ** (t - j) for j in B_t])
+        want = (w[:, None] * v[0, 0, B_t]).sum(0) / w.sum()
+        np.testing.assert_allclose(r["y_la"][0, 0, t], want, rtol=1e-12, atol=1e-13)
+    c_last = (L - 1) // C
+    R = bf.full_chunks_out_of_window(c_last, W, C) * C
+    geo = sum(G64 ** (R - j) for j in range(R) if j not in kept)
+    np.testing.assert_allclose(r["z"][0], geo * bf.np_map(k[0, 0, 0], F[0]), rtol=1e-12)
