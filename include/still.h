@@ -202,6 +202,22 @@ int still_prefill_gated(const still_params* p, int64_t seq_len, const void* q, c
                         const void* out_gate, void* out, int32_t* sel_idx, float* score,
                         void* state, void* workspace, size_t ws_bytes, void* stream);
 
+/* still_prefill with a forget gate on the linear state (reading of the
+ * gated linear attention of [P4 "Synergizing Linear and Sparse Attention:
+ * A Deep Dive into Hybrid LLM Architectures", §2] with write strength 1,
+ * applied to the NP-Map state of [P3 "NP-Map ..."]): the state decays by
+ * decay[kv] every token, so a linear key j enters query t with weight
+ * gate * decay^(t - j) * <phi(q), phi(k_j)>. decay: device float32 [Hkv],
+ * values in (0, 1] (1 = the plain layer; other values are not checked and
+ * give undefined results), 16-byte aligned, required. The exported state
+ * holds decay^(R - j) phi(k_j) v_j^T, R the first position past the
+ * chunks it covers; still_decode_step_decay continues it with the same
+ * decay. Same outputs, workspace and errors as still_prefill otherwise. */
+int still_prefill_decay(const still_params* p, int64_t seq_len, const void* q, const void* k,
+                        const void* v, const void* fmap_w, const float* gate, const float* decay,
+                        void* out, int32_t* sel_idx, float* score, void* state, void* workspace,
+                        size_t ws_bytes, void* stream);
+
 /* still_prefill with per-kernel timing, for benchmarks: for i < n_pairs it
  * records events[2i] before and events[2i+1] after the i-th kernel of the
  * prefill on `stream` (events are caller-created hipEvent_t handles; a NULL

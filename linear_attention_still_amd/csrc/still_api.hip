@@ -515,7 +515,7 @@ static int prefill_impl(const still_params* p, int64_t seq_len, const void* q, c
                         int32_t* sel_idx, float* score, void* state, void* workspace,
                         size_t ws_bytes, void* stream, void* const* events, int n_pairs,
                         Partials parts = Partials{nullptr, nullptr, nullptr, nullptr},
-                        const void* out_gate = nullptr) {
+                        const void* out_gate = nullptr, const float* decay = nullptr) {
   Derived d;
   int rc = derive(p, &d);
   if (rc != STILL_OK) return rc;
@@ -530,7 +530,8 @@ static int prefill_impl(const still_params* p, int64_t seq_len, const void* q, c
   if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(fmap_w) || misaligned(out) ||
       misaligned(state) || misaligned(workspace) || misaligned(gate))
     return STILL_EINVAL;
-  if (misaligned(parts.y_sa) || misaligned(parts.y_la) || misaligned(out_gate)) return STILL_EINVAL;
+  if (misaligned(parts.y_sa) || misaligned(parts.y_la) || misaligned(out_gate) || misaligned(decay))
+    return STILL_EINVAL;
   const bool merge_sum = (p->flags & STILL_FLAG_MERGE_SUM) != 0;
   const bool softmax_only = (p->flags & STILL_FLAG_SOFTMAX_ONLY) != 0;
   if (merge_sum && softmax_only) return STILL_EINVAL;
@@ -550,6 +551,7 @@ static int prefill_impl(const still_params* p, int64_t seq_len, const void* q, c
   a.gate = gate;
   a.out = out;
   a.out_gate = out_gate;
+  a.decay = decay;
   a.sel = sel_idx;
   a.route = (int)STILL_ROUTE_OF(p->flags);
   if (a.route == still::ROUTE_EXTERNAL) {  // the caller's scores are an input here
@@ -620,6 +622,16 @@ int still_prefill_gated(const still_params* p, int64_t seq_len, const void* q, c
   return prefill_impl(p, seq_len, q, k, v, fmap_w, gate, out, sel_idx, score, state, workspace,
                       ws_bytes, stream, nullptr, 0, Partials{nullptr, nullptr, nullptr, nullptr},
                       out_gate);
+}
+
+int still_prefill_decay(const still_params* p, int64_t seq_len, const void* q, const void* k,
+                        const void* v, const void* fmap_w, const float* gate, const float* decay,
+                        void* out, int32_t* sel_idx, float* score, void* state, void* workspace,
+                        size_t ws_bytes, void* stream) {
+  if (!decay) return STILL_EINVAL;
+  return prefill_impl(p, seq_len, q, k, v, fmap_w, gate, out, sel_idx, score, state, workspace,
+                      ws_bytes, stream, nullptr, 0, Partials{nullptr, nullptr, nullptr, nullptr},
+                      nullptr, decay);
 }
 
 int still_prefill_timed(const still_params* p, int64_t seq_len, const void* q, const void* k,

@@ -57,6 +57,7 @@ struct PrefillArgs {
   int route;      // routing metric (ROUTE_*)
   const void* out_gate;    // [B][Hq][L][D] T: channel-wise output gate before the sigmoid, or null
   int fuse_sel;            // the score kernel decides the chunks (Self-Saliency route, C <= 64)
+  const float* decay;      // [Hkv] forget factor of the linear state in (0, 1], or null (1)
   int n_pend_grp;          // with fuse_sel: score workgroups (first) for the undecided chunk's float64 scores
   const float* ext_score;  // [B][Hkv][L] the caller's scores (ROUTE_EXTERNAL)
   float scale, eps;
@@ -1460,7 +1461,9 @@ __device__ __forceinline__ float fold_zsum(const BlkPtr<T, D>& P, const f32x4 (&
 // Fold the block into the walk's state in LDS (SP += contribution, z += ...);
 // wave w updates the d_k tile w, i.e. half e = w % 2 of the pairs (vt, w/2).
 template <typename T, int D>
-__device__ __forceinline__ void block_fold(const BlkPtr<T, D>& P, const f32x4 (&ph)[4]) {
+// fS: the forget gate's factor on the state before the block's keys are
+// added (their features come weighted already); 1 without the gate.
+__device__ __forceinline__ void block_fold(const BlkPtr<T, D>& P, const f32x4 (&ph)[4], float fS = 1.f) {
   using B_ = Blk<T, D>;
   const int wave = opaque_tid() >> 6, lane = opaque_tid() & 63, r16 = lane & 15, g4 = lane >> 4;
   if (wave >= B_::NFT) return;
@@ -1471,10 +1474,10 @@ __device__ __forceinline__ void block_fold(const BlkPtr<T, D>& P, const f32x4 (&
 #pragma unroll
   for (int vt = 0; vt < D / 16; ++vt) {
     float* sp = P.pair(vt * (D / 32) + (wave >> 1), wave & 1);
-    *reinterpret_cast<f32x4*>(sp) += acc[vt];
+    *reinterpret_cast<f32x4*>(sp) = *reinterpret_cast<const f32x4*>(sp) * fS + acc[vt];
   }
   const float z = fold_zsum<T, D>(P, ph);
-  if (g4 == 0) P.zs[16 * wave + r16] += (double)z;
+  if (g4 == 0) P.zs[16 * wave + r16] = P.zs[16 * wave + r16] * (double)fS + (double)z;
 }
 
 // Super-chunk states in the workspace use the fragment-linear layout of SP
@@ -1564,7 +1567,7 @@ __device__ __forceinline__ uint64_t mark_big_keys(const BlkPtr<T, D>& P, const B
 // (lanes g == 0). Every thread calls it; it contains barriers.
 template <typename T, int D>
 __device__ __forceinline__ void big_key_fold(const BlkPtr<T, D>& P, const BigScratch<T, D>& Z, int kk,
-                                             double (&sum)[D / 16][4], double& zsum) {
+                                             double (&sum)[D / 16][4], double& zsum, double wgt = 1.0) {
   using B_ = Blk<T, D>;
   constexpr int NPART = 512 / D, TP = D / NPART;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, r16 = lane & 15, g4 = lane >> 4;
@@ -1611,7 +1614,7 @@ __device__ __forceinline__ void big_key_fold(const BlkPtr<T, D>& P, const BigScr
     double ss = 0.0;
 #pragma unroll
     for (int w = 0; w < D / 64; ++w) ss += Z.red[4 + w];
-    Z.phi[tid] = sqrt(k2) * e / sqrt(ss);
+    Z.phi[tid] = wgt * (sqrt(k2) * e / sqrt(ss));  // wgt: the key's forget factor
   }
   __syncthreads();
   if (wave < B_::NFT) {
@@ -1652,6 +1655,9 @@ __global__ __launch_bounds__(512) void state_delta_f32_kernel(PrefillArgs a) {
   const int lo = full_chunks_before(s * a.K, a.W, a.C) * a.C;
   const int hi = (s == a.NS - 1 ? full_chunks_before(a.T - 1, a.W, a.C)
                                 : full_chunks_before(s * a.K + a.K, a.W, a.C)) * a.C;
+  // forget gate: the delta is held at hi, key j weighted gamma^(hi - j)
+  const double l2g64 = a.decay ? log2((double)a.decay[kv]) : 0.0;
+  const float l2g = (float)l2g64;
   // block blo + 64 is issued as soon as block blo is in LDS (past hi the
   // loads read zeros past the buffer range)
   BlkRegs<T, D, 512> R;
@@ -1664,6 +1670,12 @@ __global__ __launch_bounds__(512) void state_delta_f32_kernel(PrefillArgs a) {
     const uint64_t big = mark_big_keys<T, D>(P, Z);
     f32x4 ph[4];
     block_phi<T, D>(P, ph, false);
+    if (l2g != 0.f) {  // uniform: key j weighted gamma^(hi - j)
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ph[kt][i] *= exp2f((float)(hi - (blo + 16 * kt + 4 * g4 + i)) * l2g);
+    }
     if (wave < B_::NFT) {
 #pragma unroll
       for (int kb2 = 0; kb2 < 2; ++kb2) {
@@ -1678,8 +1690,10 @@ __global__ __launch_bounds__(512) void state_delta_f32_kernel(PrefillArgs a) {
       }
       zsum += (double)fold_zsum<T, D>(P, ph);
     }
-    for (uint64_t m = big; m; m &= m - 1)  // uniform
-      big_key_fold<T, D>(P, Z, (int)__builtin_ctzll(m), sum, zsum);
+    for (uint64_t m = big; m; m &= m - 1) {  // uniform
+      const int kk = (int)__builtin_ctzll(m);
+      big_key_fold<T, D>(P, Z, kk, sum, zsum, l2g != 0.f ? exp2((double)(hi - (blo + kk)) * l2g64) : 1.0);
+    }
   }
   float* dst = a.dS + ((size_t)unit * a.NS + s) * (D * D + D);
   if (wave < B_::NFT) {
@@ -1721,7 +1735,7 @@ struct SdLds {
   static constexpr size_t ph_bytes = (size_t)D * PS * 4;
   static constexpr size_t vmx_bytes = SD_BK * 4;
   static constexpr size_t bits_bytes = 32;
-  static constexpr size_t bst_bytes = (size_t)SD_NBK * (8 * 2 + 1) * 8;
+  static constexpr size_t bst_bytes = (size_t)SD_NBK * (8 * 2 + 2) * 8;  // + |k|^2, forget factor
   static constexpr size_t bphi_bytes = (size_t)SD_NBK * D * 8;
   static constexpr size_t krow_bytes = (size_t)16 * D * sizeof(T);  // two large-key rows per wave
   static constexpr size_t kn2_bytes = (size_t)SD_BK * 8;              // float64 |k|^2 of large keys
@@ -1779,6 +1793,9 @@ __global__ __launch_bounds__(512) void state_delta_kernel(PrefillArgs a) {
   const int lo = full_chunks_before(s * a.K, a.W, a.C) * a.C;
   const int hi = (s == a.NS - 1 ? full_chunks_before(a.T - 1, a.W, a.C)
                                 : full_chunks_before(s * a.K + a.K, a.W, a.C)) * a.C;
+  // forget gate: the delta is held at hi, key j weighted gamma^(hi - j)
+  const double l2g64 = a.decay ? log2((double)a.decay[kv]) : 0.0;
+  const float l2g = (float)l2g64;
   // fold ownership: feature tile ft, d_v tiles vt0 .. vt0 + VPW - 1
   const int ft = wave % NFT, vt0 = (wave / NFT) * VPW;
   double sum[VPW][4];
@@ -1903,6 +1920,7 @@ __global__ __launch_bounds__(512) void state_delta_kernel(PrefillArgs a) {
         const float s2 = row_sum<16>(ss[i]);
         const float k2 = __shfl(n2, 4 * g4 + i);
         fac[i] = ((use16 >> (4 * g4 + i)) & 1u) ? __builtin_amdgcn_sqrtf(k2) * __builtin_amdgcn_rsqf(s2) : 0.f;
+        if (l2g != 0.f) fac[i] *= exp2f((float)(hi - (row - r16 + 4 * g4 + i)) * l2g);
       }
 #pragma unroll
       for (int f = 0; f < NFT; ++f) {
@@ -2004,7 +2022,10 @@ __global__ __launch_bounds__(512) void state_delta_kernel(PrefillArgs a) {
         if (lane == 0) {
           bst[(n * 8 + wave) * 2] = m;
           bst[(n * 8 + wave) * 2 + 1] = se;
-          if (wave == 0) bk2[n] = kn2d[kk];
+          if (wave == 0) {
+            bk2[n] = kn2d[kk];
+            bk2[SD_NBK + n] = l2g != 0.f ? exp2((double)(hi - row) * l2g64) : 1.0;  // gamma^(hi - j)
+          }
         }
       }
       __syncthreads();
@@ -2021,7 +2042,7 @@ __global__ __launch_bounds__(512) void state_delta_kernel(PrefillArgs a) {
         M = fmax(M, dppd<0x4E>(M));
         M = fmax(M, dppd<0x141>(M));
         const double S = group_sum_d<8>(bst[(n * 8 + w8) * 2 + 1] * exp(2.0 * (mw - M)));
-        if (part == 0) bphi[n * D + j] = sqrt(bk2[n]) * exp(bphi[n * D + j] - M) / sqrt(S);
+        if (part == 0) bphi[n * D + j] = bk2[SD_NBK + n] * (sqrt(bk2[n]) * exp(bphi[n * D + j] - M) / sqrt(S));
       }
       __syncthreads();
       ml = rl;
@@ -2056,13 +2077,22 @@ __global__ __launch_bounds__(512) void state_delta_kernel(PrefillArgs a) {
 // Part bx of the scan for unit (blockIdx.y, blockIdx.z): 256 of the D*D + D
 // state entries.
 template <int D>
-__device__ __forceinline__ void state_scan_part(int bx, float* dS, int NS, char* state, long st_unit, long st_S,
-                                                long st_z) {
+__device__ __forceinline__ void state_scan_part(const PrefillArgs& a, int bx) {
+  float* dS = a.dS;
+  const int NS = a.NS;
   constexpr int n_elem = D * D + D;
   const int e = bx * 256 + threadIdx.x;
   if (e >= n_elem) return;
   const int unit = blockIdx.y + gridDim.y * blockIdx.z;
   float* base = dS + (size_t)unit * NS * n_elem + e;
+  // forget gate: super-chunk s's delta is held at the end hi_s of its key
+  // range and the running sum at the start lo_s = hi_{s-1}, so it moves on
+  // by gamma^(hi_s - lo_s) before the delta is added
+  const double l2g = a.decay ? log2((double)a.decay[blockIdx.y]) : 0.0;
+  auto key_end = [&](int s2) {
+    return (s2 == NS - 1 ? full_chunks_before(a.T - 1, a.W, a.C) : full_chunks_before(s2 * a.K + a.K, a.W, a.C)) *
+           a.C;
+  };
   double run = 0.0;  // float64 running sum: one float32 rounding per start
   constexpr int NB = 32;  // loads of a batch in flight together (indices
                           // past the end re-read the last entry, unused)
@@ -2074,19 +2104,23 @@ __device__ __forceinline__ void state_scan_part(int bx, float* dS, int NS, char*
     for (int i = 0; i < NB; ++i)
       if (s0 + i < NS) {
         base[(size_t)(s0 + i) * n_elem] = (float)run;
+        if (l2g != 0.0) {
+          const int s2 = s0 + i, lo_s = full_chunks_before(s2 * a.K, a.W, a.C) * a.C;
+          run *= exp2((double)(key_end(s2) - lo_s) * l2g);
+        }
         run += (double)x[i];
       }
   }
-  char* st = state + (size_t)unit * st_unit;
+  char* st = a.state + (size_t)unit * a.st_unit;
   if (e < D * D) {
     // fragment-linear index ((2p + h) * 64 + lane) * 4 + i, pair p = vt *
     // (D/32) + bb, lane = 16g + r: S[32bb + 16h + 4g + i][16vt + r]
     const int i = e & 3, ln = (e >> 2) & 63, ph = e >> 8;
     const int h = ph & 1, p = ph >> 1, vt = p / (D / 32), bb = p % (D / 32);
     const int row = 32 * bb + 16 * h + 4 * (ln >> 4) + i, col = 16 * vt + (ln & 15);
-    reinterpret_cast<float*>(st + st_S)[row * D + col] = (float)run;
+    reinterpret_cast<float*>(st + a.st_S)[row * D + col] = (float)run;
   } else {
-    reinterpret_cast<float*>(st + st_z)[e - D * D] = (float)run;
+    reinterpret_cast<float*>(st + a.st_z)[e - D * D] = (float)run;
   }
 }
 
@@ -2099,7 +2133,7 @@ __device__ void export_part(const PrefillArgs& a, int x);
 template <typename T, int D>
 __global__ __launch_bounds__(256) void state_scan_kernel(PrefillArgs a, int n_scan) {
   if ((int)blockIdx.x < n_scan)
-    state_scan_part<D>((int)blockIdx.x, a.dS, a.NS, a.state, a.st_unit, a.st_S, a.st_z);
+    state_scan_part<D>(a, (int)blockIdx.x);
   else
     export_part<T, D>(a, (int)blockIdx.x - n_scan);
 }
@@ -2183,6 +2217,8 @@ __global__ __launch_bounds__(512) void attend_kernel(PrefillArgs a) {
     lgate2[j] = gg[j] > 0.f ? log2_acc<T>(gg[j]) : STILL_NEG_INF;
     qr[j] = make_rsrc(reinterpret_cast<const T*>(a.q) + ((size_t)(b * a.Hq + hh[j]) * L) * D, kv_bytes);
   }
+  // forget gate of the linear state (0: none), base 2
+  const float l2g = a.decay ? log2f(a.decay[kv]) : 0.f;
   // the output gates of the wave's heads (only read with a.out_gate)
   __amdgpu_buffer_rsrc_t gr[HPW];
 #pragma unroll
@@ -2327,7 +2363,9 @@ __global__ __launch_bounds__(512) void attend_kernel(PrefillArgs a) {
 #pragma unroll
       for (int j = 0; j < HPW; ++j) {
         if (gg[j] > 0.f && dz[j] > 0.f) {
-          mrun[j] = log2_acc<T>(gg[j] * dz[j]);
+          // the state is held at band_lo: the forget gate weights it
+          // gamma^(t - band_lo) at this query
+          mrun[j] = log2_acc<T>(gg[j] * dz[j]) + (float)(t - band_lo) * l2g;
           lacc[j] = f32x4{1.f, 1.f, 1.f, 1.f};
           if constexpr (sizeof(T) == 4) {
             const float inv = 1.f / dz[j];
@@ -2435,7 +2473,9 @@ __global__ __launch_bounds__(512) void attend_kernel(PrefillArgs a) {
               if (la_blk) {
                 const float w = wt[j][kt][i];
                 const bool la = ((la_s >> (16 * kt + i)) & 1ull) && w > 0.f;
-                x = la ? (lgate2[j] + log2_acc<T>(fmax_nn(w, 1e-37f))) * inv_scale2 : x;
+                x = la ? (lgate2[j] + log2_acc<T>(fmax_nn(w, 1e-37f)) +
+                          (float)(t - (blo + 16 * kt + 4 * g4 + i)) * l2g) * inv_scale2
+                       : x;
               }
               st[j][kt][i] = x;
             }
@@ -2543,8 +2583,19 @@ __global__ __launch_bounds__(512) void attend_kernel(PrefillArgs a) {
       if (la_blk || do_fold) {
         f32x4 phk[4];
         block_phi<T, D>(P, phk, la_blk);  // WF is complete on return
-        // the fold writes only SP / zs, which this chunk no longer reads
-        if (do_fold) block_fold<T, D>(P, phk);
+        // the fold writes only SP / zs, which this chunk no longer reads;
+        // with the forget gate the state moves from blo to the block's
+        // end re (factor gamma^(re - blo)) and key j enters at gamma^(re - j)
+        if (do_fold) {
+          const int re = min(blo + 64, fold_hi);
+          if (l2g != 0.f) {
+#pragma unroll
+            for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+              for (int i = 0; i < 4; ++i) phk[kt][i] *= exp2f((float)(re - (blo + 16 * kt + 4 * g4 + i)) * l2g);
+          }
+          block_fold<T, D>(P, phk, l2g != 0.f ? exp2f((float)(re - blo) * l2g) : 1.f);
+        }
       }
       // one call site, whatever the block (the accumulators then stay in
       // place); idle waves run it too on a copy of wave 0's rows and store

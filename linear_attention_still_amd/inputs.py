@@ -171,6 +171,14 @@ def make_out_gate(wl: Workload, shape, device="cpu", seed: Optional[int] = None)
     return g.to(torch.bfloat16 if wl.dtype == "bf16" else torch.float32)
 
 
+def make_decay(wl: Workload, device="cpu", seed: Optional[int] = None, lo: float = 0.9) -> torch.Tensor:
+    """Forget factors of the linear state, one per kv head, float32,
+    U(lo, 1): from a memory of ~10 tokens (0.9) to none at all (1)."""
+    gen = torch.Generator(device=device)
+    gen.manual_seed((wl.seed if seed is None else seed) + 32452843)
+    return lo + (1.0 - lo) * torch.rand((wl.n_kv_heads,), generator=gen, device=device, dtype=torch.float32)
+
+
 def make_decode_tokens(wl: Workload, n_steps: int, device="cpu",
                        seed: Optional[int] = None) -> Dict[str, torch.Tensor]:
     """New tokens for n_steps decode steps: q [S,B,Hq,d], k/v [S,B,Hkv,d].

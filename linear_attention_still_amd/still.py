@@ -81,6 +81,8 @@ def lib() -> ctypes.CDLL:
         L.still_prefill.restype = I32
         L.still_prefill_gated.argtypes = [pp, I64] + [P] * 11 + [ctypes.c_size_t, P]
         L.still_prefill_gated.restype = I32
+        L.still_prefill_decay.argtypes = [pp, I64] + [P] * 11 + [ctypes.c_size_t, P]
+        L.still_prefill_decay.restype = I32
         L.still_decode_step_gated.argtypes = [pp, I64] + [P] * 10
         L.still_decode_step_gated.restype = I32
         L.still_prefill_timed.argtypes = [pp, I64] + [P] * 10 + [ctypes.c_size_t, P, P, I32]
@@ -195,6 +197,17 @@ def still_prefill_gated(p: still_params, seq_len: int, q, k, v, fmap_w, gate, ou
                                    _stream(stream))
     if rc != STILL_OK:
         raise StillError("still_prefill_gated", rc)
+
+
+def still_prefill_decay(p: still_params, seq_len: int, q, k, v, fmap_w, gate, decay, out,
+                        sel_idx, score, state, workspace, stream=None) -> None:
+    rc = lib().still_prefill_decay(ctypes.byref(p), int(seq_len), _ptr(q), _ptr(k), _ptr(v),
+                                   _ptr(fmap_w), _ptr(gate), _ptr(decay), _ptr(out),
+                                   _ptr(sel_idx), _ptr(score), _ptr(state), _ptr(workspace),
+                                   workspace.numel() * workspace.element_size() if workspace is not None else 0,
+                                   _stream(stream))
+    if rc != STILL_OK:
+        raise StillError("still_prefill_decay", rc)
 
 
 def still_prefill_partials(p: still_params, seq_len: int, q, k, v, fmap_w, gate, out, sel_idx,

@@ -29,16 +29,19 @@ def n_threads() -> int:
 def gpu_prefill(wl: Workload, x: Dict[str, torch.Tensor], fp32_out: bool = False,
                 keep_device: bool = False, flags: int = 0, partials: bool = False,
                 ext_score: Optional[torch.Tensor] = None,
-                out_gate: Optional[torch.Tensor] = None) -> Dict[str, torch.Tensor]:
+                out_gate: Optional[torch.Tensor] = None,
+                decay: Optional[torch.Tensor] = None) -> Dict[str, torch.Tensor]:
     """still_prefill (or still_prefill_partials, or still_prefill_gated) on
     the GPU; flags are the variant flags; ext_score: the caller's routing
     scores (external route), passed in the score buffer; out_gate: the
-    output gate before the sigmoid, [B, Hq, L, d]."""
+    output gate before the sigmoid, [B, Hq, L, d]; decay: the linear
+    state's forget factors [Hkv] (still_prefill_decay)."""
     p = still.params_for(wl, fp32_out=fp32_out, flags=flags)
     xd = {k: v.cuda() for k, v in x.items()}
     L = xd["q"].shape[2]
-    print("  gpu prefill %s L=%d fp32_out=%s flags=%d partials=%s gated=%s"
-          % (wl.name, L, fp32_out, flags, partials, out_gate is not None), flush=True)
+    print("  gpu prefill %s L=%d fp32_out=%s flags=%d partials=%s gated=%s decay=%s"
+          % (wl.name, L, fp32_out, flags, partials, out_gate is not None, decay is not None),
+          flush=True)
     bufs = still.PrefillBuffers(p, L)
     if ext_score is not None:
         bufs.score.copy_(ext_score)
@@ -53,6 +56,10 @@ def gpu_prefill(wl: Workload, x: Dict[str, torch.Tensor], fp32_out: bool = False
                                      bufs.out, bufs.sel if bufs.sel.numel() else None,
                                      bufs.score, bufs.state, bufs.workspace, out["y_sa"],
                                      out["lse_sa"], out["y_la"], out["lse_la"])
+    elif decay is not None:
+        still.still_prefill_decay(p, L, xd["q"], xd["k"], xd["v"], xd["fmap_w"], xd["gate"],
+                                  decay.cuda(), bufs.out, bufs.sel if bufs.sel.numel() else None,
+                                  bufs.score, bufs.state, bufs.workspace)
     elif out_gate is not None:
         still.still_prefill_gated(p, L, xd["q"], xd["k"], xd["v"], xd["fmap_w"], xd["gate"],
                                   out_gate.cuda(), bufs.out, bufs.sel if bufs.sel.numel() else None,
@@ -71,13 +78,13 @@ def gpu_prefill(wl: Workload, x: Dict[str, torch.Tensor], fp32_out: bool = False
 
 def oracle(wl: Workload, x: Dict[str, torch.Tensor], units=None, merge: str = "one",
            partials: bool = False, route: str = "saliency",
-           ext_score=None) -> Dict[str, np.ndarray]:
+           ext_score=None, decay=None) -> Dict[str, np.ndarray]:
     print("  oracle %s units=%s threads=%d merge=%s route=%s" % (
         wl.name, "all" if units is None else len(units), n_threads(), merge, route), flush=True)
     return rec.prefill(x["q"], x["k"], x["v"], x["fmap_w"], x["gate"], window=wl.window,
                        chunk=wl.chunk, budget=wl.budget, t_max=wl.t_max, units=units,
                        n_threads=n_threads(), merge=merge, partials=partials, route=route,
-                       ext_score=ext_score)
+                       ext_score=ext_score, decay=decay)
 
 
 def bf16_half_ulp(ref: np.ndarray) -> np.ndarray:

@@ -25,14 +25,20 @@ survey (§4, gating): the entries still_prefill_gated and
 still_decode_step_gated against the oracle's output times the sigmoid of the
 same seeded gates; the bars of the ungated outputs (the sigmoid lies in
 [0, 1], so it shrinks the error with the output).
+
+The forget gate of the linear state (the survey's §2 gated linear
+attention, write strength 1): still_prefill_decay and
+still_decode_step_decay against the oracle with the same float32 factors
+per kv head (seeded U(0.9, 1)); the default path's bars for outputs,
+selections, scores and state.
 """
 import numpy as np
 import pytest
 import torch
 
 from linear_attention_still_amd import still
-from linear_attention_still_amd.inputs import (WORKLOADS, Workload, make_decode_tokens, make_inputs,
-                                               make_out_gate, make_route_scores)
+from linear_attention_still_amd.inputs import (WORKLOADS, Workload, make_decay, make_decode_tokens,
+                                               make_inputs, make_out_gate, make_route_scores)
 from oracle import bf, rec
 from tests import _parity as P
 
@@ -313,3 +319,34 @@ def test_decode_output_gate(case):
         if t % wl.chunk == 0 and o["lam"] > 0:
             got = np.stack([sels[s, b, kv].numpy() for b, kv in units])
             assert np.array_equal(got, o["sel"][:, t // wl.chunk - 1]), s
+
+
+DECAY_SHAPES = [SHAPES[0], SHAPES[1], SHAPES[2], SHAPES[3], SHAPES[5], SHAPES[6]]
+
+
+@pytest.mark.parametrize("wl", DECAY_SHAPES, ids=[w.name for w in DECAY_SHAPES])
+def test_prefill_decay(wl):
+    """still_prefill_decay: the linear keys and the state decay per token;
+    outputs, selections, scores and the exported state (held at the first
+    position past it) against the oracle."""
+    x = make_inputs(wl)
+    dec = make_decay(wl)
+    o = P.oracle(wl, x, decay=dec.numpy())
+    g = P.gpu_prefill(wl, x, fp32_out=(wl.dtype == "bf16"), decay=dec)
+    P.compare_prefill(wl, g, o, out_fp32=(wl.dtype == "bf16"))
+    if wl.dtype == "bf16":
+        g2 = P.gpu_prefill(wl, x, fp32_out=False, decay=dec)
+        P.compare_prefill(wl, g2, o, out_fp32=False, check_state_too=False)
+
+
+@pytest.mark.timeout(900)
+def test_llama8b_L16K_decay_sampled_units():
+    """The 16K workload with slow forget factors U(0.99, 1) (the state
+    spans hundreds of chunks); the oracle checks two kv-head units."""
+    wl = WORKLOADS["llama8b_bf16_L16K"]
+    x = make_inputs(wl)
+    dec = make_decay(wl, lo=0.99)
+    units = [(0, 1), (0, 6)]
+    o = P.oracle(wl, x, units=units, decay=dec.numpy())
+    g = P.gpu_prefill(wl, x, fp32_out=True, decay=dec)
+    P.compare_prefill(wl, g, o, units=units, out_fp32=True)
