@@ -295,6 +295,17 @@ int still_decode_step_gated(const still_params* p, int64_t pos, const void* q, c
                             const void* out_gate, void* state, void* out, int32_t* sel_new,
                             void* stream);
 
+/* still_decode_step with the forget gate of still_prefill_decay: decay
+ * device float32 [Hkv] in (0, 1] (required, 16-byte aligned, read only), the
+ * same factors the state was built with; linear keys and the state are
+ * weighted decay^(t - j), the chunk-boundary fold moves the state on by
+ * decay^C. Needs no workspace. Same errors as still_decode_step (a NULL
+ * decay returns STILL_EINVAL). */
+int still_decode_step_decay(const still_params* p, int64_t pos, const void* q, const void* k,
+                            const void* v, const void* fmap_w, const float* gate,
+                            const float* decay, void* state, void* out, int32_t* sel_new,
+                            void* stream);
+
 /* Ragged batches [P3 "Delayed Chunk-Level Selection ..."]: prefill and
  * decode keep one routing and memory-update rule per sequence, so each row
  * of a batch may be at its own length.

@@ -738,7 +738,7 @@ int64_t still_noalloc_scratch_bytes(void) { return (int64_t)kNoAllocScratchBytes
 static int decode_impl(const still_params* p, int64_t pos, const int32_t* row_pos, int n_tokens,
                        const void* q, const void* k, const void* v, const void* fmap_w,
                        const float* gate, void* state, void* out, int32_t* sel_new, void* stream,
-                       const void* out_gate = nullptr) {
+                       const void* out_gate = nullptr, const float* decay = nullptr) {
   Derived d;
   int rc = derive(p, &d);
   if (rc != STILL_OK) return rc;
@@ -749,7 +749,8 @@ static int decode_impl(const still_params* p, int64_t pos, const int32_t* row_po
   if (!row_pos && (pos < 1 || pos + n_tokens - 1 > ((int64_t)1 << 30))) return STILL_EINVAL;
   if (!q || !k || !v || !fmap_w || !gate || !state || !out) return STILL_EINVAL;
   if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(fmap_w) || misaligned(out) ||
-      misaligned(state) || misaligned(gate) || misaligned(out_gate) || ((uintptr_t)row_pos & 3u))
+      misaligned(state) || misaligned(gate) || misaligned(out_gate) || misaligned(decay) ||
+      ((uintptr_t)row_pos & 3u))
     return STILL_EINVAL;
   still_state_layout SL;
   layout(d, &SL);
@@ -757,6 +758,7 @@ static int decode_impl(const still_params* p, int64_t pos, const int32_t* row_po
   memset(&a, 0, sizeof(a));
   a.fmap_w = fmap_w;
   a.gate = gate;
+  a.decay = decay;
   a.state = reinterpret_cast<char*>(state);
   a.B = d.B;
   a.Hq = d.Hq;
@@ -816,6 +818,15 @@ int still_decode_step_gated(const still_params* p, int64_t pos, const void* q, c
   if (!out_gate) return STILL_EINVAL;
   return decode_impl(p, pos, nullptr, 1, q, k, v, fmap_w, gate, state, out, sel_new, stream,
                      out_gate);
+}
+
+int still_decode_step_decay(const still_params* p, int64_t pos, const void* q, const void* k,
+                            const void* v, const void* fmap_w, const float* gate,
+                            const float* decay, void* state, void* out, int32_t* sel_new,
+                            void* stream) {
+  if (!decay) return STILL_EINVAL;
+  return decode_impl(p, pos, nullptr, 1, q, k, v, fmap_w, gate, state, out, sel_new, stream,
+                     nullptr, decay);
 }
 
 int still_decode_tokens(const still_params* p, int64_t pos, const int32_t* row_pos, int n_tokens,

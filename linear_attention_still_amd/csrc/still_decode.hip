@@ -51,6 +51,7 @@ struct DecodeArgs {
   int softmax_only;  // the linear branch dropped (every gate taken as 0)
   int route;         // routing metric (ROUTE_*; not ROUTE_EXTERNAL)
   const void* out_gate;  // [B][Hq][D] T: channel-wise output gate before the sigmoid, or null
+  const float* decay;    // [Hkv] forget factor of the linear state in (0, 1], or null (1)
   float scale, eps;
   double scale64, eps64;  // the same parameters for the float64 score
   long st_unit, st_S, st_z, st_pool_k, st_pool_v, st_pool_pos, st_ring_k, st_ring_v,
@@ -264,7 +265,7 @@ struct BndFoldLds {
 
 template <typename T, int D>
 __device__ __forceinline__ void boundary_fold_mfma(const DecodeArgs& a, char* st, const T* F, int f_lo, int f_hi,
-                                                   char* lds) {
+                                                   char* lds, float l2g) {
   static_assert(sizeof(T) == 2, "16-bit data");
   using BL = BndFoldLds<D>;
   constexpr int NFT = D / 16, VPW = NFT * NFT / 8, CPR = D / 8;
@@ -359,6 +360,8 @@ __device__ __forceinline__ void boundary_fold_mfma(const DecodeArgs& a, char* st
         const float s2 = row_sum<16>(ss[i]);
         const float k2 = __shfl(n2, 4 * g4 + i);
         fac[i] = ((use16 >> (4 * g4 + i)) & 1u) ? __builtin_amdgcn_sqrtf(k2) * __builtin_amdgcn_rsqf(s2) : 0.f;
+        // forget gate: key j enters the state held at f_hi as gamma^(f_hi - j)
+        if (l2g != 0.f) fac[i] *= exp2f((float)(f_hi - (pos - r16 + 4 * g4 + i)) * l2g);
       }
 #pragma unroll
       for (int f = 0; f < NFT; ++f) {
@@ -384,13 +387,18 @@ __device__ __forceinline__ void boundary_fold_mfma(const DecodeArgs& a, char* st
       }
     }
   }
+  // the state moves from f_lo to f_hi: factor gamma^(f_hi - f_lo) (1 without the gate)
+  const float fS = l2g != 0.f ? exp2f((float)(f_hi - f_lo) * l2g) : 1.f;
 #pragma unroll
   for (int v = 0; v < VPW; ++v)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) S[(size_t)(16 * ft + 4 * g4 + i) * D + 16 * (vt0 + v) + r16] += acc[v][i];
+    for (int i = 0; i < 4; ++i) {
+      float* e = S + (size_t)(16 * ft + 4 * g4 + i) * D + 16 * (vt0 + v) + r16;
+      *e = *e * fS + acc[v][i];
+    }
   if (vt0 == 0) {
     zl = sum_over_g(zl);
-    if (g4 == 0) z[16 * ft + r16] += zl;
+    if (g4 == 0) z[16 * ft + r16] = z[16 * ft + r16] * fS + zl;
   }
 }
 
@@ -474,8 +482,11 @@ __global__ __launch_bounds__(BND_THREADS) void decode_boundary_kernel(DecodeArgs
   // float32 data with float32 features and exact expf on the VALU
   const int f_lo = full_chunks_before(c - 1, W, C) * C;
   const int f_hi = full_chunks_before(c, W, C) * C;
+  // forget gate of the linear state (base 2; 0: none): the state held at
+  // f_lo moves to f_hi, key j enters at gamma^(f_hi - j)
+  const float l2g = a.decay ? log2f(a.decay[kv]) : 0.f;
   if constexpr (sizeof(T) == 2) {
-    if (f_hi > f_lo) boundary_fold_mfma<T, D>(a, st, F, f_lo, f_hi, smem + LD::uni);  // uniform
+    if (f_hi > f_lo) boundary_fold_mfma<T, D>(a, st, F, f_lo, f_hi, smem + LD::uni, l2g);  // uniform
     __syncthreads();
     return;
   }
@@ -512,19 +523,21 @@ __global__ __launch_bounds__(BND_THREADS) void decode_boundary_kernel(DecodeArgs
     // thread tid owns S[i][jv] for jv = tid % D and i = tid / D + q2 * (512 / D)
 #pragma unroll 1
     for (int r = 0; r < FR; ++r) {
-      const float vr = vs[r * D + tid % D];
+      const float wr = l2g != 0.f ? exp2f((float)(f_hi - (g0 + r)) * l2g) : 1.f;
+      const float vr = vs[r * D + tid % D] * wr;
       const float* pr = ph + r * D + tid / D;
 #pragma unroll
       for (int q2 = 0; q2 < PER; ++q2) dacc[q2] += pr[q2 * (BND_THREADS / D)] * vr;
     }
     if (tid < D)
-      for (int r = 0; r < FR; ++r) dz += ph[r * D + tid];
+      for (int r = 0; r < FR; ++r) dz += ph[r * D + tid] * (l2g != 0.f ? exp2f((float)(f_hi - (g0 + r)) * l2g) : 1.f);
     __syncthreads();
   }
   if (f_hi > f_lo) {
+    const float fS = l2g != 0.f ? exp2f((float)(f_hi - f_lo) * l2g) : 1.f;
 #pragma unroll
-    for (int q2 = 0; q2 < PER; ++q2) S[tid + BND_THREADS * q2] += dacc[q2];
-    if (tid < D) z[tid] += dz;
+    for (int q2 = 0; q2 < PER; ++q2) S[tid + BND_THREADS * q2] = S[tid + BND_THREADS * q2] * fS + dacc[q2];
+    if (tid < D) z[tid] = z[tid] * fS + dz;
   }
   __syncthreads();
 }
@@ -608,6 +621,7 @@ void decode_kernel(DecodeArgs a) {
   const int n_win = t - lo + 1;
   const int la_lo = full_chunks_before(c, W, C) * C;
   const int la_hi = min(t - W, cC - 1);  // inclusive
+  const float lng = a.decay ? logf(a.decay[kv]) : 0.f;  // forget gate, natural log (0: none)
   const int n_la = la_hi >= la_lo ? la_hi - la_lo + 1 : 0;
   const int sc_lo = t - W + 1 > 0 ? t - W + 1 : 0;  // score window
   // ring slots of consecutive positions: one modulo each, then a wrap
@@ -1039,9 +1053,10 @@ void decode_kernel(DecodeArgs a) {
     }
     const float g_r = g_lane;  // zero for r >= G
     const float lgate = g_r > 0.f ? __logf(g_r) : STILL_NEG_INF;
+    // forget gate: linear key la_lo + kk weighted gamma^(t - la_lo - kk)
     auto weight = [&](float w, int kk) {
       const bool la = lfl[kk] == 0;
-      return (la && w > 0.f) ? lgate + __logf(w) : STILL_NEG_INF;
+      return (la && w > 0.f) ? lgate + __logf(w) + (float)(t - la_lo - kk) * lng : STILL_NEG_INF;
     };
     run_tiles(LA_EARLY ? TC : TA, TB, LA_EARLY, n_la, krow_la, vrow_la, pb,
               sizeof(T) == 2 ? pb2 : (const Frag<T>*)nullptr, weight, INT_MAX);
@@ -1117,7 +1132,8 @@ void decode_kernel(DecodeArgs a) {
     for (int u = 0; u < D / 64; ++u) dz += phq[h * D + lane + 64 * u] * zreg[u];
     dz = wave_sum(dz);
     const float g = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, g_lane), h));
-    const float lws = (g > 0.f && dz > 0.f) ? __logf(g * dz) : STILL_NEG_INF;
+    // (the state is held at la_lo: the forget gate weights it gamma^(t - la_lo))
+    const float lws = (g > 0.f && dz > 0.f) ? __logf(g * dz) + (float)(t - la_lo) * lng : STILL_NEG_INF;
     float mx = lws;
 #pragma unroll
     for (int w = 0; w < DEC_WAVES; ++w) mx = fmax_nn(mx, mlw[(w * G + h) * 2]);

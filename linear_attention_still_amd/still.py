@@ -85,6 +85,8 @@ def lib() -> ctypes.CDLL:
         L.still_prefill_decay.restype = I32
         L.still_decode_step_gated.argtypes = [pp, I64] + [P] * 10
         L.still_decode_step_gated.restype = I32
+        L.still_decode_step_decay.argtypes = [pp, I64] + [P] * 10
+        L.still_decode_step_decay.restype = I32
         L.still_prefill_timed.argtypes = [pp, I64] + [P] * 10 + [ctypes.c_size_t, P, P, I32]
         L.still_prefill_timed.restype = I32
         L.still_prefill_partials.argtypes = [pp, I64] + [P] * 10 + [ctypes.c_size_t, P] + [P] * 4
@@ -275,6 +277,15 @@ def still_decode_step_gated(p: still_params, pos: int, q, k, v, fmap_w, gate, ou
                                        _ptr(out), _ptr(sel_new), _stream(stream))
     if rc != STILL_OK:
         raise StillError("still_decode_step_gated", rc)
+
+
+def still_decode_step_decay(p: still_params, pos: int, q, k, v, fmap_w, gate, decay, state, out,
+                            sel_new=None, stream=None) -> None:
+    rc = lib().still_decode_step_decay(ctypes.byref(p), int(pos), _ptr(q), _ptr(k), _ptr(v),
+                                       _ptr(fmap_w), _ptr(gate), _ptr(decay), _ptr(state),
+                                       _ptr(out), _ptr(sel_new), _stream(stream))
+    if rc != STILL_OK:
+        raise StillError("still_decode_step_decay", rc)
 
 
 # ---- allocation helpers (torch memory only) --------------------------------

@@ -230,7 +230,7 @@ def test_gated_entries_validate_before_any_hip_call():
     args[5] = fake
     assert L.still_prefill_gated(ctypes.byref(p), 256, *args, ws - 1, None) == still.STILL_EWORKSPACE
     p = still.params_for(WORKLOADS["decode_bf16_B64_ctx16K"])
-    f9 = [fake] * 9  # q, k, v, fmap_w, gate, out_gate, state, out, sel_new (then the stream)
+    f9 = [fake] * 9  # q, k, v, fmap_w, gate, out_gate | decay, state, out, sel_new (then the stream)
     for bad in (None, odd):
         f9[5] = bad
         assert L.still_decode_step_gated(ctypes.byref(p), 16384, *f9, None) == still.STILL_EINVAL
@@ -238,3 +238,27 @@ def test_gated_entries_validate_before_any_hip_call():
     assert L.still_decode_step_gated(ctypes.byref(p), 0, *f9, None) == still.STILL_EINVAL
     p = still.params_for(WORKLOADS["decode_bf16_B64_ctx16K"], flags=still.STILL_FLAG_MERGE_SUM)
     assert L.still_decode_step_gated(ctypes.byref(p), 16384, *f9, None) == still.STILL_EUNSUPPORTED
+
+
+def test_decay_entries_validate_before_any_hip_call():
+    """The forget-gated prefill and decode step require their factors, 16-byte
+    aligned; their other checks are those of the plain entries."""
+    L = still.lib()
+    fake = ctypes.c_void_p(1 << 20)
+    odd = ctypes.c_void_p((1 << 20) + 4)
+    p = still.params_for(WORKLOADS["small_f32_L256"])
+    ws = still.still_workspace_bytes(p, 256)
+    args = [fake] * 11  # q, k, v, fmap_w, gate, decay, out, sel_idx, score, state, workspace
+    for bad in (None, odd):
+        args[5] = bad
+        assert L.still_prefill_decay(ctypes.byref(p), 256, *args, ws, None) == still.STILL_EINVAL
+    args[5] = fake
+    assert L.still_prefill_decay(ctypes.byref(p), 256, *args, ws - 1, None) == still.STILL_EWORKSPACE
+    p = still.params_for(WORKLOADS["decode_bf16_B64_ctx16K"])
+    f9 = [fake] * 9
+    for bad in (None, odd):
+        f9[5] = bad
+        assert L.still_decode_step_decay(ctypes.byref(p), 16384, *f9, None) == still.STILL_EINVAL
+    f9[5] = fake
+    p = still.params_for(WORKLOADS["decode_bf16_B64_ctx16K"], flags=still.STILL_FLAG_MERGE_SUM)
+    assert L.still_decode_step_decay(ctypes.byref(p), 16384, *f9, None) == still.STILL_EUNSUPPORTED

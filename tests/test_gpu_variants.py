@@ -350,3 +350,46 @@ def test_llama8b_L16K_decay_sampled_units():
     o = P.oracle(wl, x, units=units, decay=dec.numpy())
     g = P.gpu_prefill(wl, x, fp32_out=True, decay=dec)
     P.compare_prefill(wl, g, o, units=units, out_fp32=True)
+
+
+@pytest.mark.parametrize("case", DECODE_SHAPES, ids=[c[0].name for c in DECODE_SHAPES])
+def test_decode_decay(case):
+    """still_prefill_decay, then still_decode_step_decay steps over chunk
+    boundaries (the fold moves the state on by gamma^C); outputs, kept
+    positions and the state against the oracle's run over L0 + n tokens."""
+    wl, L0, n = case
+    x = make_inputs(wl, seq_len=L0)
+    toks = make_decode_tokens(wl, n)
+    dec = make_decay(wl, seed=wl.seed + 2)
+    g = P.gpu_prefill(wl, x, keep_device=True, decay=dec)
+    p = still.params_for(wl, fp32_out=True)
+    xd = {k: v.cuda() for k, v in x.items()}
+    td = {k: v.cuda() for k, v in toks.items()}
+    dd = dec.cuda()
+    lam = still.still_lambda(p)
+    outs, sels = [], []
+    for s in range(n):
+        out = torch.empty((wl.batch, wl.n_q_heads, wl.head_dim), dtype=torch.float32, device="cuda")
+        sel = torch.empty((wl.batch, wl.n_kv_heads, max(lam, 1)), dtype=torch.int32, device="cuda")
+        still.still_decode_step_decay(p, L0 + s, td["q"][s], td["k"][s], td["v"][s], xd["fmap_w"],
+                                      xd["gate"], dd, g["_state"], out, sel if lam > 0 else None)
+        outs.append(out)
+        sels.append(sel[..., :lam])
+    torch.cuda.synchronize()
+    outs, sels = torch.stack(outs).cpu(), torch.stack(sels).cpu()
+    units = [(b, kv) for b in range(wl.batch) for kv in range(wl.n_kv_heads)]
+    qs, ks, vs, Fs, gs = P.concat_units(x, toks, wl, units)
+    o = rec.run_units(qs, ks, vs, Fs, gs, window=wl.window, chunk=wl.chunk, budget=wl.budget,
+                      t_max=wl.t_max, n_threads=P.n_threads(),
+                      decay=np.array([dec[kv].item() for _, kv in units], np.float32))
+    G = wl.group
+    yg = np.stack([outs[:, b, kv * G:(kv + 1) * G].numpy().transpose(1, 0, 2) for b, kv in units])
+    P.check_outputs(yg, o["y"][:, :, L0:], wl.dtype, True, "decay decode y")
+    for s in range(n):
+        t = L0 + s
+        if t % wl.chunk == 0 and o["lam"] > 0:
+            got = np.stack([sels[s, b, kv].numpy() for b, kv in units])
+            assert np.array_equal(got, o["sel"][:, t // wl.chunk - 1]), s
+    sv = still.state_views(p, g["_state"])
+    P.check_state(sv["S"].cpu().numpy(), o["S"], wl.dtype, "decay decode S")
+    P.check_state(sv["z"].cpu().numpy(), o["z"], wl.dtype, "decay decode z")
