@@ -212,7 +212,8 @@ int still_prefill_gated(const still_params* p, int64_t seq_len, const void* q, c
  * give undefined results), 16-byte aligned, required. The exported state
  * holds decay^(R - j) phi(k_j) v_j^T, R the first position past the
  * chunks it covers; still_decode_step_decay continues it with the same
- * decay. Same outputs, workspace and errors as still_prefill otherwise. */
+ * decay. Same outputs, workspace and errors as still_prefill otherwise;
+ * STILL_FLAG_MERGE_SUM returns STILL_EUNSUPPORTED. */
 int still_prefill_decay(const still_params* p, int64_t seq_len, const void* q, const void* k,
                         const void* v, const void* fmap_w, const float* gate, const float* decay,
                         void* out, int32_t* sel_idx, float* score, void* state, void* workspace,

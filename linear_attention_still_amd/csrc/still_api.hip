@@ -196,12 +196,22 @@ void set_prefill_attrs(int family) {
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)still::Blk<T, D>::bytes);
   (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&still::attend_kernel<T, D, 2, true>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)still::Blk<T, D>::bytes);
-  if constexpr (sizeof(T) == 2)
+  // the forget-gate (decay) instantiations
+  (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&still::attend_kernel<T, D, 1, false, true>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)still::Blk<T, D>::bytes);
+  (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&still::attend_kernel<T, D, 2, false, true>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)still::Blk<T, D>::bytes);
+  if constexpr (sizeof(T) == 2) {
     (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&still::state_delta_kernel<T, D>),
                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)still::SdLds<T, D>::bytes);
-  else
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&still::state_delta_kernel<T, D, true>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)still::SdLds<T, D>::bytes);
+  } else {
     (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&still::state_delta_f32_kernel<D>),
                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)still::Blk<T, D>::bytes);
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&still::state_delta_f32_kernel<D, true>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)still::Blk<T, D>::bytes);
+  }
   g_attr_done[dev] |= 1ull << family;
 }
 
@@ -306,10 +316,16 @@ int launch_prefill(const Derived& d, const Plan& pl, still::PrefillArgs a, hipSt
   if (!fuse) select_kernel<T, D><<<dim3(n_sel, d.Hkv, d.B), dim3(256), lds_sel, s>>>(a);
   mk.at(2, 1);
   mk.at(3, 0);
-  if constexpr (sizeof(T) == 2)
-    state_delta_kernel<T, D><<<dim3(pl.NS, d.Hkv, d.B), dim3(512), SdLds<T, D>::bytes, s>>>(a);
-  else
-    state_delta_f32_kernel<D><<<dim3(pl.NS, d.Hkv, d.B), dim3(512), Blk<T, D>::bytes, s>>>(a);
+  // the forget gate (a.decay) takes instantiations of its own, so the
+  // plain layer's kernels carry none of its arithmetic
+  const bool dk = a.decay != nullptr;
+  if constexpr (sizeof(T) == 2) {
+    if (dk) state_delta_kernel<T, D, true><<<dim3(pl.NS, d.Hkv, d.B), dim3(512), SdLds<T, D>::bytes, s>>>(a);
+    else state_delta_kernel<T, D><<<dim3(pl.NS, d.Hkv, d.B), dim3(512), SdLds<T, D>::bytes, s>>>(a);
+  } else {
+    if (dk) state_delta_f32_kernel<D, true><<<dim3(pl.NS, d.Hkv, d.B), dim3(512), Blk<T, D>::bytes, s>>>(a);
+    else state_delta_f32_kernel<D><<<dim3(pl.NS, d.Hkv, d.B), dim3(512), Blk<T, D>::bytes, s>>>(a);
+  }
   mk.at(3, 1);
   mk.at(4, 0);
   // the scan and, as further workgroups of the same launch, the decode-state
@@ -319,12 +335,20 @@ int launch_prefill(const Derived& d, const Plan& pl, still::PrefillArgs a, hipSt
   const int n_ring_grp = (pl.L - ring_lo + 63) / 64;
   const int n_pool = pool_count_at(pl.n_dec, d.lam, d.cap_chunks);
   const int n_pool_grp = n_pool > 0 ? (n_pool + 15) / 16 : 1;  // >= 1: it writes the position
-  state_scan_kernel<T, D><<<dim3(n_scan + n_ring_grp + n_pool_grp, d.Hkv, d.B), dim3(256), Blk<T, D>::ft_bytes, s>>>(
-      a, n_scan);
+  if (dk)
+    state_scan_kernel<T, D, true><<<dim3(n_scan + n_ring_grp + n_pool_grp, d.Hkv, d.B), dim3(256),
+                                    Blk<T, D>::ft_bytes, s>>>(a, n_scan);
+  else
+    state_scan_kernel<T, D><<<dim3(n_scan + n_ring_grp + n_pool_grp, d.Hkv, d.B), dim3(256), Blk<T, D>::ft_bytes,
+                              s>>>(a, n_scan);
   mk.at(4, 1);
   mk.at(5, 0);
-  if (pl.part)
+  if (pl.part)  // (the forget gate is refused with the separate branches on the host)
     attend_kernel<T, D, 2, true><<<dim3(pl.NS * d.Hkv * pl.nHG * d.B), dim3(512), Blk<T, D>::bytes, s>>>(a);
+  else if (dk && pl.HPW == 2)
+    attend_kernel<T, D, 2, false, true><<<dim3(pl.NS * d.Hkv * pl.nHG * d.B), dim3(512), Blk<T, D>::bytes, s>>>(a);
+  else if (dk)
+    attend_kernel<T, D, 1, false, true><<<dim3(pl.NS * d.Hkv * pl.nHG * d.B), dim3(512), Blk<T, D>::bytes, s>>>(a);
   else if (pl.HPW == 2)
     attend_kernel<T, D, 2><<<dim3(pl.NS * d.Hkv * pl.nHG * d.B), dim3(512), Blk<T, D>::bytes, s>>>(a);
   else
@@ -535,6 +559,7 @@ static int prefill_impl(const still_params* p, int64_t seq_len, const void* q, c
   const bool merge_sum = (p->flags & STILL_FLAG_MERGE_SUM) != 0;
   const bool softmax_only = (p->flags & STILL_FLAG_SOFTMAX_ONLY) != 0;
   if (merge_sum && softmax_only) return STILL_EINVAL;
+  if (decay && merge_sum) return STILL_EUNSUPPORTED;  // the forget gate takes the single-normaliser walk
   // the branches are kept apart for the sum merge and for the partials
   const Plan pl = plan(d, seq_len, merge_sum || parts.any());
   if ((int64_t)ws_bytes < pl.ws_total) return STILL_EWORKSPACE;

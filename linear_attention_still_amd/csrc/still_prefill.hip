@@ -1460,9 +1460,9 @@ __device__ __forceinline__ float fold_zsum(const BlkPtr<T, D>& P, const f32x4 (&
 
 // Fold the block into the walk's state in LDS (SP += contribution, z += ...);
 // wave w updates the d_k tile w, i.e. half e = w % 2 of the pairs (vt, w/2).
-template <typename T, int D>
-// fS: the forget gate's factor on the state before the block's keys are
-// added (their features come weighted already); 1 without the gate.
+// DK: with the forget gate, fS is its factor on the state before the
+// block's keys are added (their features come weighted already).
+template <typename T, int D, bool DK = false>
 __device__ __forceinline__ void block_fold(const BlkPtr<T, D>& P, const f32x4 (&ph)[4], float fS = 1.f) {
   using B_ = Blk<T, D>;
   const int wave = opaque_tid() >> 6, lane = opaque_tid() & 63, r16 = lane & 15, g4 = lane >> 4;
@@ -1474,10 +1474,14 @@ __device__ __forceinline__ void block_fold(const BlkPtr<T, D>& P, const f32x4 (&
 #pragma unroll
   for (int vt = 0; vt < D / 16; ++vt) {
     float* sp = P.pair(vt * (D / 32) + (wave >> 1), wave & 1);
-    *reinterpret_cast<f32x4*>(sp) = *reinterpret_cast<const f32x4*>(sp) * fS + acc[vt];
+    if constexpr (DK) *reinterpret_cast<f32x4*>(sp) = *reinterpret_cast<const f32x4*>(sp) * fS + acc[vt];
+    else *reinterpret_cast<f32x4*>(sp) += acc[vt];
   }
   const float z = fold_zsum<T, D>(P, ph);
-  if (g4 == 0) P.zs[16 * wave + r16] = P.zs[16 * wave + r16] * (double)fS + (double)z;
+  if (g4 == 0) {
+    if constexpr (DK) P.zs[16 * wave + r16] = P.zs[16 * wave + r16] * (double)fS + (double)z;
+    else P.zs[16 * wave + r16] += (double)z;
+  }
 }
 
 // Super-chunk states in the workspace use the fragment-linear layout of SP
@@ -1631,7 +1635,7 @@ __device__ __forceinline__ void big_key_fold(const BlkPtr<T, D>& P, const BigScr
 // float32 data: in blocks of 64 keys through the attention kernel's block
 // helpers (features of feature tile w by wave w, per-key statistics combined
 // across the waves through LDS).
-template <int D>
+template <int D, bool DK = false>
 __global__ __launch_bounds__(512) void state_delta_f32_kernel(PrefillArgs a) {
   using T = float;
   using B_ = Blk<T, D>;
@@ -1656,7 +1660,7 @@ __global__ __launch_bounds__(512) void state_delta_f32_kernel(PrefillArgs a) {
   const int hi = (s == a.NS - 1 ? full_chunks_before(a.T - 1, a.W, a.C)
                                 : full_chunks_before(s * a.K + a.K, a.W, a.C)) * a.C;
   // forget gate: the delta is held at hi, key j weighted gamma^(hi - j)
-  const double l2g64 = a.decay ? log2((double)a.decay[kv]) : 0.0;
+  const double l2g64 = DK ? log2((double)a.decay[kv]) : 0.0;
   const float l2g = (float)l2g64;
   // block blo + 64 is issued as soon as block blo is in LDS (past hi the
   // loads read zeros past the buffer range)
@@ -1670,7 +1674,7 @@ __global__ __launch_bounds__(512) void state_delta_f32_kernel(PrefillArgs a) {
     const uint64_t big = mark_big_keys<T, D>(P, Z);
     f32x4 ph[4];
     block_phi<T, D>(P, ph, false);
-    if (l2g != 0.f) {  // uniform: key j weighted gamma^(hi - j)
+    if constexpr (DK) {  // key j weighted gamma^(hi - j)
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
@@ -1692,7 +1696,7 @@ __global__ __launch_bounds__(512) void state_delta_f32_kernel(PrefillArgs a) {
     }
     for (uint64_t m = big; m; m &= m - 1) {  // uniform
       const int kk = (int)__builtin_ctzll(m);
-      big_key_fold<T, D>(P, Z, kk, sum, zsum, l2g != 0.f ? exp2((double)(hi - (blo + kk)) * l2g64) : 1.0);
+      big_key_fold<T, D>(P, Z, kk, sum, zsum, DK ? exp2((double)(hi - (blo + kk)) * l2g64) : 1.0);
     }
   }
   float* dst = a.dS + ((size_t)unit * a.NS + s) * (D * D + D);
@@ -1754,7 +1758,7 @@ __device__ __forceinline__ double group_sum_d(double x) {
   return x;
 }
 
-template <typename T, int D>
+template <typename T, int D, bool DK = false>
 __global__ __launch_bounds__(512) void state_delta_kernel(PrefillArgs a) {
   static_assert(sizeof(T) == 2, "16-bit data");
   using L_ = SdLds<T, D>;
@@ -1794,7 +1798,7 @@ __global__ __launch_bounds__(512) void state_delta_kernel(PrefillArgs a) {
   const int hi = (s == a.NS - 1 ? full_chunks_before(a.T - 1, a.W, a.C)
                                 : full_chunks_before(s * a.K + a.K, a.W, a.C)) * a.C;
   // forget gate: the delta is held at hi, key j weighted gamma^(hi - j)
-  const double l2g64 = a.decay ? log2((double)a.decay[kv]) : 0.0;
+  const double l2g64 = DK ? log2((double)a.decay[kv]) : 0.0;
   const float l2g = (float)l2g64;
   // fold ownership: feature tile ft, d_v tiles vt0 .. vt0 + VPW - 1
   const int ft = wave % NFT, vt0 = (wave / NFT) * VPW;
@@ -1920,7 +1924,7 @@ __global__ __launch_bounds__(512) void state_delta_kernel(PrefillArgs a) {
         const float s2 = row_sum<16>(ss[i]);
         const float k2 = __shfl(n2, 4 * g4 + i);
         fac[i] = ((use16 >> (4 * g4 + i)) & 1u) ? __builtin_amdgcn_sqrtf(k2) * __builtin_amdgcn_rsqf(s2) : 0.f;
-        if (l2g != 0.f) fac[i] *= exp2f((float)(hi - (row - r16 + 4 * g4 + i)) * l2g);
+        if constexpr (DK) fac[i] *= exp2f((float)(hi - (row - r16 + 4 * g4 + i)) * l2g);
       }
 #pragma unroll
       for (int f = 0; f < NFT; ++f) {
@@ -2024,7 +2028,7 @@ __global__ __launch_bounds__(512) void state_delta_kernel(PrefillArgs a) {
           bst[(n * 8 + wave) * 2 + 1] = se;
           if (wave == 0) {
             bk2[n] = kn2d[kk];
-            bk2[SD_NBK + n] = l2g != 0.f ? exp2((double)(hi - row) * l2g64) : 1.0;  // gamma^(hi - j)
+            if constexpr (DK) bk2[SD_NBK + n] = exp2((double)(hi - row) * l2g64);  // gamma^(hi - j)
           }
         }
       }
@@ -2042,7 +2046,10 @@ __global__ __launch_bounds__(512) void state_delta_kernel(PrefillArgs a) {
         M = fmax(M, dppd<0x4E>(M));
         M = fmax(M, dppd<0x141>(M));
         const double S = group_sum_d<8>(bst[(n * 8 + w8) * 2 + 1] * exp(2.0 * (mw - M)));
-        if (part == 0) bphi[n * D + j] = bk2[SD_NBK + n] * (sqrt(bk2[n]) * exp(bphi[n * D + j] - M) / sqrt(S));
+        if (part == 0) {
+          if constexpr (DK) bphi[n * D + j] = bk2[SD_NBK + n] * (sqrt(bk2[n]) * exp(bphi[n * D + j] - M) / sqrt(S));
+          else bphi[n * D + j] = sqrt(bk2[n]) * exp(bphi[n * D + j] - M) / sqrt(S);
+        }
       }
       __syncthreads();
       ml = rl;
@@ -2076,7 +2083,7 @@ __global__ __launch_bounds__(512) void state_delta_kernel(PrefillArgs a) {
 // and z, each rounded to float32 once from a float64 running sum.
 // Part bx of the scan for unit (blockIdx.y, blockIdx.z): 256 of the D*D + D
 // state entries.
-template <int D>
+template <int D, bool DK>
 __device__ __forceinline__ void state_scan_part(const PrefillArgs& a, int bx) {
   float* dS = a.dS;
   const int NS = a.NS;
@@ -2088,7 +2095,7 @@ __device__ __forceinline__ void state_scan_part(const PrefillArgs& a, int bx) {
   // forget gate: super-chunk s's delta is held at the end hi_s of its key
   // range and the running sum at the start lo_s = hi_{s-1}, so it moves on
   // by gamma^(hi_s - lo_s) before the delta is added
-  const double l2g = a.decay ? log2((double)a.decay[blockIdx.y]) : 0.0;
+  const double l2g = DK ? log2((double)a.decay[blockIdx.y]) : 0.0;
   auto key_end = [&](int s2) {
     return (s2 == NS - 1 ? full_chunks_before(a.T - 1, a.W, a.C) : full_chunks_before(s2 * a.K + a.K, a.W, a.C)) *
            a.C;
@@ -2104,7 +2111,7 @@ __device__ __forceinline__ void state_scan_part(const PrefillArgs& a, int bx) {
     for (int i = 0; i < NB; ++i)
       if (s0 + i < NS) {
         base[(size_t)(s0 + i) * n_elem] = (float)run;
-        if (l2g != 0.0) {
+        if constexpr (DK) {
           const int s2 = s0 + i, lo_s = full_chunks_before(s2 * a.K, a.W, a.C) * a.C;
           run *= exp2((double)(key_end(s2) - lo_s) * l2g);
         }
@@ -2130,10 +2137,10 @@ __device__ __forceinline__ void state_scan_part(const PrefillArgs& a, int bx) {
 // instead of after the attention walk.
 template <typename T, int D>
 __device__ void export_part(const PrefillArgs& a, int x);
-template <typename T, int D>
+template <typename T, int D, bool DK = false>
 __global__ __launch_bounds__(256) void state_scan_kernel(PrefillArgs a, int n_scan) {
   if ((int)blockIdx.x < n_scan)
-    state_scan_part<D>(a, (int)blockIdx.x);
+    state_scan_part<D, DK>(a, (int)blockIdx.x);
   else
     export_part<T, D>(a, (int)blockIdx.x - n_scan);
 }
@@ -2171,7 +2178,7 @@ __global__ __launch_bounds__(256) void state_scan_kernel(PrefillArgs a, int n_sc
 // the state, without the gate); the output is their merge (the single
 // normaliser, or the sum y_SA + g y_LA), and the branch partials (normalised
 // outputs and natural-log normalisers) are written when asked for.
-template <typename T, int D, int HPW, bool PART = false>
+template <typename T, int D, int HPW, bool PART = false, bool DK = false>
 __global__ __launch_bounds__(512) void attend_kernel(PrefillArgs a) {
   static_assert(!PART || HPW == 2, "the separate-branch walk uses both head slots");
   using B_ = Blk<T, D>;
@@ -2218,7 +2225,7 @@ __global__ __launch_bounds__(512) void attend_kernel(PrefillArgs a) {
     qr[j] = make_rsrc(reinterpret_cast<const T*>(a.q) + ((size_t)(b * a.Hq + hh[j]) * L) * D, kv_bytes);
   }
   // forget gate of the linear state (0: none), base 2
-  const float l2g = a.decay ? log2f(a.decay[kv]) : 0.f;
+  const float l2g = DK ? log2f(a.decay[kv]) : 0.f;
   // the output gates of the wave's heads (only read with a.out_gate)
   __amdgpu_buffer_rsrc_t gr[HPW];
 #pragma unroll
@@ -2365,7 +2372,8 @@ __global__ __launch_bounds__(512) void attend_kernel(PrefillArgs a) {
         if (gg[j] > 0.f && dz[j] > 0.f) {
           // the state is held at band_lo: the forget gate weights it
           // gamma^(t - band_lo) at this query
-          mrun[j] = log2_acc<T>(gg[j] * dz[j]) + (float)(t - band_lo) * l2g;
+          mrun[j] = log2_acc<T>(gg[j] * dz[j]);
+          if constexpr (DK) mrun[j] += (float)(t - band_lo) * l2g;
           lacc[j] = f32x4{1.f, 1.f, 1.f, 1.f};
           if constexpr (sizeof(T) == 4) {
             const float inv = 1.f / dz[j];
@@ -2473,9 +2481,12 @@ __global__ __launch_bounds__(512) void attend_kernel(PrefillArgs a) {
               if (la_blk) {
                 const float w = wt[j][kt][i];
                 const bool la = ((la_s >> (16 * kt + i)) & 1ull) && w > 0.f;
-                x = la ? (lgate2[j] + log2_acc<T>(fmax_nn(w, 1e-37f)) +
-                          (float)(t - (blo + 16 * kt + 4 * g4 + i)) * l2g) * inv_scale2
-                       : x;
+                if constexpr (DK)
+                  x = la ? (lgate2[j] + log2_acc<T>(fmax_nn(w, 1e-37f)) +
+                            (float)(t - (blo + 16 * kt + 4 * g4 + i)) * l2g) * inv_scale2
+                         : x;
+                else
+                  x = la ? (lgate2[j] + log2_acc<T>(fmax_nn(w, 1e-37f))) * inv_scale2 : x;
               }
               st[j][kt][i] = x;
             }
@@ -2588,13 +2599,15 @@ __global__ __launch_bounds__(512) void attend_kernel(PrefillArgs a) {
         // end re (factor gamma^(re - blo)) and key j enters at gamma^(re - j)
         if (do_fold) {
           const int re = min(blo + 64, fold_hi);
-          if (l2g != 0.f) {
+          if constexpr (DK) {
 #pragma unroll
             for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
               for (int i = 0; i < 4; ++i) phk[kt][i] *= exp2f((float)(re - (blo + 16 * kt + 4 * g4 + i)) * l2g);
+            block_fold<T, D, true>(P, phk, exp2f((float)(re - blo) * l2g));
+          } else {
+            block_fold<T, D>(P, phk);
           }
-          block_fold<T, D>(P, phk, l2g != 0.f ? exp2f((float)(re - blo) * l2g) : 1.f);
         }
       }
       // one call site, whatever the block (the accumulators then stay in

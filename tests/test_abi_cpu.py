@@ -262,3 +262,11 @@ def test_decay_entries_validate_before_any_hip_call():
     f9[5] = fake
     p = still.params_for(WORKLOADS["decode_bf16_B64_ctx16K"], flags=still.STILL_FLAG_MERGE_SUM)
     assert L.still_decode_step_decay(ctypes.byref(p), 16384, *f9, None) == still.STILL_EUNSUPPORTED
+
+
+def test_decay_refuses_the_sum_merge():
+    L = still.lib()
+    fake = ctypes.c_void_p(1 << 20)
+    p = still.params_for(WORKLOADS["small_f32_L256"], flags=still.STILL_FLAG_MERGE_SUM)
+    ws = still.still_workspace_bytes(p, 256)
+    assert L.still_prefill_decay(ctypes.byref(p), 256, *([fake] * 11), ws, None) == still.STILL_EUNSUPPORTED
