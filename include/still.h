@@ -89,6 +89,15 @@ enum { STILL_DTYPE_F32 = 0, STILL_DTYPE_BF16 = 1 };
  *     only (decode returns STILL_EUNSUPPORTED). */
 #define STILL_FLAG_SOFTMAX_ONLY 2u
 #define STILL_FLAG_MERGE_SUM 4u
+/* Paged kept pool (serving layout for ragged batches, [P3 "Delayed
+ * Chunk-Level Selection ..."]: each sequence keeps its own pool): the decode
+ * state holds no pool rows (its pool_k and pool_v regions are empty) and the
+ * rows live in pages of an arena the caller allocates and maps per unit
+ * through a page table (see still_prefill_paged); only the _paged entries
+ * accept such params (the others return STILL_EINVAL). The pool's capacity
+ * (budget - window rows) may span at most 256 pages. */
+#define STILL_FLAG_PAGED_POOL 16u
+#define STILL_POOL_PAGE_ROWS 16 /* kept tokens per page */
 /* Routing metric, flags bits 8..11 (STILL_FLAG_ROUTE(r)): the score that
  * ranks a chunk's tokens for the delayed Top-lambda. The default is the
  * Self-Saliency Score; the others are the alternatives of the STILL
@@ -219,6 +228,30 @@ int still_prefill_decay(const still_params* p, int64_t seq_len, const void* q, c
                         void* out, int32_t* sel_idx, float* score, void* state, void* workspace,
                         size_t ws_bytes, void* stream);
 
+/* still_prefill with the kept pool in pages (STILL_FLAG_PAGED_POOL set in
+ * p->flags). pool_pages: the arena, n_pages pages of the params' dtype,
+ * page = STILL_POOL_PAGE_ROWS key rows of d elements then as many value
+ * rows (2 * 16 * d elements), 16-byte aligned, at most 2^31 bytes.
+ * page_table: device int32 [B * Hkv][ceil((budget - window) / 16)], entry i
+ * of unit u = b * Hkv + kv the arena page holding pool rows 16 i .. 16 i + 15
+ * of that unit. The caller allocates and maps the pages (the library
+ * allocates nothing): after a prefill of L tokens the pool holds
+ * still_pool_rows(p, L) rows, whose pages must be mapped; an entry outside
+ * [0, n_pages) for a needed row sets the state's error word (meta[2] =
+ * STILL_ESTATE) and that row is not written. Outputs, selection, scores and
+ * state as still_prefill otherwise. */
+int still_prefill_paged(const still_params* p, int64_t seq_len, const void* q, const void* k,
+                        const void* v, const void* fmap_w, const float* gate, void* out,
+                        int32_t* sel_idx, float* score, void* state, void* pool_pages,
+                        const int32_t* page_table, int64_t n_pages, void* workspace, size_t ws_bytes,
+                        void* stream);
+
+/* Rows of the kept pool once n_tokens tokens have been processed (prefill
+ * or decode): lambda rows per decided chunk until the budget is full. For a
+ * paged pool, the pages of rows [0, still_pool_rows(p, pos + 1)) must be
+ * mapped before the decode step at position pos. < 0 on error. */
+int64_t still_pool_rows(const still_params* p, int64_t n_tokens);
+
 /* still_prefill with per-kernel timing, for benchmarks: for i < n_pairs it
  * records events[2i] before and events[2i+1] after the i-th kernel of the
  * prefill on `stream` (events are caller-created hipEvent_t handles; a NULL
@@ -306,6 +339,18 @@ int still_decode_step_decay(const still_params* p, int64_t pos, const void* q, c
                             const void* v, const void* fmap_w, const float* gate,
                             const float* decay, void* state, void* out, int32_t* sel_new,
                             void* stream);
+
+/* still_decode_step with the kept pool in pages (STILL_FLAG_PAGED_POOL), the
+ * arena and table as for still_prefill_paged: the step reads pool rows
+ * [0, n_pool) and at a chunk boundary appends the kept tokens' rows, whose
+ * pages must be mapped beforehand (still_pool_rows(p, pos + 1) rows in
+ * all); an unmapped page sets the state's error word (meta[2] =
+ * STILL_ESTATE) and skips the step. Same results and errors as
+ * still_decode_step otherwise. */
+int still_decode_step_paged(const still_params* p, int64_t pos, const void* q, const void* k,
+                            const void* v, const void* fmap_w, const float* gate, void* state,
+                            void* pool_pages, const int32_t* page_table, int64_t n_pages, void* out,
+                            int32_t* sel_new, void* stream);
 
 /* Ragged batches [P3 "Delayed Chunk-Level Selection ..."]: prefill and
  * decode keep one routing and memory-update rule per sequence, so each row

@@ -24,6 +24,7 @@ struct Derived {
   int B, Hq, Hkv, G, D, W, C, m, t_max, lam, cap_chunks, R, P, esz;
   float eps, scale;
   double eps64, scale64;
+  bool paged;  // STILL_FLAG_PAGED_POOL: the pool rows live in the caller's pages
 };
 
 int derive(const still_params* p, Derived* d) {
@@ -31,7 +32,7 @@ int derive(const still_params* p, Derived* d) {
   if (p->abi_version != STILL_ABI_VERSION) return STILL_EINVAL;
   if (p->dtype != STILL_DTYPE_F32 && p->dtype != STILL_DTYPE_BF16) return STILL_EINVAL;
   if (p->flags & ~(STILL_FLAG_FP32_OUT | STILL_FLAG_SOFTMAX_ONLY | STILL_FLAG_MERGE_SUM |
-                   STILL_FLAG_ROUTE(15u)))
+                   STILL_FLAG_PAGED_POOL | STILL_FLAG_ROUTE(15u)))
     return STILL_EINVAL;  // unknown flag bits
   if (STILL_ROUTE_OF(p->flags) > STILL_ROUTE_EXTERNAL) return STILL_EINVAL;
   if ((p->flags & STILL_FLAG_SOFTMAX_ONLY) && (p->flags & STILL_FLAG_MERGE_SUM))
@@ -48,6 +49,10 @@ int derive(const still_params* p, Derived* d) {
     return STILL_EUNSUPPORTED;
   if (p->window > 256) return STILL_EUNSUPPORTED;
   if ((int64_t)p->budget - p->window > (1 << 20)) return STILL_EUNSUPPORTED;
+  // the paged pool's table of a unit is staged in LDS (at most 256 pages)
+  if ((p->flags & STILL_FLAG_PAGED_POOL) &&
+      ((int64_t)p->budget - p->window + STILL_POOL_PAGE_ROWS - 1) / STILL_POOL_PAGE_ROWS > 256)
+    return STILL_EUNSUPPORTED;
   d->B = p->batch;
   d->Hq = p->n_q_heads;
   d->Hkv = p->n_kv_heads;
@@ -64,6 +69,7 @@ int derive(const still_params* p, Derived* d) {
   d->R = p->window + 2 * p->chunk;
   d->P = p->budget - p->window;
   d->esz = p->dtype == STILL_DTYPE_F32 ? 4 : 2;
+  d->paged = (p->flags & STILL_FLAG_PAGED_POOL) != 0;
   d->eps = p->eps > 0.f ? p->eps : 1e-6f;
   d->scale = p->sm_scale > 0.f ? p->sm_scale : 1.0f / sqrtf((float)p->head_dim);
   // float64 paths (score refinement, decode score): the default values are
@@ -82,8 +88,9 @@ void layout(const Derived& d, still_state_layout* s) {
   };
   s->S = take((int64_t)d.D * d.D * 4);
   s->z = take((int64_t)d.D * 4);
-  s->pool_k = take((int64_t)d.P * d.D * d.esz);
-  s->pool_v = take((int64_t)d.P * d.D * d.esz);
+  // with the paged pool the rows live in the caller's pages (empty regions)
+  s->pool_k = take(d.paged ? 0 : (int64_t)d.P * d.D * d.esz);
+  s->pool_v = take(d.paged ? 0 : (int64_t)d.P * d.D * d.esz);
   s->pool_pos = take((int64_t)d.P * 4);
   s->ring_k = take((int64_t)d.R * d.D * d.esz);
   s->ring_v = take((int64_t)d.R * d.D * d.esz);
@@ -222,6 +229,8 @@ void set_decode_attr(int family) {
   std::lock_guard<std::mutex> lk(g_attr_mu);
   if (g_attr_done[dev] & (1ull << family)) return;
   (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&still::decode_kernel<T, D, G>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+  (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&still::decode_kernel<T, D, G, true>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
   g_attr_done[dev] |= 1ull << family;
 }
@@ -362,10 +371,12 @@ int launch_prefill(const Derived& d, const Plan& pl, still::PrefillArgs a, hipSt
 template <typename T, int D, int G>
 int launch_decode_g(const Derived& d, still::DecodeArgs a, hipStream_t s) {
   using namespace still;
-  const size_t lds = DecLds<T, D, G>::bytes(d.W);
+  const bool paged = a.pages.base != nullptr;
+  const size_t lds = paged ? DecLds<T, D, G>::bytes_paged(d.W) : DecLds<T, D, G>::bytes(d.W);
   if (lds > 160 * 1024) return STILL_EUNSUPPORTED;
   set_decode_attr<T, D, G>(decode_family<T, D, G>());
-  decode_kernel<T, D, G><<<dim3(d.Hkv, d.B), dim3(DEC_THREADS), lds, s>>>(a);
+  if (paged) decode_kernel<T, D, G, true><<<dim3(d.Hkv, d.B), dim3(DEC_THREADS), lds, s>>>(a);
+  else decode_kernel<T, D, G><<<dim3(d.Hkv, d.B), dim3(DEC_THREADS), lds, s>>>(a);
   return hipGetLastError() == hipSuccess ? STILL_OK : STILL_EHIP;
 }
 
@@ -534,14 +545,44 @@ struct Partials {
   bool any() const { return y_sa || lse_sa || y_la || lse_la; }
 };
 
+// The caller's pages of a paged pool (STILL_FLAG_PAGED_POOL).
+struct PagesArg {
+  void* base;
+  const int32_t* table;
+  int64_t n_pages;
+};
+
+// Paged params need the paged entries and the paged entries paged params;
+// the arena is addressed with 31-bit byte offsets.
+static int check_pages(const Derived& d, const PagesArg* pg) {
+  if (d.paged != (pg != nullptr)) return STILL_EINVAL;
+  if (!pg) return STILL_OK;
+  if (!pg->base || !pg->table || misaligned(pg->base) || ((uintptr_t)pg->table & 3u)) return STILL_EINVAL;
+  const int64_t page_bytes = (int64_t)2 * STILL_POOL_PAGE_ROWS * d.D * d.esz;
+  if (pg->n_pages < 1 || pg->n_pages > ((int64_t)1 << 31) / page_bytes - 1) return STILL_EINVAL;
+  return STILL_OK;
+}
+
+static still::PoolPages to_pool_pages(const Derived& d, const PagesArg& pg) {
+  still::PoolPages r;
+  r.base = reinterpret_cast<char*>(pg.base);
+  r.table = pg.table;
+  r.n_pages = (int)pg.n_pages;
+  r.width = (d.P + STILL_POOL_PAGE_ROWS - 1) / STILL_POOL_PAGE_ROWS;
+  return r;
+}
+
 static int prefill_impl(const still_params* p, int64_t seq_len, const void* q, const void* k,
                         const void* v, const void* fmap_w, const float* gate, void* out,
                         int32_t* sel_idx, float* score, void* state, void* workspace,
                         size_t ws_bytes, void* stream, void* const* events, int n_pairs,
                         Partials parts = Partials{nullptr, nullptr, nullptr, nullptr},
-                        const void* out_gate = nullptr, const float* decay = nullptr) {
+                        const void* out_gate = nullptr, const float* decay = nullptr,
+                        const PagesArg* pages = nullptr) {
   Derived d;
   int rc = derive(p, &d);
+  if (rc != STILL_OK) return rc;
+  rc = check_pages(d, pages);
   if (rc != STILL_OK) return rc;
   if (seq_len < 1 || seq_len > ((int64_t)1 << 30)) return STILL_EINVAL;
   if ((int64_t)d.B * d.Hq * seq_len * d.D > ((int64_t)1 << 40)) return STILL_EINVAL;
@@ -577,6 +618,7 @@ static int prefill_impl(const still_params* p, int64_t seq_len, const void* q, c
   a.out = out;
   a.out_gate = out_gate;
   a.decay = decay;
+  if (pages) a.pages = to_pool_pages(d, *pages);
   a.sel = sel_idx;
   a.route = (int)STILL_ROUTE_OF(p->flags);
   if (a.route == still::ROUTE_EXTERNAL) {  // the caller's scores are an input here
@@ -657,6 +699,26 @@ int still_prefill_decay(const still_params* p, int64_t seq_len, const void* q, c
   return prefill_impl(p, seq_len, q, k, v, fmap_w, gate, out, sel_idx, score, state, workspace,
                       ws_bytes, stream, nullptr, 0, Partials{nullptr, nullptr, nullptr, nullptr},
                       nullptr, decay);
+}
+
+int still_prefill_paged(const still_params* p, int64_t seq_len, const void* q, const void* k,
+                        const void* v, const void* fmap_w, const float* gate, void* out,
+                        int32_t* sel_idx, float* score, void* state, void* pool_pages,
+                        const int32_t* page_table, int64_t n_pages, void* workspace, size_t ws_bytes,
+                        void* stream) {
+  const PagesArg pg{pool_pages, page_table, n_pages};
+  return prefill_impl(p, seq_len, q, k, v, fmap_w, gate, out, sel_idx, score, state, workspace,
+                      ws_bytes, stream, nullptr, 0, Partials{nullptr, nullptr, nullptr, nullptr},
+                      nullptr, nullptr, &pg);
+}
+
+int64_t still_pool_rows(const still_params* p, int64_t n_tokens) {
+  Derived d;
+  const int rc = derive(p, &d);
+  if (rc != STILL_OK) return rc;
+  if (n_tokens < 0 || n_tokens > ((int64_t)1 << 30)) return STILL_EINVAL;
+  const int n_dec = n_tokens > 0 ? (int)((n_tokens - 1) / d.C) : 0;
+  return still::pool_count_at(n_dec, d.lam, d.cap_chunks);
 }
 
 int still_prefill_timed(const still_params* p, int64_t seq_len, const void* q, const void* k,
@@ -746,6 +808,7 @@ int still_prefill_noalloc(const still_params* p, int64_t seq_len, const void* q,
   Derived d;
   const int rc = derive(p, &d);
   if (rc != STILL_OK) return rc;
+  if (d.paged) return STILL_EINVAL;  // the paged pool has its own entries
   if (seq_len < 1 || seq_len > ((int64_t)1 << 30)) return STILL_EINVAL;
   if (ws_bytes_any(d, seq_len) > (int64_t)kNoAllocScratchBytes) return STILL_ESCRATCH;
   void* ws = nullptr;
@@ -763,9 +826,12 @@ int64_t still_noalloc_scratch_bytes(void) { return (int64_t)kNoAllocScratchBytes
 static int decode_impl(const still_params* p, int64_t pos, const int32_t* row_pos, int n_tokens,
                        const void* q, const void* k, const void* v, const void* fmap_w,
                        const float* gate, void* state, void* out, int32_t* sel_new, void* stream,
-                       const void* out_gate = nullptr, const float* decay = nullptr) {
+                       const void* out_gate = nullptr, const float* decay = nullptr,
+                       const PagesArg* pages = nullptr) {
   Derived d;
   int rc = derive(p, &d);
+  if (rc != STILL_OK) return rc;
+  rc = check_pages(d, pages);
   if (rc != STILL_OK) return rc;
   if (p->flags & STILL_FLAG_MERGE_SUM) return STILL_EUNSUPPORTED;  // decode keeps one normaliser
   // the caller's scores are a prefill input only
@@ -784,6 +850,7 @@ static int decode_impl(const still_params* p, int64_t pos, const int32_t* row_po
   a.fmap_w = fmap_w;
   a.gate = gate;
   a.decay = decay;
+  if (pages) a.pages = to_pool_pages(d, *pages);
   a.state = reinterpret_cast<char*>(state);
   a.B = d.B;
   a.Hq = d.Hq;
@@ -852,6 +919,15 @@ int still_decode_step_decay(const still_params* p, int64_t pos, const void* q, c
   if (!decay) return STILL_EINVAL;
   return decode_impl(p, pos, nullptr, 1, q, k, v, fmap_w, gate, state, out, sel_new, stream,
                      nullptr, decay);
+}
+
+int still_decode_step_paged(const still_params* p, int64_t pos, const void* q, const void* k,
+                            const void* v, const void* fmap_w, const float* gate, void* state,
+                            void* pool_pages, const int32_t* page_table, int64_t n_pages, void* out,
+                            int32_t* sel_new, void* stream) {
+  const PagesArg pg{pool_pages, page_table, n_pages};
+  return decode_impl(p, pos, nullptr, 1, q, k, v, fmap_w, gate, state, out, sel_new, stream, nullptr,
+                     nullptr, &pg);
 }
 
 int still_decode_tokens(const still_params* p, int64_t pos, const int32_t* row_pos, int n_tokens,

@@ -402,6 +402,25 @@ __device__ __forceinline__ f32x4 sigmoid_gate4(__amdgpu_buffer_rsrc_t r, uint32_
   return g;
 }
 
+// Paged kept pool (the decode state without its pool rows): page p of the
+// caller's arena holds POOL_PAGE_ROWS key rows, then as many value rows, of
+// D elements each; table[unit * width + i] is the physical page of the
+// unit's logical page i (pool rows 16 i .. 16 i + 15).
+constexpr int POOL_PAGE_ROWS = 16;
+struct PoolPages {
+  char* base;            // the arena, or null: the pool rows live in the state
+  const int32_t* table;  // [units][width]
+  int n_pages, width;
+};
+// Byte offset in the arena of pool row i of the unit (v = 0: key, 1: value;
+// row_bytes = D * element size), or -1 where its page is not one of the
+// arena's.
+__device__ __forceinline__ long pool_page_off(const PoolPages& pg, int unit, int i, int v, int row_bytes) {
+  const int p = pg.table[(size_t)unit * pg.width + i / POOL_PAGE_ROWS];
+  if (p < 0 || p >= pg.n_pages) return -1;
+  return ((long)p * 2 + v) * POOL_PAGE_ROWS * row_bytes + (long)(i % POOL_PAGE_ROWS) * row_bytes;
+}
+
 // acc + sum of squares of a bf16 fragment, by packed bf16 dot products
 __device__ __forceinline__ float frag_dot2_sumsq(const Frag<bf16>& f, float acc) {
   typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));

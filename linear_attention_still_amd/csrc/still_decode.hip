@@ -52,6 +52,7 @@ struct DecodeArgs {
   int route;         // routing metric (ROUTE_*; not ROUTE_EXTERNAL)
   const void* out_gate;  // [B][Hq][D] T: channel-wise output gate before the sigmoid, or null
   const float* decay;    // [Hkv] forget factor of the linear state in (0, 1], or null (1)
+  PoolPages pages;       // the pool rows in pages (base null: in the state)
   float scale, eps;
   double scale64, eps64;  // the same parameters for the float64 score
   long st_unit, st_S, st_z, st_pool_k, st_pool_v, st_pool_pos, st_ring_k, st_ring_v,
@@ -88,6 +89,10 @@ struct DecLds {
   // then int [W + 256]: ring flags of the linear keys (at most R = W + 2C)
   __host__ __device__ static size_t lfl(int W) { return lg + (size_t)G * W * 8; }
   __host__ __device__ static size_t bytes(int W) { return lfl(W) + (size_t)(W + 256) * 4; }
+  // paged pool: the unit's page table (at most MAX_PAGE_TABLE entries)
+  static constexpr int MAX_PAGE_TABLE = 256;
+  __host__ __device__ static size_t ptab(int W) { return bytes(W); }
+  __host__ __device__ static size_t bytes_paged(int W) { return bytes(W) + (size_t)MAX_PAGE_TABLE * 4; }
 };
 
 // 8 bytes of a row as floats: rows are read as 8-byte vectors, so a row of
@@ -446,6 +451,14 @@ __global__ __launch_bounds__(BND_THREADS) void decode_boundary_kernel(DecodeArgs
   for (int j = tid; j < C; j += BND_THREADS) ps[j] = pend[j];
   __syncthreads();
   const int lam_c = (n_pool + a.lam <= a.m - W) ? a.lam : 0;
+  if (a.pages.base) {  // uniform: the rows this step appends need pages of the arena
+    bool bad = false;
+    for (int i = n_pool; i < n_pool + lam_c; ++i) bad = bad || pool_page_off(a.pages, unit, i, 0, 1) < 0;
+    if (bad) {
+      if (tid == 0) meta[2] = -5;  // STILL_ESTATE; decode_kernel then skips the step
+      return;
+    }
+  }
   for (int j = tid; j < C; j += BND_THREADS) {
     int r = 0;  // rank by (score desc, position asc)
     for (int i = 0; i < C; ++i) r += (ps[i] > ps[j] || (ps[i] == ps[j] && i < j)) ? 1 : 0;
@@ -463,8 +476,15 @@ __global__ __launch_bounds__(BND_THREADS) void decode_boundary_kernel(DecodeArgs
     if (kept[j] < 0) continue;
     const int pos = base + j, slot = pos % R, row = n_pool + kept[j];
     const size_t src = (size_t)slot * D + part * VEC, dst = (size_t)row * D + part * VEC;
-    *reinterpret_cast<uint2*>(pool_k + dst) = ld8(ring_k + src);
-    *reinterpret_cast<uint2*>(pool_v + dst) = ld8(ring_v + src);
+    if (a.pages.base) {  // (mapped: checked above)
+      const long ok = pool_page_off(a.pages, unit, row, 0, D * sizeof(T));
+      const long ov = pool_page_off(a.pages, unit, row, 1, D * sizeof(T));
+      *reinterpret_cast<uint2*>(a.pages.base + ok + part * VEC * sizeof(T)) = ld8(ring_k + src);
+      *reinterpret_cast<uint2*>(a.pages.base + ov + part * VEC * sizeof(T)) = ld8(ring_v + src);
+    } else {
+      *reinterpret_cast<uint2*>(pool_k + dst) = ld8(ring_k + src);
+      *reinterpret_cast<uint2*>(pool_v + dst) = ld8(ring_v + src);
+    }
     if (part == 0) {
       pool_pos[row] = pos;
       ring_flag[slot] = 1;
@@ -542,7 +562,7 @@ __global__ __launch_bounds__(BND_THREADS) void decode_boundary_kernel(DecodeArgs
   __syncthreads();
 }
 
-template <typename T, int D, int G>
+template <typename T, int D, int G, bool PAGED = false>
 __global__ __launch_bounds__(DEC_THREADS) __attribute__((amdgpu_waves_per_eu(2)))
 void decode_kernel(DecodeArgs a) {
   using LD = DecLds<T, D, G>;
@@ -670,6 +690,17 @@ void decode_kernel(DecodeArgs a) {
     return;
   }
   int n_pool = (int)__builtin_amdgcn_readfirstlane(mv[2]);
+  if constexpr (PAGED) {  // every pool row read needs a page of the arena (uniform)
+    bool bad = false;
+    for (int p = lane; p < (n_pool + POOL_PAGE_ROWS - 1) / POOL_PAGE_ROWS; p += 64) {
+      const int pg = a.pages.table[(size_t)unit * a.pages.width + p];
+      bad = bad || pg < 0 || pg >= a.pages.n_pages;
+    }
+    if (__builtin_amdgcn_ballot_w64(bad)) {
+      if (tid == 0) meta[2] = -5;  // STILL_ESTATE
+      return;
+    }
+  }
 
   if (a.sel_new && !boundary)
     for (int i = tid; i < a.lam; i += DEC_THREADS) a.sel_new[(size_t)unit * a.lam + i] = -1;
@@ -709,6 +740,10 @@ void decode_kernel(DecodeArgs a) {
 #pragma unroll
   for (int u = 0; u < FPT; ++u)
     if (tid + u * DEC_THREADS < n_la) lfl[tid + u * DEC_THREADS] = flg[u];
+  int* ptab = reinterpret_cast<int*>(smem + LD::ptab(W));  // paged pool: the unit's pages
+  if constexpr (PAGED)
+    for (int i = tid; i < (n_pool + POOL_PAGE_ROWS - 1) / POOL_PAGE_ROWS; i += DEC_THREADS)
+      ptab[i] = a.pages.table[(size_t)unit * a.pages.width + i];
   __syncthreads();
   int n_oob = 0;
 #pragma unroll
@@ -717,7 +752,15 @@ void decode_kernel(DecodeArgs a) {
 
   const int r16 = lane & 15, g4 = lane >> 4;
   constexpr int DV = D / 64;  // value columns per lane
+  // paged pool: a pool row's offset is in the arena, tagged with bit 31
+  // (the arena and the state blob both stay below 2^31 bytes)
+  auto pool_row = [&](int kk, int v) -> uint32_t {
+    return 0x80000000u | (uint32_t)(((ptab[kk / POOL_PAGE_ROWS] * 2 + v) * POOL_PAGE_ROWS + kk % POOL_PAGE_ROWS) *
+                                    (D * (int)sizeof(T)));
+  };
   auto krow_sa = [&](int kk) -> uint32_t {  // byte offset of key row kk in the state blob
+    if constexpr (PAGED)
+      if (kk < n_oob) return pool_row(kk, 0);
     return kk < n_oob ? (uint32_t)a.st_pool_k + (uint32_t)kk * (D * sizeof(T))
                       : (uint32_t)a.st_ring_k + (uint32_t)wrap(lo_slot + kk - n_oob) * (D * sizeof(T));
   };
@@ -725,6 +768,8 @@ void decode_kernel(DecodeArgs a) {
   // resource, the row offset a scalar)
   const uint32_t pv_off = (uint32_t)a.st_pool_v, rv_off = (uint32_t)a.st_ring_v;
   auto vrow_sa = [&](int kk) -> uint32_t {
+    if constexpr (PAGED)
+      if (kk < n_oob) return pool_row(kk, 1);
     return kk < n_oob ? pv_off + (uint32_t)kk * (D * sizeof(T))
                       : rv_off + (uint32_t)wrap(lo_slot + kk - n_oob) * (D * sizeof(T));
   };
@@ -789,6 +834,47 @@ void decode_kernel(DecodeArgs a) {
   // columns: buffer loads with the row in the scalar offset, so the 16 rows
   // of a tile need no per-row address registers
   auto load_tile = [&](TileRegs& X, int kk0, int n, auto krow, auto vrow) {
+    if constexpr (PAGED) {
+      // rows in the state blob or, offsets tagged with bit 31, in the
+      // arena's pages: loads through addresses; absent rows read a row that
+      // exists and are zeroed after the load
+      auto rowp = [&](uint32_t o) -> const char* {
+        return (o & 0x80000000u) ? a.pages.base + (o & 0x7fffffffu) : st + o;
+      };
+      const int kr_ = kk0 + r16;
+      const bool kin = kr_ < n;
+      const char* kp = rowp(kin ? krow(kr_) : (uint32_t)a.st_ring_k) + 8 * g4 * sizeof(T);
+#pragma unroll
+      for (int kb = 0; kb < D / 32; ++kb) {
+        const Frag<T> f = ld_frag(reinterpret_cast<const T*>(kp + 32 * kb * sizeof(T)));
+        X.af[kb] = kin ? f : zero_frag<T>();
+      }
+      if constexpr (PV_MFMA) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int kk = kk0 + 4 * g4 + i;
+          const bool vin = kk < n;
+          const char* vp = rowp(vin ? vrow(kk) : (uint32_t)a.st_ring_v);
+#pragma unroll
+          for (int blk = 0; blk < D / 32; ++blk) {
+            const uint32_t w = *reinterpret_cast<const uint32_t*>(vp + (32 * blk + 2 * r16) * sizeof(T));
+            X.vw[i * (D / 32) + blk] = vin ? w : 0u;
+          }
+        }
+      } else {
+#pragma unroll
+        for (int jj = 0; jj < 16; ++jj) {
+          const int kk = kk0 + jj;  // uniform
+          const bool vin = kk < n;
+          const char* vp = rowp(vin ? vrow(kk) : (uint32_t)a.st_ring_v) + lane * DV * sizeof(T);
+          uint32_t w;
+          if constexpr (DV * sizeof(T) == 4) w = *reinterpret_cast<const uint32_t*>(vp);
+          else w = *reinterpret_cast<const uint16_t*>(vp);
+          X.vw[jj] = vin ? w : 0u;
+        }
+      }
+      return;
+    }
     // absent rows read at the end of the blob, past the range: zeros
     const uint32_t oob = (uint32_t)a.st_unit;
     const int kr_ = kk0 + r16;

@@ -58,6 +58,7 @@ struct PrefillArgs {
   const void* out_gate;    // [B][Hq][L][D] T: channel-wise output gate before the sigmoid, or null
   int fuse_sel;            // the score kernel decides the chunks (Self-Saliency route, C <= 64)
   const float* decay;      // [Hkv] forget factor of the linear state in (0, 1], or null (1)
+  PoolPages pages;         // the decode state's pool rows in pages (base null: in the state)
   int n_pend_grp;          // with fuse_sel: score workgroups (first) for the undecided chunk's float64 scores
   const float* ext_score;  // [B][Hkv][L] the caller's scores (ROUTE_EXTERNAL)
   float scale, eps;
@@ -2790,15 +2791,30 @@ __device__ void export_part(const PrefillArgs& a, int x) {
     const int r = e / CPR, c = (e % CPR) * VEC, i = i0 + r;
     if (i >= n_pool) continue;
     const int q = selu[i];
-    *reinterpret_cast<uint4*>(pk + (size_t)i * D + c) = *reinterpret_cast<const uint4*>(kg + (size_t)q * D + c);
-    *reinterpret_cast<uint4*>(pvv + (size_t)i * D + c) = *reinterpret_cast<const uint4*>(vg + (size_t)q * D + c);
+    if (a.pages.base) {  // the row's page of the arena (unmapped: the error word below)
+      const long ok = pool_page_off(a.pages, unit, i, 0, D * sizeof(T));
+      const long ov = pool_page_off(a.pages, unit, i, 1, D * sizeof(T));
+      if (ok >= 0) {
+        *reinterpret_cast<uint4*>(a.pages.base + ok + c * sizeof(T)) =
+            *reinterpret_cast<const uint4*>(kg + (size_t)q * D + c);
+        *reinterpret_cast<uint4*>(a.pages.base + ov + c * sizeof(T)) =
+            *reinterpret_cast<const uint4*>(vg + (size_t)q * D + c);
+      }
+    } else {
+      *reinterpret_cast<uint4*>(pk + (size_t)i * D + c) = *reinterpret_cast<const uint4*>(kg + (size_t)q * D + c);
+      *reinterpret_cast<uint4*>(pvv + (size_t)i * D + c) = *reinterpret_cast<const uint4*>(vg + (size_t)q * D + c);
+    }
     if (c == 0) pp[i] = q;
   }
   if (x == n_ring_grp && tid == 0) {
     int64_t* meta = reinterpret_cast<int64_t*>(st + a.st_meta);
     meta[0] = L;
     meta[1] = n_pool;
-    meta[2] = 0;
+    int64_t err = 0;
+    if (a.pages.base)  // every pool row needs a page of the arena
+      for (int i = 0; i < n_pool; i += POOL_PAGE_ROWS)
+        if (pool_page_off(a.pages, unit, i, 0, 1) < 0) err = -5;
+    meta[2] = err;
     meta[3] = 0;
   }
 }

@@ -23,6 +23,8 @@ STILL_DTYPE_BF16 = 1
 STILL_FLAG_FP32_OUT = 1
 STILL_FLAG_SOFTMAX_ONLY = 2
 STILL_FLAG_MERGE_SUM = 4
+STILL_FLAG_PAGED_POOL = 16
+STILL_POOL_PAGE_ROWS = 16
 # routing metrics (flags bits 8..11)
 ROUTES = {"saliency": 0, "diag": 1, "qk": 2, "keynorm": 3, "uniform": 4, "external": 5}
 
@@ -83,6 +85,12 @@ def lib() -> ctypes.CDLL:
         L.still_prefill_gated.restype = I32
         L.still_prefill_decay.argtypes = [pp, I64] + [P] * 11 + [ctypes.c_size_t, P]
         L.still_prefill_decay.restype = I32
+        L.still_prefill_paged.argtypes = [pp, I64] + [P] * 11 + [I64, P, ctypes.c_size_t, P]
+        L.still_prefill_paged.restype = I32
+        L.still_decode_step_paged.argtypes = [pp, I64] + [P] * 8 + [I64, P, P, P]
+        L.still_decode_step_paged.restype = I32
+        L.still_pool_rows.argtypes = [pp, I64]
+        L.still_pool_rows.restype = I64
         L.still_decode_step_gated.argtypes = [pp, I64] + [P] * 10
         L.still_decode_step_gated.restype = I32
         L.still_decode_step_decay.argtypes = [pp, I64] + [P] * 10
@@ -212,6 +220,30 @@ def still_prefill_decay(p: still_params, seq_len: int, q, k, v, fmap_w, gate, de
         raise StillError("still_prefill_decay", rc)
 
 
+def still_prefill_paged(p: still_params, seq_len: int, q, k, v, fmap_w, gate, out, sel_idx, score,
+                        state, pool_pages, page_table, workspace, stream=None) -> None:
+    """pool_pages: [n_pages, 2, STILL_POOL_PAGE_ROWS, d] device tensor of the
+    params' dtype; page_table: int32 [B * Hkv, width] (see include/still.h)."""
+    rc = lib().still_prefill_paged(ctypes.byref(p), int(seq_len), _ptr(q), _ptr(k), _ptr(v),
+                                   _ptr(fmap_w), _ptr(gate), _ptr(out), _ptr(sel_idx), _ptr(score),
+                                   _ptr(state), _ptr(pool_pages), _ptr(page_table),
+                                   int(pool_pages.shape[0]), _ptr(workspace),
+                                   workspace.numel() * workspace.element_size(), _stream(stream))
+    if rc != STILL_OK:
+        raise StillError("still_prefill_paged", rc)
+
+
+def still_pool_rows(p: still_params, n_tokens: int) -> int:
+    r = int(lib().still_pool_rows(ctypes.byref(p), int(n_tokens)))
+    if r < 0:
+        raise StillError("still_pool_rows", r)
+    return r
+
+
+def pool_table_width(p: still_params) -> int:
+    return (p.budget - p.window + STILL_POOL_PAGE_ROWS - 1) // STILL_POOL_PAGE_ROWS
+
+
 def still_prefill_partials(p: still_params, seq_len: int, q, k, v, fmap_w, gate, out, sel_idx,
                            score, state, workspace, y_sa, lse_sa, y_la, lse_la,
                            stream=None) -> None:
@@ -286,6 +318,16 @@ def still_decode_step_decay(p: still_params, pos: int, q, k, v, fmap_w, gate, de
                                        _ptr(out), _ptr(sel_new), _stream(stream))
     if rc != STILL_OK:
         raise StillError("still_decode_step_decay", rc)
+
+
+def still_decode_step_paged(p: still_params, pos: int, q, k, v, fmap_w, gate, state, pool_pages,
+                            page_table, out, sel_new=None, stream=None) -> None:
+    rc = lib().still_decode_step_paged(ctypes.byref(p), int(pos), _ptr(q), _ptr(k), _ptr(v),
+                                       _ptr(fmap_w), _ptr(gate), _ptr(state), _ptr(pool_pages),
+                                       _ptr(page_table), int(pool_pages.shape[0]), _ptr(out),
+                                       _ptr(sel_new), _stream(stream))
+    if rc != STILL_OK:
+        raise StillError("still_decode_step_paged", rc)
 
 
 # ---- allocation helpers (torch memory only) --------------------------------
@@ -390,8 +432,11 @@ def state_views(p: still_params, state: torch.Tensor) -> dict:
     return {
         "S": sec(lay.S, d * d, torch.float32, 4).view(U, d, d),
         "z": sec(lay.z, d, torch.float32, 4),
-        "pool_k": sec(lay.pool_k, P * d, edt, es).view(U, P, d),
-        "pool_v": sec(lay.pool_v, P * d, edt, es).view(U, P, d),
+        # (a paged pool keeps its rows in the caller's pages: empty here)
+        "pool_k": sec(lay.pool_k, P * d, edt, es).view(U, P, d) if not p.flags & STILL_FLAG_PAGED_POOL
+        else None,
+        "pool_v": sec(lay.pool_v, P * d, edt, es).view(U, P, d) if not p.flags & STILL_FLAG_PAGED_POOL
+        else None,
         "pool_pos": sec(lay.pool_pos, P, torch.int32, 4),
         "ring_k": sec(lay.ring_k, R * d, edt, es).view(U, R, d),
         "ring_v": sec(lay.ring_v, R * d, edt, es).view(U, R, d),

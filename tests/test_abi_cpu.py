@@ -270,3 +270,85 @@ def test_decay_refuses_the_sum_merge():
     p = still.params_for(WORKLOADS["small_f32_L256"], flags=still.STILL_FLAG_MERGE_SUM)
     ws = still.still_workspace_bytes(p, 256)
     assert L.still_prefill_decay(ctypes.byref(p), 256, *([fake] * 11), ws, None) == still.STILL_EUNSUPPORTED
+
+
+def test_paged_entries_validate_before_any_hip_call():
+    """The paged flag and the paged entries go together; the arena is 16-byte
+    aligned and its page count fits 31-bit byte offsets; the table is int32
+    aligned. The other checks are those of the plain entries."""
+    L = still.lib()
+    fake = ctypes.c_void_p(1 << 20)
+    odd = ctypes.c_void_p((1 << 20) + 8)
+    wl = WORKLOADS["small_f32_L256"]
+    plain = still.params_for(wl)
+    p = still.params_for(wl, flags=still.STILL_FLAG_PAGED_POOL)
+    ws = still.still_workspace_bytes(p, 256)
+    page_bytes = 2 * still.STILL_POOL_PAGE_ROWS * wl.head_dim * 4
+
+    def pre(pp, arena=fake, table=fake, n_pages=4, wsb=ws):
+        # q, k, v, fmap_w, gate, out, sel_idx, score, state, then the pages
+        return L.still_prefill_paged(ctypes.byref(pp), 256, *([fake] * 9), arena, table, n_pages,
+                                     fake, wsb, None)
+    assert pre(plain) == still.STILL_EINVAL  # paged entry, unpaged params
+    args = [fake] * 9
+    assert L.still_prefill(ctypes.byref(p), 256, *args, fake, ws, None) == still.STILL_EINVAL
+    assert pre(p, arena=None) == still.STILL_EINVAL
+    assert pre(p, arena=odd) == still.STILL_EINVAL
+    assert pre(p, table=None) == still.STILL_EINVAL
+    assert pre(p, table=ctypes.c_void_p((1 << 20) + 2)) == still.STILL_EINVAL
+    assert pre(p, n_pages=0) == still.STILL_EINVAL
+    assert pre(p, n_pages=(1 << 31) // page_bytes) == still.STILL_EINVAL
+    assert pre(p, wsb=ws - 1) == still.STILL_EWORKSPACE
+
+    pd = still.params_for(WORKLOADS["decode_bf16_B64_ctx16K"])
+    pdp = still.params_for(WORKLOADS["decode_bf16_B64_ctx16K"], flags=still.STILL_FLAG_PAGED_POOL)
+
+    def dec(pp, arena=fake, n_pages=4, pos=16384):
+        # q, k, v, fmap_w, gate, state, then the pages, out, sel_new
+        return L.still_decode_step_paged(ctypes.byref(pp), pos, *([fake] * 6), arena, fake, n_pages,
+                                         fake, fake, None)
+    assert dec(pd) == still.STILL_EINVAL
+    assert L.still_decode_step(ctypes.byref(pdp), 16384, *([fake] * 9), 1 << 30, None) == still.STILL_EINVAL
+    assert dec(pdp, arena=odd) == still.STILL_EINVAL
+    assert dec(pdp, n_pages=0) == still.STILL_EINVAL
+    assert dec(pdp, pos=0) == still.STILL_EINVAL
+    # the ragged and allocation-free entries keep their pool in the state
+    assert L.still_prefill_noalloc(ctypes.byref(p), 256, *args, None) == still.STILL_EINVAL
+
+
+def test_paged_params_state_and_limits():
+    """A paged pool leaves its rows out of the state; a table wider than 256
+    pages per unit is refused."""
+    wl = WORKLOADS["small_f32_L256"]
+    plain = still.params_for(wl)
+    p = still.params_for(wl, flags=still.STILL_FLAG_PAGED_POOL)
+    P = wl.budget - wl.window
+    units = wl.batch * wl.n_kv_heads
+    assert still.still_state_bytes(plain) - still.still_state_bytes(p) >= 2 * P * wl.head_dim * 4 * units
+    lay = still.still_state_layout_get(p)
+    assert lay.pool_k == lay.pool_v
+    big = still.make_params(dtype="bf16", batch=1, n_q_heads=8, n_kv_heads=1, head_dim=128,
+                            window=64, chunk=64, budget=64 + 256 * 16 + 1, t_max=128,
+                            flags=still.STILL_FLAG_PAGED_POOL)
+    with pytest.raises(still.StillError):
+        still.still_state_bytes(big)
+    ok = still.make_params(dtype="bf16", batch=1, n_q_heads=8, n_kv_heads=1, head_dim=128,
+                           window=64, chunk=64, budget=64 + 256 * 16, t_max=128,
+                           flags=still.STILL_FLAG_PAGED_POOL)
+    assert still.pool_table_width(ok) == 256
+    assert still.still_state_bytes(ok) > 0
+
+
+def test_pool_rows_counts_lambda_rows_per_decided_chunk():
+    """Chunk c is decided once chunk c + 1 has begun: after n tokens,
+    (n - 1) // C chunks are decided, each adding lambda rows until the
+    budget's chunks are used up."""
+    wl = WORKLOADS["small_f32_L256"]
+    p = still.params_for(wl)
+    lam, C = still.still_lambda(p), wl.chunk
+    cap = (wl.budget - wl.window) // lam
+    for n in (0, 1, C, C + 1, 2 * C, 2 * C + 1, 5 * C + 3, 10 ** 6):
+        n_dec = (n - 1) // C if n > 0 else 0
+        assert still.still_pool_rows(p, n) == lam * min(n_dec, cap), n
+    with pytest.raises(still.StillError):
+        still.still_pool_rows(p, -1)
