@@ -296,7 +296,7 @@ def run_decode_bench(torch, still, inputs, n_steps):
     x = inputs.make_inputs(wl, device="cuda")
     bufs = still.PrefillBuffers(p, wl.seq_len)
     still.run_prefill(p, x, bufs)
-    del x["q"]
+    del bufs.out, bufs.workspace
     toks = inputs.make_decode_tokens(wl, n_steps + 8, device="cuda")
     out = torch.empty((wl.batch, wl.n_q_heads, wl.head_dim), dtype=torch.bfloat16, device="cuda")
     sel = torch.empty((wl.batch, wl.n_kv_heads, still.still_lambda(p)), dtype=torch.int32,
@@ -319,6 +319,7 @@ def run_decode_bench(torch, still, inputs, n_steps):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     step_ms = e0.elapsed_time(e1) / n_steps
+    paged_ms = run_decode_paged(torch, still, wl, x, toks, n_steps)
     d, units = wl.head_dim, wl.batch * wl.n_kv_heads
     n_pool = 256  # 255 kept after the prefill, +1 at the boundary of step 0
     per_unit = (wl.window + n_pool) * 2 * d * 2 + d * d * 4 + d * 4
@@ -330,7 +331,46 @@ def run_decode_bench(torch, still, inputs, n_steps):
             "hbm_gbs": step_bytes / (step_ms * 1e-3) / 1e9,
             "hbm_frac": step_bytes / (step_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
             "traffic": measured_traffic("decode_kernel", "decode_llama8b_B64_ctx16K.md",
-                                        DECODE_SOURCES)}
+                                        DECODE_SOURCES),
+            "paged": {"ms_per_step": paged_ms, "hbm_gbs": step_bytes / (paged_ms * 1e-3) / 1e9,
+                      "vs_unpaged": paged_ms / step_ms,
+                      "layout": "kept pool in 16-row pages of a shared arena, "
+                                "each unit's pages a seeded random permutation"}}
+
+
+def run_decode_paged(torch, still, wl, x, toks, n_steps):
+    """The same decode steps with the kept pool in pages
+    (STILL_FLAG_PAGED_POOL): a paged prefill of the same inputs, every
+    unit's pages mapped to a seeded permutation of the arena's pages, then
+    the timed steps through still_decode_step_paged. Returns ms per step."""
+    p = still.params_for(wl, flags=still.STILL_FLAG_PAGED_POOL)
+    units, width = wl.batch * wl.n_kv_heads, still.pool_table_width(p)
+    rows = still.STILL_POOL_PAGE_ROWS
+    pages = torch.zeros((units * width, 2, rows, wl.head_dim), dtype=torch.bfloat16, device="cuda")
+    gen = torch.Generator().manual_seed(7)
+    table = torch.randperm(units * width, generator=gen).to(torch.int32).view(units, width).cuda()
+    bufs = still.PrefillBuffers(p, wl.seq_len)
+    still.still_prefill_paged(p, wl.seq_len, x["q"], x["k"], x["v"], x["fmap_w"], x["gate"], bufs.out,
+                              bufs.sel, bufs.score, bufs.state, pages, table, bufs.workspace)
+    del bufs.out, bufs.workspace
+    out = torch.empty((wl.batch, wl.n_q_heads, wl.head_dim), dtype=torch.bfloat16, device="cuda")
+    sel = torch.empty((wl.batch, wl.n_kv_heads, still.still_lambda(p)), dtype=torch.int32,
+                      device="cuda")
+    st2 = bufs.state.clone()
+    for s in range(8):
+        still.still_decode_step_paged(p, wl.seq_len + s, toks["q"][s], toks["k"][s], toks["v"][s],
+                                      x["fmap_w"], x["gate"], st2, pages, table, out, sel)
+    torch.cuda.synchronize()
+    del st2
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for s in range(n_steps):
+        still.still_decode_step_paged(p, wl.seq_len + s, toks["q"][8 + s], toks["k"][8 + s],
+                                      toks["v"][8 + s], x["fmap_w"], x["gate"], bufs.state, pages,
+                                      table, out, sel)
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / n_steps
 
 
 def run_cpu_baseline(wl, x):
