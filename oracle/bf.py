@@ -22,7 +22,7 @@ listed under "Readings" in the design notes; each function names its own.
 from __future__ import annotations
 
 import math
-from typing import Dict, List, Optional
+from typing import Dict, List, Optional, Tuple
 
 import numpy as np
 
@@ -95,7 +95,7 @@ def np_map(x: np.ndarray, F: np.ndarray) -> np.ndarray:
 def prefill(q, k, v, fmap_w, gate, *, window: int, chunk: int, budget: int,
             t_max: int, eps: float = 1e-6, sm_scale: Optional[float] = None,
             partials: bool = False, merge: str = "one", route: str = "saliency",
-            ext_score=None, decay=None) -> Dict[str, np.ndarray]:
+            ext_score=None, decay=None, fp8_from: int = -1) -> Dict[str, np.ndarray]:
     """One STILL layer over a whole sequence, every query by brute force.
 
     q [B,Hq,L,d], k/v [B,Hkv,L,d], fmap_w [Hkv,d,d], gate [Hq] (any array
@@ -127,6 +127,11 @@ def prefill(q, k, v, fmap_w, gate, *, window: int, chunk: int, budget: int,
     [P4 §2], write strength 1, applied to the linear state): the linear key j
     of query t is weighted decay^(t - j); the exported state holds
     decay^(R - j) with R = cf C, the first position past it. None = 1.
+
+    fp8_from: queries t >= fp8_from read the kept tokens that lie below
+    their window band (before both the window and the own chunk) from an
+    8-bit store, the values of e4m3_row (reading of the pages' fp8 pool);
+    -1: never.
     """
     if merge not in ("one", "sum", "softmax_only"):
         raise ValueError("merge must be one, sum or softmax_only")
@@ -166,6 +171,9 @@ def prefill(q, k, v, fmap_w, gate, *, window: int, chunk: int, budget: int,
     for b in range(B):
         for kv in range(Hkv):
             K, V, F = k[b, kv], v[b, kv], Fw[kv]
+            if fp8_from >= 0:
+                K8 = np.stack([e4m3_row(K[j])[2] for j in range(L)]) if L else K
+                V8 = np.stack([e4m3_row(V[j])[2] for j in range(L)]) if L else V
             gam = 1.0 if dec is None else float(dec[kv])
             heads = range(kv * G, kv * G + G)
             # Score of every token, summed over the query heads of the group
@@ -213,13 +221,17 @@ def prefill(q, k, v, fmap_w, gate, *, window: int, chunk: int, budget: int,
                 in_a = (pos <= t) & ((pos >= t - W + 1) | (chunk_of == c) | in_pool)
                 in_b = (pos <= t) & ~in_a
                 ia, ib = np.nonzero(in_a)[0], np.nonzero(in_b)[0]
+                Ka, Va = K[ia], V[ia]
+                if 0 <= fp8_from <= t:  # the pool below the band, as stored
+                    low = in_pool[ia] & (ia < t - W + 1)
+                    Ka, Va = np.where(low[:, None], K8[ia], Ka), np.where(low[:, None], V8[ia], Va)
                 for h in heads:
-                    s = scale * (K[ia] @ q[b, h, t])
+                    s = scale * (Ka @ q[b, h, t])
                     w0 = phik[ib] @ np_map(q[b, h, t], F)  # linear weights, no gate
                     if gam != 1.0:
                         w0 = w0 * gam ** (t - ib).astype(np.float64)
                     ea = np.exp(s - s.max())
-                    ysa = (ea @ V[ia]) / ea.sum()
+                    ysa = (ea @ Va) / ea.sum()
                     yla = (w0 @ V[ib]) / w0.sum() if len(ib) and w0.sum() > 0 else np.zeros(d)
                     if merge == "one":
                         w = g_all[h] * w0
@@ -227,7 +239,7 @@ def prefill(q, k, v, fmap_w, gate, *, window: int, chunk: int, budget: int,
                             logw = np.concatenate([s, np.log(w)])
                         mx = logw.max()
                         e = np.exp(logw - mx)
-                        vals = np.concatenate([V[ia], V[ib]])
+                        vals = np.concatenate([Va, V[ib]])
                         y[b, h, t] = (e @ vals) / e.sum()
                     elif merge == "sum":
                         y[b, h, t] = ysa + g_all[h] * yla
@@ -256,6 +268,39 @@ def prefill(q, k, v, fmap_w, gate, *, window: int, chunk: int, budget: int,
     if partials:
         out.update(y_sa=y_sa, lse_sa=lse_sa, y_la=y_la, lse_la=lse_la)
     return out
+
+
+def e4m3_values() -> np.ndarray:
+    """The 127 non-negative finite values of OCP E4M3 by code 0..126 (sign
+    bit clear): 4 exponent bits (bias 7), 3 mantissa bits, exponent field 0
+    subnormal (m/8 2^-6), code 127 NaN."""
+    out = []
+    for c in range(127):
+        e, m = c >> 3, c & 7
+        out.append(m / 8 * 2.0 ** -6 if e == 0 else (1 + m / 8) * 2.0 ** (e - 7))
+    return np.array(out)
+
+
+def e4m3_row(x) -> Tuple[np.ndarray, np.float32, np.ndarray]:
+    """One row as the kept pool's 8-bit store (reading: the pages name an
+    fp8 pool, not its format): scale s = amax / 448 in float32 (1 for a zero
+    row), each x_i / s (float32) to the nearest E4M3 value, ties to the even
+    code, beyond 448 to 448. Returns codes (uint8), s, and the values
+    code * s (float64). Nearest-value search over the code table."""
+    x = np.asarray(x, dtype=np.float32)
+    amax = np.float32(np.max(np.abs(x))) if x.size else np.float32(0)
+    s = np.float32(amax / np.float32(448)) if amax > 0 else np.float32(1)
+    y = (x / s).astype(np.float32).astype(np.float64)
+    table = e4m3_values()
+    a = np.abs(y)
+    hi = np.clip(np.searchsorted(table, a), 1, 126)  # table[hi - 1] <= a <= table[hi] inside
+    lo = hi - 1
+    dlo, dhi = a - table[lo], table[hi] - a
+    pick = np.where(dlo < dhi, lo, np.where(dhi < dlo, hi, np.where(lo % 2 == 0, lo, hi)))
+    pick = np.where(a >= 448, 126, pick)
+    codes = (pick | np.where(y < 0, 0x80, 0)).astype(np.uint8)
+    vals = table[pick] * np.where(y < 0, -1.0, 1.0) * float(s)
+    return codes, s, vals
 
 
 def output_gate(y, gate_out) -> np.ndarray:

@@ -50,8 +50,11 @@ def _load():
         f = lib.still_oracle_run
         P = ctypes.c_void_p
         f.argtypes = [ctypes.c_int] * 8 + [ctypes.c_double] * 2 + [P] * 5 + \
-            [ctypes.c_int] + [P] * 7 + [ctypes.c_int] + [P] * 4 + [ctypes.c_int, P, P]
+            [ctypes.c_int] + [P] * 7 + [ctypes.c_int] + [P] * 4 + [ctypes.c_int, P, P, ctypes.c_int]
         f.restype = ctypes.c_int
+        g = lib.still_oracle_e4m3_rows
+        g.argtypes = [ctypes.c_int, ctypes.c_int, P, P, P, P]
+        g.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -71,7 +74,7 @@ def prefill(q, k, v, fmap_w, gate, *, window: int, chunk: int, budget: int,
             units: Optional[Sequence[Tuple[int, int]]] = None,
             n_threads: int = 1, merge: str = "one",
             partials: bool = False, route: str = "saliency",
-            ext_score=None, decay=None) -> Dict[str, np.ndarray]:
+            ext_score=None, decay=None, fp8_from: int = -1) -> Dict[str, np.ndarray]:
     """Run the recurrent oracle on the listed (batch, kv head) units.
 
     q [B,Hq,L,d], k/v [B,Hkv,L,d], fmap_w [Hkv,d,d], gate [Hq]. Outputs
@@ -108,16 +111,20 @@ def prefill(q, k, v, fmap_w, gate, *, window: int, chunk: int, budget: int,
         dec = np.array([d32[kv] for _, kv in units], dtype=np.float32)
     return run_units(qs, ks, vs, Fs, gs, window=window, chunk=chunk, budget=budget,
                      t_max=t_max, eps=eps, sm_scale=sm_scale, n_threads=n_threads,
-                     merge=merge, partials=partials, route=route, ext=ext, decay=dec)
+                     merge=merge, partials=partials, route=route, ext=ext, decay=dec,
+                     fp8_from=fp8_from)
 
 
 def run_units(qs, ks, vs, Fs, gs, *, window: int, chunk: int, budget: int, t_max: int,
               eps: float = 1e-6, sm_scale: Optional[float] = None,
               n_threads: int = 1, merge: str = "one", partials: bool = False,
-              route: str = "saliency", ext=None, decay=None) -> Dict[str, np.ndarray]:
+              route: str = "saliency", ext=None, decay=None,
+              fp8_from: int = -1) -> Dict[str, np.ndarray]:
     """Run on pre-gathered per-unit arrays (see still_oracle_run); ext
     [U, L]: the caller's scores for route "external"; decay [U]: the
-    units' forget factors of the linear state (float32 values), or None."""
+    units' forget factors of the linear state (float32 values), or None;
+    fp8_from: queries from this position on read the kept tokens below
+    their window band in E4M3 (e4m3_rows), -1: never."""
     qs, ks, vs, Fs, gs = (_f32(a) for a in (qs, ks, vs, Fs, gs))
     if route == "external":
         if ext is None:
@@ -151,7 +158,7 @@ def run_units(qs, ks, vs, Fs, gs, *, window: int, chunk: int, budget: int, t_max
                               ptr(y), ptr(score), ptr(sel), ptr(S), ptr(z), ptr(pending),
                               ptr(n_pool), MERGES[merge], *pp, ROUTES[route],
                               ptr(ext) if route == "external" else None,
-                              ptr(dec64) if dec64 is not None else None)
+                              ptr(dec64) if dec64 is not None else None, int(fp8_from))
     if rc != 0:
         raise ValueError("still_oracle_run rejected its arguments (rc=%d)" % rc)
     out = {"y": y, "score": score, "sel": sel, "S": S, "z": z, "pending": pending,
@@ -159,3 +166,18 @@ def run_units(qs, ks, vs, Fs, gs, *, window: int, chunk: int, budget: int, t_max
     if part is not None:
         out.update(part)
     return out
+
+
+def e4m3_rows(x) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """Rows x [n, d] (float32) as the kept pool's 8-bit store: E4M3 codes
+    [n, d] uint8, float32 scales [n] and the values they stand for [n, d]
+    (float64). See e4m3_row in still_oracle.c."""
+    x = _f32(x)
+    n, d = x.shape
+    codes = np.zeros((n, d), np.uint8)
+    scales = np.zeros((n,), np.float32)
+    values = np.zeros((n, d))
+    ptr = lambda a: a.ctypes.data_as(ctypes.c_void_p)
+    if _load().still_oracle_e4m3_rows(n, d, ptr(x), ptr(codes), ptr(scales), ptr(values)) != 0:
+        raise ValueError("still_oracle_e4m3_rows rejected its arguments")
+    return codes, scales, values

@@ -67,6 +67,7 @@ typedef struct {
   int32_t *sel, *n_pool;
   double *y_sa, *lse_sa, *y_la, *lse_la; /* branch partials, or all null */
   const double* decay; /* [n_units] forget factor of the linear state, or null (1) */
+  int fp8_from;        /* queries t >= fp8_from read the kept pool in e4m3; < 0: never */
 } oracle_job;
 
 typedef struct {
@@ -161,6 +162,58 @@ static int full_chunks_out_of_window(int c, int W, int C) {
   return x >= 0 ? (int)(x / C) : 0;
 }
 
+/* OCP 8-bit floating point, E4M3 ("FN": no infinities, one NaN pattern per
+ * sign): 1 sign bit, 4 exponent bits with bias 7, 3 mantissa bits; code
+ * (e, m) with e > 0 is 2^(e-7) (1 + m/8), e = 0 is 2^-6 m/8; the largest
+ * finite value is 448 (e = 15, m = 6), e = 15, m = 7 is NaN. Reading for
+ * the kept pool's storage (the pages name fp8 pools, not a format): a row
+ * x of d values is stored as codes of x_i / s and the float32 scale
+ * s = amax / 448 (amax = max |x_i|; s = 1 for a zero row), each x_i / s
+ * rounded to the nearest E4M3 value, ties to the even code, magnitudes
+ * beyond 448 to 448. The divisions are float32 operations, so the codes are
+ * the same wherever float32 division is correctly rounded. */
+static uint8_t e4m3_code(float y) {
+  const uint8_t sign = y < 0.0f ? 0x80 : 0x00;
+  const float a = fabsf(y);
+  if (!(a < 448.0f)) return sign | 0x7E;
+  if (a < 0.015625f) { /* below 2^-6: multiples of 2^-9 (m = 8 is 2^-6, code 0x08) */
+    return sign | (uint8_t)rintf(a * 512.0f);
+  }
+  int e;
+  frexpf(a, &e); /* a = f 2^e, f in [0.5, 1): the binade is 2^(e-1) */
+  e -= 1;
+  int n = (int)rintf(ldexpf(a, 3 - e)); /* 8 .. 16 eighths of 2^e */
+  if (n == 16) { n = 8; e += 1; }
+  return sign | (uint8_t)(((e + 7) << 3) | (n - 8));
+}
+
+static double e4m3_value(uint8_t c) {
+  const int e = (c >> 3) & 15, m = c & 7;
+  const double v = e == 0 ? ldexp((double)m, -9) : ldexp(8.0 + m, e - 10);
+  return (c & 0x80) ? -v : v;
+}
+
+/* One row: codes and the scale, and the values they stand for. */
+static float e4m3_row(const float* x, int d, uint8_t* codes) {
+  float amax = 0.0f;
+  for (int i = 0; i < d; ++i) amax = fabsf(x[i]) > amax ? fabsf(x[i]) : amax;
+  const float s = amax > 0.0f ? amax / 448.0f : 1.0f;
+  for (int i = 0; i < d; ++i) codes[i] = e4m3_code(x[i] / s);
+  return s;
+}
+
+int still_oracle_e4m3_rows(int n, int d, const float* x, uint8_t* codes, float* scales,
+                           double* values) {
+  if (n < 0 || d < 1) return -1;
+  for (int r = 0; r < n; ++r) {
+    const float s = e4m3_row(x + (size_t)r * d, d, codes + (size_t)r * d);
+    if (scales) scales[r] = s;
+    if (values)
+      for (int i = 0; i < d; ++i) values[(size_t)r * d + i] = e4m3_value(codes[(size_t)r * d + i]) * (double)s;
+  }
+  return 0;
+}
+
 static void run_unit(const oracle_job* J, int u) {
   const int L = J->L, d = J->d, G = J->G, W = J->W, C = J->C;
   const size_t Ld = (size_t)L * d;
@@ -184,6 +237,21 @@ static void run_unit(const oracle_job* J, int u) {
   const float* ks = J->k + (size_t)u * Ld;
   const float* vs = J->v + (size_t)u * Ld;
   for (size_t i = 0; i < Ld; ++i) { K[i] = ks[i]; V[i] = vs[i]; }
+  /* the kept pool as an 8-bit store holds every row quantised (only the
+   * rows of kept tokens are read) */
+  double *K8 = NULL, *V8 = NULL;
+  if (J->fp8_from >= 0 && L > 0) {
+    uint8_t* codes = malloc((size_t)d);
+    K8 = malloc(sizeof(double) * Ld);
+    V8 = malloc(sizeof(double) * Ld);
+    for (int j = 0; j < L; ++j) {
+      const float sk = e4m3_row(ks + (size_t)j * d, d, codes);
+      for (int i = 0; i < d; ++i) K8[(size_t)j * d + i] = e4m3_value(codes[i]) * (double)sk;
+      const float sv = e4m3_row(vs + (size_t)j * d, d, codes);
+      for (int i = 0; i < d; ++i) V8[(size_t)j * d + i] = e4m3_value(codes[i]) * (double)sv;
+    }
+    free(codes);
+  }
   for (size_t i = 0; i < Ld * G; ++i) Q[i] = qs[i];
   for (size_t i = 0; i < (size_t)d * d; ++i) F[i] = J->F[(size_t)u * d * d + i];
   double* score = J->score + (size_t)u * L;
@@ -282,13 +350,17 @@ static void run_unit(const oracle_job* J, int u) {
      * weights g <phi(q), phi(k_j)>, taken in the log domain. */
     int lo = t - W + 1 < c * C ? t - W + 1 : c * C;
     if (lo < 0) lo = 0;
+    /* kept tokens below lo come from the pool's store: 8-bit from fp8_from on */
+    const int p8 = K8 != NULL && t >= J->fp8_from;
+    const double* Kp = p8 ? K8 : K;
+    const double* Vp = p8 ? V8 : V;
     int n_keys = 0;
     for (int h = 0; h < G; ++h) {
       const double* qh = Q + (size_t)h * Ld + (size_t)t * d;
       const double g = J->gate[(size_t)u * G + h];
       n_keys = 0;
       for (int p = 0; p < n_pool && pool[p] < lo; ++p) {
-        const double* kj = K + (size_t)pool[p] * d;
+        const double* kj = Kp + (size_t)pool[p] * d;
         double s = 0.0;
         for (int i = 0; i < d; ++i) s += qh[i] * kj[i];
         logit[n_keys++] = J->scale * s;
@@ -308,7 +380,7 @@ static void run_unit(const oracle_job* J, int u) {
         const int j = a < n_pool_keys ? pool[a] : lo + (a - n_pool_keys);
         const double w = exp(logit[a] - mx);
         l += w;
-        const double* vj = V + (size_t)j * d;
+        const double* vj = (a < n_pool_keys ? Vp : V) + (size_t)j * d;
         for (int b2 = 0; b2 < d; ++b2) num[b2] += w * vj[b2];
       }
       double* yt = yu + (size_t)h * Ld + (size_t)t * d;
@@ -379,6 +451,7 @@ static void run_unit(const oracle_job* J, int u) {
 
   free(K); free(V); free(Q); free(F); free(SB); free(zB); free(phi); free(phq);
   free(tmp); free(logit); free(num); free(lnum); free(selected); free(pool);
+  free(K8); free(V8);
 }
 
 static void* worker(void* p) {
@@ -403,6 +476,8 @@ static void* worker(void* p) {
  * log of the branch's weight sum. decay: null, or [n_units] forget factors
  * in (0, 1] of the linear state (key j weighted decay^(t - j) at query t;
  * the exported state holds decay^(R - j), R = the first position past it).
+ * fp8_from: queries at t >= fp8_from read the kept tokens below their
+ * window band as E4M3 codes times the row scale (e4m3_row); < 0: never.
  * Returns 0, or -1 on invalid sizes. */
 int still_oracle_run(int n_units, int L, int d, int G, int W, int C, int m, int t_max,
                      double eps, double scale, const float* q, const float* k,
@@ -410,7 +485,7 @@ int still_oracle_run(int n_units, int L, int d, int G, int W, int C, int m, int 
                      double* y, double* score, int32_t* sel, double* S, double* z,
                      double* pending, int32_t* n_pool, int merge, double* y_sa,
                      double* lse_sa, double* y_la, double* lse_la, int route,
-                     const float* ext, const double* decay) {
+                     const float* ext, const double* decay, int fp8_from) {
   if (n_units < 0 || L < 0 || d < 1 || G < 1 || W < 1 || C < 1 || m < W || t_max < 1)
     return -1;
   if (merge < MERGE_ONE || merge > MERGE_SOFTMAX_ONLY) return -1;
@@ -425,7 +500,7 @@ int still_oracle_run(int n_units, int L, int d, int G, int W, int C, int m, int 
   oracle_job J = {L, d, G, W, C, m, t_max, lam, L > 0 ? (L - 1) / C : 0, merge, route, ext,
                   eps, scale,
                   q, k, v, F, gate, y, score, S, z, pending, sel, n_pool,
-                  y_sa, lse_sa, y_la, lse_la, decay};
+                  y_sa, lse_sa, y_la, lse_la, decay, fp8_from};
   if (n_threads < 1) n_threads = 1;
   if (n_threads > n_units) n_threads = n_units > 0 ? n_units : 1;
   pthread_t th[256];

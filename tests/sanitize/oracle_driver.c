@@ -18,7 +18,7 @@ int still_oracle_run(int n_units, int L, int d, int G, int W, int C, int m, int 
                      double* y, double* score, int32_t* sel, double* S, double* z,
                      double* pending, int32_t* n_pool, int merge, double* y_sa,
                      double* lse_sa, double* y_la, double* lse_la, int route,
-                     const float* ext, const double* decay);
+                     const float* ext, const double* decay, int fp8_from);
 
 static void* rd(FILE* f, size_t n, size_t sz) {
   void* p = malloc(n * sz > 0 ? n * sz : 1);
@@ -63,7 +63,7 @@ int main(int argc, char** argv) {
     lla = calloc((size_t)U * G * L + 1, 8);
   }
   const int32_t rc = still_oracle_run(U, L, d, G, W, C, m, tm, es[0], es[1], q, k, v, F, g, nt, y, sc, sel,
-                                      S, z, pend, np, merge, ysa, lsa, yla, lla, route, ext, NULL);
+                                      S, z, pend, np, merge, ysa, lsa, yla, lla, route, ext, NULL, -1);
   FILE* fo = fopen(argv[2], "wb");
   if (!fo) return 2;
   fwrite(&rc, 4, 1, fo);

@@ -663,3 +663,105 @@ def test_decay_geometric_closed_form():
     R = bf.full_chunks_out_of_window(c_last, W, C) * C
     geo = sum(G64 ** (R - j) for j in range(R) if j not in kept)
     np.testing.assert_allclose(r["z"][0], geo * bf.np_map(k[0, 0, 0], F[0]), rtol=1e-12)
+
+
+# ---- the kept pool as an 8-bit store (OCP E4M3 codes, a float32 scale per row)
+
+def test_e4m3_code_points_of_the_format():
+    """Fixed points of the OCP E4M3 definition: the largest finite value 448
+    is code 0x7E, 1 is 0x38, the smallest normal 2^-6 is 0x08, the smallest
+    subnormal 2^-9 is 0x01; with a row maximum of 448 the scale is 1."""
+    row = np.array([448, 1, 2.0 ** -6, 2.0 ** -9, -448, -1, 0, 0.5], np.float32)
+    for codes, s in (rec.e4m3_rows(row[None])[:2], bf.e4m3_row(row)[:2]):
+        assert float(np.asarray(s).reshape(-1)[0]) == 1.0
+        assert list(np.asarray(codes).reshape(-1)) == [0x7E, 0x38, 0x08, 0x01, 0xFE, 0xB8, 0x00, 0x30]
+
+
+def test_e4m3_every_finite_value_round_trips():
+    """Every finite E4M3 magnitude (and its negative), in a row whose maximum
+    is 448 (scale 1), is stored exactly as its own code."""
+    table = bf.e4m3_values()
+    assert table[0] == 0 and table[-1] == 448 and np.all(np.diff(table) > 0)
+    row = np.concatenate([table, -table[1:]]).astype(np.float32)
+    codes, s, vals = rec.e4m3_rows(row[None])
+    assert s[0] == 1.0
+    np.testing.assert_array_equal(vals[0], row.astype(np.float64))
+    np.testing.assert_array_equal(codes[0][:127], np.arange(127))
+    np.testing.assert_array_equal(codes[0][127:], np.arange(1, 127) | 0x80)
+
+
+def test_e4m3_ties_go_to_the_even_code():
+    """Midpoints between neighbouring codes (scale 1) round to the even
+    code; just above a midpoint rounds up."""
+    table = bf.e4m3_values()
+    mids = (table[:-1] + table[1:]) / 2
+    row = np.concatenate([[448.0], mids]).astype(np.float32)
+    assert np.array_equal(row[1:].astype(np.float64), mids)  # midpoints are exact in float32
+    codes = rec.e4m3_rows(row[None])[0][0][1:]
+    want = np.where(np.arange(126) % 2 == 0, np.arange(126), np.arange(1, 127))
+    np.testing.assert_array_equal(codes, want)
+    up = np.nextafter(mids.astype(np.float32), np.float32(np.inf))
+    codes = rec.e4m3_rows(np.concatenate([[448.0], up]).astype(np.float32)[None])[0][0][1:]
+    np.testing.assert_array_equal(codes, np.arange(1, 127))
+
+
+def test_e4m3_rows_two_implementations_agree():
+    """The recurrent oracle's quantiser (arithmetic on the binade) and the
+    brute-force one (nearest entry of the code table) give the same codes,
+    scales and values on rows of every magnitude, zero rows included; the
+    relative error of a value is at most 2^-4 of the row maximum's scale
+    times 448 (half a step of the top binade)."""
+    rng = np.random.default_rng(11)
+    X = (rng.standard_normal((300, 64)) * np.exp(rng.uniform(-20, 12, (300, 1)))).astype(np.float32)
+    X[5] = 0
+    X[6, ::3] = 0
+    c, s, v = rec.e4m3_rows(X)
+    for i in range(len(X)):
+        cb, sb, vb = bf.e4m3_row(X[i])
+        assert np.array_equal(cb, c[i]) and sb == s[i] and np.array_equal(vb, v[i]), i
+    amax = np.abs(X).max(axis=1, keepdims=True)
+    assert np.all(np.abs(v - X) <= amax * 2.0 ** -4 + 1e-300)
+    assert s[5] == 1.0 and not c[5].any()
+
+
+FP8_CASES = [
+    # (B, Hq, Hkv, L, d, W, C, m, t_max, fp8_from)
+    (1, 2, 1, 60, 8, 4, 8, 4 + 2 * 7, 7, 30),
+    (2, 4, 2, 75, 16, 8, 8, 8 + 3 * 9, 9, 40),
+    (1, 1, 1, 50, 8, 12, 4, 12 + 1 * 12, 12, 20),
+]
+
+
+@pytest.mark.parametrize("case", FP8_CASES)
+def test_fp8_pool_recurrent_matches_brute_force(case):
+    """Both forms read the kept pool below the window band in E4M3 from
+    fp8_from on: they agree, the queries before fp8_from equal the plain
+    layer's exactly, the later ones differ from it (the 8-bit store is
+    read), and fp8_from past the end is the plain layer."""
+    B, Hq, Hkv, L, d, W, C, m, tm, f = case
+    rng = np.random.default_rng(sum(case) + 9)
+    q, k, v, F, g = rand_inputs(rng, B, Hq, Hkv, L, d, outliers=1)
+    kw = dict(window=W, chunk=C, budget=m, t_max=tm)
+    a = bf.prefill(q, k, v, F, g, fp8_from=f, **kw)
+    r = rec.prefill(q, k, v, F, g, fp8_from=f, **kw)
+    plain = rec.prefill(q, k, v, F, g, **kw)
+    G, U = Hq // Hkv, B * Hkv
+    np.testing.assert_allclose(r["y"], a["y"].reshape(U, G, L, d), rtol=1e-11, atol=1e-12)
+    np.testing.assert_array_equal(r["y"][:, :, :f], plain["y"][:, :, :f])
+    assert np.abs(r["y"][:, :, f:] - plain["y"][:, :, f:]).max() > 1e-4
+    for key in ("sel", "score", "S", "z"):
+        np.testing.assert_array_equal(r[key], plain[key])
+    late = rec.prefill(q, k, v, F, g, fp8_from=L, **kw)
+    np.testing.assert_array_equal(late["y"], plain["y"])
+
+
+def test_fp8_pool_leaves_the_band_exact():
+    """A kept token still inside a query's window band is read at full
+    precision: with the window covering the whole sequence (no kept token
+    ever lies below the band) the 8-bit store changes nothing."""
+    rng = np.random.default_rng(3)
+    L, d = 40, 8
+    q, k, v, F, g = rand_inputs(rng, 1, 2, 1, L, d)
+    kw = dict(window=L, chunk=8, budget=L + 10, t_max=5)
+    np.testing.assert_array_equal(rec.prefill(q, k, v, F, g, fp8_from=0, **kw)["y"],
+                                  rec.prefill(q, k, v, F, g, **kw)["y"])
