@@ -98,6 +98,20 @@ enum { STILL_DTYPE_F32 = 0, STILL_DTYPE_BF16 = 1 };
  * (budget - window rows) may span at most 256 pages. */
 #define STILL_FLAG_PAGED_POOL 16u
 #define STILL_POOL_PAGE_ROWS 16 /* kept tokens per page */
+/* 8-bit kept pool (the fp8 pool K/V of the pages' precision work; the
+ * format is a reading, the pages name none): the decode state stores each
+ * kept key and value row as OCP E4M3 codes of x_i / 2^e with one scale
+ * exponent per row (as the E8M0 scales of the OCP microscaling formats):
+ * e the smallest integer with amax_i |x_i| <= 448 * 2^e, at least -126, 0
+ * for a zero row; x_i / 2^e (exact) rounded to the nearest E4M3 value, ties
+ * to the even code, beyond 448 to 448. Region pool_k holds the
+ * (budget - window) rows of head_dim key codes, then one byte e + 127 per
+ * row; pool_v likewise. Decode steps read the kept tokens below the window
+ * band from this store (exactly: 2^e multiplies the logit, and the weight
+ * of the value); the band, the linear state and the prefill's own outputs
+ * keep the data's precision. bf16 data only, not with
+ * STILL_FLAG_PAGED_POOL (STILL_EUNSUPPORTED). */
+#define STILL_FLAG_POOL_FP8 32u
 /* Routing metric, flags bits 8..11 (STILL_FLAG_ROUTE(r)): the score that
  * ranks a chunk's tokens for the delayed Top-lambda. The default is the
  * Self-Saliency Score; the others are the alternatives of the STILL

@@ -25,6 +25,7 @@ struct Derived {
   float eps, scale;
   double eps64, scale64;
   bool paged;  // STILL_FLAG_PAGED_POOL: the pool rows live in the caller's pages
+  bool pool8;  // STILL_FLAG_POOL_FP8: pool rows as E4M3 codes, then a float32 scale per row
 };
 
 int derive(const still_params* p, Derived* d) {
@@ -32,7 +33,7 @@ int derive(const still_params* p, Derived* d) {
   if (p->abi_version != STILL_ABI_VERSION) return STILL_EINVAL;
   if (p->dtype != STILL_DTYPE_F32 && p->dtype != STILL_DTYPE_BF16) return STILL_EINVAL;
   if (p->flags & ~(STILL_FLAG_FP32_OUT | STILL_FLAG_SOFTMAX_ONLY | STILL_FLAG_MERGE_SUM |
-                   STILL_FLAG_PAGED_POOL | STILL_FLAG_ROUTE(15u)))
+                   STILL_FLAG_PAGED_POOL | STILL_FLAG_POOL_FP8 | STILL_FLAG_ROUTE(15u)))
     return STILL_EINVAL;  // unknown flag bits
   if (STILL_ROUTE_OF(p->flags) > STILL_ROUTE_EXTERNAL) return STILL_EINVAL;
   if ((p->flags & STILL_FLAG_SOFTMAX_ONLY) && (p->flags & STILL_FLAG_MERGE_SUM))
@@ -49,6 +50,10 @@ int derive(const still_params* p, Derived* d) {
     return STILL_EUNSUPPORTED;
   if (p->window > 256) return STILL_EUNSUPPORTED;
   if ((int64_t)p->budget - p->window > (1 << 20)) return STILL_EUNSUPPORTED;
+  // the 8-bit pool: 16-bit data, rows in the state
+  if ((p->flags & STILL_FLAG_POOL_FP8) &&
+      (p->dtype != STILL_DTYPE_BF16 || (p->flags & STILL_FLAG_PAGED_POOL)))
+    return STILL_EUNSUPPORTED;
   // the paged pool's table of a unit is staged in LDS (at most 256 pages)
   if ((p->flags & STILL_FLAG_PAGED_POOL) &&
       ((int64_t)p->budget - p->window + STILL_POOL_PAGE_ROWS - 1) / STILL_POOL_PAGE_ROWS > 256)
@@ -70,6 +75,7 @@ int derive(const still_params* p, Derived* d) {
   d->P = p->budget - p->window;
   d->esz = p->dtype == STILL_DTYPE_F32 ? 4 : 2;
   d->paged = (p->flags & STILL_FLAG_PAGED_POOL) != 0;
+  d->pool8 = (p->flags & STILL_FLAG_POOL_FP8) != 0;
   d->eps = p->eps > 0.f ? p->eps : 1e-6f;
   d->scale = p->sm_scale > 0.f ? p->sm_scale : 1.0f / sqrtf((float)p->head_dim);
   // float64 paths (score refinement, decode score): the default values are
@@ -89,8 +95,9 @@ void layout(const Derived& d, still_state_layout* s) {
   s->S = take((int64_t)d.D * d.D * 4);
   s->z = take((int64_t)d.D * 4);
   // with the paged pool the rows live in the caller's pages (empty regions)
-  s->pool_k = take(d.paged ? 0 : (int64_t)d.P * d.D * d.esz);
-  s->pool_v = take(d.paged ? 0 : (int64_t)d.P * d.D * d.esz);
+  const int64_t pool_bytes = d.paged ? 0 : d.pool8 ? (int64_t)d.P * (d.D + 1) : (int64_t)d.P * d.D * d.esz;
+  s->pool_k = take(pool_bytes);
+  s->pool_v = take(pool_bytes);
   s->pool_pos = take((int64_t)d.P * 4);
   s->ring_k = take((int64_t)d.R * d.D * d.esz);
   s->ring_v = take((int64_t)d.R * d.D * d.esz);
@@ -232,6 +239,9 @@ void set_decode_attr(int family) {
                             hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
   (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&still::decode_kernel<T, D, G, true>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+  if constexpr (sizeof(T) == 2)
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&still::decode_kernel<T, D, G, false, true>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
   g_attr_done[dev] |= 1ull << family;
 }
 
@@ -375,8 +385,14 @@ int launch_decode_g(const Derived& d, still::DecodeArgs a, hipStream_t s) {
   const size_t lds = paged ? DecLds<T, D, G>::bytes_paged(d.W) : DecLds<T, D, G>::bytes(d.W);
   if (lds > 160 * 1024) return STILL_EUNSUPPORTED;
   set_decode_attr<T, D, G>(decode_family<T, D, G>());
-  if (paged) decode_kernel<T, D, G, true><<<dim3(d.Hkv, d.B), dim3(DEC_THREADS), lds, s>>>(a);
-  else decode_kernel<T, D, G><<<dim3(d.Hkv, d.B), dim3(DEC_THREADS), lds, s>>>(a);
+  if (paged) {
+    decode_kernel<T, D, G, true><<<dim3(d.Hkv, d.B), dim3(DEC_THREADS), lds, s>>>(a);
+  } else if (a.pool8) {
+    if constexpr (sizeof(T) == 2) decode_kernel<T, D, G, false, true><<<dim3(d.Hkv, d.B), dim3(DEC_THREADS), lds, s>>>(a);
+    else return STILL_EUNSUPPORTED;
+  } else {
+    decode_kernel<T, D, G><<<dim3(d.Hkv, d.B), dim3(DEC_THREADS), lds, s>>>(a);
+  }
   return hipGetLastError() == hipSuccess ? STILL_OK : STILL_EHIP;
 }
 
@@ -651,6 +667,7 @@ static int prefill_impl(const still_params* p, int64_t seq_len, const void* q, c
   a.Gs = pl.Gs;
   a.fp32_out = (p->flags & STILL_FLAG_FP32_OUT) ? 1 : 0;
   a.softmax_only = softmax_only ? 1 : 0;
+  a.pool8 = d.pool8 ? 1 : 0;
   a.merge_sum = merge_sum ? 1 : 0;
   a.y_sa = parts.y_sa;
   a.lse_sa = parts.lse_sa;
@@ -863,6 +880,7 @@ static int decode_impl(const still_params* p, int64_t pos, const int32_t* row_po
   a.R = d.R;
   a.pos = row_pos;
   a.softmax_only = (p->flags & STILL_FLAG_SOFTMAX_ONLY) ? 1 : 0;
+  a.pool8 = d.pool8 ? 1 : 0;
   a.route = (int)STILL_ROUTE_OF(p->flags);
   a.fp32_out = (p->flags & STILL_FLAG_FP32_OUT) ? 1 : 0;
   a.scale = d.scale;

@@ -620,4 +620,75 @@ __device__ __host__ __forceinline__ int pool_count_at(int c, int lam, int cap_ch
   return (c < cap_chunks ? c : cap_chunks) * lam;
 }
 
+// ---- the kept pool as an 8-bit store: OCP E4M3 codes (sign, 4 exponent
+// bits with bias 7, 3 mantissa bits; exponent field 0 holds the multiples of
+// 2^-9 below 2^-6; 448 the largest finite value, code 0x7F a NaN) of x / 2^e
+// and one scale exponent byte e + 127 per row, e the smallest integer with
+// amax <= 448 * 2^e, at least -126 (0 for a zero row).
+
+// Code of y: the nearest E4M3 value, ties to the even code, magnitudes from
+// 448 up to 448. Works on the float's bit fields.
+__device__ __forceinline__ uint32_t e4m3_code(float y) {
+  const uint32_t bits = __float_as_uint(y), sign = (bits >> 24) & 0x80u;
+  const float a = __uint_as_float(bits & 0x7FFFFFFFu);
+  if (!(a < 448.f)) return sign | 0x7Eu;
+  if (a < 0.015625f) return sign | (uint32_t)rintf(a * 512.f);  // exact scaling, ties to even
+  const uint32_t ab = __float_as_uint(a);
+  int e = (int)(ab >> 23) - 127;  // -6 .. 8
+  uint32_t keep = (ab >> 20) & 7u;
+  const uint32_t rem = ab & 0xFFFFFu;
+  keep += (rem > 0x80000u || (rem == 0x80000u && (keep & 1u))) ? 1u : 0u;
+  if (keep == 8u) { keep = 0u; ++e; }
+  return sign | ((uint32_t)(e + 7) << 3) | keep;
+}
+
+// The scale exponent of a row whose largest magnitude is amax: with
+// amax = 1.f * 2^E and 448 = 1.75 * 2^8, e = E - 8, plus one if f > 0.75;
+// clamped to [-126, ..] (0 for a zero row).
+__device__ __forceinline__ int e4m3_row_exp(float amax) {
+  if (!(amax > 0.f)) return 0;
+  const uint32_t ab = __float_as_uint(amax);
+  const int e = (int)(ab >> 23) - 127 - 8 + ((ab & 0x7FFFFFu) > 0x600000u ? 1 : 0);
+  return e < -126 ? -126 : e;
+}
+// 2^k for k in [-126, 127] (a normal float32)
+__device__ __forceinline__ float pow2_int(int k) { return __uint_as_float((uint32_t)(k + 127) << 23); }
+
+// Largest value over NL consecutive lanes (NL a power of two dividing 64,
+// the group aligned to NL): every lane of the group gets it.
+template <int NL>
+__device__ __forceinline__ float group_max(float m) {
+#pragma unroll
+  for (int o = 1; o < NL; o <<= 1) m = fmaxf(m, __shfl_xor(m, o));
+  return m;
+}
+
+// Two E4M3 codes (bytes 0, 1 of c; with HI bytes 2, 3) as two bf16 values
+// packed in 32 bits: exact, every E4M3 value is a bf16 value (the float32
+// conversion leaves the low 16 bits zero).
+template <bool HI = false>
+__device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t c) {
+  typedef float f2_t __attribute__((ext_vector_type(2)));
+  const f2_t f = __builtin_amdgcn_cvt_pk_f32_fp8((int)c, HI);
+  return (__float_as_uint(f[0]) >> 16) | (__float_as_uint(f[1]) & 0xFFFF0000u);
+}
+
+// Eight E4M3 codes (bytes of w0, then of w1, element order) as a bf16 fragment.
+__device__ __forceinline__ Frag<bf16> e4m3x8_frag(uint32_t w0, uint32_t w1) {
+  const u32x4 r = {e4m3x2_to_bf16x2<false>(w0), e4m3x2_to_bf16x2<true>(w0), e4m3x2_to_bf16x2<false>(w1),
+                   e4m3x2_to_bf16x2<true>(w1)};
+  Frag<bf16> f;
+  f.v = __builtin_bit_cast(bf16x8, r);
+  return f;
+}
+// A fragment loaded raw: with codes, its first 8 bytes are E4M3 codes, made
+// 8 bf16 values; else it is returned as it is (Tag keeps this out of code
+// paths a template discards).
+template <typename T, typename Tag>
+__device__ __forceinline__ Frag<T> e4m3x8_or_raw(Tag, bool codes, const Frag<T>& f) {
+  static_assert(sizeof(T) == 2 && Tag::value, "8-bit rows: 16-bit data");
+  const u32x4 w = __builtin_bit_cast(u32x4, f.v);
+  return codes ? e4m3x8_frag(w[0], w[1]) : f;
+}
+
 }  // namespace still

@@ -49,6 +49,7 @@ struct DecodeArgs {
   // returns where pos[b] + t is not a chunk start
   const int32_t* pos;
   int softmax_only;  // the linear branch dropped (every gate taken as 0)
+  int pool8;         // pool rows as E4M3 codes, then a float32 scale per row
   int route;         // routing metric (ROUTE_*; not ROUTE_EXTERNAL)
   const void* out_gate;  // [B][Hq][D] T: channel-wise output gate before the sigmoid, or null
   const float* decay;    // [Hkv] forget factor of the linear state in (0, 1], or null (1)
@@ -481,6 +482,36 @@ __global__ __launch_bounds__(BND_THREADS) void decode_boundary_kernel(DecodeArgs
       const long ov = pool_page_off(a.pages, unit, row, 1, D * sizeof(T));
       *reinterpret_cast<uint2*>(a.pages.base + ok + part * VEC * sizeof(T)) = ld8(ring_k + src);
       *reinterpret_cast<uint2*>(a.pages.base + ov + part * VEC * sizeof(T)) = ld8(ring_v + src);
+    } else if (sizeof(T) == 2 && a.pool8) {
+      // the 8-bit store: the row's LPK lanes (consecutive, aligned) share
+      // its largest magnitude; codes of x / 2^e, the exponent bytes after
+      // the P rows
+      const uint2 kw = ld8(ring_k + src), vw = ld8(ring_v + src);
+      const T* kt = reinterpret_cast<const T*>(&kw);
+      const T* vt = reinterpret_cast<const T*>(&vw);
+      float km = 0.f, vm = 0.f;
+#pragma unroll
+      for (int e2 = 0; e2 < VEC; ++e2) {
+        km = fmaxf(km, fabsf(to_f32(kt[e2])));
+        vm = fmaxf(vm, fabsf(to_f32(vt[e2])));
+      }
+      const int ek = e4m3_row_exp(group_max<LPK>(km)), ev = e4m3_row_exp(group_max<LPK>(vm));
+      const float rk = pow2_int(-ek), rv = pow2_int(-ev);  // x / 2^e, exact
+      uint32_t kc = 0u, vc = 0u;
+#pragma unroll
+      for (int e2 = 0; e2 < VEC; ++e2) {
+        kc |= e4m3_code(to_f32(kt[e2]) * rk) << (8 * e2);
+        vc |= e4m3_code(to_f32(vt[e2]) * rv) << (8 * e2);
+      }
+      uint8_t* k8 = reinterpret_cast<uint8_t*>(st + a.st_pool_k);
+      uint8_t* v8 = reinterpret_cast<uint8_t*>(st + a.st_pool_v);
+      static_assert(sizeof(T) != 2 || VEC == 4, "four codes per lane");
+      *reinterpret_cast<uint32_t*>(k8 + dst) = kc;
+      *reinterpret_cast<uint32_t*>(v8 + dst) = vc;
+      if (part == 0) {
+        k8[(size_t)(a.m - W) * D + row] = (uint8_t)(ek + 127);
+        v8[(size_t)(a.m - W) * D + row] = (uint8_t)(ev + 127);
+      }
     } else {
       *reinterpret_cast<uint2*>(pool_k + dst) = ld8(ring_k + src);
       *reinterpret_cast<uint2*>(pool_v + dst) = ld8(ring_v + src);
@@ -562,9 +593,10 @@ __global__ __launch_bounds__(BND_THREADS) void decode_boundary_kernel(DecodeArgs
   __syncthreads();
 }
 
-template <typename T, int D, int G, bool PAGED = false>
+template <typename T, int D, int G, bool PAGED = false, bool P8 = false>
 __global__ __launch_bounds__(DEC_THREADS) __attribute__((amdgpu_waves_per_eu(2)))
 void decode_kernel(DecodeArgs a) {
+  static_assert(!P8 || (sizeof(T) == 2 && !PAGED), "8-bit pool: 16-bit data in the state");
   using LD = DecLds<T, D, G>;
   constexpr int VEC = RowVec<T>::N;  // elements per 8-byte vector
   constexpr int LPK = D / VEC;       // lanes per K/V row
@@ -784,6 +816,7 @@ void decode_kernel(DecodeArgs a) {
   struct TileRegs0 {
     Frag<T> af[D / 32];
     uint32_t vw[NVW];
+    uint32_t sc[P8 ? 2 : 1];  // 8-bit pool: scale exponent bytes (+127) of keys 4g + i, keys then values
   };
   TileRegs0 TA0;
 
@@ -833,7 +866,10 @@ void decode_kernel(DecodeArgs a) {
   // key rows: flat loads (a tile may span the pool and the ring); value
   // columns: buffer loads with the row in the scalar offset, so the 16 rows
   // of a tile need no per-row address registers
-  auto load_tile = [&](TileRegs& X, int kk0, int n, auto krow, auto vrow) {
+  // p8: std::true_type where the first n_oob keys are the kept pool's
+  // 8-bit store (the softmax walk with P8), else std::false_type
+  auto load_tile = [&](TileRegs& X, int kk0, int n, auto krow, auto vrow, auto p8) {
+    constexpr bool Q8 = decltype(p8)::value;
     if constexpr (PAGED) {
       // rows in the state blob or, offsets tagged with bit 31, in the
       // arena's pages: loads through addresses; absent rows read a row that
@@ -878,6 +914,38 @@ void decode_kernel(DecodeArgs a) {
     // absent rows read at the end of the blob, past the range: zeros
     const uint32_t oob = (uint32_t)a.st_unit;
     const int kr_ = kk0 + r16;
+    if constexpr (Q8) {
+      // keys below n_oob: E4M3 codes (converted exactly to bf16) and row
+      // scales; the rest: bf16 rows of the ring. One load per lane from its
+      // row's store, of the same width (a code load reads 8 bytes past the
+      // lane's 8 codes, inside the blob or past its range)
+      const uint32_t P = (uint32_t)(a.m - a.W);
+      const bool in8 = kr_ < n_oob;
+      const uint32_t koff = in8 ? (uint32_t)a.st_pool_k + (uint32_t)kr_ * D + 8 * g4
+                                : (kr_ < n ? krow(kr_) : oob) + 8 * g4 * sizeof(T);
+#pragma unroll
+      for (int kb = 0; kb < D / 32; ++kb)  // raw: converted where the tile is used
+        X.af[kb] = ld_frag_buf<T>(st_r, koff + (in8 ? 32 : 64) * kb, 0);
+      const int ks = kk0 + 4 * g4;  // the lane's keys ks .. ks + 3: 4 exponent bytes
+      const uint32_t eko = ks < n_oob ? (uint32_t)a.st_pool_k + P * D + (uint32_t)ks : oob;
+      const uint32_t evo = ks < n_oob ? (uint32_t)a.st_pool_v + P * D + (uint32_t)ks : oob;
+      X.sc[0] = __builtin_amdgcn_raw_buffer_load_b32(st_r, eko, 0, 0);
+      X.sc[1] = __builtin_amdgcn_raw_buffer_load_b32(st_r, evo, 0, 0);
+      // values: dims 32 blk + 2 r, + 1 of key ks + i; an 8-bit row's two
+      // codes sit in the aligned 4 bytes at 32 blk + 4 (r / 2), half r % 2
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int kk = ks + i;
+        const bool v8 = kk < n_oob;
+        const uint32_t roff = v8 ? (uint32_t)a.st_pool_v + (uint32_t)kk * D + 4 * (r16 >> 1)
+                                 : (kk < n ? vrow(kk) : oob) + 2 * r16 * sizeof(T);
+#pragma unroll
+        for (int blk = 0; blk < D / 32; ++blk) {
+          X.vw[i * (D / 32) + blk] = __builtin_amdgcn_raw_buffer_load_b32(st_r, roff + (v8 ? 32 : 64) * blk, 0, 0);
+        }
+      }
+      return;
+    }
     const uint32_t koff = (kr_ < n ? krow(kr_) : oob) + 8 * g4 * sizeof(T);
 #pragma unroll
     for (int kb = 0; kb < D / 32; ++kb) X.af[kb] = ld_frag_buf<T>(st_r, koff, 32 * kb * sizeof(T));
@@ -905,7 +973,8 @@ void decode_kernel(DecodeArgs a) {
   };
   // one tile: weight(c, kk) turns a product into a log-weight
   auto tile = [&](const TileRegs& X, int kk0, int n, const Frag<T>* qb, const Frag<T>* qb2,
-                  auto weight, int sc_first) {
+                  auto weight, int sc_first, auto p8) {
+    constexpr bool Q8 = decltype(p8)::value;
     if (kk0 + 16 > sc_first) {  // wave-uniform: score-window keys in the tile
       // float64 logits of the new token's score: the products of bf16/f32
       // values are exact in float64; lane (r, g) sums its 8 columns per
@@ -928,12 +997,23 @@ void decode_kernel(DecodeArgs a) {
       }
     }
     f32x4 c = {0.f, 0.f, 0.f, 0.f};
+    // 8-bit pool: the lane's key row kk0 + r below n_oob holds codes (the
+    // first 8 bytes of its load), converted here, where the tile is used
+    const bool k8 = Q8 && kk0 + r16 < n_oob;
 #pragma unroll
     for (int kb = 0; kb < D / 32; ++kb) {
-      mma(c, X.af[kb], qb[kb]);
-      if (qb2) mma(c, X.af[kb], qb2[kb]);
+      Frag<T> af = X.af[kb];
+      if constexpr (Q8) af = e4m3x8_or_raw<T>(p8, k8, af);
+      mma(c, af, qb[kb]);
+      if (qb2) mma(c, af, qb2[kb]);
     }
-    // c[i] = <key kk0 + 4g + i, query-side column r>
+    // c[i] = <key kk0 + 4g + i, query-side column r>; an 8-bit key's
+    // product times its row scale (1 for the others)
+    if constexpr (Q8) {  // scale 2^(byte - 127); the ring's keys 1
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        c[i] *= kk0 + 4 * g4 + i < n_oob ? __uint_as_float(((X.sc[0] >> (8 * i)) & 255u) << 23) : 1.f;
+    }
     float mx = STILL_NEG_INF;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -974,6 +1054,12 @@ void decode_kernel(DecodeArgs a) {
             for (int i = 0; i < 4; ++i) accm[blk][par][i] *= ar[i];
         wave_sync();  // the slot is written again by the next tile
       }
+      // an 8-bit value row's scale goes into its weight (after the sum l)
+      if constexpr (Q8) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          c[i] *= kk0 + 4 * g4 + i < n_oob ? __uint_as_float(((X.sc[1] >> (8 * i)) & 255u) << 23) : 1.f;
+      }
       // weights as bf16 hi (the top 16 bits) + lo (the remainder's top 16
       // bits): ~16 significant bits; A operand: row = head r, keys 4g + i
       typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -986,8 +1072,15 @@ void decode_kernel(DecodeArgs a) {
       }
 #pragma unroll
       for (int blk = 0; blk < D / 32; ++blk) {
-        const uint32_t w0 = X.vw[blk], w1 = X.vw[(D / 32) + blk];
-        const uint32_t w2 = X.vw[2 * (D / 32) + blk], w3 = X.vw[3 * (D / 32) + blk];
+        uint32_t w0 = X.vw[blk], w1 = X.vw[(D / 32) + blk];
+        uint32_t w2 = X.vw[2 * (D / 32) + blk], w3 = X.vw[3 * (D / 32) + blk];
+        if constexpr (Q8) {  // an 8-bit row's two codes: half r % 2 of its aligned 4 bytes
+          const int k0 = kk0 + 4 * g4, sh = 16 * (r16 & 1);
+          w0 = k0 < n_oob ? e4m3x2_to_bf16x2(w0 >> sh) : w0;
+          w1 = k0 + 1 < n_oob ? e4m3x2_to_bf16x2(w1 >> sh) : w1;
+          w2 = k0 + 2 < n_oob ? e4m3x2_to_bf16x2(w2 >> sh) : w2;
+          w3 = k0 + 3 < n_oob ? e4m3x2_to_bf16x2(w3 >> sh) : w3;
+        }
 #pragma unroll
         for (int par = 0; par < 2; ++par) {
           // keys 0..3 of the lane's group at dim 32 blk + 2 r + par
@@ -1033,19 +1126,19 @@ void decode_kernel(DecodeArgs a) {
   };
   // the tiles of wave w: w, w + waves, ...; two in flight
   auto run_tiles = [&](TileRegs& A, TileRegs& B, bool a_loaded, int n, auto krow, auto vrow,
-                       const Frag<T>* qb, const Frag<T>* qb2, auto weight, int sc_first) {
+                       const Frag<T>* qb, const Frag<T>* qb2, auto weight, int sc_first, auto p8) {
     constexpr int STEP = 16 * DEC_WAVES;
     const int first = 16 * wave;
     // loads are issued whether or not their tile exists (absent rows read
     // zeros past the range): a load on one side of a branch only would make
     // the next wait one for every load in flight
-    if (!a_loaded) load_tile(A, first, n, krow, vrow);
+    if (!a_loaded) load_tile(A, first, n, krow, vrow, p8);
     for (int kk0 = first; kk0 < n; kk0 += 2 * STEP) {  // wave-uniform
-      load_tile(B, kk0 + STEP, n, krow, vrow);
-      tile(A, kk0, n, qb, qb2, weight, sc_first);
+      load_tile(B, kk0 + STEP, n, krow, vrow, p8);
+      tile(A, kk0, n, qb, qb2, weight, sc_first, p8);
       if (kk0 + STEP >= n) break;
-      load_tile(A, kk0 + 2 * STEP, n, krow, vrow);
-      tile(B, kk0 + STEP, n, qb, qb2, weight, sc_first);
+      load_tile(A, kk0 + 2 * STEP, n, krow, vrow, p8);
+      tile(B, kk0 + STEP, n, qb, qb2, weight, sc_first, p8);
     }
   };
   // ---- 3b. NP-Map phi(q_h), phi(k_t), with the wave's state rows and its
@@ -1069,7 +1162,8 @@ void decode_kernel(DecodeArgs a) {
         srow[j][jj] = __builtin_amdgcn_raw_buffer_load_b32(st_r, lane * 4, soff, 0);
       }
     }
-  load_tile(TA, 16 * wave, n_sa, krow_sa, vrow_sa);
+  using SaP8 = std::integral_constant<bool, P8>;  // the softmax walk reads the 8-bit pool
+  load_tile(TA, 16 * wave, n_sa, krow_sa, vrow_sa, SaP8{});
 
   np_map_vec<T, D, G + 1, DEC_THREADS>(frows, xs, red8, us, ph, rowst);
   for (int e = tid; e < G * D; e += DEC_THREADS) phq[e] = ph[e];
@@ -1117,7 +1211,7 @@ void decode_kernel(DecodeArgs a) {
   auto vrow_la = [&](int kk) -> uint32_t { return rv_off + (uint32_t)wrap(la_slot + kk) * (D * sizeof(T)); };
   constexpr bool LA_EARLY = G <= 4;
   TileRegs TC;
-  if constexpr (LA_EARLY) load_tile(TC, 16 * wave, n_la, krow_la, vrow_la);
+  if constexpr (LA_EARLY) load_tile(TC, 16 * wave, n_la, krow_la, vrow_la, std::false_type{});
   {
     Frag<T> qb[D / 32];
 #pragma unroll
@@ -1125,7 +1219,7 @@ void decode_kernel(DecodeArgs a) {
     const float scale = a.scale;
     const int n_sc = t - sc_lo + 1;  // the score window: the last n_sc keys
     run_tiles(TA, TB, true, n_sa, krow_sa, vrow_sa, qb, (const Frag<T>*)nullptr,
-              [&](float x, int) { return x * scale; }, n_sa - n_sc);
+              [&](float x, int) { return x * scale; }, n_sa - n_sc, SaP8{});
   }
 
   // ---- 3e. linear keys: log-weight log(g) + log <phi(q), phi(k)> --------
@@ -1145,7 +1239,7 @@ void decode_kernel(DecodeArgs a) {
       return (la && w > 0.f) ? lgate + __logf(w) + (float)(t - la_lo - kk) * lng : STILL_NEG_INF;
     };
     run_tiles(LA_EARLY ? TC : TA, TB, LA_EARLY, n_la, krow_la, vrow_la, pb,
-              sizeof(T) == 2 ? pb2 : (const Frag<T>*)nullptr, weight, INT_MAX);
+              sizeof(T) == 2 ? pb2 : (const Frag<T>*)nullptr, weight, INT_MAX, std::false_type{});
   }
   // publish per wave: (m, l) per head from lanes r = h, the value slices
   if constexpr (PV_MFMA) {

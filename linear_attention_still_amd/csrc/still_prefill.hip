@@ -49,6 +49,7 @@ struct PrefillArgs {
   int B, Hq, Hkv, G, L, W, C, m, T, n_dec, lam, cap_chunks, K, NS, nHG, Gs, fp32_out;
   int score_out;  // the caller asked for the scores (score is theirs)
   int softmax_only, merge_sum;  // branch variants (linear branch dropped / sum merge)
+  int pool8;                    // the decode state's pool rows as E4M3 codes + row scales
   float* y_sa;    // [B][Hq][L][D] softmax-branch output, or null (separate walk)
   float* lse_sa;  // [B][Hq][L] natural log of its normaliser, or null
   float* y_la;    // [B][Hq][L][D] linear-branch output (no gate), or null
@@ -2799,6 +2800,42 @@ __device__ void export_part(const PrefillArgs& a, int x) {
             *reinterpret_cast<const uint4*>(kg + (size_t)q * D + c);
         *reinterpret_cast<uint4*>(a.pages.base + ov + c * sizeof(T)) =
             *reinterpret_cast<const uint4*>(vg + (size_t)q * D + c);
+      }
+    } else if (sizeof(T) == 2 && a.pool8) {
+      // the 8-bit store: the row's CPR lanes (consecutive, aligned) share
+      // its largest magnitude; codes of x / 2^e, the exponent bytes after
+      // the P rows
+      const int P = a.m - a.W;
+      const T* kr = kg + (size_t)q * D + c;
+      const T* vr = vg + (size_t)q * D + c;
+      float km = 0.f, vm = 0.f;
+#pragma unroll
+      for (int j = 0; j < VEC; ++j) {
+        km = fmaxf(km, fabsf(to_f32(kr[j])));
+        vm = fmaxf(vm, fabsf(to_f32(vr[j])));
+      }
+      const int ek = e4m3_row_exp(group_max<CPR>(km)), ev = e4m3_row_exp(group_max<CPR>(vm));
+      const float rk = pow2_int(-ek), rv = pow2_int(-ev);  // x / 2^e, exact
+      uint32_t kc[VEC / 4], vc[VEC / 4];
+#pragma unroll
+      for (int j = 0; j < VEC / 4; ++j) {
+        kc[j] = vc[j] = 0u;
+#pragma unroll
+        for (int e2 = 0; e2 < 4; ++e2) {
+          kc[j] |= e4m3_code(to_f32(kr[4 * j + e2]) * rk) << (8 * e2);
+          vc[j] |= e4m3_code(to_f32(vr[4 * j + e2]) * rv) << (8 * e2);
+        }
+      }
+      uint8_t* k8 = reinterpret_cast<uint8_t*>(st + a.st_pool_k);
+      uint8_t* v8 = reinterpret_cast<uint8_t*>(st + a.st_pool_v);
+#pragma unroll
+      for (int j = 0; j < VEC / 4; ++j) {
+        *reinterpret_cast<uint32_t*>(k8 + (size_t)i * D + c + 4 * j) = kc[j];
+        *reinterpret_cast<uint32_t*>(v8 + (size_t)i * D + c + 4 * j) = vc[j];
+      }
+      if (c == 0) {
+        k8[(size_t)P * D + i] = (uint8_t)(ek + 127);
+        v8[(size_t)P * D + i] = (uint8_t)(ev + 127);
       }
     } else {
       *reinterpret_cast<uint4*>(pk + (size_t)i * D + c) = *reinterpret_cast<const uint4*>(kg + (size_t)q * D + c);

@@ -24,6 +24,7 @@ STILL_FLAG_FP32_OUT = 1
 STILL_FLAG_SOFTMAX_ONLY = 2
 STILL_FLAG_MERGE_SUM = 4
 STILL_FLAG_PAGED_POOL = 16
+STILL_FLAG_POOL_FP8 = 32
 STILL_POOL_PAGE_ROWS = 16
 # routing metrics (flags bits 8..11)
 ROUTES = {"saliency": 0, "diag": 1, "qk": 2, "keynorm": 3, "uniform": 4, "external": 5}
@@ -429,14 +430,22 @@ def state_views(p: still_params, state: torch.Tensor) -> dict:
 
     def sec(off, n, dt, size):
         return blob[:, off:off + n * size].contiguous().view(dt).view(U, n)
-    return {
+    if p.flags & STILL_FLAG_POOL_FP8:  # E4M3 codes, then one exponent byte (+127) per row
+        extra = {"pool_k8": sec(lay.pool_k, P * d, torch.uint8, 1).view(U, P, d),
+                 "pool_k_exp": sec(lay.pool_k + P * d, P, torch.uint8, 1),
+                 "pool_v8": sec(lay.pool_v, P * d, torch.uint8, 1).view(U, P, d),
+                 "pool_v_exp": sec(lay.pool_v + P * d, P, torch.uint8, 1)}
+        edt_pool = None
+    else:
+        extra, edt_pool = {}, edt
+    return {**extra,
         "S": sec(lay.S, d * d, torch.float32, 4).view(U, d, d),
         "z": sec(lay.z, d, torch.float32, 4),
         # (a paged pool keeps its rows in the caller's pages: empty here)
-        "pool_k": sec(lay.pool_k, P * d, edt, es).view(U, P, d) if not p.flags & STILL_FLAG_PAGED_POOL
-        else None,
-        "pool_v": sec(lay.pool_v, P * d, edt, es).view(U, P, d) if not p.flags & STILL_FLAG_PAGED_POOL
-        else None,
+        "pool_k": sec(lay.pool_k, P * d, edt, es).view(U, P, d)
+        if edt_pool is not None and not p.flags & STILL_FLAG_PAGED_POOL else None,
+        "pool_v": sec(lay.pool_v, P * d, edt, es).view(U, P, d)
+        if edt_pool is not None and not p.flags & STILL_FLAG_PAGED_POOL else None,
         "pool_pos": sec(lay.pool_pos, P, torch.int32, 4),
         "ring_k": sec(lay.ring_k, R * d, edt, es).view(U, R, d),
         "ring_v": sec(lay.ring_v, R * d, edt, es).view(U, R, d),

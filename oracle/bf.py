@@ -281,16 +281,25 @@ def e4m3_values() -> np.ndarray:
     return np.array(out)
 
 
-def e4m3_row(x) -> Tuple[np.ndarray, np.float32, np.ndarray]:
+def e4m3_row(x) -> Tuple[np.ndarray, int, np.ndarray]:
     """One row as the kept pool's 8-bit store (reading: the pages name an
-    fp8 pool, not its format): scale s = amax / 448 in float32 (1 for a zero
-    row), each x_i / s (float32) to the nearest E4M3 value, ties to the even
-    code, beyond 448 to 448. Returns codes (uint8), s, and the values
-    code * s (float64). Nearest-value search over the code table."""
-    x = np.asarray(x, dtype=np.float32)
-    amax = np.float32(np.max(np.abs(x))) if x.size else np.float32(0)
-    s = np.float32(amax / np.float32(448)) if amax > 0 else np.float32(1)
-    y = (x / s).astype(np.float32).astype(np.float64)
+    fp8 pool, not its format): a power-of-two scale 2^e (an E8M0 exponent as
+    in the OCP microscaling formats), e the smallest integer with
+    max |x_i| <= 448 2^e (0 for a zero row), at least -126; each x_i / 2^e to
+    the nearest E4M3 value, ties to the even code, beyond 448 to 448.
+    Returns codes (uint8), e, and the values code 2^e (float64). The
+    exponent by search, the code by the nearest entry of the code table."""
+    x = np.asarray(x, dtype=np.float32).astype(np.float64)
+    amax = float(np.max(np.abs(x))) if x.size else 0.0
+    e = 0
+    if amax > 0:
+        e = math.floor(math.log2(amax)) - 9
+        while amax > 448 * 2.0 ** e:
+            e += 1
+        while e > -126 and amax <= 448 * 2.0 ** (e - 1):
+            e -= 1
+        e = max(e, -126)
+    y = x / 2.0 ** e
     table = e4m3_values()
     a = np.abs(y)
     hi = np.clip(np.searchsorted(table, a), 1, 126)  # table[hi - 1] <= a <= table[hi] inside
@@ -299,8 +308,8 @@ def e4m3_row(x) -> Tuple[np.ndarray, np.float32, np.ndarray]:
     pick = np.where(dlo < dhi, lo, np.where(dhi < dlo, hi, np.where(lo % 2 == 0, lo, hi)))
     pick = np.where(a >= 448, 126, pick)
     codes = (pick | np.where(y < 0, 0x80, 0)).astype(np.uint8)
-    vals = table[pick] * np.where(y < 0, -1.0, 1.0) * float(s)
-    return codes, s, vals
+    vals = table[pick] * np.where(y < 0, -1.0, 1.0) * 2.0 ** e
+    return codes, e, vals
 
 
 def output_gate(y, gate_out) -> np.ndarray:

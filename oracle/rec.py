@@ -124,7 +124,8 @@ def run_units(qs, ks, vs, Fs, gs, *, window: int, chunk: int, budget: int, t_max
     [U, L]: the caller's scores for route "external"; decay [U]: the
     units' forget factors of the linear state (float32 values), or None;
     fp8_from: queries from this position on read the kept tokens below
-    their window band in E4M3 (e4m3_rows), -1: never."""
+    their window band in E4M3 with power-of-two row scales (e4m3_rows),
+    -1: never."""
     qs, ks, vs, Fs, gs = (_f32(a) for a in (qs, ks, vs, Fs, gs))
     if route == "external":
         if ext is None:
@@ -170,14 +171,14 @@ def run_units(qs, ks, vs, Fs, gs, *, window: int, chunk: int, budget: int, t_max
 
 def e4m3_rows(x) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
     """Rows x [n, d] (float32) as the kept pool's 8-bit store: E4M3 codes
-    [n, d] uint8, float32 scales [n] and the values they stand for [n, d]
-    (float64). See e4m3_row in still_oracle.c."""
+    [n, d] uint8, scale exponents [n] (int32, scale 2^e) and the values they
+    stand for [n, d] (float64). See e4m3_row in still_oracle.c."""
     x = _f32(x)
     n, d = x.shape
     codes = np.zeros((n, d), np.uint8)
-    scales = np.zeros((n,), np.float32)
+    exps = np.zeros((n,), np.int32)
     values = np.zeros((n, d))
     ptr = lambda a: a.ctypes.data_as(ctypes.c_void_p)
-    if _load().still_oracle_e4m3_rows(n, d, ptr(x), ptr(codes), ptr(scales), ptr(values)) != 0:
+    if _load().still_oracle_e4m3_rows(n, d, ptr(x), ptr(codes), ptr(exps), ptr(values)) != 0:
         raise ValueError("still_oracle_e4m3_rows rejected its arguments")
-    return codes, scales, values
+    return codes, exps, values

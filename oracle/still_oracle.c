@@ -167,11 +167,11 @@ static int full_chunks_out_of_window(int c, int W, int C) {
  * (e, m) with e > 0 is 2^(e-7) (1 + m/8), e = 0 is 2^-6 m/8; the largest
  * finite value is 448 (e = 15, m = 6), e = 15, m = 7 is NaN. Reading for
  * the kept pool's storage (the pages name fp8 pools, not a format): a row
- * x of d values is stored as codes of x_i / s and the float32 scale
- * s = amax / 448 (amax = max |x_i|; s = 1 for a zero row), each x_i / s
- * rounded to the nearest E4M3 value, ties to the even code, magnitudes
- * beyond 448 to 448. The divisions are float32 operations, so the codes are
- * the same wherever float32 division is correctly rounded. */
+ * x of d values is stored as the codes of x_i / s with a power-of-two scale
+ * s = 2^e (an E8M0 exponent, as in the OCP microscaling formats), e the
+ * smallest integer with amax <= 448 s (amax = max |x_i|; e = 0 for a zero
+ * row), at least -126; each x_i / s (exact) rounded to the nearest E4M3
+ * value, ties to the even code, magnitudes beyond 448 to 448. */
 static uint8_t e4m3_code(float y) {
   const uint8_t sign = y < 0.0f ? 0x80 : 0x00;
   const float a = fabsf(y);
@@ -193,23 +193,31 @@ static double e4m3_value(uint8_t c) {
   return (c & 0x80) ? -v : v;
 }
 
-/* One row: codes and the scale, and the values they stand for. */
-static float e4m3_row(const float* x, int d, uint8_t* codes) {
+/* One row: codes and the scale exponent e (s = 2^e). */
+static int e4m3_row(const float* x, int d, uint8_t* codes) {
   float amax = 0.0f;
   for (int i = 0; i < d; ++i) amax = fabsf(x[i]) > amax ? fabsf(x[i]) : amax;
-  const float s = amax > 0.0f ? amax / 448.0f : 1.0f;
-  for (int i = 0; i < d; ++i) codes[i] = e4m3_code(x[i] / s);
-  return s;
+  int e = 0;
+  if (amax > 0.0f) {
+    int E;
+    const float f = frexpf(amax, &E); /* amax = f 2^E, 448 = 0.875 2^9 */
+    e = E - 9 + (f > 0.875f ? 1 : 0);
+    if (e < -126) e = -126;
+  }
+  for (int i = 0; i < d; ++i) codes[i] = e4m3_code(ldexpf(x[i], -e));
+  return e;
 }
 
-int still_oracle_e4m3_rows(int n, int d, const float* x, uint8_t* codes, float* scales,
+/* Rows x [n, d]: codes [n, d], scale exponents [n] (s = 2^e) and, if not
+ * null, the values code * s [n, d]. */
+int still_oracle_e4m3_rows(int n, int d, const float* x, uint8_t* codes, int32_t* exps,
                            double* values) {
   if (n < 0 || d < 1) return -1;
   for (int r = 0; r < n; ++r) {
-    const float s = e4m3_row(x + (size_t)r * d, d, codes + (size_t)r * d);
-    if (scales) scales[r] = s;
+    const int e = e4m3_row(x + (size_t)r * d, d, codes + (size_t)r * d);
+    if (exps) exps[r] = e;
     if (values)
-      for (int i = 0; i < d; ++i) values[(size_t)r * d + i] = e4m3_value(codes[(size_t)r * d + i]) * (double)s;
+      for (int i = 0; i < d; ++i) values[(size_t)r * d + i] = ldexp(e4m3_value(codes[(size_t)r * d + i]), e);
   }
   return 0;
 }
@@ -245,10 +253,10 @@ static void run_unit(const oracle_job* J, int u) {
     K8 = malloc(sizeof(double) * Ld);
     V8 = malloc(sizeof(double) * Ld);
     for (int j = 0; j < L; ++j) {
-      const float sk = e4m3_row(ks + (size_t)j * d, d, codes);
-      for (int i = 0; i < d; ++i) K8[(size_t)j * d + i] = e4m3_value(codes[i]) * (double)sk;
-      const float sv = e4m3_row(vs + (size_t)j * d, d, codes);
-      for (int i = 0; i < d; ++i) V8[(size_t)j * d + i] = e4m3_value(codes[i]) * (double)sv;
+      const int ek = e4m3_row(ks + (size_t)j * d, d, codes);
+      for (int i = 0; i < d; ++i) K8[(size_t)j * d + i] = ldexp(e4m3_value(codes[i]), ek);
+      const int ev = e4m3_row(vs + (size_t)j * d, d, codes);
+      for (int i = 0; i < d; ++i) V8[(size_t)j * d + i] = ldexp(e4m3_value(codes[i]), ev);
     }
     free(codes);
   }
@@ -477,7 +485,8 @@ static void* worker(void* p) {
  * in (0, 1] of the linear state (key j weighted decay^(t - j) at query t;
  * the exported state holds decay^(R - j), R = the first position past it).
  * fp8_from: queries at t >= fp8_from read the kept tokens below their
- * window band as E4M3 codes times the row scale (e4m3_row); < 0: never.
+ * window band as E4M3 codes times the row's power-of-two scale (e4m3_row);
+ * < 0: never.
  * Returns 0, or -1 on invalid sizes. */
 int still_oracle_run(int n_units, int L, int d, int G, int W, int C, int m, int t_max,
                      double eps, double scale, const float* q, const float* k,

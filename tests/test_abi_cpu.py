@@ -352,3 +352,22 @@ def test_pool_rows_counts_lambda_rows_per_decided_chunk():
         assert still.still_pool_rows(p, n) == lam * min(n_dec, cap), n
     with pytest.raises(still.StillError):
         still.still_pool_rows(p, -1)
+
+
+def test_pool_fp8_params_and_layout():
+    """The 8-bit pool takes bf16 data and an unpaged pool; its pool regions
+    hold (budget - window) rows of head_dim codes plus one exponent byte
+    per row."""
+    wl = WORKLOADS["decode_bf16_B64_ctx16K"]
+    plain = still.params_for(wl)
+    p8 = still.params_for(wl, flags=still.STILL_FLAG_POOL_FP8)
+    P, d = wl.budget - wl.window, wl.head_dim
+    lay, lay0 = still.still_state_layout_get(p8), still.still_state_layout_get(plain)
+    assert lay.pool_v - lay.pool_k >= P * (d + 1) and lay.pool_v - lay.pool_k < P * (d + 1) + 256
+    assert lay0.pool_v - lay0.pool_k >= P * d * 2
+    assert still.still_state_bytes(p8) < still.still_state_bytes(plain)
+    with pytest.raises(still.StillError):
+        still.still_state_bytes(still.params_for(WORKLOADS["small_f32_L256"], flags=still.STILL_FLAG_POOL_FP8))
+    with pytest.raises(still.StillError):
+        still.still_state_bytes(still.params_for(
+            wl, flags=still.STILL_FLAG_POOL_FP8 | still.STILL_FLAG_PAGED_POOL))

@@ -670,11 +670,15 @@ def test_decay_geometric_closed_form():
 def test_e4m3_code_points_of_the_format():
     """Fixed points of the OCP E4M3 definition: the largest finite value 448
     is code 0x7E, 1 is 0x38, the smallest normal 2^-6 is 0x08, the smallest
-    subnormal 2^-9 is 0x01; with a row maximum of 448 the scale is 1."""
+    subnormal 2^-9 is 0x01; with a row maximum of 448 the scale is 2^0, with
+    449 it is 2^1 (the smallest power of two that brings the row within 448)."""
     row = np.array([448, 1, 2.0 ** -6, 2.0 ** -9, -448, -1, 0, 0.5], np.float32)
-    for codes, s in (rec.e4m3_rows(row[None])[:2], bf.e4m3_row(row)[:2]):
-        assert float(np.asarray(s).reshape(-1)[0]) == 1.0
+    for codes, e in (rec.e4m3_rows(row[None])[:2], bf.e4m3_row(row)[:2]):
+        assert int(np.asarray(e).reshape(-1)[0]) == 0
         assert list(np.asarray(codes).reshape(-1)) == [0x7E, 0x38, 0x08, 0x01, 0xFE, 0xB8, 0x00, 0x30]
+    for amax, e in ((449.0, 1), (896.0, 1), (897.0, 2), (224.0, -1), (225.0, 0), (1e-40, -126)):
+        assert rec.e4m3_rows(np.array([[amax, 0]], np.float32))[1][0] == e, amax
+        assert bf.e4m3_row(np.array([amax, 0], np.float32))[1] == e, amax
 
 
 def test_e4m3_every_finite_value_round_trips():
@@ -683,8 +687,8 @@ def test_e4m3_every_finite_value_round_trips():
     table = bf.e4m3_values()
     assert table[0] == 0 and table[-1] == 448 and np.all(np.diff(table) > 0)
     row = np.concatenate([table, -table[1:]]).astype(np.float32)
-    codes, s, vals = rec.e4m3_rows(row[None])
-    assert s[0] == 1.0
+    codes, e, vals = rec.e4m3_rows(row[None])
+    assert e[0] == 0
     np.testing.assert_array_equal(vals[0], row.astype(np.float64))
     np.testing.assert_array_equal(codes[0][:127], np.arange(127))
     np.testing.assert_array_equal(codes[0][127:], np.arange(1, 127) | 0x80)
@@ -708,9 +712,9 @@ def test_e4m3_ties_go_to_the_even_code():
 def test_e4m3_rows_two_implementations_agree():
     """The recurrent oracle's quantiser (arithmetic on the binade) and the
     brute-force one (nearest entry of the code table) give the same codes,
-    scales and values on rows of every magnitude, zero rows included; the
-    relative error of a value is at most 2^-4 of the row maximum's scale
-    times 448 (half a step of the top binade)."""
+    scale exponents and values on rows of every magnitude, zero rows
+    included; a value is off by at most half a step of the top binade,
+    16 times the scale."""
     rng = np.random.default_rng(11)
     X = (rng.standard_normal((300, 64)) * np.exp(rng.uniform(-20, 12, (300, 1)))).astype(np.float32)
     X[5] = 0
@@ -719,9 +723,12 @@ def test_e4m3_rows_two_implementations_agree():
     for i in range(len(X)):
         cb, sb, vb = bf.e4m3_row(X[i])
         assert np.array_equal(cb, c[i]) and sb == s[i] and np.array_equal(vb, v[i]), i
-    amax = np.abs(X).max(axis=1, keepdims=True)
-    assert np.all(np.abs(v - X) <= amax * 2.0 ** -4 + 1e-300)
-    assert s[5] == 1.0 and not c[5].any()
+    assert np.all(np.abs(v - X) <= 16.0 * np.exp2(s.astype(np.float64))[:, None])
+    amax = np.abs(X).max(axis=1)
+    nz = amax > 0
+    assert np.all(amax[nz] <= 448 * np.exp2(s[nz].astype(np.float64)))
+    assert np.all(amax[nz] > 224 * np.exp2(s[nz].astype(np.float64)))
+    assert s[5] == 0 and not c[5].any()
 
 
 FP8_CASES = [
