@@ -320,11 +320,15 @@ def run_decode_bench(torch, still, inputs, n_steps):
     wall = time.perf_counter() - t0
     step_ms = e0.elapsed_time(e1) / n_steps
     paged_ms = run_decode_paged(torch, still, wl, x, toks, n_steps)
+    pool8_ms = run_decode_pool8(torch, still, wl, x, toks, n_steps)
     d, units = wl.head_dim, wl.batch * wl.n_kv_heads
     n_pool = 256  # 255 kept after the prefill, +1 at the boundary of step 0
     per_unit = (wl.window + n_pool) * 2 * d * 2 + d * d * 4 + d * 4
     io = (wl.batch * wl.n_q_heads * d * 2) * 2 + wl.batch * wl.n_kv_heads * d * 2 * 2
     step_bytes = units * per_unit + io
+    # the 8-bit pool: codes and an exponent byte per kept row, the window band at bf16
+    per_unit8 = wl.window * 2 * d * 2 + n_pool * 2 * (d + 1) + d * d * 4 + d * 4
+    step_bytes8 = units * per_unit8 + io
     return {"workload": wl.name, "batch": wl.batch, "context": wl.seq_len, "steps": n_steps,
             "ms_per_step": step_ms, "tokens_per_s": wl.batch / (step_ms * 1e-3),
             "wall_s": wall, "algorithmic_bytes_per_step": step_bytes,
@@ -332,10 +336,42 @@ def run_decode_bench(torch, still, inputs, n_steps):
             "hbm_frac": step_bytes / (step_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
             "traffic": measured_traffic("decode_kernel", "decode_llama8b_B64_ctx16K.md",
                                         DECODE_SOURCES),
+            "pool8": {"ms_per_step": pool8_ms, "vs_full_pool": pool8_ms / step_ms,
+                      "algorithmic_bytes_per_step": step_bytes8,
+                      "hbm_gbs": step_bytes8 / (pool8_ms * 1e-3) / 1e9,
+                      "hbm_frac": step_bytes8 / (pool8_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                      "layout": "kept K/V rows as E4M3 codes, one power-of-two scale byte per row"},
             "paged": {"ms_per_step": paged_ms, "hbm_gbs": step_bytes / (paged_ms * 1e-3) / 1e9,
                       "vs_unpaged": paged_ms / step_ms,
                       "layout": "kept pool in 16-row pages of a shared arena, "
                                 "each unit's pages a seeded random permutation"}}
+
+
+def run_decode_pool8(torch, still, wl, x, toks, n_steps):
+    """The same decode steps with the kept pool as an 8-bit store
+    (STILL_FLAG_POOL_FP8): a prefill of the same inputs with that flag,
+    then the timed steps. Returns ms per step."""
+    p = still.params_for(wl, flags=still.STILL_FLAG_POOL_FP8)
+    bufs = still.PrefillBuffers(p, wl.seq_len)
+    still.run_prefill(p, x, bufs)
+    del bufs.out, bufs.workspace
+    out = torch.empty((wl.batch, wl.n_q_heads, wl.head_dim), dtype=torch.bfloat16, device="cuda")
+    sel = torch.empty((wl.batch, wl.n_kv_heads, still.still_lambda(p)), dtype=torch.int32,
+                      device="cuda")
+    st2 = bufs.state.clone()
+    for s in range(8):
+        still.still_decode_step(p, wl.seq_len + s, toks["q"][s], toks["k"][s], toks["v"][s],
+                                x["fmap_w"], x["gate"], st2, out, sel)
+    torch.cuda.synchronize()
+    del st2
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for s in range(n_steps):
+        still.still_decode_step(p, wl.seq_len + s, toks["q"][8 + s], toks["k"][8 + s],
+                                toks["v"][8 + s], x["fmap_w"], x["gate"], bufs.state, out, sel)
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / n_steps
 
 
 def run_decode_paged(torch, still, wl, x, toks, n_steps):

@@ -663,32 +663,27 @@ __device__ __forceinline__ float group_max(float m) {
   return m;
 }
 
-// Two E4M3 codes (bytes 0, 1 of c; with HI bytes 2, 3) as two bf16 values
-// packed in 32 bits: exact, every E4M3 value is a bf16 value (the float32
-// conversion leaves the low 16 bits zero).
+// Two E4M3 codes (bytes 0, 1 of c; with HI bytes 2, 3) times the power of
+// two s, as two bf16 values packed in 32 bits (exact while the products are
+// normal bf16 values).
 template <bool HI = false>
-__device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t c) {
-  typedef float f2_t __attribute__((ext_vector_type(2)));
-  const f2_t f = __builtin_amdgcn_cvt_pk_f32_fp8((int)c, HI);
-  return (__float_as_uint(f[0]) >> 16) | (__float_as_uint(f[1]) & 0xFFFF0000u);
+__device__ __forceinline__ uint32_t e4m3x2_scaled_bf16x2(uint32_t c, float s) {
+  typedef __bf16 bf2_t __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c, s, HI));
 }
 
-// Eight E4M3 codes (bytes of w0, then of w1, element order) as a bf16 fragment.
-__device__ __forceinline__ Frag<bf16> e4m3x8_frag(uint32_t w0, uint32_t w1) {
-  const u32x4 r = {e4m3x2_to_bf16x2<false>(w0), e4m3x2_to_bf16x2<true>(w0), e4m3x2_to_bf16x2<false>(w1),
-                   e4m3x2_to_bf16x2<true>(w1)};
-  Frag<bf16> f;
-  f.v = __builtin_bit_cast(bf16x8, r);
-  return f;
-}
 // A fragment loaded raw: with codes, its first 8 bytes are E4M3 codes, made
-// 8 bf16 values; else it is returned as it is (Tag keeps this out of code
-// paths a template discards).
+// 8 bf16 values times the power of two s; else it is returned as it is (Tag
+// keeps this out of code paths a template discards).
 template <typename T, typename Tag>
-__device__ __forceinline__ Frag<T> e4m3x8_or_raw(Tag, bool codes, const Frag<T>& f) {
+__device__ __forceinline__ Frag<T> e4m3x8_or_raw(Tag, bool codes, const Frag<T>& f, float s) {
   static_assert(sizeof(T) == 2 && Tag::value, "8-bit rows: 16-bit data");
   const u32x4 w = __builtin_bit_cast(u32x4, f.v);
-  return codes ? e4m3x8_frag(w[0], w[1]) : f;
+  const u32x4 r = {e4m3x2_scaled_bf16x2<false>(w[0], s), e4m3x2_scaled_bf16x2<true>(w[0], s),
+                   e4m3x2_scaled_bf16x2<false>(w[1], s), e4m3x2_scaled_bf16x2<true>(w[1], s)};
+  Frag<T> g;
+  g.v = __builtin_bit_cast(decltype(g.v), r);
+  return codes ? g : f;
 }
 
 }  // namespace still

@@ -816,7 +816,7 @@ void decode_kernel(DecodeArgs a) {
   struct TileRegs0 {
     Frag<T> af[D / 32];
     uint32_t vw[NVW];
-    uint32_t sc[P8 ? 2 : 1];  // 8-bit pool: scale exponent bytes (+127) of keys 4g + i, keys then values
+    uint32_t sc[P8 ? 2 : 1];  // 8-bit pool: exponent bytes (+127): the word holding key row kk0 + r's, the value keys 4g + i
   };
   TileRegs0 TA0;
 
@@ -926,8 +926,10 @@ void decode_kernel(DecodeArgs a) {
 #pragma unroll
       for (int kb = 0; kb < D / 32; ++kb)  // raw: converted where the tile is used
         X.af[kb] = ld_frag_buf<T>(st_r, koff + (in8 ? 32 : 64) * kb, 0);
-      const int ks = kk0 + 4 * g4;  // the lane's keys ks .. ks + 3: 4 exponent bytes
-      const uint32_t eko = ks < n_oob ? (uint32_t)a.st_pool_k + P * D + (uint32_t)ks : oob;
+      // exponent bytes: of the lane's key row kr_ (in its aligned word), and
+      // of its value keys ks .. ks + 3
+      const int ks = kk0 + 4 * g4;
+      const uint32_t eko = in8 ? (uint32_t)a.st_pool_k + P * D + (uint32_t)(kr_ & ~3) : oob;
       const uint32_t evo = ks < n_oob ? (uint32_t)a.st_pool_v + P * D + (uint32_t)ks : oob;
       X.sc[0] = __builtin_amdgcn_raw_buffer_load_b32(st_r, eko, 0, 0);
       X.sc[1] = __builtin_amdgcn_raw_buffer_load_b32(st_r, evo, 0, 0);
@@ -1000,20 +1002,17 @@ void decode_kernel(DecodeArgs a) {
     // 8-bit pool: the lane's key row kk0 + r below n_oob holds codes (the
     // first 8 bytes of its load), converted here, where the tile is used
     const bool k8 = Q8 && kk0 + r16 < n_oob;
+    float ks8 = 1.f;  // 2^e of the lane's key row
+    if constexpr (Q8) ks8 = __uint_as_float(((X.sc[0] >> (8 * ((kk0 + r16) & 3))) & 255u) << 23);
 #pragma unroll
     for (int kb = 0; kb < D / 32; ++kb) {
       Frag<T> af = X.af[kb];
-      if constexpr (Q8) af = e4m3x8_or_raw<T>(p8, k8, af);
+      if constexpr (Q8) af = e4m3x8_or_raw<T>(p8, k8, af, ks8);
       mma(c, af, qb[kb]);
       if (qb2) mma(c, af, qb2[kb]);
     }
     // c[i] = <key kk0 + 4g + i, query-side column r>; an 8-bit key's
     // product times its row scale (1 for the others)
-    if constexpr (Q8) {  // scale 2^(byte - 127); the ring's keys 1
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        c[i] *= kk0 + 4 * g4 + i < n_oob ? __uint_as_float(((X.sc[0] >> (8 * i)) & 255u) << 23) : 1.f;
-    }
     float mx = STILL_NEG_INF;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -1054,12 +1053,6 @@ void decode_kernel(DecodeArgs a) {
             for (int i = 0; i < 4; ++i) accm[blk][par][i] *= ar[i];
         wave_sync();  // the slot is written again by the next tile
       }
-      // an 8-bit value row's scale goes into its weight (after the sum l)
-      if constexpr (Q8) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          c[i] *= kk0 + 4 * g4 + i < n_oob ? __uint_as_float(((X.sc[1] >> (8 * i)) & 255u) << 23) : 1.f;
-      }
       // weights as bf16 hi (the top 16 bits) + lo (the remainder's top 16
       // bits): ~16 significant bits; A operand: row = head r, keys 4g + i
       typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -1074,12 +1067,13 @@ void decode_kernel(DecodeArgs a) {
       for (int blk = 0; blk < D / 32; ++blk) {
         uint32_t w0 = X.vw[blk], w1 = X.vw[(D / 32) + blk];
         uint32_t w2 = X.vw[2 * (D / 32) + blk], w3 = X.vw[3 * (D / 32) + blk];
-        if constexpr (Q8) {  // an 8-bit row's two codes: half r % 2 of its aligned 4 bytes
+        if constexpr (Q8) {  // an 8-bit row's two codes (half r % 2 of its aligned 4 bytes) times 2^e
           const int k0 = kk0 + 4 * g4, sh = 16 * (r16 & 1);
-          w0 = k0 < n_oob ? e4m3x2_to_bf16x2(w0 >> sh) : w0;
-          w1 = k0 + 1 < n_oob ? e4m3x2_to_bf16x2(w1 >> sh) : w1;
-          w2 = k0 + 2 < n_oob ? e4m3x2_to_bf16x2(w2 >> sh) : w2;
-          w3 = k0 + 3 < n_oob ? e4m3x2_to_bf16x2(w3 >> sh) : w3;
+          const uint32_t ev = X.sc[1];
+          w0 = k0 < n_oob ? e4m3x2_scaled_bf16x2(w0 >> sh, __uint_as_float((ev & 255u) << 23)) : w0;
+          w1 = k0 + 1 < n_oob ? e4m3x2_scaled_bf16x2(w1 >> sh, __uint_as_float(((ev >> 8) & 255u) << 23)) : w1;
+          w2 = k0 + 2 < n_oob ? e4m3x2_scaled_bf16x2(w2 >> sh, __uint_as_float(((ev >> 16) & 255u) << 23)) : w2;
+          w3 = k0 + 3 < n_oob ? e4m3x2_scaled_bf16x2(w3 >> sh, __uint_as_float((ev >> 24) << 23)) : w3;
         }
 #pragma unroll
         for (int par = 0; par < 2; ++par) {
