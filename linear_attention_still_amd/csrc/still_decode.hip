@@ -1203,7 +1203,9 @@ void decode_kernel(DecodeArgs a) {
     return (uint32_t)a.st_ring_phi + (uint32_t)wrap(la_slot + kk) * (D * sizeof(T));
   };
   auto vrow_la = [&](int kk) -> uint32_t { return rv_off + (uint32_t)wrap(la_slot + kk) * (D * sizeof(T)); };
-  constexpr bool LA_EARLY = G <= 4;
+  // (not with the 8-bit or the paged pool: their softmax tiles carry more
+  // registers, and a third tile live through that walk would spill)
+  constexpr bool LA_EARLY = G <= 4 && !P8 && !PAGED;
   TileRegs TC;
   if constexpr (LA_EARLY) load_tile(TC, 16 * wave, n_la, krow_la, vrow_la, std::false_type{});
   {
