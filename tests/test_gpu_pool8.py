@@ -112,3 +112,43 @@ def test_pool8_prefill_and_decode(case):
         if t % wl.chunk == 0 and o["lam"] > 0:
             got = np.stack([sels[s, b, kv].numpy() for b, kv in units])
             assert np.array_equal(got, o["sel"][:, t // wl.chunk - 1]), s
+
+
+def test_pool8_decode_workload_sampled_units():
+    """Batch 64 at 16K context (32/8 heads, d = 128, W = C = 64, budget 512)
+    with the 8-bit pool, in the bench's launch configuration: prefill, 64
+    decode steps (one chunk-boundary decision); the stored codes of 16 units
+    bit-exact, their outputs against the oracle that reads the quantised
+    pool, the boundary's selections exact."""
+    from linear_attention_still_amd.inputs import WORKLOADS
+    wl = WORKLOADS["decode_bf16_B64_ctx16K"]
+    L0, n = wl.seq_len, wl.decode_steps
+    x = make_inputs(wl, device="cuda")
+    toks = make_decode_tokens(wl, n, device="cuda")
+    p = still.params_for(wl, fp32_out=True, flags=still.STILL_FLAG_POOL_FP8)
+    print("  gpu prefill (8-bit pool) B=64 L=16384", flush=True)
+    bufs = still.PrefillBuffers(p, L0)
+    still.run_prefill(p, x, bufs)
+    outs, sels = P.run_decode(wl, bufs.state, p, x, toks, L0, fp32_out=True)
+    units = [(b, (5 * i + 1) % wl.n_kv_heads) for i, b in
+             enumerate([1, 5, 8, 12, 16, 20, 25, 29, 34, 38, 41, 45, 51, 54, 58, 62])]
+    sv = still.state_views(p, bufs.state)
+    meta, pos = sv["meta"].cpu().numpy(), sv["pool_pos"].cpu().numpy()
+    for b, kv in units:
+        u = b * wl.n_kv_heads + kv
+        m = int(meta[u, 1])
+        for name, src in (("k", x["k"]), ("v", x["v"])):
+            rows = torch.cat([src[b, kv], toks[name][:, b, kv]]).float().cpu().numpy()
+            codes, exps, _ = rec.e4m3_rows(rows[pos[u, :m]])
+            assert np.array_equal(sv["pool_%s8" % name][u, :m].cpu().numpy(), codes), (name, b, kv)
+            assert np.array_equal(sv["pool_%s_exp" % name][u, :m].cpu().numpy().astype(np.int64) - 127,
+                                  exps.astype(np.int64)), (name, b, kv)
+    qs, ks, vs, Fs, gs = P.concat_units(x, toks, wl, units)
+    print("  oracle %d units, %d tokens, 8-bit pool from %d" % (len(units), L0 + n, L0), flush=True)
+    o = rec.run_units(qs, ks, vs, Fs, gs, window=wl.window, chunk=wl.chunk, budget=wl.budget,
+                      t_max=wl.t_max, n_threads=P.n_threads(), fp8_from=L0)
+    G = wl.group
+    yg = np.stack([outs[:, b, kv * G:(kv + 1) * G].numpy().transpose(1, 0, 2) for b, kv in units])
+    P.check_outputs(yg, o["y"][:, :, L0:], "bf16", True, "pool8 decode y (16K)")
+    got = np.stack([sels[0, b, kv].numpy() for b, kv in units])
+    assert np.array_equal(got, o["sel"][:, L0 // wl.chunk - 1])
